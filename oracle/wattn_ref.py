@@ -1,0 +1,268 @@
+"""O1: materialized window attention with window-local 2D RoPE, float64 (test infrastructure).
+
+Only tests, the smoke check and the benchmark's CPU-baseline leg use this
+module.  It is deliberately plain: numpy float64, a full N x N score matrix per
+window-head, no tiling, no fusion.
+
+What is computed ([FS] = the paper card "FLASHSWIN: Unlocking Large Windows and
+Dense Tokens in Swin Vision Transformers with Memory Efficient Attention"):
+
+* exact softmax attention inside each M x M window ([FS] Abstract: windowed
+  attention computed exactly, without the additive relative-position bias);
+* positions restored by window-local 2D RoPE applied to Q and K ([FS] Abstract;
+  Figure 1(B)); theta is the per-head angular frequency in rad/token, the
+  exp(omega) parameterisation of [FS] Figure S4 lives in the caller;
+* Swin's shifted windows: roll the grid by -shift, partition, attend with the
+  region mask, un-partition, roll back by +shift (the shifted configuration
+  of the workload; the pages themselves do not describe the mask).
+
+Conventions the pages leave open, and the reading taken here:
+
+* token-grid layout [B, Hg, Wg, heads, d]; window token index n = r*M + c;
+* channels [0, d/2) carry the row axis, pairs (2j, 2j+1) rotated by
+  theta_row[h, j] * r; channels [d/2, d) carry the column axis, pairs
+  (d/2+2j, d/2+2j+1) rotated by theta_col[h, j] * c, j in [0, d/4);
+* rotation (a, b) -> (a cos phi - b sin phi, a sin phi + b cos phi), the same
+  for Q and K; positions (r, c) are in the shifted frame;
+* scores S = q~ . k~ / sqrt(d); masked pairs are excluded (weight exactly 0);
+* LSE = natural log of sum_j exp(S_ij) over the live keys.
+
+Parity: pinned by tests/test_oracle.py (brute force, library attention for
+theta = 0, constant-V, closed-form RoPE pair, region decomposition, finite
+differences, invariants, agreement with O2).  The RoPE conventions above are
+"parity unpinned" against the pages (they print none).
+"""
+
+import numpy as np
+
+SUPPORTED_D = (4, 8, 16, 32, 64)
+
+
+def check_args(shape, theta_row_shape, theta_col_shape, M, shift):
+    """Validate a call; raises ValueError with the reason.
+
+    shape = (B, Hg, Wg, heads, d).  Hg and Wg must be multiples of M
+    (non-divisible grids are rejected rather than padded), 0 <= shift < M,
+    d a multiple of 4, theta arrays of shape [heads, d/4].
+    """
+    if len(shape) != 5:
+        raise ValueError("q/k/v must be [B, Hg, Wg, heads, d]")
+    B, Hg, Wg, heads, d = shape
+    if B < 0 or heads < 1:
+        raise ValueError("need B >= 0 and heads >= 1")
+    if M < 1 or Hg % M or Wg % M:
+        raise ValueError("Hg and Wg must be positive multiples of M")
+    if not (0 <= shift < M):
+        raise ValueError("need 0 <= shift < M")
+    if d % 4 or d < 4:
+        raise ValueError("d must be a positive multiple of 4")
+    if tuple(theta_row_shape) != (heads, d // 4) or tuple(theta_col_shape) != (heads, d // 4):
+        raise ValueError("theta_row/theta_col must be [heads, d/4]")
+
+
+def _roll(x, s):
+    """Swin cyclic shift: result[Y, X] = x[(Y + s) mod Hg, (X + s) mod Wg]."""
+    if s == 0:
+        return x
+    return np.roll(x, shift=(-s, -s), axis=(1, 2))
+
+
+def _unroll(x, s):
+    if s == 0:
+        return x
+    return np.roll(x, shift=(s, s), axis=(1, 2))
+
+
+def _partition(x, M):
+    """[B, Hg, Wg, *rest] -> [B*nH*nW, M*M, *rest], window index (b, wy, wx), token n = r*M + c."""
+    B, Hg, Wg = x.shape[:3]
+    rest = x.shape[3:]
+    x = x.reshape(B, Hg // M, M, Wg // M, M, *rest)
+    x = np.swapaxes(x, 2, 3)  # B, nH, nW, M(r), M(c), rest
+    return x.reshape(B * (Hg // M) * (Wg // M), M * M, *rest)
+
+
+def _unpartition(xw, B, Hg, Wg, M):
+    rest = xw.shape[2:]
+    x = xw.reshape(B, Hg // M, Wg // M, M, M, *rest)
+    x = np.swapaxes(x, 2, 3)
+    return x.reshape(B, Hg, Wg, *rest)
+
+
+def region_labels(Hg, Wg, M, s):
+    """Swin region label of every token of every window, shape [nH, nW, M*M].
+
+    In the shifted frame the rows are cut into [0, Hg-M), [Hg-M, Hg-s),
+    [Hg-s, Hg) (likewise the columns); label = 3*row_region + col_region.
+    With s == 0 every label is 0 (no mask).
+    """
+    row_lab = np.zeros(Hg, dtype=np.int64)
+    col_lab = np.zeros(Wg, dtype=np.int64)
+    if s > 0:
+        row_lab[Hg - M:Hg - s] = 1
+        row_lab[Hg - s:] = 2
+        col_lab[Wg - M:Wg - s] = 1
+        col_lab[Wg - s:] = 2
+    grid = 3 * row_lab[:, None] + col_lab[None, :]  # [Hg, Wg]
+    nH, nW = Hg // M, Wg // M
+    g = grid.reshape(nH, M, nW, M).swapaxes(1, 2)  # nH, nW, r, c
+    return g.reshape(nH, nW, M * M)
+
+
+def _angles(theta, pos):
+    """phi[h, n, j] = theta[h, j] * pos[n]."""
+    return theta[:, None, :] * pos[None, :, None]
+
+
+def rope_rotate(xw, theta_row, theta_col, M, inverse=False):
+    """Rotate channel pairs of windowed x [nWin, heads, N, d] by the 2D RoPE angles.
+
+    inverse=True applies the transpose rotation (angle -phi), used to pull
+    gradients of the rotated tensor back to the unrotated one.
+    """
+    d = xw.shape[-1]
+    h2 = d // 2
+    n = np.arange(M * M)
+    r = (n // M).astype(np.float64)
+    c = (n % M).astype(np.float64)
+    sign = -1.0 if inverse else 1.0
+    out = np.empty_like(xw)
+    for lo, theta, pos in ((0, theta_row, r), (h2, theta_col, c)):
+        phi = sign * _angles(np.asarray(theta, dtype=np.float64), pos)  # [heads, N, d/4]
+        cs, sn = np.cos(phi)[None], np.sin(phi)[None]
+        a = xw[..., lo:lo + h2:2]
+        b = xw[..., lo + 1:lo + h2:2]
+        out[..., lo:lo + h2:2] = a * cs - b * sn
+        out[..., lo + 1:lo + h2:2] = a * sn + b * cs
+    return out
+
+
+def _windows(x, M, s):
+    """Grid tensor [B, Hg, Wg, heads, d] -> windowed float64 [nWin, heads, N, d]."""
+    xw = _partition(_roll(np.asarray(x, dtype=np.float64), s), M)
+    return np.ascontiguousarray(np.swapaxes(xw, 1, 2))
+
+
+def _window_mask(B, Hg, Wg, M, s):
+    """Boolean live-pair mask [nWin, 1, N, N] or None when s == 0."""
+    if s == 0:
+        return None
+    lab = region_labels(Hg, Wg, M, s).reshape(-1, M * M)  # [nH*nW, N]
+    live = lab[:, :, None] == lab[:, None, :]
+    live = np.broadcast_to(live[None], (B,) + live.shape).reshape(-1, 1, M * M, M * M)
+    return live
+
+
+def window_scores_ref(q, k, theta_row, theta_col, M, shift):
+    """Materialized scaled scores S [nWin, heads, N, N] (masked pairs = -inf). Small inputs only."""
+    B, Hg, Wg, heads, d = np.shape(q)
+    qw = rope_rotate(_windows(q, M, shift), theta_row, theta_col, M)
+    kw = rope_rotate(_windows(k, M, shift), theta_row, theta_col, M)
+    S = qw @ np.swapaxes(kw, -1, -2) / np.sqrt(d)
+    live = _window_mask(B, Hg, Wg, M, shift)
+    if live is not None:
+        S = np.where(live, S, -np.inf)
+    return S
+
+
+def _chunks(n_win, heads, N, budget_bytes=256 << 20):
+    per = max(1, budget_bytes // (heads * N * N * 8))
+    for lo in range(0, n_win, per):
+        yield slice(lo, min(n_win, lo + per))
+
+
+def wattn_fwd_ref(q, k, v, theta_row, theta_col, M, shift):
+    """Forward: returns (out [B,Hg,Wg,heads,d] float64, lse [B,Hg,Wg,heads] float64)."""
+    q = np.asarray(q)
+    B, Hg, Wg, heads, d = q.shape
+    theta_row = np.asarray(theta_row, dtype=np.float64)
+    theta_col = np.asarray(theta_col, dtype=np.float64)
+    check_args(q.shape, theta_row.shape, theta_col.shape, M, shift)
+    N = M * M
+    qw = rope_rotate(_windows(q, M, shift), theta_row, theta_col, M)
+    kw = rope_rotate(_windows(k, M, shift), theta_row, theta_col, M)
+    vw = _windows(v, M, shift)
+    live_all = _window_mask(B, Hg, Wg, M, shift)
+    ow = np.empty_like(vw)
+    lw = np.empty(vw.shape[:3], dtype=np.float64)
+    for sl in _chunks(qw.shape[0], heads, N):
+        S = qw[sl] @ np.swapaxes(kw[sl], -1, -2) / np.sqrt(d)
+        if live_all is not None:
+            S = np.where(live_all[sl], S, -np.inf)
+        m = S.max(axis=-1, keepdims=True)
+        e = np.exp(S - m)
+        ssum = e.sum(axis=-1, keepdims=True)
+        P = e / ssum
+        ow[sl] = P @ vw[sl]
+        lw[sl] = (m + np.log(ssum))[..., 0]
+    out = _unroll(_unpartition(np.swapaxes(ow, 1, 2), B, Hg, Wg, M), shift)
+    lse = _unroll(_unpartition(np.swapaxes(lw, 1, 2), B, Hg, Wg, M), shift)
+    return out, lse
+
+
+def _dtheta_terms(xt, dxt, M):
+    """Per-pair dtheta integrand summed over windows and tokens.
+
+    For a pair (a, b) rotated by phi = theta * p, d x~_a / d phi = -x~_b and
+    d x~_b / d phi = x~_a, so dL/dtheta = sum p * (dx~_b * x~_a - dx~_a * x~_b).
+    xt, dxt: [nWin, heads, N, d] (rotated tensor and the gradient w.r.t. it).
+    Returns (row [heads, d/4], col [heads, d/4]).
+    """
+    d = xt.shape[-1]
+    h2 = d // 2
+    n = np.arange(M * M)
+    r = (n // M).astype(np.float64)
+    c = (n % M).astype(np.float64)
+    res = []
+    for lo, pos in ((0, r), (h2, c)):
+        a, b = xt[..., lo:lo + h2:2], xt[..., lo + 1:lo + h2:2]
+        da, db = dxt[..., lo:lo + h2:2], dxt[..., lo + 1:lo + h2:2]
+        integrand = (db * a - da * b) * pos[None, None, :, None]
+        res.append(integrand.sum(axis=(0, 2)))
+    return res[0], res[1]
+
+
+def wattn_bwd_ref(q, k, v, dout, theta_row, theta_col, M, shift):
+    """Analytic backward of wattn_fwd_ref.
+
+    Returns (dq, dk, dv [B,Hg,Wg,heads,d], dtheta_row, dtheta_col [heads,d/4]), float64.
+    dV = P^T dO; dP = dO V^T; D_i = sum_j P_ij dP_ij; dS = P o (dP - D);
+    dq~ = dS k~ / sqrt(d); dk~ = dS^T q~ / sqrt(d); dq = R^T dq~, dk = R^T dk~.
+    """
+    q = np.asarray(q)
+    B, Hg, Wg, heads, d = q.shape
+    theta_row = np.asarray(theta_row, dtype=np.float64)
+    theta_col = np.asarray(theta_col, dtype=np.float64)
+    check_args(q.shape, theta_row.shape, theta_col.shape, M, shift)
+    N = M * M
+    qw = rope_rotate(_windows(q, M, shift), theta_row, theta_col, M)
+    kw = rope_rotate(_windows(k, M, shift), theta_row, theta_col, M)
+    vw = _windows(v, M, shift)
+    dow = _windows(dout, M, shift)
+    live_all = _window_mask(B, Hg, Wg, M, shift)
+    dqt = np.empty_like(qw)
+    dkt = np.empty_like(kw)
+    dvw = np.empty_like(vw)
+    scale = 1.0 / np.sqrt(d)
+    for sl in _chunks(qw.shape[0], heads, N):
+        S = qw[sl] @ np.swapaxes(kw[sl], -1, -2) * scale
+        if live_all is not None:
+            S = np.where(live_all[sl], S, -np.inf)
+        m = S.max(axis=-1, keepdims=True)
+        e = np.exp(S - m)
+        P = e / e.sum(axis=-1, keepdims=True)
+        dvw[sl] = np.swapaxes(P, -1, -2) @ dow[sl]
+        dP = dow[sl] @ np.swapaxes(vw[sl], -1, -2)
+        Dr = (P * dP).sum(axis=-1, keepdims=True)
+        dS = P * (dP - Dr)
+        dqt[sl] = dS @ kw[sl] * scale
+        dkt[sl] = np.swapaxes(dS, -1, -2) @ qw[sl] * scale
+    tr_q, tc_q = _dtheta_terms(qw, dqt, M)
+    tr_k, tc_k = _dtheta_terms(kw, dkt, M)
+    dqw = rope_rotate(dqt, theta_row, theta_col, M, inverse=True)
+    dkw = rope_rotate(dkt, theta_row, theta_col, M, inverse=True)
+
+    def back(xw):
+        return _unroll(_unpartition(np.swapaxes(xw, 1, 2), B, Hg, Wg, M), shift)
+
+    return back(dqw), back(dkw), back(dvw), tr_q + tr_k, tc_q + tc_k

@@ -1,0 +1,527 @@
+"""Pins for the CPU oracle (no GPU).
+
+The oracle (O1 = oracle.wattn_ref, O2 = oracle.wattn_online) is checked
+against things other than itself:
+
+* brute force: per-token scalar loops over the whole grid with a membership
+  predicate (same shifted window, same region), math.cos/sin/exp only;
+* the hand-derived closed-form scores in tests/golden/rope_window_m2.json;
+* torch's scaled_dot_product_attention (float64, CPU) and its autograd for
+  theta = 0 (the "Naive Flash" row of Table S2 on the FlashSwin paper card is
+  exactly this case: fused attention without positional information);
+* the single-window shifted case, which decomposes into four independent
+  attentions over the Swin regions;
+* invariants: constant V, roll equivariance of interior windows, locality of a
+  perturbation, zero upstream gradient, finite differences of the backward;
+* agreement of the two independent routes O1 and O2 (forward and backward).
+
+The mutation test at the end plants plausible mistakes in O1 (on the CPU) and
+checks that at least one pin fails for each.
+"""
+
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import wattn_ref
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "rope_window_m2.json")
+
+
+def _rand_case(seed, B, Hg, Wg, H, D, theta_scale=1.0):
+    rng = np.random.default_rng(seed)
+    q, k, v, do = (rng.standard_normal((B, Hg, Wg, H, D)) for _ in range(4))
+    tr = rng.standard_normal((H, D // 4)) * theta_scale
+    tc = rng.standard_normal((H, D // 4)) * theta_scale
+    return q, k, v, do, tr, tc
+
+
+# ----------------------------------------------------------------------------- brute force
+
+def brute_force_fwd(q, k, v, tr, tc, M, s):
+    """Per-token scalar loops; every key of the grid is tested for membership."""
+    B, Hg, Wg, H, D = q.shape
+
+    def shifted(y, x):
+        return (y - s) % Hg, (x - s) % Wg
+
+    def region(Y, size):
+        if s == 0 or Y < size - M:
+            return 0
+        return 1 if Y < size - s else 2
+
+    def rot(vec, h, r, c):
+        res = [float(t) for t in vec]
+        for j in range(D // 4):
+            for lo, ang in ((0, tr[h][j] * r), (D // 2, tc[h][j] * c)):
+                a, b = float(vec[lo + 2 * j]), float(vec[lo + 2 * j + 1])
+                res[lo + 2 * j] = a * math.cos(ang) - b * math.sin(ang)
+                res[lo + 2 * j + 1] = a * math.sin(ang) + b * math.cos(ang)
+        return res
+
+    out = np.zeros_like(q, dtype=np.float64)
+    lse = np.zeros(q.shape[:4])
+    for b in range(B):
+        for y in range(Hg):
+            for x in range(Wg):
+                Y, X = shifted(y, x)
+                lab = (region(Y, Hg), region(X, Wg))
+                for h in range(H):
+                    qt = rot(q[b, y, x, h], h, Y % M, X % M)
+                    scores, vals = [], []
+                    for y2 in range(Hg):
+                        for x2 in range(Wg):
+                            Y2, X2 = shifted(y2, x2)
+                            if Y2 // M != Y // M or X2 // M != X // M:
+                                continue
+                            if (region(Y2, Hg), region(X2, Wg)) != lab:
+                                continue
+                            kt = rot(k[b, y2, x2, h], h, Y2 % M, X2 % M)
+                            scores.append(sum(qt[i] * kt[i] for i in range(D)) / math.sqrt(D))
+                            vals.append(v[b, y2, x2, h])
+                    mx = max(scores)
+                    e = [math.exp(t - mx) for t in scores]
+                    z = sum(e)
+                    out[b, y, x, h] = sum(ei * vi for ei, vi in zip(e, vals)) / z
+                    lse[b, y, x, h] = mx + math.log(z)
+    return out, lse
+
+
+BRUTE_CASES = [
+    # B, Hg, Wg, H, D, M, s
+    (1, 4, 4, 2, 8, 2, 0),
+    (1, 6, 6, 1, 8, 3, 1),
+    (2, 6, 9, 2, 4, 3, 2),
+    (1, 8, 8, 1, 8, 4, 3),
+]
+
+
+def pin_brute_force(fwd=None):
+    fwd = fwd or oracle.wattn_fwd_ref
+    for i, (B, Hg, Wg, H, D, M, s) in enumerate(BRUTE_CASES):
+        q, k, v, _, tr, tc = _rand_case(10 + i, B, Hg, Wg, H, D)
+        o, l = fwd(q, k, v, tr, tc, M, s)
+        ob, lb = brute_force_fwd(q, k, v, tr, tc, M, s)
+        np.testing.assert_allclose(o, ob, rtol=0, atol=1e-12)
+        np.testing.assert_allclose(l, lb, rtol=0, atol=1e-12)
+
+
+def test_brute_force():
+    pin_brute_force()
+
+
+# ----------------------------------------------------------------------------- golden closed form
+
+def _eval(expr):
+    return float(eval(expr, {"__builtins__": {}}, {"pi": math.pi, "sqrt": math.sqrt}))
+
+
+def pin_golden(fwd=None, scores=None):
+    fwd = fwd or oracle.wattn_fwd_ref
+    scores = scores or oracle.window_scores_ref
+    with open(GOLDEN) as f:
+        spec = json.load(f)
+    for case in spec["cases"]:
+        M, D = case["M"], case["d"]
+        N = M * M
+        tr = np.array([[_eval(t) for t in case["theta_row"]]])
+        tc = np.array([[_eval(t) for t in case["theta_col"]]])
+        q = np.tile(np.array(case["q_all_tokens"], dtype=np.float64), (1, M, M, 1, 1))
+        k = np.tile(np.array(case["k_all_tokens"], dtype=np.float64), (1, M, M, 1, 1))
+        if case["v_identity"]:
+            v = np.eye(N).reshape(1, M, M, 1, N)
+        else:
+            v = np.random.default_rng(0).standard_normal((1, M, M, 1, D))
+        S_exp = np.array([[_eval(e) for e in row] for row in case["scores"]])
+        S = scores(q, k, tr, tc, M, 0)[0, 0]
+        np.testing.assert_allclose(S, S_exp, rtol=0, atol=1e-14)
+        o, l = fwd(q, k, v, tr, tc, M, 0)
+        lse_exp = np.array([math.log(sum(math.exp(t) for t in row)) for row in S_exp])
+        np.testing.assert_allclose(l.reshape(N), lse_exp, rtol=0, atol=1e-14)
+        if case["v_identity"]:
+            P_exp = np.exp(S_exp - lse_exp[:, None])
+            np.testing.assert_allclose(o.reshape(N, N), P_exp, rtol=0, atol=1e-14)
+
+
+def test_golden_closed_form():
+    pin_golden()
+
+
+# ----------------------------------------------------------------------------- library attention
+
+def _torch_windows(x, M):
+    B, Hg, Wg, H, D = x.shape
+    t = torch.from_numpy(np.ascontiguousarray(x))
+    t = t.reshape(B, Hg // M, M, Wg // M, M, H, D).permute(0, 1, 3, 5, 2, 4, 6)
+    return t.reshape(-1, H, M * M, D).contiguous()
+
+
+def _torch_unwindows(t, B, Hg, Wg, M):
+    H, D = t.shape[1], t.shape[3]
+    t = t.reshape(B, Hg // M, Wg // M, H, M, M, D).permute(0, 1, 4, 2, 5, 3, 6)
+    return t.reshape(B, Hg, Wg, H, D)
+
+
+def pin_sdpa(fwd=None, bwd=None):
+    fwd = fwd or oracle.wattn_fwd_ref
+    bwd = bwd or oracle.wattn_bwd_ref
+    for (B, Hg, Wg, H, D, M) in [(2, 8, 8, 2, 8, 4), (1, 16, 8, 3, 32, 8)]:
+        q, k, v, do, _, _ = _rand_case(7, B, Hg, Wg, H, D)
+        tz = np.zeros((H, D // 4))
+        tq, tk, tv = (_torch_windows(x, M).requires_grad_(True) for x in (q, k, v))
+        ot = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv)
+        ot.backward(_torch_windows(do, M))
+        o, _ = fwd(q, k, v, tz, tz, M, 0)
+        np.testing.assert_allclose(o, _torch_unwindows(ot.detach(), B, Hg, Wg, M).numpy(), rtol=0, atol=1e-12)
+        dq, dk, dv, dtr, dtc = bwd(q, k, v, do, tz, tz, M, 0)
+        for mine, ref in ((dq, tq.grad), (dk, tk.grad), (dv, tv.grad)):
+            np.testing.assert_allclose(mine, _torch_unwindows(ref, B, Hg, Wg, M).numpy(), rtol=0, atol=1e-11)
+
+
+def test_theta_zero_matches_library_attention():
+    pin_sdpa()
+
+
+def pin_single_window_regions(fwd=None):
+    """Hg = Wg = M with shift s: the one window holds four Swin regions that attend independently."""
+    fwd = fwd or oracle.wattn_fwd_ref
+    for (M, s, H, D) in [(4, 1, 2, 8), (6, 2, 1, 4), (8, 4, 2, 8)]:
+        q, k, v, _, _, _ = _rand_case(3 + M, 1, M, M, H, D)
+        tz = np.zeros((H, D // 4))
+        o, l = fwd(q, k, v, tz, tz, M, s)
+        # shifted-frame row Y holds original row (Y + s) mod M; regions: Y < M - s -> 1, else 2
+        for rows in (range(0, M - s), range(M - s, M)):
+            for cols in (range(0, M - s), range(M - s, M)):
+                ys = [(Y + s) % M for Y in rows]
+                xs = [(X + s) % M for X in cols]
+                sel = [(y, x) for y in ys for x in xs]
+
+                def gather(t):
+                    return torch.from_numpy(np.stack([t[0, y, x] for (y, x) in sel], axis=1))  # H, n, D
+
+                ref = torch.nn.functional.scaled_dot_product_attention(gather(q), gather(k), gather(v))
+                for i, (y, x) in enumerate(sel):
+                    np.testing.assert_allclose(o[0, y, x], ref[:, i].numpy(), rtol=0, atol=1e-12)
+
+
+def test_single_window_shift_is_four_attentions():
+    pin_single_window_regions()
+
+
+# ----------------------------------------------------------------------------- invariants
+
+def test_constant_v_gives_constant_output():
+    q, k, _, _, tr, tc = _rand_case(5, 2, 8, 8, 2, 8)
+    const = np.random.default_rng(1).standard_normal((2, 8))
+    v = np.broadcast_to(const, q.shape).copy()
+    for s in (0, 3):
+        o, _ = oracle.wattn_fwd_ref(q, k, v, tr, tc, 4, s)
+        np.testing.assert_allclose(o, v, rtol=0, atol=1e-13)
+
+
+def test_interior_windows_equal_unmasked_attention_on_rolled_grid():
+    B, Hg, Wg, H, D, M, s = 1, 12, 12, 2, 8, 4, 2
+    q, k, v, _, tr, tc = _rand_case(6, B, Hg, Wg, H, D)
+    o, l = oracle.wattn_fwd_ref(q, k, v, tr, tc, M, s)
+    rolled = [np.roll(x, (-s, -s), axis=(1, 2)) for x in (q, k, v)]
+    o0, l0 = oracle.wattn_fwd_ref(*rolled, tr, tc, M, 0)
+    o0 = np.roll(o0, (s, s), axis=(1, 2))
+    l0 = np.roll(l0, (s, s), axis=(1, 2))
+    for y in range(Hg):
+        for x in range(Wg):
+            Y, X = (y - s) % Hg, (x - s) % Wg
+            if Y < Hg - M and X < Wg - M:  # window away from the bottom/right edge of the shifted frame
+                np.testing.assert_allclose(o[0, y, x], o0[0, y, x], rtol=0, atol=1e-13)
+                np.testing.assert_allclose(l[0, y, x], l0[0, y, x], rtol=0, atol=1e-13)
+
+
+def test_perturbation_stays_in_window_region():
+    B, Hg, Wg, H, D, M, s = 1, 8, 8, 1, 4, 4, 1
+    q, k, v, _, tr, tc = _rand_case(8, B, Hg, Wg, H, D)
+    o, _ = oracle.wattn_fwd_ref(q, k, v, tr, tc, M, s)
+
+    def key(y, x):
+        Y, X = (y - s) % Hg, (x - s) % Wg
+
+        def reg(t, size):
+            return 0 if t < size - M else (1 if t < size - s else 2)
+
+        return (Y // M, X // M, reg(Y, Hg), reg(X, Wg))
+
+    for (py, px) in [(0, 0), (7, 7), (3, 4), (0, 7)]:
+        k2, v2 = k.copy(), v.copy()
+        k2[0, py, px] += 3.0
+        v2[0, py, px] += 3.0
+        o2, _ = oracle.wattn_fwd_ref(q, k2, v2, tr, tc, M, s)
+        changed = np.abs(o2 - o).max(axis=(3, 4))[0] > 1e-12
+        for y in range(Hg):
+            for x in range(Wg):
+                assert changed[y, x] == (key(y, x) == key(py, px)), (py, px, y, x)
+
+
+def test_zero_upstream_gradient():
+    q, k, v, _, tr, tc = _rand_case(9, 1, 8, 8, 2, 8)
+    grads = oracle.wattn_bwd_ref(q, k, v, np.zeros_like(q), tr, tc, 4, 2)
+    for g in grads:
+        assert np.all(g == 0)
+
+
+def test_lse_from_scores():
+    q, k, _, _, tr, tc = _rand_case(11, 1, 8, 8, 2, 8)
+    S = oracle.window_scores_ref(q, k, tr, tc, 4, 3)
+    v = np.zeros_like(q)
+    _, l = oracle.wattn_fwd_ref(q, k, v, tr, tc, 4, 3)
+    # LSE per window token, compared in window order via the library logsumexp
+    from scipy.special import logsumexp
+    lw = logsumexp(S, axis=-1)  # [nWin, H, N]
+    lw_grid = np.roll(
+        lw.reshape(1, 2, 2, 2, 4, 4).transpose(0, 1, 4, 2, 5, 3).reshape(1, 8, 8, 2), (3, 3), axis=(1, 2))
+    np.testing.assert_allclose(l, lw_grid, rtol=0, atol=1e-13)
+
+
+# ----------------------------------------------------------------------------- backward: finite differences
+
+FD_CASES = [
+    # B, Hg, Wg, H, D, M, s
+    (1, 4, 4, 2, 8, 2, 1),
+    (1, 6, 6, 1, 4, 3, 2),
+]
+
+
+def pin_finite_differences(fwd=None, bwd=None):
+    fwd = fwd or oracle.wattn_fwd_ref
+    bwd = bwd or oracle.wattn_bwd_ref
+    h = 1e-6
+    for i, (B, Hg, Wg, H, D, M, s) in enumerate(FD_CASES):
+        q, k, v, do, tr, tc = _rand_case(20 + i, B, Hg, Wg, H, D)
+        args = [q, k, v, tr, tc]
+        grads = bwd(q, k, v, do, tr, tc, M, s)
+
+        def loss(a):
+            o, _ = fwd(a[0], a[1], a[2], a[3], a[4], M, s)
+            return float((o * do).sum())
+
+        for which, g in zip(range(5), (grads[0], grads[1], grads[2], grads[3], grads[4])):
+            base = args[which]
+            num = np.zeros_like(base)
+            it = np.nditer(base, flags=["multi_index"])
+            for _ in it:
+                idx = it.multi_index
+                plus = [a.copy() for a in args]
+                minus = [a.copy() for a in args]
+                plus[which][idx] += h
+                minus[which][idx] -= h
+                num[idx] = (loss(plus) - loss(minus)) / (2 * h)
+            np.testing.assert_allclose(g, num, rtol=0, atol=2e-8 * max(1.0, np.abs(num).max()))
+
+
+def test_finite_differences():
+    pin_finite_differences()
+
+
+def test_dv_closed_form_and_dtheta_origin_invariance():
+    """dV = P^T dO per window; per window and pair, sum of (dx~_b x~_a - dx~_a x~_b) over Q and K is 0."""
+    B, Hg, Wg, H, D, M, s = 1, 8, 8, 2, 8, 4, 2
+    q, k, v, do, tr, tc = _rand_case(12, B, Hg, Wg, H, D)
+    S = oracle.window_scores_ref(q, k, tr, tc, M, s)
+    P = np.exp(S - S.max(-1, keepdims=True))
+    P /= P.sum(-1, keepdims=True)
+    dow = wattn_ref._windows(do, M, s)
+    dv_w = np.swapaxes(P, -1, -2) @ dow
+    _, _, dv, _, _ = oracle.wattn_bwd_ref(q, k, v, do, tr, tc, M, s)
+    np.testing.assert_allclose(wattn_ref._windows(dv, M, s), dv_w, rtol=0, atol=1e-13)
+    # origin invariance: a common rotation of every q~ and k~ of a window leaves S unchanged
+    qw = wattn_ref.rope_rotate(wattn_ref._windows(q, M, s), tr, tc, M)
+    kw = wattn_ref.rope_rotate(wattn_ref._windows(k, M, s), tr, tc, M)
+    vw = wattn_ref._windows(v, M, s)
+    dP = dow @ np.swapaxes(vw, -1, -2)
+    dS = P * (dP - (P * dP).sum(-1, keepdims=True))
+    np.testing.assert_allclose(dS.sum(-1), 0, atol=1e-13)
+    dqt = dS @ kw / np.sqrt(D)
+    dkt = np.swapaxes(dS, -1, -2) @ qw / np.sqrt(D)
+    tot = 0
+    for xt, dxt in ((qw, dqt), (kw, dkt)):
+        a, b = xt[..., 0::2], xt[..., 1::2]
+        da, db = dxt[..., 0::2], dxt[..., 1::2]
+        tot = tot + (db * a - da * b).sum(axis=2)  # [nWin, H, d/2]
+    np.testing.assert_allclose(tot, 0, atol=1e-12)
+
+
+# ----------------------------------------------------------------------------- O1 vs O2
+
+O12_CASES = [
+    (2, 8, 8, 2, 8, 4, 0),
+    (2, 8, 8, 2, 8, 4, 2),
+    (1, 6, 9, 1, 4, 3, 1),
+    (1, 12, 12, 2, 16, 6, 3),
+    (1, 16, 16, 2, 32, 8, 4),
+    (2, 3, 3, 1, 4, 1, 0),
+]
+
+
+@pytest.mark.parametrize("case", O12_CASES)
+def test_o1_matches_o2_forward_and_backward(case):
+    B, Hg, Wg, H, D, M, s = case
+    q, k, v, do, tr, tc = _rand_case(30, B, Hg, Wg, H, D)
+    o1, l1 = oracle.wattn_fwd_ref(q, k, v, tr, tc, M, s)
+    o2, l2 = oracle.wattn_fwd_online(q, k, v, tr, tc, M, s, key_tile=5)
+    np.testing.assert_allclose(o1, o2, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(l1, l2, rtol=1e-12, atol=1e-12)
+    g1 = oracle.wattn_bwd_ref(q, k, v, do, tr, tc, M, s)
+    g2 = oracle.wattn_bwd_online(q, k, v, o2, l2, do, tr, tc, M, s, key_tile=7)
+    for a, b in zip(g1, g2):
+        np.testing.assert_allclose(a, b, rtol=1e-11, atol=1e-11 * max(1.0, np.abs(a).max()))
+
+
+def test_o1_matches_o2_on_tiny_workload():
+    from vision_transformer_windowed_amd.inputs import workload_inputs
+    x = workload_inputs("tiny_f32_m8", with_dout=True)
+    args = [x[n].double().numpy() for n in ("q", "k", "v")]
+    tr, tc = x["theta_row"].double().numpy(), x["theta_col"].double().numpy()
+    o1, l1 = oracle.wattn_fwd_ref(*args, tr, tc, 8, 0)
+    o2, l2 = oracle.wattn_fwd_online(*args, tr, tc, 8, 0)
+    np.testing.assert_allclose(o1, o2, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(l1, l2, rtol=1e-12, atol=1e-12)
+
+
+# ----------------------------------------------------------------------------- argument checks
+
+@pytest.mark.parametrize("shape,M,s", [
+    ((1, 8, 8, 2, 8), 3, 0),   # grid not a multiple of M
+    ((1, 8, 8, 2, 8), 4, 4),   # shift >= M
+    ((1, 8, 8, 2, 8), 4, -1),  # negative shift
+    ((1, 8, 8, 2, 6), 4, 0),   # d not a multiple of 4
+    ((1, 8, 8, 0, 8), 4, 0),   # no heads
+])
+def test_check_args_rejects(shape, M, s):
+    H, D = shape[3], shape[4]
+    with pytest.raises(ValueError):
+        oracle.check_args(shape, (H, D // 4), (H, D // 4), M, s)
+
+
+def test_empty_batch():
+    q = np.zeros((0, 8, 8, 2, 8))
+    tr = np.zeros((2, 2))
+    o, l = oracle.wattn_fwd_ref(q, q, q, tr, tr, 4, 1)
+    assert o.shape == q.shape and l.shape == q.shape[:4]
+
+
+# ----------------------------------------------------------------------------- mutation test
+
+def _mutants():
+    """Plausible mistakes planted in copies of O1's building blocks (CPU only)."""
+    import types
+
+    def make(patch):
+        m = types.SimpleNamespace()
+        ref = wattn_ref
+        saved = {n: getattr(ref, n) for n in patch}
+
+        def fwd(*a, **kw):
+            for n, f in patch.items():
+                setattr(ref, n, f)
+            try:
+                return ref.wattn_fwd_ref(*a, **kw)
+            finally:
+                for n, f in saved.items():
+                    setattr(ref, n, f)
+
+        def bwd(*a, **kw):
+            for n, f in patch.items():
+                setattr(ref, n, f)
+            try:
+                return ref.wattn_bwd_ref(*a, **kw)
+            finally:
+                for n, f in saved.items():
+                    setattr(ref, n, f)
+
+        def scores(*a, **kw):
+            for n, f in patch.items():
+                setattr(ref, n, f)
+            try:
+                return ref.window_scores_ref(*a, **kw)
+            finally:
+                for n, f in saved.items():
+                    setattr(ref, n, f)
+
+        m.fwd, m.bwd, m.scores = fwd, bwd, scores
+        return m
+
+    orig_rope = wattn_ref.rope_rotate
+    orig_roll = wattn_ref._roll
+    orig_unroll = wattn_ref._unroll
+    orig_labels = wattn_ref.region_labels
+    orig_terms = wattn_ref._dtheta_terms
+
+    def rope_flipped_sign(xw, tr, tc, M, inverse=False):
+        return orig_rope(xw, tr, tc, M, inverse=not inverse)
+
+    def rope_axes_swapped(xw, tr, tc, M, inverse=False):
+        return orig_rope(xw, tc, tr, M, inverse=inverse)
+
+    def rope_rotate_half(xw, tr, tc, M, inverse=False):
+        d = xw.shape[-1]
+        perm = []
+        for lo in (0, d // 2):
+            half = list(range(lo, lo + d // 2))
+            q4 = d // 4
+            for j in range(q4):
+                perm += [half[j], half[j + q4]]
+        perm = np.array(perm)
+        out = np.empty_like(xw)
+        out[..., perm] = orig_rope(xw[..., perm], tr, tc, M, inverse=inverse)
+        return out
+
+    def roll_wrong_direction(x, s):
+        return orig_unroll(x, s)
+
+    def unroll_wrong_direction(x, s):
+        return orig_roll(x, s)
+
+    def labels_ignore_columns(Hg, Wg, M, s):
+        lab = orig_labels(Hg, Wg, M, s)
+        return lab // 3
+
+    def terms_wrong_sign(xt, dxt, M):
+        r, c = orig_terms(xt, dxt, M)
+        return -r, -c
+
+    def terms_swapped_axes(xt, dxt, M):
+        r, c = orig_terms(xt, dxt, M)
+        return c, r
+
+    return {
+        "rotation sign flipped": make({"rope_rotate": rope_flipped_sign}),
+        "row/col axes swapped": make({"rope_rotate": rope_axes_swapped}),
+        "rotate-half pairing": make({"rope_rotate": rope_rotate_half}),
+        "shift rolled the wrong way": make({"_roll": roll_wrong_direction, "_unroll": unroll_wrong_direction}),
+        "column regions ignored": make({"region_labels": labels_ignore_columns}),
+        "dtheta sign flipped": make({"_dtheta_terms": terms_wrong_sign}),
+        "dtheta axes swapped": make({"_dtheta_terms": terms_swapped_axes}),
+    }
+
+
+def _fails(fn):
+    try:
+        fn()
+    except AssertionError:
+        return True
+    return False
+
+
+@pytest.mark.parametrize("name", list(_mutants().keys()))
+def test_pins_catch_planted_mistakes(name):
+    m = _mutants()[name]
+    caught = (
+        _fails(lambda: pin_golden(m.fwd, m.scores))
+        or _fails(lambda: pin_single_window_regions(m.fwd))
+        or _fails(lambda: pin_brute_force(m.fwd))
+        or _fails(lambda: pin_finite_differences(m.fwd, m.bwd))
+        or _fails(lambda: pin_sdpa(m.fwd, m.bwd))
+    )
+    assert caught, f"no pin failed for planted mistake: {name}"

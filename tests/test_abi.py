@@ -1,0 +1,121 @@
+"""C-ABI checks that need no GPU: the library loads, exports every declared symbol, and rejects
+invalid arguments with the documented status before any HIP call is made."""
+
+import os
+import re
+
+import pytest
+
+import vision_transformer_windowed_amd as F
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "flashswin.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(F.LIB_PATH), reason="libflashswin.so not built")
+
+FAKE = 1 << 20  # a 256-byte aligned, non-null address never dereferenced (validation fails first)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(flashswin_\w+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = F.load()
+    names = declared_functions()
+    assert set(names) == set(F.EXPORTED)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_version_and_status_strings():
+    assert F.flashswin_version() >= 100
+    for code in range(5):
+        assert F.flashswin_status_string(code).startswith("FSW_")
+    assert "unknown" in F.flashswin_status_string(99)
+
+
+def fwd(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, tr=FAKE, tc=FAKE, out=FAKE + 4096, lse=FAKE + 8192,
+             B=1, Hg=16, Wg=16, heads=2, d=32, M=8, shift=0, dtype=F.FSW_BF16)
+    a.update(kw)
+    return F.flashswin_wattn_fwd(a["q"], a["k"], a["v"], a["tr"], a["tc"], a["out"], a["lse"], a["B"], a["Hg"],
+                                 a["Wg"], a["heads"], a["d"], a["M"], a["shift"], a["dtype"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(Hg=12), F.FSW_ERR_INVALID_ARG),          # Hg not a multiple of M
+    (dict(Wg=20), F.FSW_ERR_INVALID_ARG),          # Wg not a multiple of M
+    (dict(shift=8), F.FSW_ERR_INVALID_ARG),        # shift >= M
+    (dict(shift=-1), F.FSW_ERR_INVALID_ARG),       # negative shift
+    (dict(d=6), F.FSW_ERR_INVALID_ARG),            # d not a multiple of 4
+    (dict(d=12), F.FSW_ERR_UNSUPPORTED),           # valid d without a kernel
+    (dict(d=128), F.FSW_ERR_UNSUPPORTED),
+    (dict(Hg=64, Wg=64, M=64), F.FSW_ERR_UNSUPPORTED),  # windows beyond 32 x 32
+    (dict(heads=0), F.FSW_ERR_INVALID_ARG),
+    (dict(B=-1), F.FSW_ERR_INVALID_ARG),
+    (dict(M=0), F.FSW_ERR_INVALID_ARG),
+    (dict(dtype=7), F.FSW_ERR_INVALID_ARG),
+    (dict(q=None), F.FSW_ERR_INVALID_ARG),
+    (dict(tr=None), F.FSW_ERR_INVALID_ARG),
+    (dict(out=None), F.FSW_ERR_INVALID_ARG),
+    (dict(q=FAKE + 2), F.FSW_ERR_INVALID_ARG),     # misaligned
+    (dict(out=FAKE + 8), F.FSW_ERR_INVALID_ARG),
+    (dict(tc=FAKE + 2), F.FSW_ERR_INVALID_ARG),
+    (dict(lse=FAKE + 1), F.FSW_ERR_INVALID_ARG),
+    (dict(out=FAKE), F.FSW_ERR_INVALID_ARG),       # out aliases q
+    (dict(B=1 << 40), F.FSW_ERR_UNSUPPORTED),      # index space overflow
+])
+def test_forward_rejects_before_launch(kw, status):
+    assert fwd(**kw) == status
+
+
+def test_forward_empty_batch_is_a_no_op():
+    assert fwd(B=0, q=None, k=None, v=None, out=None, lse=None, tr=None, tc=None) == F.FSW_OK
+
+
+def bwd(**kw):
+    a = dict(q=FAKE, k=FAKE + 256, v=FAKE + 512, out=FAKE + 768, dout=FAKE + 1024, lse=FAKE + 1280,
+             tr=FAKE + 1536, tc=FAKE + 1792, dq=FAKE + 2048, dk=FAKE + 2304, dv=FAKE + 2560,
+             dtr=FAKE + 2816, dtc=FAKE + 3072, ws=FAKE + 4096, wsb=None,
+             B=1, Hg=16, Wg=16, heads=2, d=32, M=8, shift=4, dtype=F.FSW_BF16)
+    a.update(kw)
+    if a["wsb"] is None:
+        a["wsb"] = F.flashswin_wattn_bwd_workspace_size(a["B"], a["Hg"], a["Wg"], a["heads"], a["d"], a["M"],
+                                                        a["shift"], a["dtype"])
+    return F.flashswin_wattn_bwd(a["q"], a["k"], a["v"], a["out"], a["dout"], a["lse"], a["tr"], a["tc"], a["dq"],
+                                 a["dk"], a["dv"], a["dtr"], a["dtc"], a["ws"], a["wsb"], a["B"], a["Hg"], a["Wg"],
+                                 a["heads"], a["d"], a["M"], a["shift"], a["dtype"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(Hg=10), F.FSW_ERR_INVALID_ARG),
+    (dict(shift=9), F.FSW_ERR_INVALID_ARG),
+    (dict(lse=None), F.FSW_ERR_INVALID_ARG),       # the backward needs the forward's LSE
+    (dict(dout=None), F.FSW_ERR_INVALID_ARG),
+    (dict(dtr=None), F.FSW_ERR_INVALID_ARG),
+    (dict(dq=FAKE + 4), F.FSW_ERR_INVALID_ARG),
+    (dict(dk=FAKE), F.FSW_ERR_INVALID_ARG),        # dk aliases q
+    (dict(dv=FAKE + 2304), F.FSW_ERR_INVALID_ARG),  # dv aliases dk
+    (dict(dtc=FAKE + 2816), F.FSW_ERR_INVALID_ARG),  # dtheta_col aliases dtheta_row
+    (dict(ws=None), F.FSW_ERR_WORKSPACE),
+    (dict(ws=FAKE + 4100), F.FSW_ERR_WORKSPACE),   # misaligned workspace
+    (dict(wsb=16), F.FSW_ERR_WORKSPACE),           # too small
+    (dict(d=12), F.FSW_ERR_UNSUPPORTED),
+])
+def test_backward_rejects_before_launch(kw, status):
+    assert bwd(**kw) == status
+
+
+def test_workspace_size():
+    ws = F.flashswin_wattn_bwd_workspace_size
+    assert ws(0, 16, 16, 2, 32, 8, 0, 1) == 0
+    assert ws(1, 12, 16, 2, 32, 8, 0, 1) == 0           # invalid shape
+    small = ws(1, 16, 16, 2, 32, 8, 0, 1)
+    big = ws(4, 16, 16, 2, 32, 8, 0, 1)
+    assert 0 < small < big
+    assert small % 256 == 0
+    # at least the per-token Delta buffer
+    assert ws(32, 128, 128, 3, 32, 32, 16, 1) >= 32 * 128 * 128 * 3 * 4

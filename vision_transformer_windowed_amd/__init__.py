@@ -1,0 +1,31 @@
+"""FlashSwin window attention for AMD MI355X (gfx950).
+
+Exact softmax attention inside M x M windows of a token grid, with Swin's
+cyclic shift and region mask and window-local 2D RoPE on Q and K, computed by
+hand-written HIP kernels behind the C ABI in include/flashswin.h.  The Python
+layer only marshals arguments (see _lib.py); torch provides device memory and
+streams.
+"""
+
+from ._lib import (  # noqa: F401
+    EXPORTED,
+    FSW_BF16,
+    FSW_ERR_HIP,
+    FSW_ERR_INVALID_ARG,
+    FSW_ERR_UNSUPPORTED,
+    FSW_ERR_WORKSPACE,
+    FSW_F32,
+    FSW_OK,
+    FlashSwinError,
+    LIB_PATH,
+    WindowAttention,
+    flashswin_status_string,
+    flashswin_version,
+    flashswin_wattn_bwd,
+    flashswin_wattn_bwd_workspace_size,
+    flashswin_wattn_fwd,
+    load,
+    wattn_bwd,
+    wattn_fwd,
+    window_attention,
+)

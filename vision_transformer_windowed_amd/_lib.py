@@ -1,0 +1,193 @@
+"""ctypes binding of libflashswin.so: argument marshalling only.
+
+Every computation happens in the HIP kernels behind the C ABI declared in
+include/flashswin.h.  This module only checks tensor properties torch knows
+about (device, dtype, contiguity, shape), allocates outputs and the backward
+workspace through torch's caching allocator, and passes raw device pointers and
+the current HIP stream.  There is no CPU fallback: if the library is missing
+or no GPU is present, calls raise.
+"""
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libflashswin.so")
+
+FSW_OK, FSW_ERR_INVALID_ARG, FSW_ERR_UNSUPPORTED, FSW_ERR_WORKSPACE, FSW_ERR_HIP = range(5)
+FSW_F32, FSW_BF16 = 0, 1
+
+EXPORTED = (
+    "flashswin_wattn_fwd",
+    "flashswin_wattn_bwd_workspace_size",
+    "flashswin_wattn_bwd",
+    "flashswin_status_string",
+    "flashswin_version",
+)
+
+_lib = None
+
+
+class FlashSwinError(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)} (status {status})")
+
+
+def load():
+    """Load the shared library (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(
+            f"{LIB_PATH} is not built; run `python -m vision_transformer_windowed_amd.build` "
+            "(or __graft_entry__.build()) first")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i64, i32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
+    lib.flashswin_wattn_fwd.restype = i32
+    lib.flashswin_wattn_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i32, i32, i32, i32, i32, vp]
+    lib.flashswin_wattn_bwd_workspace_size.restype = sz
+    lib.flashswin_wattn_bwd_workspace_size.argtypes = [i64, i64, i64, i32, i32, i32, i32, i32]
+    lib.flashswin_wattn_bwd.restype = i32
+    lib.flashswin_wattn_bwd.argtypes = [vp] * 13 + [vp, sz, i64, i64, i64, i32, i32, i32, i32, i32, vp]
+    lib.flashswin_status_string.restype = ctypes.c_char_p
+    lib.flashswin_status_string.argtypes = [i32]
+    lib.flashswin_version.restype = i32
+    lib.flashswin_version.argtypes = []
+    _lib = lib
+    return lib
+
+
+def status_string(status):
+    return load().flashswin_status_string(int(status)).decode()
+
+
+# ------------------------------------------------------------------ raw C-ABI calls (same names)
+
+def flashswin_wattn_fwd(q, k, v, theta_row, theta_col, out, lse, B, Hg, Wg, heads, d, M, shift, dtype, stream):
+    """Raw call: pointers are ints (device addresses) or None; returns the status code."""
+    return load().flashswin_wattn_fwd(q, k, v, theta_row, theta_col, out, lse, B, Hg, Wg, heads, d, M, shift,
+                                      dtype, stream)
+
+
+def flashswin_wattn_bwd_workspace_size(B, Hg, Wg, heads, d, M, shift, dtype):
+    return load().flashswin_wattn_bwd_workspace_size(B, Hg, Wg, heads, d, M, shift, dtype)
+
+
+def flashswin_wattn_bwd(q, k, v, out, dout, lse, theta_row, theta_col, dq, dk, dv, dtheta_row, dtheta_col,
+                        workspace, workspace_bytes, B, Hg, Wg, heads, d, M, shift, dtype, stream):
+    return load().flashswin_wattn_bwd(q, k, v, out, dout, lse, theta_row, theta_col, dq, dk, dv, dtheta_row,
+                                      dtheta_col, workspace, workspace_bytes, B, Hg, Wg, heads, d, M, shift, dtype,
+                                      stream)
+
+
+def flashswin_status_string(status):
+    return status_string(status)
+
+
+def flashswin_version():
+    return load().flashswin_version()
+
+
+# ------------------------------------------------------------------ torch-tensor helpers
+
+def _dtype_code(t):
+    if t.dtype == torch.bfloat16:
+        return FSW_BF16
+    if t.dtype == torch.float32:
+        return FSW_F32
+    raise TypeError(f"unsupported dtype {t.dtype}; use torch.bfloat16 or torch.float32")
+
+
+def _check_grid(name, t, shape, dtype):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(device):
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def wattn_fwd(q, k, v, theta_row, theta_col, M, shift=0, out=None, lse=None, need_lse=True):
+    """Forward window attention on the GPU.  Returns (out, lse); lse is None when need_lse=False."""
+    if q.dim() != 5:
+        raise ValueError("q must be [B, Hg, Wg, heads, d]")
+    B, Hg, Wg, H, D = q.shape
+    code = _dtype_code(q)
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check_grid(name, t, q.shape, q.dtype)
+    for name, t in (("theta_row", theta_row), ("theta_col", theta_col)):
+        _check_grid(name, t, (H, D // 4), torch.float32)
+    if out is None:
+        out = torch.empty_like(q)
+    _check_grid("out", out, q.shape, q.dtype)
+    if need_lse:
+        if lse is None:
+            lse = torch.empty((B, Hg, Wg, H), device=q.device, dtype=torch.float32)
+        _check_grid("lse", lse, (B, Hg, Wg, H), torch.float32)
+    else:
+        lse = None
+    st = flashswin_wattn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(theta_row), _ptr(theta_col), _ptr(out), _ptr(lse),
+                             B, Hg, Wg, H, D, int(M), int(shift), code, _stream(q.device))
+    if st != FSW_OK:
+        raise FlashSwinError(st, "flashswin_wattn_fwd")
+    return out, lse
+
+
+def wattn_bwd(q, k, v, out, dout, lse, theta_row, theta_col, M, shift=0, workspace=None):
+    """Backward on the GPU.  Returns (dq, dk, dv, dtheta_row, dtheta_col)."""
+    B, Hg, Wg, H, D = q.shape
+    code = _dtype_code(q)
+    for name, t in (("q", q), ("k", k), ("v", v), ("out", out), ("dout", dout)):
+        _check_grid(name, t, q.shape, q.dtype)
+    _check_grid("lse", lse, (B, Hg, Wg, H), torch.float32)
+    for name, t in (("theta_row", theta_row), ("theta_col", theta_col)):
+        _check_grid(name, t, (H, D // 4), torch.float32)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    dtr = torch.empty_like(theta_row)
+    dtc = torch.empty_like(theta_col)
+    nbytes = flashswin_wattn_bwd_workspace_size(B, Hg, Wg, H, D, int(M), int(shift), code)
+    if workspace is None or workspace.numel() < nbytes:
+        workspace = torch.empty(max(nbytes, 1), device=q.device, dtype=torch.uint8)
+    st = flashswin_wattn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _ptr(lse), _ptr(theta_row),
+                             _ptr(theta_col), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dtr), _ptr(dtc),
+                             _ptr(workspace), workspace.numel(), B, Hg, Wg, H, D, int(M), int(shift), code,
+                             _stream(q.device))
+    if st != FSW_OK:
+        raise FlashSwinError(st, "flashswin_wattn_bwd")
+    return dq, dk, dv, dtr, dtc
+
+
+class WindowAttention(torch.autograd.Function):
+    """Autograd wrapper: forward saves LSE, backward recomputes P (no score matrix is stored)."""
+
+    @staticmethod
+    def forward(ctx, q, k, v, theta_row, theta_col, M, shift):
+        out, lse = wattn_fwd(q, k, v, theta_row, theta_col, M, shift)
+        ctx.save_for_backward(q, k, v, out, lse, theta_row, theta_col)
+        ctx.M, ctx.shift = M, shift
+        return out
+
+    @staticmethod
+    def backward(ctx, dout):
+        q, k, v, out, lse, tr, tc = ctx.saved_tensors
+        dq, dk, dv, dtr, dtc = wattn_bwd(q, k, v, out, dout.contiguous(), lse, tr, tc, ctx.M, ctx.shift)
+        return dq, dk, dv, dtr, dtc, None, None
+
+
+def window_attention(q, k, v, theta_row, theta_col, M, shift=0):
+    """Differentiable windowed attention with window-local 2D RoPE; q/k/v [B, Hg, Wg, heads, d]."""
+    return WindowAttention.apply(q, k, v, theta_row, theta_col, M, shift)

@@ -1,0 +1,142 @@
+// C ABI of the window-attention library: argument validation, workspace sizing, dispatch.
+//
+// Every check runs on the host before any HIP call, so an invalid call never touches the device.
+// Dispatch: bf16 with d == 32 and M <= 32 goes to the MFMA kernels; everything else (float32
+// tensors, other d) goes to the float32-arithmetic kernels.
+#include <algorithm>
+
+#include "../../include/flashswin.h"
+#include "fsw_launch.h"
+
+namespace {
+
+constexpr int kMaxM = 32;
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+bool supported_d(int d) { return d == 8 || d == 16 || d == 32 || d == 64; }
+
+// Shape rules shared by forward, backward and workspace sizing.  Fills g on success.
+int check_shape(int64_t B, int64_t Hg, int64_t Wg, int heads, int d, int M, int shift, int dtype, fsw::Geom* g) {
+  if (B < 0 || Hg < 1 || Wg < 1 || heads < 1 || M < 1 || d < 1) return FSW_ERR_INVALID_ARG;
+  if (Hg % M != 0 || Wg % M != 0) return FSW_ERR_INVALID_ARG;
+  if (shift < 0 || shift >= M) return FSW_ERR_INVALID_ARG;
+  if (d % 4 != 0) return FSW_ERR_INVALID_ARG;
+  if (dtype != FSW_F32 && dtype != FSW_BF16) return FSW_ERR_INVALID_ARG;
+  if (!supported_d(d) || M > kMaxM) return FSW_ERR_UNSUPPORTED;
+  // int32 grid coordinates and int64 element offsets: keep every product well inside int64,
+  // and the flat 1-D launch grid inside 2^31 workgroups.
+  const int64_t lim = (int64_t)1 << 30;
+  if (Hg > lim || Wg > lim || heads > (1 << 20)) return FSW_ERR_UNSUPPORTED;
+  const long double elems = (long double)B * Hg * Wg * heads * d;
+  if (elems > (long double)((int64_t)1 << 56)) return FSW_ERR_UNSUPPORTED;
+  const long double wgs = (long double)B * (Hg / M) * (Wg / M) * heads * 8;
+  if (wgs > (long double)((int64_t)1 << 31) - 1) return FSW_ERR_UNSUPPORTED;
+  g->B = B;
+  g->Hg = (int)Hg;
+  g->Wg = (int)Wg;
+  g->heads = heads;
+  g->d = d;
+  g->M = M;
+  g->shift = shift;
+  g->nH = (int)(Hg / M);
+  g->nW = (int)(Wg / M);
+  g->N = M * M;
+  return FSW_OK;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+struct WsLayout {
+  size_t delta_off, partials_off, total;
+  int64_t n_partials;
+};
+
+WsLayout workspace_layout(const fsw::Geom& g, bool mfma) {
+  WsLayout w;
+  const int64_t rows = g.B * g.Hg * g.Wg * g.heads;
+  w.delta_off = 0;
+  w.partials_off = align256((size_t)rows * sizeof(float));
+  w.n_partials = mfma ? fsw::bwd_mfma_partials(g) : fsw::bwd_scalar_partials(g);
+  w.total = w.partials_off + align256((size_t)w.n_partials * (g.d / 2) * sizeof(float));
+  return w;
+}
+
+bool use_mfma(const fsw::Geom& g, int dtype) { return fsw::kHaveMfma && dtype == FSW_BF16 && g.d == 32 && g.M <= kMaxM; }
+
+}  // namespace
+
+extern "C" {
+
+int flashswin_version(void) { return 100; }
+
+const char* flashswin_status_string(int status) {
+  switch (status) {
+    case FSW_OK: return "FSW_OK";
+    case FSW_ERR_INVALID_ARG: return "FSW_ERR_INVALID_ARG: invalid shape, pointer, alignment, shift or dtype";
+    case FSW_ERR_UNSUPPORTED: return "FSW_ERR_UNSUPPORTED: valid arguments this library does not implement";
+    case FSW_ERR_WORKSPACE: return "FSW_ERR_WORKSPACE: workspace missing or too small";
+    case FSW_ERR_HIP: return "FSW_ERR_HIP: a HIP kernel launch failed";
+    default: return "unknown flashswin status";
+  }
+}
+
+int flashswin_wattn_fwd(const void* q, const void* k, const void* v, const float* theta_row, const float* theta_col,
+                        void* out, float* lse, int64_t B, int64_t Hg, int64_t Wg, int heads, int d, int M, int shift,
+                        int dtype, void* hip_stream) {
+  fsw::Geom g;
+  int st = check_shape(B, Hg, Wg, heads, d, M, shift, dtype, &g);
+  if (st != FSW_OK) return st;
+  if (B == 0) return FSW_OK;
+  if (!q || !k || !v || !out || !theta_row || !theta_col) return FSW_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16)) return FSW_ERR_INVALID_ARG;
+  if (!aligned(theta_row, 4) || !aligned(theta_col, 4) || (lse && !aligned(lse, 4))) return FSW_ERR_INVALID_ARG;
+  if (out == q || out == k || out == v) return FSW_ERR_INVALID_ARG;
+  fsw::FwdArgs a{q, k, v, theta_row, theta_col, out, lse, g, dtype};
+  hipStream_t s = reinterpret_cast<hipStream_t>(hip_stream);
+  const hipError_t e = use_mfma(g, dtype) ? fsw::launch_fwd_mfma(a, s) : fsw::launch_fwd_scalar(a, s);
+  return e == hipSuccess ? FSW_OK : FSW_ERR_HIP;
+}
+
+size_t flashswin_wattn_bwd_workspace_size(int64_t B, int64_t Hg, int64_t Wg, int heads, int d, int M, int shift,
+                                          int dtype) {
+  fsw::Geom g;
+  if (check_shape(B, Hg, Wg, heads, d, M, shift, dtype, &g) != FSW_OK) return 0;
+  if (B == 0) return 0;
+  return workspace_layout(g, use_mfma(g, dtype)).total;
+}
+
+int flashswin_wattn_bwd(const void* q, const void* k, const void* v, const void* out, const void* dout,
+                        const float* lse, const float* theta_row, const float* theta_col, void* dq, void* dk, void* dv,
+                        float* dtheta_row, float* dtheta_col, void* workspace, size_t workspace_bytes, int64_t B,
+                        int64_t Hg, int64_t Wg, int heads, int d, int M, int shift, int dtype, void* hip_stream) {
+  fsw::Geom g;
+  int st = check_shape(B, Hg, Wg, heads, d, M, shift, dtype, &g);
+  if (st != FSW_OK) return st;
+  if (B == 0) return FSW_OK;
+  const void* ptrs16[] = {q, k, v, out, dout, dq, dk, dv};
+  for (const void* p : ptrs16)
+    if (!p || !aligned(p, 16)) return FSW_ERR_INVALID_ARG;
+  const void* ptrs4[] = {lse, theta_row, theta_col, dtheta_row, dtheta_col};
+  for (const void* p : ptrs4)
+    if (!p || !aligned(p, 4)) return FSW_ERR_INVALID_ARG;
+  const void* outs[] = {dq, dk, dv};
+  const void* ins[] = {q, k, v, out, dout};
+  for (const void* o : outs)
+    for (const void* i : ins)
+      if (o == i) return FSW_ERR_INVALID_ARG;
+  if (dq == dk || dq == dv || dk == dv || dtheta_row == dtheta_col) return FSW_ERR_INVALID_ARG;
+  const bool mfma = use_mfma(g, dtype);
+  const WsLayout ws = workspace_layout(g, mfma);
+  if (!workspace || !aligned(workspace, 256) || workspace_bytes < ws.total) return FSW_ERR_WORKSPACE;
+  char* base = static_cast<char*>(workspace);
+  fsw::BwdArgs a{q,  k,  v,          out,        dout, lse, theta_row, theta_col,
+                 dq, dk, dv,         dtheta_row, dtheta_col, g, dtype,
+                 reinterpret_cast<float*>(base + ws.delta_off), reinterpret_cast<float*>(base + ws.partials_off),
+                 ws.n_partials};
+  hipStream_t s = reinterpret_cast<hipStream_t>(hip_stream);
+  const hipError_t e = mfma ? fsw::launch_bwd_mfma(a, s) : fsw::launch_bwd_scalar(a, s);
+  return e == hipSuccess ? FSW_OK : FSW_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,231 @@
+#!/usr/bin/env python3
+"""Benchmark: FlashSwin window attention, one training-step pass (forward + backward) on one GPU.
+
+Workload (default): FlashSwin-T stage 1 with p=2, M=32: q/k/v/dO [128, 128, 128, 3, 32] bf16,
+no shift, seeded synthetic N(0,1) inputs (no dataset), RoPE theta from the geometric schedule plus
+N(0, 0.01^2) noise.  One step = the whole hot path over the batch: the forward (RoPE, online-softmax
+attention, LSE) then the backward (Delta, recomputed P, dQ/dK/dV, dtheta).  FLOPs per window-head:
+4 N^2 d forward + 10 N^2 d backward (N = M^2), the dense convention of the workload's metric.
+
+Prints ONE JSON line.  `roofline` describes the dominant kernel launch (the longer of the forward
+and backward calls), timed with HIP events on the stream the library launches on.  `traffic` is
+taken from the committed rocprofv3 counter summary in profiles/ when that summary was measured on
+the current kernel source (sha256 match), else null.  `cpu_baseline` times the fp64 CPU oracle on
+a bounded sample of the same workload (rank 0, N=1 only).
+
+Modes for profiling runs: --only fwd|bwd runs just that call per step; --copy-calibration runs a
+plain device-to-device copy of a known size (for scaling HBM counters).
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
+KERNEL_SOURCES = ["fwd_mfma.hip", "bwd_mfma.hip", "fwd_scalar.hip", "bwd_scalar.hip", "fsw_common.h",
+                  "fsw_mfma.h", "fsw_api.hip"]
+
+
+def kernel_source_sha():
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        p = os.path.join(ROOT, "vision_transformer_windowed_amd", "csrc", f)
+        if os.path.exists(p):
+            h.update(f.encode())
+            h.update(open(p, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(kernel_tag, workload, sha):
+    """HBM bytes per launch from profiles/traffic_<kernel_tag>_<workload>.md if its sha matches."""
+    p = os.path.join(ROOT, "profiles", f"traffic_{kernel_tag}_{workload}.md")
+    if not os.path.exists(p):
+        return None
+    text = open(p).read()
+    m_sha = re.search(r"kernel_source_sha:\s*([0-9a-f]+)", text)
+    m_rd = re.search(r"hbm_read_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    m_wr = re.search(r"hbm_write_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not (m_sha and m_rd and m_wr) or m_sha.group(1) != sha:
+        return None
+    return float(m_rd.group(1)) + float(m_wr.group(1))
+
+
+def cpu_baseline(x, w, shift, images, gpu_out=None):
+    """Time the fp64 oracle (forward + backward) on the first `images` images of the batch."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        cores = len(os.sched_getaffinity(0))
+    sl = slice(0, images)
+    args = [x[n][sl].double().numpy() for n in ("q", "k", "v")]
+    dout = x["dout"][sl].double().numpy()
+    tr, tc = x["theta_row"].double().numpy(), x["theta_col"].double().numpy()
+    t0 = time.perf_counter()
+    ro, rl = oracle.wattn_fwd_ref(*args, tr, tc, w["M"], shift)
+    g = oracle.wattn_bwd_ref(*args, dout, tr, tc, w["M"], shift)
+    dt = time.perf_counter() - t0
+    N = w["M"] ** 2
+    nwh = images * (w["Hg"] // w["M"]) * (w["Wg"] // w["M"]) * w["heads"]
+    flops = 14.0 * N * N * w["d"] * nwh
+    res = {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+           "sample": f"first {images} of {w['B']} images (forward + backward, fp64 NumPy), {dt:.1f} s wall"}
+    parity = None
+    if gpu_out is not None:
+        parity = {}
+        for name, ref, got in (("O", ro, gpu_out["out"]), ("LSE", rl, gpu_out["lse"]), ("dQ", g[0], gpu_out["dq"]),
+                               ("dK", g[1], gpu_out["dk"]), ("dV", g[2], gpu_out["dv"])):
+            got = got[sl].double().cpu().numpy()
+            parity[name] = {"max_abs": float(np.abs(got - ref).max()),
+                            "rel_l2": float(np.linalg.norm(got - ref) / np.linalg.norm(ref))}
+    return res, parity
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="flashswin_t_s1_p2_m32")
+    ap.add_argument("--shift", type=int, default=None)
+    ap.add_argument("--only", choices=["step", "fwd", "bwd"], default="step")
+    ap.add_argument("--cpu-images", type=int, default=4)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(the batch would shard across GPUs with one dtheta all-reduce; see DESIGN.md).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import vision_transformer_windowed_amd as F
+    from vision_transformer_windowed_amd.inputs import WORKLOADS, workload_inputs
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+
+    if args.copy_calibration:
+        n = 1 << 30  # 1 GiB
+        a = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        b = torch.empty_like(a)
+        for _ in range(args.warmup + args.steps):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n, "launches": args.warmup + args.steps + 1}))
+        return
+
+    w = WORKLOADS[args.workload]
+    shift = w["shifts"][0] if args.shift is None else args.shift
+    M = w["M"]
+    t_gen = time.perf_counter()
+    x = workload_inputs(args.workload, with_dout=True)
+    xd = {k: v.to(dev) for k, v in x.items()}
+    gen_s = time.perf_counter() - t_gen
+    q, k, v, dout = xd["q"], xd["k"], xd["v"], xd["dout"]
+    tr, tc = xd["theta_row"], xd["theta_col"]
+    out = torch.empty_like(q)
+    lse = torch.empty(q.shape[:4], device=dev, dtype=torch.float32)
+    grads = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v), torch.empty_like(tr),
+             torch.empty_like(tc))
+    ws = torch.empty(max(F.bwd_workspace_bytes(q, M, shift), 1), device=dev, dtype=torch.uint8)
+
+    def fwd():
+        F.wattn_fwd(q, k, v, tr, tc, M, shift, out=out, lse=lse)
+
+    def bwd():
+        F.wattn_bwd(q, k, v, out, dout, lse, tr, tc, M, shift, workspace=ws, grads=grads)
+
+    fwd()  # the backward needs a valid LSE even in --only bwd mode
+    for _ in range(args.warmup):
+        if args.only in ("step", "fwd"):
+            fwd()
+        if args.only in ("step", "bwd"):
+            bwd()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        ev[i][0].record(stream)
+        if args.only in ("step", "fwd"):
+            fwd()
+        ev[i][1].record(stream)
+        if args.only in ("step", "bwd"):
+            bwd()
+        ev[i][2].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    fwd_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / K
+    bwd_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / K
+
+    N = M * M
+    nwh = w["B"] * (w["Hg"] // M) * (w["Wg"] // M) * w["heads"]
+    fwd_flops = 4.0 * N * N * w["d"] * nwh
+    bwd_flops = 10.0 * N * N * w["d"] * nwh
+    step_flops = (fwd_flops if args.only != "bwd" else 0) + (bwd_flops if args.only != "fwd" else 0)
+    ms_per_step = wall / K * 1e3
+    value = step_flops / (ms_per_step * 1e-3) / 1e12
+
+    sha = kernel_source_sha()
+    if fwd_ms >= bwd_ms:
+        dom, dom_ms, dom_flops = "wattn_fwd", fwd_ms, fwd_flops
+    else:
+        dom, dom_ms, dom_flops = "wattn_bwd", bwd_ms, bwd_flops
+    achieved = dom_flops / (dom_ms * 1e-3) / 1e12
+    traffic = read_traffic(dom, args.workload, sha)
+    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / BF16_MFMA_PEAK_TFLOPS, 4), "traffic": traffic, "kernel": dom,
+                "launch_ms": round(dom_ms, 4), "kernel_source_sha": sha}
+
+    gpu_out = {"out": out, "lse": lse, "dq": grads[0], "dk": grads[1], "dv": grads[2]}
+    cpu, parity = (None, None)
+    if not args.no_cpu_baseline and args.only == "step":
+        cpu, parity = cpu_baseline(x, w, shift, args.cpu_images, gpu_out)
+
+    line = {
+        "metric": "window-attn TFLOP/s + % MFMA/HBM roofline, FlashSwin-T stage-1 p=2 M=32",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w["dtype"] == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "B": w["B"], "grid": [w["Hg"], w["Wg"]], "heads": w["heads"],
+                   "d": w["d"], "M": M, "shift": shift, "pass": args.only,
+                   "flops_per_step": step_flops},
+        "fwd_ms": round(fwd_ms, 4),
+        "bwd_ms": round(bwd_ms, 4),
+        "fwd_tflops": round(fwd_flops / (fwd_ms * 1e-3) / 1e12, 2) if args.only != "bwd" else None,
+        "bwd_tflops": round(bwd_flops / (bwd_ms * 1e-3) / 1e12, 2) if args.only != "fwd" else None,
+        "window_heads_per_s": round(nwh / (ms_per_step * 1e-3), 1),
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "parity_sample": parity,
+        "input_gen_s": round(gen_s, 1),
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -19,6 +19,7 @@ from ._lib import (  # noqa: F401
     FlashSwinError,
     LIB_PATH,
     WindowAttention,
+    bwd_workspace_bytes,
     flashswin_status_string,
     flashswin_version,
     flashswin_wattn_bwd,

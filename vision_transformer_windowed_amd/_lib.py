@@ -88,6 +88,11 @@ def flashswin_status_string(status):
     return status_string(status)
 
 
+def bwd_workspace_bytes(q, M, shift=0):
+    B, Hg, Wg, H, D = q.shape
+    return flashswin_wattn_bwd_workspace_size(B, Hg, Wg, H, D, int(M), int(shift), _dtype_code(q))
+
+
 def flashswin_version():
     return load().flashswin_version()
 
@@ -147,8 +152,11 @@ def wattn_fwd(q, k, v, theta_row, theta_col, M, shift=0, out=None, lse=None, nee
     return out, lse
 
 
-def wattn_bwd(q, k, v, out, dout, lse, theta_row, theta_col, M, shift=0, workspace=None):
-    """Backward on the GPU.  Returns (dq, dk, dv, dtheta_row, dtheta_col)."""
+def wattn_bwd(q, k, v, out, dout, lse, theta_row, theta_col, M, shift=0, workspace=None, grads=None):
+    """Backward on the GPU.  Returns (dq, dk, dv, dtheta_row, dtheta_col).
+
+    `grads` may hold preallocated (dq, dk, dv, dtheta_row, dtheta_col) to write into.
+    """
     B, Hg, Wg, H, D = q.shape
     code = _dtype_code(q)
     for name, t in (("q", q), ("k", k), ("v", v), ("out", out), ("dout", dout)):
@@ -156,9 +164,16 @@ def wattn_bwd(q, k, v, out, dout, lse, theta_row, theta_col, M, shift=0, workspa
     _check_grid("lse", lse, (B, Hg, Wg, H), torch.float32)
     for name, t in (("theta_row", theta_row), ("theta_col", theta_col)):
         _check_grid(name, t, (H, D // 4), torch.float32)
-    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    dtr = torch.empty_like(theta_row)
-    dtc = torch.empty_like(theta_col)
+    if grads is None:
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        dtr = torch.empty_like(theta_row)
+        dtc = torch.empty_like(theta_col)
+    else:
+        dq, dk, dv, dtr, dtc = grads
+        for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+            _check_grid(name, t, q.shape, q.dtype)
+        for name, t in (("dtheta_row", dtr), ("dtheta_col", dtc)):
+            _check_grid(name, t, (H, D // 4), torch.float32)
     nbytes = flashswin_wattn_bwd_workspace_size(B, Hg, Wg, H, D, int(M), int(shift), code)
     if workspace is None or workspace.numel() < nbytes:
         workspace = torch.empty(max(nbytes, 1), device=q.device, dtype=torch.uint8)

@@ -62,7 +62,8 @@ WsLayout workspace_layout(const fsw::Geom& g, bool mfma) {
   return w;
 }
 
-bool use_mfma(const fsw::Geom& g, int dtype) { return fsw::kHaveMfma && dtype == FSW_BF16 && g.d == 32 && g.M <= kMaxM; }
+bool use_mfma_fwd(const fsw::Geom& g, int dtype) { return dtype == FSW_BF16 && g.d == 32 && g.M <= kMaxM; }
+bool use_mfma(const fsw::Geom& g, int dtype) { return fsw::kHaveMfmaBwd && use_mfma_fwd(g, dtype); }
 
 }  // namespace
 
@@ -94,7 +95,7 @@ int flashswin_wattn_fwd(const void* q, const void* k, const void* v, const float
   if (out == q || out == k || out == v) return FSW_ERR_INVALID_ARG;
   fsw::FwdArgs a{q, k, v, theta_row, theta_col, out, lse, g, dtype};
   hipStream_t s = reinterpret_cast<hipStream_t>(hip_stream);
-  const hipError_t e = use_mfma(g, dtype) ? fsw::launch_fwd_mfma(a, s) : fsw::launch_fwd_scalar(a, s);
+  const hipError_t e = use_mfma_fwd(g, dtype) ? fsw::launch_fwd_mfma(a, s) : fsw::launch_fwd_scalar(a, s);
   return e == hipSuccess ? FSW_OK : FSW_ERR_HIP;
 }
 

@@ -50,8 +50,8 @@ hipError_t launch_bwd_scalar(const BwdArgs& a, hipStream_t st);
 int64_t bwd_scalar_partials(const Geom& g);
 
 // bf16 MFMA paths (d == 32, M <= 32).
-constexpr bool kHaveMfma = false;
-inline hipError_t launch_fwd_mfma(const FwdArgs&, hipStream_t) { return hipErrorNotSupported; }
+hipError_t launch_fwd_mfma(const FwdArgs& a, hipStream_t st);
+constexpr bool kHaveMfmaBwd = false;
 inline hipError_t launch_bwd_mfma(const BwdArgs&, hipStream_t) { return hipErrorNotSupported; }
 inline int64_t bwd_mfma_partials(const Geom&) { return 0; }
 

@@ -1,0 +1,66 @@
+// MFMA helpers for gfx950 (CDNA4): bf16 32x32x16 tiles, operand layouts, LDS layout of a window.
+//
+// v_mfma_f32_32x32x16_bf16, D[32x32] += A[32x16] * B[16x32], wave64.  Lane l (h = l / 32):
+//   A: row l % 32, k = 8h .. 8h+7            (8 bf16 per lane)
+//   B: col l % 32, k = 8h .. 8h+7            (8 bf16 per lane)
+//   D: col l % 32, value v (0..15) at row 8*(v/4) + 4h + (v%4)
+// The attention tiles are transposed (S^T = K~ Q^T, O^T = V^T P^T) so that a lane owns one query:
+// its 16 score values all belong to query l % 32, and its O^T values are that query's channels.
+// A lane's 16 scores cover keys 8g + 4h + j (g, j in 0..3) of a 32-key block; the P.V product
+// takes them as B operands of two MFMAs (keys with g in {0,1}, then {2,3}), which fixes the order
+// in which V^T must present the keys: within each 16-key group, positions 4..7 and 8..11 swap.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fsw {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ f32x16_t mfma32x32x16(const bf16x8_t& a, const bf16x8_t& b, const f32x16_t& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Storage position of key w (0..15 within its 16-key group) in the V^T rows.
+__device__ __forceinline__ int vt_pos(int key) {
+  const int w = key & 15;
+  const int sw = ((w >> 2) == 1 || (w >> 2) == 2) ? (w ^ 12) : w;  // swap quads 1 and 2
+  return (key & ~15) | sw;
+}
+
+// LDS layout of one staged window-head (bf16 d = 32):
+//   K~ rows: NP keys x 40 bf16 (32 channels + 16 bytes pad: conflict-free 16-byte row reads)
+//   V^T rows: 32 channels x (NP + 8) bf16 (keys in vt_pos order, 16 bytes pad)
+constexpr int kKStride = 40;
+__host__ __device__ constexpr int vt_stride(int np) { return np + 8; }
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8_t, u); }
+
+__device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+  bf16x2_t v;
+  v[0] = (__bf16)lo;
+  v[1] = (__bf16)hi;
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// sum of a packed bf16 pair added to acc in float32 (v_dot2 with (1, 1))
+__device__ __forceinline__ float add_pair(uint32_t pair, float acc) {
+  const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pair), ones, acc, false);
+}
+
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, 64));
+  return x;
+}
+__device__ __forceinline__ uint32_t wave_or(uint32_t x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x |= (uint32_t)__shfl_xor((int)x, o, 64);
+  return x;
+}
+
+}  // namespace fsw

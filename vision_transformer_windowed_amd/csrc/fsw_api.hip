@@ -48,15 +48,17 @@ int check_shape(int64_t B, int64_t Hg, int64_t Wg, int heads, int d, int M, int 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct WsLayout {
-  size_t delta_off, partials_off, total;
+  size_t delta_off, scal_off, partials_off, total;
   int64_t n_partials;
 };
 
 WsLayout workspace_layout(const fsw::Geom& g, bool mfma) {
   WsLayout w;
   const int64_t rows = g.B * g.Hg * g.Wg * g.heads;
+  const int64_t nwh = g.B * g.nH * g.nW * g.heads;
   w.delta_off = 0;
-  w.partials_off = align256((size_t)rows * sizeof(float));
+  w.scal_off = align256((size_t)rows * sizeof(float));
+  w.partials_off = w.scal_off + align256((size_t)nwh * 2 * sizeof(float));
   w.n_partials = mfma ? fsw::bwd_mfma_partials(g) : fsw::bwd_scalar_partials(g);
   w.total = w.partials_off + align256((size_t)w.n_partials * (g.d / 2) * sizeof(float));
   return w;
@@ -133,8 +135,8 @@ int flashswin_wattn_bwd(const void* q, const void* k, const void* v, const void*
   char* base = static_cast<char*>(workspace);
   fsw::BwdArgs a{q,  k,  v,          out,        dout, lse, theta_row, theta_col,
                  dq, dk, dv,         dtheta_row, dtheta_col, g, dtype,
-                 reinterpret_cast<float*>(base + ws.delta_off), reinterpret_cast<float*>(base + ws.partials_off),
-                 ws.n_partials};
+                 reinterpret_cast<float*>(base + ws.delta_off), reinterpret_cast<float*>(base + ws.scal_off),
+                 reinterpret_cast<float*>(base + ws.partials_off), ws.n_partials};
   hipStream_t s = reinterpret_cast<hipStream_t>(hip_stream);
   const hipError_t e = mfma ? fsw::launch_bwd_mfma(a, s) : fsw::launch_bwd_scalar(a, s);
   return e == hipSuccess ? FSW_OK : FSW_ERR_HIP;

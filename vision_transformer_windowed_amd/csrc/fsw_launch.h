@@ -39,6 +39,7 @@ struct BwdArgs {
   int dtype;
   // workspace carve-up (device pointers inside the caller's workspace)
   float* delta;     // [B*Hg*Wg*heads]  rowsum(dO * O)
+  float* scal;      // [windows*heads][2]  max |dO|, max |v| per window-head (MFMA path)
   float* partials;  // [n_partials][2][d/4]  per-workgroup dtheta partial sums
   int64_t n_partials;
 };
@@ -51,9 +52,11 @@ int64_t bwd_scalar_partials(const Geom& g);
 
 // bf16 MFMA paths (d == 32, M <= 32).
 hipError_t launch_fwd_mfma(const FwdArgs& a, hipStream_t st);
-constexpr bool kHaveMfmaBwd = false;
-inline hipError_t launch_bwd_mfma(const BwdArgs&, hipStream_t) { return hipErrorNotSupported; }
-inline int64_t bwd_mfma_partials(const Geom&) { return 0; }
+hipError_t launch_bwd_mfma(const BwdArgs& a, hipStream_t st);
+int64_t bwd_mfma_partials(const Geom& g);
+constexpr bool kHaveMfmaBwd = true;
+// Delta = rowsum(dO * O) (bf16, d == 32) into a.delta.
+hipError_t launch_bwd_delta(const BwdArgs& a, hipStream_t st);
 
 // Deterministic fixed-order reduction of dtheta partials into dth_row / dth_col.
 hipError_t launch_dtheta_reduce(const float* partials, int64_t n_partials, int64_t partials_per_head_stride,

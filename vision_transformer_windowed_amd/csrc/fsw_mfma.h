@@ -20,8 +20,49 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+
 __device__ __forceinline__ f32x16_t mfma32x32x16(const bf16x8_t& a, const bf16x8_t& b, const f32x16_t& c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Score products S = q^ . k~ take operands that are computed in float32 (rotation, scaling), so
+// they are rounded to fp16 (11-bit significand) when every operand is in fp16 range, else to bf16.
+// Raw operand bits travel as uint4; H16 selects the format and the MFMA.
+template <bool H16>
+__device__ __forceinline__ f32x16_t mfma_op(uint4 a, uint4 b, const f32x16_t& c) {
+  if constexpr (H16)
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, a), __builtin_bit_cast(f16x8_t, b), c,
+                                                  0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b),
+                                                   c, 0, 0, 0);
+}
+
+// Largest operand magnitude accepted for the fp16 score products (fp16 max is 65504).
+constexpr float kF16Limit = 16384.f;
+
+__device__ __forceinline__ uint32_t pack2h(float lo, float hi) {
+  f16x2_t v;
+  v[0] = (_Float16)lo;
+  v[1] = (_Float16)hi;
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// Pack 8 floats into 8 fp16 (h16) or bf16 values.
+__device__ __forceinline__ uint4 pack8_op(const float (&x)[8], bool h16) {
+  if (h16) return make_uint4(pack2h(x[0], x[1]), pack2h(x[2], x[3]), pack2h(x[4], x[5]), pack2h(x[6], x[7]));
+  typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+  uint32_t w[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    b2 v;
+    v[0] = (__bf16)x[2 * e];
+    v[1] = (__bf16)x[2 * e + 1];
+    w[e] = __builtin_bit_cast(uint32_t, v);
+  }
+  return make_uint4(w[0], w[1], w[2], w[3]);
 }
 
 // Storage position of key w (0..15 within its 16-key group) in the V^T rows.
@@ -61,6 +102,41 @@ __device__ __forceinline__ uint32_t wave_or(uint32_t x) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) x |= (uint32_t)__shfl_xor((int)x, o, 64);
   return x;
+}
+
+// Rotate 8 consecutive channels (4 pairs) with the LDS sin/cos table; pairs j0..j0+3 of `axis`.
+__device__ __forceinline__ void rotate8(float (&x)[8], const float* sn, const float* cs, int axis, int M, int p,
+                                        int j0) {
+  const float* s = sn + (axis * M + p) * 8 + j0;
+  const float* c = cs + (axis * M + p) * 8 + j0;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const float a = x[2 * u], b = x[2 * u + 1];
+    x[2 * u] = a * c[u] - b * s[u];
+    x[2 * u + 1] = a * s[u] + b * c[u];
+  }
+}
+
+__device__ __forceinline__ void unpack8(uint4 t, float (&x)[8]) {
+  const uint32_t w[4] = {t.x, t.y, t.z, t.w};
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    x[2 * e] = __uint_as_float(w[e] << 16);
+    x[2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
+  }
+}
+
+// Per-element live mask for the lane's 16 scores in key block kb: keys kb*32 + 8g + 4h + j.
+__device__ __forceinline__ uint32_t live_bits(const uint8_t* lab, int kb, int h, int qlab) {
+  uint32_t bits = 0;
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    const uint32_t w = *reinterpret_cast<const uint32_t*>(lab + kb * 32 + 8 * g + 4 * h);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (((w >> (8 * j)) & 0xff) == (uint32_t)qlab) bits |= 1u << (4 * g + j);
+  }
+  return bits;
 }
 
 }  // namespace fsw

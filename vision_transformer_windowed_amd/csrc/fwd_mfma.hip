@@ -37,7 +37,7 @@ struct FwdSmem {
   float* cs;       // [2][M][8]  cos
   uint8_t* lab;    // [NP]  key labels, 0xff past the window
   uint32_t* blk;   // [NP/32]  bits 0..8: labels present, bit 9: all 32 keys valid
-  float* red;      // [16]
+  float* red;      // [16]: per-wave max |k~|^2 (0..7), max |q^|^2 (8..15)
 };
 
 __host__ __device__ inline size_t fwd_smem_bytes(int NP, int M) {
@@ -62,48 +62,14 @@ __device__ inline FwdSmem carve(unsigned char* base, int NP, int M) {
   return s;
 }
 
-// Rotate 8 consecutive channels (4 pairs) with the LDS sin/cos table; pairs j0..j0+3 of `axis`.
-__device__ __forceinline__ void rotate8(float (&x)[8], const float* sn, const float* cs, int axis, int M, int p,
-                                        int j0) {
-  const float* s = sn + (axis * M + p) * 8 + j0;
-  const float* c = cs + (axis * M + p) * 8 + j0;
-#pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const float a = x[2 * u], b = x[2 * u + 1];
-    x[2 * u] = a * c[u] - b * s[u];
-    x[2 * u + 1] = a * s[u] + b * c[u];
-  }
-}
-
-__device__ __forceinline__ void unpack8(uint4 t, float (&x)[8]) {
-  const uint32_t w[4] = {t.x, t.y, t.z, t.w};
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    x[2 * e] = __uint_as_float(w[e] << 16);
-    x[2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
-  }
-}
-
-// Per-element live mask for the lane's 16 scores in key block kb: keys kb*32 + 8g + 4h + j.
-__device__ __forceinline__ uint32_t live_bits(const uint8_t* lab, int kb, int h, int qlab) {
-  uint32_t bits = 0;
-#pragma unroll
-  for (int g = 0; g < 4; ++g) {
-    const uint32_t w = *reinterpret_cast<const uint32_t*>(lab + kb * 32 + 8 * g + 4 * h);
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      if (((w >> (8 * j)) & 0xff) == (uint32_t)qlab) bits |= 1u << (4 * g + j);
-  }
-  return bits;
-}
-
 // One pass over the key blocks for the wave's two query tiles.
 //  MODE 0: scores offset by the accumulator init `cinit`; p = exp2(s); accumulate l and O.
 //  MODE 1: exact maximum only: m[t] = max over live keys of the raw score.
 //  MODE 2: p = exp2(s - m[t]) with the exact per-query maximum; accumulate l and O.
-template <int MODE>
+// H16: the score operands (K~ rows in LDS, Q^ in registers) are fp16, else bf16.
+template <int MODE, bool H16>
 __device__ __forceinline__ void key_pass(const FwdSmem& sm, int NB, int lane, uint32_t wave_labels, bool wave_single,
-                                         const bf16x8_t (&qb)[2][2], const int (&qlab)[2], const f32x16_t& cinit,
+                                         const uint4 (&qb)[2][2], const int (&qlab)[2], const f32x16_t& cinit,
                                          float (&m)[2], float (&l)[2], f32x16_t (&o)[2]) {
   const int h = lane >> 5;
   const int row = lane & 31;
@@ -114,13 +80,13 @@ __device__ __forceinline__ void key_pass(const FwdSmem& sm, int NB, int lane, ui
     if ((bl & wave_labels) == 0) continue;  // no query of this wave may see these keys
     const bool need_mask = !((info >> 9) & 1u) || !wave_single || bl != wave_labels;
     const uint16_t* krow = sm.K + (size_t)(kb * 32 + row) * kKStride + 8 * h;
-    const bf16x8_t ka0 = as_bf16x8(*reinterpret_cast<const uint4*>(krow));
-    const bf16x8_t ka1 = as_bf16x8(*reinterpret_cast<const uint4*>(krow + 16));
+    const uint4 ka0 = *reinterpret_cast<const uint4*>(krow);
+    const uint4 ka1 = *reinterpret_cast<const uint4*>(krow + 16);
     f32x16_t s[2];
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-      s[t] = mfma32x32x16(ka0, qb[t][0], cinit);
-      s[t] = mfma32x32x16(ka1, qb[t][1], s[t]);
+      s[t] = mfma_op<H16>(ka0, qb[t][0], cinit);
+      s[t] = mfma_op<H16>(ka1, qb[t][1], s[t]);
     }
     uint32_t live[2] = {0xffffu, 0xffffu};
     if (need_mask) {
@@ -169,6 +135,72 @@ __device__ __forceinline__ void key_pass(const FwdSmem& sm, int NB, int lane, ui
   }
 }
 
+// Stage the rotated K~ rows of the window into LDS in fp16 (h16) or bf16; returns this thread's
+// max |k~|^2 over the keys it staged (float32 values before rounding).
+__device__ inline float stage_k_rows(const FwdSmem& sm, const uint16_t* __restrict__ k, const Geom& g,
+                                     const WinHead& w, int NP, int tid, int nt, bool h16) {
+  constexpr int D = 32;
+  const int M = g.M, N = g.N;
+  const int64_t rowstride = (int64_t)g.heads * D;
+  float kmax2 = 0.f;
+  for (int it = tid; it < NP * 4; it += nt) {
+    const int key = it >> 2;
+    const int part = it & 3;
+    uint4 kr = make_uint4(0, 0, 0, 0);
+    float ss = 0.f;
+    if (key < N) {
+      const int r = key / M, c = key - (key / M) * M;
+      const int64_t off = token_index(g, w.b, w.wy, w.wx, r, c) * rowstride + w.h * D + part * 8;
+      float x[8];
+      unpack8(*reinterpret_cast<const uint4*>(k + off), x);
+      const int axis = part >> 1;
+      rotate8(x, sm.sn, sm.cs, axis, M, axis ? c : r, (part & 1) * 4);
+      kr = pack8_op(x, h16);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ss = __builtin_fmaf(x[e], x[e], ss);
+    }
+    *reinterpret_cast<uint4*>(sm.K + (size_t)key * kKStride + part * 8) = kr;
+    ss += __shfl_xor(ss, 1, 64);
+    ss += __shfl_xor(ss, 2, 64);
+    kmax2 = fmaxf(kmax2, ss);
+  }
+  return kmax2;
+}
+
+// Main pass with the bound as softmax reference, then the exact-maximum fallback if needed.
+template <bool H16>
+__device__ __forceinline__ void attend(const FwdSmem& sm, int NB, int lane, uint32_t wave_labels, bool wave_single,
+                                       const uint4 (&qb)[2][2], const int (&qlab)[2], const bool (&qvalid)[2],
+                                       float bound, float (&ref)[2], float (&l)[2], f32x16_t (&o)[2]) {
+  f32x16_t cinit;
+#pragma unroll
+  for (int v2 = 0; v2 < 16; ++v2) cinit[v2] = -bound;
+  float m[2] = {-bound, -bound};
+  if (wave_labels != 0) key_pass<0, H16>(sm, NB, lane, wave_labels, wave_single, qb, qlab, cinit, m, l, o);
+  ref[0] = ref[1] = bound;
+  bool low = false;
+#pragma unroll
+  for (int t = 0; t < 2; ++t) low |= qvalid[t] && !(l[t] + __shfl_xor(l[t], 32, 64) >= kLowSum);
+  if (__builtin_amdgcn_ballot_w64(low) != 0) {
+    f32x16_t zero;
+#pragma unroll
+    for (int v2 = 0; v2 < 16; ++v2) zero[v2] = 0.f;
+    m[0] = m[1] = -INFINITY;
+    key_pass<1, H16>(sm, NB, lane, wave_labels, wave_single, qb, qlab, zero, m, l, o);
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      m[t] = fmaxf(m[t], __shfl_xor(m[t], 32, 64));
+      if (!(m[t] > -INFINITY)) m[t] = 0.f;  // invalid query lanes
+      l[t] = 0.f;
+#pragma unroll
+      for (int v2 = 0; v2 < 16; ++v2) o[t][v2] = 0.f;
+    }
+    key_pass<2, H16>(sm, NB, lane, wave_labels, wave_single, qb, qlab, zero, m, l, o);
+    ref[0] = m[0];
+    ref[1] = m[1];
+  }
+}
+
 template <int NWAVES>
 __global__ __launch_bounds__(NWAVES * 64) void fwd_mfma_kernel(const uint16_t* __restrict__ q,
                                                                const uint16_t* __restrict__ k,
@@ -192,6 +224,8 @@ __global__ __launch_bounds__(NWAVES * 64) void fwd_mfma_kernel(const uint16_t* _
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int64_t rowstride = (int64_t)g.heads * D;
+  const int h = lane >> 5;
+  const int col = lane & 31;
 
   // 1. RoPE sin/cos table and key labels
   for (int i = tid; i < 2 * M * 8; i += NT) {
@@ -209,33 +243,19 @@ __global__ __launch_bounds__(NWAVES * 64) void fwd_mfma_kernel(const uint16_t* _
     if (n < N) lb = (uint8_t)token_label(g, w.wy, w.wx, n / M, n % M);
     sm.lab[n] = lb;
   }
-  if (tid < 16) sm.red[tid] = 0.f;
   __syncthreads();
 
-  // 2. stage K~ (rotated, bf16) and V^T; track max |k~|^2
-  float kmax2 = 0.f;
+  // 2. stage K~ (rotated, fp16) and V^T (bf16, keys in vt_pos order); track max |k~|^2
+  float kmax2 = stage_k_rows(sm, k, g, w, NP, tid, NT, true);
   for (int it = tid; it < NP * 4; it += NT) {
     const int key = it >> 2;
     const int part = it & 3;
-    uint4 kr = make_uint4(0, 0, 0, 0), vr = make_uint4(0, 0, 0, 0);
-    float ss = 0.f;
+    uint4 vr = make_uint4(0, 0, 0, 0);
     if (key < N) {
       const int r = key / M, c = key - (key / M) * M;
-      const int64_t tok = token_index(g, w.b, w.wy, w.wx, r, c);
-      const int64_t off = tok * rowstride + w.h * D + part * 8;
-      const uint4 kraw = *reinterpret_cast<const uint4*>(k + off);
+      const int64_t off = token_index(g, w.b, w.wy, w.wx, r, c) * rowstride + w.h * D + part * 8;
       vr = *reinterpret_cast<const uint4*>(v + off);
-      float x[8];
-      unpack8(kraw, x);
-      const int axis = part >> 1;
-      rotate8(x, sm.sn, sm.cs, axis, M, axis ? c : r, (part & 1) * 4);
-      kr = make_uint4(pack2(x[0], x[1]), pack2(x[2], x[3]), pack2(x[4], x[5]), pack2(x[6], x[7]));
-      float y[8];
-      unpack8(kr, y);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) ss = __builtin_fmaf(y[e], y[e], ss);
     }
-    *reinterpret_cast<uint4*>(sm.K + (size_t)key * kKStride + part * 8) = kr;
     const int pos = vt_pos(key);
     const uint32_t vw[4] = {vr.x, vr.y, vr.z, vr.w};
 #pragma unroll
@@ -243,9 +263,6 @@ __global__ __launch_bounds__(NWAVES * 64) void fwd_mfma_kernel(const uint16_t* _
       sm.Vt[(size_t)(part * 8 + 2 * e) * vt_stride(NP) + pos] = (uint16_t)(vw[e] & 0xffffu);
       sm.Vt[(size_t)(part * 8 + 2 * e + 1) * vt_stride(NP) + pos] = (uint16_t)(vw[e] >> 16);
     }
-    ss += __shfl_xor(ss, 1, 64);
-    ss += __shfl_xor(ss, 2, 64);
-    kmax2 = fmaxf(kmax2, ss);
   }
   // block label summaries
   for (int b = tid; b < NB; b += NT) {
@@ -259,20 +276,11 @@ __global__ __launch_bounds__(NWAVES * 64) void fwd_mfma_kernel(const uint16_t* _
     }
     sm.blk[b] = bits | (full << 9);
   }
-  kmax2 = wave_max(kmax2);
-  if (lane == 0) sm.red[wave] = kmax2;
-  __syncthreads();
-  float kmax2_all = 0.f;
-#pragma unroll
-  for (int i = 0; i < NWAVES; ++i) kmax2_all = fmaxf(kmax2_all, sm.red[i]);
-  const float kmax = sqrtf(kmax2_all);
 
-  // 3. the wave's queries: two 32-query tiles, rotated, scaled by log2(e)/sqrt(d), bf16 B operands
-  const int h = lane >> 5;
-  const int col = lane & 31;
+  // 3. the wave's queries (two 32-query tiles): raw loads, labels and |q^| (rotation keeps norms)
   const float qscale = kLog2e * 0.17677669529663687f;  // log2(e) / sqrt(32)
-  bf16x8_t qb[2][2];
-  int qlab[2];
+  uint4 qraw[2][2];
+  int qlab[2], qr[2], qc[2];
   bool qvalid[2];
   int64_t qtok[2];
   float qn2max = 0.f;
@@ -282,37 +290,64 @@ __global__ __launch_bounds__(NWAVES * 64) void fwd_mfma_kernel(const uint16_t* _
     qvalid[t] = qi < N;
     qlab[t] = 0xff;
     qtok[t] = 0;
-    uint4 lo = make_uint4(0, 0, 0, 0), hi = make_uint4(0, 0, 0, 0);
+    qr[t] = qc[t] = 0;
+    qraw[t][0] = qraw[t][1] = make_uint4(0, 0, 0, 0);
     float n2 = 0.f;
     if (qvalid[t]) {
-      const int r = qi / M, c = qi - (qi / M) * M;
-      qtok[t] = token_index(g, w.b, w.wy, w.wx, r, c);
-      qlab[t] = token_label(g, w.wy, w.wx, r, c);
+      qr[t] = qi / M;
+      qc[t] = qi - qr[t] * M;
+      qtok[t] = token_index(g, w.b, w.wy, w.wx, qr[t], qc[t]);
+      qlab[t] = token_label(g, w.wy, w.wx, qr[t], qc[t]);
       const int64_t off = qtok[t] * rowstride + w.h * D;
+      qraw[t][0] = *reinterpret_cast<const uint4*>(q + off + 8 * h);
+      qraw[t][1] = *reinterpret_cast<const uint4*>(q + off + 16 + 8 * h);
       float x[8], y[8];
-      unpack8(*reinterpret_cast<const uint4*>(q + off + 8 * h), x);
-      unpack8(*reinterpret_cast<const uint4*>(q + off + 16 + 8 * h), y);
-      rotate8(x, sm.sn, sm.cs, 0, M, r, 4 * h);
-      rotate8(y, sm.sn, sm.cs, 1, M, c, 4 * h);
+      unpack8(qraw[t][0], x);
+      unpack8(qraw[t][1], y);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        x[e] *= qscale;
-        y[e] *= qscale;
-      }
-      lo = make_uint4(pack2(x[0], x[1]), pack2(x[2], x[3]), pack2(x[4], x[5]), pack2(x[6], x[7]));
-      hi = make_uint4(pack2(y[0], y[1]), pack2(y[2], y[3]), pack2(y[4], y[5]), pack2(y[6], y[7]));
-      float xr[8], yr[8];
-      unpack8(lo, xr);
-      unpack8(hi, yr);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) n2 = __builtin_fmaf(xr[e], xr[e], __builtin_fmaf(yr[e], yr[e], n2));
+      for (int e = 0; e < 8; ++e) n2 = __builtin_fmaf(x[e], x[e], __builtin_fmaf(y[e], y[e], n2));
     }
     n2 += __shfl_xor(n2, 32, 64);
     qn2max = fmaxf(qn2max, n2);
-    qb[t][0] = as_bf16x8(lo);
-    qb[t][1] = as_bf16x8(hi);
   }
-  qn2max = wave_max(qn2max);
+  qn2max = wave_max(qn2max) * (qscale * qscale);
+  kmax2 = wave_max(kmax2);
+  if (lane == 0) {
+    sm.red[wave] = kmax2;
+    sm.red[8 + wave] = qn2max;
+  }
+  __syncthreads();
+  float kmax2_all = 0.f, qmax2_all = 0.f;
+#pragma unroll
+  for (int i = 0; i < NWAVES; ++i) {
+    kmax2_all = fmaxf(kmax2_all, sm.red[i]);
+    qmax2_all = fmaxf(qmax2_all, sm.red[8 + i]);
+  }
+  const float kmax = sqrtf(kmax2_all);
+  // fp16 score operands unless some |k~| or |q^| (hence some component) could leave fp16 range
+  const bool h16 = kmax < kF16Limit && sqrtf(qmax2_all) < kF16Limit;
+  if (!h16) {
+    __syncthreads();
+    stage_k_rows(sm, k, g, w, NP, tid, NT, false);
+    __syncthreads();
+  }
+
+  uint4 qb[2][2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    float x[8], y[8];
+    unpack8(qraw[t][0], x);
+    unpack8(qraw[t][1], y);
+    rotate8(x, sm.sn, sm.cs, 0, M, qr[t], 4 * h);
+    rotate8(y, sm.sn, sm.cs, 1, M, qc[t], 4 * h);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      x[e] *= qscale;
+      y[e] *= qscale;
+    }
+    qb[t][0] = pack8_op(x, h16);
+    qb[t][1] = pack8_op(y, h16);
+  }
   const float bound = sqrtf(qn2max) * kmax;  // >= every score of this wave (log2 units)
   uint32_t wl = 0;
 #pragma unroll
@@ -323,42 +358,17 @@ __global__ __launch_bounds__(NWAVES * 64) void fwd_mfma_kernel(const uint16_t* _
 
   f32x16_t o[2];
   float l[2] = {0.f, 0.f};
-  float m[2] = {-bound, -bound};
-  f32x16_t cinit;
-#pragma unroll
-  for (int v2 = 0; v2 < 16; ++v2) cinit[v2] = -bound;
+  float ref[2];
 #pragma unroll
   for (int t = 0; t < 2; ++t)
 #pragma unroll
     for (int v2 = 0; v2 < 16; ++v2) o[t][v2] = 0.f;
+  if (h16)
+    attend<true>(sm, NB, lane, wave_labels, wave_single, qb, qlab, qvalid, bound, ref, l, o);
+  else
+    attend<false>(sm, NB, lane, wave_labels, wave_single, qb, qlab, qvalid, bound, ref, l, o);
 
-  if (wave_labels != 0) key_pass<0>(sm, NB, lane, wave_labels, wave_single, qb, qlab, cinit, m, l, o);
-  float ref[2] = {bound, bound};
-
-  // 4. exact-maximum fallback when the bound was too loose for some query of this wave
-  bool low = false;
-#pragma unroll
-  for (int t = 0; t < 2; ++t) low |= qvalid[t] && !(l[t] + __shfl_xor(l[t], 32, 64) >= kLowSum);
-  if (__builtin_amdgcn_ballot_w64(low) != 0) {
-    f32x16_t zero;
-#pragma unroll
-    for (int v2 = 0; v2 < 16; ++v2) zero[v2] = 0.f;
-    m[0] = m[1] = -INFINITY;
-    key_pass<1>(sm, NB, lane, wave_labels, wave_single, qb, qlab, zero, m, l, o);
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      m[t] = fmaxf(m[t], __shfl_xor(m[t], 32, 64));
-      if (!(m[t] > -INFINITY)) m[t] = 0.f;  // invalid query lanes
-      l[t] = 0.f;
-#pragma unroll
-      for (int v2 = 0; v2 < 16; ++v2) o[t][v2] = 0.f;
-    }
-    key_pass<2>(sm, NB, lane, wave_labels, wave_single, qb, qlab, zero, m, l, o);
-    ref[0] = m[0];
-    ref[1] = m[1];
-  }
-
-  // 5. epilogue: O = O^T / l (lane: query col, channels 8g + 4h + j), LSE = (ref + log2 l) ln 2
+  // 4. epilogue: O = O^T / l (lane: query col, channels 8g + 4h + j), LSE = (ref + log2 l) ln 2
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
     const float lt = l[t] + __shfl_xor(l[t], 32, 64);

@@ -8,21 +8,23 @@
 // dq~ = sum_j dS k~ / sqrt(d),  dk~ = sum_i dS q~ / sqrt(d),  dv = sum_i P dO,
 // dq = R^T dq~, dk = R^T dk~, and dtheta += p (dx~_b x~_a - dx~_a x~_b) over Q and K tokens.
 //
-// Three kernels, all deterministic (no atomics):
-//  * prologue, one workgroup per window-head: Delta = rowsum(dO * O) per token, and the window's
-//    largest |dO| and |v| components, which fix power-of-two scales for the fp16 operands below;
+// Kernels, all deterministic (no atomics on results):
+//  * prologue, one workgroup per window-head: Delta = rowsum(dO * O) per token and the window's
+//    largest |dO|, |v|, |q|, |k| components, which fix the operand format and power-of-two scales;
 //  * dK/dV, key-stationary: a wave owns 32 keys (lane = key); queries stream through LDS in
-//    chunks.  S = Q^ K~^T and dP = dO V^T start from -LSE / -Delta tiles read from LDS (one value
-//    per query row), so P = exp2(S) and dS = P * dP cost one exp and one multiply per score;
-//    dV^T += dO^T P and dK~^T += Q^T dS;
+//    chunks.  S = Q^ K~^T and tau (dP - Delta) = dO (tau V)^T start from -LSE / -tau Delta tiles
+//    read from LDS, so P = exp2(S) and tau dS = P * (tau dP') cost one exp and one multiply per
+//    score; dV^T += (g dO)^T P and dK~^T += Q^T (tau dS), with the Q^T and dO^T operands read
+//    transposed from row-major LDS (ds_read_b64_tr_b16);
 //  * dQ, query-stationary: a wave owns 32 queries (lane = query); keys stream through LDS.
-//    S^T = K~ Q^T and dP^T = V dO^T start from the lane's -LSE and -Delta; dQ~^T += K~^T dS^T.
-// Operand precision: the inputs q, k, v, dO are bf16, so dP = dO V^T is exact on bf16 MFMA.  The
-// derived operands (rotated Q^ and K~, P, dS, the scaled dO of the dV product) go to fp16 MFMAs,
-// 8x finer than bf16; dS and dO are pre-scaled by powers of two derived from the prologue's
-// bounds (|dS| <= 64 max|dO| max|v|), so they cannot leave fp16 range.  A chunk whose rotated
-// Q^ or K~ exceeds the fp16 range is done with bf16 operands instead.  Each workgroup reduces its
-// dtheta terms in a fixed order into one partials row; a last kernel sums the rows in order.
+//    S^T = K~ Q^T and tau dP'^T = V (tau dO)^T start from the lane's -LSE and -tau Delta;
+//    dQ~^T += K~^T (tau dS)^T.
+// Operand precision: dP = dO V^T multiplies bf16 inputs exactly (tau is a power of two).  The
+// derived operands (rotated Q^ and K~, P, tau dS, g dO) go to fp16 MFMAs, 8x finer than bf16, when
+// the prologue's maxima put every one of them in fp16 range (|tau dS| <= 2^14 by construction:
+// |dS| <= |dO . v| + |Delta| <= 64 max|dO| max|v|); otherwise the window uses bf16 operands.
+// Each workgroup reduces its dtheta terms in a fixed order into one partials row; a last kernel
+// sums the rows in a fixed order.
 #include <algorithm>
 #include <mutex>
 
@@ -34,12 +36,36 @@ namespace fsw {
 
 namespace {
 
-constexpr int kCh = 128;       // tokens per LDS chunk
-constexpr int kMaxChunks = 8;  // NP <= 1024
-constexpr int kNW = 4;         // waves per workgroup: 128 queries (dQ) or 128 keys (dK/dV)
+constexpr int kCh = 128;  // tokens per LDS chunk
+constexpr float kSqrt2 = 1.4142135623730951f;
+constexpr float kQScale = kLog2e * 0.17677669529663687f;  // log2(e) / sqrt(32)
+
+__device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+__device__ __forceinline__ uint32_t uniform(uint32_t x) { return (uint32_t)__builtin_amdgcn_readfirstlane((int)x); }
 
 __host__ __device__ inline int chunk_len(int NP) { return NP < kCh ? NP : kCh; }
-__host__ __device__ inline size_t table_bytes(int M) { return (size_t)2 * 2 * M * 8 * 4; }
+
+// Power of two 2^k (k clamped to [-100, 100]) with 2^k * bound <= 2^14 (1 when bound is 0 or not
+// finite).
+__device__ __forceinline__ float pow2_scale(float bound) {
+  if (!(bound > 0.f) || !(bound < INFINITY)) return 1.f;
+  int e;
+  frexpf(bound, &e);  // bound < 2^e
+  return ldexpf(1.f, min(100, max(-100, 14 - e)));
+}
+
+// Operand format of a window-head: fp16 when every rotated, scaled score operand is in range.
+__device__ __forceinline__ bool window_h16(const float* scal, int64_t wh) {
+  return kSqrt2 * scal[wh * 4 + 2] * kQScale < kF16Limit && kSqrt2 * scal[wh * 4 + 3] < kF16Limit;
+}
+
+template <bool H16>
+__device__ __forceinline__ uint32_t pack_op2(float a, float b) {
+  if constexpr (H16)
+    return pack2h(a, b);
+  else
+    return pack2(a, b);
+}
 
 __device__ inline void fill_table(float* sn, float* cs, const float* th_row, const float* th_col, int head, int M,
                                   int tid, int nt) {
@@ -52,114 +78,6 @@ __device__ inline void fill_table(float* sn, float* cs, const float* th_row, con
     rope_sincos(th, p, &s, &c);
     sn[i] = s;
     cs[i] = c;
-  }
-}
-
-// Labels of the tokens of one chunk and the per-32-block summaries (labels present, all valid).
-__device__ inline void chunk_labels(const Geom& g, const WinHead& w, int c0, int ch, uint8_t* lab, int tid, int nt) {
-  for (int n = tid; n < ch; n += nt) {
-    const int t = c0 + n;
-    lab[n] = t < g.N ? (uint8_t)token_label(g, w.wy, w.wx, t / g.M, t % g.M) : (uint8_t)0xff;
-  }
-}
-__device__ inline void block_info(const uint8_t* lab, int ch, uint32_t* blk, int tid, int nt) {
-  for (int b = tid; b < ch / 32; b += nt) {
-    uint32_t bits = 0, full = 1;
-    for (int j = 0; j < 32; ++j) {
-      const uint8_t lb = lab[b * 32 + j];
-      if (lb == 0xff)
-        full = 0;
-      else
-        bits |= 1u << lb;
-    }
-    blk[b] = bits | (full << 9);
-  }
-}
-
-// Write 8 16-bit values (one 16-byte part of a token row) into a transposed [32][stride] array.
-__device__ __forceinline__ void write_t(uint16_t* t, int stride, int part, int pos, uint4 val) {
-  const uint32_t w4[4] = {val.x, val.y, val.z, val.w};
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    t[(size_t)(part * 8 + 2 * e) * stride + pos] = (uint16_t)(w4[e] & 0xffffu);
-    t[(size_t)(part * 8 + 2 * e + 1) * stride + pos] = (uint16_t)(w4[e] >> 16);
-  }
-}
-
-__device__ __forceinline__ bool any_big(const float (&x)[8]) {
-  bool b = false;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) b |= !(fabsf(x[e]) < kF16Limit);
-  return b;
-}
-
-// Power of two 2^k with 2^k * bound <= 2^14 (1 when bound is 0 or not finite).
-__device__ __forceinline__ float pow2_scale(float bound) {
-  if (!(bound > 0.f) || !(bound < INFINITY)) return 1.f;
-  int e;
-  frexpf(bound, &e);  // bound < 2^e
-  return ldexpf(1.f, 14 - e);
-}
-
-template <bool H16>
-__device__ __forceinline__ uint32_t pack_op2(float a, float b) {
-  if constexpr (H16)
-    return pack2h(a, b);
-  else
-    return pack2(a, b);
-}
-
-// Stage rotated rows (times `scale`) of tokens c0 .. c0+CH of `src`: row-major into `rows` and,
-// when tr != nullptr, transposed into `tr`; fp16 (h16) or bf16.  Sets *flag when a value is out
-// of fp16 range (only checked when h16).
-__device__ inline void stage_rotated(const uint16_t* __restrict__ src, const Geom& g, const WinHead& w, int c0, int CH,
-                                     const float* sn, const float* cs, float scale, bool h16, uint16_t* rows,
-                                     uint16_t* tr, int tst, uint32_t* flag, int tid, int nt) {
-  const int M = g.M, N = g.N;
-  const int64_t rowstride = (int64_t)g.heads * 32;
-  for (int it = tid; it < CH * 4; it += nt) {
-    const int n = it >> 2, part = it & 3;
-    const int tn = c0 + n;
-    float x[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    if (tn < N) {
-      const int r = tn / M, c = tn - (tn / M) * M;
-      const int64_t off = token_index(g, w.b, w.wy, w.wx, r, c) * rowstride + w.h * 32 + part * 8;
-      unpack8(*reinterpret_cast<const uint4*>(src + off), x);
-      const int axis = part >> 1;
-      rotate8(x, sn, cs, axis, M, axis ? c : r, (part & 1) * 4);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) x[e] *= scale;
-    }
-    const uint4 packed = pack8_op(x, h16);
-    *reinterpret_cast<uint4*>(rows + n * kKStride + part * 8) = packed;
-    if (tr) write_t(tr, tst, part, vt_pos(n), packed);
-    if (h16 && flag && any_big(x)) atomicOr(flag, 1u);
-  }
-}
-
-// Rows of tokens c0 .. c0+CH of `src` (bf16, unchanged) into `rows` (when not null); when tr is
-// not null also `scale * src` transposed into `tr` in fp16 (h16) or bf16.
-__device__ inline void stage_plain(const uint16_t* __restrict__ src, const Geom& g, const WinHead& w, int c0, int CH,
-                                   uint16_t* rows, uint16_t* tr, int tst, float scale, bool h16, int tid, int nt) {
-  const int M = g.M, N = g.N;
-  const int64_t rowstride = (int64_t)g.heads * 32;
-  for (int it = tid; it < CH * 4; it += nt) {
-    const int n = it >> 2, part = it & 3;
-    const int tn = c0 + n;
-    uint4 val = make_uint4(0, 0, 0, 0);
-    if (tn < N) {
-      const int r = tn / M, c = tn - (tn / M) * M;
-      val = *reinterpret_cast<const uint4*>(src + token_index(g, w.b, w.wy, w.wx, r, c) * rowstride + w.h * 32 +
-                                            part * 8);
-    }
-    if (rows) *reinterpret_cast<uint4*>(rows + n * kKStride + part * 8) = val;
-    if (tr) {
-      float x[8];
-      unpack8(val, x);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) x[e] *= scale;
-      write_t(tr, tst, part, vt_pos(n), pack8_op(x, h16));
-    }
   }
 }
 
@@ -234,19 +152,45 @@ __device__ inline void unrotate_store(const f32x16_t& dxt, float scale, float op
   }
 }
 
+// Rotate the 8 channels of `raw` (part `part` of token (r, c)), scale, pack to the operand format.
+template <bool H16>
+__device__ __forceinline__ uint4 rotated_part(uint4 raw, const float* sn, const float* cs, int M, int r, int c,
+                                              int part, float scale) {
+  float x[8];
+  unpack8(raw, x);
+  const int axis = part >> 1;
+  rotate8(x, sn, cs, axis, M, axis ? c : r, (part & 1) * 4);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) x[e] *= scale;
+  return pack8_op(x, H16);
+}
+
+// Scale 8 bf16 values by a power of two; result in the operand format.
+template <bool H16>
+__device__ __forceinline__ uint4 scaled_part(uint4 raw, float scale) {
+  float x[8];
+  unpack8(raw, x);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) x[e] *= scale;
+  return pack8_op(x, H16);
+}
+
 // ------------------------------------------------------------------------------------ prologue
 
-// One workgroup per window-head: Delta for every token, and scal[wh] = {max |dO|, max |v|}.
+// One workgroup per window-head: Delta for every token, and
+// scal[wh] = {max |dO|, max |v|, max |q|, max |k|} over the window's components.
 __global__ __launch_bounds__(256) void bwd_pre_kernel(const uint16_t* __restrict__ out,
                                                       const uint16_t* __restrict__ dout,
-                                                      const uint16_t* __restrict__ v, float* __restrict__ delta,
+                                                      const uint16_t* __restrict__ v,
+                                                      const uint16_t* __restrict__ q,
+                                                      const uint16_t* __restrict__ k, float* __restrict__ delta,
                                                       float* __restrict__ scal, Geom g) {
-  __shared__ float red[2][4];
+  __shared__ float red[4][4];
   const int64_t wh = blockIdx.x;
   const WinHead w = decode_winhead(g, wh);
   const int tid = threadIdx.x;
   const int64_t rowstride = (int64_t)g.heads * 32;
-  float gmax = 0.f, vmax = 0.f;
+  float mx[4] = {0.f, 0.f, 0.f, 0.f};
   const int items = g.N * 4;
   const int iters = (items + 255) / 256;
   for (int i = 0; i < iters; ++i) {  // uniform trip count: the shuffles below see every lane
@@ -259,140 +203,106 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const uint16_t* __restrict
       const int r = n / g.M, c = n - (n / g.M) * g.M;
       tok = token_index(g, w.b, w.wy, w.wx, r, c);
       const int64_t off = tok * rowstride + w.h * 32 + part * 8;
-      float o[8], d[8], vv[8];
-      unpack8(*reinterpret_cast<const uint4*>(out + off), o);
-      unpack8(*reinterpret_cast<const uint4*>(dout + off), d);
-      unpack8(*reinterpret_cast<const uint4*>(v + off), vv);
+      const uint4 ro = *reinterpret_cast<const uint4*>(out + off);
+      const uint4 rd = *reinterpret_cast<const uint4*>(dout + off);
+      const uint4 rv = *reinterpret_cast<const uint4*>(v + off);
+      const uint4 rq = *reinterpret_cast<const uint4*>(q + off);
+      const uint4 rk = *reinterpret_cast<const uint4*>(k + off);
+      float o[8], d[8], x[8];
+      unpack8(ro, o);
+      unpack8(rd, d);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         s = __builtin_fmaf(o[e], d[e], s);
-        gmax = fmaxf(gmax, fabsf(d[e]));
-        vmax = fmaxf(vmax, fabsf(vv[e]));
+        mx[0] = fmaxf(mx[0], fabsf(d[e]));
       }
+      unpack8(rv, x);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) mx[1] = fmaxf(mx[1], fabsf(x[e]));
+      unpack8(rq, x);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) mx[2] = fmaxf(mx[2], fabsf(x[e]));
+      unpack8(rk, x);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) mx[3] = fmaxf(mx[3], fabsf(x[e]));
     }
     s += __shfl_xor(s, 1, 64);
     s += __shfl_xor(s, 2, 64);
     if (ok && (it & 3) == 0) delta[tok * g.heads + w.h] = s;
   }
-  gmax = wave_max(gmax);
-  vmax = wave_max(vmax);
-  if ((tid & 63) == 0) {
-    red[0][tid >> 6] = gmax;
-    red[1][tid >> 6] = vmax;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    mx[i] = wave_max(mx[i]);
+    if ((tid & 63) == 0) red[i][tid >> 6] = mx[i];
   }
   __syncthreads();
-  if (tid == 0) {
-    scal[wh * 2] = fmaxf(fmaxf(red[0][0], red[0][1]), fmaxf(red[0][2], red[0][3]));
-    scal[wh * 2 + 1] = fmaxf(fmaxf(red[1][0], red[1][1]), fmaxf(red[1][2], red[1][3]));
-  }
+  if (tid < 4) scal[wh * 4 + tid] = fmaxf(fmaxf(red[tid][0], red[tid][1]), fmaxf(red[tid][2], red[tid][3]));
+}
+
+// Chunk staging helper shared by both kernels: label of chunk token n and its block summary bit
+// (bit L for label L, bit 10 for a position past the window) OR-ed into blk[n / 32].
+__device__ __forceinline__ uint8_t chunk_label(const Geom& g, const WinHead& w, int M, int tn, uint32_t* blk,
+                                               int n) {
+  const int N = M * M;
+  uint8_t lb = 0xff;
+  if (tn < N) lb = (uint8_t)token_label(g, w.wy, w.wx, tn / M, tn - (tn / M) * M);
+  atomicOr(&blk[n >> 5], lb == 0xff ? (1u << 10) : (1u << lb));
+  return lb;
 }
 
 // ---------------------------------------------------------------------------------------- dQ
 
-template <bool H16>
-__device__ __forceinline__ void dq_chunk(const uint16_t* sK, const uint16_t* sV, const uint16_t* sKt,
-                                         const uint8_t* sLab, const uint32_t* sBlk, int kst, int nblk, int col, int h,
-                                         uint32_t wave_labels, bool wave_single, int qlab, uint4 qo0, uint4 qo1,
-                                         const bf16x8_t& gb0, const bf16x8_t& gb1, const f32x16_t& cL,
-                                         const f32x16_t& cD, float ds_scale, f32x16_t& acc) {
-  for (int kb = 0; kb < nblk; ++kb) {
-    const uint32_t info = sBlk[kb];
-    const uint32_t bl = info & 0x1ffu;
-    if ((bl & wave_labels) == 0) continue;
-    const bool need_mask = !((info >> 9) & 1u) || !wave_single || bl != wave_labels;
-    const uint16_t* krow = sK + (kb * 32 + col) * kKStride + 8 * h;
-    const uint16_t* vrow = sV + (kb * 32 + col) * kKStride + 8 * h;
-    f32x16_t s = mfma_op<H16>(*reinterpret_cast<const uint4*>(krow), qo0, cL);
-    s = mfma_op<H16>(*reinterpret_cast<const uint4*>(krow + 16), qo1, s);
-    f32x16_t dp = mfma32x32x16(as_bf16x8(*reinterpret_cast<const uint4*>(vrow)), gb0, cD);
-    dp = mfma32x32x16(as_bf16x8(*reinterpret_cast<const uint4*>(vrow + 16)), gb1, dp);
-    const uint32_t live = need_mask ? live_bits(sLab, kb, h, qlab) : 0xffffu;
-    float ds[16];
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const float p = __builtin_amdgcn_exp2f(s[e]) * ds_scale;
-      ds[e] = ((live >> e) & 1u) ? p * dp[e] : 0.f;
-    }
-    uint32_t pk[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) pk[e] = pack_op2<H16>(ds[2 * e], ds[2 * e + 1]);
-    const uint16_t* ktrow = sKt + col * kst + kb * 32 + 8 * h;
-    acc = mfma_op<H16>(*reinterpret_cast<const uint4*>(ktrow), make_uint4(pk[0], pk[1], pk[2], pk[3]), acc);
-    acc = mfma_op<H16>(*reinterpret_cast<const uint4*>(ktrow + 16), make_uint4(pk[4], pk[5], pk[6], pk[7]), acc);
-  }
+template <int NW>
+struct DqSmem {
+  uint16_t* K;   // [CH][kKStride] rotated K~ (operand format)
+  uint16_t* V;   // [CH][kKStride] bf16 V
+  float* sn;
+  float* cs;
+  float* red;    // [NW * 16]
+  uint32_t* blk; // [kCh / 32]
+  uint8_t* lab;  // [kCh]
+};
+template <int NW>
+__host__ __device__ inline size_t dq_smem(int NP, int M) {
+  const int CH = chunk_len(NP);
+  return (size_t)CH * kKStride * 2 * 2 + (size_t)2 * 2 * M * 8 * 4 + NW * 16 * 4 + (kCh / 32) * 4 + kCh;
 }
 
-template <int NW>
-__global__ __launch_bounds__(NW * 64) void bwd_dq_mfma_kernel(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-    const uint16_t* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ delta,
-    const float* __restrict__ scal, const float* __restrict__ th_row, const float* __restrict__ th_col,
-    uint16_t* __restrict__ dq, float* __restrict__ partials, Geom g, int nb, int NP) {
-  extern __shared__ __align__(16) unsigned char smem_raw[];
+template <int NW, int MT, bool H16>
+__device__ inline void dq_body(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+                               const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout,
+                               const float* __restrict__ lse, const float* __restrict__ delta,
+                               const float* __restrict__ scal, uint16_t* __restrict__ dq,
+                               float* __restrict__ partials, const Geom& g, int nb, int NP, const DqSmem<NW>& sm,
+                               const WinHead& w, int64_t wh, int qblock) {
   constexpr int D = 32;
   constexpr int NT = NW * 64;
-  const int M = g.M, N = g.N;
+  const int M = MT > 0 ? MT : g.M;
+  const int N = M * M;
   const int CH = chunk_len(NP);
-  const int kst = vt_stride(CH);
-  uint16_t* sK = reinterpret_cast<uint16_t*>(smem_raw);
-  uint16_t* sV = sK + CH * kKStride;
-  uint16_t* sKt = sV + CH * kKStride;
-  float* sn = reinterpret_cast<float*>(sKt + 32 * kst);
-  float* cs = sn + 2 * M * 8;
-  float* red = cs + 2 * M * 8;
-  uint32_t* sBlk = reinterpret_cast<uint32_t*>(red + NW * 16);
-  uint32_t* sFlag = sBlk + kCh / 32;  // [0]: some |q^| out of fp16 range; [1 + chunk]: some |k~| in the chunk
-  uint8_t* sLab = reinterpret_cast<uint8_t*>(sFlag + 1 + kMaxChunks);
-
-  const int64_t blk = blockIdx.x;
-  const int64_t wh = blk / nb;
-  const WinHead w = decode_winhead(g, wh);
-  const int qblock = (int)(blk % nb);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int h = lane >> 5, col = lane & 31;
   const int64_t rowstride = (int64_t)g.heads * D;
-  const float qscale = kLog2e * 0.17677669529663687f;
-  // |dS| <= |dO . v| + |Delta| <= 64 max|dO| max|v|: scale so the fp16 dS stays in range
-  const float ds_scale = pow2_scale(64.f * scal[wh * 2] * scal[wh * 2 + 1]);
+  const float ds_scale = pow2_scale(64.f * scal[wh * 4] * scal[wh * 4 + 1]);
 
-  fill_table(sn, cs, th_row, th_col, w.h, M, tid, NT);
-  if (tid <= kMaxChunks) sFlag[tid] = 0;
-  __syncthreads();
-
-  // the lane's query: Q^ in both operand formats, dO as bf16 B operands, -LSE and -Delta
+  // the lane's query: Q^ operands, tau * dO as bf16 B operands, -LSE and -tau Delta
   const int qi = qblock * NW * 32 + wave * 32 + col;
   const bool valid = qi < N;
-  int r = 0, c = 0, qlab = 0xff;
-  int64_t tok = 0;
-  uint4 qh0 = make_uint4(0, 0, 0, 0), qh1 = qh0, qf0 = qh0, qf1 = qh0, g0 = qh0, g1 = qh0;
+  const int r = valid ? qi / M : 0, c = valid ? qi - (qi / M) * M : 0;
+  const int64_t tok = valid ? token_index(g, w.b, w.wy, w.wx, r, c) : 0;
+  const int qlab = valid ? token_label(g, w.wy, w.wx, r, c) : 0xff;
+  uint4 qb0 = make_uint4(0, 0, 0, 0), qb1 = qb0, gb0 = qb0, gb1 = qb0;
   float lse2 = 0.f, del = 0.f;
   if (valid) {
-    r = qi / M;
-    c = qi - r * M;
-    tok = token_index(g, w.b, w.wy, w.wx, r, c);
-    qlab = token_label(g, w.wy, w.wx, r, c);
     const int64_t off = tok * rowstride + w.h * D;
-    float x[8], y[8];
-    unpack8(*reinterpret_cast<const uint4*>(q + off + 8 * h), x);
-    unpack8(*reinterpret_cast<const uint4*>(q + off + 16 + 8 * h), y);
-    rotate8(x, sn, cs, 0, M, r, 4 * h);
-    rotate8(y, sn, cs, 1, M, c, 4 * h);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      x[e] *= qscale;
-      y[e] *= qscale;
-    }
-    qh0 = pack8_op(x, true);
-    qh1 = pack8_op(y, true);
-    qf0 = pack8_op(x, false);
-    qf1 = pack8_op(y, false);
-    if (any_big(x) || any_big(y)) atomicOr(&sFlag[0], 1u);
-    g0 = *reinterpret_cast<const uint4*>(dout + off + 8 * h);
-    g1 = *reinterpret_cast<const uint4*>(dout + off + 16 + 8 * h);
+    qb0 = rotated_part<H16>(*reinterpret_cast<const uint4*>(q + off + 8 * h), sm.sn, sm.cs, M, r, c, h, kQScale);
+    qb1 = rotated_part<H16>(*reinterpret_cast<const uint4*>(q + off + 16 + 8 * h), sm.sn, sm.cs, M, r, c, 2 + h,
+                            kQScale);
+    gb0 = scaled_part<false>(*reinterpret_cast<const uint4*>(dout + off + 8 * h), ds_scale);
+    gb1 = scaled_part<false>(*reinterpret_cast<const uint4*>(dout + off + 16 + 8 * h), ds_scale);
     lse2 = lse[tok * g.heads + w.h] * kLog2e;
-    del = delta[tok * g.heads + w.h];
+    del = delta[tok * g.heads + w.h] * ds_scale;
   }
-  const bf16x8_t gb0 = as_bf16x8(g0), gb1 = as_bf16x8(g1);
   f32x16_t cL, cD, acc;
 #pragma unroll
   for (int e = 0; e < 16; ++e) {
@@ -400,213 +310,252 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_mfma_kernel(
     cD[e] = -del;
     acc[e] = 0.f;
   }
-  const uint32_t wave_labels = wave_or(valid ? (1u << qlab) : 0u);
+  const uint32_t wave_labels = uniform(wave_or(valid ? (1u << qlab) : 0u));
   const bool wave_single = __builtin_popcount(wave_labels) == 1;
-  bool all16 = true;
 
-  for (int c0 = 0, ci = 0; c0 < NP; c0 += CH, ++ci) {
+  for (int c0 = 0; c0 < NP; c0 += CH) {
     __syncthreads();
-    const bool qbig = sFlag[0] != 0;
-    stage_rotated(k, g, w, c0, CH, sn, cs, 1.f, !qbig, sK, sKt, kst, &sFlag[1 + ci], tid, NT);
-    stage_plain(v, g, w, c0, CH, sV, nullptr, 0, 1.f, false, tid, NT);
-    chunk_labels(g, w, c0, CH, sLab, tid, NT);
+    if (tid < kCh / 32) sm.blk[tid] = 0;
     __syncthreads();
-    block_info(sLab, CH, sBlk, tid, NT);
-    const bool h16 = !qbig && sFlag[1 + ci] == 0;
-    if (!h16 && !qbig) stage_rotated(k, g, w, c0, CH, sn, cs, 1.f, false, sK, sKt, kst, nullptr, tid, NT);
+    for (int it = tid; it < CH * 4; it += NT) {
+      const int n = it >> 2, part = it & 3;
+      const int kn = c0 + n;
+      uint4 kr = make_uint4(0, 0, 0, 0), vr = kr;
+      if (kn < N) {
+        const int kr_ = kn / M, kc_ = kn - (kn / M) * M;
+        const int64_t off = token_index(g, w.b, w.wy, w.wx, kr_, kc_) * rowstride + w.h * D + part * 8;
+        const uint4 raw = *reinterpret_cast<const uint4*>(k + off);
+        vr = *reinterpret_cast<const uint4*>(v + off);
+        kr = rotated_part<H16>(raw, sm.sn, sm.cs, M, kr_, kc_, part, 1.f);
+      }
+      *reinterpret_cast<uint4*>(sm.K + n * kKStride + part * 8) = kr;
+      *reinterpret_cast<uint4*>(sm.V + n * kKStride + part * 8) = vr;
+      if (part == 0) sm.lab[n] = chunk_label(g, w, M, kn, sm.blk, n);
+    }
     __syncthreads();
-    all16 = all16 && h16;
     if (wave_labels == 0) continue;
     const int nblk = min(CH, NP - c0) / 32;
-    if (h16)
-      dq_chunk<true>(sK, sV, sKt, sLab, sBlk, kst, nblk, col, h, wave_labels, wave_single, qlab, qh0, qh1, gb0, gb1,
-                     cL, cD, ds_scale, acc);
-    else
-      dq_chunk<false>(sK, sV, sKt, sLab, sBlk, kst, nblk, col, h, wave_labels, wave_single, qlab, qf0, qf1, gb0, gb1,
-                      cL, cD, ds_scale, acc);
+    for (int kb = 0; kb < nblk; ++kb) {
+      const uint32_t info = uniform(sm.blk[kb]);
+      const uint32_t bl = info & 0x1ffu;
+      if ((bl & wave_labels) == 0) continue;
+      const bool need_mask = ((info >> 10) & 1u) || !wave_single || bl != wave_labels;
+      const uint16_t* krow = sm.K + (kb * 32 + col) * kKStride + 8 * h;
+      const uint16_t* vrow = sm.V + (kb * 32 + col) * kKStride + 8 * h;
+      f32x16_t s = mfma_op<H16>(*reinterpret_cast<const uint4*>(krow), qb0, cL);
+      s = mfma_op<H16>(*reinterpret_cast<const uint4*>(krow + 16), qb1, s);
+      f32x16_t dp = mfma_op<false>(*reinterpret_cast<const uint4*>(vrow), gb0, cD);
+      dp = mfma_op<false>(*reinterpret_cast<const uint4*>(vrow + 16), gb1, dp);
+      float ds[16];
+      if (need_mask) {
+        const uint32_t live = live_bits(sm.lab, kb, h, qlab);
+#pragma unroll
+        for (int e = 0; e < 16; ++e) ds[e] = ((live >> e) & 1u) ? __builtin_amdgcn_exp2f(s[e]) * dp[e] : 0.f;
+      } else {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) ds[e] = __builtin_amdgcn_exp2f(s[e]) * dp[e];
+      }
+      uint32_t pk[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) pk[e] = pack_op2<H16>(ds[2 * e], ds[2 * e + 1]);
+      const uint4 kt0 = tr_operand(sm.K, kKStride, kb * 32, lane);
+      const uint4 kt1 = tr_operand(sm.K, kKStride, kb * 32 + 16, lane);
+      acc = mfma_op<H16>(kt0, make_uint4(pk[0], pk[1], pk[2], pk[3]), acc);
+      acc = mfma_op<H16>(kt1, make_uint4(pk[4], pk[5], pk[6], pk[7]), acc);
+    }
   }
 
   float t[8] = {0, 0, 0, 0, 0, 0, 0, 0};
   if (valid) {
     const int64_t off = tok * rowstride + w.h * D;
-    // dq~ = acc / ds_scale / sqrt(d); the dtheta integrand takes q~ as the dK product saw it
-    unrotate_store(acc, 0.17677669529663687f / ds_scale, qscale, all16, q + off, dq + off, sn, cs, M, r, c, h, t);
+    // dq~ = acc / tau / sqrt(d); the dtheta integrand takes q~ as the dK product saw it
+    unrotate_store(acc, 0.17677669529663687f / ds_scale, kQScale, H16, q + off, dq + off, sm.sn, sm.cs, M, r, c, h,
+                   t);
   }
   const int64_t prow = ((int64_t)w.h * 2 + 1) * (g.B * g.nH * g.nW * nb) + wh / g.heads * nb + qblock;
-  reduce_dtheta<NW>(t, red, partials + prow * 16, lane, wave, tid);
+  reduce_dtheta<NW>(t, sm.red, partials + prow * 16, lane, wave, tid);
+}
+
+template <int NW, int MT>
+__global__ __launch_bounds__(NW * 64) void bwd_dq_mfma_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const uint16_t* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ delta,
+    const float* __restrict__ scal, const float* __restrict__ th_row, const float* __restrict__ th_col,
+    uint16_t* __restrict__ dq, float* __restrict__ partials, Geom g, int nb, int NP) {
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  const int M = MT > 0 ? MT : g.M;
+  const int CH = chunk_len(NP);
+  DqSmem<NW> sm;
+  sm.K = reinterpret_cast<uint16_t*>(smem_raw);
+  sm.V = sm.K + CH * kKStride;
+  sm.sn = reinterpret_cast<float*>(sm.V + CH * kKStride);
+  sm.cs = sm.sn + 2 * M * 8;
+  sm.red = sm.cs + 2 * M * 8;
+  sm.blk = reinterpret_cast<uint32_t*>(sm.red + NW * 16);
+  sm.lab = reinterpret_cast<uint8_t*>(sm.blk + kCh / 32);
+  const int64_t blk = blockIdx.x;
+  const int64_t wh = blk / nb;
+  const WinHead w = decode_winhead(g, wh);
+  fill_table(sm.sn, sm.cs, th_row, th_col, w.h, M, threadIdx.x, NW * 64);
+  __syncthreads();
+  if (window_h16(scal, wh))
+    dq_body<NW, MT, true>(q, k, v, dout, lse, delta, scal, dq, partials, g, nb, NP, sm, w, wh, (int)(blk % nb));
+  else
+    dq_body<NW, MT, false>(q, k, v, dout, lse, delta, scal, dq, partials, g, nb, NP, sm, w, wh, (int)(blk % nb));
 }
 
 // -------------------------------------------------------------------------------------- dK / dV
 
-template <bool H16>
-__device__ __forceinline__ void dkdv_chunk(const uint16_t* sQ, const uint16_t* sG, const uint16_t* sQt,
-                                           const uint16_t* sGt, const float* sL, const float* sD, const uint8_t* sLab,
-                                           const uint32_t* sBlk, int tst, int nblk, int col, int h,
-                                           uint32_t wave_labels, bool wave_single, int klab, uint4 ko0, uint4 ko1,
-                                           const bf16x8_t& vb0, const bf16x8_t& vb1, float ds_scale,
-                                           f32x16_t& accv, f32x16_t& acck) {
-  for (int qb = 0; qb < nblk; ++qb) {
-    const uint32_t info = sBlk[qb];
-    const uint32_t bl = info & 0x1ffu;
-    if ((bl & wave_labels) == 0) continue;
-    const bool need_mask = !((info >> 9) & 1u) || !wave_single || bl != wave_labels;
-    // -LSE and -Delta of the 16 query rows this lane's accumulators hold: 8g + 4h + j
-    f32x16_t cL, cD;
-#pragma unroll
-    for (int gq = 0; gq < 4; ++gq) {
-      const float4 l4 = *reinterpret_cast<const float4*>(sL + qb * 32 + 8 * gq + 4 * h);
-      const float4 d4 = *reinterpret_cast<const float4*>(sD + qb * 32 + 8 * gq + 4 * h);
-      cL[4 * gq] = -l4.x;
-      cL[4 * gq + 1] = -l4.y;
-      cL[4 * gq + 2] = -l4.z;
-      cL[4 * gq + 3] = -l4.w;
-      cD[4 * gq] = -d4.x;
-      cD[4 * gq + 1] = -d4.y;
-      cD[4 * gq + 2] = -d4.z;
-      cD[4 * gq + 3] = -d4.w;
-    }
-    const uint16_t* qrow = sQ + (qb * 32 + col) * kKStride + 8 * h;
-    const uint16_t* grow = sG + (qb * 32 + col) * kKStride + 8 * h;
-    f32x16_t s = mfma_op<H16>(*reinterpret_cast<const uint4*>(qrow), ko0, cL);
-    s = mfma_op<H16>(*reinterpret_cast<const uint4*>(qrow + 16), ko1, s);
-    f32x16_t dp = mfma32x32x16(as_bf16x8(*reinterpret_cast<const uint4*>(grow)), vb0, cD);
-    dp = mfma32x32x16(as_bf16x8(*reinterpret_cast<const uint4*>(grow + 16)), vb1, dp);
-    const uint32_t live = need_mask ? live_bits(sLab, qb, h, klab) : 0xffffu;
-    float p[16], ds[16];
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const float pe = ((live >> e) & 1u) ? __builtin_amdgcn_exp2f(s[e]) : 0.f;
-      p[e] = pe;
-      ds[e] = pe * ds_scale * dp[e];
-    }
-    uint32_t pp[8], pd[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      pp[e] = pack_op2<H16>(p[2 * e], p[2 * e + 1]);
-      pd[e] = pack_op2<H16>(ds[2 * e], ds[2 * e + 1]);
-    }
-    const uint16_t* gtrow = sGt + col * tst + qb * 32 + 8 * h;
-    const uint16_t* qtrow = sQt + col * tst + qb * 32 + 8 * h;
-    accv = mfma_op<H16>(*reinterpret_cast<const uint4*>(gtrow), make_uint4(pp[0], pp[1], pp[2], pp[3]), accv);
-    accv = mfma_op<H16>(*reinterpret_cast<const uint4*>(gtrow + 16), make_uint4(pp[4], pp[5], pp[6], pp[7]), accv);
-    acck = mfma_op<H16>(*reinterpret_cast<const uint4*>(qtrow), make_uint4(pd[0], pd[1], pd[2], pd[3]), acck);
-    acck = mfma_op<H16>(*reinterpret_cast<const uint4*>(qtrow + 16), make_uint4(pd[4], pd[5], pd[6], pd[7]), acck);
-  }
+template <int NW>
+struct DkdvSmem {
+  uint16_t* Q;   // [CH][kKStride] rotated, scaled Q^ (operand format)
+  uint16_t* G;   // [CH][kKStride] bf16 dO
+  uint16_t* Gs;  // [CH][32] g * dO (operand format)
+  float* L;      // [kCh] -LSE log2(e)
+  float* Dl;     // [kCh] -tau Delta
+  float* sn;
+  float* cs;
+  float* red;    // [NW * 16]
+  uint32_t* blk; // [kCh / 32]
+  uint8_t* lab;  // [kCh]
+};
+template <int NW>
+__host__ __device__ inline size_t dkdv_smem(int NP, int M) {
+  const int CH = chunk_len(NP);
+  return (size_t)CH * kKStride * 2 * 2 + (size_t)CH * 32 * 2 + kCh * 4 * 2 + (size_t)2 * 2 * M * 8 * 4 +
+         NW * 16 * 4 + (kCh / 32) * 4 + kCh;
 }
 
-template <int NW>
-__global__ __launch_bounds__(NW * 64) void bwd_dkdv_mfma_kernel(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-    const uint16_t* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ delta,
-    const float* __restrict__ scal, const float* __restrict__ th_row, const float* __restrict__ th_col,
-    uint16_t* __restrict__ dk, uint16_t* __restrict__ dv, float* __restrict__ partials, Geom g, int nb, int NP) {
-  extern __shared__ __align__(16) unsigned char smem_raw[];
+template <int NW, int MT, bool H16>
+__device__ inline void dkdv_body(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+                                 const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout,
+                                 const float* __restrict__ lse, const float* __restrict__ delta,
+                                 const float* __restrict__ scal, uint16_t* __restrict__ dk, uint16_t* __restrict__ dv,
+                                 float* __restrict__ partials, const Geom& g, int nb, int NP,
+                                 const DkdvSmem<NW>& sm, const WinHead& w, int64_t wh, int kblock) {
   constexpr int D = 32;
   constexpr int NT = NW * 64;
-  const int M = g.M, N = g.N;
+  const int M = MT > 0 ? MT : g.M;
+  const int N = M * M;
   const int CH = chunk_len(NP);
-  const int tst = vt_stride(CH);
-  uint16_t* sQ = reinterpret_cast<uint16_t*>(smem_raw);
-  uint16_t* sG = sQ + CH * kKStride;
-  uint16_t* sQt = sG + CH * kKStride;
-  uint16_t* sGt = sQt + 32 * tst;
-  float* sL = reinterpret_cast<float*>(sGt + 32 * tst);
-  float* sD = sL + kCh;
-  float* sn = sD + kCh;
-  float* cs = sn + 2 * M * 8;
-  float* red = cs + 2 * M * 8;
-  uint32_t* sBlk = reinterpret_cast<uint32_t*>(red + NW * 16);
-  uint32_t* sFlag = sBlk + kCh / 32;  // [0]: some |k~| out of fp16 range; [1 + chunk]: some |q^| in the chunk
-  uint8_t* sLab = reinterpret_cast<uint8_t*>(sFlag + 1 + kMaxChunks);
-
-  const int64_t blk = blockIdx.x;
-  const int64_t wh = blk / nb;
-  const WinHead w = decode_winhead(g, wh);
-  const int kblock = (int)(blk % nb);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int h = lane >> 5, col = lane & 31;
   const int64_t rowstride = (int64_t)g.heads * D;
-  const float qscale = kLog2e * 0.17677669529663687f;
-  const float g_scale = pow2_scale(scal[wh * 2]);                             // fp16 dO of the dV product
-  const float ds_scale = pow2_scale(64.f * scal[wh * 2] * scal[wh * 2 + 1]);  // fp16 dS of the dK product
+  const float g_scale = pow2_scale(scal[wh * 4]);                              // dO of the dV product
+  const float ds_scale = pow2_scale(64.f * scal[wh * 4] * scal[wh * 4 + 1]);  // dS of the dK product
 
-  fill_table(sn, cs, th_row, th_col, w.h, M, tid, NT);
-  if (tid <= kMaxChunks) sFlag[tid] = 0;
-  __syncthreads();
-
-  // the lane's key: K~ in both operand formats, V as bf16 B operands
+  // the lane's key: K~ operands, tau * V as bf16 B operands
   const int kj = kblock * NW * 32 + wave * 32 + col;
   const bool valid = kj < N;
-  int r = 0, c = 0, klab = 0xff;
-  int64_t tok = 0;
-  uint4 kh0 = make_uint4(0, 0, 0, 0), kh1 = kh0, kf0 = kh0, kf1 = kh0, v0 = kh0, v1 = kh0;
+  const int r = valid ? kj / M : 0, c = valid ? kj - (kj / M) * M : 0;
+  const int64_t tok = valid ? token_index(g, w.b, w.wy, w.wx, r, c) : 0;
+  const int klab = valid ? token_label(g, w.wy, w.wx, r, c) : 0xff;
+  uint4 kb0 = make_uint4(0, 0, 0, 0), kb1 = kb0, vb0 = kb0, vb1 = kb0;
   if (valid) {
-    r = kj / M;
-    c = kj - r * M;
-    tok = token_index(g, w.b, w.wy, w.wx, r, c);
-    klab = token_label(g, w.wy, w.wx, r, c);
     const int64_t off = tok * rowstride + w.h * D;
-    float x[8], y[8];
-    unpack8(*reinterpret_cast<const uint4*>(k + off + 8 * h), x);
-    unpack8(*reinterpret_cast<const uint4*>(k + off + 16 + 8 * h), y);
-    rotate8(x, sn, cs, 0, M, r, 4 * h);
-    rotate8(y, sn, cs, 1, M, c, 4 * h);
-    kh0 = pack8_op(x, true);
-    kh1 = pack8_op(y, true);
-    kf0 = pack8_op(x, false);
-    kf1 = pack8_op(y, false);
-    if (any_big(x) || any_big(y)) atomicOr(&sFlag[0], 1u);
-    v0 = *reinterpret_cast<const uint4*>(v + off + 8 * h);
-    v1 = *reinterpret_cast<const uint4*>(v + off + 16 + 8 * h);
+    kb0 = rotated_part<H16>(*reinterpret_cast<const uint4*>(k + off + 8 * h), sm.sn, sm.cs, M, r, c, h, 1.f);
+    kb1 = rotated_part<H16>(*reinterpret_cast<const uint4*>(k + off + 16 + 8 * h), sm.sn, sm.cs, M, r, c, 2 + h, 1.f);
+    vb0 = scaled_part<false>(*reinterpret_cast<const uint4*>(v + off + 8 * h), ds_scale);
+    vb1 = scaled_part<false>(*reinterpret_cast<const uint4*>(v + off + 16 + 8 * h), ds_scale);
   }
-  const bf16x8_t vb0 = as_bf16x8(v0), vb1 = as_bf16x8(v1);
   f32x16_t accv, acck;
 #pragma unroll
   for (int e = 0; e < 16; ++e) accv[e] = acck[e] = 0.f;
-  const uint32_t wave_labels = wave_or(valid ? (1u << klab) : 0u);
+  const uint32_t wave_labels = uniform(wave_or(valid ? (1u << klab) : 0u));
   const bool wave_single = __builtin_popcount(wave_labels) == 1;
-  bool all16 = true;
 
-  for (int c0 = 0, ci = 0; c0 < NP; c0 += CH, ++ci) {
+  for (int c0 = 0; c0 < NP; c0 += CH) {
     __syncthreads();
-    const bool kbig = sFlag[0] != 0;
-    stage_rotated(q, g, w, c0, CH, sn, cs, qscale, !kbig, sQ, sQt, tst, &sFlag[1 + ci], tid, NT);
-    stage_plain(dout, g, w, c0, CH, sG, sGt, tst, g_scale, !kbig, tid, NT);
-    for (int n = tid; n < CH; n += NT) {
+    if (tid < kCh / 32) sm.blk[tid] = 0;
+    __syncthreads();
+    for (int it = tid; it < CH * 4; it += NT) {
+      const int n = it >> 2, part = it & 3;
       const int qn = c0 + n;
+      uint4 qr = make_uint4(0, 0, 0, 0), gr = qr, gs = qr;
       float l2 = 0.f, dl = 0.f;
       if (qn < N) {
-        const int64_t t_ = token_index(g, w.b, w.wy, w.wx, qn / M, qn % M);
-        l2 = lse[t_ * g.heads + w.h] * kLog2e;
-        dl = delta[t_ * g.heads + w.h];
+        const int qr_ = qn / M, qc_ = qn - (qn / M) * M;
+        const int64_t t_ = token_index(g, w.b, w.wy, w.wx, qr_, qc_);
+        const int64_t off = t_ * rowstride + w.h * D + part * 8;
+        const uint4 raw = *reinterpret_cast<const uint4*>(q + off);
+        gr = *reinterpret_cast<const uint4*>(dout + off);
+        if (part == 0) {
+          l2 = lse[t_ * g.heads + w.h] * kLog2e;
+          dl = delta[t_ * g.heads + w.h] * ds_scale;
+        }
+        qr = rotated_part<H16>(raw, sm.sn, sm.cs, M, qr_, qc_, part, kQScale);
+        gs = scaled_part<H16>(gr, g_scale);
       }
-      sL[n] = l2;
-      sD[n] = dl;
-    }
-    chunk_labels(g, w, c0, CH, sLab, tid, NT);
-    __syncthreads();
-    block_info(sLab, CH, sBlk, tid, NT);
-    const bool h16 = !kbig && sFlag[1 + ci] == 0;
-    if (!h16 && !kbig) {
-      stage_rotated(q, g, w, c0, CH, sn, cs, qscale, false, sQ, sQt, tst, nullptr, tid, NT);
-      stage_plain(dout, g, w, c0, CH, nullptr, sGt, tst, g_scale, false, tid, NT);
+      *reinterpret_cast<uint4*>(sm.Q + n * kKStride + part * 8) = qr;
+      *reinterpret_cast<uint4*>(sm.G + n * kKStride + part * 8) = gr;
+      *reinterpret_cast<uint4*>(sm.Gs + n * 32 + part * 8) = gs;
+      if (part == 0) {
+        sm.L[n] = -l2;
+        sm.Dl[n] = -dl;
+        sm.lab[n] = chunk_label(g, w, M, qn, sm.blk, n);
+      }
     }
     __syncthreads();
-    all16 = all16 && h16;
     if (wave_labels == 0) continue;
     const int nblk = min(CH, NP - c0) / 32;
-    if (h16)
-      dkdv_chunk<true>(sQ, sG, sQt, sGt, sL, sD, sLab, sBlk, tst, nblk, col, h, wave_labels, wave_single, klab, kh0,
-                       kh1, vb0, vb1, ds_scale, accv, acck);
-    else
-      dkdv_chunk<false>(sQ, sG, sQt, sGt, sL, sD, sLab, sBlk, tst, nblk, col, h, wave_labels, wave_single, klab, kf0,
-                        kf1, vb0, vb1, ds_scale, accv, acck);
+    for (int qb = 0; qb < nblk; ++qb) {
+      const uint32_t info = uniform(sm.blk[qb]);
+      const uint32_t bl = info & 0x1ffu;
+      if ((bl & wave_labels) == 0) continue;
+      const bool need_mask = ((info >> 10) & 1u) || !wave_single || bl != wave_labels;
+      // -LSE and -tau Delta of the 16 query rows this lane's accumulators hold: 8g + 4h + j
+      f32x16_t cL, cD;
+#pragma unroll
+      for (int gq = 0; gq < 4; ++gq) {
+        const float4 l4 = *reinterpret_cast<const float4*>(sm.L + qb * 32 + 8 * gq + 4 * h);
+        const float4 d4 = *reinterpret_cast<const float4*>(sm.Dl + qb * 32 + 8 * gq + 4 * h);
+        cL[4 * gq] = l4.x;
+        cL[4 * gq + 1] = l4.y;
+        cL[4 * gq + 2] = l4.z;
+        cL[4 * gq + 3] = l4.w;
+        cD[4 * gq] = d4.x;
+        cD[4 * gq + 1] = d4.y;
+        cD[4 * gq + 2] = d4.z;
+        cD[4 * gq + 3] = d4.w;
+      }
+      const uint16_t* qrow = sm.Q + (qb * 32 + col) * kKStride + 8 * h;
+      const uint16_t* grow = sm.G + (qb * 32 + col) * kKStride + 8 * h;
+      f32x16_t s = mfma_op<H16>(*reinterpret_cast<const uint4*>(qrow), kb0, cL);
+      s = mfma_op<H16>(*reinterpret_cast<const uint4*>(qrow + 16), kb1, s);
+      f32x16_t dp = mfma_op<false>(*reinterpret_cast<const uint4*>(grow), vb0, cD);
+      dp = mfma_op<false>(*reinterpret_cast<const uint4*>(grow + 16), vb1, dp);
+      float p[16], ds[16];
+      if (need_mask) {
+        const uint32_t live = live_bits(sm.lab, qb, h, klab);
+#pragma unroll
+        for (int e = 0; e < 16; ++e) p[e] = ((live >> e) & 1u) ? __builtin_amdgcn_exp2f(s[e]) : 0.f;
+      } else {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) p[e] = __builtin_amdgcn_exp2f(s[e]);
+      }
+#pragma unroll
+      for (int e = 0; e < 16; ++e) ds[e] = p[e] * dp[e];
+      uint32_t pp[8], pd[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        pp[e] = pack_op2<H16>(p[2 * e], p[2 * e + 1]);
+        pd[e] = pack_op2<H16>(ds[2 * e], ds[2 * e + 1]);
+      }
+      const uint4 gt0 = tr_operand(sm.Gs, 32, qb * 32, lane);
+      const uint4 gt1 = tr_operand(sm.Gs, 32, qb * 32 + 16, lane);
+      accv = mfma_op<H16>(gt0, make_uint4(pp[0], pp[1], pp[2], pp[3]), accv);
+      accv = mfma_op<H16>(gt1, make_uint4(pp[4], pp[5], pp[6], pp[7]), accv);
+      const uint4 qt0 = tr_operand(sm.Q, kKStride, qb * 32, lane);
+      const uint4 qt1 = tr_operand(sm.Q, kKStride, qb * 32 + 16, lane);
+      acck = mfma_op<H16>(qt0, make_uint4(pd[0], pd[1], pd[2], pd[3]), acck);
+      acck = mfma_op<H16>(qt1, make_uint4(pd[4], pd[5], pd[6], pd[7]), acck);
+    }
   }
 
   float t[8] = {0, 0, 0, 0, 0, 0, 0, 0};
   if (valid) {
     const int64_t off = tok * rowstride + w.h * D;
-    // dV = accv / g_scale: lane holds channels 8g + 4h + j of its key
+    // dV = accv / g: lane holds channels 8g + 4h + j of its key
     const float inv_g = 1.f / g_scale;
 #pragma unroll
     for (int gq = 0; gq < 4; ++gq) {
@@ -615,28 +564,82 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_mfma_kernel(
       o.y = pack2(accv[4 * gq + 2] * inv_g, accv[4 * gq + 3] * inv_g);
       *reinterpret_cast<uint2*>(dv + off + 8 * gq + 4 * h) = o;
     }
-    // dk~ = acck * ln 2 / ds_scale (the Q operand carried log2(e) / sqrt(d))
-    unrotate_store(acck, kLn2 / ds_scale, 1.0f, all16, k + off, dk + off, sn, cs, M, r, c, h, t);
+    // dk~ = acck * ln 2 / tau (the Q operand carried log2(e) / sqrt(d))
+    unrotate_store(acck, kLn2 / ds_scale, 1.0f, H16, k + off, dk + off, sm.sn, sm.cs, M, r, c, h, t);
   }
   const int64_t prow = ((int64_t)w.h * 2 + 0) * (g.B * g.nH * g.nW * nb) + wh / g.heads * nb + kblock;
-  reduce_dtheta<NW>(t, red, partials + prow * 16, lane, wave, tid);
+  reduce_dtheta<NW>(t, sm.red, partials + prow * 16, lane, wave, tid);
 }
 
-size_t dq_smem(int NP, int M) {
+template <int NW, int MT>
+__global__ __launch_bounds__(NW * 64) void bwd_dkdv_mfma_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const uint16_t* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ delta,
+    const float* __restrict__ scal, const float* __restrict__ th_row, const float* __restrict__ th_col,
+    uint16_t* __restrict__ dk, uint16_t* __restrict__ dv, float* __restrict__ partials, Geom g, int nb, int NP) {
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  const int M = MT > 0 ? MT : g.M;
   const int CH = chunk_len(NP);
-  return (size_t)CH * kKStride * 2 * 2 + (size_t)32 * vt_stride(CH) * 2 + table_bytes(M) + kNW * 16 * 4 +
-         (kCh / 32) * 4 + (1 + kMaxChunks) * 4 + kCh;
+  DkdvSmem<NW> sm;
+  sm.Q = reinterpret_cast<uint16_t*>(smem_raw);
+  sm.G = sm.Q + CH * kKStride;
+  sm.Gs = sm.G + CH * kKStride;
+  sm.L = reinterpret_cast<float*>(sm.Gs + CH * 32);
+  sm.Dl = sm.L + kCh;
+  sm.sn = sm.Dl + kCh;
+  sm.cs = sm.sn + 2 * M * 8;
+  sm.red = sm.cs + 2 * M * 8;
+  sm.blk = reinterpret_cast<uint32_t*>(sm.red + NW * 16);
+  sm.lab = reinterpret_cast<uint8_t*>(sm.blk + kCh / 32);
+  const int64_t blk = blockIdx.x;
+  const int64_t wh = blk / nb;
+  const WinHead w = decode_winhead(g, wh);
+  fill_table(sm.sn, sm.cs, th_row, th_col, w.h, M, threadIdx.x, NW * 64);
+  __syncthreads();
+  if (window_h16(scal, wh))
+    dkdv_body<NW, MT, true>(q, k, v, dout, lse, delta, scal, dk, dv, partials, g, nb, NP, sm, w, wh,
+                            (int)(blk % nb));
+  else
+    dkdv_body<NW, MT, false>(q, k, v, dout, lse, delta, scal, dk, dv, partials, g, nb, NP, sm, w, wh,
+                             (int)(blk % nb));
 }
-size_t dkdv_smem(int NP, int M) {
-  const int CH = chunk_len(NP);
-  return (size_t)CH * kKStride * 2 * 2 + (size_t)32 * vt_stride(CH) * 2 * 2 + kCh * 4 * 2 + table_bytes(M) +
-         kNW * 16 * 4 + (kCh / 32) * 4 + (1 + kMaxChunks) * 4 + kCh;
+
+template <int NW, int MT>
+hipError_t launch_main(const BwdArgs& a, hipStream_t st) {
+  const Geom& g = a.g;
+  const int64_t nwh = g.B * g.nH * g.nW * g.heads;
+  const int NP = (g.N + 31) / 32 * 32;
+  const int nb = (g.N + NW * 32 - 1) / (NW * 32);
+  const int64_t blocks = nwh * nb;
+  static std::once_flag once;
+  std::call_once(once, [] {
+    (void)hipFuncSetAttribute((const void*)bwd_dq_mfma_kernel<NW, MT>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              160 * 1024);
+    (void)hipFuncSetAttribute((const void*)bwd_dkdv_mfma_kernel<NW, MT>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+  });
+  hipLaunchKernelGGL((bwd_dkdv_mfma_kernel<NW, MT>), dim3((unsigned)blocks), dim3(NW * 64), dkdv_smem<NW>(NP, g.M),
+                     st, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (const uint16_t*)a.dout,
+                     a.lse, a.delta, a.scal, a.th_row, a.th_col, (uint16_t*)a.dk, (uint16_t*)a.dv, a.partials, g, nb,
+                     NP);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((bwd_dq_mfma_kernel<NW, MT>), dim3((unsigned)blocks), dim3(NW * 64), dq_smem<NW>(NP, g.M), st,
+                     (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (const uint16_t*)a.dout,
+                     a.lse, a.delta, a.scal, a.th_row, a.th_col, (uint16_t*)a.dq, a.partials, g, nb, NP);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t rows_per_head = 2 * g.B * g.nH * g.nW * nb;
+  return launch_dtheta_reduce(a.partials, a.n_partials, rows_per_head, g, a.dth_row, a.dth_col, st);
 }
+
+int waves_for(int N) { return N > 128 ? 8 : N > 64 ? 4 : 2; }
 
 }  // namespace
 
 int64_t bwd_mfma_partials(const Geom& g) {
-  const int64_t nb = (g.N + kNW * 32 - 1) / (kNW * 32);
+  const int nw = waves_for(g.N);
+  const int64_t nb = (g.N + nw * 32 - 1) / (nw * 32);
   return (int64_t)g.heads * 2 * g.B * g.nH * g.nW * nb;
 }
 
@@ -644,32 +647,17 @@ hipError_t launch_bwd_mfma(const BwdArgs& a, hipStream_t st) {
   const Geom& g = a.g;
   const int64_t nwh = g.B * g.nH * g.nW * g.heads;
   hipLaunchKernelGGL(bwd_pre_kernel, dim3((unsigned)nwh), dim3(256), 0, st, (const uint16_t*)a.out,
-                     (const uint16_t*)a.dout, (const uint16_t*)a.v, a.delta, a.scal, g);
+                     (const uint16_t*)a.dout, (const uint16_t*)a.v, (const uint16_t*)a.q, (const uint16_t*)a.k,
+                     a.delta, a.scal, g);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int NP = (g.N + 31) / 32 * 32;
-  const int nb = (g.N + kNW * 32 - 1) / (kNW * 32);
-  const int64_t blocks = nwh * nb;
-  static std::once_flag once;
-  std::call_once(once, [] {
-    (void)hipFuncSetAttribute((const void*)bwd_dq_mfma_kernel<kNW>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                              160 * 1024);
-    (void)hipFuncSetAttribute((const void*)bwd_dkdv_mfma_kernel<kNW>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                              160 * 1024);
-  });
-  hipLaunchKernelGGL(bwd_dkdv_mfma_kernel<kNW>, dim3((unsigned)blocks), dim3(kNW * 64), dkdv_smem(NP, g.M), st,
-                     (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (const uint16_t*)a.dout,
-                     a.lse, a.delta, a.scal, a.th_row, a.th_col, (uint16_t*)a.dk, (uint16_t*)a.dv, a.partials, g, nb,
-                     NP);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(bwd_dq_mfma_kernel<kNW>, dim3((unsigned)blocks), dim3(kNW * 64), dq_smem(NP, g.M), st,
-                     (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (const uint16_t*)a.dout,
-                     a.lse, a.delta, a.scal, a.th_row, a.th_col, (uint16_t*)a.dq, a.partials, g, nb, NP);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  const int64_t rows_per_head = 2 * g.B * g.nH * g.nW * nb;
-  return launch_dtheta_reduce(a.partials, a.n_partials, rows_per_head, g, a.dth_row, a.dth_col, st);
+  if (g.M == 32) return launch_main<8, 32>(a, st);
+  if (g.M == 8) return launch_main<2, 8>(a, st);
+  switch (waves_for(g.N)) {
+    case 8: return launch_main<8, 0>(a, st);
+    case 4: return launch_main<4, 0>(a, st);
+    default: return launch_main<2, 0>(a, st);
+  }
 }
 
 }  // namespace fsw

@@ -328,17 +328,6 @@ static hipError_t launch_bwd_scalar_t(const BwdArgs& a, hipStream_t st) {
   return launch_dtheta_reduce(a.partials, a.n_partials, rows_per_head, g, a.dth_row, a.dth_col, st);
 }
 
-hipError_t launch_bwd_delta(const BwdArgs& a, hipStream_t st) {
-  const int64_t rows = a.g.B * a.g.Hg * a.g.Wg * a.g.heads;
-  const int64_t dblocks = std::min<int64_t>((rows + 255) / 256, 65536);
-  if (a.dtype == 1 && a.g.d == 32) {
-    hipLaunchKernelGGL((bwd_delta_kernel<uint16_t, 32>), dim3((unsigned)dblocks), dim3(256), 0, st,
-                       (const uint16_t*)a.out, (const uint16_t*)a.dout, a.delta, rows);
-    return hipGetLastError();
-  }
-  return hipErrorInvalidValue;
-}
-
 hipError_t launch_bwd_scalar(const BwdArgs& a, hipStream_t st) {
   const bool bf = a.dtype == 1;
   switch (a.g.d) {

@@ -58,7 +58,7 @@ WsLayout workspace_layout(const fsw::Geom& g, bool mfma) {
   const int64_t nwh = g.B * g.nH * g.nW * g.heads;
   w.delta_off = 0;
   w.scal_off = align256((size_t)rows * sizeof(float));
-  w.partials_off = w.scal_off + align256((size_t)nwh * 2 * sizeof(float));
+  w.partials_off = w.scal_off + align256((size_t)nwh * 4 * sizeof(float));
   w.n_partials = mfma ? fsw::bwd_mfma_partials(g) : fsw::bwd_scalar_partials(g);
   w.total = w.partials_off + align256((size_t)w.n_partials * (g.d / 2) * sizeof(float));
   return w;

@@ -39,7 +39,7 @@ struct BwdArgs {
   int dtype;
   // workspace carve-up (device pointers inside the caller's workspace)
   float* delta;     // [B*Hg*Wg*heads]  rowsum(dO * O)
-  float* scal;      // [windows*heads][2]  max |dO|, max |v| per window-head (MFMA path)
+  float* scal;      // [windows*heads][4]  per window-head: max |dO|, max |v|, max |q|, max |k| components
   float* partials;  // [n_partials][2][d/4]  per-workgroup dtheta partial sums
   int64_t n_partials;
 };
@@ -55,8 +55,6 @@ hipError_t launch_fwd_mfma(const FwdArgs& a, hipStream_t st);
 hipError_t launch_bwd_mfma(const BwdArgs& a, hipStream_t st);
 int64_t bwd_mfma_partials(const Geom& g);
 constexpr bool kHaveMfmaBwd = true;
-// Delta = rowsum(dO * O) (bf16, d == 32) into a.delta.
-hipError_t launch_bwd_delta(const BwdArgs& a, hipStream_t st);
 
 // Deterministic fixed-order reduction of dtheta partials into dth_row / dth_col.
 hipError_t launch_dtheta_reduce(const float* partials, int64_t n_partials, int64_t partials_per_head_stride,

@@ -40,6 +40,30 @@ __device__ __forceinline__ f32x16_t mfma_op(uint4 a, uint4 b, const f32x16_t& c)
                                                    c, 0, 0, 0);
 }
 
+// ds_read_b64_tr_b16 (gfx950): a group of 16 lanes loads 16 x 8 bytes and redistributes the
+// 16-bit elements: output lane i of the group receives, in slot m, element (i % 4) of the chunk
+// addressed by lane 4m + i/4 of the group.  If lane 4m + q addresses 4 consecutive channels
+// 4q..4q+3 of key row m, output lane i holds channel i of keys 0..3: a row-major [key][channel]
+// tile is read transposed, as the MFMA k-dimension needs it.
+__device__ __forceinline__ uint2 lds_read_tr16(const uint16_t* p) {
+  typedef short v4s __attribute__((ext_vector_type(4)));
+  const v4s r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)(p));
+  return __builtin_bit_cast(uint2, r);
+}
+
+// A operand (8 values of one channel) for the P.V / dO^T.P style products from a row-major
+// [key][32 channels] LDS array with row stride `rs` elements: lane l supplies channel l % 32 of
+// the keys in slot order 4h + {0..3}, 8 + 4h + {0..3} (h = l / 32) of the 16-key group at `k0`,
+// matching the key order of the score accumulator (keys 8g + 4h + j).
+__device__ __forceinline__ uint4 tr_operand(const uint16_t* rows, int rs, int k0, int lane) {
+  const int j = lane & 15;
+  const int key = k0 + 4 * (lane >> 5) + (j >> 2);
+  const uint16_t* p = rows + (size_t)key * rs + (lane & 16) + 4 * (j & 3);
+  const uint2 lo = lds_read_tr16(p);
+  const uint2 hi = lds_read_tr16(p + 8 * rs);
+  return make_uint4(lo.x, lo.y, hi.x, hi.y);
+}
+
 // Largest operand magnitude accepted for the fp16 score products (fp16 max is 65504).
 constexpr float kF16Limit = 16384.f;
 

@@ -4,19 +4,27 @@
 // the score matrix (FlashSwin paper card, "FLASHSWIN: Unlocking Large Windows and Dense Tokens in
 // Swin Vision Transformers with Memory Efficient Attention": Abstract; Figure 1(B)).
 //
-// Workgroup = (window, head, block of NWAVES*64 queries).  The window's K (rotated, bf16) and V
-// (transposed) are staged once in LDS; each wave owns 64 queries (two 32-query MFMA tiles) held as
-// bf16 B operands, and walks the keys in 32-key blocks: S^T = K~ Q^T (2 MFMAs), P = exp2(S^T),
-// O^T += V^T P^T (2 MFMAs).  The shift and window partition are index arithmetic on the loads and
-// stores; the Swin region mask is applied per element only in key blocks whose labels are mixed,
-// and key blocks with no label in common with the wave are skipped.
+// Workgroup = (window, head, block of NWAVES*32 queries).  The window's K (rotated) and V rows are
+// staged once in LDS (the P.V operands are read transposed by ds_read_b64_tr_b16); each wave owns
+// 32 queries (one MFMA tile) held as B operands and walks the keys in 32-key blocks:
+// S^T = K~ Q^T (2 MFMAs), P = exp2(S^T), O^T += V^T P^T (2 MFMAs).  One tile per wave keeps a wave
+// under 128 registers, so four waves share each SIMD and hide each other's latencies.  The shift
+// and window partition are index arithmetic on the loads and stores.  A window with a single Swin
+// region and an even number of whole 32-key blocks takes a branch-free, software-pipelined loop
+// (the score MFMAs of block b+1 are issued before the exponentials of block b).  Other windows mask
+// per element in key blocks whose labels are mixed and skip blocks with no label in common with
+// the wave.
 //
 // Softmax reference: softmax is unchanged by subtracting any per-row constant.  Instead of a
 // running maximum, each wave subtracts the Cauchy-Schwarz bound B = max_i |q_i| * max_j |k_j| of its
 // scores, folded into the MFMA accumulator initialisation (so the subtraction costs nothing), and
 // the sum is accumulated without rescaling.  Every exponent is then <= 0 (no overflow).  If a
 // query's sum comes out below 2^-80 (a bound so loose that small terms could underflow), the wave
-// recomputes its tiles with the exact row maximum in a second pass; results are exact either way.
+// recomputes its tile with the exact row maximum in a second pass; results are exact either way.
+//
+// Precision: the score operands (rotated, scaled Q^ and K~) are rounded to fp16 when every one of
+// them is in fp16 range (else bf16); P is bf16 (it may be far below 1 under the bound reference,
+// where bf16 keeps the exponent range); V is the bf16 input; accumulation is float32.
 #include <algorithm>
 #include <mutex>
 
@@ -29,31 +37,35 @@ namespace fsw {
 namespace {
 
 constexpr float kLowSum = 8.271806125530277e-25f;  // 2^-80
+constexpr int kMaxWaves = 16;
+
+__device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+__device__ __forceinline__ uint32_t uniform(uint32_t x) { return (uint32_t)__builtin_amdgcn_readfirstlane((int)x); }
 
 struct FwdSmem {
   uint16_t* K;     // [NP][kKStride]
-  uint16_t* Vt;    // [32][NP + 8]
+  uint16_t* V;     // [NP][32] row-major; P.V operands come from transposing LDS reads
   float* sn;       // [2][M][8]  sin of RoPE angle (row axis, column axis)
   float* cs;       // [2][M][8]  cos
   uint8_t* lab;    // [NP]  key labels, 0xff past the window
   uint32_t* blk;   // [NP/32]  bits 0..8: labels present, bit 9: all 32 keys valid
-  float* red;      // [16]: per-wave max |k~|^2 (0..7), max |q^|^2 (8..15)
+  float* red;      // [2 * kMaxWaves]: per-wave max |k~|^2, then max |q^|^2
 };
 
 __host__ __device__ inline size_t fwd_smem_bytes(int NP, int M) {
-  size_t b = (size_t)NP * kKStride * 2 + (size_t)32 * vt_stride(NP) * 2;
+  size_t b = (size_t)NP * kKStride * 2 + (size_t)NP * 32 * 2;
   b += (size_t)2 * 2 * M * 8 * 4;
   b += (size_t)NP;
   b = (b + 3) & ~(size_t)3;
-  b += (size_t)(NP / 32) * 4 + 16 * 4;
+  b += (size_t)(NP / 32) * 4 + 2 * kMaxWaves * 4;
   return b;
 }
 
 __device__ inline FwdSmem carve(unsigned char* base, int NP, int M) {
   FwdSmem s;
   s.K = reinterpret_cast<uint16_t*>(base);
-  s.Vt = s.K + (size_t)NP * kKStride;
-  s.sn = reinterpret_cast<float*>(s.Vt + (size_t)32 * vt_stride(NP));
+  s.V = s.K + (size_t)NP * kKStride;
+  s.sn = reinterpret_cast<float*>(s.V + (size_t)NP * 32);
   s.cs = s.sn + 2 * M * 8;
   s.lab = reinterpret_cast<uint8_t*>(s.cs + 2 * M * 8);
   size_t off = ((size_t)(s.lab + NP - base) + 3) & ~(size_t)3;
@@ -62,102 +74,155 @@ __device__ inline FwdSmem carve(unsigned char* base, int NP, int M) {
   return s;
 }
 
-// One pass over the key blocks for the wave's two query tiles.
-//  MODE 0: scores offset by the accumulator init `cinit`; p = exp2(s); accumulate l and O.
-//  MODE 1: exact maximum only: m[t] = max over live keys of the raw score.
-//  MODE 2: p = exp2(s - m[t]) with the exact per-query maximum; accumulate l and O.
-// H16: the score operands (K~ rows in LDS, Q^ in registers) are fp16, else bf16.
+// Grid token of in-window position (r, c) with the window size M passed explicitly (a constant in
+// the specialised kernels, so the index arithmetic folds).
+__device__ __forceinline__ int64_t tok_of(const Geom& g, const WinHead& w, int M, int r, int c) {
+  int y = w.wy * M + r + g.shift;
+  y = y >= g.Hg ? y - g.Hg : y;
+  int x = w.wx * M + c + g.shift;
+  x = x >= g.Wg ? x - g.Wg : x;
+  return (w.b * g.Hg + y) * g.Wg + x;
+}
+
+// Score tile S^T = K~ Q^T + cinit of key block b.
+template <bool H16>
+__device__ __forceinline__ f32x16_t block_scores(const FwdSmem& sm, int b, int row, int h, uint4 qb0, uint4 qb1,
+                                                 const f32x16_t& cinit) {
+  const uint16_t* krow = sm.K + (size_t)(b * 32 + row) * kKStride + 8 * h;
+  f32x16_t s = mfma_op<H16>(*reinterpret_cast<const uint4*>(krow), qb0, cinit);
+  return mfma_op<H16>(*reinterpret_cast<const uint4*>(krow + 16), qb1, s);
+}
+
+// P = exp2(S^T - m) of key block b (masked by `live` when MASK), row sums, O^T += V^T P^T.
+template <bool MASK, bool SUBM>
+__device__ __forceinline__ void block_consume(const FwdSmem& sm, int b, int lane, uint32_t live, float m,
+                                              const f32x16_t& s, float& la, float& lb, f32x16_t& o) {
+  const bf16x8_t va0 = as_bf16x8(tr_operand(sm.V, 32, b * 32, lane));
+  const bf16x8_t va1 = as_bf16x8(tr_operand(sm.V, 32, b * 32 + 16, lane));
+  float p[16];
+#pragma unroll
+  for (int v = 0; v < 16; ++v) p[v] = __builtin_amdgcn_exp2f(SUBM ? s[v] - m : s[v]);
+  if (MASK) {
+#pragma unroll
+    for (int v = 0; v < 16; ++v) p[v] = ((live >> v) & 1u) ? p[v] : 0.f;
+  }
+  uint32_t pk[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) pk[e] = pack2(p[2 * e], p[2 * e + 1]);
+#pragma unroll
+  for (int e = 0; e < 8; e += 2) {
+    la = add_pair(pk[e], la);
+    lb = add_pair(pk[e + 1], lb);
+  }
+  o = mfma32x32x16(va0, as_bf16x8(make_uint4(pk[0], pk[1], pk[2], pk[3])), o);
+  o = mfma32x32x16(va1, as_bf16x8(make_uint4(pk[4], pk[5], pk[6], pk[7])), o);
+}
+
+// Main pass for a window with one region and an even number of whole blocks: no masks, no skips,
+// pipelined with two score buffers.
+template <bool H16>
+__device__ __forceinline__ void pass_uniform(const FwdSmem& sm, int NB, int lane, uint4 qb0, uint4 qb1,
+                                             const f32x16_t& cinit, float& l, f32x16_t& o) {
+  const int h = lane >> 5, row = lane & 31;
+  float la = 0.f, lb = 0.f;
+  // the prefetch after the last pair recomputes block NB-1 and is not used
+  f32x16_t sa = block_scores<H16>(sm, 0, row, h, qb0, qb1, cinit);
+  for (int kb = 0; kb < NB; kb += 2) {
+    const f32x16_t sb = block_scores<H16>(sm, kb + 1, row, h, qb0, qb1, cinit);
+    block_consume<false, false>(sm, kb, lane, 0xffffu, 0.f, sa, la, lb, o);
+    sa = block_scores<H16>(sm, min(kb + 2, NB - 1), row, h, qb0, qb1, cinit);
+    block_consume<false, false>(sm, kb + 1, lane, 0xffffu, 0.f, sb, la, lb, o);
+  }
+  l = la + lb;
+}
+
+// General pass over the key blocks (regions mixed, ragged last block):
+//  MODE 0: scores offset by `cinit`; p = exp2(s); accumulate l and O.
+//  MODE 1: exact maximum only: m = max over live keys of the raw score.
+//  MODE 2: p = exp2(s - m) with the exact per-query maximum; accumulate l and O.
 template <int MODE, bool H16>
-__device__ __forceinline__ void key_pass(const FwdSmem& sm, int NB, int lane, uint32_t wave_labels, bool wave_single,
-                                         const uint4 (&qb)[2][2], const int (&qlab)[2], const f32x16_t& cinit,
-                                         float (&m)[2], float (&l)[2], f32x16_t (&o)[2]) {
-  const int h = lane >> 5;
-  const int row = lane & 31;
-  const int vst = vt_stride(NB * 32);
+__device__ __forceinline__ void pass_general(const FwdSmem& sm, int NB, int lane, uint32_t wave_labels,
+                                             bool wave_single, uint4 qb0, uint4 qb1, int qlab,
+                                             const f32x16_t& cinit, float& m, float& l, f32x16_t& o) {
+  const int h = lane >> 5, row = lane & 31;
+  float la = l, lb = 0.f;
   for (int kb = 0; kb < NB; ++kb) {
-    const uint32_t info = sm.blk[kb];
+    const uint32_t info = uniform(sm.blk[kb]);
     const uint32_t bl = info & 0x1ffu;
     if ((bl & wave_labels) == 0) continue;  // no query of this wave may see these keys
     const bool need_mask = !((info >> 9) & 1u) || !wave_single || bl != wave_labels;
-    const uint16_t* krow = sm.K + (size_t)(kb * 32 + row) * kKStride + 8 * h;
-    const uint4 ka0 = *reinterpret_cast<const uint4*>(krow);
-    const uint4 ka1 = *reinterpret_cast<const uint4*>(krow + 16);
-    f32x16_t s[2];
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      s[t] = mfma_op<H16>(ka0, qb[t][0], cinit);
-      s[t] = mfma_op<H16>(ka1, qb[t][1], s[t]);
-    }
-    uint32_t live[2] = {0xffffu, 0xffffu};
-    if (need_mask) {
-#pragma unroll
-      for (int t = 0; t < 2; ++t) live[t] = live_bits(sm.lab, kb, h, qlab[t]);
-    }
+    const f32x16_t s = block_scores<H16>(sm, kb, row, h, qb0, qb1, cinit);
+    const uint32_t live = need_mask ? live_bits(sm.lab, kb, h, qlab) : 0xffffu;
     if (MODE == 1) {
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
-#pragma unroll
-        for (int v = 0; v < 16; ++v)
-          if ((live[t] >> v) & 1u) m[t] = fmaxf(m[t], s[t][v]);
-      }
+      for (int v = 0; v < 16; ++v)
+        if ((live >> v) & 1u) m = fmaxf(m, s[v]);
       continue;
     }
-    const uint16_t* vrow = sm.Vt + (size_t)row * vst + kb * 32 + 8 * h;
-    const bf16x8_t va0 = as_bf16x8(*reinterpret_cast<const uint4*>(vrow));
-    const bf16x8_t va1 = as_bf16x8(*reinterpret_cast<const uint4*>(vrow + 16));
+    if (need_mask)
+      block_consume<true, MODE == 2>(sm, kb, lane, live, m, s, la, lb, o);
+    else
+      block_consume<false, MODE == 2>(sm, kb, lane, live, m, s, la, lb, o);
+  }
+  l = la + lb;
+}
+
+// The attention of the wave's tile: uniform fast path or the general pass, then the exact-maximum
+// fallback when the bound reference was too loose for some query.
+template <bool H16>
+__device__ __forceinline__ void attend(const FwdSmem& sm, int NB, int lane, bool uniform_win, uint32_t wave_labels,
+                                       bool wave_single, uint4 qb0, uint4 qb1, int qlab, bool qvalid, float bound,
+                                       float& ref, float& l, f32x16_t& o) {
+  f32x16_t cinit;
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      float p[16];
+  for (int v2 = 0; v2 < 16; ++v2) cinit[v2] = -bound;
+  float m = 0.f;
+  if (uniform_win)
+    pass_uniform<H16>(sm, NB, lane, qb0, qb1, cinit, l, o);
+  else if (wave_labels != 0)
+    pass_general<0, H16>(sm, NB, lane, wave_labels, wave_single, qb0, qb1, qlab, cinit, m, l, o);
+  ref = bound;
+  const bool low = qvalid && !(l + __shfl_xor(l, 32, 64) >= kLowSum);
+  if (__builtin_amdgcn_ballot_w64(low) != 0) {
+    f32x16_t zero;
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const float x = (MODE == 2) ? s[t][v] - m[t] : s[t][v];
-        p[v] = __builtin_amdgcn_exp2f(x);
-      }
-      if (need_mask) {
+    for (int v2 = 0; v2 < 16; ++v2) zero[v2] = 0.f;
+    m = -INFINITY;
+    pass_general<1, H16>(sm, NB, lane, wave_labels, wave_single, qb0, qb1, qlab, zero, m, l, o);
+    m = fmaxf(m, __shfl_xor(m, 32, 64));
+    if (!(m > -INFINITY)) m = 0.f;  // invalid query lanes
+    l = 0.f;
 #pragma unroll
-        for (int v = 0; v < 16; ++v) p[v] = ((live[t] >> v) & 1u) ? p[v] : 0.f;
-      }
-      uint32_t pk[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) pk[e] = pack2(p[2 * e], p[2 * e + 1]);
-      float acc0 = l[t], acc1 = 0.f;
-#pragma unroll
-      for (int e = 0; e < 8; e += 2) {
-        acc0 = add_pair(pk[e], acc0);
-        acc1 = add_pair(pk[e + 1], acc1);
-      }
-      l[t] = acc0 + acc1;
-      const uint4 b0 = make_uint4(pk[0], pk[1], pk[2], pk[3]);
-      const uint4 b1 = make_uint4(pk[4], pk[5], pk[6], pk[7]);
-      o[t] = mfma32x32x16(va0, as_bf16x8(b0), o[t]);
-      o[t] = mfma32x32x16(va1, as_bf16x8(b1), o[t]);
-    }
+    for (int v2 = 0; v2 < 16; ++v2) o[v2] = 0.f;
+    pass_general<2, H16>(sm, NB, lane, wave_labels, wave_single, qb0, qb1, qlab, zero, m, l, o);
+    ref = m;
   }
 }
 
-// Stage the rotated K~ rows of the window into LDS in fp16 (h16) or bf16; returns this thread's
-// max |k~|^2 over the keys it staged (float32 values before rounding).
-__device__ inline float stage_k_rows(const FwdSmem& sm, const uint16_t* __restrict__ k, const Geom& g,
-                                     const WinHead& w, int NP, int tid, int nt, bool h16) {
-  constexpr int D = 32;
-  const int M = g.M, N = g.N;
-  const int64_t rowstride = (int64_t)g.heads * D;
+// Rotated K~ rows of the staged items (raw bf16 loads in kraw) into LDS in fp16 (h16) or bf16;
+// returns this thread's max |k|^2 (rotation keeps norms).
+template <int MAXIT>
+__device__ __forceinline__ float stage_k(const FwdSmem& sm, const uint4 (&kraw)[MAXIT], int M, int NP, int tid,
+                                         int nt, bool h16) {
+  const int N = M * M;
   float kmax2 = 0.f;
-  for (int it = tid; it < NP * 4; it += nt) {
+#pragma unroll
+  for (int i = 0; i < MAXIT; ++i) {
+    const int it = tid + i * nt;
+    if (it >= NP * 4) break;  // uniform across a wave: NP * 4 is a multiple of 64
     const int key = it >> 2;
     const int part = it & 3;
     uint4 kr = make_uint4(0, 0, 0, 0);
     float ss = 0.f;
     if (key < N) {
       const int r = key / M, c = key - (key / M) * M;
-      const int64_t off = token_index(g, w.b, w.wy, w.wx, r, c) * rowstride + w.h * D + part * 8;
       float x[8];
-      unpack8(*reinterpret_cast<const uint4*>(k + off), x);
+      unpack8(kraw[i], x);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ss = __builtin_fmaf(x[e], x[e], ss);
       const int axis = part >> 1;
       rotate8(x, sm.sn, sm.cs, axis, M, axis ? c : r, (part & 1) * 4);
       kr = pack8_op(x, h16);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) ss = __builtin_fmaf(x[e], x[e], ss);
     }
     *reinterpret_cast<uint4*>(sm.K + (size_t)key * kKStride + part * 8) = kr;
     ss += __shfl_xor(ss, 1, 64);
@@ -167,41 +232,30 @@ __device__ inline float stage_k_rows(const FwdSmem& sm, const uint16_t* __restri
   return kmax2;
 }
 
-// Main pass with the bound as softmax reference, then the exact-maximum fallback if needed.
-template <bool H16>
-__device__ __forceinline__ void attend(const FwdSmem& sm, int NB, int lane, uint32_t wave_labels, bool wave_single,
-                                       const uint4 (&qb)[2][2], const int (&qlab)[2], const bool (&qvalid)[2],
-                                       float bound, float (&ref)[2], float (&l)[2], f32x16_t (&o)[2]) {
-  f32x16_t cinit;
+// Global loads of the thread's K and V items (16 bytes each), issued together.
+template <int MAXIT>
+__device__ __forceinline__ void load_kv(const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, const Geom& g,
+                                        const WinHead& w, int M, int NP, int tid, int nt, bool with_v,
+                                        uint4 (&kraw)[MAXIT], uint4 (&vraw)[MAXIT]) {
+  const int N = M * M;
+  const int64_t rowstride = (int64_t)g.heads * 32;
 #pragma unroll
-  for (int v2 = 0; v2 < 16; ++v2) cinit[v2] = -bound;
-  float m[2] = {-bound, -bound};
-  if (wave_labels != 0) key_pass<0, H16>(sm, NB, lane, wave_labels, wave_single, qb, qlab, cinit, m, l, o);
-  ref[0] = ref[1] = bound;
-  bool low = false;
-#pragma unroll
-  for (int t = 0; t < 2; ++t) low |= qvalid[t] && !(l[t] + __shfl_xor(l[t], 32, 64) >= kLowSum);
-  if (__builtin_amdgcn_ballot_w64(low) != 0) {
-    f32x16_t zero;
-#pragma unroll
-    for (int v2 = 0; v2 < 16; ++v2) zero[v2] = 0.f;
-    m[0] = m[1] = -INFINITY;
-    key_pass<1, H16>(sm, NB, lane, wave_labels, wave_single, qb, qlab, zero, m, l, o);
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      m[t] = fmaxf(m[t], __shfl_xor(m[t], 32, 64));
-      if (!(m[t] > -INFINITY)) m[t] = 0.f;  // invalid query lanes
-      l[t] = 0.f;
-#pragma unroll
-      for (int v2 = 0; v2 < 16; ++v2) o[t][v2] = 0.f;
+  for (int i = 0; i < MAXIT; ++i) {
+    const int it = tid + i * nt;
+    const int key = it >> 2;
+    kraw[i] = vraw[i] = make_uint4(0, 0, 0, 0);
+    if (it < NP * 4 && key < N) {
+      const int r = key / M, c = key - (key / M) * M;
+      const int64_t off = tok_of(g, w, M, r, c) * rowstride + w.h * 32 + (it & 3) * 8;
+      kraw[i] = *reinterpret_cast<const uint4*>(k + off);
+      if (with_v) vraw[i] = *reinterpret_cast<const uint4*>(v + off);
     }
-    key_pass<2, H16>(sm, NB, lane, wave_labels, wave_single, qb, qlab, zero, m, l, o);
-    ref[0] = m[0];
-    ref[1] = m[1];
   }
 }
 
-template <int NWAVES>
+// NWAVES waves of one 32-query tile each.  MT: compile-time window size (0 = g.M at run time).
+// NPMAX: the largest padded window this configuration serves.
+template <int NWAVES, int MT, int NPMAX>
 __global__ __launch_bounds__(NWAVES * 64) void fwd_mfma_kernel(const uint16_t* __restrict__ q,
                                                                const uint16_t* __restrict__ k,
                                                                const uint16_t* __restrict__ v,
@@ -212,8 +266,10 @@ __global__ __launch_bounds__(NWAVES * 64) void fwd_mfma_kernel(const uint16_t* _
   extern __shared__ __align__(16) unsigned char smem_raw[];
   constexpr int D = 32;
   constexpr int NT = NWAVES * 64;
-  const int M = g.M;
-  const int N = g.N;
+  constexpr int MAXIT = (NPMAX * 4 + NT - 1) / NT;
+  static_assert(NWAVES <= kMaxWaves, "too many waves");
+  const int M = MT > 0 ? MT : g.M;
+  const int N = M * M;
   const int NB = NP / 32;
   const FwdSmem sm = carve(smem_raw, NP, M);
 
@@ -227,7 +283,21 @@ __global__ __launch_bounds__(NWAVES * 64) void fwd_mfma_kernel(const uint16_t* _
   const int h = lane >> 5;
   const int col = lane & 31;
 
-  // 1. RoPE sin/cos table and key labels
+  // 0. every global load of the thread first (K and V items, the query), so they overlap
+  uint4 kraw[MAXIT], vraw[MAXIT];
+  load_kv<MAXIT>(k, v, g, w, M, NP, tid, NT, true, kraw, vraw);
+  const int qi = qblock * NT / 2 + wave * 32 + col;
+  const bool qvalid = qi < N;
+  const int qr = qvalid ? qi / M : 0, qc = qvalid ? qi - (qi / M) * M : 0;
+  const int64_t qtok = qvalid ? tok_of(g, w, M, qr, qc) : 0;
+  uint4 qraw0 = make_uint4(0, 0, 0, 0), qraw1 = qraw0;
+  if (qvalid) {
+    const int64_t off = qtok * rowstride + w.h * D;
+    qraw0 = *reinterpret_cast<const uint4*>(q + off + 8 * h);
+    qraw1 = *reinterpret_cast<const uint4*>(q + off + 16 + 8 * h);
+  }
+
+  // 1. RoPE sin/cos table and key labels (while the loads are in flight)
   for (int i = tid; i < 2 * M * 8; i += NT) {
     const int axis = i / (M * 8);
     const int p = (i / 8) % M;
@@ -245,26 +315,13 @@ __global__ __launch_bounds__(NWAVES * 64) void fwd_mfma_kernel(const uint16_t* _
   }
   __syncthreads();
 
-  // 2. stage K~ (rotated, fp16) and V^T (bf16, keys in vt_pos order); track max |k~|^2
-  float kmax2 = stage_k_rows(sm, k, g, w, NP, tid, NT, true);
-  for (int it = tid; it < NP * 4; it += NT) {
-    const int key = it >> 2;
-    const int part = it & 3;
-    uint4 vr = make_uint4(0, 0, 0, 0);
-    if (key < N) {
-      const int r = key / M, c = key - (key / M) * M;
-      const int64_t off = token_index(g, w.b, w.wy, w.wx, r, c) * rowstride + w.h * D + part * 8;
-      vr = *reinterpret_cast<const uint4*>(v + off);
-    }
-    const int pos = vt_pos(key);
-    const uint32_t vw[4] = {vr.x, vr.y, vr.z, vr.w};
+  // 2. K~ rows (rotated, fp16), V rows, block label summaries, norms
+  float kmax2 = stage_k<MAXIT>(sm, kraw, M, NP, tid, NT, true);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      sm.Vt[(size_t)(part * 8 + 2 * e) * vt_stride(NP) + pos] = (uint16_t)(vw[e] & 0xffffu);
-      sm.Vt[(size_t)(part * 8 + 2 * e + 1) * vt_stride(NP) + pos] = (uint16_t)(vw[e] >> 16);
-    }
+  for (int i = 0; i < MAXIT; ++i) {
+    const int it = tid + i * NT;
+    if (it < NP * 4) *reinterpret_cast<uint4*>(sm.V + (size_t)(it >> 2) * 32 + (it & 3) * 8) = vraw[i];
   }
-  // block label summaries
   for (int b = tid; b < NB; b += NT) {
     uint32_t bits = 0, full = 1;
     for (int j = 0; j < 32; ++j) {
@@ -276,129 +333,112 @@ __global__ __launch_bounds__(NWAVES * 64) void fwd_mfma_kernel(const uint16_t* _
     }
     sm.blk[b] = bits | (full << 9);
   }
-
-  // 3. the wave's queries (two 32-query tiles): raw loads, labels and |q^| (rotation keeps norms)
   const float qscale = kLog2e * 0.17677669529663687f;  // log2(e) / sqrt(32)
-  uint4 qraw[2][2];
-  int qlab[2], qr[2], qc[2];
-  bool qvalid[2];
-  int64_t qtok[2];
-  float qn2max = 0.f;
+  float qn2 = 0.f;
+  {
+    float x[8], y[8];
+    unpack8(qraw0, x);
+    unpack8(qraw1, y);
 #pragma unroll
-  for (int t = 0; t < 2; ++t) {
-    const int qi = qblock * NT + wave * 64 + t * 32 + col;
-    qvalid[t] = qi < N;
-    qlab[t] = 0xff;
-    qtok[t] = 0;
-    qr[t] = qc[t] = 0;
-    qraw[t][0] = qraw[t][1] = make_uint4(0, 0, 0, 0);
-    float n2 = 0.f;
-    if (qvalid[t]) {
-      qr[t] = qi / M;
-      qc[t] = qi - qr[t] * M;
-      qtok[t] = token_index(g, w.b, w.wy, w.wx, qr[t], qc[t]);
-      qlab[t] = token_label(g, w.wy, w.wx, qr[t], qc[t]);
-      const int64_t off = qtok[t] * rowstride + w.h * D;
-      qraw[t][0] = *reinterpret_cast<const uint4*>(q + off + 8 * h);
-      qraw[t][1] = *reinterpret_cast<const uint4*>(q + off + 16 + 8 * h);
-      float x[8], y[8];
-      unpack8(qraw[t][0], x);
-      unpack8(qraw[t][1], y);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) n2 = __builtin_fmaf(x[e], x[e], __builtin_fmaf(y[e], y[e], n2));
-    }
-    n2 += __shfl_xor(n2, 32, 64);
-    qn2max = fmaxf(qn2max, n2);
+    for (int e = 0; e < 8; ++e) qn2 = __builtin_fmaf(x[e], x[e], __builtin_fmaf(y[e], y[e], qn2));
   }
-  qn2max = wave_max(qn2max) * (qscale * qscale);
+  qn2 += __shfl_xor(qn2, 32, 64);
+  const float qn2max = wave_max(qn2) * (qscale * qscale);
   kmax2 = wave_max(kmax2);
   if (lane == 0) {
     sm.red[wave] = kmax2;
-    sm.red[8 + wave] = qn2max;
+    sm.red[kMaxWaves + wave] = qn2max;
   }
   __syncthreads();
   float kmax2_all = 0.f, qmax2_all = 0.f;
 #pragma unroll
   for (int i = 0; i < NWAVES; ++i) {
     kmax2_all = fmaxf(kmax2_all, sm.red[i]);
-    qmax2_all = fmaxf(qmax2_all, sm.red[8 + i]);
+    qmax2_all = fmaxf(qmax2_all, sm.red[kMaxWaves + i]);
   }
   const float kmax = sqrtf(kmax2_all);
   // fp16 score operands unless some |k~| or |q^| (hence some component) could leave fp16 range
   const bool h16 = kmax < kF16Limit && sqrtf(qmax2_all) < kF16Limit;
   if (!h16) {
+    load_kv<MAXIT>(k, v, g, w, M, NP, tid, NT, false, kraw, vraw);
     __syncthreads();
-    stage_k_rows(sm, k, g, w, NP, tid, NT, false);
+    stage_k<MAXIT>(sm, kraw, M, NP, tid, NT, false);
     __syncthreads();
   }
 
-  uint4 qb[2][2];
-#pragma unroll
-  for (int t = 0; t < 2; ++t) {
+  // 3. the wave's query operands (rotated, scaled by log2(e)/sqrt(d)), reference bound, labels
+  uint4 qb0, qb1;
+  {
     float x[8], y[8];
-    unpack8(qraw[t][0], x);
-    unpack8(qraw[t][1], y);
-    rotate8(x, sm.sn, sm.cs, 0, M, qr[t], 4 * h);
-    rotate8(y, sm.sn, sm.cs, 1, M, qc[t], 4 * h);
+    unpack8(qraw0, x);
+    unpack8(qraw1, y);
+    rotate8(x, sm.sn, sm.cs, 0, M, qr, 4 * h);
+    rotate8(y, sm.sn, sm.cs, 1, M, qc, 4 * h);
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       x[e] *= qscale;
       y[e] *= qscale;
     }
-    qb[t][0] = pack8_op(x, h16);
-    qb[t][1] = pack8_op(y, h16);
+    qb0 = pack8_op(x, h16);
+    qb1 = pack8_op(y, h16);
   }
   const float bound = sqrtf(qn2max) * kmax;  // >= every score of this wave (log2 units)
-  uint32_t wl = 0;
-#pragma unroll
-  for (int t = 0; t < 2; ++t)
-    if (qvalid[t]) wl |= 1u << qlab[t];
-  const uint32_t wave_labels = wave_or(wl);
+  const int qlab = qvalid ? token_label(g, w.wy, w.wx, qr, qc) : 0xff;
+  const uint32_t wave_labels = uniform(wave_or(qvalid ? 1u << qlab : 0u));
   const bool wave_single = __builtin_popcount(wave_labels) == 1;
+  // window summary over its blocks: one label everywhere and every block whole
+  uint32_t wb = 0xffffffffu, wor = 0;
+  for (int b = lane; b < NB; b += 64) {
+    const uint32_t info = sm.blk[b];
+    wb &= info;
+    wor |= info & 0x1ffu;
+  }
+#pragma unroll
+  for (int o2 = 32; o2 > 0; o2 >>= 1) {
+    wb &= (uint32_t)__shfl_xor((int)wb, o2, 64);
+    wor |= (uint32_t)__shfl_xor((int)wor, o2, 64);
+  }
+  const bool uniform_win =
+      uniform((int)(((wb >> 9) & 1u) && __builtin_popcount(wor) == 1 && wor == wave_labels && (NB % 2) == 0)) != 0;
 
-  f32x16_t o[2];
-  float l[2] = {0.f, 0.f};
-  float ref[2];
+  f32x16_t o;
+  float l = 0.f, ref;
 #pragma unroll
-  for (int t = 0; t < 2; ++t)
-#pragma unroll
-    for (int v2 = 0; v2 < 16; ++v2) o[t][v2] = 0.f;
+  for (int v2 = 0; v2 < 16; ++v2) o[v2] = 0.f;
   if (h16)
-    attend<true>(sm, NB, lane, wave_labels, wave_single, qb, qlab, qvalid, bound, ref, l, o);
+    attend<true>(sm, NB, lane, uniform_win, wave_labels, wave_single, qb0, qb1, qlab, qvalid, bound, ref, l, o);
   else
-    attend<false>(sm, NB, lane, wave_labels, wave_single, qb, qlab, qvalid, bound, ref, l, o);
+    attend<false>(sm, NB, lane, uniform_win, wave_labels, wave_single, qb0, qb1, qlab, qvalid, bound, ref, l, o);
 
   // 4. epilogue: O = O^T / l (lane: query col, channels 8g + 4h + j), LSE = (ref + log2 l) ln 2
-#pragma unroll
-  for (int t = 0; t < 2; ++t) {
-    const float lt = l[t] + __shfl_xor(l[t], 32, 64);
-    if (!qvalid[t]) continue;
+  const float lt = l + __shfl_xor(l, 32, 64);
+  if (qvalid) {
     const float inv = 1.f / lt;
-    uint16_t* dst = out + qtok[t] * rowstride + w.h * D + 4 * h;
+    uint16_t* dst = out + qtok * rowstride + w.h * D + 4 * h;
 #pragma unroll
     for (int gq = 0; gq < 4; ++gq) {
       uint2 pr;
-      pr.x = pack2(o[t][4 * gq] * inv, o[t][4 * gq + 1] * inv);
-      pr.y = pack2(o[t][4 * gq + 2] * inv, o[t][4 * gq + 3] * inv);
+      pr.x = pack2(o[4 * gq] * inv, o[4 * gq + 1] * inv);
+      pr.y = pack2(o[4 * gq + 2] * inv, o[4 * gq + 3] * inv);
       *reinterpret_cast<uint2*>(dst + 8 * gq) = pr;
     }
-    if (lse && h == 0) lse[qtok[t] * g.heads + w.h] = (ref[t] + __log2f(lt)) * kLn2;
+    if (lse && h == 0) lse[qtok * g.heads + w.h] = (ref + __log2f(lt)) * kLn2;
   }
 }
 
-template <int NWAVES>
+template <int NWAVES, int MT, int NPMAX>
 hipError_t launch_nw(const FwdArgs& a, hipStream_t st) {
   const Geom& g = a.g;
   const int NP = (g.N + 31) / 32 * 32;
-  const int nqb = (g.N + NWAVES * 64 - 1) / (NWAVES * 64);
+  const int nqb = (g.N + NWAVES * 32 - 1) / (NWAVES * 32);
   const size_t smem = fwd_smem_bytes(NP, g.M);
   static std::once_flag once;
   std::call_once(once, [] {
-    (void)hipFuncSetAttribute((const void*)fwd_mfma_kernel<NWAVES>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                              160 * 1024);
+    (void)hipFuncSetAttribute((const void*)fwd_mfma_kernel<NWAVES, MT, NPMAX>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
   });
   const int64_t blocks = g.B * g.nH * g.nW * g.heads * nqb;
-  hipLaunchKernelGGL(fwd_mfma_kernel<NWAVES>, dim3((unsigned)blocks), dim3(NWAVES * 64), smem, st,
+  hipLaunchKernelGGL((fwd_mfma_kernel<NWAVES, MT, NPMAX>), dim3((unsigned)blocks), dim3(NWAVES * 64), smem, st,
                      (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, a.th_row, a.th_col,
                      (uint16_t*)a.out, a.lse, g, nqb, NP);
   return hipGetLastError();
@@ -408,10 +448,12 @@ hipError_t launch_nw(const FwdArgs& a, hipStream_t st) {
 
 hipError_t launch_fwd_mfma(const FwdArgs& a, hipStream_t st) {
   const int N = a.g.N;
-  if (N <= 64) return launch_nw<1>(a, st);
-  if (N <= 128) return launch_nw<2>(a, st);
-  if (N <= 256) return launch_nw<4>(a, st);
-  return launch_nw<8>(a, st);
+  if (a.g.M == 32) return launch_nw<16, 32, 1024>(a, st);
+  if (a.g.M == 8) return launch_nw<2, 8, 64>(a, st);
+  if (N <= 64) return launch_nw<2, 0, 64>(a, st);
+  if (N <= 128) return launch_nw<4, 0, 128>(a, st);
+  if (N <= 256) return launch_nw<8, 0, 256>(a, st);
+  return launch_nw<16, 0, 1024>(a, st);
 }
 
 }  // namespace fsw

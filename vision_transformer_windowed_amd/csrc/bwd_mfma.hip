@@ -43,7 +43,7 @@ constexpr float kQScale = kLog2e * 0.17677669529663687f;  // log2(e) / sqrt(32)
 __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 __device__ __forceinline__ uint32_t uniform(uint32_t x) { return (uint32_t)__builtin_amdgcn_readfirstlane((int)x); }
 
-__host__ __device__ inline int chunk_len(int NP) { return NP < kCh ? NP : kCh; }
+__host__ __device__ constexpr int chunk_len(int NP) { return NP < kCh ? NP : kCh; }
 
 // Power of two 2^k (k clamped to [-100, 100]) with 2^k * bound <= 2^14 (1 when bound is 0 or not
 // finite).
@@ -186,7 +186,7 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const uint16_t* __restrict
                                                       const uint16_t* __restrict__ k, float* __restrict__ delta,
                                                       float* __restrict__ scal, Geom g) {
   __shared__ float red[4][4];
-  const int64_t wh = blockIdx.x;
+  const int64_t wh = xcd_order(blockIdx.x, gridDim.x);
   const WinHead w = decode_winhead(g, wh);
   const int tid = threadIdx.x;
   const int64_t rowstride = (int64_t)g.heads * 32;
@@ -239,8 +239,8 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const uint16_t* __restrict
   if (tid < 4) scal[wh * 4 + tid] = fmaxf(fmaxf(red[tid][0], red[tid][1]), fmaxf(red[tid][2], red[tid][3]));
 }
 
-// Chunk staging helper shared by both kernels: label of chunk token n and its block summary bit
-// (bit L for label L, bit 10 for a position past the window) OR-ed into blk[n / 32].
+// Label of chunk token n (0xff past the window) and its block summary bit (bit L for label L,
+// bit 10 for a position past the window) OR-ed into blk[n / 32].
 __device__ __forceinline__ uint8_t chunk_label(const Geom& g, const WinHead& w, int M, int tn, uint32_t* blk,
                                                int n) {
   const int N = M * M;
@@ -250,22 +250,31 @@ __device__ __forceinline__ uint8_t chunk_label(const Geom& g, const WinHead& w, 
   return lb;
 }
 
+// Both main kernels stream the window's other side through LDS in chunks of up to kCh tokens:
+//   load (global -> registers, chunk c + 1)  |  compute on chunk c from LDS
+//   barrier; registers -> LDS (RoPE, scaling, operand format); barrier
+// Block summaries (which labels a 32-token block holds) are double-buffered, so the buffer that
+// the next chunk's stores OR into was cleared during the previous chunk's stores.
+// Tile rows use the swizzled 64-byte layout (srow), so row and transposed operand reads are free
+// of LDS bank conflicts, and every operand address is a per-lane base plus a constant.
+
+__host__ __device__ inline int items_per_thread(int nt) { return (kCh * 4 + nt - 1) / nt; }
+
 // ---------------------------------------------------------------------------------------- dQ
 
-template <int NW>
 struct DqSmem {
-  uint16_t* K;   // [CH][kKStride] rotated K~ (operand format)
-  uint16_t* V;   // [CH][kKStride] bf16 V
+  uint16_t* K;    // [CH] swizzled rows: rotated K~ (operand format)
+  uint16_t* V;    // [CH] swizzled rows: bf16 V
   float* sn;
   float* cs;
-  float* red;    // [NW * 16]
-  uint32_t* blk; // [kCh / 32]
-  uint8_t* lab;  // [kCh]
+  float* red;     // [NW * 16]
+  uint32_t* blk;  // [2][kCh / 32]
+  uint8_t* lab;   // [kCh]
 };
 template <int NW>
 __host__ __device__ inline size_t dq_smem(int NP, int M) {
   const int CH = chunk_len(NP);
-  return (size_t)CH * kKStride * 2 * 2 + (size_t)2 * 2 * M * 8 * 4 + NW * 16 * 4 + (kCh / 32) * 4 + kCh;
+  return (size_t)CH * 32 * 2 * 2 + (size_t)2 * 2 * M * 8 * 4 + NW * 16 * 4 + 2 * (kCh / 32) * 4 + kCh;
 }
 
 template <int NW, int MT, bool H16>
@@ -273,10 +282,11 @@ __device__ inline void dq_body(const uint16_t* __restrict__ q, const uint16_t* _
                                const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout,
                                const float* __restrict__ lse, const float* __restrict__ delta,
                                const float* __restrict__ scal, uint16_t* __restrict__ dq,
-                               float* __restrict__ partials, const Geom& g, int nb, int NP, const DqSmem<NW>& sm,
+                               float* __restrict__ partials, const Geom& g, int nb, int NP, const DqSmem& sm,
                                const WinHead& w, int64_t wh, int qblock) {
   constexpr int D = 32;
   constexpr int NT = NW * 64;
+  constexpr int IPT = (kCh * 4 + NT - 1) / NT;
   const int M = MT > 0 ? MT : g.M;
   const int N = M * M;
   const int CH = chunk_len(NP);
@@ -284,6 +294,24 @@ __device__ inline void dq_body(const uint16_t* __restrict__ q, const uint16_t* _
   const int h = lane >> 5, col = lane & 31;
   const int64_t rowstride = (int64_t)g.heads * D;
   const float ds_scale = pow2_scale(64.f * scal[wh * 4] * scal[wh * 4 + 1]);
+
+  uint4 ik[IPT], iv[IPT];
+  auto load_chunk = [&](int c0) {
+#pragma unroll
+    for (int i = 0; i < IPT; ++i) {
+      const int it = tid + i * NT;
+      const int kn = c0 + (it >> 2);
+      ik[i] = make_uint4(0, 0, 0, 0);
+      iv[i] = ik[i];
+      if (it < CH * 4 && kn < N) {
+        const int r_ = kn / M, c_ = kn - (kn / M) * M;
+        const int64_t off = token_index(g, w.b, w.wy, w.wx, r_, c_) * rowstride + w.h * D + (it & 3) * 8;
+        ik[i] = *reinterpret_cast<const uint4*>(k + off);
+        iv[i] = *reinterpret_cast<const uint4*>(v + off);
+      }
+    }
+  };
+  load_chunk(0);
 
   // the lane's query: Q^ operands, tau * dO as bf16 B operands, -LSE and -tau Delta
   const int qi = qblock * NW * 32 + wave * 32 + col;
@@ -295,13 +323,16 @@ __device__ inline void dq_body(const uint16_t* __restrict__ q, const uint16_t* _
   float lse2 = 0.f, del = 0.f;
   if (valid) {
     const int64_t off = tok * rowstride + w.h * D;
-    qb0 = rotated_part<H16>(*reinterpret_cast<const uint4*>(q + off + 8 * h), sm.sn, sm.cs, M, r, c, h, kQScale);
-    qb1 = rotated_part<H16>(*reinterpret_cast<const uint4*>(q + off + 16 + 8 * h), sm.sn, sm.cs, M, r, c, 2 + h,
-                            kQScale);
-    gb0 = scaled_part<false>(*reinterpret_cast<const uint4*>(dout + off + 8 * h), ds_scale);
-    gb1 = scaled_part<false>(*reinterpret_cast<const uint4*>(dout + off + 16 + 8 * h), ds_scale);
+    const uint4 q0 = *reinterpret_cast<const uint4*>(q + off + 8 * h);
+    const uint4 q1 = *reinterpret_cast<const uint4*>(q + off + 16 + 8 * h);
+    const uint4 g0 = *reinterpret_cast<const uint4*>(dout + off + 8 * h);
+    const uint4 g1 = *reinterpret_cast<const uint4*>(dout + off + 16 + 8 * h);
     lse2 = lse[tok * g.heads + w.h] * kLog2e;
     del = delta[tok * g.heads + w.h] * ds_scale;
+    qb0 = rotated_part<H16>(q0, sm.sn, sm.cs, M, r, c, h, kQScale);
+    qb1 = rotated_part<H16>(q1, sm.sn, sm.cs, M, r, c, 2 + h, kQScale);
+    gb0 = scaled_part<false>(g0, ds_scale);
+    gb1 = scaled_part<false>(g1, ds_scale);
   }
   f32x16_t cL, cD, acc;
 #pragma unroll
@@ -312,56 +343,70 @@ __device__ inline void dq_body(const uint16_t* __restrict__ q, const uint16_t* _
   }
   const uint32_t wave_labels = uniform(wave_or(valid ? (1u << qlab) : 0u));
   const bool wave_single = __builtin_popcount(wave_labels) == 1;
+  int tlo, thi;
+  srow_tr_offsets(lane, tlo, thi);
+  const int ro0 = srow(col, h), ro1 = srow(col, 2 + h);
 
-  for (int c0 = 0; c0 < NP; c0 += CH) {
+  int buf = 0;
+  for (int c0 = 0; c0 < NP; c0 += CH, buf ^= 1) {
     __syncthreads();
-    if (tid < kCh / 32) sm.blk[tid] = 0;
-    __syncthreads();
-    for (int it = tid; it < CH * 4; it += NT) {
-      const int n = it >> 2, part = it & 3;
-      const int kn = c0 + n;
-      uint4 kr = make_uint4(0, 0, 0, 0), vr = kr;
-      if (kn < N) {
-        const int kr_ = kn / M, kc_ = kn - (kn / M) * M;
-        const int64_t off = token_index(g, w.b, w.wy, w.wx, kr_, kc_) * rowstride + w.h * D + part * 8;
-        const uint4 raw = *reinterpret_cast<const uint4*>(k + off);
-        vr = *reinterpret_cast<const uint4*>(v + off);
-        kr = rotated_part<H16>(raw, sm.sn, sm.cs, M, kr_, kc_, part, 1.f);
+#pragma unroll
+    for (int i = 0; i < IPT; ++i) {
+      const int it = tid + i * NT;
+      if (it < CH * 4) {
+        const int n = it >> 2, part = it & 3, kn = c0 + n;
+        uint4 kr = make_uint4(0, 0, 0, 0);
+        if (kn < N) kr = rotated_part<H16>(ik[i], sm.sn, sm.cs, M, kn / M, kn - (kn / M) * M, part, 1.f);
+        *reinterpret_cast<uint4*>(sm.K + srow(n, part)) = kr;
+        *reinterpret_cast<uint4*>(sm.V + srow(n, part)) = iv[i];
+        if (part == 0) sm.lab[n] = chunk_label(g, w, M, kn, sm.blk + buf * (kCh / 32), n);
       }
-      *reinterpret_cast<uint4*>(sm.K + n * kKStride + part * 8) = kr;
-      *reinterpret_cast<uint4*>(sm.V + n * kKStride + part * 8) = vr;
-      if (part == 0) sm.lab[n] = chunk_label(g, w, M, kn, sm.blk, n);
     }
+    if (tid < kCh / 32) sm.blk[(buf ^ 1) * (kCh / 32) + tid] = 0;
     __syncthreads();
+    if (c0 + CH < NP) load_chunk(c0 + CH);
     if (wave_labels == 0) continue;
-    const int nblk = min(CH, NP - c0) / 32;
-    for (int kb = 0; kb < nblk; ++kb) {
-      const uint32_t info = uniform(sm.blk[kb]);
+    const uint4 bw = *reinterpret_cast<const uint4*>(sm.blk + buf * (kCh / 32));
+    const uint32_t info4[4] = {uniform(bw.x), uniform(bw.y), uniform(bw.z), uniform(bw.w)};
+    const int nblk = min(CH, NP - c0) >> 5;
+#pragma unroll
+    for (int kb = 0; kb < kCh / 32; ++kb) {
+      if (kb >= nblk) break;
+      const uint32_t info = info4[kb];
       const uint32_t bl = info & 0x1ffu;
       if ((bl & wave_labels) == 0) continue;
       const bool need_mask = ((info >> 10) & 1u) || !wave_single || bl != wave_labels;
-      const uint16_t* krow = sm.K + (kb * 32 + col) * kKStride + 8 * h;
-      const uint16_t* vrow = sm.V + (kb * 32 + col) * kKStride + 8 * h;
-      f32x16_t s = mfma_op<H16>(*reinterpret_cast<const uint4*>(krow), qb0, cL);
-      s = mfma_op<H16>(*reinterpret_cast<const uint4*>(krow + 16), qb1, s);
-      f32x16_t dp = mfma_op<false>(*reinterpret_cast<const uint4*>(vrow), gb0, cD);
-      dp = mfma_op<false>(*reinterpret_cast<const uint4*>(vrow + 16), gb1, dp);
-      float ds[16];
+      const uint16_t* Kb = sm.K + kb * 1024;
+      const uint16_t* Vb = sm.V + kb * 1024;
+      f32x16_t s = mfma_op<H16>(*reinterpret_cast<const uint4*>(Kb + ro0), qb0, cL);
+      s = mfma_op<H16>(*reinterpret_cast<const uint4*>(Kb + ro1), qb1, s);
+      f32x16_t dp = mfma_op<false>(*reinterpret_cast<const uint4*>(Vb + ro0), gb0, cD);
+      dp = mfma_op<false>(*reinterpret_cast<const uint4*>(Vb + ro1), gb1, dp);
+      float p[16];
       if (need_mask) {
         const uint32_t live = live_bits(sm.lab, kb, h, qlab);
 #pragma unroll
-        for (int e = 0; e < 16; ++e) ds[e] = ((live >> e) & 1u) ? __builtin_amdgcn_exp2f(s[e]) * dp[e] : 0.f;
+        for (int e = 0; e < 16; ++e) p[e] = ((live >> e) & 1u) ? __builtin_amdgcn_exp2f(s[e]) : 0.f;
       } else {
 #pragma unroll
-        for (int e = 0; e < 16; ++e) ds[e] = __builtin_amdgcn_exp2f(s[e]) * dp[e];
+        for (int e = 0; e < 16; ++e) p[e] = __builtin_amdgcn_exp2f(s[e]);
       }
       uint32_t pk[8];
+      if constexpr (H16) {
+        // tau dS = P * tau (dP - Delta) as a packed fp16 product of the fp16 operands
 #pragma unroll
-      for (int e = 0; e < 8; ++e) pk[e] = pack_op2<H16>(ds[2 * e], ds[2 * e + 1]);
-      const uint4 kt0 = tr_operand(sm.K, kKStride, kb * 32, lane);
-      const uint4 kt1 = tr_operand(sm.K, kKStride, kb * 32 + 16, lane);
-      acc = mfma_op<H16>(kt0, make_uint4(pk[0], pk[1], pk[2], pk[3]), acc);
-      acc = mfma_op<H16>(kt1, make_uint4(pk[4], pk[5], pk[6], pk[7]), acc);
+        for (int e = 0; e < 8; ++e) {
+          const f16x2_t a = __builtin_bit_cast(f16x2_t, pack2h(p[2 * e], p[2 * e + 1]));
+          const f16x2_t b = __builtin_bit_cast(f16x2_t, pack2h(dp[2 * e], dp[2 * e + 1]));
+          pk[e] = __builtin_bit_cast(uint32_t, a * b);
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pk[e] = pack2(p[2 * e] * dp[2 * e], p[2 * e + 1] * dp[2 * e + 1]);
+      }
+      acc = mfma_op<H16>(tr_operand_at(Kb, tlo, thi), make_uint4(pk[0], pk[1], pk[2], pk[3]), acc);
+      acc = mfma_op<H16>(tr_operand_at(Kb + 512, tlo, thi), make_uint4(pk[4], pk[5], pk[6], pk[7]), acc);
+      __builtin_amdgcn_sched_barrier(0);  // keep blocks apart: bounded register pressure
     }
   }
 
@@ -377,53 +422,53 @@ __device__ inline void dq_body(const uint16_t* __restrict__ q, const uint16_t* _
 }
 
 template <int NW, int MT>
-__global__ __launch_bounds__(NW * 64) void bwd_dq_mfma_kernel(
+__global__ __launch_bounds__(NW * 64, NW >= 8 ? 4 : 2) void bwd_dq_mfma_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ delta,
     const float* __restrict__ scal, const float* __restrict__ th_row, const float* __restrict__ th_col,
     uint16_t* __restrict__ dq, float* __restrict__ partials, Geom g, int nb, int NP) {
   extern __shared__ __align__(16) unsigned char smem_raw[];
+  if constexpr (MT > 0) NP = (MT * MT + 31) / 32 * 32;  // compile-time chunk geometry
   const int M = MT > 0 ? MT : g.M;
   const int CH = chunk_len(NP);
-  DqSmem<NW> sm;
+  DqSmem sm;
   sm.K = reinterpret_cast<uint16_t*>(smem_raw);
-  sm.V = sm.K + CH * kKStride;
-  sm.sn = reinterpret_cast<float*>(sm.V + CH * kKStride);
+  sm.V = sm.K + CH * 32;
+  sm.sn = reinterpret_cast<float*>(sm.V + CH * 32);
   sm.cs = sm.sn + 2 * M * 8;
   sm.red = sm.cs + 2 * M * 8;
   sm.blk = reinterpret_cast<uint32_t*>(sm.red + NW * 16);
-  sm.lab = reinterpret_cast<uint8_t*>(sm.blk + kCh / 32);
-  const int64_t blk = blockIdx.x;
-  const int64_t wh = blk / nb;
+  sm.lab = reinterpret_cast<uint8_t*>(sm.blk + 2 * (kCh / 32));
+  const int64_t lb = xcd_order(blockIdx.x, gridDim.x);
+  const int64_t wh = lb / nb;
   const WinHead w = decode_winhead(g, wh);
+  if (threadIdx.x < 2 * (kCh / 32)) sm.blk[threadIdx.x] = 0;
   fill_table(sm.sn, sm.cs, th_row, th_col, w.h, M, threadIdx.x, NW * 64);
   __syncthreads();
   if (window_h16(scal, wh))
-    dq_body<NW, MT, true>(q, k, v, dout, lse, delta, scal, dq, partials, g, nb, NP, sm, w, wh, (int)(blk % nb));
+    dq_body<NW, MT, true>(q, k, v, dout, lse, delta, scal, dq, partials, g, nb, NP, sm, w, wh, (int)(lb % nb));
   else
-    dq_body<NW, MT, false>(q, k, v, dout, lse, delta, scal, dq, partials, g, nb, NP, sm, w, wh, (int)(blk % nb));
+    dq_body<NW, MT, false>(q, k, v, dout, lse, delta, scal, dq, partials, g, nb, NP, sm, w, wh, (int)(lb % nb));
 }
 
 // -------------------------------------------------------------------------------------- dK / dV
 
-template <int NW>
 struct DkdvSmem {
-  uint16_t* Q;   // [CH][kKStride] rotated, scaled Q^ (operand format)
-  uint16_t* G;   // [CH][kKStride] bf16 dO
-  uint16_t* Gs;  // [CH][32] g * dO (operand format)
-  float* L;      // [kCh] -LSE log2(e)
-  float* Dl;     // [kCh] -tau Delta
+  uint16_t* Q;    // [CH] swizzled rows: rotated, scaled Q^ (operand format)
+  uint16_t* G;    // [CH] swizzled rows: bf16 dO
+  uint16_t* Gs;   // [CH] swizzled rows: g * dO (operand format)
+  float* L;       // [kCh] -LSE log2(e)
+  float* Dl;      // [kCh] -tau Delta
   float* sn;
   float* cs;
-  float* red;    // [NW * 16]
-  uint32_t* blk; // [kCh / 32]
-  uint8_t* lab;  // [kCh]
+  float* red;     // [NW * 16]
+  uint32_t* blk;  // [2][kCh / 32]
+  uint8_t* lab;   // [kCh]
 };
 template <int NW>
 __host__ __device__ inline size_t dkdv_smem(int NP, int M) {
   const int CH = chunk_len(NP);
-  return (size_t)CH * kKStride * 2 * 2 + (size_t)CH * 32 * 2 + kCh * 4 * 2 + (size_t)2 * 2 * M * 8 * 4 +
-         NW * 16 * 4 + (kCh / 32) * 4 + kCh;
+  return (size_t)CH * 32 * 2 * 3 + kCh * 4 * 2 + (size_t)2 * 2 * M * 8 * 4 + NW * 16 * 4 + 2 * (kCh / 32) * 4 + kCh;
 }
 
 template <int NW, int MT, bool H16>
@@ -431,10 +476,11 @@ __device__ inline void dkdv_body(const uint16_t* __restrict__ q, const uint16_t*
                                  const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout,
                                  const float* __restrict__ lse, const float* __restrict__ delta,
                                  const float* __restrict__ scal, uint16_t* __restrict__ dk, uint16_t* __restrict__ dv,
-                                 float* __restrict__ partials, const Geom& g, int nb, int NP,
-                                 const DkdvSmem<NW>& sm, const WinHead& w, int64_t wh, int kblock) {
+                                 float* __restrict__ partials, const Geom& g, int nb, int NP, const DkdvSmem& sm,
+                                 const WinHead& w, int64_t wh, int kblock) {
   constexpr int D = 32;
   constexpr int NT = NW * 64;
+  constexpr int IPT = (kCh * 4 + NT - 1) / NT;
   const int M = MT > 0 ? MT : g.M;
   const int N = M * M;
   const int CH = chunk_len(NP);
@@ -443,6 +489,32 @@ __device__ inline void dkdv_body(const uint16_t* __restrict__ q, const uint16_t*
   const int64_t rowstride = (int64_t)g.heads * D;
   const float g_scale = pow2_scale(scal[wh * 4]);                              // dO of the dV product
   const float ds_scale = pow2_scale(64.f * scal[wh * 4] * scal[wh * 4 + 1]);  // dS of the dK product
+
+  uint4 iq[IPT], ig[IPT];
+  float il[IPT], id[IPT];
+  auto load_chunk = [&](int c0) {
+#pragma unroll
+    for (int i = 0; i < IPT; ++i) {
+      const int it = tid + i * NT;
+      const int qn = c0 + (it >> 2);
+      iq[i] = make_uint4(0, 0, 0, 0);
+      ig[i] = iq[i];
+      il[i] = 0.f;
+      id[i] = 0.f;
+      if (it < CH * 4 && qn < N) {
+        const int r_ = qn / M, c_ = qn - (qn / M) * M;
+        const int64_t t_ = token_index(g, w.b, w.wy, w.wx, r_, c_);
+        const int64_t off = t_ * rowstride + w.h * D + (it & 3) * 8;
+        iq[i] = *reinterpret_cast<const uint4*>(q + off);
+        ig[i] = *reinterpret_cast<const uint4*>(dout + off);
+        if ((it & 3) == 0) {
+          il[i] = lse[t_ * g.heads + w.h];
+          id[i] = delta[t_ * g.heads + w.h];
+        }
+      }
+    }
+  };
+  load_chunk(0);
 
   // the lane's key: K~ operands, tau * V as bf16 B operands
   const int kj = kblock * NW * 32 + wave * 32 + col;
@@ -453,53 +525,55 @@ __device__ inline void dkdv_body(const uint16_t* __restrict__ q, const uint16_t*
   uint4 kb0 = make_uint4(0, 0, 0, 0), kb1 = kb0, vb0 = kb0, vb1 = kb0;
   if (valid) {
     const int64_t off = tok * rowstride + w.h * D;
-    kb0 = rotated_part<H16>(*reinterpret_cast<const uint4*>(k + off + 8 * h), sm.sn, sm.cs, M, r, c, h, 1.f);
-    kb1 = rotated_part<H16>(*reinterpret_cast<const uint4*>(k + off + 16 + 8 * h), sm.sn, sm.cs, M, r, c, 2 + h, 1.f);
-    vb0 = scaled_part<false>(*reinterpret_cast<const uint4*>(v + off + 8 * h), ds_scale);
-    vb1 = scaled_part<false>(*reinterpret_cast<const uint4*>(v + off + 16 + 8 * h), ds_scale);
+    const uint4 k0 = *reinterpret_cast<const uint4*>(k + off + 8 * h);
+    const uint4 k1 = *reinterpret_cast<const uint4*>(k + off + 16 + 8 * h);
+    const uint4 v0 = *reinterpret_cast<const uint4*>(v + off + 8 * h);
+    const uint4 v1 = *reinterpret_cast<const uint4*>(v + off + 16 + 8 * h);
+    kb0 = rotated_part<H16>(k0, sm.sn, sm.cs, M, r, c, h, 1.f);
+    kb1 = rotated_part<H16>(k1, sm.sn, sm.cs, M, r, c, 2 + h, 1.f);
+    vb0 = scaled_part<false>(v0, ds_scale);
+    vb1 = scaled_part<false>(v1, ds_scale);
   }
   f32x16_t accv, acck;
 #pragma unroll
   for (int e = 0; e < 16; ++e) accv[e] = acck[e] = 0.f;
   const uint32_t wave_labels = uniform(wave_or(valid ? (1u << klab) : 0u));
   const bool wave_single = __builtin_popcount(wave_labels) == 1;
+  int tlo, thi;
+  srow_tr_offsets(lane, tlo, thi);
+  const int ro0 = srow(col, h), ro1 = srow(col, 2 + h);
 
-  for (int c0 = 0; c0 < NP; c0 += CH) {
+  int buf = 0;
+  for (int c0 = 0; c0 < NP; c0 += CH, buf ^= 1) {
     __syncthreads();
-    if (tid < kCh / 32) sm.blk[tid] = 0;
-    __syncthreads();
-    for (int it = tid; it < CH * 4; it += NT) {
-      const int n = it >> 2, part = it & 3;
-      const int qn = c0 + n;
-      uint4 qr = make_uint4(0, 0, 0, 0), gr = qr, gs = qr;
-      float l2 = 0.f, dl = 0.f;
-      if (qn < N) {
-        const int qr_ = qn / M, qc_ = qn - (qn / M) * M;
-        const int64_t t_ = token_index(g, w.b, w.wy, w.wx, qr_, qc_);
-        const int64_t off = t_ * rowstride + w.h * D + part * 8;
-        const uint4 raw = *reinterpret_cast<const uint4*>(q + off);
-        gr = *reinterpret_cast<const uint4*>(dout + off);
+#pragma unroll
+    for (int i = 0; i < IPT; ++i) {
+      const int it = tid + i * NT;
+      if (it < CH * 4) {
+        const int n = it >> 2, part = it & 3, qn = c0 + n;
+        uint4 qr = make_uint4(0, 0, 0, 0);
+        if (qn < N) qr = rotated_part<H16>(iq[i], sm.sn, sm.cs, M, qn / M, qn - (qn / M) * M, part, kQScale);
+        *reinterpret_cast<uint4*>(sm.Q + srow(n, part)) = qr;
+        *reinterpret_cast<uint4*>(sm.G + srow(n, part)) = ig[i];
+        *reinterpret_cast<uint4*>(sm.Gs + srow(n, part)) = scaled_part<H16>(ig[i], g_scale);
         if (part == 0) {
-          l2 = lse[t_ * g.heads + w.h] * kLog2e;
-          dl = delta[t_ * g.heads + w.h] * ds_scale;
+          sm.L[n] = -il[i] * kLog2e;
+          sm.Dl[n] = -id[i] * ds_scale;
+          sm.lab[n] = chunk_label(g, w, M, qn, sm.blk + buf * (kCh / 32), n);
         }
-        qr = rotated_part<H16>(raw, sm.sn, sm.cs, M, qr_, qc_, part, kQScale);
-        gs = scaled_part<H16>(gr, g_scale);
-      }
-      *reinterpret_cast<uint4*>(sm.Q + n * kKStride + part * 8) = qr;
-      *reinterpret_cast<uint4*>(sm.G + n * kKStride + part * 8) = gr;
-      *reinterpret_cast<uint4*>(sm.Gs + n * 32 + part * 8) = gs;
-      if (part == 0) {
-        sm.L[n] = -l2;
-        sm.Dl[n] = -dl;
-        sm.lab[n] = chunk_label(g, w, M, qn, sm.blk, n);
       }
     }
+    if (tid < kCh / 32) sm.blk[(buf ^ 1) * (kCh / 32) + tid] = 0;
     __syncthreads();
+    if (c0 + CH < NP) load_chunk(c0 + CH);
     if (wave_labels == 0) continue;
-    const int nblk = min(CH, NP - c0) / 32;
-    for (int qb = 0; qb < nblk; ++qb) {
-      const uint32_t info = uniform(sm.blk[qb]);
+    const uint4 bw = *reinterpret_cast<const uint4*>(sm.blk + buf * (kCh / 32));
+    const uint32_t info4[4] = {uniform(bw.x), uniform(bw.y), uniform(bw.z), uniform(bw.w)};
+    const int nblk = min(CH, NP - c0) >> 5;
+#pragma unroll
+    for (int qb = 0; qb < kCh / 32; ++qb) {
+      if (qb >= nblk) break;
+      const uint32_t info = info4[qb];
       const uint32_t bl = info & 0x1ffu;
       if ((bl & wave_labels) == 0) continue;
       const bool need_mask = ((info >> 10) & 1u) || !wave_single || bl != wave_labels;
@@ -518,13 +592,13 @@ __device__ inline void dkdv_body(const uint16_t* __restrict__ q, const uint16_t*
         cD[4 * gq + 2] = d4.z;
         cD[4 * gq + 3] = d4.w;
       }
-      const uint16_t* qrow = sm.Q + (qb * 32 + col) * kKStride + 8 * h;
-      const uint16_t* grow = sm.G + (qb * 32 + col) * kKStride + 8 * h;
-      f32x16_t s = mfma_op<H16>(*reinterpret_cast<const uint4*>(qrow), kb0, cL);
-      s = mfma_op<H16>(*reinterpret_cast<const uint4*>(qrow + 16), kb1, s);
-      f32x16_t dp = mfma_op<false>(*reinterpret_cast<const uint4*>(grow), vb0, cD);
-      dp = mfma_op<false>(*reinterpret_cast<const uint4*>(grow + 16), vb1, dp);
-      float p[16], ds[16];
+      const uint16_t* Qb = sm.Q + qb * 1024;
+      const uint16_t* Gb = sm.G + qb * 1024;
+      f32x16_t s = mfma_op<H16>(*reinterpret_cast<const uint4*>(Qb + ro0), kb0, cL);
+      s = mfma_op<H16>(*reinterpret_cast<const uint4*>(Qb + ro1), kb1, s);
+      f32x16_t dp = mfma_op<false>(*reinterpret_cast<const uint4*>(Gb + ro0), vb0, cD);
+      dp = mfma_op<false>(*reinterpret_cast<const uint4*>(Gb + ro1), vb1, dp);
+      float p[16];
       if (need_mask) {
         const uint32_t live = live_bits(sm.lab, qb, h, klab);
 #pragma unroll
@@ -533,22 +607,29 @@ __device__ inline void dkdv_body(const uint16_t* __restrict__ q, const uint16_t*
 #pragma unroll
         for (int e = 0; e < 16; ++e) p[e] = __builtin_amdgcn_exp2f(s[e]);
       }
-#pragma unroll
-      for (int e = 0; e < 16; ++e) ds[e] = p[e] * dp[e];
       uint32_t pp[8], pd[8];
+      if constexpr (H16) {
+        // tau dS = P * tau (dP - Delta) as a packed fp16 product of the fp16 operands
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        pp[e] = pack_op2<H16>(p[2 * e], p[2 * e + 1]);
-        pd[e] = pack_op2<H16>(ds[2 * e], ds[2 * e + 1]);
+        for (int e = 0; e < 8; ++e) {
+          pp[e] = pack2h(p[2 * e], p[2 * e + 1]);
+          const f16x2_t a = __builtin_bit_cast(f16x2_t, pp[e]);
+          const f16x2_t b = __builtin_bit_cast(f16x2_t, pack2h(dp[2 * e], dp[2 * e + 1]));
+          pd[e] = __builtin_bit_cast(uint32_t, a * b);
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          pp[e] = pack2(p[2 * e], p[2 * e + 1]);
+          pd[e] = pack2(p[2 * e] * dp[2 * e], p[2 * e + 1] * dp[2 * e + 1]);
+        }
       }
-      const uint4 gt0 = tr_operand(sm.Gs, 32, qb * 32, lane);
-      const uint4 gt1 = tr_operand(sm.Gs, 32, qb * 32 + 16, lane);
-      accv = mfma_op<H16>(gt0, make_uint4(pp[0], pp[1], pp[2], pp[3]), accv);
-      accv = mfma_op<H16>(gt1, make_uint4(pp[4], pp[5], pp[6], pp[7]), accv);
-      const uint4 qt0 = tr_operand(sm.Q, kKStride, qb * 32, lane);
-      const uint4 qt1 = tr_operand(sm.Q, kKStride, qb * 32 + 16, lane);
-      acck = mfma_op<H16>(qt0, make_uint4(pd[0], pd[1], pd[2], pd[3]), acck);
-      acck = mfma_op<H16>(qt1, make_uint4(pd[4], pd[5], pd[6], pd[7]), acck);
+      const uint16_t* Gsb = sm.Gs + qb * 1024;
+      accv = mfma_op<H16>(tr_operand_at(Gsb, tlo, thi), make_uint4(pp[0], pp[1], pp[2], pp[3]), accv);
+      accv = mfma_op<H16>(tr_operand_at(Gsb + 512, tlo, thi), make_uint4(pp[4], pp[5], pp[6], pp[7]), accv);
+      acck = mfma_op<H16>(tr_operand_at(Qb, tlo, thi), make_uint4(pd[0], pd[1], pd[2], pd[3]), acck);
+      acck = mfma_op<H16>(tr_operand_at(Qb + 512, tlo, thi), make_uint4(pd[4], pd[5], pd[6], pd[7]), acck);
+      __builtin_amdgcn_sched_barrier(0);  // keep blocks apart: bounded register pressure
     }
   }
 
@@ -572,36 +653,38 @@ __device__ inline void dkdv_body(const uint16_t* __restrict__ q, const uint16_t*
 }
 
 template <int NW, int MT>
-__global__ __launch_bounds__(NW * 64) void bwd_dkdv_mfma_kernel(
+__global__ __launch_bounds__(NW * 64, NW >= 8 ? 4 : 2) void bwd_dkdv_mfma_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ delta,
     const float* __restrict__ scal, const float* __restrict__ th_row, const float* __restrict__ th_col,
     uint16_t* __restrict__ dk, uint16_t* __restrict__ dv, float* __restrict__ partials, Geom g, int nb, int NP) {
   extern __shared__ __align__(16) unsigned char smem_raw[];
+  if constexpr (MT > 0) NP = (MT * MT + 31) / 32 * 32;  // compile-time chunk geometry
   const int M = MT > 0 ? MT : g.M;
   const int CH = chunk_len(NP);
-  DkdvSmem<NW> sm;
+  DkdvSmem sm;
   sm.Q = reinterpret_cast<uint16_t*>(smem_raw);
-  sm.G = sm.Q + CH * kKStride;
-  sm.Gs = sm.G + CH * kKStride;
+  sm.G = sm.Q + CH * 32;
+  sm.Gs = sm.G + CH * 32;
   sm.L = reinterpret_cast<float*>(sm.Gs + CH * 32);
   sm.Dl = sm.L + kCh;
   sm.sn = sm.Dl + kCh;
   sm.cs = sm.sn + 2 * M * 8;
   sm.red = sm.cs + 2 * M * 8;
   sm.blk = reinterpret_cast<uint32_t*>(sm.red + NW * 16);
-  sm.lab = reinterpret_cast<uint8_t*>(sm.blk + kCh / 32);
-  const int64_t blk = blockIdx.x;
-  const int64_t wh = blk / nb;
+  sm.lab = reinterpret_cast<uint8_t*>(sm.blk + 2 * (kCh / 32));
+  const int64_t lb = xcd_order(blockIdx.x, gridDim.x);
+  const int64_t wh = lb / nb;
   const WinHead w = decode_winhead(g, wh);
+  if (threadIdx.x < 2 * (kCh / 32)) sm.blk[threadIdx.x] = 0;
   fill_table(sm.sn, sm.cs, th_row, th_col, w.h, M, threadIdx.x, NW * 64);
   __syncthreads();
   if (window_h16(scal, wh))
     dkdv_body<NW, MT, true>(q, k, v, dout, lse, delta, scal, dk, dv, partials, g, nb, NP, sm, w, wh,
-                            (int)(blk % nb));
+                            (int)(lb % nb));
   else
     dkdv_body<NW, MT, false>(q, k, v, dout, lse, delta, scal, dk, dv, partials, g, nb, NP, sm, w, wh,
-                             (int)(blk % nb));
+                             (int)(lb % nb));
 }
 
 template <int NW, int MT>
@@ -611,13 +694,6 @@ hipError_t launch_main(const BwdArgs& a, hipStream_t st) {
   const int NP = (g.N + 31) / 32 * 32;
   const int nb = (g.N + NW * 32 - 1) / (NW * 32);
   const int64_t blocks = nwh * nb;
-  static std::once_flag once;
-  std::call_once(once, [] {
-    (void)hipFuncSetAttribute((const void*)bwd_dq_mfma_kernel<NW, MT>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                              160 * 1024);
-    (void)hipFuncSetAttribute((const void*)bwd_dkdv_mfma_kernel<NW, MT>,
-                              hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-  });
   hipLaunchKernelGGL((bwd_dkdv_mfma_kernel<NW, MT>), dim3((unsigned)blocks), dim3(NW * 64), dkdv_smem<NW>(NP, g.M),
                      st, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (const uint16_t*)a.dout,
                      a.lse, a.delta, a.scal, a.th_row, a.th_col, (uint16_t*)a.dk, (uint16_t*)a.dv, a.partials, g, nb,

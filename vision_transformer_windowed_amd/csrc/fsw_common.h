@@ -23,6 +23,15 @@ struct Geom {
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
+// XCD-aware workgroup order.  Workgroup b is dispatched to XCD b % 8 and each XCD has its own L2;
+// the returned logical index gives every XCD a contiguous range, so workgroups with neighbouring
+// logical indices (the heads and blocks of one window, which read the same token rows) share one
+// L2.  A bijection of [0, n).
+__device__ __forceinline__ int64_t xcd_order(int64_t b, int64_t n) {
+  const int64_t q = n >> 3, r = n & 7, x = b & 7;
+  return x * q + (x < r ? x : r) + (b >> 3);
+}
+
 // Grid row (or column) of shifted-frame coordinate Y: (Y + shift) mod size, with Y < size.
 __device__ __forceinline__ int grid_coord(int Y, int shift, int size) {
   int y = Y + shift;

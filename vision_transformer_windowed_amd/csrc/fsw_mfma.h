@@ -64,6 +64,29 @@ __device__ __forceinline__ uint4 tr_operand(const uint16_t* rows, int rs, int k0
   return make_uint4(lo.x, lo.y, hi.x, hi.y);
 }
 
+// Swizzled LDS tile of [token][32 channels] 16-bit values: 64-byte rows, and the 16-byte chunk c
+// (channels 8c..8c+7) of row n stored at chunk c ^ ((n / 4) % 4).  The MFMA row reads (16 rows,
+// the same chunk) and the transposed reads (4 rows x 64 bytes per 32 lanes) then touch every LDS
+// bank once.  Element offset of chunk c of row n:
+__host__ __device__ __forceinline__ int srow(int n, int c) { return n * 32 + ((c ^ ((n >> 2) & 3)) << 3); }
+
+// Per-lane element offsets (relative to a 16-row group) of the two ds_read_b64_tr_b16 reads that
+// build a tr_operand-ordered operand from a swizzled tile: the group at row k0 (k0 % 16 == 0) is at
+// k0 * 32 + lo and k0 * 32 + hi.
+__device__ __forceinline__ void srow_tr_offsets(int lane, int& lo, int& hi) {
+  const int j = lane & 15;
+  const int key = 4 * (lane >> 5) + (j >> 2);
+  const int ch = (lane & 16) + 4 * (j & 3);
+  lo = srow(key, ch >> 3) + (ch & 7);
+  hi = srow(key + 8, ch >> 3) + (ch & 7);
+}
+
+__device__ __forceinline__ uint4 tr_operand_at(const uint16_t* base, int lo, int hi) {
+  const uint2 a = lds_read_tr16(base + lo);
+  const uint2 b = lds_read_tr16(base + hi);
+  return make_uint4(a.x, a.y, b.x, b.y);
+}
+
 // Largest operand magnitude accepted for the fp16 score products (fp16 max is 65504).
 constexpr float kF16Limit = 16384.f;
 

@@ -7,14 +7,17 @@ N(0, 0.01^2) noise.  One step = the whole hot path over the batch: the forward (
 attention, LSE) then the backward (Delta, recomputed P, dQ/dK/dV, dtheta).  FLOPs per window-head:
 4 N^2 d forward + 10 N^2 d backward (N = M^2), the dense convention of the workload's metric.
 
-Prints ONE JSON line.  `roofline` describes the dominant kernel launch (the longer of the forward
-and backward calls), timed with HIP events on the stream the library launches on.  `traffic` is
-taken from the committed rocprofv3 counter summary in profiles/ when that summary was measured on
-the current kernel source (sha256 match), else null.  `cpu_baseline` times the fp64 CPU oracle on
-a bounded sample of the same workload (rank 0, N=1 only).
+Prints ONE JSON line.  `roofline` describes the dominant call (the longer of the forward and
+backward C-ABI calls; `launches` names the kernels it enqueues), timed with HIP events on the
+stream the library launches on.  `traffic` is taken from the committed rocprofv3 counter summary
+in profiles/ when that summary was measured on the current kernel source (sha256 match), else
+null.  `fwd_roofline` is the M=32 forward kernel against the bf16 MFMA peak; `m8_fwd_roofline`
+times the forward on the M=8 Swin-T stage-1 workload (memory-bound) against the HBM peak.
+`cpu_baseline` times the fp64 CPU oracle on a bounded sample of the same workload (rank 0, N=1
+only).
 
 Modes for profiling runs: --only fwd|bwd runs just that call per step; --copy-calibration runs a
-plain device-to-device copy of a known size (for scaling HBM counters).
+plain streaming kernel of known traffic, b = -a over 1 GiB (for scaling HBM counters).
 """
 
 import argparse
@@ -30,6 +33,9 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
+# kernels each C-ABI call launches, in order
+CALL_LAUNCHES = {"wattn_fwd": ["fwd_mfma_kernel"],
+                 "wattn_bwd": ["bwd_pre_kernel", "bwd_dkdv_mfma_kernel", "bwd_dq_mfma_kernel", "dtheta_reduce_kernel"]}
 KERNEL_SOURCES = ["fwd_mfma.hip", "bwd_mfma.hip", "fwd_scalar.hip", "bwd_scalar.hip", "fsw_common.h",
                   "fsw_mfma.h", "fsw_api.hip"]
 
@@ -59,7 +65,7 @@ def read_traffic(kernel_tag, workload, sha):
 
 
 def cpu_baseline(x, w, shift, images, gpu_out=None):
-    """Time the fp64 oracle (forward + backward) on the first `images` images of the batch."""
+    """Time the fp64 oracle (forward + backward) on the first `images` images, one image per call."""
     import numpy as np
     import oracle
     try:
@@ -67,28 +73,65 @@ def cpu_baseline(x, w, shift, images, gpu_out=None):
         cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     except Exception:
         cores = len(os.sched_getaffinity(0))
-    sl = slice(0, images)
-    args = [x[n][sl].double().numpy() for n in ("q", "k", "v")]
-    dout = x["dout"][sl].double().numpy()
     tr, tc = x["theta_row"].double().numpy(), x["theta_col"].double().numpy()
-    t0 = time.perf_counter()
-    ro, rl = oracle.wattn_fwd_ref(*args, tr, tc, w["M"], shift)
-    g = oracle.wattn_bwd_ref(*args, dout, tr, tc, w["M"], shift)
-    dt = time.perf_counter() - t0
+    dt = 0.0
+    parity = {} if gpu_out is not None else None
+    acc = {}
+    for b in range(images):
+        sl = slice(b, b + 1)
+        args = [x[n][sl].double().numpy() for n in ("q", "k", "v")]
+        dout = x["dout"][sl].double().numpy()
+        t0 = time.perf_counter()
+        ro, rl = oracle.wattn_fwd_ref(*args, tr, tc, w["M"], shift)
+        g = oracle.wattn_bwd_ref(*args, dout, tr, tc, w["M"], shift)
+        dt += time.perf_counter() - t0
+        if gpu_out is not None:
+            for name, ref, got in (("O", ro, gpu_out["out"]), ("LSE", rl, gpu_out["lse"]), ("dQ", g[0], gpu_out["dq"]),
+                                   ("dK", g[1], gpu_out["dk"]), ("dV", g[2], gpu_out["dv"])):
+                got = got[sl].double().cpu().numpy()
+                a = acc.setdefault(name, [0.0, 0.0, 0.0])
+                a[0] = max(a[0], float(np.abs(got - ref).max()))
+                a[1] += float(((got - ref) ** 2).sum())
+                a[2] += float((ref ** 2).sum())
     N = w["M"] ** 2
     nwh = images * (w["Hg"] // w["M"]) * (w["Wg"] // w["M"]) * w["heads"]
     flops = 14.0 * N * N * w["d"] * nwh
     res = {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
-           "sample": f"first {images} of {w['B']} images (forward + backward, fp64 NumPy), {dt:.1f} s wall"}
-    parity = None
+           "sample": f"first {images} of {w['B']} images, one image per oracle call (forward + backward, fp64 "
+                     f"NumPy), {dt:.1f} s of oracle time"}
     if gpu_out is not None:
-        parity = {}
-        for name, ref, got in (("O", ro, gpu_out["out"]), ("LSE", rl, gpu_out["lse"]), ("dQ", g[0], gpu_out["dq"]),
-                               ("dK", g[1], gpu_out["dk"]), ("dV", g[2], gpu_out["dv"])):
-            got = got[sl].double().cpu().numpy()
-            parity[name] = {"max_abs": float(np.abs(got - ref).max()),
-                            "rel_l2": float(np.linalg.norm(got - ref) / np.linalg.norm(ref))}
+        for name, (ma, se, sr) in acc.items():
+            parity[name] = {"max_abs": ma, "rel_l2": (se / sr) ** 0.5}
     return res, parity
+
+
+def m8_forward_roofline(dev, steps, warmup):
+    """Forward on the M=8 Swin-T stage-1 workload (HBM-bound): achieved GB/s of algorithmic bytes."""
+    import torch
+    import vision_transformer_windowed_amd as F
+    from vision_transformer_windowed_amd.inputs import WORKLOADS, workload_inputs
+    name = "swin_t_s1_p4_m8"
+    w = WORKLOADS[name]
+    x = {k: v.to(dev) for k, v in workload_inputs(name, with_dout=False).items()}
+    q, k, v = x["q"], x["k"], x["v"]
+    out = torch.empty_like(q)
+    lse = torch.empty(q.shape[:4], device=dev, dtype=torch.float32)
+    stream = torch.cuda.current_stream(dev)
+    for _ in range(warmup):
+        F.wattn_fwd(q, k, v, x["theta_row"], x["theta_col"], w["M"], 0, out=out, lse=lse)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        F.wattn_fwd(q, k, v, x["theta_row"], x["theta_col"], w["M"], 0, out=out, lse=lse)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    nbytes = 4 * q.numel() * q.element_size() + lse.numel() * 4  # q, k, v read; out written; lse written
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"workload": name, "kernel": "wattn_fwd", "bound": "hbm", "achieved": round(gbs, 1),
+            "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+            "algorithmic_bytes": nbytes, "launch_ms": round(ms, 4)}
 
 
 def main():
@@ -99,7 +142,8 @@ def main():
     ap.add_argument("--workload", default="flashswin_t_s1_p2_m32")
     ap.add_argument("--shift", type=int, default=None)
     ap.add_argument("--only", choices=["step", "fwd", "bwd"], default="step")
-    ap.add_argument("--cpu-images", type=int, default=4)
+    ap.add_argument("--cpu-images", type=int, default=20)
+    ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
     args = ap.parse_args()
@@ -119,13 +163,14 @@ def main():
     stream = torch.cuda.current_stream(dev)
 
     if args.copy_calibration:
-        n = 1 << 30  # 1 GiB
-        a = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        # a plain streaming kernel of known traffic: b = -a over 1 GiB of float32 (1 GiB read, 1 GiB written)
+        n = 1 << 28
+        a = torch.ones(n, dtype=torch.float32, device=dev)
         b = torch.empty_like(a)
         for _ in range(args.warmup + args.steps):
-            b.copy_(a)
+            torch.neg(a, out=b)
         torch.cuda.synchronize()
-        print(json.dumps({"copy_calibration_bytes": n, "launches": args.warmup + args.steps + 1}))
+        print(json.dumps({"copy_calibration_bytes": n * 4, "kernel": "neg", "launches": args.warmup + args.steps}))
         return
 
     w = WORKLOADS[args.workload]
@@ -191,7 +236,16 @@ def main():
     traffic = read_traffic(dom, args.workload, sha)
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / BF16_MFMA_PEAK_TFLOPS, 4), "traffic": traffic, "kernel": dom,
-                "launch_ms": round(dom_ms, 4), "kernel_source_sha": sha}
+                "launches": CALL_LAUNCHES[dom], "launch_ms": round(dom_ms, 4), "kernel_source_sha": sha}
+    fwd_roofline = None
+    if args.only != "bwd":
+        fwd_tf = fwd_flops / (fwd_ms * 1e-3) / 1e12
+        fwd_roofline = {"kernel": "wattn_fwd", "bound": "mfma", "achieved": round(fwd_tf, 2),
+                        "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(fwd_tf / BF16_MFMA_PEAK_TFLOPS, 4),
+                        "launch_ms": round(fwd_ms, 4)}
+    m8 = None
+    if not args.no_secondary and args.only == "step":
+        m8 = m8_forward_roofline(dev, max(args.steps, 10), max(args.warmup, 2))
 
     gpu_out = {"out": out, "lse": lse, "dq": grads[0], "dk": grads[1], "dv": grads[2]}
     cpu, parity = (None, None)
@@ -220,6 +274,8 @@ def main():
         "bwd_tflops": round(bwd_flops / (bwd_ms * 1e-3) / 1e12, 2) if args.only != "fwd" else None,
         "window_heads_per_s": round(nwh / (ms_per_step * 1e-3), 1),
         "roofline": roofline,
+        "fwd_roofline": fwd_roofline,
+        "m8_fwd_roofline": m8,
         "cpu_baseline": cpu,
         "parity_sample": parity,
         "input_gen_s": round(gen_s, 1),

@@ -393,13 +393,9 @@ __device__ inline void dq_body(const uint16_t* __restrict__ q, const uint16_t* _
       }
       uint32_t pk[8];
       if constexpr (H16) {
-        // tau dS = P * tau (dP - Delta) as a packed fp16 product of the fp16 operands
+        // tau dS = P * tau (dP - Delta), the float32 product rounded once to fp16
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const f16x2_t a = __builtin_bit_cast(f16x2_t, pack2h(p[2 * e], p[2 * e + 1]));
-          const f16x2_t b = __builtin_bit_cast(f16x2_t, pack2h(dp[2 * e], dp[2 * e + 1]));
-          pk[e] = __builtin_bit_cast(uint32_t, a * b);
-        }
+        for (int e = 0; e < 8; ++e) pk[e] = mul2h(p[2 * e], dp[2 * e], p[2 * e + 1], dp[2 * e + 1]);
       } else {
 #pragma unroll
         for (int e = 0; e < 8; ++e) pk[e] = pack2(p[2 * e] * dp[2 * e], p[2 * e + 1] * dp[2 * e + 1]);
@@ -422,7 +418,7 @@ __device__ inline void dq_body(const uint16_t* __restrict__ q, const uint16_t* _
 }
 
 template <int NW, int MT>
-__global__ __launch_bounds__(NW * 64, NW >= 8 ? 4 : 2) void bwd_dq_mfma_kernel(
+__global__ __launch_bounds__(NW * 64, 2) void bwd_dq_mfma_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ delta,
     const float* __restrict__ scal, const float* __restrict__ th_row, const float* __restrict__ th_col,
@@ -653,7 +649,7 @@ __device__ inline void dkdv_body(const uint16_t* __restrict__ q, const uint16_t*
 }
 
 template <int NW, int MT>
-__global__ __launch_bounds__(NW * 64, NW >= 8 ? 4 : 2) void bwd_dkdv_mfma_kernel(
+__global__ __launch_bounds__(NW * 64, 2) void bwd_dkdv_mfma_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ delta,
     const float* __restrict__ scal, const float* __restrict__ th_row, const float* __restrict__ th_col,

@@ -97,6 +97,15 @@ __device__ __forceinline__ uint32_t pack2h(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
+// fp16 pair (lo, hi) = (a0 * b0, a1 * b1): float32 products rounded once to fp16 (v_fma_mix with
+// a zero addend; ALU only).
+__device__ __forceinline__ uint32_t mul2h(float a0, float b0, float a1, float b1) {
+  uint32_t r;
+  asm("v_fma_mixlo_f16 %0, %1, %2, 0" : "=v"(r) : "v"(a0), "v"(b0));
+  asm("v_fma_mixhi_f16 %0, %1, %2, 0" : "+v"(r) : "v"(a1), "v"(b1));
+  return r;
+}
+
 // Pack 8 floats into 8 fp16 (h16) or bf16 values.
 __device__ __forceinline__ uint4 pack8_op(const float (&x)[8], bool h16) {
   if (h16) return make_uint4(pack2h(x[0], x[1]), pack2h(x[2], x[3]), pack2h(x[4], x[5]), pack2h(x[6], x[7]));

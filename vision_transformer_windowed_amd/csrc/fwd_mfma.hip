@@ -273,7 +273,7 @@ __global__ __launch_bounds__(NWAVES * 64) void fwd_mfma_kernel(const uint16_t* _
   const int NB = NP / 32;
   const FwdSmem sm = carve(smem_raw, NP, M);
 
-  const int64_t blk = blockIdx.x;
+  const int64_t blk = xcd_order(blockIdx.x, gridDim.x);  // a window's heads and query blocks share one L2
   const WinHead w = decode_winhead(g, blk / nqb);
   const int qblock = (int)(blk % nqb);
   const int tid = threadIdx.x;

@@ -277,7 +277,10 @@ __host__ __device__ inline size_t dq_smem(int NP, int M) {
   return (size_t)CH * 32 * 2 * 2 + (size_t)2 * 2 * M * 8 * 4 + NW * 16 * 4 + 2 * (kCh / 32) * 4 + kCh;
 }
 
-template <int NW, int MT, bool H16>
+// Each wave owns S sets of 32 queries (lane = query within a set).  The sets share every LDS
+// operand read (K~ and V rows, the transposed K~^T), so staging and LDS traffic per tile shrink
+// with S, and the S independent tiles give the scheduler work to interleave.
+template <int NW, int MT, int S, bool H16>
 __device__ inline void dq_body(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                                const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout,
                                const float* __restrict__ lse, const float* __restrict__ delta,
@@ -313,35 +316,43 @@ __device__ inline void dq_body(const uint16_t* __restrict__ q, const uint16_t* _
   };
   load_chunk(0);
 
-  // the lane's query: Q^ operands, tau * dO as bf16 B operands, -LSE and -tau Delta
-  const int qi = qblock * NW * 32 + wave * 32 + col;
-  const bool valid = qi < N;
-  const int r = valid ? qi / M : 0, c = valid ? qi - (qi / M) * M : 0;
-  const int64_t tok = valid ? token_index(g, w.b, w.wy, w.wx, r, c) : 0;
-  const int qlab = valid ? token_label(g, w.wy, w.wx, r, c) : 0xff;
-  uint4 qb0 = make_uint4(0, 0, 0, 0), qb1 = qb0, gb0 = qb0, gb1 = qb0;
-  float lse2 = 0.f, del = 0.f;
-  if (valid) {
-    const int64_t off = tok * rowstride + w.h * D;
-    const uint4 q0 = *reinterpret_cast<const uint4*>(q + off + 8 * h);
-    const uint4 q1 = *reinterpret_cast<const uint4*>(q + off + 16 + 8 * h);
-    const uint4 g0 = *reinterpret_cast<const uint4*>(dout + off + 8 * h);
-    const uint4 g1 = *reinterpret_cast<const uint4*>(dout + off + 16 + 8 * h);
-    lse2 = lse[tok * g.heads + w.h] * kLog2e;
-    del = delta[tok * g.heads + w.h] * ds_scale;
-    qb0 = rotated_part<H16>(q0, sm.sn, sm.cs, M, r, c, h, kQScale);
-    qb1 = rotated_part<H16>(q1, sm.sn, sm.cs, M, r, c, 2 + h, kQScale);
-    gb0 = scaled_part<false>(g0, ds_scale);
-    gb1 = scaled_part<false>(g1, ds_scale);
-  }
-  f32x16_t cL, cD, acc;
+  // the lane's queries: Q^ operands, tau * dO as bf16 B operands, -LSE and -tau Delta
+  const int qbase = (qblock * NW + wave) * 32 * S + col;
+  uint4 qb0[S], qb1[S], gb0[S], gb1[S];
+  f32x16_t cL[S], cD[S], acc[S];
+  int qlab[S];
+  uint32_t wl = 0;
 #pragma unroll
-  for (int e = 0; e < 16; ++e) {
-    cL[e] = -lse2;
-    cD[e] = -del;
-    acc[e] = 0.f;
+  for (int t = 0; t < S; ++t) {
+    const int qi = qbase + 32 * t;
+    const bool valid = qi < N;
+    const int r = valid ? qi / M : 0, c = valid ? qi - (qi / M) * M : 0;
+    qlab[t] = valid ? token_label(g, w.wy, w.wx, r, c) : 0xff;
+    wl |= valid ? (1u << qlab[t]) : 0u;
+    qb0[t] = qb1[t] = gb0[t] = gb1[t] = make_uint4(0, 0, 0, 0);
+    float lse2 = 0.f, del = 0.f;
+    if (valid) {
+      const int64_t tok = token_index(g, w.b, w.wy, w.wx, r, c);
+      const int64_t off = tok * rowstride + w.h * D;
+      const uint4 q0 = *reinterpret_cast<const uint4*>(q + off + 8 * h);
+      const uint4 q1 = *reinterpret_cast<const uint4*>(q + off + 16 + 8 * h);
+      const uint4 g0 = *reinterpret_cast<const uint4*>(dout + off + 8 * h);
+      const uint4 g1 = *reinterpret_cast<const uint4*>(dout + off + 16 + 8 * h);
+      lse2 = lse[tok * g.heads + w.h] * kLog2e;
+      del = delta[tok * g.heads + w.h] * ds_scale;
+      qb0[t] = rotated_part<H16>(q0, sm.sn, sm.cs, M, r, c, h, kQScale);
+      qb1[t] = rotated_part<H16>(q1, sm.sn, sm.cs, M, r, c, 2 + h, kQScale);
+      gb0[t] = scaled_part<false>(g0, ds_scale);
+      gb1[t] = scaled_part<false>(g1, ds_scale);
+    }
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      cL[t][e] = -lse2;
+      cD[t][e] = -del;
+      acc[t][e] = 0.f;
+    }
   }
-  const uint32_t wave_labels = uniform(wave_or(valid ? (1u << qlab) : 0u));
+  const uint32_t wave_labels = uniform(wave_or(wl));
   const bool wave_single = __builtin_popcount(wave_labels) == 1;
   int tlo, thi;
   srow_tr_offsets(lane, tlo, thi);
@@ -378,46 +389,66 @@ __device__ inline void dq_body(const uint16_t* __restrict__ q, const uint16_t* _
       const bool need_mask = ((info >> 10) & 1u) || !wave_single || bl != wave_labels;
       const uint16_t* Kb = sm.K + kb * 1024;
       const uint16_t* Vb = sm.V + kb * 1024;
-      f32x16_t s = mfma_op<H16>(*reinterpret_cast<const uint4*>(Kb + ro0), qb0, cL);
-      s = mfma_op<H16>(*reinterpret_cast<const uint4*>(Kb + ro1), qb1, s);
-      f32x16_t dp = mfma_op<false>(*reinterpret_cast<const uint4*>(Vb + ro0), gb0, cD);
-      dp = mfma_op<false>(*reinterpret_cast<const uint4*>(Vb + ro1), gb1, dp);
-      float p[16];
-      if (need_mask) {
-        const uint32_t live = live_bits(sm.lab, kb, h, qlab);
+      const uint4 ka0 = *reinterpret_cast<const uint4*>(Kb + ro0);
+      const uint4 ka1 = *reinterpret_cast<const uint4*>(Kb + ro1);
+      const uint4 va0 = *reinterpret_cast<const uint4*>(Vb + ro0);
+      const uint4 va1 = *reinterpret_cast<const uint4*>(Vb + ro1);
+      // S^T = K~ Q^T from -LSE, tau (dP - Delta)^T = V (tau dO)^T from -tau Delta
+      f32x16_t sc[S], dc[S];
 #pragma unroll
-        for (int e = 0; e < 16; ++e) p[e] = ((live >> e) & 1u) ? __builtin_amdgcn_exp2f(s[e]) : 0.f;
-      } else {
-#pragma unroll
-        for (int e = 0; e < 16; ++e) p[e] = __builtin_amdgcn_exp2f(s[e]);
+      for (int t = 0; t < S; ++t) {
+        sc[t] = mfma_op<H16>(ka1, qb1[t], mfma_op<H16>(ka0, qb0[t], cL[t]));
+        dc[t] = mfma_op<false>(va1, gb1[t], mfma_op<false>(va0, gb0[t], cD[t]));
       }
-      uint32_t pk[8];
-      if constexpr (H16) {
-        // tau dS = P * tau (dP - Delta), the float32 product rounded once to fp16
+      // tau dS^T = exp2(S^T) * tau (dP - Delta)^T, the float32 product rounded once to the operand format
+      uint32_t pk[S][8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) pk[e] = mul2h(p[2 * e], dp[2 * e], p[2 * e + 1], dp[2 * e + 1]);
-      } else {
+      for (int t = 0; t < S; ++t) {
+        float p[16];
+        if (need_mask) {
+          const uint32_t live = live_bits(sm.lab, kb, h, qlab[t]);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) pk[e] = pack2(p[2 * e] * dp[2 * e], p[2 * e + 1] * dp[2 * e + 1]);
+          for (int e = 0; e < 16; ++e) p[e] = ((live >> e) & 1u) ? __builtin_amdgcn_exp2f(sc[t][e]) : 0.f;
+        } else {
+#pragma unroll
+          for (int e = 0; e < 16; ++e) p[e] = __builtin_amdgcn_exp2f(sc[t][e]);
+        }
+        if constexpr (H16) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) pk[t][e] = mul2h(p[2 * e], dc[t][2 * e], p[2 * e + 1], dc[t][2 * e + 1]);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) pk[t][e] = pack2(p[2 * e] * dc[t][2 * e], p[2 * e + 1] * dc[t][2 * e + 1]);
+        }
       }
-      acc = mfma_op<H16>(tr_operand_at(Kb, tlo, thi), make_uint4(pk[0], pk[1], pk[2], pk[3]), acc);
-      acc = mfma_op<H16>(tr_operand_at(Kb + 512, tlo, thi), make_uint4(pk[4], pk[5], pk[6], pk[7]), acc);
-      __builtin_amdgcn_sched_barrier(0);  // keep blocks apart: bounded register pressure
+      // dQ~^T += K~^T (tau dS)^T
+      const uint4 kt0 = tr_operand_at(Kb, tlo, thi);
+      const uint4 kt1 = tr_operand_at(Kb + 512, tlo, thi);
+#pragma unroll
+      for (int t = 0; t < S; ++t) {
+        acc[t] = mfma_op<H16>(kt0, make_uint4(pk[t][0], pk[t][1], pk[t][2], pk[t][3]), acc[t]);
+        acc[t] = mfma_op<H16>(kt1, make_uint4(pk[t][4], pk[t][5], pk[t][6], pk[t][7]), acc[t]);
+      }
     }
   }
 
-  float t[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  if (valid) {
-    const int64_t off = tok * rowstride + w.h * D;
-    // dq~ = acc / tau / sqrt(d); the dtheta integrand takes q~ as the dK product saw it
-    unrotate_store(acc, 0.17677669529663687f / ds_scale, kQScale, H16, q + off, dq + off, sm.sn, sm.cs, M, r, c, h,
-                   t);
+  float th[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+  for (int t = 0; t < S; ++t) {
+    const int qi = qbase + 32 * t;
+    if (qi < N) {
+      const int r = qi / M, c = qi - (qi / M) * M;
+      const int64_t off = token_index(g, w.b, w.wy, w.wx, r, c) * rowstride + w.h * D;
+      // dq~ = acc / tau / sqrt(d); the dtheta integrand takes q~ as the dK product saw it
+      unrotate_store(acc[t], 0.17677669529663687f / ds_scale, kQScale, H16, q + off, dq + off, sm.sn, sm.cs, M, r, c,
+                     h, th);
+    }
   }
   const int64_t prow = ((int64_t)w.h * 2 + 1) * (g.B * g.nH * g.nW * nb) + wh / g.heads * nb + qblock;
-  reduce_dtheta<NW>(t, sm.red, partials + prow * 16, lane, wave, tid);
+  reduce_dtheta<NW>(th, sm.red, partials + prow * 16, lane, wave, tid);
 }
 
-template <int NW, int MT>
+template <int NW, int MT, int S>
 __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_mfma_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ delta,
@@ -442,9 +473,9 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_mfma_kernel(
   fill_table(sm.sn, sm.cs, th_row, th_col, w.h, M, threadIdx.x, NW * 64);
   __syncthreads();
   if (window_h16(scal, wh))
-    dq_body<NW, MT, true>(q, k, v, dout, lse, delta, scal, dq, partials, g, nb, NP, sm, w, wh, (int)(lb % nb));
+    dq_body<NW, MT, S, true>(q, k, v, dout, lse, delta, scal, dq, partials, g, nb, NP, sm, w, wh, (int)(lb % nb));
   else
-    dq_body<NW, MT, false>(q, k, v, dout, lse, delta, scal, dq, partials, g, nb, NP, sm, w, wh, (int)(lb % nb));
+    dq_body<NW, MT, S, false>(q, k, v, dout, lse, delta, scal, dq, partials, g, nb, NP, sm, w, wh, (int)(lb % nb));
 }
 
 // -------------------------------------------------------------------------------------- dK / dV
@@ -467,7 +498,9 @@ __host__ __device__ inline size_t dkdv_smem(int NP, int M) {
   return (size_t)CH * 32 * 2 * 3 + kCh * 4 * 2 + (size_t)2 * 2 * M * 8 * 4 + NW * 16 * 4 + 2 * (kCh / 32) * 4 + kCh;
 }
 
-template <int NW, int MT, bool H16>
+// Each wave owns S sets of 32 keys (lane = key within a set); the sets share the LDS reads of the
+// query-side operands (Q^ and dO rows, -LSE and -tau Delta, the transposed Q^T and (g dO)^T).
+template <int NW, int MT, int S, bool H16>
 __device__ inline void dkdv_body(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                                  const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout,
                                  const float* __restrict__ lse, const float* __restrict__ delta,
@@ -512,28 +545,35 @@ __device__ inline void dkdv_body(const uint16_t* __restrict__ q, const uint16_t*
   };
   load_chunk(0);
 
-  // the lane's key: K~ operands, tau * V as bf16 B operands
-  const int kj = kblock * NW * 32 + wave * 32 + col;
-  const bool valid = kj < N;
-  const int r = valid ? kj / M : 0, c = valid ? kj - (kj / M) * M : 0;
-  const int64_t tok = valid ? token_index(g, w.b, w.wy, w.wx, r, c) : 0;
-  const int klab = valid ? token_label(g, w.wy, w.wx, r, c) : 0xff;
-  uint4 kb0 = make_uint4(0, 0, 0, 0), kb1 = kb0, vb0 = kb0, vb1 = kb0;
-  if (valid) {
-    const int64_t off = tok * rowstride + w.h * D;
-    const uint4 k0 = *reinterpret_cast<const uint4*>(k + off + 8 * h);
-    const uint4 k1 = *reinterpret_cast<const uint4*>(k + off + 16 + 8 * h);
-    const uint4 v0 = *reinterpret_cast<const uint4*>(v + off + 8 * h);
-    const uint4 v1 = *reinterpret_cast<const uint4*>(v + off + 16 + 8 * h);
-    kb0 = rotated_part<H16>(k0, sm.sn, sm.cs, M, r, c, h, 1.f);
-    kb1 = rotated_part<H16>(k1, sm.sn, sm.cs, M, r, c, 2 + h, 1.f);
-    vb0 = scaled_part<false>(v0, ds_scale);
-    vb1 = scaled_part<false>(v1, ds_scale);
-  }
-  f32x16_t accv, acck;
+  // the lane's keys (one per set): K~ operands, tau * V as bf16 B operands
+  const int kbase = (kblock * NW + wave) * 32 * S + col;
+  uint4 kb0[S], kb1[S], vb0[S], vb1[S];
+  f32x16_t accv[S], acck[S];
+  int klab[S];
+  uint32_t wl = 0;
 #pragma unroll
-  for (int e = 0; e < 16; ++e) accv[e] = acck[e] = 0.f;
-  const uint32_t wave_labels = uniform(wave_or(valid ? (1u << klab) : 0u));
+  for (int t = 0; t < S; ++t) {
+    const int kj = kbase + 32 * t;
+    const bool valid = kj < N;
+    const int r = valid ? kj / M : 0, c = valid ? kj - (kj / M) * M : 0;
+    klab[t] = valid ? token_label(g, w.wy, w.wx, r, c) : 0xff;
+    wl |= valid ? (1u << klab[t]) : 0u;
+    kb0[t] = kb1[t] = vb0[t] = vb1[t] = make_uint4(0, 0, 0, 0);
+    if (valid) {
+      const int64_t off = token_index(g, w.b, w.wy, w.wx, r, c) * rowstride + w.h * D;
+      const uint4 k0 = *reinterpret_cast<const uint4*>(k + off + 8 * h);
+      const uint4 k1 = *reinterpret_cast<const uint4*>(k + off + 16 + 8 * h);
+      const uint4 v0 = *reinterpret_cast<const uint4*>(v + off + 8 * h);
+      const uint4 v1 = *reinterpret_cast<const uint4*>(v + off + 16 + 8 * h);
+      kb0[t] = rotated_part<H16>(k0, sm.sn, sm.cs, M, r, c, h, 1.f);
+      kb1[t] = rotated_part<H16>(k1, sm.sn, sm.cs, M, r, c, 2 + h, 1.f);
+      vb0[t] = scaled_part<false>(v0, ds_scale);
+      vb1[t] = scaled_part<false>(v1, ds_scale);
+    }
+#pragma unroll
+    for (int e = 0; e < 16; ++e) accv[t][e] = acck[t][e] = 0.f;
+  }
+  const uint32_t wave_labels = uniform(wave_or(wl));
   const bool wave_single = __builtin_popcount(wave_labels) == 1;
   int tlo, thi;
   srow_tr_offsets(lane, tlo, thi);
@@ -573,6 +613,8 @@ __device__ inline void dkdv_body(const uint16_t* __restrict__ q, const uint16_t*
       const uint32_t bl = info & 0x1ffu;
       if ((bl & wave_labels) == 0) continue;
       const bool need_mask = ((info >> 10) & 1u) || !wave_single || bl != wave_labels;
+      const uint16_t* Qb = sm.Q + qb * 1024;
+      const uint16_t* Gb = sm.G + qb * 1024;
       // -LSE and -tau Delta of the 16 query rows this lane's accumulators hold: 8g + 4h + j
       f32x16_t cL, cD;
 #pragma unroll
@@ -588,67 +630,91 @@ __device__ inline void dkdv_body(const uint16_t* __restrict__ q, const uint16_t*
         cD[4 * gq + 2] = d4.z;
         cD[4 * gq + 3] = d4.w;
       }
-      const uint16_t* Qb = sm.Q + qb * 1024;
-      const uint16_t* Gb = sm.G + qb * 1024;
-      f32x16_t s = mfma_op<H16>(*reinterpret_cast<const uint4*>(Qb + ro0), kb0, cL);
-      s = mfma_op<H16>(*reinterpret_cast<const uint4*>(Qb + ro1), kb1, s);
-      f32x16_t dp = mfma_op<false>(*reinterpret_cast<const uint4*>(Gb + ro0), vb0, cD);
-      dp = mfma_op<false>(*reinterpret_cast<const uint4*>(Gb + ro1), vb1, dp);
-      float p[16];
-      if (need_mask) {
-        const uint32_t live = live_bits(sm.lab, qb, h, klab);
+      const uint4 qa0 = *reinterpret_cast<const uint4*>(Qb + ro0);
+      const uint4 qa1 = *reinterpret_cast<const uint4*>(Qb + ro1);
+      const uint4 ga0 = *reinterpret_cast<const uint4*>(Gb + ro0);
+      const uint4 ga1 = *reinterpret_cast<const uint4*>(Gb + ro1);
+      // S = Q^ K~^T from -LSE, tau (dP - Delta) = dO (tau V)^T from -tau Delta
+      f32x16_t sc[S], dc[S];
 #pragma unroll
-        for (int e = 0; e < 16; ++e) p[e] = ((live >> e) & 1u) ? __builtin_amdgcn_exp2f(s[e]) : 0.f;
-      } else {
-#pragma unroll
-        for (int e = 0; e < 16; ++e) p[e] = __builtin_amdgcn_exp2f(s[e]);
+      for (int t = 0; t < S; ++t) {
+        sc[t] = mfma_op<H16>(qa1, kb1[t], mfma_op<H16>(qa0, kb0[t], cL));
+        dc[t] = mfma_op<false>(ga1, vb1[t], mfma_op<false>(ga0, vb0[t], cD));
       }
-      uint32_t pp[8], pd[8];
-      if constexpr (H16) {
-        // tau dS = P * tau (dP - Delta) as a packed fp16 product of the fp16 operands
+      // P = exp2(S), tau dS = P * tau (dP - Delta)
+      uint32_t pp[S][8], pd[S][8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          pp[e] = pack2h(p[2 * e], p[2 * e + 1]);
-          const f16x2_t a = __builtin_bit_cast(f16x2_t, pp[e]);
-          const f16x2_t b = __builtin_bit_cast(f16x2_t, pack2h(dp[2 * e], dp[2 * e + 1]));
-          pd[e] = __builtin_bit_cast(uint32_t, a * b);
+      for (int t = 0; t < S; ++t) {
+        float p[16];
+        if (need_mask) {
+          const uint32_t live = live_bits(sm.lab, qb, h, klab[t]);
+#pragma unroll
+          for (int e = 0; e < 16; ++e) p[e] = ((live >> e) & 1u) ? __builtin_amdgcn_exp2f(sc[t][e]) : 0.f;
+        } else {
+#pragma unroll
+          for (int e = 0; e < 16; ++e) p[e] = __builtin_amdgcn_exp2f(sc[t][e]);
         }
-      } else {
+        if constexpr (H16) {
+          // tau dS as a packed fp16 product of the fp16 P and tau (dP - Delta)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          pp[e] = pack2(p[2 * e], p[2 * e + 1]);
-          pd[e] = pack2(p[2 * e] * dp[2 * e], p[2 * e + 1] * dp[2 * e + 1]);
+          for (int e = 0; e < 8; ++e) {
+            pp[t][e] = pack2h(p[2 * e], p[2 * e + 1]);
+            const f16x2_t a = __builtin_bit_cast(f16x2_t, pp[t][e]);
+            const f16x2_t b = __builtin_bit_cast(f16x2_t, pack2h(dc[t][2 * e], dc[t][2 * e + 1]));
+            pd[t][e] = __builtin_bit_cast(uint32_t, a * b);
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            pp[t][e] = pack2(p[2 * e], p[2 * e + 1]);
+            pd[t][e] = pack2(p[2 * e] * dc[t][2 * e], p[2 * e + 1] * dc[t][2 * e + 1]);
+          }
         }
       }
+      // dV^T += (g dO)^T P, dK~^T += Q^T (tau dS)
       const uint16_t* Gsb = sm.Gs + qb * 1024;
-      accv = mfma_op<H16>(tr_operand_at(Gsb, tlo, thi), make_uint4(pp[0], pp[1], pp[2], pp[3]), accv);
-      accv = mfma_op<H16>(tr_operand_at(Gsb + 512, tlo, thi), make_uint4(pp[4], pp[5], pp[6], pp[7]), accv);
-      acck = mfma_op<H16>(tr_operand_at(Qb, tlo, thi), make_uint4(pd[0], pd[1], pd[2], pd[3]), acck);
-      acck = mfma_op<H16>(tr_operand_at(Qb + 512, tlo, thi), make_uint4(pd[4], pd[5], pd[6], pd[7]), acck);
-      __builtin_amdgcn_sched_barrier(0);  // keep blocks apart: bounded register pressure
+      const uint4 gt0 = tr_operand_at(Gsb, tlo, thi);
+      const uint4 gt1 = tr_operand_at(Gsb + 512, tlo, thi);
+#pragma unroll
+      for (int t = 0; t < S; ++t) {
+        accv[t] = mfma_op<H16>(gt0, make_uint4(pp[t][0], pp[t][1], pp[t][2], pp[t][3]), accv[t]);
+        accv[t] = mfma_op<H16>(gt1, make_uint4(pp[t][4], pp[t][5], pp[t][6], pp[t][7]), accv[t]);
+      }
+      const uint4 qt0 = tr_operand_at(Qb, tlo, thi);
+      const uint4 qt1 = tr_operand_at(Qb + 512, tlo, thi);
+#pragma unroll
+      for (int t = 0; t < S; ++t) {
+        acck[t] = mfma_op<H16>(qt0, make_uint4(pd[t][0], pd[t][1], pd[t][2], pd[t][3]), acck[t]);
+        acck[t] = mfma_op<H16>(qt1, make_uint4(pd[t][4], pd[t][5], pd[t][6], pd[t][7]), acck[t]);
+      }
     }
   }
 
-  float t[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  if (valid) {
-    const int64_t off = tok * rowstride + w.h * D;
-    // dV = accv / g: lane holds channels 8g + 4h + j of its key
-    const float inv_g = 1.f / g_scale;
+  float th[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  const float inv_g = 1.f / g_scale;
 #pragma unroll
-    for (int gq = 0; gq < 4; ++gq) {
-      uint2 o;
-      o.x = pack2(accv[4 * gq] * inv_g, accv[4 * gq + 1] * inv_g);
-      o.y = pack2(accv[4 * gq + 2] * inv_g, accv[4 * gq + 3] * inv_g);
-      *reinterpret_cast<uint2*>(dv + off + 8 * gq + 4 * h) = o;
+  for (int t = 0; t < S; ++t) {
+    const int kj = kbase + 32 * t;
+    if (kj < N) {
+      const int r = kj / M, c = kj - (kj / M) * M;
+      const int64_t off = token_index(g, w.b, w.wy, w.wx, r, c) * rowstride + w.h * D;
+      // dV = accv / g: lane holds channels 8g + 4h + j of its key
+#pragma unroll
+      for (int gq = 0; gq < 4; ++gq) {
+        uint2 o;
+        o.x = pack2(accv[t][4 * gq] * inv_g, accv[t][4 * gq + 1] * inv_g);
+        o.y = pack2(accv[t][4 * gq + 2] * inv_g, accv[t][4 * gq + 3] * inv_g);
+        *reinterpret_cast<uint2*>(dv + off + 8 * gq + 4 * h) = o;
+      }
+      // dk~ = acck * ln 2 / tau (the Q operand carried log2(e) / sqrt(d))
+      unrotate_store(acck[t], kLn2 / ds_scale, 1.0f, H16, k + off, dk + off, sm.sn, sm.cs, M, r, c, h, th);
     }
-    // dk~ = acck * ln 2 / tau (the Q operand carried log2(e) / sqrt(d))
-    unrotate_store(acck, kLn2 / ds_scale, 1.0f, H16, k + off, dk + off, sm.sn, sm.cs, M, r, c, h, t);
   }
   const int64_t prow = ((int64_t)w.h * 2 + 0) * (g.B * g.nH * g.nW * nb) + wh / g.heads * nb + kblock;
-  reduce_dtheta<NW>(t, sm.red, partials + prow * 16, lane, wave, tid);
+  reduce_dtheta<NW>(th, sm.red, partials + prow * 16, lane, wave, tid);
 }
 
-template <int NW, int MT>
+template <int NW, int MT, int S>
 __global__ __launch_bounds__(NW * 64, 2) void bwd_dkdv_mfma_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ delta,
@@ -676,28 +742,42 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dkdv_mfma_kernel(
   fill_table(sm.sn, sm.cs, th_row, th_col, w.h, M, threadIdx.x, NW * 64);
   __syncthreads();
   if (window_h16(scal, wh))
-    dkdv_body<NW, MT, true>(q, k, v, dout, lse, delta, scal, dk, dv, partials, g, nb, NP, sm, w, wh,
-                            (int)(lb % nb));
+    dkdv_body<NW, MT, S, true>(q, k, v, dout, lse, delta, scal, dk, dv, partials, g, nb, NP, sm, w, wh,
+                               (int)(lb % nb));
   else
-    dkdv_body<NW, MT, false>(q, k, v, dout, lse, delta, scal, dk, dv, partials, g, nb, NP, sm, w, wh,
-                             (int)(lb % nb));
+    dkdv_body<NW, MT, S, false>(q, k, v, dout, lse, delta, scal, dk, dv, partials, g, nb, NP, sm, w, wh,
+                                (int)(lb % nb));
 }
 
-template <int NW, int MT>
+// Waves per workgroup and 32-token sets per wave for N tokens per window; the workgroups of a
+// window-head each cover waves * sets * 32 tokens of the stationary side.
+struct MainShape {
+  int waves, sets;
+};
+MainShape main_shape(int N) {
+  if (N > 128) return {8, 2};
+  return {N > 64 ? 4 : 2, 1};
+}
+int64_t blocks_per_windowhead(int N) {
+  const MainShape m = main_shape(N);
+  return (N + m.waves * m.sets * 32 - 1) / (m.waves * m.sets * 32);
+}
+
+template <int NW, int MT, int S>
 hipError_t launch_main(const BwdArgs& a, hipStream_t st) {
   const Geom& g = a.g;
   const int64_t nwh = g.B * g.nH * g.nW * g.heads;
   const int NP = (g.N + 31) / 32 * 32;
-  const int nb = (g.N + NW * 32 - 1) / (NW * 32);
+  const int nb = (int)blocks_per_windowhead(g.N);
   const int64_t blocks = nwh * nb;
-  hipLaunchKernelGGL((bwd_dkdv_mfma_kernel<NW, MT>), dim3((unsigned)blocks), dim3(NW * 64), dkdv_smem<NW>(NP, g.M),
-                     st, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (const uint16_t*)a.dout,
-                     a.lse, a.delta, a.scal, a.th_row, a.th_col, (uint16_t*)a.dk, (uint16_t*)a.dv, a.partials, g, nb,
-                     NP);
+  hipLaunchKernelGGL((bwd_dkdv_mfma_kernel<NW, MT, S>), dim3((unsigned)blocks), dim3(NW * 64),
+                     dkdv_smem<NW>(NP, g.M), st, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
+                     (const uint16_t*)a.dout, a.lse, a.delta, a.scal, a.th_row, a.th_col, (uint16_t*)a.dk,
+                     (uint16_t*)a.dv, a.partials, g, nb, NP);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((bwd_dq_mfma_kernel<NW, MT>), dim3((unsigned)blocks), dim3(NW * 64), dq_smem<NW>(NP, g.M), st,
-                     (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (const uint16_t*)a.dout,
+  hipLaunchKernelGGL((bwd_dq_mfma_kernel<NW, MT, S>), dim3((unsigned)blocks), dim3(NW * 64), dq_smem<NW>(NP, g.M),
+                     st, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (const uint16_t*)a.dout,
                      a.lse, a.delta, a.scal, a.th_row, a.th_col, (uint16_t*)a.dq, a.partials, g, nb, NP);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -705,14 +785,10 @@ hipError_t launch_main(const BwdArgs& a, hipStream_t st) {
   return launch_dtheta_reduce(a.partials, a.n_partials, rows_per_head, g, a.dth_row, a.dth_col, st);
 }
 
-int waves_for(int N) { return N > 128 ? 8 : N > 64 ? 4 : 2; }
-
 }  // namespace
 
 int64_t bwd_mfma_partials(const Geom& g) {
-  const int nw = waves_for(g.N);
-  const int64_t nb = (g.N + nw * 32 - 1) / (nw * 32);
-  return (int64_t)g.heads * 2 * g.B * g.nH * g.nW * nb;
+  return (int64_t)g.heads * 2 * g.B * g.nH * g.nW * blocks_per_windowhead(g.N);
 }
 
 hipError_t launch_bwd_mfma(const BwdArgs& a, hipStream_t st) {
@@ -723,13 +799,12 @@ hipError_t launch_bwd_mfma(const BwdArgs& a, hipStream_t st) {
                      a.delta, a.scal, g);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (g.M == 32) return launch_main<8, 32>(a, st);
-  if (g.M == 8) return launch_main<2, 8>(a, st);
-  switch (waves_for(g.N)) {
-    case 8: return launch_main<8, 0>(a, st);
-    case 4: return launch_main<4, 0>(a, st);
-    default: return launch_main<2, 0>(a, st);
-  }
+  if (g.M == 32) return launch_main<8, 32, 2>(a, st);
+  if (g.M == 8) return launch_main<2, 8, 1>(a, st);
+  const MainShape m = main_shape(g.N);
+  if (m.waves == 8) return launch_main<8, 0, 2>(a, st);
+  if (m.waves == 4) return launch_main<4, 0, 1>(a, st);
+  return launch_main<2, 0, 1>(a, st);
 }
 
 }  // namespace fsw

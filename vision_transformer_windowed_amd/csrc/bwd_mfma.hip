@@ -36,7 +36,7 @@ namespace fsw {
 
 namespace {
 
-constexpr int kCh = 128;  // tokens per LDS chunk
+constexpr int kCh = 128;  // tokens per LDS chunk (a multiple of 128)
 constexpr float kSqrt2 = 1.4142135623730951f;
 constexpr float kQScale = kLog2e * 0.17677669529663687f;  // log2(e) / sqrt(32)
 
@@ -377,8 +377,15 @@ __device__ inline void dq_body(const uint16_t* __restrict__ q, const uint16_t* _
     __syncthreads();
     if (c0 + CH < NP) load_chunk(c0 + CH);
     if (wave_labels == 0) continue;
-    const uint4 bw = *reinterpret_cast<const uint4*>(sm.blk + buf * (kCh / 32));
-    const uint32_t info4[4] = {uniform(bw.x), uniform(bw.y), uniform(bw.z), uniform(bw.w)};
+    uint32_t info4[kCh / 32];
+#pragma unroll
+    for (int i = 0; i < kCh / 128; ++i) {
+      const uint4 bw = *reinterpret_cast<const uint4*>(sm.blk + buf * (kCh / 32) + 4 * i);
+      info4[4 * i] = uniform(bw.x);
+      info4[4 * i + 1] = uniform(bw.y);
+      info4[4 * i + 2] = uniform(bw.z);
+      info4[4 * i + 3] = uniform(bw.w);
+    }
     const int nblk = min(CH, NP - c0) >> 5;
 #pragma unroll
     for (int kb = 0; kb < kCh / 32; ++kb) {
@@ -603,8 +610,15 @@ __device__ inline void dkdv_body(const uint16_t* __restrict__ q, const uint16_t*
     __syncthreads();
     if (c0 + CH < NP) load_chunk(c0 + CH);
     if (wave_labels == 0) continue;
-    const uint4 bw = *reinterpret_cast<const uint4*>(sm.blk + buf * (kCh / 32));
-    const uint32_t info4[4] = {uniform(bw.x), uniform(bw.y), uniform(bw.z), uniform(bw.w)};
+    uint32_t info4[kCh / 32];
+#pragma unroll
+    for (int i = 0; i < kCh / 128; ++i) {
+      const uint4 bw = *reinterpret_cast<const uint4*>(sm.blk + buf * (kCh / 32) + 4 * i);
+      info4[4 * i] = uniform(bw.x);
+      info4[4 * i + 1] = uniform(bw.y);
+      info4[4 * i + 2] = uniform(bw.z);
+      info4[4 * i + 3] = uniform(bw.w);
+    }
     const int nblk = min(CH, NP - c0) >> 5;
 #pragma unroll
     for (int qb = 0; qb < kCh / 32; ++qb) {

@@ -38,6 +38,7 @@ namespace {
 
 constexpr float kLowSum = 8.271806125530277e-25f;  // 2^-80
 constexpr int kMaxWaves = 16;
+constexpr int kMaxQBlocks = 2;
 
 __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 __device__ __forceinline__ uint32_t uniform(uint32_t x) { return (uint32_t)__builtin_amdgcn_readfirstlane((int)x); }
@@ -253,8 +254,9 @@ __device__ __forceinline__ void load_kv(const uint16_t* __restrict__ k, const ui
   }
 }
 
-// NWAVES waves of one 32-query tile each.  MT: compile-time window size (0 = g.M at run time).
-// NPMAX: the largest padded window this configuration serves.
+// NWAVES waves of one 32-query tile each; one workgroup per window-head stages the window's K/V
+// once and then walks its query blocks of NWAVES*32 queries.  MT: compile-time window size
+// (0 = g.M at run time).  NPMAX: the largest padded window this configuration serves.
 template <int NWAVES, int MT, int NPMAX>
 __global__ __launch_bounds__(NWAVES * 64) void fwd_mfma_kernel(const uint16_t* __restrict__ q,
                                                                const uint16_t* __restrict__ k,
@@ -267,15 +269,16 @@ __global__ __launch_bounds__(NWAVES * 64) void fwd_mfma_kernel(const uint16_t* _
   constexpr int D = 32;
   constexpr int NT = NWAVES * 64;
   constexpr int MAXIT = (NPMAX * 4 + NT - 1) / NT;
+  constexpr int QBM = (NPMAX + NWAVES * 32 - 1) / (NWAVES * 32);  // query blocks per window, at most
   static_assert(NWAVES <= kMaxWaves, "too many waves");
+  static_assert(QBM <= kMaxQBlocks, "too many query blocks");
   const int M = MT > 0 ? MT : g.M;
   const int N = M * M;
   const int NB = NP / 32;
   const FwdSmem sm = carve(smem_raw, NP, M);
 
-  const int64_t blk = xcd_order(blockIdx.x, gridDim.x);  // a window's heads and query blocks share one L2
-  const WinHead w = decode_winhead(g, blk / nqb);
-  const int qblock = (int)(blk % nqb);
+  const int64_t wh = xcd_order(blockIdx.x, gridDim.x);  // a window's heads share one L2
+  const WinHead w = decode_winhead(g, wh);
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -283,19 +286,22 @@ __global__ __launch_bounds__(NWAVES * 64) void fwd_mfma_kernel(const uint16_t* _
   const int h = lane >> 5;
   const int col = lane & 31;
 
-  // 0. every global load of the thread first (K and V items, the query), so they overlap
+  // 0. every global load of the thread first (K and V items, the queries of every block)
   uint4 kraw[MAXIT], vraw[MAXIT];
   load_kv<MAXIT>(k, v, g, w, M, NP, tid, NT, true, kraw, vraw);
-  const int qi = qblock * NT / 2 + wave * 32 + col;
-  const bool qvalid = qi < N;
-  const int qr = qvalid ? qi / M : 0, qc = qvalid ? qi - (qi / M) * M : 0;
-  const int64_t qtok = qvalid ? tok_of(g, w, M, qr, qc) : 0;
-  uint4 qraw0 = make_uint4(0, 0, 0, 0), qraw1 = qraw0;
-  if (qvalid) {
-    const int64_t off = qtok * rowstride + w.h * D;
-    qraw0 = *reinterpret_cast<const uint4*>(q + off + 8 * h);
-    qraw1 = *reinterpret_cast<const uint4*>(q + off + 16 + 8 * h);
-  }
+  // the lane's query of block qb (two 16-byte halves: channels 8h.., 16+8h..)
+  auto load_q = [&](int qb, uint4& a, uint4& b) {
+    const int qi = qb * NT / 2 + wave * 32 + col;
+    a = b = make_uint4(0, 0, 0, 0);
+    if (qb < nqb && qi < N) {
+      const int64_t off = tok_of(g, w, M, qi / M, qi - (qi / M) * M) * rowstride + w.h * D;
+      a = *reinterpret_cast<const uint4*>(q + off + 8 * h);
+      b = *reinterpret_cast<const uint4*>(q + off + 16 + 8 * h);
+    }
+  };
+  uint4 qraw[QBM][2];
+#pragma unroll
+  for (int qb = 0; qb < QBM; ++qb) load_q(qb, qraw[qb][0], qraw[qb][1]);
 
   // 1. RoPE sin/cos table and key labels (while the loads are in flight)
   for (int i = tid; i < 2 * M * 8; i += NT) {
@@ -334,20 +340,24 @@ __global__ __launch_bounds__(NWAVES * 64) void fwd_mfma_kernel(const uint16_t* _
     sm.blk[b] = bits | (full << 9);
   }
   const float qscale = kLog2e * 0.17677669529663687f;  // log2(e) / sqrt(32)
-  float qn2 = 0.f;
-  {
-    float x[8], y[8];
-    unpack8(qraw0, x);
-    unpack8(qraw1, y);
+  float qn2max[QBM];
+#pragma unroll
+  for (int qb = 0; qb < QBM; ++qb) {
+    float x[8], y[8], qn2 = 0.f;
+    unpack8(qraw[qb][0], x);
+    unpack8(qraw[qb][1], y);
 #pragma unroll
     for (int e = 0; e < 8; ++e) qn2 = __builtin_fmaf(x[e], x[e], __builtin_fmaf(y[e], y[e], qn2));
+    qn2 += __shfl_xor(qn2, 32, 64);
+    qn2max[qb] = wave_max(qn2) * (qscale * qscale);
   }
-  qn2 += __shfl_xor(qn2, 32, 64);
-  const float qn2max = wave_max(qn2) * (qscale * qscale);
   kmax2 = wave_max(kmax2);
   if (lane == 0) {
+    float qm = 0.f;
+#pragma unroll
+    for (int qb = 0; qb < QBM; ++qb) qm = fmaxf(qm, qn2max[qb]);
     sm.red[wave] = kmax2;
-    sm.red[kMaxWaves + wave] = qn2max;
+    sm.red[kMaxWaves + wave] = qm;
   }
   __syncthreads();
   float kmax2_all = 0.f, qmax2_all = 0.f;
@@ -365,27 +375,6 @@ __global__ __launch_bounds__(NWAVES * 64) void fwd_mfma_kernel(const uint16_t* _
     stage_k<MAXIT>(sm, kraw, M, NP, tid, NT, false);
     __syncthreads();
   }
-
-  // 3. the wave's query operands (rotated, scaled by log2(e)/sqrt(d)), reference bound, labels
-  uint4 qb0, qb1;
-  {
-    float x[8], y[8];
-    unpack8(qraw0, x);
-    unpack8(qraw1, y);
-    rotate8(x, sm.sn, sm.cs, 0, M, qr, 4 * h);
-    rotate8(y, sm.sn, sm.cs, 1, M, qc, 4 * h);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      x[e] *= qscale;
-      y[e] *= qscale;
-    }
-    qb0 = pack8_op(x, h16);
-    qb1 = pack8_op(y, h16);
-  }
-  const float bound = sqrtf(qn2max) * kmax;  // >= every score of this wave (log2 units)
-  const int qlab = qvalid ? token_label(g, w.wy, w.wx, qr, qc) : 0xff;
-  const uint32_t wave_labels = uniform(wave_or(qvalid ? 1u << qlab : 0u));
-  const bool wave_single = __builtin_popcount(wave_labels) == 1;
   // window summary over its blocks: one label everywhere and every block whole
   uint32_t wb = 0xffffffffu, wor = 0;
   for (int b = lane; b < NB; b += 64) {
@@ -398,31 +387,68 @@ __global__ __launch_bounds__(NWAVES * 64) void fwd_mfma_kernel(const uint16_t* _
     wb &= (uint32_t)__shfl_xor((int)wb, o2, 64);
     wor |= (uint32_t)__shfl_xor((int)wor, o2, 64);
   }
-  const bool uniform_win =
-      uniform((int)(((wb >> 9) & 1u) && __builtin_popcount(wor) == 1 && wor == wave_labels && (NB % 2) == 0)) != 0;
 
-  f32x16_t o;
-  float l = 0.f, ref;
 #pragma unroll
-  for (int v2 = 0; v2 < 16; ++v2) o[v2] = 0.f;
-  if (h16)
-    attend<true>(sm, NB, lane, uniform_win, wave_labels, wave_single, qb0, qb1, qlab, qvalid, bound, ref, l, o);
-  else
-    attend<false>(sm, NB, lane, uniform_win, wave_labels, wave_single, qb0, qb1, qlab, qvalid, bound, ref, l, o);
-
-  // 4. epilogue: O = O^T / l (lane: query col, channels 8g + 4h + j), LSE = (ref + log2 l) ln 2
-  const float lt = l + __shfl_xor(l, 32, 64);
-  if (qvalid) {
-    const float inv = 1.f / lt;
-    uint16_t* dst = out + qtok * rowstride + w.h * D + 4 * h;
+  for (int qb = 0; qb < QBM; ++qb) {
+    if (qb >= nqb) break;
+    // 3. the wave's query operands (rotated, scaled by log2(e)/sqrt(d)), reference bound, labels
+    const int qi = qb * NT / 2 + wave * 32 + col;
+    const bool qvalid = qi < N;
+    const int qr = qvalid ? qi / M : 0, qc = qvalid ? qi - (qi / M) * M : 0;
+    uint4 qb0, qb1;
+    {
+      // reloaded (an L2 hit): keeping every block's raw query live across attend() costs registers
+      uint4 qa, qc2;
+      if (qb == 0) {
+        qa = qraw[0][0];
+        qc2 = qraw[0][1];
+      } else {
+        load_q(qb, qa, qc2);
+      }
+      float x[8], y[8];
+      unpack8(qa, x);
+      unpack8(qc2, y);
+      rotate8(x, sm.sn, sm.cs, 0, M, qr, 4 * h);
+      rotate8(y, sm.sn, sm.cs, 1, M, qc, 4 * h);
 #pragma unroll
-    for (int gq = 0; gq < 4; ++gq) {
-      uint2 pr;
-      pr.x = pack2(o[4 * gq] * inv, o[4 * gq + 1] * inv);
-      pr.y = pack2(o[4 * gq + 2] * inv, o[4 * gq + 3] * inv);
-      *reinterpret_cast<uint2*>(dst + 8 * gq) = pr;
+      for (int e = 0; e < 8; ++e) {
+        x[e] *= qscale;
+        y[e] *= qscale;
+      }
+      qb0 = pack8_op(x, h16);
+      qb1 = pack8_op(y, h16);
     }
-    if (lse && h == 0) lse[qtok * g.heads + w.h] = (ref + __log2f(lt)) * kLn2;
+    const float bound = sqrtf(qn2max[qb]) * kmax;  // >= every score of this wave (log2 units)
+    const int qlab = qvalid ? token_label(g, w.wy, w.wx, qr, qc) : 0xff;
+    const uint32_t wave_labels = uniform(wave_or(qvalid ? 1u << qlab : 0u));
+    const bool wave_single = __builtin_popcount(wave_labels) == 1;
+    const bool uniform_win = uniform((int)(((wb >> 9) & 1u) && __builtin_popcount(wor) == 1 &&
+                                           wor == wave_labels && (NB % 2) == 0)) != 0;
+
+    f32x16_t o;
+    float l = 0.f, ref;
+#pragma unroll
+    for (int v2 = 0; v2 < 16; ++v2) o[v2] = 0.f;
+    if (h16)
+      attend<true>(sm, NB, lane, uniform_win, wave_labels, wave_single, qb0, qb1, qlab, qvalid, bound, ref, l, o);
+    else
+      attend<false>(sm, NB, lane, uniform_win, wave_labels, wave_single, qb0, qb1, qlab, qvalid, bound, ref, l, o);
+
+    // 4. epilogue: O = O^T / l (lane: query col, channels 8g + 4h + j), LSE = (ref + log2 l) ln 2
+    const float lt = l + __shfl_xor(l, 32, 64);
+    if (qvalid) {
+      const int64_t qtok = tok_of(g, w, M, qr, qc);
+      const float inv = 1.f / lt;
+      uint16_t* dst = out + qtok * rowstride + w.h * D + 4 * h;
+#pragma unroll
+      for (int gq = 0; gq < 4; ++gq) {
+        uint2 pr;
+        pr.x = pack2(o[4 * gq] * inv, o[4 * gq + 1] * inv);
+        pr.y = pack2(o[4 * gq + 2] * inv, o[4 * gq + 3] * inv);
+        *reinterpret_cast<uint2*>(dst + 8 * gq) = pr;
+      }
+      if (lse && h == 0) lse[qtok * g.heads + w.h] = (ref + __log2f(lt)) * kLn2;
+    }
   }
 }
 
@@ -437,7 +463,7 @@ hipError_t launch_nw(const FwdArgs& a, hipStream_t st) {
     (void)hipFuncSetAttribute((const void*)fwd_mfma_kernel<NWAVES, MT, NPMAX>,
                               hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
   });
-  const int64_t blocks = g.B * g.nH * g.nW * g.heads * nqb;
+  const int64_t blocks = g.B * g.nH * g.nW * g.heads;
   hipLaunchKernelGGL((fwd_mfma_kernel<NWAVES, MT, NPMAX>), dim3((unsigned)blocks), dim3(NWAVES * 64), smem, st,
                      (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, a.th_row, a.th_col,
                      (uint16_t*)a.out, a.lse, g, nqb, NP);

@@ -178,57 +178,70 @@ __device__ __forceinline__ uint4 scaled_part(uint4 raw, float scale) {
 // ------------------------------------------------------------------------------------ prologue
 
 // One workgroup per window-head: Delta for every token, and
-// scal[wh] = {max |dO|, max |v|, max |q|, max |k|} over the window's components.
-__global__ __launch_bounds__(256) void bwd_pre_kernel(const uint16_t* __restrict__ out,
-                                                      const uint16_t* __restrict__ dout,
-                                                      const uint16_t* __restrict__ v,
-                                                      const uint16_t* __restrict__ q,
-                                                      const uint16_t* __restrict__ k, float* __restrict__ delta,
-                                                      float* __restrict__ scal, Geom g) {
-  __shared__ float red[4][4];
+// scal[wh] = {max |dO|, max |v|, max |q|, max |k|} over the window's components.  Each thread
+// handles kPreBatch 8-channel items per step with all of their 5 x 16-byte loads issued together.
+constexpr int kPreThreads = 256;
+constexpr int kPreBatch = 4;
+__global__ __launch_bounds__(kPreThreads) void bwd_pre_kernel(const uint16_t* __restrict__ out,
+                                                              const uint16_t* __restrict__ dout,
+                                                              const uint16_t* __restrict__ v,
+                                                              const uint16_t* __restrict__ q,
+                                                              const uint16_t* __restrict__ k,
+                                                              float* __restrict__ delta, float* __restrict__ scal,
+                                                              Geom g) {
+  __shared__ float red[4][kPreThreads / 64];
   const int64_t wh = xcd_order(blockIdx.x, gridDim.x);
   const WinHead w = decode_winhead(g, wh);
   const int tid = threadIdx.x;
   const int64_t rowstride = (int64_t)g.heads * 32;
   float mx[4] = {0.f, 0.f, 0.f, 0.f};
   const int items = g.N * 4;
-  const int iters = (items + 255) / 256;
-  for (int i = 0; i < iters; ++i) {  // uniform trip count: the shuffles below see every lane
-    const int it = i * 256 + tid;
-    float s = 0.f;
-    int64_t tok = 0;
-    const bool ok = it < items;
-    if (ok) {
-      const int n = it >> 2, part = it & 3;
-      const int r = n / g.M, c = n - (n / g.M) * g.M;
-      tok = token_index(g, w.b, w.wy, w.wx, r, c);
-      const int64_t off = tok * rowstride + w.h * 32 + part * 8;
-      const uint4 ro = *reinterpret_cast<const uint4*>(out + off);
-      const uint4 rd = *reinterpret_cast<const uint4*>(dout + off);
-      const uint4 rv = *reinterpret_cast<const uint4*>(v + off);
-      const uint4 rq = *reinterpret_cast<const uint4*>(q + off);
-      const uint4 rk = *reinterpret_cast<const uint4*>(k + off);
-      float o[8], d[8], x[8];
-      unpack8(ro, o);
-      unpack8(rd, d);
+  const int steps = (items + kPreThreads * kPreBatch - 1) / (kPreThreads * kPreBatch);
+  for (int st = 0; st < steps; ++st) {  // uniform trip count: the shuffles below see every lane
+    uint4 ro[kPreBatch], rd[kPreBatch], rv[kPreBatch], rq[kPreBatch], rk[kPreBatch];
+    int64_t tok[kPreBatch];
+#pragma unroll
+    for (int u = 0; u < kPreBatch; ++u) {
+      const int it = (st * kPreBatch + u) * kPreThreads + tid;
+      ro[u] = rd[u] = rv[u] = rq[u] = rk[u] = make_uint4(0, 0, 0, 0);
+      tok[u] = 0;
+      if (it < items) {
+        const int n = it >> 2, part = it & 3;
+        const int r = n / g.M, c = n - (n / g.M) * g.M;
+        tok[u] = token_index(g, w.b, w.wy, w.wx, r, c);
+        const int64_t off = tok[u] * rowstride + w.h * 32 + part * 8;
+        ro[u] = *reinterpret_cast<const uint4*>(out + off);
+        rd[u] = *reinterpret_cast<const uint4*>(dout + off);
+        rv[u] = *reinterpret_cast<const uint4*>(v + off);
+        rq[u] = *reinterpret_cast<const uint4*>(q + off);
+        rk[u] = *reinterpret_cast<const uint4*>(k + off);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kPreBatch; ++u) {
+      const int it = (st * kPreBatch + u) * kPreThreads + tid;
+      float o[8], d[8], x[8], s = 0.f;
+      unpack8(ro[u], o);
+      unpack8(rd[u], d);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         s = __builtin_fmaf(o[e], d[e], s);
         mx[0] = fmaxf(mx[0], fabsf(d[e]));
       }
-      unpack8(rv, x);
+      unpack8(rv[u], x);
 #pragma unroll
       for (int e = 0; e < 8; ++e) mx[1] = fmaxf(mx[1], fabsf(x[e]));
-      unpack8(rq, x);
+      unpack8(rq[u], x);
 #pragma unroll
       for (int e = 0; e < 8; ++e) mx[2] = fmaxf(mx[2], fabsf(x[e]));
-      unpack8(rk, x);
+      unpack8(rk[u], x);
 #pragma unroll
       for (int e = 0; e < 8; ++e) mx[3] = fmaxf(mx[3], fabsf(x[e]));
+      // Delta of the token: the four 8-channel parts sit in four consecutive lanes
+      s += __shfl_xor(s, 1, 64);
+      s += __shfl_xor(s, 2, 64);
+      if (it < items && (it & 3) == 0) delta[tok[u] * g.heads + w.h] = s;
     }
-    s += __shfl_xor(s, 1, 64);
-    s += __shfl_xor(s, 2, 64);
-    if (ok && (it & 3) == 0) delta[tok * g.heads + w.h] = s;
   }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -236,7 +249,12 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const uint16_t* __restrict
     if ((tid & 63) == 0) red[i][tid >> 6] = mx[i];
   }
   __syncthreads();
-  if (tid < 4) scal[wh * 4 + tid] = fmaxf(fmaxf(red[tid][0], red[tid][1]), fmaxf(red[tid][2], red[tid][3]));
+  if (tid < 4) {
+    float m = 0.f;
+#pragma unroll
+    for (int j = 0; j < kPreThreads / 64; ++j) m = fmaxf(m, red[tid][j]);
+    scal[wh * 4 + tid] = m;
+  }
 }
 
 // Label of chunk token n (0xff past the window) and its block summary bit (bit L for label L,
@@ -808,7 +826,7 @@ int64_t bwd_mfma_partials(const Geom& g) {
 hipError_t launch_bwd_mfma(const BwdArgs& a, hipStream_t st) {
   const Geom& g = a.g;
   const int64_t nwh = g.B * g.nH * g.nW * g.heads;
-  hipLaunchKernelGGL(bwd_pre_kernel, dim3((unsigned)nwh), dim3(256), 0, st, (const uint16_t*)a.out,
+  hipLaunchKernelGGL(bwd_pre_kernel, dim3((unsigned)nwh), dim3(kPreThreads), 0, st, (const uint16_t*)a.out,
                      (const uint16_t*)a.dout, (const uint16_t*)a.v, (const uint16_t*)a.q, (const uint16_t*)a.k,
                      a.delta, a.scal, g);
   hipError_t e = hipGetLastError();

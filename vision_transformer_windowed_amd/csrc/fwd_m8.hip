@@ -1,0 +1,298 @@
+// bf16 window-attention forward for M = 8 windows (N = 64 tokens), d = 32, on MFMA (gfx950).
+//
+// Exact softmax attention inside each window with window-local 2D RoPE on Q and K (FlashSwin paper
+// card, "FLASHSWIN: Unlocking Large Windows and Dense Tokens in Swin Vision Transformers with Memory
+// Efficient Attention": Abstract; Figure 1(B)).  Small windows move ~12 KB per window-head for
+// ~0.5 MFLOP, so this path is bound by HBM and by load latency, not by the matrix cores.
+//
+// One wave owns one window-head.  Its Q, K and V rows travel straight from HBM into the wave's LDS
+// buffers (global_load_lds, 16 bytes per lane, four lanes per 64-byte head row: fully used cache
+// lines); no register holds data in flight, so occupancy is set by LDS alone.  Q and K land in
+// the swizzled row layout (conflict-free operand reads) and are rotated on their way into
+// registers: the 64 keys become two MFMA A blocks (lane = key), the 64 queries two B tiles (lane =
+// query).  V stays row-major for the transposed ds_read_b64_tr_b16 reads of the P.V product.  The
+// RoPE sin/cos tables of every head are built once per workgroup while the loads are in flight.
+// The softmax reference is the Cauchy-Schwarz bound max|q^| * max|k~| of the tile, with an
+// exact-maximum recomputation of a tile whose row sums come out below 2^-80.
+#include <algorithm>
+
+#include "fsw_common.h"
+#include "fsw_launch.h"
+#include "fsw_mfma.h"
+
+namespace fsw {
+
+namespace {
+
+constexpr int kM8Waves = 4;                                 // waves (window-heads) per workgroup
+constexpr int kM8MaxHeads = 32;                             // tables: heads * 1 KB of LDS
+constexpr int kM8WaveLds = 3 * 64 * 32 + 32;                // per wave, 16-bit units: Q, K, V rows, labels
+constexpr float kM8LowSum = 8.271806125530277e-25f;         // 2^-80
+constexpr float kM8QScale = kLog2e * 0.17677669529663687f;  // log2(e) / sqrt(32)
+
+__device__ __forceinline__ uint32_t uniform_u32(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_readfirstlane((int)x);
+}
+
+// Issue the HBM -> LDS transfers of window-head wh.  Instruction i moves 64 x 16 bytes into slots
+// i*64 .. i*64+63 of a buffer (lane L's bytes land in slot i*64 + L: row (i*64+L)/4, 16-byte
+// chunk (i*64+L)%4).  For Q and K the lane fetches the logical chunk that the swizzled layout
+// stores in that physical chunk (srow); V is stored unswizzled.
+__device__ __forceinline__ void m8_issue(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+                                         const uint16_t* __restrict__ v, const Geom& g, int64_t wh, int lane,
+                                         uint16_t* qs, uint16_t* ks, uint16_t* vs) {
+  typedef __attribute__((address_space(3))) void lds_t;
+  const WinHead w = decode_winhead(g, wh);
+  const int64_t rowstride = (int64_t)g.heads * 32;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int slot = i * 64 + lane;
+    const int row = slot >> 2, pc = slot & 3;
+    const int lc = pc ^ ((row >> 2) & 3);
+    const int64_t base = token_index(g, w.b, w.wy, w.wx, row >> 3, row & 7) * rowstride + w.h * 32;
+    __builtin_amdgcn_global_load_lds((const void*)(q + base + lc * 8), (lds_t*)(qs + i * 512), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds((const void*)(k + base + lc * 8), (lds_t*)(ks + i * 512), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds((const void*)(v + base + pc * 8), (lds_t*)(vs + i * 512), 16, 0, 0);
+  }
+}
+
+// 8 channels of one lane, rotated with the head's table (row axis: part 0, column axis: part 1;
+// pairs 4h .. 4h+3), scaled, packed to the operand format.
+template <bool H16>
+__device__ __forceinline__ uint4 m8_rotate(uint4 raw, const float* sn, const float* cs, int axis, int pos, int h,
+                                           float scale) {
+  float x[8];
+  unpack8(raw, x);
+  rotate8(x, sn, cs, axis, 8, pos, 4 * h);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) x[e] *= scale;
+  return pack8_op(x, H16);
+}
+
+// Sum of squares of the 16 channels a lane holds for one token (halves add across h afterwards).
+__device__ __forceinline__ float m8_norm2(uint4 a, uint4 b) {
+  float x[8], y[8], s = 0.f;
+  unpack8(a, x);
+  unpack8(b, y);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) s = __builtin_fmaf(x[e], x[e], __builtin_fmaf(y[e], y[e], s));
+  return s;
+}
+
+// Attention of one query tile over the window's two key blocks with softmax reference `ref` (the
+// tile's bound, or a query's exact row maximum); returns l (per lane half) and O^T.
+template <bool H16>
+__device__ __forceinline__ void m8_tile(const uint4 (&kop)[2][2], uint4 qa, uint4 qb, const uint16_t* vbuf,
+                                        const uint8_t* lab, bool masked, int qlab, int lane, float ref, float& l,
+                                        f32x16_t& o) {
+  const int h = lane >> 5;
+  f32x16_t zero;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) zero[e] = 0.f;
+  float la = 0.f, lb = 0.f;
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+    // the reference is subtracted on the VALU (memory-bound path: registers matter more than ALU)
+    f32x16_t s = mfma_op<H16>(kop[kb][0], qa, zero);
+    s = mfma_op<H16>(kop[kb][1], qb, s);
+    const uint32_t live = masked ? live_bits(lab, kb, h, qlab) : 0xffffu;
+    float p[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const float x = __builtin_amdgcn_exp2f(s[e] - ref);
+      p[e] = ((live >> e) & 1u) ? x : 0.f;
+    }
+    uint32_t pk[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) pk[e] = pack2(p[2 * e], p[2 * e + 1]);
+#pragma unroll
+    for (int e = 0; e < 8; e += 2) {
+      la = add_pair(pk[e], la);
+      lb = add_pair(pk[e + 1], lb);
+    }
+    o = mfma32x32x16(as_bf16x8(tr_operand(vbuf, 32, kb * 32, lane)), as_bf16x8(make_uint4(pk[0], pk[1], pk[2], pk[3])),
+                     o);
+    o = mfma32x32x16(as_bf16x8(tr_operand(vbuf, 32, kb * 32 + 16, lane)),
+                     as_bf16x8(make_uint4(pk[4], pk[5], pk[6], pk[7])), o);
+  }
+  l = la + lb;
+}
+
+// Exact row maximum of one query tile over the live keys (raw scores, log2 units).
+template <bool H16>
+__device__ __forceinline__ float m8_rowmax(const uint4 (&kop)[2][2], uint4 qa, uint4 qb, const uint8_t* lab,
+                                           bool masked, int qlab, int lane) {
+  const int h = lane >> 5;
+  f32x16_t zero;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) zero[e] = 0.f;
+  float m = -INFINITY;
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+    f32x16_t s = mfma_op<H16>(kop[kb][0], qa, zero);
+    s = mfma_op<H16>(kop[kb][1], qb, s);
+    const uint32_t live = masked ? live_bits(lab, kb, h, qlab) : 0xffffu;
+#pragma unroll
+    for (int e = 0; e < 16; ++e)
+      if ((live >> e) & 1u) m = fmaxf(m, s[e]);
+  }
+  m = fmaxf(m, __shfl_xor(m, 32, 64));
+  return m;
+}
+
+// Both query tiles: attention, exact-maximum pass when needed, O and LSE stores.
+template <bool H16>
+__device__ __forceinline__ void m8_attend(const uint4 (&kop)[2][2], const uint4 (&qop)[2][2],
+                                          uint16_t* __restrict__ out, float* __restrict__ lse, const Geom& g,
+                                          const WinHead& w, const uint16_t* vbuf, const uint8_t* lab, bool masked,
+                                          float kmax, const float (&qn2)[2], int lane) {
+  const int h = lane >> 5, col = lane & 31;
+  const int64_t rowstride = (int64_t)g.heads * 32;
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const int n = t * 32 + col;
+    const int qr = n >> 3, qc = n & 7;
+    const int qlab = masked ? lab[n] : 0;
+    const float bound = sqrtf(qn2[t]) * kM8QScale * kmax;  // >= every score of this tile (log2 units)
+    f32x16_t o;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) o[e] = 0.f;
+    float l;
+    m8_tile<H16>(kop, qop[t][0], qop[t][1], vbuf, lab, masked, qlab, lane, bound, l, o);
+    float lt = l + __shfl_xor(l, 32, 64);
+    float ref = bound;
+    if (__builtin_amdgcn_ballot_w64(!(lt >= kM8LowSum)) != 0) {
+      // the bound was too loose for some query of the tile: exact maximum, second pass
+      ref = m8_rowmax<H16>(kop, qop[t][0], qop[t][1], lab, masked, qlab, lane);
+#pragma unroll
+      for (int e = 0; e < 16; ++e) o[e] = 0.f;
+      m8_tile<H16>(kop, qop[t][0], qop[t][1], vbuf, lab, masked, qlab, lane, ref, l, o);
+      lt = l + __shfl_xor(l, 32, 64);
+    }
+    // O = O^T / l (lane: query col, channels 8g + 4h + j), LSE = (ref + log2 l) ln 2
+    const int64_t qtok = token_index(g, w.b, w.wy, w.wx, qr, qc);
+    const float inv = 1.f / lt;
+    uint16_t* dst = out + qtok * rowstride + w.h * 32 + 4 * h;
+#pragma unroll
+    for (int gq = 0; gq < 4; ++gq) {
+      uint2 pr;
+      pr.x = pack2(o[4 * gq] * inv, o[4 * gq + 1] * inv);
+      pr.y = pack2(o[4 * gq + 2] * inv, o[4 * gq + 3] * inv);
+      *reinterpret_cast<uint2*>(dst + 8 * gq) = pr;
+    }
+    if (lse && h == 0) lse[qtok * g.heads + w.h] = (ref + __log2f(lt)) * kLn2;
+    __builtin_amdgcn_sched_barrier(0);  // one tile at a time: bounded register pressure
+  }
+}
+
+// Rotated operands from the raw LDS rows: keys as A blocks, queries (scaled by log2(e)/sqrt(d)) as
+// B tiles; token n = tile * 32 + col sits at position (n / 8, n % 8).
+template <bool H16>
+__device__ __forceinline__ void m8_operands(const uint4 (&kr)[2][2], const uint4 (&qr)[2][2], const float* sn,
+                                            const float* cs, int lane, uint4 (&kop)[2][2], uint4 (&qop)[2][2]) {
+  const int h = lane >> 5, col = lane & 31;
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const int n = t * 32 + col;
+    kop[t][0] = m8_rotate<H16>(kr[t][0], sn, cs, 0, n >> 3, h, 1.f);
+    kop[t][1] = m8_rotate<H16>(kr[t][1], sn, cs, 1, n & 7, h, 1.f);
+    qop[t][0] = m8_rotate<H16>(qr[t][0], sn, cs, 0, n >> 3, h, kM8QScale);
+    qop[t][1] = m8_rotate<H16>(qr[t][1], sn, cs, 1, n & 7, h, kM8QScale);
+  }
+}
+
+// Workgroup b (in XCD order) owns window-heads b * kM8Waves .. + kM8Waves - 1, one per wave, so a
+// workgroup's waves work on neighbouring window-heads (the heads of one window share cache lines).
+__global__ __launch_bounds__(kM8Waves * 64) void fwd_m8_kernel(const uint16_t* __restrict__ q,
+                                                               const uint16_t* __restrict__ k,
+                                                               const uint16_t* __restrict__ v,
+                                                               const float* __restrict__ th_row,
+                                                               const float* __restrict__ th_col,
+                                                               uint16_t* __restrict__ out, float* __restrict__ lse,
+                                                               Geom g, int64_t nwh) {
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  // [heads][2 axes][8 positions][8 pairs] sin, then cos; per wave: Q, K, V rows [64][32], labels [64]
+  float* tsn = reinterpret_cast<float*>(smem_raw);
+  float* tcs = tsn + g.heads * 128;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  uint16_t* qs = reinterpret_cast<uint16_t*>(tcs + g.heads * 128) + wave * kM8WaveLds;
+  uint16_t* ks = qs + 64 * 32;
+  uint16_t* vs = ks + 64 * 32;
+  uint8_t* lab = reinterpret_cast<uint8_t*>(vs + 64 * 32);
+
+  const int64_t wh = xcd_order(blockIdx.x, gridDim.x) * kM8Waves + wave;
+  const bool active = wh < nwh;
+  if (active) m8_issue(q, k, v, g, wh, lane, qs, ks, vs);  // in flight while the tables are built
+
+  for (int i = tid; i < g.heads * 128; i += kM8Waves * 64) {
+    const int head = i >> 7, axis = (i >> 6) & 1, p = (i >> 3) & 7, j = i & 7;
+    const float th = axis ? th_col[head * 8 + j] : th_row[head * 8 + j];
+    float s, c;
+    rope_sincos(th, p, &s, &c);
+    tsn[i] = s;
+    tcs[i] = c;
+  }
+  __syncthreads();
+  if (!active) return;
+
+  const WinHead w = decode_winhead(g, wh);
+  // Swin region labels of the 64 tokens (one per lane); mask only when the window has several
+  const int lbl = token_label(g, w.wy, w.wx, lane >> 3, lane & 7);
+  const uint32_t labels = uniform_u32(wave_or(1u << lbl));
+  const bool masked = __builtin_popcount(labels) > 1;
+  if (masked) lab[lane] = (uint8_t)lbl;
+  // the wave's transfers are complete once its vector-memory count drains (the asm also keeps the
+  // compiler from moving LDS reads above it)
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+
+  const int h = lane >> 5, col = lane & 31;
+  uint4 kr[2][2], qr[2][2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const int n = t * 32 + col;
+    kr[t][0] = *reinterpret_cast<const uint4*>(ks + srow(n, h));
+    kr[t][1] = *reinterpret_cast<const uint4*>(ks + srow(n, 2 + h));
+    qr[t][0] = *reinterpret_cast<const uint4*>(qs + srow(n, h));
+    qr[t][1] = *reinterpret_cast<const uint4*>(qs + srow(n, 2 + h));
+  }
+  // norms: |k|^2 max over the 64 keys, |q|^2 max per query tile (rotation keeps norms)
+  float kn0 = m8_norm2(kr[0][0], kr[0][1]);
+  float kn1 = m8_norm2(kr[1][0], kr[1][1]);
+  kn0 += __shfl_xor(kn0, 32, 64);
+  kn1 += __shfl_xor(kn1, 32, 64);
+  const float kmax = sqrtf(wave_max(fmaxf(kn0, kn1)));
+  float qn2[2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    float qq = m8_norm2(qr[t][0], qr[t][1]);
+    qq += __shfl_xor(qq, 32, 64);
+    qn2[t] = wave_max(qq);
+  }
+  const bool h16 = kmax < kF16Limit && sqrtf(fmaxf(qn2[0], qn2[1])) * kM8QScale < kF16Limit;
+  const float* sn = tsn + w.h * 128;
+  const float* cs = tcs + w.h * 128;
+  uint4 kop[2][2], qop[2][2];
+  if (h16) {
+    m8_operands<true>(kr, qr, sn, cs, lane, kop, qop);
+    m8_attend<true>(kop, qop, out, lse, g, w, vs, lab, masked, kmax, qn2, lane);
+  } else {
+    m8_operands<false>(kr, qr, sn, cs, lane, kop, qop);
+    m8_attend<false>(kop, qop, out, lse, g, w, vs, lab, masked, kmax, qn2, lane);
+  }
+}
+
+}  // namespace
+
+bool fwd_m8_supported(const Geom& g) { return g.M == 8 && g.d == 32 && g.heads <= kM8MaxHeads; }
+
+hipError_t launch_fwd_m8(const FwdArgs& a, hipStream_t st) {
+  const Geom& g = a.g;
+  const int64_t nwh = g.B * g.nH * g.nW * g.heads;
+  const size_t smem = (size_t)g.heads * 128 * 4 * 2 + (size_t)kM8Waves * kM8WaveLds * 2;
+  const int64_t grid = (nwh + kM8Waves - 1) / kM8Waves;
+  hipLaunchKernelGGL(fwd_m8_kernel, dim3((unsigned)grid), dim3(kM8Waves * 64), smem, st, (const uint16_t*)a.q,
+                     (const uint16_t*)a.k, (const uint16_t*)a.v, a.th_row, a.th_col, (uint16_t*)a.out, a.lse, g, nwh);
+  return hipGetLastError();
+}
+
+}  // namespace fsw

@@ -397,14 +397,10 @@ __global__ __launch_bounds__(NWAVES * 64) void fwd_mfma_kernel(const uint16_t* _
     const int qr = qvalid ? qi / M : 0, qc = qvalid ? qi - (qi / M) * M : 0;
     uint4 qb0, qb1;
     {
-      // reloaded (an L2 hit): keeping every block's raw query live across attend() costs registers
-      uint4 qa, qc2;
-      if (qb == 0) {
-        qa = qraw[0][0];
-        qc2 = qraw[0][1];
-      } else {
-        load_q(qb, qa, qc2);
-      }
+      // block 0's query was loaded with K and V; later blocks reload theirs (an L2 hit) during
+      // the previous block's epilogue: keeping every block's raw query live across attend() costs
+      // registers
+      const uint4 qa = qraw[qb][0], qc2 = qraw[qb][1];
       float x[8], y[8];
       unpack8(qa, x);
       unpack8(qc2, y);
@@ -434,6 +430,8 @@ __global__ __launch_bounds__(NWAVES * 64) void fwd_mfma_kernel(const uint16_t* _
     else
       attend<false>(sm, NB, lane, uniform_win, wave_labels, wave_single, qb0, qb1, qlab, qvalid, bound, ref, l, o);
 
+    // the next block's query loads go out before this block's epilogue
+    if (qb + 1 < QBM) load_q(qb + 1, qraw[qb + 1][0], qraw[qb + 1][1]);  // zeros past the last block
     // 4. epilogue: O = O^T / l (lane: query col, channels 8g + 4h + j), LSE = (ref + log2 l) ln 2
     const float lt = l + __shfl_xor(l, 32, 64);
     if (qvalid) {
@@ -475,6 +473,7 @@ hipError_t launch_nw(const FwdArgs& a, hipStream_t st) {
 hipError_t launch_fwd_mfma(const FwdArgs& a, hipStream_t st) {
   const int N = a.g.N;
   if (a.g.M == 32) return launch_nw<16, 32, 1024>(a, st);
+  if (fwd_m8_supported(a.g)) return launch_fwd_m8(a, st);
   if (a.g.M == 8) return launch_nw<2, 8, 64>(a, st);
   if (N <= 64) return launch_nw<2, 0, 64>(a, st);
   if (N <= 128) return launch_nw<4, 0, 128>(a, st);

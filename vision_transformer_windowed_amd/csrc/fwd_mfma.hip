@@ -264,7 +264,7 @@ __global__ __launch_bounds__(NWAVES * 64) void fwd_mfma_kernel(const uint16_t* _
                                                                const float* __restrict__ th_row,
                                                                const float* __restrict__ th_col,
                                                                uint16_t* __restrict__ out, float* __restrict__ lse,
-                                                               Geom g, int nqb, int NP) {
+                                                               Geom g, int nqb, int NP, int nsplit) {
   extern __shared__ __align__(16) unsigned char smem_raw[];
   constexpr int D = 32;
   constexpr int NT = NWAVES * 64;
@@ -277,7 +277,24 @@ __global__ __launch_bounds__(NWAVES * 64) void fwd_mfma_kernel(const uint16_t* _
   const int NB = NP / 32;
   const FwdSmem sm = carve(smem_raw, NP, M);
 
-  const int64_t wh = xcd_order(blockIdx.x, gridDim.x);  // a window's heads share one L2
+  // Work of this workgroup: window-head wh, query blocks qoff .. qoff + nqw - 1.  The first nsplit
+  // window-heads are split into one workgroup per query block, dispatched first (the first
+  // 2*nsplit/8 slots of every XCD): those CUs finish their first task early, so from then on the
+  // CUs stage K/V at staggered times instead of all at once.  The rest are ordered per XCD so a
+  // window's heads share one L2.
+  int64_t wh;
+  int qoff = 0, nqw = nqb;
+  {
+    const int64_t b = blockIdx.x, shorts = 2 * (int64_t)nsplit, pos = b >> 3, x = b & 7;
+    if (pos < shorts / 8) {
+      const int64_t sidx = x * (shorts / 8) + pos;
+      wh = sidx >> 1;
+      qoff = (int)(sidx & 1);
+      nqw = 1;
+    } else {
+      wh = nsplit + xcd_order(b - shorts, (int64_t)gridDim.x - shorts);
+    }
+  }
   const WinHead w = decode_winhead(g, wh);
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -291,9 +308,9 @@ __global__ __launch_bounds__(NWAVES * 64) void fwd_mfma_kernel(const uint16_t* _
   load_kv<MAXIT>(k, v, g, w, M, NP, tid, NT, true, kraw, vraw);
   // the lane's query of block qb (two 16-byte halves: channels 8h.., 16+8h..)
   auto load_q = [&](int qb, uint4& a, uint4& b) {
-    const int qi = qb * NT / 2 + wave * 32 + col;
+    const int qi = (qoff + qb) * NT / 2 + wave * 32 + col;
     a = b = make_uint4(0, 0, 0, 0);
-    if (qb < nqb && qi < N) {
+    if (qb < nqw && qi < N) {
       const int64_t off = tok_of(g, w, M, qi / M, qi - (qi / M) * M) * rowstride + w.h * D;
       a = *reinterpret_cast<const uint4*>(q + off + 8 * h);
       b = *reinterpret_cast<const uint4*>(q + off + 16 + 8 * h);
@@ -390,9 +407,9 @@ __global__ __launch_bounds__(NWAVES * 64) void fwd_mfma_kernel(const uint16_t* _
 
 #pragma unroll
   for (int qb = 0; qb < QBM; ++qb) {
-    if (qb >= nqb) break;
+    if (qb >= nqw) break;
     // 3. the wave's query operands (rotated, scaled by log2(e)/sqrt(d)), reference bound, labels
-    const int qi = qb * NT / 2 + wave * 32 + col;
+    const int qi = (qoff + qb) * NT / 2 + wave * 32 + col;
     const bool qvalid = qi < N;
     const int qr = qvalid ? qi / M : 0, qc = qvalid ? qi - (qi / M) * M : 0;
     uint4 qb0, qb1;
@@ -461,10 +478,14 @@ hipError_t launch_nw(const FwdArgs& a, hipStream_t st) {
     (void)hipFuncSetAttribute((const void*)fwd_mfma_kernel<NWAVES, MT, NPMAX>,
                               hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
   });
-  const int64_t blocks = g.B * g.nH * g.nW * g.heads;
+  const int64_t nwh = g.B * g.nH * g.nW * g.heads;
+  // staggered start (see the kernel): 64 window-heads split into 128 half tasks when there are
+  // two query blocks and enough work for several rounds of workgroups per CU
+  const int nsplit = (nqb == 2 && nwh >= 64 * 8) ? 64 : 0;
+  const int64_t blocks = nwh + nsplit;
   hipLaunchKernelGGL((fwd_mfma_kernel<NWAVES, MT, NPMAX>), dim3((unsigned)blocks), dim3(NWAVES * 64), smem, st,
                      (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, a.th_row, a.th_col,
-                     (uint16_t*)a.out, a.lse, g, nqb, NP);
+                     (uint16_t*)a.out, a.lse, g, nqb, NP, nsplit);
   return hipGetLastError();
 }
 

@@ -148,6 +148,31 @@ def test_forward_nan_stays_in_its_window_region():
     assert not torch.isnan(out[..., 1, :].float()).any()  # other head untouched
 
 
+@pytest.mark.parametrize("M,shift,grid", [(32, 16, 64), (32, 0, 64), (8, 3, 32), (12, 5, 36)])
+def test_forward_loose_bound_falls_back(M, shift, grid):
+    """One key with a large norm makes max|q| * max|k| overshoot the true row maximum of most
+    queries by more than 80 (log2 units): their sums under the bound reference fall below
+    2^-80 and the kernels redo those rows with the exact maximum.  Logits reach ~40 here, and
+    operand rounding errors grow with the logit, so max-abs is taken relative to max |ref|."""
+    H, D = 2, 32
+    x = make_inputs(1, grid, grid, H, D, "bf16", seed=31 + M)
+    ky, kx = grid // 2 + 1, 3
+    x["k"][0, ky, kx, 0] *= 14.0
+    xd = to_dev(x)
+    out, lse = F.wattn_fwd(xd["q"], xd["k"], xd["v"], xd["theta_row"], xd["theta_col"], M, shift)
+    torch.cuda.synchronize()
+    (q, k, v), tr, tc = oracle_args(x)
+    ro, rl = oracle.wattn_fwd_ref(q, k, v, tr, tc, M, shift)
+    # the case is meant: some query's row maximum sits more than 90 below |q_i^| * max|k| (log2
+    # units, q^ = q log2(e) / sqrt(d)), which is at most any wave's bound for that query
+    l2e = 1.4426950408889634
+    qn = np.linalg.norm(q[0, :, :, 0], axis=-1) * l2e / np.sqrt(D)
+    kmax = np.linalg.norm(k[0, :, :, 0], axis=-1).max()
+    assert np.any(rl[0, :, :, 0] * l2e < qn * kmax - 90.0)
+    assert_close("O", _np(out), ro, 2e-2, 5e-3)
+    assert_close("LSE", _np(lse), rl, 2e-2, 5e-3, scale_abs=True)
+
+
 # ------------------------------------------------------------------------- forward, full workloads
 
 SAMPLE_IMAGES = {

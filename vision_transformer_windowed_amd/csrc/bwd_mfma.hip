@@ -31,19 +31,14 @@
 #include "fsw_common.h"
 #include "fsw_launch.h"
 #include "fsw_mfma.h"
+#include "fsw_stream.h"
 
 namespace fsw {
 
 namespace {
 
-constexpr int kCh = 128;  // tokens per LDS chunk (a multiple of 128)
 constexpr float kSqrt2 = 1.4142135623730951f;
 constexpr float kQScale = kLog2e * 0.17677669529663687f;  // log2(e) / sqrt(32)
-
-__device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
-__device__ __forceinline__ uint32_t uniform(uint32_t x) { return (uint32_t)__builtin_amdgcn_readfirstlane((int)x); }
-
-__host__ __device__ constexpr int chunk_len(int NP) { return NP < kCh ? NP : kCh; }
 
 // Power of two 2^k (k clamped to [-100, 100]) with 2^k * bound <= 2^14 (1 when bound is 0 or not
 // finite).
@@ -57,28 +52,6 @@ __device__ __forceinline__ float pow2_scale(float bound) {
 // Operand format of a window-head: fp16 when every rotated, scaled score operand is in range.
 __device__ __forceinline__ bool window_h16(const float* scal, int64_t wh) {
   return kSqrt2 * scal[wh * 4 + 2] * kQScale < kF16Limit && kSqrt2 * scal[wh * 4 + 3] < kF16Limit;
-}
-
-template <bool H16>
-__device__ __forceinline__ uint32_t pack_op2(float a, float b) {
-  if constexpr (H16)
-    return pack2h(a, b);
-  else
-    return pack2(a, b);
-}
-
-__device__ inline void fill_table(float* sn, float* cs, const float* th_row, const float* th_col, int head, int M,
-                                  int tid, int nt) {
-  for (int i = tid; i < 2 * M * 8; i += nt) {
-    const int axis = i / (M * 8);
-    const int p = (i / 8) % M;
-    const int j = i % 8;
-    const float th = axis ? th_col[head * 8 + j] : th_row[head * 8 + j];
-    float s, c;
-    rope_sincos(th, p, &s, &c);
-    sn[i] = s;
-    cs[i] = c;
-  }
 }
 
 // Fixed-order reduction of each lane's 8 dtheta slots (for its channels 8g + 4h + {0..3}) over
@@ -150,29 +123,6 @@ __device__ inline void unrotate_store(const f32x16_t& dxt, float scale, float op
     o.y = pack2(res[2], res[3]);
     *reinterpret_cast<uint2*>(dst + 8 * gq + 4 * h) = o;
   }
-}
-
-// Rotate the 8 channels of `raw` (part `part` of token (r, c)), scale, pack to the operand format.
-template <bool H16>
-__device__ __forceinline__ uint4 rotated_part(uint4 raw, const float* sn, const float* cs, int M, int r, int c,
-                                              int part, float scale) {
-  float x[8];
-  unpack8(raw, x);
-  const int axis = part >> 1;
-  rotate8(x, sn, cs, axis, M, axis ? c : r, (part & 1) * 4);
-#pragma unroll
-  for (int e = 0; e < 8; ++e) x[e] *= scale;
-  return pack8_op(x, H16);
-}
-
-// Scale 8 bf16 values by a power of two; result in the operand format.
-template <bool H16>
-__device__ __forceinline__ uint4 scaled_part(uint4 raw, float scale) {
-  float x[8];
-  unpack8(raw, x);
-#pragma unroll
-  for (int e = 0; e < 8; ++e) x[e] *= scale;
-  return pack8_op(x, H16);
 }
 
 // ------------------------------------------------------------------------------------ prologue
@@ -255,17 +205,6 @@ __global__ __launch_bounds__(kPreThreads) void bwd_pre_kernel(const uint16_t* __
     for (int j = 0; j < kPreThreads / 64; ++j) m = fmaxf(m, red[tid][j]);
     scal[wh * 4 + tid] = m;
   }
-}
-
-// Label of chunk token n (0xff past the window) and its block summary bit (bit L for label L,
-// bit 10 for a position past the window) OR-ed into blk[n / 32].
-__device__ __forceinline__ uint8_t chunk_label(const Geom& g, const WinHead& w, int M, int tn, uint32_t* blk,
-                                               int n) {
-  const int N = M * M;
-  uint8_t lb = 0xff;
-  if (tn < N) lb = (uint8_t)token_label(g, w.wy, w.wx, tn / M, tn - (tn / M) * M);
-  atomicOr(&blk[n >> 5], lb == 0xff ? (1u << 10) : (1u << lb));
-  return lb;
 }
 
 // Both main kernels stream the window's other side through LDS in chunks of up to kCh tokens:

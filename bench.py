@@ -134,6 +134,46 @@ def m8_forward_roofline(dev, steps, warmup):
             "algorithmic_bytes": nbytes, "launch_ms": round(ms, 4)}
 
 
+def packed_forward(dev, steps, warmup):
+    """M=8 Swin-T stage-1 forward (HBM-bound) from packed qkv [B, Hg, Wg, 3, heads, d]: read in place by
+    the packed entry point, against splitting it into contiguous q, k, v first (three copies) and calling
+    the separate-tensor entry point."""
+    import torch
+    import vision_transformer_windowed_amd as F
+    from vision_transformer_windowed_amd.inputs import WORKLOADS, workload_inputs
+    name = "swin_t_s1_p4_m8"
+    w = WORKLOADS[name]
+    x = workload_inputs(name, with_dout=False)
+    qkv = torch.stack([x["q"], x["k"], x["v"]], dim=3).contiguous().to(dev)
+    tr, tc = x["theta_row"].to(dev), x["theta_col"].to(dev)
+    out = torch.empty(qkv.shape[:3] + qkv.shape[4:], device=dev, dtype=qkv.dtype)
+    lse = torch.empty(qkv.shape[:3] + qkv.shape[4:5], device=dev, dtype=torch.float32)
+    stream = torch.cuda.current_stream(dev)
+
+    def packed():
+        F.wattn_fwd_packed(qkv, tr, tc, w["M"], 0, out=out, lse=lse)
+
+    def split():
+        q, k, v = (t.contiguous() for t in qkv.unbind(3))
+        F.wattn_fwd(q, k, v, tr, tc, w["M"], 0, out=out, lse=lse)
+
+    res = {"workload": name, "layout": "qkv [B, Hg, Wg, 3, heads, d]"}
+    for tag, fn in (("packed_ms", packed), ("split_then_call_ms", split)):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(steps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        res[tag] = round(e0.elapsed_time(e1) / steps, 4)
+    nbytes = 4 * out.numel() * out.element_size() + lse.numel() * 4
+    res["packed_GBps"] = round(nbytes / (res["packed_ms"] * 1e-3) / 1e9, 1)
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -243,9 +283,10 @@ def main():
         fwd_roofline = {"kernel": "wattn_fwd", "bound": "mfma", "achieved": round(fwd_tf, 2),
                         "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(fwd_tf / BF16_MFMA_PEAK_TFLOPS, 4),
                         "launch_ms": round(fwd_ms, 4)}
-    m8 = None
+    m8 = packed = None
     if not args.no_secondary and args.only == "step":
         m8 = m8_forward_roofline(dev, max(args.steps, 10), max(args.warmup, 2))
+        packed = packed_forward(dev, max(args.steps, 10), max(args.warmup, 2))
 
     gpu_out = {"out": out, "lse": lse, "dq": grads[0], "dk": grads[1], "dv": grads[2]}
     cpu, parity = (None, None)
@@ -276,6 +317,7 @@ def main():
         "roofline": roofline,
         "fwd_roofline": fwd_roofline,
         "m8_fwd_roofline": m8,
+        "m8_fwd_packed_qkv": packed,
         "cpu_baseline": cpu,
         "parity_sample": parity,
         "input_gen_s": round(gen_s, 1),

@@ -108,6 +108,43 @@ int flashswin_wattn_bwd(const void* q, const void* k, const void* v,
                         int64_t B, int64_t Hg, int64_t Wg, int heads, int d,
                         int M, int shift, int dtype, void* hip_stream);
 
+/*
+ * Forward from a packed qkv tensor, the layout a fused qkv projection writes ([FS] Figure 1(B):
+ * the qkv projection feeds RoPE and the fused attention kernel).
+ *
+ *   qkv          device, [B, Hg, Wg, 3, heads, d] of `dtype`, 16-byte aligned: q, k and v are the
+ *                slices qkv[..., 0, :, :], qkv[..., 1, :, :], qkv[..., 2, :, :], read in place
+ *                (no split, no copy).
+ *   out, lse     as in flashswin_wattn_fwd ([B, Hg, Wg, heads, d] and [B, Hg, Wg, heads]); out may
+ *                not overlap qkv.
+ * Same shape rules and return codes as flashswin_wattn_fwd.  out and lse are bit-identical to
+ * flashswin_wattn_fwd on the three slices.
+ */
+int flashswin_wattn_fwd_packed(const void* qkv, const float* theta_row, const float* theta_col,
+                               void* out, float* lse,
+                               int64_t B, int64_t Hg, int64_t Wg, int heads, int d,
+                               int M, int shift, int dtype, void* hip_stream);
+
+/*
+ * Backward of flashswin_wattn_fwd_packed: the gradient is written packed as well.
+ *
+ *   qkv           the forward's packed input, [B, Hg, Wg, 3, heads, d].
+ *   out, dout,
+ *   lse, theta    as in flashswin_wattn_bwd.
+ *   dqkv          device, [B, Hg, Wg, 3, heads, d] of `dtype`, 16-byte aligned, overwritten with
+ *                 dq, dk, dv in the places of q, k, v.  May not overlap qkv, out or dout.
+ *   dtheta_row/col, workspace  as in flashswin_wattn_bwd; the workspace size is
+ *                 flashswin_wattn_bwd_workspace_size() of the same shape.
+ * Same shape rules and return codes as flashswin_wattn_bwd.  Results are bit-identical to
+ * flashswin_wattn_bwd on the slices.
+ */
+int flashswin_wattn_bwd_packed(const void* qkv, const void* out, const void* dout, const float* lse,
+                               const float* theta_row, const float* theta_col,
+                               void* dqkv, float* dtheta_row, float* dtheta_col,
+                               void* workspace, size_t workspace_bytes,
+                               int64_t B, int64_t Hg, int64_t Wg, int heads, int d,
+                               int M, int shift, int dtype, void* hip_stream);
+
 /* Static, human-readable name of a status code. */
 const char* flashswin_status_string(int status);
 

@@ -119,3 +119,65 @@ def test_workspace_size():
     assert small % 256 == 0
     # at least the per-token Delta buffer
     assert ws(32, 128, 128, 3, 32, 32, 16, 1) >= 32 * 128 * 128 * 3 * 4
+
+
+# ----------------------------------------------------------------------- packed qkv entry points
+# Shape 1 x 16 x 16 tokens, 2 heads, d 32, bf16: one tensor of q's shape is 32 KiB, packed qkv 96 KiB.
+TENS = 16 * 16 * 2 * 32 * 2
+
+
+def fwd_packed(**kw):
+    a = dict(qkv=FAKE, tr=FAKE + 4 * TENS, tc=FAKE + 4 * TENS + 256, out=FAKE + 3 * TENS,
+             lse=FAKE + 4 * TENS + 512, B=1, Hg=16, Wg=16, heads=2, d=32, M=8, shift=0, dtype=F.FSW_BF16)
+    a.update(kw)
+    return F.flashswin_wattn_fwd_packed(a["qkv"], a["tr"], a["tc"], a["out"], a["lse"], a["B"], a["Hg"], a["Wg"],
+                                        a["heads"], a["d"], a["M"], a["shift"], a["dtype"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(Hg=12), F.FSW_ERR_INVALID_ARG),
+    (dict(qkv=None), F.FSW_ERR_INVALID_ARG),
+    (dict(qkv=FAKE + 8), F.FSW_ERR_INVALID_ARG),            # misaligned
+    (dict(out=None), F.FSW_ERR_INVALID_ARG),
+    (dict(out=FAKE + TENS), F.FSW_ERR_INVALID_ARG),         # out is the k slice
+    (dict(out=FAKE + 3 * TENS - 4096), F.FSW_ERR_INVALID_ARG),  # out overlaps the tail of qkv
+    (dict(d=12), F.FSW_ERR_UNSUPPORTED),
+    (dict(B=1 << 38), F.FSW_ERR_UNSUPPORTED),               # 3x the elements of q overflow the index space
+])
+def test_packed_forward_rejects_before_launch(kw, status):
+    assert fwd_packed(**kw) == status
+
+
+def test_packed_forward_empty_batch_is_a_no_op():
+    assert fwd_packed(B=0, qkv=None, out=None, lse=None, tr=None, tc=None) == F.FSW_OK
+
+
+def bwd_packed(**kw):
+    base = FAKE + 16 * TENS
+    a = dict(qkv=FAKE, out=base, dout=base + TENS, lse=base + 2 * TENS, tr=base + 2 * TENS + 4096,
+             tc=base + 2 * TENS + 4352, dqkv=FAKE + 4 * TENS, dtr=base + 2 * TENS + 4608,
+             dtc=base + 2 * TENS + 4864, ws=base + 4 * TENS, wsb=None,
+             B=1, Hg=16, Wg=16, heads=2, d=32, M=8, shift=4, dtype=F.FSW_BF16)
+    a.update(kw)
+    if a["wsb"] is None:
+        a["wsb"] = F.flashswin_wattn_bwd_workspace_size(a["B"], a["Hg"], a["Wg"], a["heads"], a["d"], a["M"],
+                                                        a["shift"], a["dtype"])
+    return F.flashswin_wattn_bwd_packed(a["qkv"], a["out"], a["dout"], a["lse"], a["tr"], a["tc"], a["dqkv"],
+                                        a["dtr"], a["dtc"], a["ws"], a["wsb"], a["B"], a["Hg"], a["Wg"],
+                                        a["heads"], a["d"], a["M"], a["shift"], a["dtype"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(qkv=None), F.FSW_ERR_INVALID_ARG),
+    (dict(dqkv=None), F.FSW_ERR_INVALID_ARG),
+    (dict(lse=None), F.FSW_ERR_INVALID_ARG),
+    (dict(dqkv=FAKE + 2 * TENS), F.FSW_ERR_INVALID_ARG),    # dqkv overlaps qkv
+    (dict(out=FAKE + 5 * TENS), F.FSW_ERR_INVALID_ARG),     # out inside dqkv
+    (dict(dout=FAKE + 6 * TENS - 64), F.FSW_ERR_INVALID_ARG),  # dout overlaps the end of dqkv
+    (dict(dqkv=FAKE + 4 * TENS + 2), F.FSW_ERR_INVALID_ARG),  # misaligned
+    (dict(ws=None), F.FSW_ERR_WORKSPACE),
+    (dict(wsb=16), F.FSW_ERR_WORKSPACE),
+    (dict(shift=8), F.FSW_ERR_INVALID_ARG),
+])
+def test_packed_backward_rejects_before_launch(kw, status):
+    assert bwd_packed(**kw) == status

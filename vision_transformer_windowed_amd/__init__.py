@@ -19,14 +19,20 @@ from ._lib import (  # noqa: F401
     FlashSwinError,
     LIB_PATH,
     WindowAttention,
+    WindowAttentionPacked,
     bwd_workspace_bytes,
     flashswin_status_string,
     flashswin_version,
     flashswin_wattn_bwd,
     flashswin_wattn_bwd_workspace_size,
+    flashswin_wattn_bwd_packed,
     flashswin_wattn_fwd,
+    flashswin_wattn_fwd_packed,
     load,
     wattn_bwd,
+    wattn_bwd_packed,
     wattn_fwd,
+    wattn_fwd_packed,
     window_attention,
+    window_attention_packed,
 )

@@ -23,6 +23,8 @@ EXPORTED = (
     "flashswin_wattn_fwd",
     "flashswin_wattn_bwd_workspace_size",
     "flashswin_wattn_bwd",
+    "flashswin_wattn_fwd_packed",
+    "flashswin_wattn_bwd_packed",
     "flashswin_status_string",
     "flashswin_version",
 )
@@ -53,6 +55,10 @@ def load():
     lib.flashswin_wattn_bwd_workspace_size.argtypes = [i64, i64, i64, i32, i32, i32, i32, i32]
     lib.flashswin_wattn_bwd.restype = i32
     lib.flashswin_wattn_bwd.argtypes = [vp] * 13 + [vp, sz, i64, i64, i64, i32, i32, i32, i32, i32, vp]
+    lib.flashswin_wattn_fwd_packed.restype = i32
+    lib.flashswin_wattn_fwd_packed.argtypes = [vp] * 5 + [i64, i64, i64, i32, i32, i32, i32, i32, vp]
+    lib.flashswin_wattn_bwd_packed.restype = i32
+    lib.flashswin_wattn_bwd_packed.argtypes = [vp] * 9 + [vp, sz, i64, i64, i64, i32, i32, i32, i32, i32, vp]
     lib.flashswin_status_string.restype = ctypes.c_char_p
     lib.flashswin_status_string.argtypes = [i32]
     lib.flashswin_version.restype = i32
@@ -82,6 +88,18 @@ def flashswin_wattn_bwd(q, k, v, out, dout, lse, theta_row, theta_col, dq, dk, d
     return load().flashswin_wattn_bwd(q, k, v, out, dout, lse, theta_row, theta_col, dq, dk, dv, dtheta_row,
                                       dtheta_col, workspace, workspace_bytes, B, Hg, Wg, heads, d, M, shift, dtype,
                                       stream)
+
+
+def flashswin_wattn_fwd_packed(qkv, theta_row, theta_col, out, lse, B, Hg, Wg, heads, d, M, shift, dtype, stream):
+    return load().flashswin_wattn_fwd_packed(qkv, theta_row, theta_col, out, lse, B, Hg, Wg, heads, d, M, shift,
+                                             dtype, stream)
+
+
+def flashswin_wattn_bwd_packed(qkv, out, dout, lse, theta_row, theta_col, dqkv, dtheta_row, dtheta_col, workspace,
+                               workspace_bytes, B, Hg, Wg, heads, d, M, shift, dtype, stream):
+    return load().flashswin_wattn_bwd_packed(qkv, out, dout, lse, theta_row, theta_col, dqkv, dtheta_row,
+                                             dtheta_col, workspace, workspace_bytes, B, Hg, Wg, heads, d, M, shift,
+                                             dtype, stream)
 
 
 def flashswin_status_string(status):
@@ -186,6 +204,67 @@ def wattn_bwd(q, k, v, out, dout, lse, theta_row, theta_col, M, shift=0, workspa
     return dq, dk, dv, dtr, dtc
 
 
+def _packed_shape(qkv):
+    if qkv.dim() != 6 or qkv.shape[3] != 3:
+        raise ValueError("qkv must be [B, Hg, Wg, 3, heads, d]")
+    B, Hg, Wg, _, H, D = qkv.shape
+    return B, Hg, Wg, H, D
+
+
+def wattn_fwd_packed(qkv, theta_row, theta_col, M, shift=0, out=None, lse=None, need_lse=True):
+    """Forward from packed qkv [B, Hg, Wg, 3, heads, d], read in place.  Returns (out, lse)."""
+    B, Hg, Wg, H, D = _packed_shape(qkv)
+    code = _dtype_code(qkv)
+    _check_grid("qkv", qkv, qkv.shape, qkv.dtype)
+    for name, t in (("theta_row", theta_row), ("theta_col", theta_col)):
+        _check_grid(name, t, (H, D // 4), torch.float32)
+    if out is None:
+        out = torch.empty((B, Hg, Wg, H, D), device=qkv.device, dtype=qkv.dtype)
+    _check_grid("out", out, (B, Hg, Wg, H, D), qkv.dtype)
+    if need_lse:
+        if lse is None:
+            lse = torch.empty((B, Hg, Wg, H), device=qkv.device, dtype=torch.float32)
+        _check_grid("lse", lse, (B, Hg, Wg, H), torch.float32)
+    else:
+        lse = None
+    st = flashswin_wattn_fwd_packed(_ptr(qkv), _ptr(theta_row), _ptr(theta_col), _ptr(out), _ptr(lse), B, Hg, Wg,
+                                    H, D, int(M), int(shift), code, _stream(qkv.device))
+    if st != FSW_OK:
+        raise FlashSwinError(st, "flashswin_wattn_fwd_packed")
+    return out, lse
+
+
+def wattn_bwd_packed(qkv, out, dout, lse, theta_row, theta_col, M, shift=0, workspace=None, grads=None):
+    """Backward of wattn_fwd_packed.  Returns (dqkv, dtheta_row, dtheta_col), dqkv packed like qkv.
+
+    `grads` may hold preallocated (dqkv, dtheta_row, dtheta_col) to write into.
+    """
+    B, Hg, Wg, H, D = _packed_shape(qkv)
+    code = _dtype_code(qkv)
+    _check_grid("qkv", qkv, qkv.shape, qkv.dtype)
+    for name, t in (("out", out), ("dout", dout)):
+        _check_grid(name, t, (B, Hg, Wg, H, D), qkv.dtype)
+    _check_grid("lse", lse, (B, Hg, Wg, H), torch.float32)
+    for name, t in (("theta_row", theta_row), ("theta_col", theta_col)):
+        _check_grid(name, t, (H, D // 4), torch.float32)
+    if grads is None:
+        dqkv, dtr, dtc = torch.empty_like(qkv), torch.empty_like(theta_row), torch.empty_like(theta_col)
+    else:
+        dqkv, dtr, dtc = grads
+        _check_grid("dqkv", dqkv, qkv.shape, qkv.dtype)
+        for name, t in (("dtheta_row", dtr), ("dtheta_col", dtc)):
+            _check_grid(name, t, (H, D // 4), torch.float32)
+    nbytes = flashswin_wattn_bwd_workspace_size(B, Hg, Wg, H, D, int(M), int(shift), code)
+    if workspace is None or workspace.numel() < nbytes:
+        workspace = torch.empty(max(nbytes, 1), device=qkv.device, dtype=torch.uint8)
+    st = flashswin_wattn_bwd_packed(_ptr(qkv), _ptr(out), _ptr(dout), _ptr(lse), _ptr(theta_row), _ptr(theta_col),
+                                    _ptr(dqkv), _ptr(dtr), _ptr(dtc), _ptr(workspace), workspace.numel(), B, Hg, Wg,
+                                    H, D, int(M), int(shift), code, _stream(qkv.device))
+    if st != FSW_OK:
+        raise FlashSwinError(st, "flashswin_wattn_bwd_packed")
+    return dqkv, dtr, dtc
+
+
 class WindowAttention(torch.autograd.Function):
     """Autograd wrapper: forward saves LSE, backward recomputes P (no score matrix is stored)."""
 
@@ -206,3 +285,25 @@ class WindowAttention(torch.autograd.Function):
 def window_attention(q, k, v, theta_row, theta_col, M, shift=0):
     """Differentiable windowed attention with window-local 2D RoPE; q/k/v [B, Hg, Wg, heads, d]."""
     return WindowAttention.apply(q, k, v, theta_row, theta_col, M, shift)
+
+
+class WindowAttentionPacked(torch.autograd.Function):
+    """Autograd wrapper over packed qkv [B, Hg, Wg, 3, heads, d]; the gradient comes back packed."""
+
+    @staticmethod
+    def forward(ctx, qkv, theta_row, theta_col, M, shift):
+        out, lse = wattn_fwd_packed(qkv, theta_row, theta_col, M, shift)
+        ctx.save_for_backward(qkv, out, lse, theta_row, theta_col)
+        ctx.M, ctx.shift = M, shift
+        return out
+
+    @staticmethod
+    def backward(ctx, dout):
+        qkv, out, lse, tr, tc = ctx.saved_tensors
+        dqkv, dtr, dtc = wattn_bwd_packed(qkv, out, dout.contiguous(), lse, tr, tc, ctx.M, ctx.shift)
+        return dqkv, dtr, dtc, None, None
+
+
+def window_attention_packed(qkv, theta_row, theta_col, M, shift=0):
+    """Differentiable windowed attention reading packed qkv [B, Hg, Wg, 3, heads, d] in place."""
+    return WindowAttentionPacked.apply(qkv, theta_row, theta_col, M, shift)

@@ -143,7 +143,6 @@ __global__ __launch_bounds__(kPreThreads) void bwd_pre_kernel(const uint16_t* __
   const int64_t wh = xcd_order(blockIdx.x, gridDim.x);
   const WinHead w = decode_winhead(g, wh);
   const int tid = threadIdx.x;
-  const int64_t rowstride = (int64_t)g.heads * 32;
   float mx[4] = {0.f, 0.f, 0.f, 0.f};
   const int items = g.N * 4;
   const int steps = (items + kPreThreads * kPreBatch - 1) / (kPreThreads * kPreBatch);
@@ -159,12 +158,13 @@ __global__ __launch_bounds__(kPreThreads) void bwd_pre_kernel(const uint16_t* __
         const int n = it >> 2, part = it & 3;
         const int r = n / g.M, c = n - (n / g.M) * g.M;
         tok[u] = token_index(g, w.b, w.wy, w.wx, r, c);
-        const int64_t off = tok[u] * rowstride + w.h * 32 + part * 8;
-        ro[u] = *reinterpret_cast<const uint4*>(out + off);
-        rd[u] = *reinterpret_cast<const uint4*>(dout + off);
-        rv[u] = *reinterpret_cast<const uint4*>(v + off);
-        rq[u] = *reinterpret_cast<const uint4*>(q + off);
-        rk[u] = *reinterpret_cast<const uint4*>(k + off);
+        const int64_t oo = tok[u] * g.os + w.h * 32 + part * 8;
+        const int64_t xo = tok[u] * g.xs + w.h * 32 + part * 8;
+        ro[u] = *reinterpret_cast<const uint4*>(out + oo);
+        rd[u] = *reinterpret_cast<const uint4*>(dout + oo);
+        rv[u] = *reinterpret_cast<const uint4*>(v + xo);
+        rq[u] = *reinterpret_cast<const uint4*>(q + xo);
+        rk[u] = *reinterpret_cast<const uint4*>(k + xo);
       }
     }
 #pragma unroll
@@ -252,7 +252,7 @@ __device__ inline void dq_body(const uint16_t* __restrict__ q, const uint16_t* _
   const int CH = chunk_len(NP);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int h = lane >> 5, col = lane & 31;
-  const int64_t rowstride = (int64_t)g.heads * D;
+  const int64_t xs = g.xs;
   const float ds_scale = pow2_scale(64.f * scal[wh * 4] * scal[wh * 4 + 1]);
 
   uint4 ik[IPT], iv[IPT];
@@ -265,7 +265,7 @@ __device__ inline void dq_body(const uint16_t* __restrict__ q, const uint16_t* _
       iv[i] = ik[i];
       if (it < CH * 4 && kn < N) {
         const int r_ = kn / M, c_ = kn - (kn / M) * M;
-        const int64_t off = token_index(g, w.b, w.wy, w.wx, r_, c_) * rowstride + w.h * D + (it & 3) * 8;
+        const int64_t off = token_index(g, w.b, w.wy, w.wx, r_, c_) * xs + w.h * D + (it & 3) * 8;
         ik[i] = *reinterpret_cast<const uint4*>(k + off);
         iv[i] = *reinterpret_cast<const uint4*>(v + off);
       }
@@ -290,11 +290,11 @@ __device__ inline void dq_body(const uint16_t* __restrict__ q, const uint16_t* _
     float lse2 = 0.f, del = 0.f;
     if (valid) {
       const int64_t tok = token_index(g, w.b, w.wy, w.wx, r, c);
-      const int64_t off = tok * rowstride + w.h * D;
+      const int64_t off = tok * xs + w.h * D, goff = tok * g.os + w.h * D;
       const uint4 q0 = *reinterpret_cast<const uint4*>(q + off + 8 * h);
       const uint4 q1 = *reinterpret_cast<const uint4*>(q + off + 16 + 8 * h);
-      const uint4 g0 = *reinterpret_cast<const uint4*>(dout + off + 8 * h);
-      const uint4 g1 = *reinterpret_cast<const uint4*>(dout + off + 16 + 8 * h);
+      const uint4 g0 = *reinterpret_cast<const uint4*>(dout + goff + 8 * h);
+      const uint4 g1 = *reinterpret_cast<const uint4*>(dout + goff + 16 + 8 * h);
       lse2 = lse[tok * g.heads + w.h] * kLog2e;
       del = delta[tok * g.heads + w.h] * ds_scale;
       qb0[t] = rotated_part<H16>(q0, sm.sn, sm.cs, M, r, c, h, kQScale);
@@ -402,7 +402,7 @@ __device__ inline void dq_body(const uint16_t* __restrict__ q, const uint16_t* _
     const int qi = qbase + 32 * t;
     if (qi < N) {
       const int r = qi / M, c = qi - (qi / M) * M;
-      const int64_t off = token_index(g, w.b, w.wy, w.wx, r, c) * rowstride + w.h * D;
+      const int64_t off = token_index(g, w.b, w.wy, w.wx, r, c) * xs + w.h * D;
       // dq~ = acc / tau / sqrt(d); the dtheta integrand takes q~ as the dK product saw it
       unrotate_store(acc[t], 0.17677669529663687f / ds_scale, kQScale, H16, q + off, dq + off, sm.sn, sm.cs, M, r, c,
                      h, th);
@@ -479,7 +479,7 @@ __device__ inline void dkdv_body(const uint16_t* __restrict__ q, const uint16_t*
   const int CH = chunk_len(NP);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int h = lane >> 5, col = lane & 31;
-  const int64_t rowstride = (int64_t)g.heads * D;
+  const int64_t xs = g.xs;
   const float g_scale = pow2_scale(scal[wh * 4]);                              // dO of the dV product
   const float ds_scale = pow2_scale(64.f * scal[wh * 4] * scal[wh * 4 + 1]);  // dS of the dK product
 
@@ -497,9 +497,9 @@ __device__ inline void dkdv_body(const uint16_t* __restrict__ q, const uint16_t*
       if (it < CH * 4 && qn < N) {
         const int r_ = qn / M, c_ = qn - (qn / M) * M;
         const int64_t t_ = token_index(g, w.b, w.wy, w.wx, r_, c_);
-        const int64_t off = t_ * rowstride + w.h * D + (it & 3) * 8;
+        const int64_t off = t_ * xs + w.h * D + (it & 3) * 8;
         iq[i] = *reinterpret_cast<const uint4*>(q + off);
-        ig[i] = *reinterpret_cast<const uint4*>(dout + off);
+        ig[i] = *reinterpret_cast<const uint4*>(dout + t_ * g.os + w.h * D + (it & 3) * 8);
         if ((it & 3) == 0) {
           il[i] = lse[t_ * g.heads + w.h];
           id[i] = delta[t_ * g.heads + w.h];
@@ -524,7 +524,7 @@ __device__ inline void dkdv_body(const uint16_t* __restrict__ q, const uint16_t*
     wl |= valid ? (1u << klab[t]) : 0u;
     kb0[t] = kb1[t] = vb0[t] = vb1[t] = make_uint4(0, 0, 0, 0);
     if (valid) {
-      const int64_t off = token_index(g, w.b, w.wy, w.wx, r, c) * rowstride + w.h * D;
+      const int64_t off = token_index(g, w.b, w.wy, w.wx, r, c) * xs + w.h * D;
       const uint4 k0 = *reinterpret_cast<const uint4*>(k + off + 8 * h);
       const uint4 k1 = *reinterpret_cast<const uint4*>(k + off + 16 + 8 * h);
       const uint4 v0 = *reinterpret_cast<const uint4*>(v + off + 8 * h);
@@ -668,7 +668,7 @@ __device__ inline void dkdv_body(const uint16_t* __restrict__ q, const uint16_t*
     const int kj = kbase + 32 * t;
     if (kj < N) {
       const int r = kj / M, c = kj - (kj / M) * M;
-      const int64_t off = token_index(g, w.b, w.wy, w.wx, r, c) * rowstride + w.h * D;
+      const int64_t off = token_index(g, w.b, w.wy, w.wx, r, c) * xs + w.h * D;
       // dV = accv / g: lane holds channels 8g + 4h + j of its key
 #pragma unroll
       for (int gq = 0; gq < 4; ++gq) {

@@ -94,7 +94,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkdv_scalar_kernel(
   const bool active = j < N;
   const float* tr = th_row + w.h * (D / 4);
   const float* tc = th_col + w.h * (D / 4);
-  const int64_t rowstride = (int64_t)g.heads * D;
+  const int64_t xs = g.xs, os = g.os;
   const float qscale = kLog2e * rsqrtf((float)D);
 
   float kt[D], vv[D];
@@ -104,8 +104,8 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkdv_scalar_kernel(
     kr = j / g.M;
     kc = j - kr * g.M;
     ktok = token_index(g, w.b, w.wy, w.wx, kr, kc);
-    load_row<D>(k + ktok * rowstride + w.h * D, kt);
-    load_row<D>(v + ktok * rowstride + w.h * D, vv);
+    load_row<D>(k + ktok * xs + w.h * D, kt);
+    load_row<D>(v + ktok * xs + w.h * D, vv);
     rope_rotate<D>(kt, tr, tc, kr, kc);
     klab = token_label(g, w.wy, w.wx, kr, kc);
   } else {
@@ -124,8 +124,8 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkdv_scalar_kernel(
         const int r = i / g.M, c = i - (i / g.M) * g.M;
         const int64_t tok = token_index(g, w.b, w.wy, w.wx, r, c);
         float qv[D], gv[D];
-        load_row<D>(q + tok * rowstride + w.h * D, qv);
-        load_row<D>(dout + tok * rowstride + w.h * D, gv);
+        load_row<D>(q + tok * xs + w.h * D, qv);
+        load_row<D>(dout + tok * os + w.h * D, gv);
         rope_rotate<D>(qv, tr, tc, r, c);
 #pragma unroll
         for (int e = 0; e < D; ++e) {
@@ -165,8 +165,8 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkdv_scalar_kernel(
   if (active) {
     dtheta_terms<D>(kt, dkt, kr, kc, terms);
     rope_unrotate<D>(dkt, tr, tc, kr, kc);
-    store_row<D>(dk + ktok * rowstride + w.h * D, dkt);
-    store_row<D>(dv + ktok * rowstride + w.h * D, dvv);
+    store_row<D>(dk + ktok * xs + w.h * D, dkt);
+    store_row<D>(dv + ktok * xs + w.h * D, dvv);
   }
   reduce_dtheta_block<D>(terms, partials + partial_row(g, blk, nb, 0) * (D / 2));
 }
@@ -188,7 +188,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dq_scalar_kernel(
   const bool active = i < N;
   const float* tr = th_row + w.h * (D / 4);
   const float* tc = th_col + w.h * (D / 4);
-  const int64_t rowstride = (int64_t)g.heads * D;
+  const int64_t xs = g.xs, os = g.os;
   const float qscale = kLog2e * rsqrtf((float)D);
   const float kscale = rsqrtf((float)D);
 
@@ -200,8 +200,8 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dq_scalar_kernel(
     qr = i / g.M;
     qc = i - qr * g.M;
     qtok = token_index(g, w.b, w.wy, w.wx, qr, qc);
-    load_row<D>(q + qtok * rowstride + w.h * D, qt);
-    load_row<D>(dout + qtok * rowstride + w.h * D, gv);
+    load_row<D>(q + qtok * xs + w.h * D, qt);
+    load_row<D>(dout + qtok * os + w.h * D, gv);
     rope_rotate<D>(qt, tr, tc, qr, qc);
     l2 = lse[qtok * g.heads + w.h] * kLog2e;
     del = delta[qtok * g.heads + w.h];
@@ -224,8 +224,8 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dq_scalar_kernel(
         const int r = j / g.M, c = j - (j / g.M) * g.M;
         const int64_t tok = token_index(g, w.b, w.wy, w.wx, r, c);
         float kv[D], vv[D];
-        load_row<D>(k + tok * rowstride + w.h * D, kv);
-        load_row<D>(v + tok * rowstride + w.h * D, vv);
+        load_row<D>(k + tok * xs + w.h * D, kv);
+        load_row<D>(v + tok * xs + w.h * D, vv);
         rope_rotate<D>(kv, tr, tc, r, c);
 #pragma unroll
         for (int e = 0; e < D; ++e) {
@@ -260,7 +260,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dq_scalar_kernel(
   if (active) {
     dtheta_terms<D>(qt, dqt, qr, qc, terms);
     rope_unrotate<D>(dqt, tr, tc, qr, qc);
-    store_row<D>(dq + qtok * rowstride + w.h * D, dqt);
+    store_row<D>(dq + qtok * xs + w.h * D, dqt);
   }
   reduce_dtheta_block<D>(terms, partials + partial_row(g, blk, nb, 1) * (D / 2));
 }

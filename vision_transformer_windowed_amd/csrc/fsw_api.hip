@@ -42,7 +42,17 @@ int check_shape(int64_t B, int64_t Hg, int64_t Wg, int heads, int d, int M, int 
   g->nH = (int)(Hg / M);
   g->nW = (int)(Wg / M);
   g->N = M * M;
+  g->xs = (int64_t)heads * d;
+  g->os = (int64_t)heads * d;
   return FSW_OK;
+}
+
+size_t elem_bytes(int dtype) { return dtype == FSW_BF16 ? 2 : 4; }
+
+// Byte ranges [a, a + na) and [b, b + nb) overlap.
+bool overlap(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return x < y + nb && y < x + na;
 }
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -67,11 +77,48 @@ WsLayout workspace_layout(const fsw::Geom& g, bool mfma) {
 bool use_mfma_fwd(const fsw::Geom& g, int dtype) { return dtype == FSW_BF16 && g.d == 32 && g.M <= kMaxM; }
 bool use_mfma(const fsw::Geom& g, int dtype) { return fsw::kHaveMfmaBwd && use_mfma_fwd(g, dtype); }
 
+// Pointer checks and dispatch of a forward whose shape (and q/k/v token stride) is in g.
+int fwd_impl(const void* q, const void* k, const void* v, const float* theta_row, const float* theta_col, void* out,
+             float* lse, const fsw::Geom& g, int dtype, void* hip_stream) {
+  if (!q || !k || !v || !out || !theta_row || !theta_col) return FSW_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16)) return FSW_ERR_INVALID_ARG;
+  if (!aligned(theta_row, 4) || !aligned(theta_col, 4) || (lse && !aligned(lse, 4))) return FSW_ERR_INVALID_ARG;
+  fsw::FwdArgs a{q, k, v, theta_row, theta_col, out, lse, g, dtype};
+  hipStream_t s = reinterpret_cast<hipStream_t>(hip_stream);
+  const hipError_t e = use_mfma_fwd(g, dtype) ? fsw::launch_fwd_mfma(a, s) : fsw::launch_fwd_scalar(a, s);
+  return e == hipSuccess ? FSW_OK : FSW_ERR_HIP;
+}
+
+// Pointer, workspace checks and dispatch of a backward whose shape (and strides) is in g.
+int bwd_impl(const void* q, const void* k, const void* v, const void* out, const void* dout, const float* lse,
+             const float* theta_row, const float* theta_col, void* dq, void* dk, void* dv, float* dtheta_row,
+             float* dtheta_col, void* workspace, size_t workspace_bytes, const fsw::Geom& g, int dtype,
+             void* hip_stream) {
+  const void* ptrs16[] = {q, k, v, out, dout, dq, dk, dv};
+  for (const void* p : ptrs16)
+    if (!p || !aligned(p, 16)) return FSW_ERR_INVALID_ARG;
+  const void* ptrs4[] = {lse, theta_row, theta_col, dtheta_row, dtheta_col};
+  for (const void* p : ptrs4)
+    if (!p || !aligned(p, 4)) return FSW_ERR_INVALID_ARG;
+  if (dtheta_row == dtheta_col) return FSW_ERR_INVALID_ARG;
+  const bool mfma = use_mfma(g, dtype);
+  const WsLayout ws = workspace_layout(g, mfma);
+  if (!workspace || !aligned(workspace, 256) || workspace_bytes < ws.total) return FSW_ERR_WORKSPACE;
+  char* base = static_cast<char*>(workspace);
+  fsw::BwdArgs a{q,  k,  v,          out,        dout, lse, theta_row, theta_col,
+                 dq, dk, dv,         dtheta_row, dtheta_col, g, dtype,
+                 reinterpret_cast<float*>(base + ws.delta_off), reinterpret_cast<float*>(base + ws.scal_off),
+                 reinterpret_cast<float*>(base + ws.partials_off), ws.n_partials};
+  hipStream_t s = reinterpret_cast<hipStream_t>(hip_stream);
+  const hipError_t e = mfma ? fsw::launch_bwd_mfma(a, s) : fsw::launch_bwd_scalar(a, s);
+  return e == hipSuccess ? FSW_OK : FSW_ERR_HIP;
+}
+
 }  // namespace
 
 extern "C" {
 
-int flashswin_version(void) { return 100; }
+int flashswin_version(void) { return 101; }
 
 const char* flashswin_status_string(int status) {
   switch (status) {
@@ -91,14 +138,25 @@ int flashswin_wattn_fwd(const void* q, const void* k, const void* v, const float
   int st = check_shape(B, Hg, Wg, heads, d, M, shift, dtype, &g);
   if (st != FSW_OK) return st;
   if (B == 0) return FSW_OK;
-  if (!q || !k || !v || !out || !theta_row || !theta_col) return FSW_ERR_INVALID_ARG;
-  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16)) return FSW_ERR_INVALID_ARG;
-  if (!aligned(theta_row, 4) || !aligned(theta_col, 4) || (lse && !aligned(lse, 4))) return FSW_ERR_INVALID_ARG;
   if (out == q || out == k || out == v) return FSW_ERR_INVALID_ARG;
-  fsw::FwdArgs a{q, k, v, theta_row, theta_col, out, lse, g, dtype};
-  hipStream_t s = reinterpret_cast<hipStream_t>(hip_stream);
-  const hipError_t e = use_mfma_fwd(g, dtype) ? fsw::launch_fwd_mfma(a, s) : fsw::launch_fwd_scalar(a, s);
-  return e == hipSuccess ? FSW_OK : FSW_ERR_HIP;
+  return fwd_impl(q, k, v, theta_row, theta_col, out, lse, g, dtype, hip_stream);
+}
+
+int flashswin_wattn_fwd_packed(const void* qkv, const float* theta_row, const float* theta_col, void* out, float* lse,
+                               int64_t B, int64_t Hg, int64_t Wg, int heads, int d, int M, int shift, int dtype,
+                               void* hip_stream) {
+  fsw::Geom g;
+  int st = check_shape(B, Hg, Wg, heads, d, M, shift, dtype, &g);
+  if (st != FSW_OK) return st;
+  if (B == 0) return FSW_OK;
+  if ((long double)B * Hg * Wg * 3 * heads * d > (long double)((int64_t)1 << 56)) return FSW_ERR_UNSUPPORTED;
+  if (!qkv) return FSW_ERR_INVALID_ARG;
+  const size_t eb = elem_bytes(dtype), tens = (size_t)(B * Hg * Wg) * g.os * eb;
+  if (out && overlap(qkv, 3 * tens, out, tens)) return FSW_ERR_INVALID_ARG;
+  g.xs = 3 * g.os;
+  const char* base = static_cast<const char*>(qkv);
+  const size_t slot = (size_t)g.os * eb;  // bytes from q to k and from k to v within a token
+  return fwd_impl(base, base + slot, base + 2 * slot, theta_row, theta_col, out, lse, g, dtype, hip_stream);
 }
 
 size_t flashswin_wattn_bwd_workspace_size(int64_t B, int64_t Hg, int64_t Wg, int heads, int d, int M, int shift,
@@ -117,29 +175,36 @@ int flashswin_wattn_bwd(const void* q, const void* k, const void* v, const void*
   int st = check_shape(B, Hg, Wg, heads, d, M, shift, dtype, &g);
   if (st != FSW_OK) return st;
   if (B == 0) return FSW_OK;
-  const void* ptrs16[] = {q, k, v, out, dout, dq, dk, dv};
-  for (const void* p : ptrs16)
-    if (!p || !aligned(p, 16)) return FSW_ERR_INVALID_ARG;
-  const void* ptrs4[] = {lse, theta_row, theta_col, dtheta_row, dtheta_col};
-  for (const void* p : ptrs4)
-    if (!p || !aligned(p, 4)) return FSW_ERR_INVALID_ARG;
   const void* outs[] = {dq, dk, dv};
   const void* ins[] = {q, k, v, out, dout};
   for (const void* o : outs)
     for (const void* i : ins)
-      if (o == i) return FSW_ERR_INVALID_ARG;
-  if (dq == dk || dq == dv || dk == dv || dtheta_row == dtheta_col) return FSW_ERR_INVALID_ARG;
-  const bool mfma = use_mfma(g, dtype);
-  const WsLayout ws = workspace_layout(g, mfma);
-  if (!workspace || !aligned(workspace, 256) || workspace_bytes < ws.total) return FSW_ERR_WORKSPACE;
-  char* base = static_cast<char*>(workspace);
-  fsw::BwdArgs a{q,  k,  v,          out,        dout, lse, theta_row, theta_col,
-                 dq, dk, dv,         dtheta_row, dtheta_col, g, dtype,
-                 reinterpret_cast<float*>(base + ws.delta_off), reinterpret_cast<float*>(base + ws.scal_off),
-                 reinterpret_cast<float*>(base + ws.partials_off), ws.n_partials};
-  hipStream_t s = reinterpret_cast<hipStream_t>(hip_stream);
-  const hipError_t e = mfma ? fsw::launch_bwd_mfma(a, s) : fsw::launch_bwd_scalar(a, s);
-  return e == hipSuccess ? FSW_OK : FSW_ERR_HIP;
+      if (o && o == i) return FSW_ERR_INVALID_ARG;
+  if (dq == dk || dq == dv || dk == dv) return FSW_ERR_INVALID_ARG;
+  return bwd_impl(q, k, v, out, dout, lse, theta_row, theta_col, dq, dk, dv, dtheta_row, dtheta_col, workspace,
+                  workspace_bytes, g, dtype, hip_stream);
+}
+
+int flashswin_wattn_bwd_packed(const void* qkv, const void* out, const void* dout, const float* lse,
+                               const float* theta_row, const float* theta_col, void* dqkv, float* dtheta_row,
+                               float* dtheta_col, void* workspace, size_t workspace_bytes, int64_t B, int64_t Hg,
+                               int64_t Wg, int heads, int d, int M, int shift, int dtype, void* hip_stream) {
+  fsw::Geom g;
+  int st = check_shape(B, Hg, Wg, heads, d, M, shift, dtype, &g);
+  if (st != FSW_OK) return st;
+  if (B == 0) return FSW_OK;
+  if ((long double)B * Hg * Wg * 3 * heads * d > (long double)((int64_t)1 << 56)) return FSW_ERR_UNSUPPORTED;
+  if (!qkv || !dqkv) return FSW_ERR_INVALID_ARG;
+  const size_t eb = elem_bytes(dtype), tens = (size_t)(B * Hg * Wg) * g.os * eb;
+  if (overlap(dqkv, 3 * tens, qkv, 3 * tens) || (out && overlap(dqkv, 3 * tens, out, tens)) ||
+      (dout && overlap(dqkv, 3 * tens, dout, tens)))
+    return FSW_ERR_INVALID_ARG;
+  g.xs = 3 * g.os;
+  const size_t slot = (size_t)g.os * eb;
+  const char* x = static_cast<const char*>(qkv);
+  char* dx = static_cast<char*>(dqkv);
+  return bwd_impl(x, x + slot, x + 2 * slot, out, dout, lse, theta_row, theta_col, dx, dx + slot, dx + 2 * slot,
+                  dtheta_row, dtheta_col, workspace, workspace_bytes, g, dtype, hip_stream);
 }
 
 }  // extern "C"

@@ -18,6 +18,8 @@ struct Geom {
   int Hg, Wg, heads, d, M, shift;
   int nH, nW;  // windows per image along rows / columns
   int N;       // tokens per window, M*M
+  int64_t xs;  // elements between consecutive tokens of q, k, v and of dq, dk, dv
+  int64_t os;  // elements between consecutive tokens of out and dout (heads * d)
 };
 
 constexpr float kLog2e = 1.4426950408889634f;

@@ -43,13 +43,12 @@ __device__ __forceinline__ void m8_issue(const uint16_t* __restrict__ q, const u
                                          uint16_t* qs, uint16_t* ks, uint16_t* vs) {
   typedef __attribute__((address_space(3))) void lds_t;
   const WinHead w = decode_winhead(g, wh);
-  const int64_t rowstride = (int64_t)g.heads * 32;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int slot = i * 64 + lane;
     const int row = slot >> 2, pc = slot & 3;
     const int lc = pc ^ ((row >> 2) & 3);
-    const int64_t base = token_index(g, w.b, w.wy, w.wx, row >> 3, row & 7) * rowstride + w.h * 32;
+    const int64_t base = token_index(g, w.b, w.wy, w.wx, row >> 3, row & 7) * g.xs + w.h * 32;
     __builtin_amdgcn_global_load_lds((const void*)(q + base + lc * 8), (lds_t*)(qs + i * 512), 16, 0, 0);
     __builtin_amdgcn_global_load_lds((const void*)(k + base + lc * 8), (lds_t*)(ks + i * 512), 16, 0, 0);
     __builtin_amdgcn_global_load_lds((const void*)(v + base + pc * 8), (lds_t*)(vs + i * 512), 16, 0, 0);
@@ -147,7 +146,6 @@ __device__ __forceinline__ void m8_attend(const uint4 (&kop)[2][2], const uint4 
                                           const WinHead& w, const uint16_t* vbuf, const uint8_t* lab, bool masked,
                                           float kmax, const float (&qn2)[2], int lane) {
   const int h = lane >> 5, col = lane & 31;
-  const int64_t rowstride = (int64_t)g.heads * 32;
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
     const int n = t * 32 + col;
@@ -172,7 +170,7 @@ __device__ __forceinline__ void m8_attend(const uint4 (&kop)[2][2], const uint4 
     // O = O^T / l (lane: query col, channels 8g + 4h + j), LSE = (ref + log2 l) ln 2
     const int64_t qtok = token_index(g, w.b, w.wy, w.wx, qr, qc);
     const float inv = 1.f / lt;
-    uint16_t* dst = out + qtok * rowstride + w.h * 32 + 4 * h;
+    uint16_t* dst = out + qtok * g.os + w.h * 32 + 4 * h;
 #pragma unroll
     for (int gq = 0; gq < 4; ++gq) {
       uint2 pr;

@@ -239,7 +239,6 @@ __device__ __forceinline__ void load_kv(const uint16_t* __restrict__ k, const ui
                                         const WinHead& w, int M, int NP, int tid, int nt, bool with_v,
                                         uint4 (&kraw)[MAXIT], uint4 (&vraw)[MAXIT]) {
   const int N = M * M;
-  const int64_t rowstride = (int64_t)g.heads * 32;
 #pragma unroll
   for (int i = 0; i < MAXIT; ++i) {
     const int it = tid + i * nt;
@@ -247,7 +246,7 @@ __device__ __forceinline__ void load_kv(const uint16_t* __restrict__ k, const ui
     kraw[i] = vraw[i] = make_uint4(0, 0, 0, 0);
     if (it < NP * 4 && key < N) {
       const int r = key / M, c = key - (key / M) * M;
-      const int64_t off = tok_of(g, w, M, r, c) * rowstride + w.h * 32 + (it & 3) * 8;
+      const int64_t off = tok_of(g, w, M, r, c) * g.xs + w.h * 32 + (it & 3) * 8;
       kraw[i] = *reinterpret_cast<const uint4*>(k + off);
       if (with_v) vraw[i] = *reinterpret_cast<const uint4*>(v + off);
     }
@@ -299,7 +298,6 @@ __global__ __launch_bounds__(NWAVES * 64) void fwd_mfma_kernel(const uint16_t* _
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int64_t rowstride = (int64_t)g.heads * D;
   const int h = lane >> 5;
   const int col = lane & 31;
 
@@ -311,7 +309,7 @@ __global__ __launch_bounds__(NWAVES * 64) void fwd_mfma_kernel(const uint16_t* _
     const int qi = (qoff + qb) * NT / 2 + wave * 32 + col;
     a = b = make_uint4(0, 0, 0, 0);
     if (qb < nqw && qi < N) {
-      const int64_t off = tok_of(g, w, M, qi / M, qi - (qi / M) * M) * rowstride + w.h * D;
+      const int64_t off = tok_of(g, w, M, qi / M, qi - (qi / M) * M) * g.xs + w.h * D;
       a = *reinterpret_cast<const uint4*>(q + off + 8 * h);
       b = *reinterpret_cast<const uint4*>(q + off + 16 + 8 * h);
     }
@@ -454,7 +452,7 @@ __global__ __launch_bounds__(NWAVES * 64) void fwd_mfma_kernel(const uint16_t* _
     if (qvalid) {
       const int64_t qtok = tok_of(g, w, M, qr, qc);
       const float inv = 1.f / lt;
-      uint16_t* dst = out + qtok * rowstride + w.h * D + 4 * h;
+      uint16_t* dst = out + qtok * g.os + w.h * D + 4 * h;
 #pragma unroll
       for (int gq = 0; gq < 4; ++gq) {
         uint2 pr;

@@ -35,7 +35,7 @@ __global__ __launch_bounds__(kScalarThreads) void fwd_scalar_kernel(const IO* __
   const bool active = n < N;
   const float* tr = th_row + w.h * (D / 4);
   const float* tc = th_col + w.h * (D / 4);
-  const int64_t rowstride = (int64_t)g.heads * D;
+  const int64_t xs = g.xs, os = g.os;
 
   float qv[D];
   int qlab = 0;
@@ -43,7 +43,7 @@ __global__ __launch_bounds__(kScalarThreads) void fwd_scalar_kernel(const IO* __
   if (active) {
     const int r = n / g.M, c = n - (n / g.M) * g.M;
     qtok = token_index(g, w.b, w.wy, w.wx, r, c);
-    load_row<D>(q + qtok * rowstride + w.h * D, qv);
+    load_row<D>(q + qtok * xs + w.h * D, qv);
     rope_rotate<D>(qv, tr, tc, r, c);
     const float sc = kLog2e * rsqrtf((float)D);
 #pragma unroll
@@ -67,8 +67,8 @@ __global__ __launch_bounds__(kScalarThreads) void fwd_scalar_kernel(const IO* __
         const int r = j / g.M, c = j - (j / g.M) * g.M;
         const int64_t tok = token_index(g, w.b, w.wy, w.wx, r, c);
         float kv[D], vv[D];
-        load_row<D>(k + tok * rowstride + w.h * D, kv);
-        load_row<D>(v + tok * rowstride + w.h * D, vv);
+        load_row<D>(k + tok * xs + w.h * D, kv);
+        load_row<D>(v + tok * xs + w.h * D, vv);
         rope_rotate<D>(kv, tr, tc, r, c);
 #pragma unroll
         for (int i = 0; i < D; ++i) {
@@ -127,7 +127,7 @@ __global__ __launch_bounds__(kScalarThreads) void fwd_scalar_kernel(const IO* __
     const float inv = 1.f / l;
 #pragma unroll
     for (int i = 0; i < D; ++i) acc[i] *= inv;
-    store_row<D>(out + qtok * rowstride + w.h * D, acc);
+    store_row<D>(out + qtok * os + w.h * D, acc);
     if (lse) lse[qtok * g.heads + w.h] = m * kLn2 + logf(l);
   }
 }

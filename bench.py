@@ -134,6 +134,44 @@ def m8_forward_roofline(dev, steps, warmup):
             "algorithmic_bytes": nbytes, "launch_ms": round(ms, 4)}
 
 
+def m16_step(dev, steps, warmup):
+    """Forward and backward at M = 16 (the pages' comparison-table window) on the stage-1 grid:
+    TFLOP/s under the dense 4 N^2 d / 10 N^2 d conventions."""
+    import torch
+    import vision_transformer_windowed_amd as F
+    from vision_transformer_windowed_amd.inputs import WORKLOADS, workload_inputs
+    name = "flashswin_t_s1_p2_m16"
+    w = WORKLOADS[name]
+    M = w["M"]
+    x = {k: v.to(dev) for k, v in workload_inputs(name, with_dout=True).items()}
+    q, k, v, dout, tr, tc = x["q"], x["k"], x["v"], x["dout"], x["theta_row"], x["theta_col"]
+    out = torch.empty_like(q)
+    lse = torch.empty(q.shape[:4], device=dev, dtype=torch.float32)
+    grads = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v), torch.empty_like(tr),
+             torch.empty_like(tc))
+    ws = torch.empty(max(F.bwd_workspace_bytes(q, M, 0), 1), device=dev, dtype=torch.uint8)
+    stream = torch.cuda.current_stream(dev)
+    N = M * M
+    nwh = w["B"] * (w["Hg"] // M) * (w["Wg"] // M) * w["heads"]
+    res = {"workload": name, "shift": 0}
+    for tag, fn in (("fwd", lambda: F.wattn_fwd(q, k, v, tr, tc, M, 0, out=out, lse=lse)),
+                    ("bwd", lambda: F.wattn_bwd(q, k, v, out, dout, lse, tr, tc, M, 0, workspace=ws, grads=grads))):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(steps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / steps
+        flops = (4.0 if tag == "fwd" else 10.0) * N * N * w["d"] * nwh
+        res[tag + "_ms"] = round(ms, 4)
+        res[tag + "_tflops"] = round(flops / (ms * 1e-3) / 1e12, 2)
+    return res
+
+
 def packed_forward(dev, steps, warmup):
     """M=8 Swin-T stage-1 forward (HBM-bound) from packed qkv [B, Hg, Wg, 3, heads, d]: read in place by
     the packed entry point, against splitting it into contiguous q, k, v first (three copies) and calling
@@ -283,10 +321,11 @@ def main():
         fwd_roofline = {"kernel": "wattn_fwd", "bound": "mfma", "achieved": round(fwd_tf, 2),
                         "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(fwd_tf / BF16_MFMA_PEAK_TFLOPS, 4),
                         "launch_ms": round(fwd_ms, 4)}
-    m8 = packed = None
+    m8 = packed = m16 = None
     if not args.no_secondary and args.only == "step":
         m8 = m8_forward_roofline(dev, max(args.steps, 10), max(args.warmup, 2))
         packed = packed_forward(dev, max(args.steps, 10), max(args.warmup, 2))
+        m16 = m16_step(dev, max(args.steps, 10), max(args.warmup, 2))
 
     gpu_out = {"out": out, "lse": lse, "dq": grads[0], "dk": grads[1], "dv": grads[2]}
     cpu, parity = (None, None)
@@ -318,6 +357,7 @@ def main():
         "fwd_roofline": fwd_roofline,
         "m8_fwd_roofline": m8,
         "m8_fwd_packed_qkv": packed,
+        "m16_step": m16,
         "cpu_baseline": cpu,
         "parity_sample": parity,
         "input_gen_s": round(gen_s, 1),

@@ -86,6 +86,7 @@ FWD_SMALL = [
     (1, 6, 6, 2, 32, 1, 0, "bf16"),
     (1, 14, 14, 2, 64, 7, 3, "bf16"),
     (1, 16, 16, 2, 16, 8, 4, "bf16"),
+    (1, 32, 48, 2, 32, 16, 8, "bf16"),
 ]
 
 
@@ -214,6 +215,7 @@ BWD_SMALL = [
     (1, 24, 24, 2, 32, 12, 5, "bf16"),
     (1, 10, 10, 2, 32, 5, 2, "bf16"),
     (1, 16, 16, 2, 16, 8, 4, "bf16"),
+    (1, 32, 48, 2, 32, 16, 8, "bf16"),
 ]
 
 
@@ -287,6 +289,29 @@ def test_backward_workload(shift):
     g = oracle.wattn_bwd_ref(q, k, v, x["dout"][:chunk].double().numpy(), tr, tc, M, shift)
     assert_close("dtheta_row (chunk)", _np(first[0]), g[3], 2e-2, 5e-3, scale_abs=True)
     assert_close("dtheta_col (chunk)", _np(first[1]), g[4], 2e-2, 5e-3, scale_abs=True)
+
+
+@pytest.mark.parametrize("shift", [0, 8])
+def test_m16_workload(shift):
+    """M = 16 at full size (128 images of 128 x 128 tokens, 3 heads): forward and backward on sampled
+    images against the oracle."""
+    name = "flashswin_t_s1_p2_m16"
+    w = WORKLOADS[name]
+    M = w["M"]
+    x = workload_inputs(name, with_dout=True)
+    xd = to_dev(x)
+    out, lse = F.wattn_fwd(xd["q"], xd["k"], xd["v"], xd["theta_row"], xd["theta_col"], M, shift)
+    dq, dk, dv, _, _ = F.wattn_bwd(xd["q"], xd["k"], xd["v"], out, xd["dout"], lse, xd["theta_row"],
+                                   xd["theta_col"], M, shift)
+    torch.cuda.synchronize()
+    imgs = [0, w["B"] - 1]
+    (q, k, v), tr, tc = oracle_args(x, imgs)
+    ro, rl = oracle.wattn_fwd_ref(q, k, v, tr, tc, M, shift)
+    assert_close("O", _np(out[imgs]), ro, 2e-2, 5e-3)
+    assert_close("LSE", _np(lse[imgs]), rl, 2e-2, 5e-3)
+    g = oracle.wattn_bwd_ref(q, k, v, x["dout"][imgs].double().numpy(), tr, tc, M, shift)
+    for nm, got, ref in (("dQ", dq[imgs], g[0]), ("dK", dk[imgs], g[1]), ("dV", dv[imgs], g[2])):
+        assert_close(nm, _np(got), ref, 2e-2, 5e-3)
 
 
 def test_autograd_matches_backward_entry_point():

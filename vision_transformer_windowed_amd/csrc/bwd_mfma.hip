@@ -726,7 +726,8 @@ struct MainShape {
   int waves, sets;
 };
 MainShape main_shape(int N) {
-  if (N > 128) return {8, 2};
+  if (N > 256) return {8, 2};
+  if (N > 128) return {4, 2};
   return {N > 64 ? 4 : 2, 1};
 }
 int64_t blocks_per_windowhead(int N) {
@@ -772,9 +773,10 @@ hipError_t launch_bwd_mfma(const BwdArgs& a, hipStream_t st) {
   if (e != hipSuccess) return e;
   if (g.M == 32) return launch_main<8, 32, 2>(a, st);
   if (g.M == 8) return launch_main<2, 8, 1>(a, st);
+  if (g.M == 16) return launch_main<4, 16, 2>(a, st);
   const MainShape m = main_shape(g.N);
   if (m.waves == 8) return launch_main<8, 0, 2>(a, st);
-  if (m.waves == 4) return launch_main<4, 0, 1>(a, st);
+  if (m.waves == 4) return m.sets == 2 ? launch_main<4, 0, 2>(a, st) : launch_main<4, 0, 1>(a, st);
   return launch_main<2, 0, 1>(a, st);
 }
 

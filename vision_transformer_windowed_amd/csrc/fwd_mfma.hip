@@ -494,6 +494,7 @@ hipError_t launch_fwd_mfma(const FwdArgs& a, hipStream_t st) {
   if (a.g.M == 32) return launch_nw<16, 32, 1024>(a, st);
   if (fwd_m8_supported(a.g)) return launch_fwd_m8(a, st);
   if (a.g.M == 8) return launch_nw<2, 8, 64>(a, st);
+  if (a.g.M == 16) return launch_nw<8, 16, 256>(a, st);
   if (N <= 64) return launch_nw<2, 0, 64>(a, st);
   if (N <= 128) return launch_nw<4, 0, 128>(a, st);
   if (N <= 256) return launch_nw<8, 0, 256>(a, st);

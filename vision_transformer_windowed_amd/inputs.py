@@ -20,6 +20,8 @@ WORKLOADS = {
     "flashswin_t_s1_p2_m32": dict(B=128, Hg=128, Wg=128, heads=3, d=32, M=32, shifts=(0,), dtype="bf16", kind="fwd", seed=1002),
     "flashswin_t_s2_shift16_m32": dict(B=128, Hg=64, Wg=64, heads=6, d=32, M=32, shifts=(16,), dtype="bf16", kind="fwd", seed=1003),
     "flashswin_t_s1_p2_m32_bwd": dict(B=32, Hg=128, Wg=128, heads=3, d=32, M=32, shifts=(0, 16), dtype="bf16", kind="bwd", seed=1004),
+    # the M = 16 windows of the pages' comparison tables, on the stage-1 grid of the M = 32 workload
+    "flashswin_t_s1_p2_m16": dict(B=128, Hg=128, Wg=128, heads=3, d=32, M=16, shifts=(0, 8), dtype="bf16", kind="fwd", seed=1005),
 }
 
 

@@ -5,13 +5,14 @@
 // Efficient Attention": Abstract; Figure 1(B)).  Small windows move ~12 KB per window-head for
 // ~0.5 MFLOP, so this path is bound by HBM and by load latency, not by the matrix cores.
 //
-// One wave owns one window-head.  Its Q, K and V rows travel straight from HBM into the wave's LDS
-// buffers (global_load_lds, 16 bytes per lane, four lanes per 64-byte head row: fully used cache
-// lines); no register holds data in flight, so occupancy is set by LDS alone.  Q and K land in
-// the swizzled row layout (conflict-free operand reads) and are rotated on their way into
-// registers: the 64 keys become two MFMA A blocks (lane = key), the 64 queries two B tiles (lane =
-// query).  V stays row-major for the transposed ds_read_b64_tr_b16 reads of the P.V product.  The
-// RoPE sin/cos tables of every head are built once per workgroup while the loads are in flight.
+// One wave owns one window-head.  Q and K are loaded straight into the registers that hold them as
+// MFMA operands (lane = token, the two 16-byte channel chunks a lane half needs; the two halves
+// together read each 64-byte head row whole) and rotated there: the 64 keys become two A blocks
+// (lane = key), the 64 queries two B tiles (lane = query).  V travels from HBM into the wave's LDS
+// buffer (global_load_lds, 16 bytes per lane, four lanes per row) and stays row-major for the
+// transposed ds_read_b64_tr_b16 reads of the P.V product.  With 4 KB of LDS per wave, four waves
+// share a SIMD (128 registers each).  The RoPE sin/cos tables of every head are built once per
+// workgroup while the loads are in flight.
 // The softmax reference is the Cauchy-Schwarz bound max|q^| * max|k~| of the tile, with an
 // exact-maximum recomputation of a tile whose row sums come out below 2^-80.
 #include <algorithm>
@@ -26,7 +27,7 @@ namespace {
 
 constexpr int kM8Waves = 4;                                 // waves (window-heads) per workgroup
 constexpr int kM8MaxHeads = 32;                             // tables: heads * 1 KB of LDS
-constexpr int kM8WaveLds = 3 * 64 * 32 + 32;                // per wave, 16-bit units: Q, K, V rows, labels
+constexpr int kM8WaveLds = 64 * 32 + 32;                    // per wave, 16-bit units: V rows, labels
 constexpr float kM8LowSum = 8.271806125530277e-25f;         // 2^-80
 constexpr float kM8QScale = kLog2e * 0.17677669529663687f;  // log2(e) / sqrt(32)
 
@@ -34,23 +35,30 @@ __device__ __forceinline__ uint32_t uniform_u32(uint32_t x) {
   return (uint32_t)__builtin_amdgcn_readfirstlane((int)x);
 }
 
-// Issue the HBM -> LDS transfers of window-head wh.  Instruction i moves 64 x 16 bytes into slots
-// i*64 .. i*64+63 of a buffer (lane L's bytes land in slot i*64 + L: row (i*64+L)/4, 16-byte
-// chunk (i*64+L)%4).  For Q and K the lane fetches the logical chunk that the swizzled layout
-// stores in that physical chunk (srow); V is stored unswizzled.
+// Issue every load of window-head wh.  K and Q: the lane's token n = t * 32 + (lane % 32) of tile
+// t, channel chunks h and 2 + h (h = lane / 32), into registers.  V: HBM -> LDS, instruction i
+// moving 64 x 16 bytes into slots i*64 .. i*64+63 (lane L's bytes land in slot i*64 + L: row
+// (i*64+L)/4, 16-byte chunk (i*64+L)%4), row-major.
 __device__ __forceinline__ void m8_issue(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                                          const uint16_t* __restrict__ v, const Geom& g, int64_t wh, int lane,
-                                         uint16_t* qs, uint16_t* ks, uint16_t* vs) {
+                                         uint16_t* vs, uint4 (&kr)[2][2], uint4 (&qr)[2][2]) {
   typedef __attribute__((address_space(3))) void lds_t;
   const WinHead w = decode_winhead(g, wh);
+  const int h = lane >> 5, col = lane & 31;
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const int n = t * 32 + col;
+    const int64_t base = token_index(g, w.b, w.wy, w.wx, n >> 3, n & 7) * g.xs + w.h * 32;
+    kr[t][0] = *reinterpret_cast<const uint4*>(k + base + 8 * h);
+    kr[t][1] = *reinterpret_cast<const uint4*>(k + base + 16 + 8 * h);
+    qr[t][0] = *reinterpret_cast<const uint4*>(q + base + 8 * h);
+    qr[t][1] = *reinterpret_cast<const uint4*>(q + base + 16 + 8 * h);
+  }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int slot = i * 64 + lane;
     const int row = slot >> 2, pc = slot & 3;
-    const int lc = pc ^ ((row >> 2) & 3);
     const int64_t base = token_index(g, w.b, w.wy, w.wx, row >> 3, row & 7) * g.xs + w.h * 32;
-    __builtin_amdgcn_global_load_lds((const void*)(q + base + lc * 8), (lds_t*)(qs + i * 512), 16, 0, 0);
-    __builtin_amdgcn_global_load_lds((const void*)(k + base + lc * 8), (lds_t*)(ks + i * 512), 16, 0, 0);
     __builtin_amdgcn_global_load_lds((const void*)(v + base + pc * 8), (lds_t*)(vs + i * 512), 16, 0, 0);
   }
 }
@@ -183,7 +191,7 @@ __device__ __forceinline__ void m8_attend(const uint4 (&kop)[2][2], const uint4 
   }
 }
 
-// Rotated operands from the raw LDS rows: keys as A blocks, queries (scaled by log2(e)/sqrt(d)) as
+// Rotated operands from the raw rows: keys as A blocks, queries (scaled by log2(e)/sqrt(d)) as
 // B tiles; token n = tile * 32 + col sits at position (n / 8, n % 8).
 template <bool H16>
 __device__ __forceinline__ void m8_operands(const uint4 (&kr)[2][2], const uint4 (&qr)[2][2], const float* sn,
@@ -201,7 +209,7 @@ __device__ __forceinline__ void m8_operands(const uint4 (&kr)[2][2], const uint4
 
 // Workgroup b (in XCD order) owns window-heads b * kM8Waves .. + kM8Waves - 1, one per wave, so a
 // workgroup's waves work on neighbouring window-heads (the heads of one window share cache lines).
-__global__ __launch_bounds__(kM8Waves * 64) void fwd_m8_kernel(const uint16_t* __restrict__ q,
+__global__ __launch_bounds__(kM8Waves * 64, 4) void fwd_m8_kernel(const uint16_t* __restrict__ q,
                                                                const uint16_t* __restrict__ k,
                                                                const uint16_t* __restrict__ v,
                                                                const float* __restrict__ th_row,
@@ -213,14 +221,13 @@ __global__ __launch_bounds__(kM8Waves * 64) void fwd_m8_kernel(const uint16_t* _
   float* tsn = reinterpret_cast<float*>(smem_raw);
   float* tcs = tsn + g.heads * 128;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  uint16_t* qs = reinterpret_cast<uint16_t*>(tcs + g.heads * 128) + wave * kM8WaveLds;
-  uint16_t* ks = qs + 64 * 32;
-  uint16_t* vs = ks + 64 * 32;
+  uint16_t* vs = reinterpret_cast<uint16_t*>(tcs + g.heads * 128) + wave * kM8WaveLds;
   uint8_t* lab = reinterpret_cast<uint8_t*>(vs + 64 * 32);
 
   const int64_t wh = xcd_order(blockIdx.x, gridDim.x) * kM8Waves + wave;
   const bool active = wh < nwh;
-  if (active) m8_issue(q, k, v, g, wh, lane, qs, ks, vs);  // in flight while the tables are built
+  uint4 kr[2][2], qr[2][2];
+  if (active) m8_issue(q, k, v, g, wh, lane, vs, kr, qr);  // in flight while the tables are built
 
   for (int i = tid; i < g.heads * 128; i += kM8Waves * 64) {
     const int head = i >> 7, axis = (i >> 6) & 1, p = (i >> 3) & 7, j = i & 7;
@@ -239,20 +246,10 @@ __global__ __launch_bounds__(kM8Waves * 64) void fwd_m8_kernel(const uint16_t* _
   const uint32_t labels = uniform_u32(wave_or(1u << lbl));
   const bool masked = __builtin_popcount(labels) > 1;
   if (masked) lab[lane] = (uint8_t)lbl;
-  // the wave's transfers are complete once its vector-memory count drains (the asm also keeps the
-  // compiler from moving LDS reads above it)
+  // the wave's V transfers are complete once its vector-memory count drains (the asm also keeps
+  // the compiler from moving LDS reads above it)
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
-  const int h = lane >> 5, col = lane & 31;
-  uint4 kr[2][2], qr[2][2];
-#pragma unroll
-  for (int t = 0; t < 2; ++t) {
-    const int n = t * 32 + col;
-    kr[t][0] = *reinterpret_cast<const uint4*>(ks + srow(n, h));
-    kr[t][1] = *reinterpret_cast<const uint4*>(ks + srow(n, 2 + h));
-    qr[t][0] = *reinterpret_cast<const uint4*>(qs + srow(n, h));
-    qr[t][1] = *reinterpret_cast<const uint4*>(qs + srow(n, 2 + h));
-  }
   // norms: |k|^2 max over the 64 keys, |q|^2 max per query tile (rotation keeps norms)
   float kn0 = m8_norm2(kr[0][0], kr[0][1]);
   float kn1 = m8_norm2(kr[1][0], kr[1][1]);

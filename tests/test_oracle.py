@@ -352,6 +352,54 @@ def test_dv_closed_form_and_dtheta_origin_invariance():
     np.testing.assert_allclose(tot, 0, atol=1e-12)
 
 
+# ----------------------------------------------------------------------------- RoPE structure
+
+def pin_rope_rotation():
+    """Each channel pair is turned by a rotation: per-token norms are unchanged, and the inverse
+    rotation undoes it."""
+    M, H, D = 5, 2, 16
+    rng = np.random.default_rng(41)
+    xw = rng.standard_normal((3, H, M * M, D))
+    tr, tc = rng.standard_normal((H, D // 4)), rng.standard_normal((H, D // 4))
+    rot = wattn_ref.rope_rotate(xw, tr, tc, M)
+    np.testing.assert_allclose(np.linalg.norm(rot, axis=-1), np.linalg.norm(xw, axis=-1), rtol=1e-13)
+    np.testing.assert_allclose(wattn_ref.rope_rotate(rot, tr, tc, M, inverse=True), xw, rtol=0, atol=1e-13)
+    # theta = 0 is the identity
+    z = np.zeros((H, D // 4))
+    np.testing.assert_array_equal(wattn_ref.rope_rotate(xw, z, z, M), xw)
+
+
+def test_rope_keeps_norms_and_inverts():
+    pin_rope_rotation()
+
+
+def pin_relative_position():
+    """With the same q at every token and the same k at every token, the rotated score of a pair
+    depends only on the offset (row_k - row_q, col_k - col_q) within the window."""
+    M, H, D = 4, 2, 8
+    rng = np.random.default_rng(42)
+    qv, kv = rng.standard_normal((H, D)), rng.standard_normal((H, D))
+    q = np.broadcast_to(qv, (1, M, M, H, D)).copy()
+    k = np.broadcast_to(kv, (1, M, M, H, D)).copy()
+    tr, tc = rng.standard_normal((H, D // 4)), rng.standard_normal((H, D // 4))
+    S = oracle.window_scores_ref(q, k, tr, tc, M, 0)[0]  # [H, N, N]
+    by_offset = {}
+    for i in range(M * M):
+        for j in range(M * M):
+            off = (j // M - i // M, j % M - i % M)
+            by_offset.setdefault(off, []).append(S[:, i, j])
+    assert len(by_offset) == (2 * M - 1) ** 2
+    for off, vals in by_offset.items():
+        for v in vals[1:]:
+            np.testing.assert_allclose(v, vals[0], rtol=0, atol=1e-13)
+    # and the zero offset is the plain dot product q . k / sqrt(d)
+    np.testing.assert_allclose(by_offset[(0, 0)][0], (qv * kv).sum(-1) / np.sqrt(D), rtol=0, atol=1e-13)
+
+
+def test_scores_depend_only_on_relative_position():
+    pin_relative_position()
+
+
 # ----------------------------------------------------------------------------- O1 vs O2
 
 O12_CASES = [
@@ -449,7 +497,16 @@ def _mutants():
                 for n, f in saved.items():
                     setattr(ref, n, f)
 
-        m.fwd, m.bwd, m.scores = fwd, bwd, scores
+        def run(fn):
+            for n, f in patch.items():
+                setattr(ref, n, f)
+            try:
+                return fn()
+            finally:
+                for n, f in saved.items():
+                    setattr(ref, n, f)
+
+        m.fwd, m.bwd, m.scores, m.run = fwd, bwd, scores, run
         return m
 
     orig_rope = wattn_ref.rope_rotate
@@ -487,6 +544,13 @@ def _mutants():
         lab = orig_labels(Hg, Wg, M, s)
         return lab // 3
 
+    def rope_not_orthogonal(xw, tr, tc, M, inverse=False):
+        # the second output of each pair built with the wrong sign: a reflection-like map, not a rotation
+        out = orig_rope(xw, tr, tc, M, inverse=inverse)
+        d = xw.shape[-1]
+        out[..., 1:d // 2:2] = 2 * orig_rope(xw, tr * 0, tc * 0, M)[..., 1:d // 2:2] - out[..., 1:d // 2:2]
+        return out
+
     def terms_wrong_sign(xt, dxt, M):
         r, c = orig_terms(xt, dxt, M)
         return -r, -c
@@ -499,6 +563,7 @@ def _mutants():
         "rotation sign flipped": make({"rope_rotate": rope_flipped_sign}),
         "row/col axes swapped": make({"rope_rotate": rope_axes_swapped}),
         "rotate-half pairing": make({"rope_rotate": rope_rotate_half}),
+        "rotation not orthogonal": make({"rope_rotate": rope_not_orthogonal}),
         "shift rolled the wrong way": make({"_roll": roll_wrong_direction, "_unroll": unroll_wrong_direction}),
         "column regions ignored": make({"region_labels": labels_ignore_columns}),
         "dtheta sign flipped": make({"_dtheta_terms": terms_wrong_sign}),
@@ -523,5 +588,7 @@ def test_pins_catch_planted_mistakes(name):
         or _fails(lambda: pin_brute_force(m.fwd))
         or _fails(lambda: pin_finite_differences(m.fwd, m.bwd))
         or _fails(lambda: pin_sdpa(m.fwd, m.bwd))
+        or _fails(lambda: m.run(pin_rope_rotation))
+        or _fails(lambda: m.run(pin_relative_position))
     )
     assert caught, f"no pin failed for planted mistake: {name}"

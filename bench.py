@@ -36,17 +36,16 @@ BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
 # kernels each C-ABI call launches, in order
 CALL_LAUNCHES = {"wattn_fwd": ["fwd_mfma_kernel"],
                  "wattn_bwd": ["bwd_pre_kernel", "bwd_dkdv_mfma_kernel", "bwd_dq_mfma_kernel", "dtheta_reduce_kernel"]}
-KERNEL_SOURCES = ["fwd_mfma.hip", "bwd_mfma.hip", "fwd_scalar.hip", "bwd_scalar.hip", "fsw_common.h",
-                  "fsw_mfma.h", "fsw_api.hip"]
 
 
 def kernel_source_sha():
+    """Hash of every kernel source file: a traffic summary measured on other sources is not used."""
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
-        p = os.path.join(ROOT, "vision_transformer_windowed_amd", "csrc", f)
-        if os.path.exists(p):
+    csrc = os.path.join(ROOT, "vision_transformer_windowed_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith((".hip", ".h")):
             h.update(f.encode())
-            h.update(open(p, "rb").read())
+            h.update(open(os.path.join(csrc, f), "rb").read())
     return h.hexdigest()[:16]
 
 

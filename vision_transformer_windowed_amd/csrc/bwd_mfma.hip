@@ -127,11 +127,32 @@ __device__ inline void unrotate_store(const f32x16_t& dxt, float scale, float op
 
 // ------------------------------------------------------------------------------------ prologue
 
-// One workgroup per window-head: Delta for every token, and
-// scal[wh] = {max |dO|, max |v|, max |q|, max |k|} over the window's components.  Each thread
-// handles kPreBatch 8-channel items per step with all of their 5 x 16-byte loads issued together.
+// Running maximum of |x| over the two bf16 values of a pair, kept as two 16-bit integers: |x| of a
+// bf16 value orders as its bits with the sign cleared.
+typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t absmax_pair(uint32_t acc, uint32_t pair) {
+  return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(u16x2_t, acc),
+                                                                __builtin_bit_cast(u16x2_t, pair & 0x7fff7fffu)));
+}
+// The larger of the two maxima as a float; a NaN component counts as infinity.
+__device__ __forceinline__ float absmax_value(uint32_t acc) {
+  return __uint_as_float(min(max(acc & 0xffffu, acc >> 16), 0x7f80u) << 16);
+}
+
+// One workgroup per window and group of up to kPreHeads heads: Delta for every token and head, and
+// scal[wh] = {max |dO|, max |v|, max |q|, max |k|} over each window-head's components.  The heads of
+// a token sit side by side in one row, so the group's slice of every token row is read whole and
+// each fetched line is used in full.  A thread keeps one 8-channel part p of the slice (head p / 4)
+// for every token it handles, so its maxima belong to one head; kPreBatch tokens per step have
+// their 5 x 16-byte loads issued together.  The work per 16 bytes is kept to a few packed
+// instructions (dot products of bf16 pairs, 16-bit integer maxima), and the loads bypass the caches;
+// the kernel runs at the HBM rate of a plain copy.
 constexpr int kPreThreads = 256;
 constexpr int kPreBatch = 4;
+constexpr int kPreHeads = 16;
+// Off is the type of byte offsets into the tensors: uint32_t when every offset fits (the host checks),
+// which keeps the per-item address arithmetic to a few 32-bit instructions.
+template <typename Off>
 __global__ __launch_bounds__(kPreThreads) void bwd_pre_kernel(const uint16_t* __restrict__ out,
                                                               const uint16_t* __restrict__ dout,
                                                               const uint16_t* __restrict__ v,
@@ -139,71 +160,89 @@ __global__ __launch_bounds__(kPreThreads) void bwd_pre_kernel(const uint16_t* __
                                                               const uint16_t* __restrict__ k,
                                                               float* __restrict__ delta, float* __restrict__ scal,
                                                               Geom g) {
-  __shared__ float red[4][kPreThreads / 64];
-  const int64_t wh = xcd_order(blockIdx.x, gridDim.x);
-  const WinHead w = decode_winhead(g, wh);
+  __shared__ float red[4][kPreThreads];
+  const int groups = (g.heads + kPreHeads - 1) / kPreHeads;
+  const int64_t blk = xcd_order(blockIdx.x, gridDim.x);
+  const int64_t win = blk / groups;
+  const int h0 = (int)(blk - win * groups) * kPreHeads;
+  const int hc = min(kPreHeads, g.heads - h0);
+  const int wx = (int)(win % g.nW);
+  const int wy = (int)((win / g.nW) % g.nH);
+  const int64_t b = win / g.nW / g.nH;
+  const int P = 4 * hc, T = kPreThreads / P;  // parts per token slice, tokens per pass
   const int tid = threadIdx.x;
-  float mx[4] = {0.f, 0.f, 0.f, 0.f};
-  const int items = g.N * 4;
-  const int steps = (items + kPreThreads * kPreBatch - 1) / (kPreThreads * kPreBatch);
+  const bool act = tid < P * T;  // P * T is a multiple of 4: the 4 parts of a head stay together
+  const int p = tid % P, t0 = tid / P;
+  // byte strides of a token and the byte offset of the thread's part within the token row
+  const Off os2 = (Off)(2 * g.os), xs2 = (Off)(2 * g.xs), ch2 = (Off)(2 * (h0 * 32 + p * 8));
+  const Off img = (Off)(b * g.Hg);  // first grid row of the image
+  const char* const po = reinterpret_cast<const char*>(out);
+  const char* const pd = reinterpret_cast<const char*>(dout);
+  const char* const pv = reinterpret_cast<const char*>(v);
+  const char* const pq = reinterpret_cast<const char*>(q);
+  const char* const pk = reinterpret_cast<const char*>(k);
+  // the thread's tokens are t0, t0 + T, ...: window (row, column) advanced by (dr, dc) per token
+  const int dr = T / g.M, dc = T - dr * g.M;
+  int r = t0 / g.M, c = t0 - (t0 / g.M) * g.M;
+  uint32_t am[4] = {0u, 0u, 0u, 0u};
+  const int steps = (g.N + T * kPreBatch - 1) / (T * kPreBatch);
   for (int st = 0; st < steps; ++st) {  // uniform trip count: the shuffles below see every lane
     uint4 ro[kPreBatch], rd[kPreBatch], rv[kPreBatch], rq[kPreBatch], rk[kPreBatch];
-    int64_t tok[kPreBatch];
+    Off tok[kPreBatch];
+    bool ok[kPreBatch];
 #pragma unroll
     for (int u = 0; u < kPreBatch; ++u) {
-      const int it = (st * kPreBatch + u) * kPreThreads + tid;
-      ro[u] = rd[u] = rv[u] = rq[u] = rk[u] = make_uint4(0, 0, 0, 0);
-      tok[u] = 0;
-      if (it < items) {
-        const int n = it >> 2, part = it & 3;
-        const int r = n / g.M, c = n - (n / g.M) * g.M;
-        tok[u] = token_index(g, w.b, w.wy, w.wx, r, c);
-        const int64_t oo = tok[u] * g.os + w.h * 32 + part * 8;
-        const int64_t xo = tok[u] * g.xs + w.h * 32 + part * 8;
-        ro[u] = *reinterpret_cast<const uint4*>(out + oo);
-        rd[u] = *reinterpret_cast<const uint4*>(dout + oo);
-        rv[u] = *reinterpret_cast<const uint4*>(v + xo);
-        rq[u] = *reinterpret_cast<const uint4*>(q + xo);
-        rk[u] = *reinterpret_cast<const uint4*>(k + xo);
+      const int n = (st * kPreBatch + u) * T + t0;
+      ok[u] = act && n < g.N;
+      // an item past the end reads the window's first token again: the maxima are unchanged by a
+      // repeated value and its Delta is not stored
+      const int y = grid_coord(wy * g.M + (ok[u] ? r : 0), g.shift, g.Hg);
+      const int x = grid_coord(wx * g.M + (ok[u] ? c : 0), g.shift, g.Wg);
+      tok[u] = (img + (Off)y) * (Off)g.Wg + (Off)x;
+      const Off oo = tok[u] * os2 + ch2, xo = tok[u] * xs2 + ch2;
+      ro[u] = load_stream(po + oo);
+      rd[u] = load_stream(pd + oo);
+      rv[u] = load_stream(pv + xo);
+      rq[u] = load_stream(pq + xo);
+      rk[u] = load_stream(pk + xo);
+      c += dc;
+      r += dr;
+      if (c >= g.M) {
+        c -= g.M;
+        ++r;
       }
     }
 #pragma unroll
     for (int u = 0; u < kPreBatch; ++u) {
-      const int it = (st * kPreBatch + u) * kPreThreads + tid;
-      float o[8], d[8], x[8], s = 0.f;
-      unpack8(ro[u], o);
-      unpack8(rd[u], d);
+      const uint32_t wo[4] = {ro[u].x, ro[u].y, ro[u].z, ro[u].w}, wd[4] = {rd[u].x, rd[u].y, rd[u].z, rd[u].w},
+                     wv[4] = {rv[u].x, rv[u].y, rv[u].z, rv[u].w}, wq[4] = {rq[u].x, rq[u].y, rq[u].z, rq[u].w},
+                     wk[4] = {rk[u].x, rk[u].y, rk[u].z, rk[u].w};
+      float s = 0.f;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        s = __builtin_fmaf(o[e], d[e], s);
-        mx[0] = fmaxf(mx[0], fabsf(d[e]));
+      for (int e = 0; e < 4; ++e) {
+        s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, wo[e]), __builtin_bit_cast(bf16x2_t, wd[e]),
+                                            s, false);
+        am[0] = absmax_pair(am[0], wd[e]);
+        am[1] = absmax_pair(am[1], wv[e]);
+        am[2] = absmax_pair(am[2], wq[e]);
+        am[3] = absmax_pair(am[3], wk[e]);
       }
-      unpack8(rv[u], x);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) mx[1] = fmaxf(mx[1], fabsf(x[e]));
-      unpack8(rq[u], x);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) mx[2] = fmaxf(mx[2], fabsf(x[e]));
-      unpack8(rk[u], x);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) mx[3] = fmaxf(mx[3], fabsf(x[e]));
-      // Delta of the token: the four 8-channel parts sit in four consecutive lanes
+      // Delta of the token and head: its four 8-channel parts sit in four consecutive lanes
       s += __shfl_xor(s, 1, 64);
       s += __shfl_xor(s, 2, 64);
-      if (it < items && (it & 3) == 0) delta[tok[u] * g.heads + w.h] = s;
+      if (ok[u] && (p & 3) == 0) delta[tok[u] * (Off)g.heads + (Off)(h0 + (p >> 2))] = s;
     }
   }
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    mx[i] = wave_max(mx[i]);
-    if ((tid & 63) == 0) red[i][tid >> 6] = mx[i];
-  }
+  for (int i = 0; i < 4; ++i) red[i][tid] = absmax_value(am[i]);
   __syncthreads();
-  if (tid < 4) {
+  if (tid < P) {  // one thread per (head, quantity): the maximum over its head's parts and tokens
+    const int i = tid & 3, hh = tid >> 2;
     float m = 0.f;
+    for (int t = 0; t < T; ++t)
 #pragma unroll
-    for (int j = 0; j < kPreThreads / 64; ++j) m = fmaxf(m, red[tid][j]);
-    scal[wh * 4 + tid] = m;
+      for (int j = 0; j < 4; ++j) m = fmaxf(m, red[i][t * P + hh * 4 + j]);
+    scal[((win * g.heads) + h0 + hh) * 4 + i] = m;
   }
 }
 
@@ -765,10 +804,17 @@ int64_t bwd_mfma_partials(const Geom& g) {
 
 hipError_t launch_bwd_mfma(const BwdArgs& a, hipStream_t st) {
   const Geom& g = a.g;
-  const int64_t nwh = g.B * g.nH * g.nW * g.heads;
-  hipLaunchKernelGGL(bwd_pre_kernel, dim3((unsigned)nwh), dim3(kPreThreads), 0, st, (const uint16_t*)a.out,
-                     (const uint16_t*)a.dout, (const uint16_t*)a.v, (const uint16_t*)a.q, (const uint16_t*)a.k,
-                     a.delta, a.scal, g);
+  const int64_t pre_blocks = g.B * g.nH * g.nW * ((g.heads + kPreHeads - 1) / kPreHeads);
+  // every byte offset the pre-kernel forms is below 2 * tokens * max(xs, os)
+  const bool off32 = (double)g.B * g.Hg * g.Wg * 2.0 * (double)std::max(g.xs, g.os) < 4294967296.0;
+  if (off32)
+    hipLaunchKernelGGL(bwd_pre_kernel<uint32_t>, dim3((unsigned)pre_blocks), dim3(kPreThreads), 0, st,
+                       (const uint16_t*)a.out, (const uint16_t*)a.dout, (const uint16_t*)a.v, (const uint16_t*)a.q,
+                       (const uint16_t*)a.k, a.delta, a.scal, g);
+  else
+    hipLaunchKernelGGL(bwd_pre_kernel<int64_t>, dim3((unsigned)pre_blocks), dim3(kPreThreads), 0, st,
+                       (const uint16_t*)a.out, (const uint16_t*)a.dout, (const uint16_t*)a.v, (const uint16_t*)a.q,
+                       (const uint16_t*)a.k, a.delta, a.scal, g);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (g.M == 32) return launch_main<8, 32, 2>(a, st);

@@ -173,6 +173,13 @@ __device__ __forceinline__ void rotate8(float (&x)[8], const float* sn, const fl
   }
 }
 
+// 16-byte load marked non-temporal, for data that is read once and need not stay in the caches.
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 load_stream(const void* p) {
+  const u32x4_t t = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  return make_uint4(t.x, t.y, t.z, t.w);
+}
+
 __device__ __forceinline__ void unpack8(uint4 t, float (&x)[8]) {
   const uint32_t w[4] = {t.x, t.y, t.z, t.w};
 #pragma unroll

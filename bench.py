@@ -133,28 +133,53 @@ def m8_forward_roofline(dev, steps, warmup):
             "algorithmic_bytes": nbytes, "launch_ms": round(ms, 4)}
 
 
-def m16_step(dev, steps, warmup):
-    """Forward and backward at M = 16 (the pages' comparison-table window) on the stage-1 grid:
-    TFLOP/s under the dense 4 N^2 d / 10 N^2 d conventions."""
+def live_fraction(Hg, Wg, M, shift):
+    """Fraction of a window's (query, key) pairs that share a Swin region label, averaged over the
+    windows of the grid.  Labels combine a row region and a column region, so a window's fraction is
+    the product of its row-axis and column-axis fractions, and the grid average factors the same way."""
+    def axis(size):
+        fr = []
+        for wi in range(size // M):
+            counts = {}
+            for r in range(M):
+                Y = wi * M + r  # shifted-frame coordinate
+                lab = int(Y >= size - M) + int(Y >= size - shift) if shift else 0
+                counts[lab] = counts.get(lab, 0) + 1
+            fr.append(sum(c * c for c in counts.values()) / (M * M))
+        return sum(fr) / len(fr)
+    return axis(Hg) * axis(Wg)
+
+
+def config_timing(dev, name, shift, passes, steps, warmup):
+    """Time the forward and/or backward call of a named workload at one shift.  TFLOP/s under the dense
+    4 N^2 d (forward) / 10 N^2 d (backward) conventions, and with a shift also over live (same-region)
+    pairs only; the dense figure's fraction of the bf16 MFMA peak."""
     import torch
     import vision_transformer_windowed_amd as F
     from vision_transformer_windowed_amd.inputs import WORKLOADS, workload_inputs
-    name = "flashswin_t_s1_p2_m16"
     w = WORKLOADS[name]
     M = w["M"]
-    x = {k: v.to(dev) for k, v in workload_inputs(name, with_dout=True).items()}
-    q, k, v, dout, tr, tc = x["q"], x["k"], x["v"], x["dout"], x["theta_row"], x["theta_col"]
+    x = {k: v.to(dev) for k, v in workload_inputs(name, with_dout="bwd" in passes).items()}
+    q, k, v, tr, tc = x["q"], x["k"], x["v"], x["theta_row"], x["theta_col"]
     out = torch.empty_like(q)
     lse = torch.empty(q.shape[:4], device=dev, dtype=torch.float32)
-    grads = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v), torch.empty_like(tr),
-             torch.empty_like(tc))
-    ws = torch.empty(max(F.bwd_workspace_bytes(q, M, 0), 1), device=dev, dtype=torch.uint8)
+    fns = {"fwd": lambda: F.wattn_fwd(q, k, v, tr, tc, M, shift, out=out, lse=lse)}
+    if "bwd" in passes:
+        dout = x["dout"]
+        grads = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v), torch.empty_like(tr),
+                 torch.empty_like(tc))
+        ws = torch.empty(max(F.bwd_workspace_bytes(q, M, shift), 1), device=dev, dtype=torch.uint8)
+        fns["bwd"] = lambda: F.wattn_bwd(q, k, v, out, dout, lse, tr, tc, M, shift, workspace=ws, grads=grads)
+        fns["fwd"]()  # out and lse for the backward
     stream = torch.cuda.current_stream(dev)
     N = M * M
     nwh = w["B"] * (w["Hg"] // M) * (w["Wg"] // M) * w["heads"]
-    res = {"workload": name, "shift": 0}
-    for tag, fn in (("fwd", lambda: F.wattn_fwd(q, k, v, tr, tc, M, 0, out=out, lse=lse)),
-                    ("bwd", lambda: F.wattn_bwd(q, k, v, out, dout, lse, tr, tc, M, 0, workspace=ws, grads=grads))):
+    live = live_fraction(w["Hg"], w["Wg"], M, shift)
+    res = {"workload": name, "shift": shift}
+    if shift:
+        res["live_pair_fraction"] = round(live, 6)
+    for tag in passes:
+        fn = fns[tag]
         for _ in range(warmup):
             fn()
         torch.cuda.synchronize()
@@ -165,10 +190,18 @@ def m16_step(dev, steps, warmup):
         e1.record(stream)
         torch.cuda.synchronize()
         ms = e0.elapsed_time(e1) / steps
-        flops = (4.0 if tag == "fwd" else 10.0) * N * N * w["d"] * nwh
+        tf = (4.0 if tag == "fwd" else 10.0) * N * N * w["d"] * nwh / (ms * 1e-3) / 1e12
         res[tag + "_ms"] = round(ms, 4)
-        res[tag + "_tflops"] = round(flops / (ms * 1e-3) / 1e12, 2)
+        res[tag + "_tflops"] = round(tf, 2)
+        res[tag + "_mfma_frac"] = round(tf / BF16_MFMA_PEAK_TFLOPS, 4)
+        if shift:
+            res[tag + "_tflops_live"] = round(tf * live, 2)
     return res
+
+
+def m16_step(dev, steps, warmup):
+    """Forward and backward at M = 16 (the pages' comparison-table window) on the stage-1 grid."""
+    return config_timing(dev, "flashswin_t_s1_p2_m16", 0, ("fwd", "bwd"), steps, warmup)
 
 
 def packed_forward(dev, steps, warmup):
@@ -320,11 +353,15 @@ def main():
         fwd_roofline = {"kernel": "wattn_fwd", "bound": "mfma", "achieved": round(fwd_tf, 2),
                         "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(fwd_tf / BF16_MFMA_PEAK_TFLOPS, 4),
                         "launch_ms": round(fwd_ms, 4)}
-    m8 = packed = m16 = None
+    m8 = packed = m16 = masked = bwd32 = None
     if not args.no_secondary and args.only == "step":
         m8 = m8_forward_roofline(dev, max(args.steps, 10), max(args.warmup, 2))
         packed = packed_forward(dev, max(args.steps, 10), max(args.warmup, 2))
         m16 = m16_step(dev, max(args.steps, 10), max(args.warmup, 2))
+        masked = config_timing(dev, "flashswin_t_s2_shift16_m32", 16, ("fwd",), max(args.steps, 10),
+                               max(args.warmup, 2))
+        bwd32 = [config_timing(dev, "flashswin_t_s1_p2_m32_bwd", s, ("bwd",), max(args.steps, 10),
+                               max(args.warmup, 2)) for s in WORKLOADS["flashswin_t_s1_p2_m32_bwd"]["shifts"]]
 
     gpu_out = {"out": out, "lse": lse, "dq": grads[0], "dk": grads[1], "dv": grads[2]}
     cpu, parity = (None, None)
@@ -357,6 +394,8 @@ def main():
         "m8_fwd_roofline": m8,
         "m8_fwd_packed_qkv": packed,
         "m16_step": m16,
+        "m32_shift16_fwd": masked,
+        "m32_bwd_b32": bwd32,
         "cpu_baseline": cpu,
         "parity_sample": parity,
         "input_gen_s": round(gen_s, 1),

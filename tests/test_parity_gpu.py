@@ -87,6 +87,7 @@ FWD_SMALL = [
     (1, 14, 14, 2, 64, 7, 3, "bf16"),
     (1, 16, 16, 2, 16, 8, 4, "bf16"),
     (1, 32, 48, 2, 32, 16, 8, "bf16"),
+    (1, 64, 96, 2, 32, 32, 16, "bf16"),
 ]
 
 
@@ -213,9 +214,12 @@ BWD_SMALL = [
     (1, 64, 64, 3, 32, 32, 0, "bf16"),
     (1, 64, 64, 3, 32, 32, 16, "bf16"),
     (1, 24, 24, 2, 32, 12, 5, "bf16"),
+    (1, 40, 40, 2, 32, 20, 7, "bf16"),
+    (1, 33, 33, 1, 32, 11, 4, "bf16"),
     (1, 10, 10, 2, 32, 5, 2, "bf16"),
     (1, 16, 16, 2, 16, 8, 4, "bf16"),
     (1, 32, 48, 2, 32, 16, 8, "bf16"),
+    (1, 64, 96, 2, 32, 32, 16, "bf16"),
 ]
 
 

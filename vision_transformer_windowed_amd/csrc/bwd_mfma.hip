@@ -288,6 +288,7 @@ __device__ inline void dq_body(const uint16_t* __restrict__ q, const uint16_t* _
   constexpr int IPT = (kCh * 4 + NT - 1) / NT;
   const int M = MT > 0 ? MT : g.M;
   const int N = M * M;
+  const WinOrder wo = win_order(g, M, w.wy, w.wx);
   const int CH = chunk_len(NP);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int h = lane >> 5, col = lane & 31;
@@ -303,7 +304,8 @@ __device__ inline void dq_body(const uint16_t* __restrict__ q, const uint16_t* _
       ik[i] = make_uint4(0, 0, 0, 0);
       iv[i] = ik[i];
       if (it < CH * 4 && kn < N) {
-        const int r_ = kn / M, c_ = kn - (kn / M) * M;
+        int r_, c_;
+        slot_rc(wo, kn, r_, c_);
         const int64_t off = token_index(g, w.b, w.wy, w.wx, r_, c_) * xs + w.h * D + (it & 3) * 8;
         ik[i] = *reinterpret_cast<const uint4*>(k + off);
         iv[i] = *reinterpret_cast<const uint4*>(v + off);
@@ -322,7 +324,8 @@ __device__ inline void dq_body(const uint16_t* __restrict__ q, const uint16_t* _
   for (int t = 0; t < S; ++t) {
     const int qi = qbase + 32 * t;
     const bool valid = qi < N;
-    const int r = valid ? qi / M : 0, c = valid ? qi - (qi / M) * M : 0;
+    int r = 0, c = 0;
+    if (valid) slot_rc(wo, qi, r, c);
     qlab[t] = valid ? token_label(g, w.wy, w.wx, r, c) : 0xff;
     wl |= valid ? (1u << qlab[t]) : 0u;
     qb0[t] = qb1[t] = gb0[t] = gb1[t] = make_uint4(0, 0, 0, 0);
@@ -363,10 +366,14 @@ __device__ inline void dq_body(const uint16_t* __restrict__ q, const uint16_t* _
       if (it < CH * 4) {
         const int n = it >> 2, part = it & 3, kn = c0 + n;
         uint4 kr = make_uint4(0, 0, 0, 0);
-        if (kn < N) kr = rotated_part<H16>(ik[i], sm.sn, sm.cs, M, kn / M, kn - (kn / M) * M, part, 1.f);
+        if (kn < N) {
+          int r_, c_;
+          slot_rc(wo, kn, r_, c_);
+          kr = rotated_part<H16>(ik[i], sm.sn, sm.cs, M, r_, c_, part, 1.f);
+        }
         *reinterpret_cast<uint4*>(sm.K + srow(n, part)) = kr;
         *reinterpret_cast<uint4*>(sm.V + srow(n, part)) = iv[i];
-        if (part == 0) sm.lab[n] = chunk_label(g, w, M, kn, sm.blk + buf * (kCh / 32), n);
+        if (part == 0) sm.lab[n] = chunk_label(g, w, wo, kn, sm.blk + buf * (kCh / 32), n);
       }
     }
     if (tid < kCh / 32) sm.blk[(buf ^ 1) * (kCh / 32) + tid] = 0;
@@ -440,7 +447,8 @@ __device__ inline void dq_body(const uint16_t* __restrict__ q, const uint16_t* _
   for (int t = 0; t < S; ++t) {
     const int qi = qbase + 32 * t;
     if (qi < N) {
-      const int r = qi / M, c = qi - (qi / M) * M;
+      int r, c;
+      slot_rc(wo, qi, r, c);
       const int64_t off = token_index(g, w.b, w.wy, w.wx, r, c) * xs + w.h * D;
       // dq~ = acc / tau / sqrt(d); the dtheta integrand takes q~ as the dK product saw it
       unrotate_store(acc[t], 0.17677669529663687f / ds_scale, kQScale, H16, q + off, dq + off, sm.sn, sm.cs, M, r, c,
@@ -515,6 +523,7 @@ __device__ inline void dkdv_body(const uint16_t* __restrict__ q, const uint16_t*
   constexpr int IPT = (kCh * 4 + NT - 1) / NT;
   const int M = MT > 0 ? MT : g.M;
   const int N = M * M;
+  const WinOrder wo = win_order(g, M, w.wy, w.wx);
   const int CH = chunk_len(NP);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int h = lane >> 5, col = lane & 31;
@@ -534,7 +543,8 @@ __device__ inline void dkdv_body(const uint16_t* __restrict__ q, const uint16_t*
       il[i] = 0.f;
       id[i] = 0.f;
       if (it < CH * 4 && qn < N) {
-        const int r_ = qn / M, c_ = qn - (qn / M) * M;
+        int r_, c_;
+        slot_rc(wo, qn, r_, c_);
         const int64_t t_ = token_index(g, w.b, w.wy, w.wx, r_, c_);
         const int64_t off = t_ * xs + w.h * D + (it & 3) * 8;
         iq[i] = *reinterpret_cast<const uint4*>(q + off);
@@ -558,7 +568,8 @@ __device__ inline void dkdv_body(const uint16_t* __restrict__ q, const uint16_t*
   for (int t = 0; t < S; ++t) {
     const int kj = kbase + 32 * t;
     const bool valid = kj < N;
-    const int r = valid ? kj / M : 0, c = valid ? kj - (kj / M) * M : 0;
+    int r = 0, c = 0;
+    if (valid) slot_rc(wo, kj, r, c);
     klab[t] = valid ? token_label(g, w.wy, w.wx, r, c) : 0xff;
     wl |= valid ? (1u << klab[t]) : 0u;
     kb0[t] = kb1[t] = vb0[t] = vb1[t] = make_uint4(0, 0, 0, 0);
@@ -591,14 +602,18 @@ __device__ inline void dkdv_body(const uint16_t* __restrict__ q, const uint16_t*
       if (it < CH * 4) {
         const int n = it >> 2, part = it & 3, qn = c0 + n;
         uint4 qr = make_uint4(0, 0, 0, 0);
-        if (qn < N) qr = rotated_part<H16>(iq[i], sm.sn, sm.cs, M, qn / M, qn - (qn / M) * M, part, kQScale);
+        if (qn < N) {
+          int r_, c_;
+          slot_rc(wo, qn, r_, c_);
+          qr = rotated_part<H16>(iq[i], sm.sn, sm.cs, M, r_, c_, part, kQScale);
+        }
         *reinterpret_cast<uint4*>(sm.Q + srow(n, part)) = qr;
         *reinterpret_cast<uint4*>(sm.G + srow(n, part)) = ig[i];
         *reinterpret_cast<uint4*>(sm.Gs + srow(n, part)) = scaled_part<H16>(ig[i], g_scale);
         if (part == 0) {
           sm.L[n] = -il[i] * kLog2e;
           sm.Dl[n] = -id[i] * ds_scale;
-          sm.lab[n] = chunk_label(g, w, M, qn, sm.blk + buf * (kCh / 32), n);
+          sm.lab[n] = chunk_label(g, w, wo, qn, sm.blk + buf * (kCh / 32), n);
         }
       }
     }
@@ -706,7 +721,8 @@ __device__ inline void dkdv_body(const uint16_t* __restrict__ q, const uint16_t*
   for (int t = 0; t < S; ++t) {
     const int kj = kbase + 32 * t;
     if (kj < N) {
-      const int r = kj / M, c = kj - (kj / M) * M;
+      int r, c;
+      slot_rc(wo, kj, r, c);
       const int64_t off = token_index(g, w.b, w.wy, w.wx, r, c) * xs + w.h * D;
       // dV = accv / g: lane holds channels 8g + 4h + j of its key
 #pragma unroll

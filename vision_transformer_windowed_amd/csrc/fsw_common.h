@@ -51,6 +51,55 @@ __device__ __forceinline__ int token_label(const Geom& g, int wy, int wx, int r,
   return 3 * region_of(wy * g.M + r, g.Hg, g.M, g.shift) + region_of(wx * g.M + c, g.Wg, g.M, g.shift);
 }
 
+// Order in which the kernels enumerate a window's tokens ("slots"): grouped by Swin region, so that
+// runs of consecutive slots share one label and whole 32-slot blocks are either attended without a
+// mask or skipped.  In the shifted frame a window's rows fall into at most two bands, [0, ra) and
+// [ra, M): ra = M - shift in the last window row of a shifted grid, ra = M (one band) elsewhere.  The
+// columns likewise with ca.  Slots enumerate band (rows 0, cols 0) row-major, then (0, 1), (1, 0),
+// (1, 1); a window without a split is plain row-major, slot = r * M + c.  Softmax attention does not
+// depend on the order of the keys, and each query keeps its own (r, c), so results are unchanged.
+struct WinOrder {
+  int M, ra, ca;
+};
+__device__ __forceinline__ WinOrder win_order(const Geom& g, int M, int wy, int wx) {
+  WinOrder o;
+  o.M = M;
+  o.ra = (g.shift > 0 && wy == g.nH - 1) ? M - g.shift : M;
+  o.ca = (g.shift > 0 && wx == g.nW - 1) ? M - g.shift : M;
+  return o;
+}
+// In-window position (r, c) of slot j < M * M.
+__device__ __forceinline__ void slot_rc(const WinOrder& o, int j, int& r, int& c) {
+  const int M = o.M;
+  if (o.ra == M && o.ca == M) {  // uniform across the workgroup: one window
+    r = j / M;
+    c = j - r * M;
+    return;
+  }
+  const int n00 = o.ra * o.ca, n01 = o.ra * (M - o.ca), n10 = (M - o.ra) * o.ca;
+  int r0 = 0, c0 = 0, w = o.ca;
+  if (j >= n00) {
+    j -= n00;
+    if (j < n01) {
+      c0 = o.ca;
+      w = M - o.ca;
+    } else {
+      j -= n01;
+      r0 = o.ra;
+      if (j >= n10) {
+        j -= n10;
+        c0 = o.ca;
+        w = M - o.ca;
+      }
+    }
+  }
+  // j / w by a float reciprocal: with j < 4096 and w <= 64 (M <= 64) the quotient (j + 1/2) / w lies at
+  // least 1/(2w) >= 2^-7 from an integer, far beyond the float error of the product (< 2^-10)
+  const int qt = (int)(((float)j + 0.5f) * __builtin_amdgcn_rcpf((float)w));
+  r = r0 + qt;
+  c = c0 + j - qt * w;
+}
+
 // Token index (b, y, x) in the grid of in-window position (r, c) of window (wy, wx) of image b.
 __device__ __forceinline__ int64_t token_index(const Geom& g, int64_t b, int wy, int wx, int r, int c) {
   const int y = grid_coord(wy * g.M + r, g.shift, g.Hg);

@@ -59,13 +59,17 @@ __device__ __forceinline__ uint4 scaled_part(uint4 raw, float scale) {
   return pack8_op(x, H16);
 }
 
-// Label of chunk token n (0xff past the window) and its block summary bit (bit L for label L,
-// bit 10 for a position past the window) OR-ed into blk[n / 32].
-__device__ __forceinline__ uint8_t chunk_label(const Geom& g, const WinHead& w, int M, int tn, uint32_t* blk,
-                                               int n) {
-  const int N = M * M;
+// Label of chunk slot tn, staged at chunk position n (0xff past the window), and its block summary
+// bit (bit L for label L, bit 10 for a position past the window) OR-ed into blk[n / 32].
+__device__ __forceinline__ uint8_t chunk_label(const Geom& g, const WinHead& w, const WinOrder& wo, int tn,
+                                               uint32_t* blk, int n) {
+  const int N = wo.M * wo.M;
   uint8_t lb = 0xff;
-  if (tn < N) lb = (uint8_t)token_label(g, w.wy, w.wx, tn / M, tn - (tn / M) * M);
+  if (tn < N) {
+    int r, c;
+    slot_rc(wo, tn, r, c);
+    lb = (uint8_t)token_label(g, w.wy, w.wx, r, c);
+  }
   atomicOr(&blk[n >> 5], lb == 0xff ? (1u << 10) : (1u << lb));
   return lb;
 }

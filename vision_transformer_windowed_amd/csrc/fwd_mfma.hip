@@ -48,6 +48,7 @@ struct FwdSmem {
   uint16_t* V;     // [NP][32] row-major; P.V operands come from transposing LDS reads
   float* sn;       // [2][M][8]  sin of RoPE angle (row axis, column axis)
   float* cs;       // [2][M][8]  cos
+  uint16_t* rc;    // [NP]  r << 8 | c of every slot (see WinOrder); read in windows split by a shift
   uint8_t* lab;    // [NP]  key labels, 0xff past the window
   uint32_t* blk;   // [NP/32]  bits 0..8: labels present, bit 9: all 32 keys valid
   float* red;      // [2 * kMaxWaves]: per-wave max |k~|^2, then max |q^|^2
@@ -56,7 +57,7 @@ struct FwdSmem {
 __host__ __device__ inline size_t fwd_smem_bytes(int NP, int M) {
   size_t b = (size_t)NP * kKStride * 2 + (size_t)NP * 32 * 2;
   b += (size_t)2 * 2 * M * 8 * 4;
-  b += (size_t)NP;
+  b += (size_t)NP * 2 + (size_t)NP;
   b = (b + 3) & ~(size_t)3;
   b += (size_t)(NP / 32) * 4 + 2 * kMaxWaves * 4;
   return b;
@@ -68,11 +69,31 @@ __device__ inline FwdSmem carve(unsigned char* base, int NP, int M) {
   s.V = s.K + (size_t)NP * kKStride;
   s.sn = reinterpret_cast<float*>(s.V + (size_t)NP * 32);
   s.cs = s.sn + 2 * M * 8;
-  s.lab = reinterpret_cast<uint8_t*>(s.cs + 2 * M * 8);
+  s.rc = reinterpret_cast<uint16_t*>(s.cs + 2 * M * 8);
+  s.lab = reinterpret_cast<uint8_t*>(s.rc + NP);
   size_t off = ((size_t)(s.lab + NP - base) + 3) & ~(size_t)3;
   s.blk = reinterpret_cast<uint32_t*>(base + off);
   s.red = reinterpret_cast<float*>(s.blk + NP / 32);
   return s;
+}
+
+// Slot range [bs, be) of the region band that holds slot j (see WinOrder).
+__device__ __forceinline__ void band_of(const WinOrder& o, int j, int& bs, int& be) {
+  const int M = o.M;
+  const int e0 = o.ra * o.ca, e1 = e0 + o.ra * (M - o.ca), e2 = e1 + (M - o.ra) * o.ca;
+  if (j < e0) {
+    bs = 0;
+    be = e0;
+  } else if (j < e1) {
+    bs = e0;
+    be = e1;
+  } else if (j < e2) {
+    bs = e1;
+    be = e2;
+  } else {
+    bs = e2;
+    be = M * M;
+  }
 }
 
 // Grid token of in-window position (r, c) with the window size M passed explicitly (a constant in
@@ -119,19 +140,19 @@ __device__ __forceinline__ void block_consume(const FwdSmem& sm, int b, int lane
   o = mfma32x32x16(va1, as_bf16x8(make_uint4(pk[4], pk[5], pk[6], pk[7])), o);
 }
 
-// Main pass for a window with one region and an even number of whole blocks: no masks, no skips,
-// pipelined with two score buffers.
+// Pipelined pass over an even number of key blocks kb0 .. kb1-1, all whole and of the wave's one
+// label: no masks, no skips, two score buffers.
 template <bool H16>
-__device__ __forceinline__ void pass_uniform(const FwdSmem& sm, int NB, int lane, uint4 qb0, uint4 qb1,
+__device__ __forceinline__ void pass_uniform(const FwdSmem& sm, int kb0, int kb1, int lane, uint4 qb0, uint4 qb1,
                                              const f32x16_t& cinit, float& l, f32x16_t& o) {
   const int h = lane >> 5, row = lane & 31;
   float la = 0.f, lb = 0.f;
-  // the prefetch after the last pair recomputes block NB-1 and is not used
-  f32x16_t sa = block_scores<H16>(sm, 0, row, h, qb0, qb1, cinit);
-  for (int kb = 0; kb < NB; kb += 2) {
+  // the prefetch after the last pair recomputes block kb1-1 and is not used
+  f32x16_t sa = block_scores<H16>(sm, kb0, row, h, qb0, qb1, cinit);
+  for (int kb = kb0; kb < kb1; kb += 2) {
     const f32x16_t sb = block_scores<H16>(sm, kb + 1, row, h, qb0, qb1, cinit);
     block_consume<false, false>(sm, kb, lane, 0xffffu, 0.f, sa, la, lb, o);
-    sa = block_scores<H16>(sm, min(kb + 2, NB - 1), row, h, qb0, qb1, cinit);
+    sa = block_scores<H16>(sm, min(kb + 2, kb1 - 1), row, h, qb0, qb1, cinit);
     block_consume<false, false>(sm, kb + 1, lane, 0xffffu, 0.f, sb, la, lb, o);
   }
   l = la + lb;
@@ -168,18 +189,20 @@ __device__ __forceinline__ void pass_general(const FwdSmem& sm, int NB, int lane
   l = la + lb;
 }
 
-// The attention of the wave's tile: uniform fast path or the general pass, then the exact-maximum
-// fallback when the bound reference was too loose for some query.
+// The attention of the wave's tile: the pipelined pass when its live keys are one even run of
+// whole blocks kb0 .. kb1-1 of its own label (run), else the general pass; then the exact-maximum fallback
+// when the bound reference was too loose for some query.
 template <bool H16>
-__device__ __forceinline__ void attend(const FwdSmem& sm, int NB, int lane, bool uniform_win, uint32_t wave_labels,
+__device__ __forceinline__ void attend(const FwdSmem& sm, int NB, int lane, bool run, int kb0, int kb1,
+                                       uint32_t wave_labels,
                                        bool wave_single, uint4 qb0, uint4 qb1, int qlab, bool qvalid, float bound,
                                        float& ref, float& l, f32x16_t& o) {
   f32x16_t cinit;
 #pragma unroll
   for (int v2 = 0; v2 < 16; ++v2) cinit[v2] = -bound;
   float m = 0.f;
-  if (uniform_win)
-    pass_uniform<H16>(sm, NB, lane, qb0, qb1, cinit, l, o);
+  if (run)
+    pass_uniform<H16>(sm, kb0, kb1, lane, qb0, qb1, cinit, l, o);
   else if (wave_labels != 0)
     pass_general<0, H16>(sm, NB, lane, wave_labels, wave_single, qb0, qb1, qlab, cinit, m, l, o);
   ref = bound;
@@ -203,8 +226,8 @@ __device__ __forceinline__ void attend(const FwdSmem& sm, int NB, int lane, bool
 // Rotated K~ rows of the staged items (raw bf16 loads in kraw) into LDS in fp16 (h16) or bf16;
 // returns this thread's max |k|^2 (rotation keeps norms).
 template <int MAXIT>
-__device__ __forceinline__ float stage_k(const FwdSmem& sm, const uint4 (&kraw)[MAXIT], int M, int NP, int tid,
-                                         int nt, bool h16) {
+__device__ __forceinline__ float stage_k(const FwdSmem& sm, const uint4 (&kraw)[MAXIT], int M, bool split, int NP,
+                                         int tid, int nt, bool h16) {
   const int N = M * M;
   float kmax2 = 0.f;
 #pragma unroll
@@ -216,7 +239,8 @@ __device__ __forceinline__ float stage_k(const FwdSmem& sm, const uint4 (&kraw)[
     uint4 kr = make_uint4(0, 0, 0, 0);
     float ss = 0.f;
     if (key < N) {
-      const int r = key / M, c = key - (key / M) * M;
+      const int rc = split ? (int)sm.rc[key] : (key / M) << 8 | (key - (key / M) * M);
+      const int r = rc >> 8, c = rc & 255;
       float x[8];
       unpack8(kraw[i], x);
 #pragma unroll
@@ -236,8 +260,8 @@ __device__ __forceinline__ float stage_k(const FwdSmem& sm, const uint4 (&kraw)[
 // Global loads of the thread's K and V items (16 bytes each), issued together.
 template <int MAXIT>
 __device__ __forceinline__ void load_kv(const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, const Geom& g,
-                                        const WinHead& w, int M, int NP, int tid, int nt, bool with_v,
-                                        uint4 (&kraw)[MAXIT], uint4 (&vraw)[MAXIT]) {
+                                        const WinHead& w, const uint16_t* rc, int M, int NP, int tid, int nt,
+                                        bool with_v, uint4 (&kraw)[MAXIT], uint4 (&vraw)[MAXIT]) {
   const int N = M * M;
 #pragma unroll
   for (int i = 0; i < MAXIT; ++i) {
@@ -245,7 +269,15 @@ __device__ __forceinline__ void load_kv(const uint16_t* __restrict__ k, const ui
     const int key = it >> 2;
     kraw[i] = vraw[i] = make_uint4(0, 0, 0, 0);
     if (it < NP * 4 && key < N) {
-      const int r = key / M, c = key - (key / M) * M;
+      int r, c;
+      if (rc) {
+        const int rk = rc[key];
+        r = rk >> 8;
+        c = rk & 255;
+      } else {  // row-major slots
+        r = key / M;
+        c = key - (key / M) * M;
+      }
       const int64_t off = tok_of(g, w, M, r, c) * g.xs + w.h * 32 + (it & 3) * 8;
       kraw[i] = *reinterpret_cast<const uint4*>(k + off);
       if (with_v) vraw[i] = *reinterpret_cast<const uint4*>(v + off);
@@ -257,7 +289,7 @@ __device__ __forceinline__ void load_kv(const uint16_t* __restrict__ k, const ui
 // once and then walks its query blocks of NWAVES*32 queries.  MT: compile-time window size
 // (0 = g.M at run time).  NPMAX: the largest padded window this configuration serves.
 template <int NWAVES, int MT, int NPMAX>
-__global__ __launch_bounds__(NWAVES * 64) void fwd_mfma_kernel(const uint16_t* __restrict__ q,
+__global__ __launch_bounds__(NWAVES * 64, NWAVES >= 8 ? 4 : 1) void fwd_mfma_kernel(const uint16_t* __restrict__ q,
                                                                const uint16_t* __restrict__ k,
                                                                const uint16_t* __restrict__ v,
                                                                const float* __restrict__ th_row,
@@ -295,21 +327,38 @@ __global__ __launch_bounds__(NWAVES * 64) void fwd_mfma_kernel(const uint16_t* _
     }
   }
   const WinHead w = decode_winhead(g, wh);
+  const WinOrder wo = win_order(g, M, w.wy, w.wx);
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int h = lane >> 5;
   const int col = lane & 31;
 
-  // 0. every global load of the thread first (K and V items, the queries of every block)
+  // 0. slot order: in-window position and label of every slot.  In a window split by the shift the
+  // loads below take their addresses from this table; otherwise slots are row-major.
+  const bool split = wo.ra != M || wo.ca != M;  // one window per workgroup: uniform
+  for (int n = tid; n < NP; n += NT) {
+    uint8_t lb = 0xff;
+    if (n < N) {
+      int r, c;
+      slot_rc(wo, n, r, c);
+      sm.rc[n] = (uint16_t)(r << 8 | c);
+      lb = (uint8_t)token_label(g, w.wy, w.wx, r, c);
+    }
+    sm.lab[n] = lb;
+  }
+  if (split) __syncthreads();
+
+  // 1. every global load of the thread (K and V items, the queries of every block)
   uint4 kraw[MAXIT], vraw[MAXIT];
-  load_kv<MAXIT>(k, v, g, w, M, NP, tid, NT, true, kraw, vraw);
+  load_kv<MAXIT>(k, v, g, w, split ? sm.rc : nullptr, M, NP, tid, NT, true, kraw, vraw);
   // the lane's query of block qb (two 16-byte halves: channels 8h.., 16+8h..)
   auto load_q = [&](int qb, uint4& a, uint4& b) {
     const int qi = (qoff + qb) * NT / 2 + wave * 32 + col;
     a = b = make_uint4(0, 0, 0, 0);
     if (qb < nqw && qi < N) {
-      const int64_t off = tok_of(g, w, M, qi / M, qi - (qi / M) * M) * g.xs + w.h * D;
+      const int rc = split ? (int)sm.rc[qi] : (qi / M) << 8 | (qi - (qi / M) * M);
+      const int64_t off = tok_of(g, w, M, rc >> 8, rc & 255) * g.xs + w.h * D;
       a = *reinterpret_cast<const uint4*>(q + off + 8 * h);
       b = *reinterpret_cast<const uint4*>(q + off + 16 + 8 * h);
     }
@@ -318,7 +367,7 @@ __global__ __launch_bounds__(NWAVES * 64) void fwd_mfma_kernel(const uint16_t* _
 #pragma unroll
   for (int qb = 0; qb < QBM; ++qb) load_q(qb, qraw[qb][0], qraw[qb][1]);
 
-  // 1. RoPE sin/cos table and key labels (while the loads are in flight)
+  // 2. RoPE sin/cos table (while the loads are in flight)
   for (int i = tid; i < 2 * M * 8; i += NT) {
     const int axis = i / (M * 8);
     const int p = (i / 8) % M;
@@ -329,15 +378,10 @@ __global__ __launch_bounds__(NWAVES * 64) void fwd_mfma_kernel(const uint16_t* _
     sm.sn[i] = s;
     sm.cs[i] = c;
   }
-  for (int n = tid; n < NP; n += NT) {
-    uint8_t lb = 0xff;
-    if (n < N) lb = (uint8_t)token_label(g, w.wy, w.wx, n / M, n % M);
-    sm.lab[n] = lb;
-  }
   __syncthreads();
 
-  // 2. K~ rows (rotated, fp16), V rows, block label summaries, norms
-  float kmax2 = stage_k<MAXIT>(sm, kraw, M, NP, tid, NT, true);
+  // 3. K~ rows (rotated, fp16), V rows, block label summaries, norms
+  float kmax2 = stage_k<MAXIT>(sm, kraw, M, split, NP, tid, NT, true);
 #pragma unroll
   for (int i = 0; i < MAXIT; ++i) {
     const int it = tid + i * NT;
@@ -385,31 +429,19 @@ __global__ __launch_bounds__(NWAVES * 64) void fwd_mfma_kernel(const uint16_t* _
   // fp16 score operands unless some |k~| or |q^| (hence some component) could leave fp16 range
   const bool h16 = kmax < kF16Limit && sqrtf(qmax2_all) < kF16Limit;
   if (!h16) {
-    load_kv<MAXIT>(k, v, g, w, M, NP, tid, NT, false, kraw, vraw);
+    load_kv<MAXIT>(k, v, g, w, split ? sm.rc : nullptr, M, NP, tid, NT, false, kraw, vraw);
     __syncthreads();
-    stage_k<MAXIT>(sm, kraw, M, NP, tid, NT, false);
+    stage_k<MAXIT>(sm, kraw, M, split, NP, tid, NT, false);
     __syncthreads();
   }
-  // window summary over its blocks: one label everywhere and every block whole
-  uint32_t wb = 0xffffffffu, wor = 0;
-  for (int b = lane; b < NB; b += 64) {
-    const uint32_t info = sm.blk[b];
-    wb &= info;
-    wor |= info & 0x1ffu;
-  }
-#pragma unroll
-  for (int o2 = 32; o2 > 0; o2 >>= 1) {
-    wb &= (uint32_t)__shfl_xor((int)wb, o2, 64);
-    wor |= (uint32_t)__shfl_xor((int)wor, o2, 64);
-  }
-
 #pragma unroll
   for (int qb = 0; qb < QBM; ++qb) {
     if (qb >= nqw) break;
-    // 3. the wave's query operands (rotated, scaled by log2(e)/sqrt(d)), reference bound, labels
+    // 4. the wave's query operands (rotated, scaled by log2(e)/sqrt(d)), reference bound, labels
     const int qi = (qoff + qb) * NT / 2 + wave * 32 + col;
     const bool qvalid = qi < N;
-    const int qr = qvalid ? qi / M : 0, qc = qvalid ? qi - (qi / M) * M : 0;
+    const int qrc = !qvalid ? 0 : split ? (int)sm.rc[qi] : (qi / M) << 8 | (qi - (qi / M) * M);
+    const int qr = qrc >> 8, qc = qrc & 255;
     uint4 qb0, qb1;
     {
       // block 0's query was loaded with K and V; later blocks reload theirs (an L2 hit) during
@@ -433,21 +465,31 @@ __global__ __launch_bounds__(NWAVES * 64) void fwd_mfma_kernel(const uint16_t* _
     const int qlab = qvalid ? token_label(g, w.wy, w.wx, qr, qc) : 0xff;
     const uint32_t wave_labels = uniform(wave_or(qvalid ? 1u << qlab : 0u));
     const bool wave_single = __builtin_popcount(wave_labels) == 1;
-    const bool uniform_win = uniform((int)(((wb >> 9) & 1u) && __builtin_popcount(wor) == 1 &&
-                                           wor == wave_labels && (NB % 2) == 0)) != 0;
+    // A single-label wave sees exactly the keys of its region band, one contiguous slot range [bs, be).
+    // When the band is whole 32-slot blocks, even in number, the wave takes the pipelined pass over
+    // them (every window without a shift, and the bands of the usual shifted shapes).
+    int kb0 = 0, kb1 = 0;
+    bool run = false;
+    if (wave_single) {
+      int bs, be;
+      band_of(wo, uniform((qoff + qb) * NT / 2 + wave * 32), bs, be);
+      run = ((bs | be) & 31) == 0 && (((be - bs) >> 5) & 1) == 0;
+      kb0 = bs >> 5;
+      kb1 = be >> 5;
+    }
 
     f32x16_t o;
     float l = 0.f, ref;
 #pragma unroll
     for (int v2 = 0; v2 < 16; ++v2) o[v2] = 0.f;
     if (h16)
-      attend<true>(sm, NB, lane, uniform_win, wave_labels, wave_single, qb0, qb1, qlab, qvalid, bound, ref, l, o);
+      attend<true>(sm, NB, lane, run, kb0, kb1, wave_labels, wave_single, qb0, qb1, qlab, qvalid, bound, ref, l, o);
     else
-      attend<false>(sm, NB, lane, uniform_win, wave_labels, wave_single, qb0, qb1, qlab, qvalid, bound, ref, l, o);
+      attend<false>(sm, NB, lane, run, kb0, kb1, wave_labels, wave_single, qb0, qb1, qlab, qvalid, bound, ref, l, o);
 
     // the next block's query loads go out before this block's epilogue
     if (qb + 1 < QBM) load_q(qb + 1, qraw[qb + 1][0], qraw[qb + 1][1]);  // zeros past the last block
-    // 4. epilogue: O = O^T / l (lane: query col, channels 8g + 4h + j), LSE = (ref + log2 l) ln 2
+    // 5. epilogue: O = O^T / l (lane: query col, channels 8g + 4h + j), LSE = (ref + log2 l) ln 2
     const float lt = l + __shfl_xor(l, 32, 64);
     if (qvalid) {
       const int64_t qtok = tok_of(g, w, M, qr, qc);

@@ -312,7 +312,18 @@ __device__ inline void dq_body(const uint16_t* __restrict__ q, const uint16_t* _
       }
     }
   };
-  load_chunk(0);
+  // In a window split by the shift, chunks holding none of the labels of this workgroup's queries
+  // are neither loaded, staged nor visited (each region band is one contiguous slot range).
+  const bool split = wo.ra != M || wo.ca != M;  // one window per workgroup: uniform
+  const int own0 = qblock * NW * 32 * S;
+  const uint32_t own = split ? range_labels(g, w, wo, own0, min(N, own0 + NW * 32 * S)) : 0u;
+  auto next_chunk = [&](int c) {
+    if (split)
+      while (c < NP && (range_labels(g, w, wo, c, c + CH) & own) == 0) c += CH;
+    return c;
+  };
+  int c0 = next_chunk(0);
+  if (c0 < NP) load_chunk(c0);
 
   // the lane's queries: Q^ operands, tau * dO as bf16 B operands, -LSE and -tau Delta
   const int qbase = (qblock * NW + wave) * 32 * S + col;
@@ -358,7 +369,8 @@ __device__ inline void dq_body(const uint16_t* __restrict__ q, const uint16_t* _
   const int ro0 = srow(col, h), ro1 = srow(col, 2 + h);
 
   int buf = 0;
-  for (int c0 = 0; c0 < NP; c0 += CH, buf ^= 1) {
+  for (int cn; c0 < NP; c0 = cn, buf ^= 1) {
+    cn = next_chunk(c0 + CH);
     __syncthreads();
 #pragma unroll
     for (int i = 0; i < IPT; ++i) {
@@ -378,7 +390,7 @@ __device__ inline void dq_body(const uint16_t* __restrict__ q, const uint16_t* _
     }
     if (tid < kCh / 32) sm.blk[(buf ^ 1) * (kCh / 32) + tid] = 0;
     __syncthreads();
-    if (c0 + CH < NP) load_chunk(c0 + CH);
+    if (cn < NP) load_chunk(cn);
     if (wave_labels == 0) continue;
     uint32_t info4[kCh / 32];
 #pragma unroll
@@ -556,7 +568,18 @@ __device__ inline void dkdv_body(const uint16_t* __restrict__ q, const uint16_t*
       }
     }
   };
-  load_chunk(0);
+  // In a window split by the shift, chunks holding none of the labels of this workgroup's keys are
+  // neither loaded, staged nor visited (each region band is one contiguous slot range).
+  const bool split = wo.ra != M || wo.ca != M;  // one window per workgroup: uniform
+  const int own0 = kblock * NW * 32 * S;
+  const uint32_t own = split ? range_labels(g, w, wo, own0, min(N, own0 + NW * 32 * S)) : 0u;
+  auto next_chunk = [&](int c) {
+    if (split)
+      while (c < NP && (range_labels(g, w, wo, c, c + CH) & own) == 0) c += CH;
+    return c;
+  };
+  int c0 = next_chunk(0);
+  if (c0 < NP) load_chunk(c0);
 
   // the lane's keys (one per set): K~ operands, tau * V as bf16 B operands
   const int kbase = (kblock * NW + wave) * 32 * S + col;
@@ -594,7 +617,8 @@ __device__ inline void dkdv_body(const uint16_t* __restrict__ q, const uint16_t*
   const int ro0 = srow(col, h), ro1 = srow(col, 2 + h);
 
   int buf = 0;
-  for (int c0 = 0; c0 < NP; c0 += CH, buf ^= 1) {
+  for (int cn; c0 < NP; c0 = cn, buf ^= 1) {
+    cn = next_chunk(c0 + CH);
     __syncthreads();
 #pragma unroll
     for (int i = 0; i < IPT; ++i) {
@@ -619,7 +643,7 @@ __device__ inline void dkdv_body(const uint16_t* __restrict__ q, const uint16_t*
     }
     if (tid < kCh / 32) sm.blk[(buf ^ 1) * (kCh / 32) + tid] = 0;
     __syncthreads();
-    if (c0 + CH < NP) load_chunk(c0 + CH);
+    if (cn < NP) load_chunk(cn);
     if (wave_labels == 0) continue;
     uint32_t info4[kCh / 32];
 #pragma unroll

@@ -59,6 +59,23 @@ __device__ __forceinline__ uint4 scaled_part(uint4 raw, float scale) {
   return pack8_op(x, H16);
 }
 
+// Labels (bit L for label L) of the tokens in slots [a, b) of a window, from its region bands: each
+// band is one contiguous slot range of one label (see WinOrder).
+__device__ inline uint32_t range_labels(const Geom& g, const WinHead& w, const WinOrder& o, int a, int b) {
+  const int M = o.M;
+  const int e[5] = {0, o.ra * o.ca, o.ra * M, o.ra * M + (M - o.ra) * o.ca, M * M};
+  uint32_t m = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if (e[i] < e[i + 1] && e[i] < b && a < e[i + 1]) {
+      int r, c;
+      slot_rc(o, e[i], r, c);
+      m |= 1u << token_label(g, w.wy, w.wx, r, c);
+    }
+  }
+  return m;
+}
+
 // Label of chunk slot tn, staged at chunk position n (0xff past the window), and its block summary
 // bit (bit L for label L, bit 10 for a position past the window) OR-ed into blk[n / 32].
 __device__ __forceinline__ uint8_t chunk_label(const Geom& g, const WinHead& w, const WinOrder& wo, int tn,

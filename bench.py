@@ -259,8 +259,8 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(the batch would shard across GPUs with one dtheta all-reduce; see DESIGN.md).",
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
+              "(the batch would shard across GPUs, with one all-reduce of dtheta in the backward).",
               file=sys.stderr)
         sys.exit(2)
 

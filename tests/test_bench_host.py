@@ -19,7 +19,7 @@ def test_live_fraction_matches_label_pairs(Hg, Wg, M, s):
     assert bench.live_fraction(Hg, Wg, M, s) == pytest.approx(float(live), rel=1e-12)
 
 
-def test_live_fraction_survey_values():
+def test_live_fraction_known_values():
     # one split axis of four windows at M = 32, s = 16: ((3 + 1/2) / 4)^2; two windows per axis: (3/4)^2
     assert bench.live_fraction(128, 128, 32, 16) == pytest.approx(0.765625)
     assert bench.live_fraction(64, 64, 32, 16) == pytest.approx(0.5625)

@@ -19,7 +19,7 @@ import torch
 
 import oracle
 import vision_transformer_windowed_amd as F
-from vision_transformer_windowed_amd.inputs import WORKLOADS, make_inputs, workload_inputs
+from vision_transformer_windowed_amd.inputs import WORKLOADS, make_device_inputs, make_inputs, workload_inputs
 
 pytestmark = pytest.mark.gpu
 
@@ -88,6 +88,7 @@ FWD_SMALL = [
     (1, 16, 16, 2, 16, 8, 4, "bf16"),
     (1, 32, 48, 2, 32, 16, 8, "bf16"),
     (1, 64, 96, 2, 32, 32, 16, "bf16"),
+    (1, 16, 16, 20, 32, 8, 3, "bf16"),
 ]
 
 
@@ -220,6 +221,7 @@ BWD_SMALL = [
     (1, 16, 16, 2, 16, 8, 4, "bf16"),
     (1, 32, 48, 2, 32, 16, 8, "bf16"),
     (1, 64, 96, 2, 32, 32, 16, "bf16"),
+    (1, 16, 16, 20, 32, 8, 3, "bf16"),
 ]
 
 
@@ -335,3 +337,25 @@ def test_empty_batch():
     xd = to_dev(x)
     out, lse = F.wattn_fwd(xd["q"], xd["k"], xd["v"], xd["theta_row"], xd["theta_col"], 8, 4)
     assert out.shape == (0, 16, 16, 2, 32) and lse.shape == (0, 16, 16, 2)
+
+
+def test_large_tensors_64bit_offsets():
+    """Tensors above 4 GiB, so byte offsets pass 2^32 in every kernel (and the backward prologue takes
+    its 64-bit addressing): [1400, 128, 128, 3, 32] bf16, M = 32, shift 16, inputs drawn on the GPU.
+    The first, middle and last images against the oracle (dtheta sums over all images: not checked)."""
+    B, Hg, Wg, H, D, M, s = 1400, 128, 128, 3, 32, 32, 16
+    assert B * Hg * Wg * H * D * 2 > 2 ** 32
+    x = make_device_inputs(B, Hg, Wg, H, D, "bf16", seed=1777, device=DEV, with_dout=True)
+    out, lse = F.wattn_fwd(x["q"], x["k"], x["v"], x["theta_row"], x["theta_col"], M, s)
+    dq, dk, dv, _, _ = F.wattn_bwd(x["q"], x["k"], x["v"], out, x["dout"], lse, x["theta_row"], x["theta_col"],
+                                   M, s)
+    torch.cuda.synchronize()
+    imgs = [0, B // 2, B - 1]
+    q, k, v, dout = (_np(x[n][imgs]) for n in ("q", "k", "v", "dout"))
+    tr, tc = _np(x["theta_row"]), _np(x["theta_col"])
+    ro, rl = oracle.wattn_fwd_ref(q, k, v, tr, tc, M, s)
+    assert_close("O", _np(out[imgs]), ro, 2e-2, 5e-3)
+    assert_close("LSE", _np(lse[imgs]), rl, 2e-2, 5e-3)
+    g = oracle.wattn_bwd_ref(q, k, v, dout, tr, tc, M, s)
+    for nm, got, ref in (("dQ", dq[imgs], g[0]), ("dK", dk[imgs], g[1]), ("dV", dv[imgs], g[2])):
+        assert_close(nm, _np(got), ref, 2e-2, 5e-3)

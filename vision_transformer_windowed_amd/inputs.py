@@ -9,6 +9,8 @@ whether dO is drawn.  bf16 workloads
 round Q, K, V, dO to bf16 (round-to-nearest-even).  The RoPE frequencies start
 from the geometric schedule 10000^(-2i/(d/2)), i < d/4, used as the
 initialisation in the FlashSwin paper card's Figure S4, plus that noise.
+`make_device_inputs` draws Q, K, V, dO the same way from a generator on the GPU
+itself, for tensors too large to draw on the host (theta as above).
 """
 
 import torch
@@ -47,6 +49,23 @@ def make_inputs(B, Hg, Wg, heads, d, dtype="bf16", seed=0, with_dout=False, thet
     for name in ("theta_row", "theta_col"):
         noise = torch.randn((heads, d // 4), generator=gt, dtype=torch.float32).double() * theta_noise
         out[name] = (base + noise).float()
+    return out
+
+
+def make_device_inputs(B, Hg, Wg, heads, d, dtype="bf16", seed=0, device="cuda", with_dout=False,
+                       theta_noise=0.01):
+    """make_inputs with Q, K, V (and dO) drawn on `device` by a generator there (a different stream of
+    numbers than the CPU draw); theta is drawn on the host exactly as in make_inputs."""
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed))
+    shape = (B, Hg, Wg, heads, d)
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    out = {}
+    for name in ("q", "k", "v") + (("dout",) if with_dout else ()):
+        out[name] = torch.randn(shape, generator=g, dtype=torch.float32, device=device).to(tdt)
+    th = make_inputs(1, 1, 1, heads, d, dtype, seed, theta_noise=theta_noise)
+    for name in ("theta_row", "theta_col"):
+        out[name] = th[name].to(device)
     return out
 
 

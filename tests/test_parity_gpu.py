@@ -89,6 +89,10 @@ FWD_SMALL = [
     (1, 32, 48, 2, 32, 16, 8, "bf16"),
     (1, 64, 96, 2, 32, 32, 16, "bf16"),
     (1, 16, 16, 20, 32, 8, 3, "bf16"),
+    (1, 8, 8, 2, 32, 8, 3, "bf16"),
+    (1, 32, 32, 2, 32, 32, 16, "bf16"),
+    (1, 64, 64, 1, 32, 32, 31, "bf16"),
+    (1, 64, 64, 1, 32, 32, 1, "bf16"),
 ]
 
 
@@ -222,6 +226,10 @@ BWD_SMALL = [
     (1, 32, 48, 2, 32, 16, 8, "bf16"),
     (1, 64, 96, 2, 32, 32, 16, "bf16"),
     (1, 16, 16, 20, 32, 8, 3, "bf16"),
+    (1, 8, 8, 2, 32, 8, 3, "bf16"),
+    (1, 32, 32, 2, 32, 32, 16, "bf16"),
+    (1, 64, 64, 1, 32, 32, 31, "bf16"),
+    (1, 64, 64, 1, 32, 32, 1, "bf16"),
 ]
 
 

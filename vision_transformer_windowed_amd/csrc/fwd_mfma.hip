@@ -513,11 +513,19 @@ hipError_t launch_nw(const FwdArgs& a, hipStream_t st) {
   const int NP = (g.N + 31) / 32 * 32;
   const int nqb = (g.N + NWAVES * 32 - 1) / (NWAVES * 32);
   const size_t smem = fwd_smem_bytes(NP, g.M);
-  static std::once_flag once;
-  std::call_once(once, [] {
+  // The dynamic-LDS limit is raised on the current device, once per device (beyond kMaxDevices:
+  // on every call).
+  constexpr int kMaxDevices = 64;
+  static std::once_flag once[kMaxDevices];
+  const auto raise = [] {
     (void)hipFuncSetAttribute((const void*)fwd_mfma_kernel<NWAVES, MT, NPMAX>,
                               hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-  });
+  };
+  int dev = 0;
+  if (hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < kMaxDevices)
+    std::call_once(once[dev], raise);
+  else
+    raise();
   const int64_t nwh = g.B * g.nH * g.nW * g.heads;
   // staggered start (see the kernel): 64 window-heads split into 128 half tasks when there are
   // two query blocks and enough work for several rounds of workgroups per CU

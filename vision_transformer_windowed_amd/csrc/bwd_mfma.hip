@@ -809,9 +809,16 @@ MainShape main_shape(int N) {
   if (N > 128) return {4, 2};
   return {N > 64 ? 4 : 2, 1};
 }
-int64_t blocks_per_windowhead(int N) {
-  const MainShape m = main_shape(N);
-  return (N + m.waves * m.sets * 32 - 1) / (m.waves * m.sets * 32);
+// The shape the dispatch launches for a geometry.  The grid, the dtheta partial rows (and so the
+// workspace size) all follow it; launch_main refuses a template shape that differs.
+MainShape bwd_shape(const Geom& g) {
+  if (g.M == 32 || g.M == 16) return {g.M == 32 ? 8 : 4, 2};
+  if (g.M == 8) return {2, 1};
+  return main_shape(g.N);
+}
+int64_t blocks_per_windowhead(const Geom& g) {
+  const MainShape m = bwd_shape(g);
+  return (g.N + m.waves * m.sets * 32 - 1) / (m.waves * m.sets * 32);
 }
 
 template <int NW, int MT, int S>
@@ -819,7 +826,9 @@ hipError_t launch_main(const BwdArgs& a, hipStream_t st) {
   const Geom& g = a.g;
   const int64_t nwh = g.B * g.nH * g.nW * g.heads;
   const int NP = (g.N + 31) / 32 * 32;
-  const int nb = (int)blocks_per_windowhead(g.N);
+  const MainShape m = bwd_shape(g);
+  if (m.waves != NW || m.sets != S) return hipErrorInvalidConfiguration;
+  const int nb = (int)blocks_per_windowhead(g);
   const int64_t blocks = nwh * nb;
   hipLaunchKernelGGL((bwd_dkdv_mfma_kernel<NW, MT, S>), dim3((unsigned)blocks), dim3(NW * 64),
                      dkdv_smem<NW>(NP, g.M), st, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
@@ -839,7 +848,7 @@ hipError_t launch_main(const BwdArgs& a, hipStream_t st) {
 }  // namespace
 
 int64_t bwd_mfma_partials(const Geom& g) {
-  return (int64_t)g.heads * 2 * g.B * g.nH * g.nW * blocks_per_windowhead(g.N);
+  return (int64_t)g.heads * 2 * g.B * g.nH * g.nW * blocks_per_windowhead(g);
 }
 
 hipError_t launch_bwd_mfma(const BwdArgs& a, hipStream_t st) {
@@ -860,7 +869,7 @@ hipError_t launch_bwd_mfma(const BwdArgs& a, hipStream_t st) {
   if (g.M == 32) return launch_main<8, 32, 2>(a, st);
   if (g.M == 8) return launch_main<2, 8, 1>(a, st);
   if (g.M == 16) return launch_main<4, 16, 2>(a, st);
-  const MainShape m = main_shape(g.N);
+  const MainShape m = bwd_shape(g);
   if (m.waves == 8) return launch_main<8, 0, 2>(a, st);
   if (m.waves == 4) return m.sets == 2 ? launch_main<4, 0, 2>(a, st) : launch_main<4, 0, 1>(a, st);
   return launch_main<2, 0, 1>(a, st);

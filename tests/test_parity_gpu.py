@@ -340,6 +340,22 @@ def test_autograd_matches_backward_entry_point():
         assert torch.equal(leaves[n].grad, r), n
 
 
+def test_caller_workspace_any_dtype_or_too_small():
+    """A caller's workspace is sized in bytes whatever its dtype, and one that is too small is
+    replaced; the gradients are bit-identical to those with the binding's own workspace."""
+    x = make_inputs(2, 32, 32, 3, 32, "bf16", seed=11, with_dout=True)
+    xd = to_dev(x)
+    out, lse = F.wattn_fwd(xd["q"], xd["k"], xd["v"], xd["theta_row"], xd["theta_col"], 16, 8)
+    args = (xd["q"], xd["k"], xd["v"], out, xd["dout"], lse, xd["theta_row"], xd["theta_col"], 16, 8)
+    ref = F.wattn_bwd(*args)
+    nbytes = F.bwd_workspace_bytes(xd["q"], 16, 8)
+    for ws in (torch.empty((nbytes + 3) // 4, device=DEV, dtype=torch.float32),
+               torch.empty(16, device=DEV, dtype=torch.uint8)):
+        got = F.wattn_bwd(*args, workspace=ws)
+        for a, b in zip(ref, got):
+            assert torch.equal(a, b)
+
+
 def test_empty_batch():
     x = make_inputs(0, 16, 16, 2, 32, "bf16", seed=1, with_dout=True)
     xd = to_dev(x)

@@ -125,9 +125,11 @@ def _dtype_code(t):
     raise TypeError(f"unsupported dtype {t.dtype}; use torch.bfloat16 or torch.float32")
 
 
-def _check_grid(name, t, shape, dtype):
+def _check_grid(name, t, shape, dtype, device=None):
     if not t.is_cuda:
         raise ValueError(f"{name} must be a GPU tensor")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device} (all tensors on one GPU)")
     if tuple(t.shape) != tuple(shape):
         raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
     if t.dtype != dtype:
@@ -144,27 +146,42 @@ def _stream(device):
     return torch.cuda.current_stream(device).cuda_stream
 
 
+def _workspace(workspace, nbytes, device):
+    """The caller's workspace when it is a contiguous GPU tensor on `device` of at least `nbytes`
+    bytes, else a fresh one; returns (tensor, its size in bytes)."""
+    if workspace is not None:
+        if not workspace.is_cuda or workspace.device != device or not workspace.is_contiguous():
+            raise ValueError(f"workspace must be a contiguous tensor on {device}")
+        size = workspace.numel() * workspace.element_size()
+        if size >= nbytes:
+            return workspace, size
+    ws = torch.empty(max(nbytes, 1), device=device, dtype=torch.uint8)
+    return ws, ws.numel()
+
+
 def wattn_fwd(q, k, v, theta_row, theta_col, M, shift=0, out=None, lse=None, need_lse=True):
     """Forward window attention on the GPU.  Returns (out, lse); lse is None when need_lse=False."""
     if q.dim() != 5:
         raise ValueError("q must be [B, Hg, Wg, heads, d]")
     B, Hg, Wg, H, D = q.shape
     code = _dtype_code(q)
+    dev = q.device
     for name, t in (("q", q), ("k", k), ("v", v)):
-        _check_grid(name, t, q.shape, q.dtype)
+        _check_grid(name, t, q.shape, q.dtype, dev)
     for name, t in (("theta_row", theta_row), ("theta_col", theta_col)):
-        _check_grid(name, t, (H, D // 4), torch.float32)
+        _check_grid(name, t, (H, D // 4), torch.float32, dev)
     if out is None:
         out = torch.empty_like(q)
-    _check_grid("out", out, q.shape, q.dtype)
+    _check_grid("out", out, q.shape, q.dtype, dev)
     if need_lse:
         if lse is None:
-            lse = torch.empty((B, Hg, Wg, H), device=q.device, dtype=torch.float32)
-        _check_grid("lse", lse, (B, Hg, Wg, H), torch.float32)
+            lse = torch.empty((B, Hg, Wg, H), device=dev, dtype=torch.float32)
+        _check_grid("lse", lse, (B, Hg, Wg, H), torch.float32, dev)
     else:
         lse = None
-    st = flashswin_wattn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(theta_row), _ptr(theta_col), _ptr(out), _ptr(lse),
-                             B, Hg, Wg, H, D, int(M), int(shift), code, _stream(q.device))
+    with torch.cuda.device(dev):
+        st = flashswin_wattn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(theta_row), _ptr(theta_col), _ptr(out),
+                                 _ptr(lse), B, Hg, Wg, H, D, int(M), int(shift), code, _stream(dev))
     if st != FSW_OK:
         raise FlashSwinError(st, "flashswin_wattn_fwd")
     return out, lse
@@ -177,11 +194,12 @@ def wattn_bwd(q, k, v, out, dout, lse, theta_row, theta_col, M, shift=0, workspa
     """
     B, Hg, Wg, H, D = q.shape
     code = _dtype_code(q)
+    dev = q.device
     for name, t in (("q", q), ("k", k), ("v", v), ("out", out), ("dout", dout)):
-        _check_grid(name, t, q.shape, q.dtype)
-    _check_grid("lse", lse, (B, Hg, Wg, H), torch.float32)
+        _check_grid(name, t, q.shape, q.dtype, dev)
+    _check_grid("lse", lse, (B, Hg, Wg, H), torch.float32, dev)
     for name, t in (("theta_row", theta_row), ("theta_col", theta_col)):
-        _check_grid(name, t, (H, D // 4), torch.float32)
+        _check_grid(name, t, (H, D // 4), torch.float32, dev)
     if grads is None:
         dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
         dtr = torch.empty_like(theta_row)
@@ -189,16 +207,15 @@ def wattn_bwd(q, k, v, out, dout, lse, theta_row, theta_col, M, shift=0, workspa
     else:
         dq, dk, dv, dtr, dtc = grads
         for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
-            _check_grid(name, t, q.shape, q.dtype)
+            _check_grid(name, t, q.shape, q.dtype, dev)
         for name, t in (("dtheta_row", dtr), ("dtheta_col", dtc)):
-            _check_grid(name, t, (H, D // 4), torch.float32)
+            _check_grid(name, t, (H, D // 4), torch.float32, dev)
     nbytes = flashswin_wattn_bwd_workspace_size(B, Hg, Wg, H, D, int(M), int(shift), code)
-    if workspace is None or workspace.numel() < nbytes:
-        workspace = torch.empty(max(nbytes, 1), device=q.device, dtype=torch.uint8)
-    st = flashswin_wattn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _ptr(lse), _ptr(theta_row),
-                             _ptr(theta_col), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dtr), _ptr(dtc),
-                             _ptr(workspace), workspace.numel(), B, Hg, Wg, H, D, int(M), int(shift), code,
-                             _stream(q.device))
+    workspace, wbytes = _workspace(workspace, nbytes, dev)
+    with torch.cuda.device(dev):
+        st = flashswin_wattn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _ptr(lse), _ptr(theta_row),
+                                 _ptr(theta_col), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dtr), _ptr(dtc),
+                                 _ptr(workspace), wbytes, B, Hg, Wg, H, D, int(M), int(shift), code, _stream(dev))
     if st != FSW_OK:
         raise FlashSwinError(st, "flashswin_wattn_bwd")
     return dq, dk, dv, dtr, dtc
@@ -215,20 +232,22 @@ def wattn_fwd_packed(qkv, theta_row, theta_col, M, shift=0, out=None, lse=None, 
     """Forward from packed qkv [B, Hg, Wg, 3, heads, d], read in place.  Returns (out, lse)."""
     B, Hg, Wg, H, D = _packed_shape(qkv)
     code = _dtype_code(qkv)
-    _check_grid("qkv", qkv, qkv.shape, qkv.dtype)
+    dev = qkv.device
+    _check_grid("qkv", qkv, qkv.shape, qkv.dtype, dev)
     for name, t in (("theta_row", theta_row), ("theta_col", theta_col)):
-        _check_grid(name, t, (H, D // 4), torch.float32)
+        _check_grid(name, t, (H, D // 4), torch.float32, dev)
     if out is None:
-        out = torch.empty((B, Hg, Wg, H, D), device=qkv.device, dtype=qkv.dtype)
-    _check_grid("out", out, (B, Hg, Wg, H, D), qkv.dtype)
+        out = torch.empty((B, Hg, Wg, H, D), device=dev, dtype=qkv.dtype)
+    _check_grid("out", out, (B, Hg, Wg, H, D), qkv.dtype, dev)
     if need_lse:
         if lse is None:
-            lse = torch.empty((B, Hg, Wg, H), device=qkv.device, dtype=torch.float32)
-        _check_grid("lse", lse, (B, Hg, Wg, H), torch.float32)
+            lse = torch.empty((B, Hg, Wg, H), device=dev, dtype=torch.float32)
+        _check_grid("lse", lse, (B, Hg, Wg, H), torch.float32, dev)
     else:
         lse = None
-    st = flashswin_wattn_fwd_packed(_ptr(qkv), _ptr(theta_row), _ptr(theta_col), _ptr(out), _ptr(lse), B, Hg, Wg,
-                                    H, D, int(M), int(shift), code, _stream(qkv.device))
+    with torch.cuda.device(dev):
+        st = flashswin_wattn_fwd_packed(_ptr(qkv), _ptr(theta_row), _ptr(theta_col), _ptr(out), _ptr(lse), B, Hg,
+                                        Wg, H, D, int(M), int(shift), code, _stream(dev))
     if st != FSW_OK:
         raise FlashSwinError(st, "flashswin_wattn_fwd_packed")
     return out, lse
@@ -241,25 +260,26 @@ def wattn_bwd_packed(qkv, out, dout, lse, theta_row, theta_col, M, shift=0, work
     """
     B, Hg, Wg, H, D = _packed_shape(qkv)
     code = _dtype_code(qkv)
-    _check_grid("qkv", qkv, qkv.shape, qkv.dtype)
+    dev = qkv.device
+    _check_grid("qkv", qkv, qkv.shape, qkv.dtype, dev)
     for name, t in (("out", out), ("dout", dout)):
-        _check_grid(name, t, (B, Hg, Wg, H, D), qkv.dtype)
-    _check_grid("lse", lse, (B, Hg, Wg, H), torch.float32)
+        _check_grid(name, t, (B, Hg, Wg, H, D), qkv.dtype, dev)
+    _check_grid("lse", lse, (B, Hg, Wg, H), torch.float32, dev)
     for name, t in (("theta_row", theta_row), ("theta_col", theta_col)):
-        _check_grid(name, t, (H, D // 4), torch.float32)
+        _check_grid(name, t, (H, D // 4), torch.float32, dev)
     if grads is None:
         dqkv, dtr, dtc = torch.empty_like(qkv), torch.empty_like(theta_row), torch.empty_like(theta_col)
     else:
         dqkv, dtr, dtc = grads
-        _check_grid("dqkv", dqkv, qkv.shape, qkv.dtype)
+        _check_grid("dqkv", dqkv, qkv.shape, qkv.dtype, dev)
         for name, t in (("dtheta_row", dtr), ("dtheta_col", dtc)):
-            _check_grid(name, t, (H, D // 4), torch.float32)
+            _check_grid(name, t, (H, D // 4), torch.float32, dev)
     nbytes = flashswin_wattn_bwd_workspace_size(B, Hg, Wg, H, D, int(M), int(shift), code)
-    if workspace is None or workspace.numel() < nbytes:
-        workspace = torch.empty(max(nbytes, 1), device=qkv.device, dtype=torch.uint8)
-    st = flashswin_wattn_bwd_packed(_ptr(qkv), _ptr(out), _ptr(dout), _ptr(lse), _ptr(theta_row), _ptr(theta_col),
-                                    _ptr(dqkv), _ptr(dtr), _ptr(dtc), _ptr(workspace), workspace.numel(), B, Hg, Wg,
-                                    H, D, int(M), int(shift), code, _stream(qkv.device))
+    workspace, wbytes = _workspace(workspace, nbytes, dev)
+    with torch.cuda.device(dev):
+        st = flashswin_wattn_bwd_packed(_ptr(qkv), _ptr(out), _ptr(dout), _ptr(lse), _ptr(theta_row),
+                                        _ptr(theta_col), _ptr(dqkv), _ptr(dtr), _ptr(dtc), _ptr(workspace), wbytes,
+                                        B, Hg, Wg, H, D, int(M), int(shift), code, _stream(dev))
     if st != FSW_OK:
         raise FlashSwinError(st, "flashswin_wattn_bwd_packed")
     return dqkv, dtr, dtc

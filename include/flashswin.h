@@ -60,9 +60,10 @@ typedef enum { FSW_F32 = 0, FSW_BF16 = 1 } fsw_dtype;
  *   theta_row,
  *   theta_col    device, float32 [heads, d/4], 4-byte aligned (angular frequency, rad per token).
  *   out          device, [B, Hg, Wg, heads, d] of `dtype`, 16-byte aligned; overwritten.
- *                May not alias q, k or v.
  *   lse          device, float32 [B, Hg, Wg, heads], 4-byte aligned, overwritten; or NULL when the
  *                caller does not need it (inference).
+ *   out and lse may not share a byte with q, k, v, theta_row, theta_col or each other
+ *   (FSW_ERR_INVALID_ARG); the inputs may share memory.
  *   B >= 0 (B == 0 returns FSW_OK with nothing enqueued); Hg, Wg positive multiples of M;
  *   1 <= M <= 32; 0 <= shift < M; heads >= 1; d in {8, 16, 32, 64}; dtype FSW_F32 or FSW_BF16.
  *   Needs no workspace.  bf16 inputs are rounded once more to bf16 after the rotation and the
@@ -91,12 +92,14 @@ size_t flashswin_wattn_bwd_workspace_size(int64_t B, int64_t Hg, int64_t Wg, int
  *   dout          device, [B, Hg, Wg, heads, d] of `dtype`: gradient of the loss w.r.t. out.
  *   lse           device, float32 [B, Hg, Wg, heads]: the forward's lse (required).
  *   theta_row/col as in the forward.
- *   dq, dk, dv    device, [B, Hg, Wg, heads, d] of `dtype`, overwritten.  May not alias inputs.
+ *   dq, dk, dv    device, [B, Hg, Wg, heads, d] of `dtype`, overwritten.
  *   dtheta_row,
  *   dtheta_col    device, float32 [heads, d/4], overwritten with d(loss)/d(theta), summed over
  *                 the whole batch, all windows and tokens, in a fixed order (bit-reproducible).
  *   workspace     device scratch of at least flashswin_wattn_bwd_workspace_size() bytes,
  *                 256-byte aligned; contents on entry are ignored.
+ *   dq, dk, dv, dtheta_row, dtheta_col and the workspace may not share a byte with any input or
+ *   with each other (FSW_ERR_INVALID_ARG).
  * Same shape rules and return codes as the forward, plus FSW_ERR_WORKSPACE.
  */
 int flashswin_wattn_bwd(const void* q, const void* k, const void* v,
@@ -115,8 +118,8 @@ int flashswin_wattn_bwd(const void* q, const void* k, const void* v,
  *   qkv          device, [B, Hg, Wg, 3, heads, d] of `dtype`, 16-byte aligned: q, k and v are the
  *                slices qkv[..., 0, :, :], qkv[..., 1, :, :], qkv[..., 2, :, :], read in place
  *                (no split, no copy).
- *   out, lse     as in flashswin_wattn_fwd ([B, Hg, Wg, heads, d] and [B, Hg, Wg, heads]); out may
- *                not overlap qkv.
+ *   out, lse     as in flashswin_wattn_fwd ([B, Hg, Wg, heads, d] and [B, Hg, Wg, heads]); they may
+ *                not share a byte with qkv, theta_row, theta_col or each other.
  * Same shape rules and return codes as flashswin_wattn_fwd.  out and lse are bit-identical to
  * flashswin_wattn_fwd on the three slices.
  */
@@ -132,7 +135,9 @@ int flashswin_wattn_fwd_packed(const void* qkv, const float* theta_row, const fl
  *   out, dout,
  *   lse, theta    as in flashswin_wattn_bwd.
  *   dqkv          device, [B, Hg, Wg, 3, heads, d] of `dtype`, 16-byte aligned, overwritten with
- *                 dq, dk, dv in the places of q, k, v.  May not overlap qkv, out or dout.
+ *                 dq, dk, dv in the places of q, k, v.
+ *   dqkv, dtheta_row, dtheta_col and the workspace may not share a byte with any input or with
+ *   each other.
  *   dtheta_row/col, workspace  as in flashswin_wattn_bwd; the workspace size is
  *                 flashswin_wattn_bwd_workspace_size() of the same shape.
  * Same shape rules and return codes as flashswin_wattn_bwd.  Results are bit-identical to

@@ -37,8 +37,11 @@ def test_version_and_status_strings():
     assert "unknown" in F.flashswin_status_string(99)
 
 
+GIB = 1 << 30  # buffers of the fixtures below sit 1 GiB apart, so none overlaps another
+
+
 def fwd(**kw):
-    a = dict(q=FAKE, k=FAKE, v=FAKE, tr=FAKE, tc=FAKE, out=FAKE + 4096, lse=FAKE + 8192,
+    a = dict(q=FAKE, k=FAKE, v=FAKE, tr=FAKE + 3 * GIB, tc=FAKE + 3 * GIB + 256, out=FAKE + GIB, lse=FAKE + 2 * GIB,
              B=1, Hg=16, Wg=16, heads=2, d=32, M=8, shift=0, dtype=F.FSW_BF16)
     a.update(kw)
     return F.flashswin_wattn_fwd(a["q"], a["k"], a["v"], a["tr"], a["tc"], a["out"], a["lse"], a["B"], a["Hg"],
@@ -66,6 +69,9 @@ def fwd(**kw):
     (dict(tc=FAKE + 2), F.FSW_ERR_INVALID_ARG),
     (dict(lse=FAKE + 1), F.FSW_ERR_INVALID_ARG),
     (dict(out=FAKE), F.FSW_ERR_INVALID_ARG),       # out aliases q
+    (dict(out=FAKE + 4096), F.FSW_ERR_INVALID_ARG),  # out overlaps the tail of q (32 KiB)
+    (dict(lse=FAKE + GIB + 1024), F.FSW_ERR_INVALID_ARG),  # lse inside out
+    (dict(tr=FAKE + GIB + 64), F.FSW_ERR_INVALID_ARG),  # theta inside out
     (dict(B=1 << 40), F.FSW_ERR_UNSUPPORTED),      # index space overflow
 ])
 def test_forward_rejects_before_launch(kw, status):
@@ -77,9 +83,10 @@ def test_forward_empty_batch_is_a_no_op():
 
 
 def bwd(**kw):
-    a = dict(q=FAKE, k=FAKE + 256, v=FAKE + 512, out=FAKE + 768, dout=FAKE + 1024, lse=FAKE + 1280,
-             tr=FAKE + 1536, tc=FAKE + 1792, dq=FAKE + 2048, dk=FAKE + 2304, dv=FAKE + 2560,
-             dtr=FAKE + 2816, dtc=FAKE + 3072, ws=FAKE + 4096, wsb=None,
+    a = dict(q=FAKE, k=FAKE + GIB, v=FAKE + 2 * GIB, out=FAKE + 3 * GIB, dout=FAKE + 4 * GIB,
+             lse=FAKE + 5 * GIB, tr=FAKE + 6 * GIB, tc=FAKE + 6 * GIB + 256, dq=FAKE + 7 * GIB,
+             dk=FAKE + 8 * GIB, dv=FAKE + 9 * GIB, dtr=FAKE + 10 * GIB, dtc=FAKE + 10 * GIB + 256,
+             ws=FAKE + 11 * GIB, wsb=None,
              B=1, Hg=16, Wg=16, heads=2, d=32, M=8, shift=4, dtype=F.FSW_BF16)
     a.update(kw)
     if a["wsb"] is None:
@@ -98,10 +105,14 @@ def bwd(**kw):
     (dict(dtr=None), F.FSW_ERR_INVALID_ARG),
     (dict(dq=FAKE + 4), F.FSW_ERR_INVALID_ARG),
     (dict(dk=FAKE), F.FSW_ERR_INVALID_ARG),        # dk aliases q
-    (dict(dv=FAKE + 2304), F.FSW_ERR_INVALID_ARG),  # dv aliases dk
-    (dict(dtc=FAKE + 2816), F.FSW_ERR_INVALID_ARG),  # dtheta_col aliases dtheta_row
+    (dict(dv=FAKE + 8 * GIB), F.FSW_ERR_INVALID_ARG),  # dv aliases dk
+    (dict(dv=FAKE + 8 * GIB + 4096), F.FSW_ERR_INVALID_ARG),  # dv overlaps the tail of dk
+    (dict(dq=FAKE + 3 * GIB + 16384), F.FSW_ERR_INVALID_ARG),  # dq overlaps out
+    (dict(dtc=FAKE + 10 * GIB), F.FSW_ERR_INVALID_ARG),  # dtheta_col aliases dtheta_row
+    (dict(dtr=FAKE + 5 * GIB + 256), F.FSW_ERR_INVALID_ARG),  # dtheta_row inside lse
+    (dict(ws=FAKE + 4 * GIB), F.FSW_ERR_INVALID_ARG),  # workspace over dout
     (dict(ws=None), F.FSW_ERR_WORKSPACE),
-    (dict(ws=FAKE + 4100), F.FSW_ERR_WORKSPACE),   # misaligned workspace
+    (dict(ws=FAKE + 11 * GIB + 4), F.FSW_ERR_WORKSPACE),  # misaligned workspace
     (dict(wsb=16), F.FSW_ERR_WORKSPACE),           # too small
     (dict(d=12), F.FSW_ERR_UNSUPPORTED),
 ])

@@ -49,10 +49,39 @@ int check_shape(int64_t B, int64_t Hg, int64_t Wg, int heads, int d, int M, int 
 
 size_t elem_bytes(int dtype) { return dtype == FSW_BF16 ? 2 : 4; }
 
-// Byte ranges [a, a + na) and [b, b + nb) overlap.
+// Byte ranges [a, a + na) and [b, b + nb) overlap (a null or empty range overlaps nothing).
 bool overlap(const void* a, size_t na, const void* b, size_t nb) {
+  if (!a || !b || na == 0 || nb == 0) return false;
   const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
   return x < y + nb && y < x + na;
+}
+
+// A buffer and its size in bytes.
+struct Span {
+  const void* p;
+  size_t n;
+};
+// Every output span is disjoint from every input span and from the other outputs.  Inputs may
+// share memory with each other (they are only read).
+template <size_t NO, size_t NI>
+bool outputs_disjoint(const Span (&outs)[NO], const Span (&ins)[NI]) {
+  for (size_t i = 0; i < NO; ++i) {
+    for (size_t j = 0; j < NI; ++j)
+      if (overlap(outs[i].p, outs[i].n, ins[j].p, ins[j].n)) return false;
+    for (size_t j = i + 1; j < NO; ++j)
+      if (overlap(outs[i].p, outs[i].n, outs[j].p, outs[j].n)) return false;
+  }
+  return true;
+}
+
+// Bytes of one token-grid tensor, of LSE and of one theta table of geometry g.
+struct Sizes {
+  size_t tens, lse, theta;
+};
+Sizes sizes_of(const fsw::Geom& g, int dtype) {
+  const size_t tokens = (size_t)(g.B * g.Hg * g.Wg);
+  return {tokens * (size_t)g.os * elem_bytes(dtype), tokens * (size_t)g.heads * 4,
+          (size_t)g.heads * (size_t)(g.d / 4) * 4};
 }
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -138,7 +167,10 @@ int flashswin_wattn_fwd(const void* q, const void* k, const void* v, const float
   int st = check_shape(B, Hg, Wg, heads, d, M, shift, dtype, &g);
   if (st != FSW_OK) return st;
   if (B == 0) return FSW_OK;
-  if (out == q || out == k || out == v) return FSW_ERR_INVALID_ARG;
+  const Sizes z = sizes_of(g, dtype);
+  const Span outs[] = {{out, z.tens}, {lse, z.lse}};
+  const Span ins[] = {{q, z.tens}, {k, z.tens}, {v, z.tens}, {theta_row, z.theta}, {theta_col, z.theta}};
+  if (!outputs_disjoint(outs, ins)) return FSW_ERR_INVALID_ARG;
   return fwd_impl(q, k, v, theta_row, theta_col, out, lse, g, dtype, hip_stream);
 }
 
@@ -151,8 +183,11 @@ int flashswin_wattn_fwd_packed(const void* qkv, const float* theta_row, const fl
   if (B == 0) return FSW_OK;
   if ((long double)B * Hg * Wg * 3 * heads * d > (long double)((int64_t)1 << 56)) return FSW_ERR_UNSUPPORTED;
   if (!qkv) return FSW_ERR_INVALID_ARG;
-  const size_t eb = elem_bytes(dtype), tens = (size_t)(B * Hg * Wg) * g.os * eb;
-  if (out && overlap(qkv, 3 * tens, out, tens)) return FSW_ERR_INVALID_ARG;
+  const size_t eb = elem_bytes(dtype);
+  const Sizes z = sizes_of(g, dtype);
+  const Span outs[] = {{out, z.tens}, {lse, z.lse}};
+  const Span ins[] = {{qkv, 3 * z.tens}, {theta_row, z.theta}, {theta_col, z.theta}};
+  if (!outputs_disjoint(outs, ins)) return FSW_ERR_INVALID_ARG;
   g.xs = 3 * g.os;
   const char* base = static_cast<const char*>(qkv);
   const size_t slot = (size_t)g.os * eb;  // bytes from q to k and from k to v within a token
@@ -175,12 +210,12 @@ int flashswin_wattn_bwd(const void* q, const void* k, const void* v, const void*
   int st = check_shape(B, Hg, Wg, heads, d, M, shift, dtype, &g);
   if (st != FSW_OK) return st;
   if (B == 0) return FSW_OK;
-  const void* outs[] = {dq, dk, dv};
-  const void* ins[] = {q, k, v, out, dout};
-  for (const void* o : outs)
-    for (const void* i : ins)
-      if (o && o == i) return FSW_ERR_INVALID_ARG;
-  if (dq == dk || dq == dv || dk == dv) return FSW_ERR_INVALID_ARG;
+  const Sizes z = sizes_of(g, dtype);
+  const Span outs[] = {{dq, z.tens},         {dk, z.tens},          {dv, z.tens},
+                       {dtheta_row, z.theta}, {dtheta_col, z.theta}, {workspace, workspace_bytes}};
+  const Span ins[] = {{q, z.tens},   {k, z.tens},           {v, z.tens},          {out, z.tens},
+                      {dout, z.tens}, {lse, z.lse}, {theta_row, z.theta}, {theta_col, z.theta}};
+  if (!outputs_disjoint(outs, ins)) return FSW_ERR_INVALID_ARG;
   return bwd_impl(q, k, v, out, dout, lse, theta_row, theta_col, dq, dk, dv, dtheta_row, dtheta_col, workspace,
                   workspace_bytes, g, dtype, hip_stream);
 }
@@ -195,10 +230,13 @@ int flashswin_wattn_bwd_packed(const void* qkv, const void* out, const void* dou
   if (B == 0) return FSW_OK;
   if ((long double)B * Hg * Wg * 3 * heads * d > (long double)((int64_t)1 << 56)) return FSW_ERR_UNSUPPORTED;
   if (!qkv || !dqkv) return FSW_ERR_INVALID_ARG;
-  const size_t eb = elem_bytes(dtype), tens = (size_t)(B * Hg * Wg) * g.os * eb;
-  if (overlap(dqkv, 3 * tens, qkv, 3 * tens) || (out && overlap(dqkv, 3 * tens, out, tens)) ||
-      (dout && overlap(dqkv, 3 * tens, dout, tens)))
-    return FSW_ERR_INVALID_ARG;
+  const size_t eb = elem_bytes(dtype);
+  const Sizes z = sizes_of(g, dtype);
+  const Span outs[] = {{dqkv, 3 * z.tens}, {dtheta_row, z.theta}, {dtheta_col, z.theta},
+                       {workspace, workspace_bytes}};
+  const Span ins[] = {{qkv, 3 * z.tens}, {out, z.tens}, {dout, z.tens}, {lse, z.lse}, {theta_row, z.theta},
+                      {theta_col, z.theta}};
+  if (!outputs_disjoint(outs, ins)) return FSW_ERR_INVALID_ARG;
   g.xs = 3 * g.os;
   const size_t slot = (size_t)g.os * eb;
   const char* x = static_cast<const char*>(qkv);

@@ -13,9 +13,17 @@ Two summaries:
   ``kernel_source_sha:``, ``hbm_read_bytes_per_launch:`` and
   ``hbm_write_bytes_per_launch:`` that bench.py reads back.
 
+* ``counters``: instruction mix and matrix-core occupancy from ``rocprofv3 --pmc`` runs of
+  ``SQ_*`` counters (at most 8 per run): per kernel, instructions per 32x32 score tile (MFMA,
+  VALU, of which transcendental, LDS, scalar, vector memory) and the MFMA pipe's busy fraction,
+  ``SQ_INSTS_MFMA`` x 32 cycles (one 32x32x16 MFMA occupies a SIMD's matrix core 32 cycles) over
+  the dispatch's duration x 2.4 GHz x 1024 SIMDs.
+
 Usage (on the CPU, after the GPU runs have written their CSVs)::
 
     python -m vision_transformer_windowed_amd.profiling stats DIR --command CMD --out FILE
+    python -m vision_transformer_windowed_amd.profiling counters DIR [DIR ...] --kernels REGEX[,REGEX] \\
+        --tiles N --title TITLE --command CMD --out FILE
     python -m vision_transformer_windowed_amd.profiling traffic --fetch DIR --write DIR \\
         --copy-fetch DIR --copy-write DIR --kernels REGEX[,REGEX] --tag TAG --workload NAME \\
         --command CMD --out FILE
@@ -84,6 +92,58 @@ def read_counter(dirpath, counter):
     return out
 
 
+def read_counters_with_time(dirpaths):
+    """{kernel: {counter: mean per dispatch, '_dur_ns': mean duration}} over several counter runs."""
+    acc, dur = {}, {}
+    for d in dirpaths:
+        per = {}
+        for r in csv.DictReader(open(_find(d, "counter_collection.csv"))):
+            k = short_name(r["Kernel_Name"])
+            key = (k, r["Dispatch_Id"], r["Counter_Name"])
+            per[key] = per.get(key, 0.0) + float(r["Counter_Value"])
+            dur.setdefault(k, {})[(d, r["Dispatch_Id"])] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+        for (k, _, c), v in per.items():
+            acc.setdefault(k, {}).setdefault(c, []).append(v)
+    out = {}
+    for k, cs in acc.items():
+        out[k] = {c: statistics.mean(vs) for c, vs in cs.items()}
+        out[k]["_dur_ns"] = statistics.mean(dur[k].values())
+    return out
+
+
+MFMA_CYCLES = 32        # cycles one v_mfma_f32_32x32x16 occupies a SIMD's matrix core
+SIMDS = 1024            # 256 CUs x 4 SIMDs
+CLOCK_HZ = 2.4e9        # peak engine clock
+
+
+def counters_markdown(dirpaths, kernels, tiles, title, command):
+    data = read_counters_with_time(dirpaths)
+    pats = [re.compile(p) for p in kernels]
+    per_tile = [("MFMA", "SQ_INSTS_MFMA"), ("VALU", "SQ_INSTS_VALU"), ("of which transcendental",
+                "SQ_INSTS_VALU_TRANS_F32"), ("LDS", "SQ_INSTS_LDS"), ("SALU", "SQ_INSTS_SALU"),
+                ("VMEM read", "SQ_INSTS_VMEM_RD"), ("VMEM write", "SQ_INSTS_VMEM_WR")]
+    lines = [f"# {title}", "",
+             "Commands (from the repository root; `cd /tmp && export TMPDIR=/tmp` first), one run per counter set:",
+             "", "```", command, "```", "",
+             f"Instructions are counted per wave instruction and divided by the {tiles:.6g} score tiles (32 queries x "
+             "32 keys) of one launch.  MFMA busy = SQ_INSTS_MFMA x 32 cycles / (dispatch duration x 2.4 GHz x 1024 "
+             "SIMDs); SQ_VALU_MFMA_BUSY_CYCLES / (MFMA x 32) checks the 32 cycles.  Durations are those of the "
+             "counter runs.", "",
+             "| kernel | duration us | " + " | ".join(n + "/tile" for n, _ in per_tile) +
+             " | MFMA busy | busy cycles / (MFMA x 32) |",
+             "|---|---|" + "---|" * len(per_tile) + "---|---|"]
+    for k in sorted(data):
+        if not any(p.search(k) for p in pats):
+            continue
+        d = data[k]
+        cells = [f"{d.get(c, float('nan')) / tiles:.2f}" for _, c in per_tile]
+        mfma = d.get("SQ_INSTS_MFMA", float("nan"))
+        busy = mfma * MFMA_CYCLES / (d["_dur_ns"] * 1e-9 * CLOCK_HZ * SIMDS)
+        chk = d.get("SQ_VALU_MFMA_BUSY_CYCLES", float("nan")) / (mfma * MFMA_CYCLES)
+        lines.append(f"| `{k}` | {d['_dur_ns'] / 1e3:.1f} | " + " | ".join(cells) + f" | {busy:.1%} | {chk:.3f} |")
+    return "\n".join(lines) + "\n"
+
+
 def _copy_factor(dirpath, counter, nbytes):
     vals = [v for k, vs in read_counter(dirpath, counter).items() for v in vs if "neg" in k.lower()]
     if not vals:
@@ -134,9 +194,18 @@ def main():
     for name in ("fetch", "write", "copy-fetch", "copy-write", "kernels", "tag", "workload", "command", "out"):
         t.add_argument("--" + name, required=True)
     t.add_argument("--sha", default=None)
+    c = sub.add_parser("counters")
+    c.add_argument("dirs", nargs="+")
+    c.add_argument("--kernels", required=True)
+    c.add_argument("--tiles", type=float, required=True)
+    c.add_argument("--title", required=True)
+    c.add_argument("--command", required=True)
+    c.add_argument("--out", required=True)
     a = ap.parse_args()
     if a.mode == "stats":
         text = stats_markdown(a.dir, a.command, a.title)
+    elif a.mode == "counters":
+        text = counters_markdown(a.dirs, a.kernels.split(","), a.tiles, a.title, a.command)
     else:
         sha = a.sha
         if sha is None:

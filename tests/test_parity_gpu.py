@@ -93,6 +93,7 @@ FWD_SMALL = [
     (1, 32, 32, 2, 32, 32, 16, "bf16"),
     (1, 64, 64, 1, 32, 32, 31, "bf16"),
     (1, 64, 64, 1, 32, 32, 1, "bf16"),
+    (1, 8, 16, 40, 32, 8, 3, "bf16"),
 ]
 
 
@@ -230,6 +231,7 @@ BWD_SMALL = [
     (1, 32, 32, 2, 32, 32, 16, "bf16"),
     (1, 64, 64, 1, 32, 32, 31, "bf16"),
     (1, 64, 64, 1, 32, 32, 1, "bf16"),
+    (1, 8, 16, 40, 32, 8, 3, "bf16"),
 ]
 
 

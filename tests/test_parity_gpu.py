@@ -385,3 +385,26 @@ def test_large_tensors_64bit_offsets():
     g = oracle.wattn_bwd_ref(q, k, v, dout, tr, tc, M, s)
     for nm, got, ref in (("dQ", dq[imgs], g[0]), ("dK", dk[imgs], g[1]), ("dV", dv[imgs], g[2])):
         assert_close(nm, _np(got), ref, 2e-2, 5e-3)
+
+
+def test_huge_image_64bit_in_image_offsets():
+    """One image whose tensors exceed 4 GiB (6.4 GB: [1, 4096, 8192, 3, 32] bf16), so offsets within
+    a single image pass 2^32 bytes.  Shift 0, so a window is a 32 x 32 sub-grid: windows at the start,
+    middle and far end of the image against the oracle on those windows alone."""
+    B, Hg, Wg, H, D, M = 1, 4096, 8192, 3, 32, 32
+    assert Hg * Wg * H * D * 2 > 2 ** 32
+    x = make_device_inputs(B, Hg, Wg, H, D, "bf16", seed=2024, device=DEV, with_dout=True)
+    out, lse = F.wattn_fwd(x["q"], x["k"], x["v"], x["theta_row"], x["theta_col"], M, 0)
+    dq, dk, dv, _, _ = F.wattn_bwd(x["q"], x["k"], x["v"], out, x["dout"], lse, x["theta_row"], x["theta_col"],
+                                   M, 0)
+    torch.cuda.synchronize()
+    tr, tc = _np(x["theta_row"]), _np(x["theta_col"])
+    for wy, wx in ((0, 0), (64, 128), (Hg // M - 1, Wg // M - 1)):
+        sl = (slice(None), slice(wy * M, wy * M + M), slice(wx * M, wx * M + M))
+        q, k, v, dout = (_np(x[n][sl]) for n in ("q", "k", "v", "dout"))
+        ro, rl = oracle.wattn_fwd_ref(q, k, v, tr, tc, M, 0)
+        assert_close(f"O {wy},{wx}", _np(out[sl]), ro, 2e-2, 5e-3)
+        assert_close(f"LSE {wy},{wx}", _np(lse[sl]), rl, 2e-2, 5e-3)
+        g = oracle.wattn_bwd_ref(q, k, v, dout, tr, tc, M, 0)
+        for nm, got, ref in (("dQ", dq[sl], g[0]), ("dK", dk[sl], g[1]), ("dV", dv[sl], g[2])):
+            assert_close(f"{nm} {wy},{wx}", _np(got), ref, 2e-2, 5e-3)

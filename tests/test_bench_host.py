@@ -24,3 +24,12 @@ def test_live_fraction_known_values():
     assert bench.live_fraction(128, 128, 32, 16) == pytest.approx(0.765625)
     assert bench.live_fraction(64, 64, 32, 16) == pytest.approx(0.5625)
     assert bench.live_fraction(64, 64, 32, 0) == 1.0
+
+
+def test_bench_refuses_more_than_one_gpu():
+    import subprocess
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=300, cwd=root)
+    assert r.returncode == 2
+    assert "one GPU only" in r.stderr

@@ -14,14 +14,15 @@ pytestmark = pytest.mark.gpu
 
 DEV = "cuda:0"
 
-# (B, Hg, Wg, heads, d, M, shift, dtype): the M=32, M=8 and general MFMA kernels, the float32
-# kernels and d = 64
+# (B, Hg, Wg, heads, d, M, shift, dtype): the M=32, M=8, M=16 and general MFMA kernels, the
+# float32 kernels and d = 64
 CASES = [
     (1, 64, 64, 2, 32, 32, 16, "bf16"),
     (2, 32, 32, 3, 32, 8, 0, "bf16"),
     (1, 24, 24, 2, 32, 12, 5, "bf16"),
     (1, 16, 16, 2, 32, 8, 3, "f32"),
     (1, 14, 14, 2, 64, 7, 3, "bf16"),
+    (1, 32, 48, 2, 32, 16, 8, "bf16"),
 ]
 IDS = ["B{}_{}x{}_h{}_d{}_M{}_s{}_{}".format(*c) for c in CASES]
 

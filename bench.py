@@ -326,8 +326,11 @@ def main():
         ev[i][2].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    fwd_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / K
-    bwd_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / K
+    fwd_each = sorted(e[0].elapsed_time(e[1]) for e in ev)
+    bwd_each = sorted(e[1].elapsed_time(e[2]) for e in ev)
+    step_each = sorted(e[0].elapsed_time(e[2]) for e in ev)
+    fwd_ms = sum(fwd_each) / K
+    bwd_ms = sum(bwd_each) / K
 
     N = M * M
     nwh = w["B"] * (w["Hg"] // M) * (w["Wg"] // M) * w["heads"]
@@ -386,6 +389,10 @@ def main():
                    "flops_per_step": step_flops},
         "fwd_ms": round(fwd_ms, 4),
         "bwd_ms": round(bwd_ms, 4),
+        # per-step event times of the timed steps: median and minimum (the means are above)
+        "step_ms_median_min": [round(step_each[K // 2], 4), round(step_each[0], 4)],
+        "fwd_ms_median_min": [round(fwd_each[K // 2], 4), round(fwd_each[0], 4)],
+        "bwd_ms_median_min": [round(bwd_each[K // 2], 4), round(bwd_each[0], 4)],
         "fwd_tflops": round(fwd_flops / (fwd_ms * 1e-3) / 1e12, 2) if args.only != "bwd" else None,
         "bwd_tflops": round(bwd_flops / (bwd_ms * 1e-3) / 1e12, 2) if args.only != "fwd" else None,
         "window_heads_per_s": round(nwh / (ms_per_step * 1e-3), 1),

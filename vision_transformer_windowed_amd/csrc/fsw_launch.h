@@ -52,7 +52,7 @@ int64_t bwd_scalar_partials(const Geom& g);
 
 // bf16 MFMA paths (d == 32, M <= 32).
 hipError_t launch_fwd_mfma(const FwdArgs& a, hipStream_t st);
-// M = 8 windows: one wave per window-head, persistent with register prefetch.
+// M = 8 windows: one wave per window-head.
 bool fwd_m8_supported(const Geom& g);
 hipError_t launch_fwd_m8(const FwdArgs& a, hipStream_t st);
 hipError_t launch_bwd_mfma(const BwdArgs& a, hipStream_t st);

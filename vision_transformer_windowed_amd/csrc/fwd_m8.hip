@@ -76,22 +76,37 @@ __device__ __forceinline__ uint4 m8_rotate(uint4 raw, const float* sn, const flo
   return pack8_op(x, H16);
 }
 
-// Sum of squares of the 16 channels a lane holds for one token (halves add across h afterwards).
+// Sum of squares of the 16 channels a lane holds for one token (halves add across h afterwards):
+// bf16 pair dot products on the raw words (the products are exact in float32).
 __device__ __forceinline__ float m8_norm2(uint4 a, uint4 b) {
-  float x[8], y[8], s = 0.f;
-  unpack8(a, x);
-  unpack8(b, y);
+  const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+  float s0 = 0.f, s1 = 0.f;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) s = __builtin_fmaf(x[e], x[e], __builtin_fmaf(y[e], y[e], s));
-  return s;
+  for (int e = 0; e < 8; e += 2) {
+    s0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w[e]), __builtin_bit_cast(bf16x2_t, w[e]), s0,
+                                         false);
+    s1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w[e + 1]),
+                                         __builtin_bit_cast(bf16x2_t, w[e + 1]), s1, false);
+  }
+  return s0 + s1;
+}
+
+// x of lane l plus x of lane l ^ 32, in both lanes (v_permlane32_swap exchanges the wave's halves:
+// the two results hold, in each lane, its own value and its partner's).
+__device__ __forceinline__ float halves_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float halves_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
 // Attention of one query tile over the window's two key blocks with softmax reference `ref` (the
 // tile's bound, or a query's exact row maximum); returns l (per lane half) and O^T.
-template <bool H16>
+template <bool H16, bool MASKED>
 __device__ __forceinline__ void m8_tile(const uint4 (&kop)[2][2], uint4 qa, uint4 qb, const uint16_t* vbuf,
-                                        const uint8_t* lab, bool masked, int qlab, int lane, float ref, float& l,
-                                        f32x16_t& o) {
+                                        const uint8_t* lab, int qlab, int lane, float ref, float& l, f32x16_t& o) {
   const int h = lane >> 5;
   f32x16_t zero;
 #pragma unroll
@@ -102,12 +117,17 @@ __device__ __forceinline__ void m8_tile(const uint4 (&kop)[2][2], uint4 qa, uint
     // the reference is subtracted on the VALU (memory-bound path: registers matter more than ALU)
     f32x16_t s = mfma_op<H16>(kop[kb][0], qa, zero);
     s = mfma_op<H16>(kop[kb][1], qb, s);
-    const uint32_t live = masked ? live_bits(lab, kb, h, qlab) : 0xffffu;
     float p[16];
+    if (MASKED) {
+      const uint32_t live = live_bits(lab, kb, h, qlab);
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const float x = __builtin_amdgcn_exp2f(s[e] - ref);
-      p[e] = ((live >> e) & 1u) ? x : 0.f;
+      for (int e = 0; e < 16; ++e) {
+        const float x = __builtin_amdgcn_exp2f(s[e] - ref);
+        p[e] = ((live >> e) & 1u) ? x : 0.f;
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) p[e] = __builtin_amdgcn_exp2f(s[e] - ref);
     }
     uint32_t pk[8];
 #pragma unroll
@@ -126,9 +146,9 @@ __device__ __forceinline__ void m8_tile(const uint4 (&kop)[2][2], uint4 qa, uint
 }
 
 // Exact row maximum of one query tile over the live keys (raw scores, log2 units).
-template <bool H16>
+template <bool H16, bool MASKED>
 __device__ __forceinline__ float m8_rowmax(const uint4 (&kop)[2][2], uint4 qa, uint4 qb, const uint8_t* lab,
-                                           bool masked, int qlab, int lane) {
+                                           int qlab, int lane) {
   const int h = lane >> 5;
   f32x16_t zero;
 #pragma unroll
@@ -138,42 +158,41 @@ __device__ __forceinline__ float m8_rowmax(const uint4 (&kop)[2][2], uint4 qa, u
   for (int kb = 0; kb < 2; ++kb) {
     f32x16_t s = mfma_op<H16>(kop[kb][0], qa, zero);
     s = mfma_op<H16>(kop[kb][1], qb, s);
-    const uint32_t live = masked ? live_bits(lab, kb, h, qlab) : 0xffffu;
+    const uint32_t live = MASKED ? live_bits(lab, kb, h, qlab) : 0xffffu;
 #pragma unroll
     for (int e = 0; e < 16; ++e)
       if ((live >> e) & 1u) m = fmaxf(m, s[e]);
   }
-  m = fmaxf(m, __shfl_xor(m, 32, 64));
-  return m;
+  return halves_max(m);
 }
 
 // Both query tiles: attention, exact-maximum pass when needed, O and LSE stores.
-template <bool H16>
+template <bool H16, bool MASKED>
 __device__ __forceinline__ void m8_attend(const uint4 (&kop)[2][2], const uint4 (&qop)[2][2],
                                           uint16_t* __restrict__ out, float* __restrict__ lse, const Geom& g,
-                                          const WinHead& w, const uint16_t* vbuf, const uint8_t* lab, bool masked,
-                                          float kmax, const float (&qn2)[2], int lane) {
+                                          const WinHead& w, const uint16_t* vbuf, const uint8_t* lab, float kmax,
+                                          const float (&qn2)[2], int lane) {
   const int h = lane >> 5, col = lane & 31;
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
     const int n = t * 32 + col;
     const int qr = n >> 3, qc = n & 7;
-    const int qlab = masked ? lab[n] : 0;
+    const int qlab = MASKED ? lab[n] : 0;
     const float bound = sqrtf(qn2[t]) * kM8QScale * kmax;  // >= every score of this tile (log2 units)
     f32x16_t o;
 #pragma unroll
     for (int e = 0; e < 16; ++e) o[e] = 0.f;
     float l;
-    m8_tile<H16>(kop, qop[t][0], qop[t][1], vbuf, lab, masked, qlab, lane, bound, l, o);
-    float lt = l + __shfl_xor(l, 32, 64);
+    m8_tile<H16, MASKED>(kop, qop[t][0], qop[t][1], vbuf, lab, qlab, lane, bound, l, o);
+    float lt = halves_sum(l);
     float ref = bound;
     if (__builtin_amdgcn_ballot_w64(!(lt >= kM8LowSum)) != 0) {
       // the bound was too loose for some query of the tile: exact maximum, second pass
-      ref = m8_rowmax<H16>(kop, qop[t][0], qop[t][1], lab, masked, qlab, lane);
+      ref = m8_rowmax<H16, MASKED>(kop, qop[t][0], qop[t][1], lab, qlab, lane);
 #pragma unroll
       for (int e = 0; e < 16; ++e) o[e] = 0.f;
-      m8_tile<H16>(kop, qop[t][0], qop[t][1], vbuf, lab, masked, qlab, lane, ref, l, o);
-      lt = l + __shfl_xor(l, 32, 64);
+      m8_tile<H16, MASKED>(kop, qop[t][0], qop[t][1], vbuf, lab, qlab, lane, ref, l, o);
+      lt = halves_sum(l);
     }
     // O = O^T / l (lane: query col, channels 8g + 4h + j), LSE = (ref + log2 l) ln 2
     const int64_t qtok = token_index(g, w.b, w.wy, w.wx, qr, qc);
@@ -204,6 +223,29 @@ __device__ __forceinline__ void m8_operands(const uint4 (&kr)[2][2], const uint4
     kop[t][1] = m8_rotate<H16>(kr[t][1], sn, cs, 1, n & 7, h, 1.f);
     qop[t][0] = m8_rotate<H16>(qr[t][0], sn, cs, 0, n >> 3, h, kM8QScale);
     qop[t][1] = m8_rotate<H16>(qr[t][1], sn, cs, 1, n & 7, h, kM8QScale);
+  }
+}
+
+// Operands and attention of one window-head, dispatched on the operand format and on whether the
+// window holds several Swin regions (only then are scores masked).
+__device__ __forceinline__ void m8_compute(const uint4 (&kr)[2][2], const uint4 (&qr)[2][2], const float* sn,
+                                           const float* cs, uint16_t* __restrict__ out, float* __restrict__ lse,
+                                           const Geom& g, const WinHead& w, const uint16_t* vbuf,
+                                           const uint8_t* lab, bool masked, bool h16, float kmax,
+                                           const float (&qn2)[2], int lane) {
+  uint4 kop[2][2], qop[2][2];
+  if (h16) {
+    m8_operands<true>(kr, qr, sn, cs, lane, kop, qop);
+    if (masked)
+      m8_attend<true, true>(kop, qop, out, lse, g, w, vbuf, lab, kmax, qn2, lane);
+    else
+      m8_attend<true, false>(kop, qop, out, lse, g, w, vbuf, lab, kmax, qn2, lane);
+  } else {
+    m8_operands<false>(kr, qr, sn, cs, lane, kop, qop);
+    if (masked)
+      m8_attend<false, true>(kop, qop, out, lse, g, w, vbuf, lab, kmax, qn2, lane);
+    else
+      m8_attend<false, false>(kop, qop, out, lse, g, w, vbuf, lab, kmax, qn2, lane);
   }
 }
 
@@ -241,40 +283,27 @@ __global__ __launch_bounds__(kM8Waves * 64, 4) void fwd_m8_kernel(const uint16_t
   if (!active) return;
 
   const WinHead w = decode_winhead(g, wh);
-  // Swin region labels of the 64 tokens (one per lane); mask only when the window has several
-  const int lbl = token_label(g, w.wy, w.wx, lane >> 3, lane & 7);
-  const uint32_t labels = uniform_u32(wave_or(1u << lbl));
-  const bool masked = __builtin_popcount(labels) > 1;
-  if (masked) lab[lane] = (uint8_t)lbl;
+  // A window holds several Swin regions exactly when the grid is shifted and the window lies in the
+  // last window row or column; only then are scores masked, by the tokens' region labels.
+  const bool masked = g.shift > 0 && (w.wy == g.nH - 1 || w.wx == g.nW - 1);
+  if (masked) lab[lane] = (uint8_t)token_label(g, w.wy, w.wx, lane >> 3, lane & 7);
   // the wave's V transfers are complete once its vector-memory count drains (the asm also keeps
   // the compiler from moving LDS reads above it)
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
   // norms: |k|^2 max over the 64 keys, |q|^2 max per query tile (rotation keeps norms)
-  float kn0 = m8_norm2(kr[0][0], kr[0][1]);
-  float kn1 = m8_norm2(kr[1][0], kr[1][1]);
-  kn0 += __shfl_xor(kn0, 32, 64);
-  kn1 += __shfl_xor(kn1, 32, 64);
+  const float kn0 = halves_sum(m8_norm2(kr[0][0], kr[0][1]));
+  const float kn1 = halves_sum(m8_norm2(kr[1][0], kr[1][1]));
   const float kmax = sqrtf(wave_max(fmaxf(kn0, kn1)));
   float qn2[2];
 #pragma unroll
-  for (int t = 0; t < 2; ++t) {
-    float qq = m8_norm2(qr[t][0], qr[t][1]);
-    qq += __shfl_xor(qq, 32, 64);
-    qn2[t] = wave_max(qq);
-  }
+  for (int t = 0; t < 2; ++t) qn2[t] = wave_max(halves_sum(m8_norm2(qr[t][0], qr[t][1])));
   const bool h16 = kmax < kF16Limit && sqrtf(fmaxf(qn2[0], qn2[1])) * kM8QScale < kF16Limit;
   const float* sn = tsn + w.h * 128;
   const float* cs = tcs + w.h * 128;
-  uint4 kop[2][2], qop[2][2];
-  if (h16) {
-    m8_operands<true>(kr, qr, sn, cs, lane, kop, qop);
-    m8_attend<true>(kop, qop, out, lse, g, w, vs, lab, masked, kmax, qn2, lane);
-  } else {
-    m8_operands<false>(kr, qr, sn, cs, lane, kop, qop);
-    m8_attend<false>(kop, qop, out, lse, g, w, vs, lab, masked, kmax, qn2, lane);
-  }
+  m8_compute(kr, qr, sn, cs, out, lse, g, w, vs, lab, masked, h16, kmax, qn2, lane);
 }
+
 
 }  // namespace
 

@@ -213,6 +213,20 @@ def test_single_window_shift_is_four_attentions():
     pin_single_window_regions()
 
 
+def test_mixed_region_windows_are_the_last_row_and_column():
+    """The M=8 kernel masks a window only when the grid is shifted and the window lies in the last
+    window row or column (a scalar test instead of a reduction over its tokens' labels).  Checked
+    here against the oracle's region labels on every window of many grids and shifts."""
+    for M in range(1, 11):
+        for nH, nW in ((1, 1), (1, 3), (2, 1), (3, 4)):
+            for s in range(M):
+                lab = oracle.region_labels(nH * M, nW * M, M, s)
+                for wy in range(nH):
+                    for wx in range(nW):
+                        mixed = len(np.unique(lab[wy, wx])) > 1
+                        assert mixed == (s > 0 and (wy == nH - 1 or wx == nW - 1)), (M, nH, nW, s, wy, wx)
+
+
 # ----------------------------------------------------------------------------- invariants
 
 def test_constant_v_gives_constant_output():

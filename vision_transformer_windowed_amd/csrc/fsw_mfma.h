@@ -149,6 +149,33 @@ __device__ __forceinline__ float add_pair(uint32_t pair, float acc) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pair), ones, acc, false);
 }
 
+// x of lane l plus x of lane l ^ 32, in both lanes (v_permlane32_swap exchanges the wave's halves:
+// the two results hold, in each lane, its own value and its partner's).
+__device__ __forceinline__ float halves_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float halves_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+// Sum of squares of the 8 bf16 values packed in t, by bf16 pair dot products (the products are
+// exact in float32).
+__device__ __forceinline__ float norm2_bf16x8(uint4 t, float acc) {
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, t.x), __builtin_bit_cast(bf16x2_t, t.x), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, t.y), __builtin_bit_cast(bf16x2_t, t.y), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, t.z), __builtin_bit_cast(bf16x2_t, t.z), acc, false);
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, t.w), __builtin_bit_cast(bf16x2_t, t.w), acc,
+                                         false);
+}
+
+// Sum over each group of 4 consecutive lanes, in all four (DPP quad permutations).
+__device__ __forceinline__ float quad_sum(float x) {
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xf, 0xf, false));  // [1,0,3,2]
+  return x + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xf, 0xf, false));  // [2,3,0,1]
+}
+
 __device__ __forceinline__ float wave_max(float x) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, 64));

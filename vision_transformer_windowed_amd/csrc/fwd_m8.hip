@@ -11,10 +11,11 @@
 // (lane = key), the 64 queries two B tiles (lane = query).  V travels from HBM into the wave's LDS
 // buffer (global_load_lds, 16 bytes per lane, four lanes per row) and stays row-major for the
 // transposed ds_read_b64_tr_b16 reads of the P.V product.  With 4 KB of LDS per wave, four waves
-// share a SIMD (128 registers each).  The RoPE sin/cos tables of every head are built once per
-// workgroup while the loads are in flight.
+// share a SIMD (at most 128 registers each).  The RoPE sin/cos tables of every head are built once
+// per workgroup while the loads are in flight.
 // The softmax reference is the Cauchy-Schwarz bound max|q^| * max|k~| of the tile, with an
-// exact-maximum recomputation of a tile whose row sums come out below 2^-80.
+// exact-maximum recomputation of a tile whose row sums come out below 2^-80.  Only windows that hold
+// several Swin regions (the last window row and column of a shifted grid) run the masked code.
 #include <algorithm>
 
 #include "fsw_common.h"
@@ -89,17 +90,6 @@ __device__ __forceinline__ float m8_norm2(uint4 a, uint4 b) {
                                          __builtin_bit_cast(bf16x2_t, w[e + 1]), s1, false);
   }
   return s0 + s1;
-}
-
-// x of lane l plus x of lane l ^ 32, in both lanes (v_permlane32_swap exchanges the wave's halves:
-// the two results hold, in each lane, its own value and its partner's).
-__device__ __forceinline__ float halves_sum(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-__device__ __forceinline__ float halves_max(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
 // Attention of one query tile over the window's two key blocks with softmax reference `ref` (the

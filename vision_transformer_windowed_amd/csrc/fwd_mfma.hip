@@ -206,14 +206,14 @@ __device__ __forceinline__ void attend(const FwdSmem& sm, int NB, int lane, bool
   else if (wave_labels != 0)
     pass_general<0, H16>(sm, NB, lane, wave_labels, wave_single, qb0, qb1, qlab, cinit, m, l, o);
   ref = bound;
-  const bool low = qvalid && !(l + __shfl_xor(l, 32, 64) >= kLowSum);
+  const bool low = qvalid && !(halves_sum(l) >= kLowSum);
   if (__builtin_amdgcn_ballot_w64(low) != 0) {
     f32x16_t zero;
 #pragma unroll
     for (int v2 = 0; v2 < 16; ++v2) zero[v2] = 0.f;
     m = -INFINITY;
     pass_general<1, H16>(sm, NB, lane, wave_labels, wave_single, qb0, qb1, qlab, zero, m, l, o);
-    m = fmaxf(m, __shfl_xor(m, 32, 64));
+    m = halves_max(m);
     if (!(m > -INFINITY)) m = 0.f;  // invalid query lanes
     l = 0.f;
 #pragma unroll
@@ -241,17 +241,15 @@ __device__ __forceinline__ float stage_k(const FwdSmem& sm, const uint4 (&kraw)[
     if (key < N) {
       const int rc = split ? (int)sm.rc[key] : (key / M) << 8 | (key - (key / M) * M);
       const int r = rc >> 8, c = rc & 255;
+      ss = norm2_bf16x8(kraw[i], 0.f);
       float x[8];
       unpack8(kraw[i], x);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) ss = __builtin_fmaf(x[e], x[e], ss);
       const int axis = part >> 1;
       rotate8(x, sm.sn, sm.cs, axis, M, axis ? c : r, (part & 1) * 4);
       kr = pack8_op(x, h16);
     }
     *reinterpret_cast<uint4*>(sm.K + (size_t)key * kKStride + part * 8) = kr;
-    ss += __shfl_xor(ss, 1, 64);
-    ss += __shfl_xor(ss, 2, 64);
+    ss = quad_sum(ss);  // the 4 parts of the key
     kmax2 = fmaxf(kmax2, ss);
   }
   return kmax2;
@@ -402,12 +400,7 @@ __global__ __launch_bounds__(NWAVES * 64, NWAVES >= 8 ? 4 : 1) void fwd_mfma_ker
   float qn2max[QBM];
 #pragma unroll
   for (int qb = 0; qb < QBM; ++qb) {
-    float x[8], y[8], qn2 = 0.f;
-    unpack8(qraw[qb][0], x);
-    unpack8(qraw[qb][1], y);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) qn2 = __builtin_fmaf(x[e], x[e], __builtin_fmaf(y[e], y[e], qn2));
-    qn2 += __shfl_xor(qn2, 32, 64);
+    const float qn2 = halves_sum(norm2_bf16x8(qraw[qb][1], norm2_bf16x8(qraw[qb][0], 0.f)));
     qn2max[qb] = wave_max(qn2) * (qscale * qscale);
   }
   kmax2 = wave_max(kmax2);
@@ -490,7 +483,7 @@ __global__ __launch_bounds__(NWAVES * 64, NWAVES >= 8 ? 4 : 1) void fwd_mfma_ker
     // the next block's query loads go out before this block's epilogue
     if (qb + 1 < QBM) load_q(qb + 1, qraw[qb + 1][0], qraw[qb + 1][1]);  // zeros past the last block
     // 5. epilogue: O = O^T / l (lane: query col, channels 8g + 4h + j), LSE = (ref + log2 l) ln 2
-    const float lt = l + __shfl_xor(l, 32, 64);
+    const float lt = halves_sum(l);
     if (qvalid) {
       const int64_t qtok = tok_of(g, w, M, qr, qc);
       const float inv = 1.f / lt;

@@ -224,6 +224,8 @@ BWD_SMALL = [
     (1, 33, 33, 1, 32, 11, 4, "bf16"),
     (1, 10, 10, 2, 32, 5, 2, "bf16"),
     (1, 16, 16, 2, 16, 8, 4, "bf16"),
+    (1, 32, 32, 2, 32, 16, 15, "bf16"),
+    (2, 16, 32, 3, 32, 16, 1, "bf16"),
     (1, 32, 48, 2, 32, 16, 8, "bf16"),
     (1, 64, 96, 2, 32, 32, 16, "bf16"),
     (1, 16, 16, 20, 32, 8, 3, "bf16"),

@@ -246,15 +246,14 @@ __global__ __launch_bounds__(kPreThreads) void bwd_pre_kernel(const uint16_t* __
   }
 }
 
-// Both main kernels stream the window's other side through LDS in chunks of up to kCh tokens:
+// Both main kernels stream the window's other side through LDS in chunks of up to chunk_max(MT)
+// tokens:
 //   load (global -> registers, chunk c + 1)  |  compute on chunk c from LDS
 //   barrier; registers -> LDS (RoPE, scaling, operand format); barrier
 // Block summaries (which labels a 32-token block holds) are double-buffered, so the buffer that
 // the next chunk's stores OR into was cleared during the previous chunk's stores.
 // Tile rows use the swizzled 64-byte layout (srow), so row and transposed operand reads are free
 // of LDS bank conflicts, and every operand address is a per-lane base plus a constant.
-
-__host__ __device__ inline int items_per_thread(int nt) { return (kCh * 4 + nt - 1) / nt; }
 
 // ---------------------------------------------------------------------------------------- dQ
 
@@ -264,13 +263,13 @@ struct DqSmem {
   float* sn;
   float* cs;
   float* red;     // [NW * 16]
-  uint32_t* blk;  // [2][kCh / 32]
-  uint8_t* lab;   // [kCh]
+  uint32_t* blk;  // [2][chunk / 32]
+  uint8_t* lab;   // [chunk]
 };
 template <int NW>
-__host__ __device__ inline size_t dq_smem(int NP, int M) {
-  const int CH = chunk_len(NP);
-  return (size_t)CH * 32 * 2 * 2 + (size_t)2 * 2 * M * 8 * 4 + NW * 16 * 4 + 2 * (kCh / 32) * 4 + kCh;
+__host__ __device__ inline size_t dq_smem(int NP, int M, int cmax) {
+  const int CH = chunk_len(NP, cmax);
+  return (size_t)CH * 32 * 2 * 2 + (size_t)2 * 2 * M * 8 * 4 + NW * 16 * 4 + 2 * (cmax / 32) * 4 + cmax;
 }
 
 // Each wave owns S sets of 32 queries (lane = query within a set).  The sets share every LDS
@@ -284,12 +283,13 @@ __device__ inline void dq_body(const uint16_t* __restrict__ q, const uint16_t* _
                                float* __restrict__ partials, const Geom& g, int nb, int NP, const DqSmem& sm,
                                const WinHead& w, int64_t wh, int qblock) {
   constexpr int D = 32;
+  constexpr int KC = chunk_max(MT);
   constexpr int NT = NW * 64;
-  constexpr int IPT = (kCh * 4 + NT - 1) / NT;
+  constexpr int IPT = (KC * 4 + NT - 1) / NT;
   const int M = MT > 0 ? MT : g.M;
   const int N = M * M;
   const WinOrder wo = win_order(g, M, w.wy, w.wx);
-  const int CH = chunk_len(NP);
+  const int CH = chunk_len(NP, KC);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int h = lane >> 5, col = lane & 31;
   const int64_t xs = g.xs;
@@ -385,17 +385,17 @@ __device__ inline void dq_body(const uint16_t* __restrict__ q, const uint16_t* _
         }
         *reinterpret_cast<uint4*>(sm.K + srow(n, part)) = kr;
         *reinterpret_cast<uint4*>(sm.V + srow(n, part)) = iv[i];
-        if (part == 0) sm.lab[n] = chunk_label(g, w, wo, kn, sm.blk + buf * (kCh / 32), n);
+        if (part == 0) sm.lab[n] = chunk_label(g, w, wo, kn, sm.blk + buf * (KC / 32), n);
       }
     }
-    if (tid < kCh / 32) sm.blk[(buf ^ 1) * (kCh / 32) + tid] = 0;
+    if (tid < KC / 32) sm.blk[(buf ^ 1) * (KC / 32) + tid] = 0;
     __syncthreads();
     if (cn < NP) load_chunk(cn);
     if (wave_labels == 0) continue;
-    uint32_t info4[kCh / 32];
+    uint32_t info4[KC / 32];
 #pragma unroll
-    for (int i = 0; i < kCh / 128; ++i) {
-      const uint4 bw = *reinterpret_cast<const uint4*>(sm.blk + buf * (kCh / 32) + 4 * i);
+    for (int i = 0; i < KC / 128; ++i) {
+      const uint4 bw = *reinterpret_cast<const uint4*>(sm.blk + buf * (KC / 32) + 4 * i);
       info4[4 * i] = uniform(bw.x);
       info4[4 * i + 1] = uniform(bw.y);
       info4[4 * i + 2] = uniform(bw.z);
@@ -403,7 +403,7 @@ __device__ inline void dq_body(const uint16_t* __restrict__ q, const uint16_t* _
     }
     const int nblk = min(CH, NP - c0) >> 5;
 #pragma unroll
-    for (int kb = 0; kb < kCh / 32; ++kb) {
+    for (int kb = 0; kb < KC / 32; ++kb) {
       if (kb >= nblk) break;
       const uint32_t info = info4[kb];
       const uint32_t bl = info & 0x1ffu;
@@ -478,9 +478,10 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_mfma_kernel(
     const float* __restrict__ scal, const float* __restrict__ th_row, const float* __restrict__ th_col,
     uint16_t* __restrict__ dq, float* __restrict__ partials, Geom g, int nb, int NP) {
   extern __shared__ __align__(16) unsigned char smem_raw[];
+  constexpr int KC = chunk_max(MT);
   if constexpr (MT > 0) NP = (MT * MT + 31) / 32 * 32;  // compile-time chunk geometry
   const int M = MT > 0 ? MT : g.M;
-  const int CH = chunk_len(NP);
+  const int CH = chunk_len(NP, KC);
   DqSmem sm;
   sm.K = reinterpret_cast<uint16_t*>(smem_raw);
   sm.V = sm.K + CH * 32;
@@ -488,11 +489,11 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_mfma_kernel(
   sm.cs = sm.sn + 2 * M * 8;
   sm.red = sm.cs + 2 * M * 8;
   sm.blk = reinterpret_cast<uint32_t*>(sm.red + NW * 16);
-  sm.lab = reinterpret_cast<uint8_t*>(sm.blk + 2 * (kCh / 32));
+  sm.lab = reinterpret_cast<uint8_t*>(sm.blk + 2 * (KC / 32));
   const int64_t lb = xcd_order(blockIdx.x, gridDim.x);
   const int64_t wh = lb / nb;
   const WinHead w = decode_winhead(g, wh);
-  if (threadIdx.x < 2 * (kCh / 32)) sm.blk[threadIdx.x] = 0;
+  if (threadIdx.x < 2 * (KC / 32)) sm.blk[threadIdx.x] = 0;
   fill_table(sm.sn, sm.cs, th_row, th_col, w.h, M, threadIdx.x, NW * 64);
   __syncthreads();
   if (window_h16(scal, wh))
@@ -507,18 +508,18 @@ struct DkdvSmem {
   uint16_t* Q;    // [CH] swizzled rows: rotated, scaled Q^ (operand format)
   uint16_t* G;    // [CH] swizzled rows: bf16 dO
   uint16_t* Gs;   // [CH] swizzled rows: g * dO (operand format)
-  float* L;       // [kCh] -LSE log2(e)
-  float* Dl;      // [kCh] -tau Delta
+  float* L;       // [chunk] -LSE log2(e)
+  float* Dl;      // [chunk] -tau Delta
   float* sn;
   float* cs;
   float* red;     // [NW * 16]
-  uint32_t* blk;  // [2][kCh / 32]
-  uint8_t* lab;   // [kCh]
+  uint32_t* blk;  // [2][chunk / 32]
+  uint8_t* lab;   // [chunk]
 };
 template <int NW>
-__host__ __device__ inline size_t dkdv_smem(int NP, int M) {
-  const int CH = chunk_len(NP);
-  return (size_t)CH * 32 * 2 * 3 + kCh * 4 * 2 + (size_t)2 * 2 * M * 8 * 4 + NW * 16 * 4 + 2 * (kCh / 32) * 4 + kCh;
+__host__ __device__ inline size_t dkdv_smem(int NP, int M, int cmax) {
+  const int CH = chunk_len(NP, cmax);
+  return (size_t)CH * 32 * 2 * 3 + cmax * 4 * 2 + (size_t)2 * 2 * M * 8 * 4 + NW * 16 * 4 + 2 * (cmax / 32) * 4 + cmax;
 }
 
 // Each wave owns S sets of 32 keys (lane = key within a set); the sets share the LDS reads of the
@@ -531,12 +532,13 @@ __device__ inline void dkdv_body(const uint16_t* __restrict__ q, const uint16_t*
                                  float* __restrict__ partials, const Geom& g, int nb, int NP, const DkdvSmem& sm,
                                  const WinHead& w, int64_t wh, int kblock) {
   constexpr int D = 32;
+  constexpr int KC = chunk_max(MT);
   constexpr int NT = NW * 64;
-  constexpr int IPT = (kCh * 4 + NT - 1) / NT;
+  constexpr int IPT = (KC * 4 + NT - 1) / NT;
   const int M = MT > 0 ? MT : g.M;
   const int N = M * M;
   const WinOrder wo = win_order(g, M, w.wy, w.wx);
-  const int CH = chunk_len(NP);
+  const int CH = chunk_len(NP, KC);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int h = lane >> 5, col = lane & 31;
   const int64_t xs = g.xs;
@@ -637,18 +639,18 @@ __device__ inline void dkdv_body(const uint16_t* __restrict__ q, const uint16_t*
         if (part == 0) {
           sm.L[n] = -il[i] * kLog2e;
           sm.Dl[n] = -id[i] * ds_scale;
-          sm.lab[n] = chunk_label(g, w, wo, qn, sm.blk + buf * (kCh / 32), n);
+          sm.lab[n] = chunk_label(g, w, wo, qn, sm.blk + buf * (KC / 32), n);
         }
       }
     }
-    if (tid < kCh / 32) sm.blk[(buf ^ 1) * (kCh / 32) + tid] = 0;
+    if (tid < KC / 32) sm.blk[(buf ^ 1) * (KC / 32) + tid] = 0;
     __syncthreads();
     if (cn < NP) load_chunk(cn);
     if (wave_labels == 0) continue;
-    uint32_t info4[kCh / 32];
+    uint32_t info4[KC / 32];
 #pragma unroll
-    for (int i = 0; i < kCh / 128; ++i) {
-      const uint4 bw = *reinterpret_cast<const uint4*>(sm.blk + buf * (kCh / 32) + 4 * i);
+    for (int i = 0; i < KC / 128; ++i) {
+      const uint4 bw = *reinterpret_cast<const uint4*>(sm.blk + buf * (KC / 32) + 4 * i);
       info4[4 * i] = uniform(bw.x);
       info4[4 * i + 1] = uniform(bw.y);
       info4[4 * i + 2] = uniform(bw.z);
@@ -656,7 +658,7 @@ __device__ inline void dkdv_body(const uint16_t* __restrict__ q, const uint16_t*
     }
     const int nblk = min(CH, NP - c0) >> 5;
 #pragma unroll
-    for (int qb = 0; qb < kCh / 32; ++qb) {
+    for (int qb = 0; qb < KC / 32; ++qb) {
       if (qb >= nblk) break;
       const uint32_t info = info4[qb];
       const uint32_t bl = info & 0x1ffu;
@@ -771,24 +773,25 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dkdv_mfma_kernel(
     const float* __restrict__ scal, const float* __restrict__ th_row, const float* __restrict__ th_col,
     uint16_t* __restrict__ dk, uint16_t* __restrict__ dv, float* __restrict__ partials, Geom g, int nb, int NP) {
   extern __shared__ __align__(16) unsigned char smem_raw[];
+  constexpr int KC = chunk_max(MT);
   if constexpr (MT > 0) NP = (MT * MT + 31) / 32 * 32;  // compile-time chunk geometry
   const int M = MT > 0 ? MT : g.M;
-  const int CH = chunk_len(NP);
+  const int CH = chunk_len(NP, KC);
   DkdvSmem sm;
   sm.Q = reinterpret_cast<uint16_t*>(smem_raw);
   sm.G = sm.Q + CH * 32;
   sm.Gs = sm.G + CH * 32;
   sm.L = reinterpret_cast<float*>(sm.Gs + CH * 32);
-  sm.Dl = sm.L + kCh;
-  sm.sn = sm.Dl + kCh;
+  sm.Dl = sm.L + KC;
+  sm.sn = sm.Dl + KC;
   sm.cs = sm.sn + 2 * M * 8;
   sm.red = sm.cs + 2 * M * 8;
   sm.blk = reinterpret_cast<uint32_t*>(sm.red + NW * 16);
-  sm.lab = reinterpret_cast<uint8_t*>(sm.blk + 2 * (kCh / 32));
+  sm.lab = reinterpret_cast<uint8_t*>(sm.blk + 2 * (KC / 32));
   const int64_t lb = xcd_order(blockIdx.x, gridDim.x);
   const int64_t wh = lb / nb;
   const WinHead w = decode_winhead(g, wh);
-  if (threadIdx.x < 2 * (kCh / 32)) sm.blk[threadIdx.x] = 0;
+  if (threadIdx.x < 2 * (KC / 32)) sm.blk[threadIdx.x] = 0;
   fill_table(sm.sn, sm.cs, th_row, th_col, w.h, M, threadIdx.x, NW * 64);
   __syncthreads();
   if (window_h16(scal, wh))
@@ -831,12 +834,12 @@ hipError_t launch_main(const BwdArgs& a, hipStream_t st) {
   const int nb = (int)blocks_per_windowhead(g);
   const int64_t blocks = nwh * nb;
   hipLaunchKernelGGL((bwd_dkdv_mfma_kernel<NW, MT, S>), dim3((unsigned)blocks), dim3(NW * 64),
-                     dkdv_smem<NW>(NP, g.M), st, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
+                     dkdv_smem<NW>(NP, g.M, chunk_max(MT)), st, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
                      (const uint16_t*)a.dout, a.lse, a.delta, a.scal, a.th_row, a.th_col, (uint16_t*)a.dk,
                      (uint16_t*)a.dv, a.partials, g, nb, NP);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((bwd_dq_mfma_kernel<NW, MT, S>), dim3((unsigned)blocks), dim3(NW * 64), dq_smem<NW>(NP, g.M),
+  hipLaunchKernelGGL((bwd_dq_mfma_kernel<NW, MT, S>), dim3((unsigned)blocks), dim3(NW * 64), dq_smem<NW>(NP, g.M, chunk_max(MT)),
                      st, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (const uint16_t*)a.dout,
                      a.lse, a.delta, a.scal, a.th_row, a.th_col, (uint16_t*)a.dq, a.partials, g, nb, NP);
   e = hipGetLastError();

@@ -7,12 +7,15 @@
 
 namespace fsw {
 
-constexpr int kCh = 128;  // tokens per LDS chunk (a multiple of 128)
+constexpr int kCh = 128;  // tokens per LDS chunk by default (chunk lengths are multiples of 128)
 
 __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 __device__ __forceinline__ uint32_t uniform(uint32_t x) { return (uint32_t)__builtin_amdgcn_readfirstlane((int)x); }
 
-__host__ __device__ constexpr int chunk_len(int NP) { return NP < kCh ? NP : kCh; }
+// Chunk length of the kernels specialised for window size MT (0: run-time size): a window of 256
+// tokens (M = 16) streams as one chunk, so each workgroup passes one pair of barriers, not two.
+__host__ __device__ constexpr int chunk_max(int MT) { return MT == 16 ? 256 : kCh; }
+__host__ __device__ constexpr int chunk_len(int NP, int cmax = kCh) { return NP < cmax ? NP : cmax; }
 
 template <bool H16>
 __device__ __forceinline__ uint32_t pack_op2(float a, float b) {

@@ -5,17 +5,19 @@
 // Efficient Attention": Abstract; Figure 1(B)).  Small windows move ~12 KB per window-head for
 // ~0.5 MFLOP, so this path is bound by HBM and by load latency, not by the matrix cores.
 //
-// One wave owns one window-head.  Q and K are loaded straight into the registers that hold them as
-// MFMA operands (lane = token, the two 16-byte channel chunks a lane half needs; the two halves
-// together read each 64-byte head row whole) and rotated there: the 64 keys become two A blocks
-// (lane = key), the 64 queries two B tiles (lane = query).  V travels from HBM into the wave's LDS
-// buffer (global_load_lds, 16 bytes per lane, four lanes per row) and stays row-major for the
-// transposed ds_read_b64_tr_b16 reads of the P.V product.  With 4 KB of LDS per wave, four waves
-// share a SIMD (at most 128 registers each).  The RoPE sin/cos tables of every head are built once
-// per workgroup while the loads are in flight.
-// The softmax reference is the Cauchy-Schwarz bound max|q^| * max|k~| of the tile, with an
-// exact-maximum recomputation of a tile whose row sums come out below 2^-80.  Only windows that hold
-// several Swin regions (the last window row and column of a shifted grid) run the masked code.
+// One wave owns one window-head and computes it with 16x16x32 MFMA products, which keep the
+// accumulators small (4 registers per 16x16 block): the kernel fits 95 registers, so four waves
+// share a SIMD.  Lane (c16, g4) = (lane % 16, lane / 16) loads channels 8 g4 .. 8 g4 + 7 of token
+// 16 b + c16 of K and of Q (b = 0..3) straight into the registers that hold them as operands and
+// rotates them there.  V travels from HBM into the wave's LDS buffer (global_load_lds, 16 bytes
+// per lane, four lanes per row) and stays row-major for the transposed ds_read_b64_tr_b16 reads of
+// the P.V product.  The queries go in four 16-query blocks: S^T of two 16-key blocks at a time,
+// P = exp2(S^T - ref) taken straight from those accumulators as the B operand of P.V (in a key
+// order the V operand follows), O^T in two 16-channel blocks.  The RoPE sin/cos tables of every
+// head are built once per workgroup while the loads are in flight.
+// The softmax reference is the Cauchy-Schwarz bound max|q^| * max|k~| of the block, with an
+// exact-maximum recomputation of a block whose row sums come out below 2^-80.  Only windows that
+// hold several Swin regions (the last window row and column of a shifted grid) run the masked code.
 #include <algorithm>
 
 #include "fsw_common.h"
@@ -32,28 +34,36 @@ constexpr int kM8WaveLds = 64 * 32 + 32;                    // per wave, 16-bit 
 constexpr float kM8LowSum = 8.271806125530277e-25f;         // 2^-80
 constexpr float kM8QScale = kLog2e * 0.17677669529663687f;  // log2(e) / sqrt(32)
 
-__device__ __forceinline__ uint32_t uniform_u32(uint32_t x) {
-  return (uint32_t)__builtin_amdgcn_readfirstlane((int)x);
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+// 16x16x32 products (gfx950): A[i][k] sits in lane i + 16 (k / 8), element k % 8; B[k][j] in lane
+// j + 16 (k / 8), element k % 8; D[i][j] in lane j + 16 (i / 4), element i % 4.
+template <bool H16>
+__device__ __forceinline__ f32x4_t mfma16_op(uint4 a, uint4 b, const f32x4_t& c) {
+  if constexpr (H16)
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a), __builtin_bit_cast(f16x8_t, b), c,
+                                                  0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b),
+                                                   c, 0, 0, 0);
 }
 
-// Issue every load of window-head wh.  K and Q: the lane's token n = t * 32 + (lane % 32) of tile
-// t, channel chunks h and 2 + h (h = lane / 32), into registers.  V: HBM -> LDS, instruction i
-// moving 64 x 16 bytes into slots i*64 .. i*64+63 (lane L's bytes land in slot i*64 + L: row
-// (i*64+L)/4, 16-byte chunk (i*64+L)%4), row-major.
+// Issue every load of window-head wh.  Lane (c16, g4) = (lane % 16, lane / 16): K and Q of token
+// 16 b + c16 of block b = 0..3, channels 8 g4 .. 8 g4 + 7 (16 bytes), into the registers that hold
+// them as operands.  V: HBM -> LDS, instruction i moving 64 x 16 bytes into slots i*64 .. i*64+63
+// (lane L's bytes land in slot i*64 + L: row (i*64+L)/4, 16-byte chunk (i*64+L)%4), row-major.
 __device__ __forceinline__ void m8_issue(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                                          const uint16_t* __restrict__ v, const Geom& g, int64_t wh, int lane,
-                                         uint16_t* vs, uint4 (&kr)[2][2], uint4 (&qr)[2][2]) {
+                                         uint16_t* vs, uint4 (&kr)[4], uint4 (&qr)[4]) {
   typedef __attribute__((address_space(3))) void lds_t;
   const WinHead w = decode_winhead(g, wh);
-  const int h = lane >> 5, col = lane & 31;
+  const int g4 = lane >> 4, c16 = lane & 15;
 #pragma unroll
-  for (int t = 0; t < 2; ++t) {
-    const int n = t * 32 + col;
-    const int64_t base = token_index(g, w.b, w.wy, w.wx, n >> 3, n & 7) * g.xs + w.h * 32;
-    kr[t][0] = *reinterpret_cast<const uint4*>(k + base + 8 * h);
-    kr[t][1] = *reinterpret_cast<const uint4*>(k + base + 16 + 8 * h);
-    qr[t][0] = *reinterpret_cast<const uint4*>(q + base + 8 * h);
-    qr[t][1] = *reinterpret_cast<const uint4*>(q + base + 16 + 8 * h);
+  for (int b = 0; b < 4; ++b) {
+    const int n = b * 16 + c16;
+    const int64_t base = token_index(g, w.b, w.wy, w.wx, n >> 3, n & 7) * g.xs + w.h * 32 + 8 * g4;
+    kr[b] = *reinterpret_cast<const uint4*>(k + base);
+    qr[b] = *reinterpret_cast<const uint4*>(q + base);
   }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -64,178 +74,148 @@ __device__ __forceinline__ void m8_issue(const uint16_t* __restrict__ q, const u
   }
 }
 
-// 8 channels of one lane, rotated with the head's table (row axis: part 0, column axis: part 1;
-// pairs 4h .. 4h+3), scaled, packed to the operand format.
+// The lane's 8 channels 8 g4 .. 8 g4 + 7 of token n, rotated with the head's table (channels
+// [0, 16) by the row position, [16, 32) by the column position), scaled, in the operand format.
 template <bool H16>
-__device__ __forceinline__ uint4 m8_rotate(uint4 raw, const float* sn, const float* cs, int axis, int pos, int h,
-                                           float scale) {
+__device__ __forceinline__ uint4 m8_operand(uint4 raw, const float* sn, const float* cs, int n, int g4, float scale) {
   float x[8];
   unpack8(raw, x);
-  rotate8(x, sn, cs, axis, 8, pos, 4 * h);
+  const int axis = g4 >> 1;
+  rotate8(x, sn, cs, axis, 8, axis ? (n & 7) : (n >> 3), 4 * (g4 & 1));
 #pragma unroll
   for (int e = 0; e < 8; ++e) x[e] *= scale;
   return pack8_op(x, H16);
 }
 
-// Sum of squares of the 16 channels a lane holds for one token (halves add across h afterwards):
-// bf16 pair dot products on the raw words (the products are exact in float32).
-__device__ __forceinline__ float m8_norm2(uint4 a, uint4 b) {
-  const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-  float s0 = 0.f, s1 = 0.f;
-#pragma unroll
-  for (int e = 0; e < 8; e += 2) {
-    s0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w[e]), __builtin_bit_cast(bf16x2_t, w[e]), s0,
-                                         false);
-    s1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w[e + 1]),
-                                         __builtin_bit_cast(bf16x2_t, w[e + 1]), s1, false);
-  }
-  return s0 + s1;
+// Sum and maximum over the four lanes that share lane % 16 (the parts of one token or query).
+__device__ __forceinline__ float groups_sum(float x) { return halves_sum(x + __shfl_xor(x, 16, 64)); }
+__device__ __forceinline__ float groups_max(float x) { return halves_max(fmaxf(x, __shfl_xor(x, 16, 64))); }
+
+// A operand of the P.V product for key group kg (32 keys) and channel block cb: lane (c16, g4)
+// holds channel 16 cb + c16 of keys 32 kg + 4 g4 + {0..3} and 32 kg + 16 + 4 g4 + {0..3}, read
+// transposed from the row-major V rows (each 16-lane group transposes a 4 x 16 block).
+__device__ __forceinline__ uint4 m8_vt(const uint16_t* vbuf, int kg, int cb, int lane) {
+  const int g4 = lane >> 4, c16 = lane & 15;
+  const uint16_t* p = vbuf + (kg * 32 + 4 * g4 + (c16 >> 2)) * 32 + cb * 16 + 4 * (c16 & 3);
+  const uint2 lo = lds_read_tr16(p);
+  const uint2 hi = lds_read_tr16(p + 16 * 32);
+  return make_uint4(lo.x, lo.y, hi.x, hi.y);
 }
 
-// Attention of one query tile over the window's two key blocks with softmax reference `ref` (the
-// tile's bound, or a query's exact row maximum); returns l (per lane half) and O^T.
-template <bool H16, bool MASKED>
-__device__ __forceinline__ void m8_tile(const uint4 (&kop)[2][2], uint4 qa, uint4 qb, const uint16_t* vbuf,
-                                        const uint8_t* lab, int qlab, int lane, float ref, float& l, f32x16_t& o) {
-  const int h = lane >> 5;
-  f32x16_t zero;
+// Live mask of the lane's 4 scores in key block kb (keys 16 kb + 4 g4 + {0..3}) for label qlab.
+__device__ __forceinline__ uint32_t m8_live4(const uint8_t* lab, int kb, int g4, int qlab) {
+  const uint32_t wd = *reinterpret_cast<const uint32_t*>(lab + kb * 16 + 4 * g4);
+  uint32_t bits = 0;
 #pragma unroll
-  for (int e = 0; e < 16; ++e) zero[e] = 0.f;
+  for (int e = 0; e < 4; ++e)
+    if (((wd >> (8 * e)) & 0xff) == (uint32_t)qlab) bits |= 1u << e;
+  return bits;
+}
+
+// Attention of one 16-query block over the window's 64 keys with softmax reference `ref`: scores
+// S^T of two 16-key blocks at a time, P = exp2(S^T - ref) straight into the B operand of the P.V
+// product (key slots 8 g4 + {0..3} from the first block, 8 g4 + {4..7} from the second, the same
+// order as the V operand), l per lane (over its 16 keys) and O^T (two 16-channel blocks).
+template <bool H16, bool MASKED>
+__device__ __forceinline__ void m8_block(const uint4 (&kop)[4], uint4 qop, const uint16_t* vbuf, const uint8_t* lab,
+                                         int qlab, int lane, float ref, float& l, f32x4_t (&o)[2]) {
+  const int g4 = lane >> 4;
+  const f32x4_t zero = {0.f, 0.f, 0.f, 0.f};
   float la = 0.f, lb = 0.f;
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb) {
-    // the reference is subtracted on the VALU (memory-bound path: registers matter more than ALU)
-    f32x16_t s = mfma_op<H16>(kop[kb][0], qa, zero);
-    s = mfma_op<H16>(kop[kb][1], qb, s);
-    float p[16];
+  for (int kg = 0; kg < 2; ++kg) {
+    const f32x4_t s0 = mfma16_op<H16>(kop[2 * kg], qop, zero);
+    const f32x4_t s1 = mfma16_op<H16>(kop[2 * kg + 1], qop, zero);
+    float p[8];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      p[e] = __builtin_amdgcn_exp2f(s0[e] - ref);
+      p[4 + e] = __builtin_amdgcn_exp2f(s1[e] - ref);
+    }
     if (MASKED) {
-      const uint32_t live = live_bits(lab, kb, h, qlab);
+      const uint32_t b0 = m8_live4(lab, 2 * kg, g4, qlab), b1 = m8_live4(lab, 2 * kg + 1, g4, qlab);
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const float x = __builtin_amdgcn_exp2f(s[e] - ref);
-        p[e] = ((live >> e) & 1u) ? x : 0.f;
+      for (int e = 0; e < 4; ++e) {
+        p[e] = ((b0 >> e) & 1u) ? p[e] : 0.f;
+        p[4 + e] = ((b1 >> e) & 1u) ? p[4 + e] : 0.f;
       }
-    } else {
-#pragma unroll
-      for (int e = 0; e < 16; ++e) p[e] = __builtin_amdgcn_exp2f(s[e] - ref);
     }
-    uint32_t pk[8];
+    uint32_t pk[4];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) pk[e] = pack2(p[2 * e], p[2 * e + 1]);
+    for (int e = 0; e < 4; ++e) pk[e] = pack2(p[2 * e], p[2 * e + 1]);
+    la = add_pair(pk[0], la);
+    lb = add_pair(pk[1], lb);
+    la = add_pair(pk[2], la);
+    lb = add_pair(pk[3], lb);
+    const uint4 pb = make_uint4(pk[0], pk[1], pk[2], pk[3]);
 #pragma unroll
-    for (int e = 0; e < 8; e += 2) {
-      la = add_pair(pk[e], la);
-      lb = add_pair(pk[e + 1], lb);
-    }
-    o = mfma32x32x16(as_bf16x8(tr_operand(vbuf, 32, kb * 32, lane)), as_bf16x8(make_uint4(pk[0], pk[1], pk[2], pk[3])),
-                     o);
-    o = mfma32x32x16(as_bf16x8(tr_operand(vbuf, 32, kb * 32 + 16, lane)),
-                     as_bf16x8(make_uint4(pk[4], pk[5], pk[6], pk[7])), o);
+    for (int cb = 0; cb < 2; ++cb) o[cb] = mfma16_op<false>(m8_vt(vbuf, kg, cb, lane), pb, o[cb]);
   }
   l = la + lb;
 }
 
-// Exact row maximum of one query tile over the live keys (raw scores, log2 units).
+// Exact row maximum of one 16-query block over the live keys (raw scores, log2 units).
 template <bool H16, bool MASKED>
-__device__ __forceinline__ float m8_rowmax(const uint4 (&kop)[2][2], uint4 qa, uint4 qb, const uint8_t* lab,
-                                           int qlab, int lane) {
-  const int h = lane >> 5;
-  f32x16_t zero;
-#pragma unroll
-  for (int e = 0; e < 16; ++e) zero[e] = 0.f;
+__device__ __forceinline__ float m8_rowmax(const uint4 (&kop)[4], uint4 qop, const uint8_t* lab, int qlab, int lane) {
+  const int g4 = lane >> 4;
+  const f32x4_t zero = {0.f, 0.f, 0.f, 0.f};
   float m = -INFINITY;
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb) {
-    f32x16_t s = mfma_op<H16>(kop[kb][0], qa, zero);
-    s = mfma_op<H16>(kop[kb][1], qb, s);
-    const uint32_t live = MASKED ? live_bits(lab, kb, h, qlab) : 0xffffu;
+  for (int kb = 0; kb < 4; ++kb) {
+    const f32x4_t s = mfma16_op<H16>(kop[kb], qop, zero);
+    const uint32_t live = MASKED ? m8_live4(lab, kb, g4, qlab) : 0xfu;
 #pragma unroll
-    for (int e = 0; e < 16; ++e)
+    for (int e = 0; e < 4; ++e)
       if ((live >> e) & 1u) m = fmaxf(m, s[e]);
   }
-  return halves_max(m);
+  return groups_max(m);
 }
 
-// Both query tiles: attention, exact-maximum pass when needed, O and LSE stores.
+// Operands and attention of one window-head: the four 16-query blocks in turn, each with the
+// exact-maximum pass when its bound was too loose, then O and LSE stores.
 template <bool H16, bool MASKED>
-__device__ __forceinline__ void m8_attend(const uint4 (&kop)[2][2], const uint4 (&qop)[2][2],
+__device__ __forceinline__ void m8_attend(const uint4 (&kr)[4], const uint4 (&qr)[4], const float* sn, const float* cs,
                                           uint16_t* __restrict__ out, float* __restrict__ lse, const Geom& g,
                                           const WinHead& w, const uint16_t* vbuf, const uint8_t* lab, float kmax,
-                                          const float (&qn2)[2], int lane) {
-  const int h = lane >> 5, col = lane & 31;
+                                          const float (&qn2)[4], int lane) {
+  const int g4 = lane >> 4, c16 = lane & 15;
+  uint4 kop[4];
 #pragma unroll
-  for (int t = 0; t < 2; ++t) {
-    const int n = t * 32 + col;
-    const int qr = n >> 3, qc = n & 7;
+  for (int b = 0; b < 4; ++b) kop[b] = m8_operand<H16>(kr[b], sn, cs, b * 16 + c16, g4, 1.f);
+#pragma unroll
+  for (int qb = 0; qb < 4; ++qb) {
+    const int n = qb * 16 + c16;
+    const uint4 qop = m8_operand<H16>(qr[qb], sn, cs, n, g4, kM8QScale);
     const int qlab = MASKED ? lab[n] : 0;
-    const float bound = sqrtf(qn2[t]) * kM8QScale * kmax;  // >= every score of this tile (log2 units)
-    f32x16_t o;
+    const float bound = sqrtf(qn2[qb]) * kM8QScale * kmax;  // >= every score of this block (log2 units)
+    f32x4_t o[2];
 #pragma unroll
-    for (int e = 0; e < 16; ++e) o[e] = 0.f;
+    for (int cb = 0; cb < 2; ++cb) o[cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     float l;
-    m8_tile<H16, MASKED>(kop, qop[t][0], qop[t][1], vbuf, lab, qlab, lane, bound, l, o);
-    float lt = halves_sum(l);
+    m8_block<H16, MASKED>(kop, qop, vbuf, lab, qlab, lane, bound, l, o);
+    float lt = groups_sum(l);
     float ref = bound;
     if (__builtin_amdgcn_ballot_w64(!(lt >= kM8LowSum)) != 0) {
-      // the bound was too loose for some query of the tile: exact maximum, second pass
-      ref = m8_rowmax<H16, MASKED>(kop, qop[t][0], qop[t][1], lab, qlab, lane);
+      // the bound was too loose for some query of the block: exact maximum, second pass
+      ref = m8_rowmax<H16, MASKED>(kop, qop, lab, qlab, lane);
 #pragma unroll
-      for (int e = 0; e < 16; ++e) o[e] = 0.f;
-      m8_tile<H16, MASKED>(kop, qop[t][0], qop[t][1], vbuf, lab, qlab, lane, ref, l, o);
-      lt = halves_sum(l);
+      for (int cb = 0; cb < 2; ++cb) o[cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      m8_block<H16, MASKED>(kop, qop, vbuf, lab, qlab, lane, ref, l, o);
+      lt = groups_sum(l);
     }
-    // O = O^T / l (lane: query col, channels 8g + 4h + j), LSE = (ref + log2 l) ln 2
-    const int64_t qtok = token_index(g, w.b, w.wy, w.wx, qr, qc);
+    // O = O^T / l (lane: query c16, channels 16 cb + 4 g4 + {0..3}), LSE = (ref + log2 l) ln 2
+    const int64_t qtok = token_index(g, w.b, w.wy, w.wx, n >> 3, n & 7);
     const float inv = 1.f / lt;
-    uint16_t* dst = out + qtok * g.os + w.h * 32 + 4 * h;
+    uint16_t* dst = out + qtok * g.os + w.h * 32 + 4 * g4;
 #pragma unroll
-    for (int gq = 0; gq < 4; ++gq) {
+    for (int cb = 0; cb < 2; ++cb) {
       uint2 pr;
-      pr.x = pack2(o[4 * gq] * inv, o[4 * gq + 1] * inv);
-      pr.y = pack2(o[4 * gq + 2] * inv, o[4 * gq + 3] * inv);
-      *reinterpret_cast<uint2*>(dst + 8 * gq) = pr;
+      pr.x = pack2(o[cb][0] * inv, o[cb][1] * inv);
+      pr.y = pack2(o[cb][2] * inv, o[cb][3] * inv);
+      *reinterpret_cast<uint2*>(dst + 16 * cb) = pr;
     }
-    if (lse && h == 0) lse[qtok * g.heads + w.h] = (ref + __log2f(lt)) * kLn2;
-    __builtin_amdgcn_sched_barrier(0);  // one tile at a time: bounded register pressure
-  }
-}
-
-// Rotated operands from the raw rows: keys as A blocks, queries (scaled by log2(e)/sqrt(d)) as
-// B tiles; token n = tile * 32 + col sits at position (n / 8, n % 8).
-template <bool H16>
-__device__ __forceinline__ void m8_operands(const uint4 (&kr)[2][2], const uint4 (&qr)[2][2], const float* sn,
-                                            const float* cs, int lane, uint4 (&kop)[2][2], uint4 (&qop)[2][2]) {
-  const int h = lane >> 5, col = lane & 31;
-#pragma unroll
-  for (int t = 0; t < 2; ++t) {
-    const int n = t * 32 + col;
-    kop[t][0] = m8_rotate<H16>(kr[t][0], sn, cs, 0, n >> 3, h, 1.f);
-    kop[t][1] = m8_rotate<H16>(kr[t][1], sn, cs, 1, n & 7, h, 1.f);
-    qop[t][0] = m8_rotate<H16>(qr[t][0], sn, cs, 0, n >> 3, h, kM8QScale);
-    qop[t][1] = m8_rotate<H16>(qr[t][1], sn, cs, 1, n & 7, h, kM8QScale);
-  }
-}
-
-// Operands and attention of one window-head, dispatched on the operand format and on whether the
-// window holds several Swin regions (only then are scores masked).
-__device__ __forceinline__ void m8_compute(const uint4 (&kr)[2][2], const uint4 (&qr)[2][2], const float* sn,
-                                           const float* cs, uint16_t* __restrict__ out, float* __restrict__ lse,
-                                           const Geom& g, const WinHead& w, const uint16_t* vbuf,
-                                           const uint8_t* lab, bool masked, bool h16, float kmax,
-                                           const float (&qn2)[2], int lane) {
-  uint4 kop[2][2], qop[2][2];
-  if (h16) {
-    m8_operands<true>(kr, qr, sn, cs, lane, kop, qop);
-    if (masked)
-      m8_attend<true, true>(kop, qop, out, lse, g, w, vbuf, lab, kmax, qn2, lane);
-    else
-      m8_attend<true, false>(kop, qop, out, lse, g, w, vbuf, lab, kmax, qn2, lane);
-  } else {
-    m8_operands<false>(kr, qr, sn, cs, lane, kop, qop);
-    if (masked)
-      m8_attend<false, true>(kop, qop, out, lse, g, w, vbuf, lab, kmax, qn2, lane);
-    else
-      m8_attend<false, false>(kop, qop, out, lse, g, w, vbuf, lab, kmax, qn2, lane);
+    if (lse && g4 == 0) lse[qtok * g.heads + w.h] = (ref + __log2f(lt)) * kLn2;
+    __builtin_amdgcn_sched_barrier(0);  // one block at a time: bounded register pressure
   }
 }
 
@@ -249,7 +229,7 @@ __global__ __launch_bounds__(kM8Waves * 64, 4) void fwd_m8_kernel(const uint16_t
                                                                uint16_t* __restrict__ out, float* __restrict__ lse,
                                                                Geom g, int64_t nwh) {
   extern __shared__ __align__(16) unsigned char smem_raw[];
-  // [heads][2 axes][8 positions][8 pairs] sin, then cos; per wave: Q, K, V rows [64][32], labels [64]
+  // [heads][2 axes][8 positions][8 pairs] sin, then cos; per wave: V rows [64][32], labels [64]
   float* tsn = reinterpret_cast<float*>(smem_raw);
   float* tcs = tsn + g.heads * 128;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -258,7 +238,7 @@ __global__ __launch_bounds__(kM8Waves * 64, 4) void fwd_m8_kernel(const uint16_t
 
   const int64_t wh = xcd_order(blockIdx.x, gridDim.x) * kM8Waves + wave;
   const bool active = wh < nwh;
-  uint4 kr[2][2], qr[2][2];
+  uint4 kr[4], qr[4];
   if (active) m8_issue(q, k, v, g, wh, lane, vs, kr, qr);  // in flight while the tables are built
 
   for (int i = tid; i < g.heads * 128; i += kM8Waves * 64) {
@@ -281,19 +261,32 @@ __global__ __launch_bounds__(kM8Waves * 64, 4) void fwd_m8_kernel(const uint16_t
   // the compiler from moving LDS reads above it)
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
-  // norms: |k|^2 max over the 64 keys, |q|^2 max per query tile (rotation keeps norms)
-  const float kn0 = halves_sum(m8_norm2(kr[0][0], kr[0][1]));
-  const float kn1 = halves_sum(m8_norm2(kr[1][0], kr[1][1]));
-  const float kmax = sqrtf(wave_max(fmaxf(kn0, kn1)));
-  float qn2[2];
+  // norms: |k|^2 max over the 64 keys, |q|^2 max per 16-query block (rotation keeps norms)
+  float kn = 0.f;
 #pragma unroll
-  for (int t = 0; t < 2; ++t) qn2[t] = wave_max(halves_sum(m8_norm2(qr[t][0], qr[t][1])));
-  const bool h16 = kmax < kF16Limit && sqrtf(fmaxf(qn2[0], qn2[1])) * kM8QScale < kF16Limit;
+  for (int b = 0; b < 4; ++b) kn = fmaxf(kn, groups_sum(norm2_bf16x8(kr[b], 0.f)));
+  const float kmax = sqrtf(wave_max(kn));
+  float qn2[4], qm = 0.f;
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    qn2[b] = wave_max(groups_sum(norm2_bf16x8(qr[b], 0.f)));
+    qm = fmaxf(qm, qn2[b]);
+  }
+  const bool h16 = kmax < kF16Limit && sqrtf(qm) * kM8QScale < kF16Limit;
   const float* sn = tsn + w.h * 128;
   const float* cs = tcs + w.h * 128;
-  m8_compute(kr, qr, sn, cs, out, lse, g, w, vs, lab, masked, h16, kmax, qn2, lane);
+  if (h16) {
+    if (masked)
+      m8_attend<true, true>(kr, qr, sn, cs, out, lse, g, w, vs, lab, kmax, qn2, lane);
+    else
+      m8_attend<true, false>(kr, qr, sn, cs, out, lse, g, w, vs, lab, kmax, qn2, lane);
+  } else {
+    if (masked)
+      m8_attend<false, true>(kr, qr, sn, cs, out, lse, g, w, vs, lab, kmax, qn2, lane);
+    else
+      m8_attend<false, false>(kr, qr, sn, cs, out, lse, g, w, vs, lab, kmax, qn2, lane);
+  }
 }
-
 
 }  // namespace
 

@@ -12,7 +12,8 @@ backward C-ABI calls; `launches` names the kernels it enqueues), timed with HIP 
 stream the library launches on.  `traffic` is taken from the committed rocprofv3 counter summary
 in profiles/ when that summary was measured on the current kernel source (sha256 match), else
 null.  `fwd_roofline` is the M=32 forward kernel against the bf16 MFMA peak; `m8_fwd_roofline`
-times the forward on the M=8 Swin-T stage-1 workload (memory-bound) against the HBM peak.
+times the forward on the M=8 Swin-T stage-1 workload (memory-bound) against the HBM peak, with
+its own `traffic` read the same way.
 `cpu_baseline` times the fp64 CPU oracle on a bounded sample of the same workload (rank 0, N=1
 only).
 
@@ -130,7 +131,8 @@ def m8_forward_roofline(dev, steps, warmup):
     gbs = nbytes / (ms * 1e-3) / 1e9
     return {"workload": name, "kernel": "wattn_fwd", "bound": "hbm", "achieved": round(gbs, 1),
             "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
-            "algorithmic_bytes": nbytes, "launch_ms": round(ms, 4)}
+            "algorithmic_bytes": nbytes, "launch_ms": round(ms, 4),
+            "traffic": read_traffic("wattn_fwd", name, kernel_source_sha())}
 
 
 def live_fraction(Hg, Wg, M, shift):

@@ -165,8 +165,16 @@ def window_scores_ref(q, k, theta_row, theta_col, M, shift):
     return S
 
 
-def _chunks(n_win, heads, N, budget_bytes=256 << 20):
-    per = max(1, budget_bytes // (heads * N * N * 8))
+# Memory bound on one materialized block of score matrices (float64).  Windows are independent, so
+# the forward and backward walk the windows in consecutive slices that fit it; the value only sets
+# how many windows share one batched matmul, never what is computed.
+CHUNK_BUDGET_BYTES = 256 << 20
+
+
+def _chunks(n_win, heads, N):
+    """Consecutive window slices covering [0, n_win), each holding at most CHUNK_BUDGET_BYTES of
+    float64 scores (at least one window per slice)."""
+    per = max(1, CHUNK_BUDGET_BYTES // (heads * N * N * 8))
     for lo in range(0, n_win, per):
         yield slice(lo, min(n_win, lo + per))
 

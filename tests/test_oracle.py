@@ -440,6 +440,60 @@ def test_o1_matches_o2_forward_and_backward(case):
         np.testing.assert_allclose(a, b, rtol=1e-11, atol=1e-11 * max(1.0, np.abs(a).max()))
 
 
+CHUNK_BUDGETS = [1, 4 * 2 * 16 * 16 * 8, 5 * 2 * 16 * 16 * 8]
+
+
+def pin_multi_chunk(budget):
+    """O1 walks the windows in slices bounded by CHUNK_BUDGET_BYTES; the full-size GPU comparisons run
+    many slices.  With a budget of one window per slice, and of 4 and 5 windows (slices that do not
+    divide the 2 x 9 = 18 windows, so the last slice is ragged), O1 still equals O2, which has no
+    slices at all, forward and backward, on a shifted grid with masked windows."""
+    B, Hg, Wg, H, D, M, s = 2, 12, 12, 2, 8, 4, 2
+    q, k, v, do, tr, tc = _rand_case(61, B, Hg, Wg, H, D)
+    saved = wattn_ref.CHUNK_BUDGET_BYTES
+    wattn_ref.CHUNK_BUDGET_BYTES = budget
+    try:
+        n_win = B * (Hg // M) * (Wg // M)
+        assert len(list(wattn_ref._chunks(n_win, H, M * M))) > 1
+        o1, l1 = oracle.wattn_fwd_ref(q, k, v, tr, tc, M, s)
+        g1 = oracle.wattn_bwd_ref(q, k, v, do, tr, tc, M, s)
+    finally:
+        wattn_ref.CHUNK_BUDGET_BYTES = saved
+    o2, l2 = oracle.wattn_fwd_online(q, k, v, tr, tc, M, s, key_tile=5)
+    np.testing.assert_allclose(o1, o2, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(l1, l2, rtol=1e-12, atol=1e-12)
+    g2 = oracle.wattn_bwd_online(q, k, v, o2, l2, do, tr, tc, M, s, key_tile=7)
+    for a, b in zip(g1, g2):
+        np.testing.assert_allclose(a, b, rtol=1e-11, atol=1e-11 * max(1.0, np.abs(a).max()))
+
+
+@pytest.mark.parametrize("budget", CHUNK_BUDGETS)
+def test_o1_multi_chunk_matches_o2(budget):
+    pin_multi_chunk(budget)
+
+
+def test_multi_chunk_pin_catches_slicing_mistakes():
+    """Two plausible slicing mistakes planted in O1 (CPU only): the ragged last slice dropped, and
+    each slice's last window left out.  The multi-chunk pin fails for both."""
+    orig = wattn_ref._chunks
+
+    def drops_tail(n_win, heads, N):
+        per = max(1, wattn_ref.CHUNK_BUDGET_BYTES // (heads * N * N * 8))
+        for lo in range(0, n_win - n_win % per if n_win % per else n_win, per):
+            yield slice(lo, lo + per)
+
+    def off_by_one(n_win, heads, N):
+        for sl in orig(n_win, heads, N):
+            yield slice(sl.start, sl.stop - 1)
+
+    for mutant in (drops_tail, off_by_one):
+        wattn_ref._chunks = mutant
+        try:
+            assert _fails(lambda: pin_multi_chunk(CHUNK_BUDGETS[1])), mutant.__name__
+        finally:
+            wattn_ref._chunks = orig
+
+
 def test_o1_matches_o2_on_tiny_workload():
     from vision_transformer_windowed_amd.inputs import workload_inputs
     x = workload_inputs("tiny_f32_m8", with_dout=True)

@@ -1,6 +1,7 @@
 """GPU tests of the packed-qkv entry points (qkv [B, Hg, Wg, 3, heads, d] read in place, dqkv written
 packed): results are bit-identical to the separate-tensor entry points on the three slices, which
-the other GPU tests hold to the oracle, and one case is compared with the oracle directly."""
+the other GPU tests hold to the oracle, and the packed forward and backward are also compared with
+the oracle directly."""
 
 import numpy as np
 import pytest
@@ -78,6 +79,31 @@ def test_packed_forward_matches_oracle():
         l2 = np.linalg.norm(g - ref) / np.linalg.norm(ref)
         print(f"  {name}: max-abs {err.max():.3e} rel-L2 {l2:.3e}", flush=True)
         assert err.max() <= 2e-2 and l2 <= 5e-3, name
+
+
+@pytest.mark.parametrize("case", [(1, 64, 64, 2, 32, 32, 16, "bf16"), (2, 32, 32, 3, 32, 8, 3, "bf16")],
+                         ids=["M32_s16", "M8_s3"])
+def test_packed_backward_matches_oracle(case):
+    """The packed backward's dq, dk, dv slices of dqkv and its dtheta against the oracle (bf16
+    tolerances: max-abs 2e-2 and rel-L2 5e-3; dtheta max-abs 2e-2 max|ref|)."""
+    B, Hg, Wg, H, D, M, s, dt = case
+    x, qkv = packed_inputs(case, seed=15, with_dout=True)
+    tr, tc = x["theta_row"].to(DEV), x["theta_col"].to(DEV)
+    out, lse = F.wattn_fwd_packed(qkv, tr, tc, M, s)
+    dqkv, dtr, dtc = F.wattn_bwd_packed(qkv, out, x["dout"].to(DEV), lse, tr, tc, M, s)
+    torch.cuda.synchronize()
+    g = oracle.wattn_bwd_ref(x["q"].double().numpy(), x["k"].double().numpy(), x["v"].double().numpy(),
+                             x["dout"].double().numpy(), x["theta_row"].double().numpy(),
+                             x["theta_col"].double().numpy(), M, s)
+    got = [dqkv[:, :, :, i] for i in range(3)] + [dtr, dtc]
+    for i, name in enumerate(("dQ", "dK", "dV", "dtheta_row", "dtheta_col")):
+        mine = got[i].to("cpu", torch.float64).numpy()
+        ref = g[i]
+        err = np.abs(mine - ref).max()
+        l2 = np.linalg.norm(mine - ref) / np.linalg.norm(ref)
+        lim = 2e-2 * (np.abs(ref).max() if i >= 3 else 1.0)
+        print(f"  {name}: max-abs {err:.3e} (tol {lim:.1e}) rel-L2 {l2:.3e}", flush=True)
+        assert err <= lim and l2 <= 5e-3, name
 
 
 def test_packed_autograd_matches_separate():

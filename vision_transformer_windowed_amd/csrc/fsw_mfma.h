@@ -90,6 +90,17 @@ __device__ __forceinline__ uint4 tr_operand_at(const uint16_t* base, int lo, int
 // Largest operand magnitude accepted for the fp16 score products (fp16 max is 65504).
 constexpr float kF16Limit = 16384.f;
 
+// Factor that turns the Cauchy-Schwarz bound max|q^| * max|k~| into a softmax reference that no
+// computed score exceeds.  Rounding q^ and k~ to the operand format (unit roundoff u = 2^-11 for
+// fp16, 2^-8 for bf16) moves a product sum by at most (2u + u^2) |q^| |k~|; the float32 rotation,
+// norms and accumulation add far less than 2^-16 of the bound.  Without the margin a score of an
+// aligned query and key with large norms can exceed the bare bound by more than 128 (log2 units),
+// and exp2 of it overflows.
+template <bool H16>
+__device__ __forceinline__ constexpr float bound_margin() {
+  return H16 ? 1.f + 0x1p-10f + 0x1p-16f : 1.f + 0x1p-7f + 0x1p-16f;
+}
+
 __device__ __forceinline__ uint32_t pack2h(float lo, float hi) {
   f16x2_t v;
   v[0] = (_Float16)lo;

@@ -15,8 +15,9 @@
 // P = exp2(S^T - ref) taken straight from those accumulators as the B operand of P.V (in a key
 // order the V operand follows), O^T in two 16-channel blocks.  The RoPE sin/cos tables of every
 // head are built once per workgroup while the loads are in flight.
-// The softmax reference is the Cauchy-Schwarz bound max|q^| * max|k~| of the block, with an
-// exact-maximum recomputation of a block whose row sums come out below 2^-80.  Only windows that
+// The softmax reference is the Cauchy-Schwarz bound max|q^| * max|k~| of the block, widened by the
+// operand rounding error (bound_margin) so that no score exceeds it, with an exact-maximum
+// recomputation of a block whose row sums come out below 2^-80 or not finite.  Only windows that
 // hold several Swin regions (the last window row and column of a shifted grid) run the masked code.
 #include <algorithm>
 
@@ -187,7 +188,8 @@ __device__ __forceinline__ void m8_attend(const uint4 (&kr)[4], const uint4 (&qr
     const int n = qb * 16 + c16;
     const uint4 qop = m8_operand<H16>(qr[qb], sn, cs, n, g4, kM8QScale);
     const int qlab = MASKED ? lab[n] : 0;
-    const float bound = sqrtf(qn2[qb]) * kM8QScale * kmax;  // >= every score of this block (log2 units)
+    // >= every computed score of this block (log2 units)
+    const float bound = sqrtf(qn2[qb]) * kM8QScale * kmax * bound_margin<H16>();
     f32x4_t o[2];
 #pragma unroll
     for (int cb = 0; cb < 2; ++cb) o[cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -195,7 +197,7 @@ __device__ __forceinline__ void m8_attend(const uint4 (&kr)[4], const uint4 (&qr
     m8_block<H16, MASKED>(kop, qop, vbuf, lab, qlab, lane, bound, l, o);
     float lt = groups_sum(l);
     float ref = bound;
-    if (__builtin_amdgcn_ballot_w64(!(lt >= kM8LowSum)) != 0) {
+    if (__builtin_amdgcn_ballot_w64(!(lt >= kM8LowSum && lt < INFINITY)) != 0) {
       // the bound was too loose for some query of the block: exact maximum, second pass
       ref = m8_rowmax<H16, MASKED>(kop, qop, lab, qlab, lane);
 #pragma unroll

@@ -17,10 +17,12 @@
 //
 // Softmax reference: softmax is unchanged by subtracting any per-row constant.  Instead of a
 // running maximum, each wave subtracts the Cauchy-Schwarz bound B = max_i |q_i| * max_j |k_j| of its
-// scores, folded into the MFMA accumulator initialisation (so the subtraction costs nothing), and
-// the sum is accumulated without rescaling.  Every exponent is then <= 0 (no overflow).  If a
-// query's sum comes out below 2^-80 (a bound so loose that small terms could underflow), the wave
-// recomputes its tile with the exact row maximum in a second pass; results are exact either way.
+// scores, widened by the operand rounding error (bound_margin), folded into the MFMA accumulator
+// initialisation (so the subtraction costs nothing), and the sum is accumulated without rescaling.
+// No computed score exceeds the widened bound, so every exponent is <= 0 up to float32 rounding
+// and none overflows.  If a query's sum comes out below 2^-80 (a bound so loose that small terms
+// could underflow) or not finite, the wave recomputes its tile with the exact row maximum in a
+// second pass; results are exact either way.
 //
 // Precision: the score operands (rotated, scaled Q^ and K~) are rounded to fp16 when every one of
 // them is in fp16 range (else bf16); P is bf16 (it may be far below 1 under the bound reference,
@@ -197,16 +199,18 @@ __device__ __forceinline__ void attend(const FwdSmem& sm, int NB, int lane, bool
                                        uint32_t wave_labels,
                                        bool wave_single, uint4 qb0, uint4 qb1, int qlab, bool qvalid, float bound,
                                        float& ref, float& l, f32x16_t& o) {
+  const float refb = bound * bound_margin<H16>();
   f32x16_t cinit;
 #pragma unroll
-  for (int v2 = 0; v2 < 16; ++v2) cinit[v2] = -bound;
+  for (int v2 = 0; v2 < 16; ++v2) cinit[v2] = -refb;
   float m = 0.f;
   if (run)
     pass_uniform<H16>(sm, kb0, kb1, lane, qb0, qb1, cinit, l, o);
   else if (wave_labels != 0)
     pass_general<0, H16>(sm, NB, lane, wave_labels, wave_single, qb0, qb1, qlab, cinit, m, l, o);
-  ref = bound;
-  const bool low = qvalid && !(halves_sum(l) >= kLowSum);
+  ref = refb;
+  const float lsum = halves_sum(l);
+  const bool low = qvalid && !(lsum >= kLowSum && lsum < INFINITY);
   if (__builtin_amdgcn_ballot_w64(low) != 0) {
     f32x16_t zero;
 #pragma unroll

@@ -28,7 +28,9 @@
  * Execution: every call validates its arguments on the host first (no HIP call is made when a
  * check fails), then enqueues kernels on `hip_stream` (a hipStream_t; NULL = the default stream)
  * and returns without waiting.  A kernel fault surfaces at the caller's next synchronisation.
- * The library allocates no device memory and keeps no global state; calls are thread-safe.
+ * The library allocates no device memory and keeps no global state, apart from the fixed scratch
+ * array behind flashswin_wattn_bwd_noalloc (and the per-device lookup of its address); calls are
+ * thread-safe, except for overlapping flashswin_wattn_bwd_noalloc calls on one GPU (see there).
  * All device buffers are owned by the caller and must stay alive until the stream reaches them.
  */
 #ifndef FLASHSWIN_H_
@@ -47,7 +49,8 @@ typedef enum {
   FSW_ERR_INVALID_ARG = 1, /* shape / pointer / alignment / shift / dtype rule violated */
   FSW_ERR_UNSUPPORTED = 2, /* valid but not implemented here (d, M, dtype combination) */
   FSW_ERR_WORKSPACE = 3,   /* workspace NULL or smaller than flashswin_wattn_bwd_workspace_size() */
-  FSW_ERR_HIP = 4          /* a HIP launch reported an error */
+  FSW_ERR_HIP = 4,         /* a HIP launch reported an error */
+  FSW_ERR_SCRATCH = 5      /* flashswin_wattn_bwd_noalloc: the shape needs more than FLASHSWIN_SCRATCH_BYTES */
 } fsw_status;
 
 /* Element type of q, k, v, out, dout, dq, dk, dv.  theta, lse and dtheta are always float32. */
@@ -149,6 +152,36 @@ int flashswin_wattn_bwd_packed(const void* qkv, const void* out, const void* dou
                                void* workspace, size_t workspace_bytes,
                                int64_t B, int64_t Hg, int64_t Wg, int heads, int d,
                                int M, int shift, int dtype, void* hip_stream);
+
+/* Size of the fixed per-GPU scratch array behind flashswin_wattn_bwd_noalloc: 32 MiB. */
+#define FLASHSWIN_SCRATCH_BYTES (32u * 1024u * 1024u)
+
+/*
+ * flashswin_wattn_bwd without a workspace argument, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).  The
+ * workspace is a fixed array of FLASHSWIN_SCRATCH_BYTES that the library places on every GPU it
+ * runs on and holds until the process ends; its device address is looked up once per device, on
+ * the first call with that device current.  This call makes no allocation of its own (no hipMalloc,
+ * no hipFree, no allocating library routine).
+ *
+ *   Arguments, layouts, ownership of the caller's buffers and results: as flashswin_wattn_bwd, whose
+ *   kernels it runs; the gradients are bit-identical to flashswin_wattn_bwd's.
+ *   Returns FSW_ERR_SCRATCH, before any HIP call, when flashswin_wattn_bwd_workspace_size() of the
+ *   shape exceeds FLASHSWIN_SCRATCH_BYTES (e.g. the bf16 M = 32 backward of 128 images of
+ *   128 x 128 tokens and 3 heads needs 26.8 MB and fits; 200 such images need 41.9 MB and do not).  FSW_ERR_HIP when
+ *   the scratch address cannot be looked up.  Otherwise the codes of flashswin_wattn_bwd.
+ *   Every call on one GPU shares that GPU's array, and each call overwrites it: calls that overlap
+ *   on one GPU (two host threads, or two streams whose work can run concurrently) race and give
+ *   wrong results.  Calls queued on one stream are ordered and safe.  No part of the array needs
+ *   to start cleared: every workspace section is written before it is read.
+ */
+int flashswin_wattn_bwd_noalloc(const void* q, const void* k, const void* v,
+                                const void* out, const void* dout, const float* lse,
+                                const float* theta_row, const float* theta_col,
+                                void* dq, void* dk, void* dv,
+                                float* dtheta_row, float* dtheta_col,
+                                int64_t B, int64_t Hg, int64_t Wg, int heads, int d,
+                                int M, int shift, int dtype, void* hip_stream);
 
 /* Static, human-readable name of a status code. */
 const char* flashswin_status_string(int status);

@@ -12,12 +12,14 @@ from ._lib import (  # noqa: F401
     FSW_BF16,
     FSW_ERR_HIP,
     FSW_ERR_INVALID_ARG,
+    FSW_ERR_SCRATCH,
     FSW_ERR_UNSUPPORTED,
     FSW_ERR_WORKSPACE,
     FSW_F32,
     FSW_OK,
     FlashSwinError,
     LIB_PATH,
+    SCRATCH_BYTES,
     WindowAttention,
     WindowAttentionPacked,
     bwd_workspace_bytes,
@@ -25,6 +27,7 @@ from ._lib import (  # noqa: F401
     flashswin_version,
     flashswin_wattn_bwd,
     flashswin_wattn_bwd_workspace_size,
+    flashswin_wattn_bwd_noalloc,
     flashswin_wattn_bwd_packed,
     flashswin_wattn_fwd,
     flashswin_wattn_fwd_packed,

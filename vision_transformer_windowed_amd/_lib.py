@@ -16,7 +16,8 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libflashswin.so")
 
-FSW_OK, FSW_ERR_INVALID_ARG, FSW_ERR_UNSUPPORTED, FSW_ERR_WORKSPACE, FSW_ERR_HIP = range(5)
+FSW_OK, FSW_ERR_INVALID_ARG, FSW_ERR_UNSUPPORTED, FSW_ERR_WORKSPACE, FSW_ERR_HIP, FSW_ERR_SCRATCH = range(6)
+SCRATCH_BYTES = 32 * 1024 * 1024  # FLASHSWIN_SCRATCH_BYTES of include/flashswin.h
 FSW_F32, FSW_BF16 = 0, 1
 
 EXPORTED = (
@@ -25,6 +26,7 @@ EXPORTED = (
     "flashswin_wattn_bwd",
     "flashswin_wattn_fwd_packed",
     "flashswin_wattn_bwd_packed",
+    "flashswin_wattn_bwd_noalloc",
     "flashswin_status_string",
     "flashswin_version",
 )
@@ -59,6 +61,8 @@ def load():
     lib.flashswin_wattn_fwd_packed.argtypes = [vp] * 5 + [i64, i64, i64, i32, i32, i32, i32, i32, vp]
     lib.flashswin_wattn_bwd_packed.restype = i32
     lib.flashswin_wattn_bwd_packed.argtypes = [vp] * 9 + [vp, sz, i64, i64, i64, i32, i32, i32, i32, i32, vp]
+    lib.flashswin_wattn_bwd_noalloc.restype = i32
+    lib.flashswin_wattn_bwd_noalloc.argtypes = [vp] * 13 + [i64, i64, i64, i32, i32, i32, i32, i32, vp]
     lib.flashswin_status_string.restype = ctypes.c_char_p
     lib.flashswin_status_string.argtypes = [i32]
     lib.flashswin_version.restype = i32
@@ -100,6 +104,13 @@ def flashswin_wattn_bwd_packed(qkv, out, dout, lse, theta_row, theta_col, dqkv, 
     return load().flashswin_wattn_bwd_packed(qkv, out, dout, lse, theta_row, theta_col, dqkv, dtheta_row,
                                              dtheta_col, workspace, workspace_bytes, B, Hg, Wg, heads, d, M, shift,
                                              dtype, stream)
+
+
+def flashswin_wattn_bwd_noalloc(q, k, v, out, dout, lse, theta_row, theta_col, dq, dk, dv, dtheta_row, dtheta_col,
+                                B, Hg, Wg, heads, d, M, shift, dtype, stream):
+    """Raw call of the backward that uses the library's fixed per-GPU scratch instead of a workspace."""
+    return load().flashswin_wattn_bwd_noalloc(q, k, v, out, dout, lse, theta_row, theta_col, dq, dk, dv,
+                                              dtheta_row, dtheta_col, B, Hg, Wg, heads, d, M, shift, dtype, stream)
 
 
 def flashswin_status_string(status):

@@ -4,9 +4,16 @@
 // Dispatch: bf16 with d == 32 and M <= 32 goes to the MFMA kernels; everything else (float32
 // tensors, other d) goes to the float32-arithmetic kernels.
 #include <algorithm>
+#include <mutex>
 
 #include "../../include/flashswin.h"
 #include "fsw_launch.h"
+
+// Backward scratch for callers that cannot allocate (flashswin_wattn_bwd_noalloc): one fixed array
+// per GPU, which that GPU holds until the process ends.  Host code never passes `scratch` itself to
+// a kernel (on the host it names a stand-in, not the device array); it passes the device address
+// that hipGetSymbolAddress returned for the current device.
+static __device__ __align__(256) unsigned char scratch[FLASHSWIN_SCRATCH_BYTES];
 
 namespace {
 
@@ -118,18 +125,26 @@ int fwd_impl(const void* q, const void* k, const void* v, const float* theta_row
   return e == hipSuccess ? FSW_OK : FSW_ERR_HIP;
 }
 
+// Null and alignment checks of a backward's tensor pointers.
+bool bwd_pointers_ok(const void* q, const void* k, const void* v, const void* out, const void* dout, const float* lse,
+                     const float* theta_row, const float* theta_col, void* dq, void* dk, void* dv, float* dtheta_row,
+                     float* dtheta_col) {
+  const void* ptrs16[] = {q, k, v, out, dout, dq, dk, dv};
+  for (const void* p : ptrs16)
+    if (!p || !aligned(p, 16)) return false;
+  const void* ptrs4[] = {lse, theta_row, theta_col, dtheta_row, dtheta_col};
+  for (const void* p : ptrs4)
+    if (!p || !aligned(p, 4)) return false;
+  return dtheta_row != dtheta_col;
+}
+
 // Pointer, workspace checks and dispatch of a backward whose shape (and strides) is in g.
 int bwd_impl(const void* q, const void* k, const void* v, const void* out, const void* dout, const float* lse,
              const float* theta_row, const float* theta_col, void* dq, void* dk, void* dv, float* dtheta_row,
              float* dtheta_col, void* workspace, size_t workspace_bytes, const fsw::Geom& g, int dtype,
              void* hip_stream) {
-  const void* ptrs16[] = {q, k, v, out, dout, dq, dk, dv};
-  for (const void* p : ptrs16)
-    if (!p || !aligned(p, 16)) return FSW_ERR_INVALID_ARG;
-  const void* ptrs4[] = {lse, theta_row, theta_col, dtheta_row, dtheta_col};
-  for (const void* p : ptrs4)
-    if (!p || !aligned(p, 4)) return FSW_ERR_INVALID_ARG;
-  if (dtheta_row == dtheta_col) return FSW_ERR_INVALID_ARG;
+  if (!bwd_pointers_ok(q, k, v, out, dout, lse, theta_row, theta_col, dq, dk, dv, dtheta_row, dtheta_col))
+    return FSW_ERR_INVALID_ARG;
   const bool mfma = use_mfma(g, dtype);
   const WsLayout ws = workspace_layout(g, mfma);
   if (!workspace || !aligned(workspace, 256) || workspace_bytes < ws.total) return FSW_ERR_WORKSPACE;
@@ -141,6 +156,29 @@ int bwd_impl(const void* q, const void* k, const void* v, const void* out, const
   hipStream_t s = reinterpret_cast<hipStream_t>(hip_stream);
   const hipError_t e = mfma ? fsw::launch_bwd_mfma(a, s) : fsw::launch_bwd_scalar(a, s);
   return e == hipSuccess ? FSW_OK : FSW_ERR_HIP;
+}
+
+// Device address of `scratch` on the current device, looked up once per device; nullptr (and the
+// HIP error in *err) when the lookup fails.
+constexpr int kMaxScratchDevices = 64;
+
+void* scratch_address(hipError_t* err) {
+  static std::once_flag once[kMaxScratchDevices];
+  static void* addr[kMaxScratchDevices];
+  static hipError_t status[kMaxScratchDevices];
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess || dev < 0 || dev >= kMaxScratchDevices) {
+    *err = e != hipSuccess ? e : hipErrorInvalidDevice;
+    return nullptr;
+  }
+  std::call_once(once[dev], [dev] {
+    void* p = nullptr;
+    status[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    addr[dev] = status[dev] == hipSuccess ? p : nullptr;
+  });
+  *err = status[dev];
+  return addr[dev];
 }
 
 }  // namespace
@@ -156,6 +194,9 @@ const char* flashswin_status_string(int status) {
     case FSW_ERR_UNSUPPORTED: return "FSW_ERR_UNSUPPORTED: valid arguments this library does not implement";
     case FSW_ERR_WORKSPACE: return "FSW_ERR_WORKSPACE: workspace missing or too small";
     case FSW_ERR_HIP: return "FSW_ERR_HIP: a HIP kernel launch failed";
+    case FSW_ERR_SCRATCH:
+      return "FSW_ERR_SCRATCH: the backward needs more workspace than the library's fixed scratch array "
+             "(FLASHSWIN_SCRATCH_BYTES) holds; call flashswin_wattn_bwd with a caller workspace";
     default: return "unknown flashswin status";
   }
 }
@@ -243,6 +284,33 @@ int flashswin_wattn_bwd_packed(const void* qkv, const void* out, const void* dou
   char* dx = static_cast<char*>(dqkv);
   return bwd_impl(x, x + slot, x + 2 * slot, out, dout, lse, theta_row, theta_col, dx, dx + slot, dx + 2 * slot,
                   dtheta_row, dtheta_col, workspace, workspace_bytes, g, dtype, hip_stream);
+}
+
+int flashswin_wattn_bwd_noalloc(const void* q, const void* k, const void* v, const void* out, const void* dout,
+                                const float* lse, const float* theta_row, const float* theta_col, void* dq, void* dk,
+                                void* dv, float* dtheta_row, float* dtheta_col, int64_t B, int64_t Hg, int64_t Wg,
+                                int heads, int d, int M, int shift, int dtype, void* hip_stream) {
+  fsw::Geom g;
+  int st = check_shape(B, Hg, Wg, heads, d, M, shift, dtype, &g);
+  if (st != FSW_OK) return st;
+  if (B == 0) return FSW_OK;
+  // the size limit is checked before any HIP call
+  const size_t need = workspace_layout(g, use_mfma(g, dtype)).total;
+  if (need > (size_t)FLASHSWIN_SCRATCH_BYTES) return FSW_ERR_SCRATCH;
+  const Sizes z = sizes_of(g, dtype);
+  const Span outs[] = {{dq, z.tens}, {dk, z.tens}, {dv, z.tens}, {dtheta_row, z.theta}, {dtheta_col, z.theta}};
+  const Span ins[] = {{q, z.tens},   {k, z.tens},           {v, z.tens},          {out, z.tens},
+                      {dout, z.tens}, {lse, z.lse}, {theta_row, z.theta}, {theta_col, z.theta}};
+  if (!outputs_disjoint(outs, ins)) return FSW_ERR_INVALID_ARG;
+  if (!bwd_pointers_ok(q, k, v, out, dout, lse, theta_row, theta_col, dq, dk, dv, dtheta_row, dtheta_col))
+    return FSW_ERR_INVALID_ARG;
+  hipError_t e = hipSuccess;
+  void* ws = scratch_address(&e);
+  if (!ws) return FSW_ERR_HIP;
+  // every section of the workspace is written before it is read (Delta and the window maxima by
+  // the prologue, each dtheta partial row by its workgroup), so nothing needs clearing first
+  return bwd_impl(q, k, v, out, dout, lse, theta_row, theta_col, dq, dk, dv, dtheta_row, dtheta_col, ws,
+                  (size_t)FLASHSWIN_SCRATCH_BYTES, g, dtype, hip_stream);
 }
 
 }  // extern "C"

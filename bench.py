@@ -3,17 +3,18 @@
 
 Workload (default): FlashSwin-T stage 1 with p=2, M=32: q/k/v/dO [128, 128, 128, 3, 32] bf16,
 no shift, seeded synthetic N(0,1) inputs (no dataset), RoPE theta from the geometric schedule plus
-N(0, 0.01^2) noise.  One step = the whole hot path over the batch: the forward (RoPE, online-softmax
+N(0, 0.01^2) noise.  One step = the whole hot path over the batch: the forward (RoPE, exact-softmax
 attention, LSE) then the backward (Delta, recomputed P, dQ/dK/dV, dtheta).  FLOPs per window-head:
 4 N^2 d forward + 10 N^2 d backward (N = M^2), the dense convention of the workload's metric.
 
-Prints ONE JSON line.  `roofline` describes the dominant call (the longer of the forward and
-backward C-ABI calls; `launches` names the kernels it enqueues), timed with HIP events on the
+Prints ONE JSON line.  `roofline` describes the forward kernel of the workload (one launch of
+fwd_mfma_kernel per forward call at M=32), the configuration the metric is quoted on, against the
+dense bf16 MFMA peak; `bwd_roofline` describes the backward call (`launches` names the four
+kernels it enqueues; together they take most of the step).  Both are timed with HIP events on the
 stream the library launches on.  `traffic` is taken from the committed rocprofv3 counter summary
 in profiles/ when that summary was measured on the current kernel source (sha256 match), else
-null.  `fwd_roofline` is the M=32 forward kernel against the bf16 MFMA peak; `m8_fwd_roofline`
-times the forward on the M=8 Swin-T stage-1 workload (memory-bound) against the HBM peak, with
-its own `traffic` read the same way.
+null.  `m8_fwd_roofline` times the forward on the M=8 Swin-T stage-1 workload (memory-bound)
+against the HBM peak, with its own `traffic` read the same way.
 `cpu_baseline` times the fp64 CPU oracle on a bounded sample of the same workload (rank 0, N=1
 only).
 
@@ -34,6 +35,8 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
+# the forward kernel instance each window size launches (M = 8: one wave per window-head)
+FWD_KERNEL = {32: "fwd_mfma_kernel<16, 32, 1024>", 16: "fwd_mfma_kernel<8, 16, 256>", 8: "fwd_m8_kernel"}
 # kernels each C-ABI call launches, in order
 CALL_LAUNCHES = {"wattn_fwd": ["fwd_mfma_kernel"],
                  "wattn_bwd": ["bwd_pre_kernel", "bwd_dkdv_mfma_kernel", "bwd_dq_mfma_kernel", "dtheta_reduce_kernel"]}
@@ -343,21 +346,22 @@ def main():
     value = step_flops / (ms_per_step * 1e-3) / 1e12
 
     sha = kernel_source_sha()
-    if fwd_ms >= bwd_ms:
-        dom, dom_ms, dom_flops = "wattn_fwd", fwd_ms, fwd_flops
-    else:
-        dom, dom_ms, dom_flops = "wattn_bwd", bwd_ms, bwd_flops
-    achieved = dom_flops / (dom_ms * 1e-3) / 1e12
-    traffic = read_traffic(dom, args.workload, sha)
-    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(achieved / BF16_MFMA_PEAK_TFLOPS, 4), "traffic": traffic, "kernel": dom,
-                "launches": CALL_LAUNCHES[dom], "launch_ms": round(dom_ms, 4), "kernel_source_sha": sha}
-    fwd_roofline = None
+    fwd_roofline = bwd_roofline = None
     if args.only != "bwd":
         fwd_tf = fwd_flops / (fwd_ms * 1e-3) / 1e12
-        fwd_roofline = {"kernel": "wattn_fwd", "bound": "mfma", "achieved": round(fwd_tf, 2),
-                        "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(fwd_tf / BF16_MFMA_PEAK_TFLOPS, 4),
-                        "launch_ms": round(fwd_ms, 4)}
+        fwd_roofline = {"bound": "mfma", "achieved": round(fwd_tf, 2), "peak": BF16_MFMA_PEAK_TFLOPS,
+                        "unit": "TFLOP/s", "frac": round(fwd_tf / BF16_MFMA_PEAK_TFLOPS, 4),
+                        "traffic": read_traffic("wattn_fwd", args.workload, sha), "kernel": FWD_KERNEL.get(M),
+                        "call": "wattn_fwd", "launches": CALL_LAUNCHES["wattn_fwd"], "launch_ms": round(fwd_ms, 4),
+                        "flops_per_launch": fwd_flops, "kernel_source_sha": sha}
+    if args.only != "fwd":
+        bwd_tf = bwd_flops / (bwd_ms * 1e-3) / 1e12
+        bwd_roofline = {"bound": "mfma", "achieved": round(bwd_tf, 2), "peak": BF16_MFMA_PEAK_TFLOPS,
+                        "unit": "TFLOP/s", "frac": round(bwd_tf / BF16_MFMA_PEAK_TFLOPS, 4),
+                        "traffic": read_traffic("wattn_bwd", args.workload, sha), "call": "wattn_bwd",
+                        "launches": CALL_LAUNCHES["wattn_bwd"], "launch_ms": round(bwd_ms, 4),
+                        "flops_per_call": bwd_flops, "kernel_source_sha": sha}
+    roofline = fwd_roofline if fwd_roofline is not None else bwd_roofline
     m8 = packed = m16 = masked = bwd32 = None
     if not args.no_secondary and args.only == "step":
         m8 = m8_forward_roofline(dev, max(args.steps, 10), max(args.warmup, 2))
@@ -399,7 +403,7 @@ def main():
         "bwd_tflops": round(bwd_flops / (bwd_ms * 1e-3) / 1e12, 2) if args.only != "fwd" else None,
         "window_heads_per_s": round(nwh / (ms_per_step * 1e-3), 1),
         "roofline": roofline,
-        "fwd_roofline": fwd_roofline,
+        "bwd_roofline": bwd_roofline,
         "m8_fwd_roofline": m8,
         "m8_fwd_packed_qkv": packed,
         "m16_step": m16,

@@ -29,7 +29,9 @@ pages for those conventions).
 
 from .wattn_ref import (  # noqa: F401
     check_args,
+    check_bias,
     region_labels,
+    relative_bias,
     rope_rotate,
     wattn_fwd_ref,
     wattn_bwd_ref,

@@ -27,6 +27,13 @@ Conventions the pages leave open, and the reading taken here:
 * scores S = q~ . k~ / sqrt(d); masked pairs are excluded (weight exactly 0);
 * LSE = natural log of sum_j exp(S_ij) over the live keys.
 
+The forward also takes an optional relative-position bias, the term that the
+standard Swin window attention adds to its materialized scores and FlashSwin
+drops ([FS] Abstract).  It is used only to check the materialized comparison
+path.  Reading (the pages give no index convention): a per-head table
+bias[h, 2M-1, 2M-1], and the pair (query i, key j) at in-window positions
+(r_i, c_i), (r_j, c_j) gets bias[h, r_i - r_j + M - 1, c_i - c_j + M - 1].
+
 Parity: pinned by tests/test_oracle.py (brute force, library attention for
 theta = 0, constant-V, closed-form RoPE pair, region decomposition, finite
 differences, invariants, agreement with O2).  The RoPE conventions above are
@@ -36,6 +43,12 @@ differences, invariants, agreement with O2).  The RoPE conventions above are
 import numpy as np
 
 SUPPORTED_D = (4, 8, 16, 32, 64)
+
+
+def check_bias(bias, heads, M):
+    """Validate an optional relative-position bias table [heads, 2M-1, 2M-1]."""
+    if bias is not None and tuple(np.shape(bias)) != (heads, 2 * M - 1, 2 * M - 1):
+        raise ValueError("bias must be [heads, 2M-1, 2M-1]")
 
 
 def check_args(shape, theta_row_shape, theta_col_shape, M, shift):
@@ -153,12 +166,25 @@ def _window_mask(B, Hg, Wg, M, s):
     return live
 
 
-def window_scores_ref(q, k, theta_row, theta_col, M, shift):
+def relative_bias(bias, M):
+    """The bias of every (query i, key j) pair of a window, [heads, N, N]:
+    bias[h, r_i - r_j + M - 1, c_i - c_j + M - 1], token n = r*M + c."""
+    n = np.arange(M * M)
+    r, c = n // M, n % M
+    dr = r[:, None] - r[None, :] + M - 1
+    dc = c[:, None] - c[None, :] + M - 1
+    return np.asarray(bias, dtype=np.float64)[:, dr, dc]
+
+
+def window_scores_ref(q, k, theta_row, theta_col, M, shift, bias=None):
     """Materialized scaled scores S [nWin, heads, N, N] (masked pairs = -inf). Small inputs only."""
     B, Hg, Wg, heads, d = np.shape(q)
+    check_bias(bias, heads, M)
     qw = rope_rotate(_windows(q, M, shift), theta_row, theta_col, M)
     kw = rope_rotate(_windows(k, M, shift), theta_row, theta_col, M)
     S = qw @ np.swapaxes(kw, -1, -2) / np.sqrt(d)
+    if bias is not None:
+        S = S + relative_bias(bias, M)[None]
     live = _window_mask(B, Hg, Wg, M, shift)
     if live is not None:
         S = np.where(live, S, -np.inf)
@@ -179,14 +205,18 @@ def _chunks(n_win, heads, N):
         yield slice(lo, min(n_win, lo + per))
 
 
-def wattn_fwd_ref(q, k, v, theta_row, theta_col, M, shift):
-    """Forward: returns (out [B,Hg,Wg,heads,d] float64, lse [B,Hg,Wg,heads] float64)."""
+def wattn_fwd_ref(q, k, v, theta_row, theta_col, M, shift, bias=None):
+    """Forward: returns (out [B,Hg,Wg,heads,d] float64, lse [B,Hg,Wg,heads] float64).
+
+    bias: optional relative-position bias table [heads, 2M-1, 2M-1] added to the scores."""
     q = np.asarray(q)
     B, Hg, Wg, heads, d = q.shape
     theta_row = np.asarray(theta_row, dtype=np.float64)
     theta_col = np.asarray(theta_col, dtype=np.float64)
     check_args(q.shape, theta_row.shape, theta_col.shape, M, shift)
+    check_bias(bias, heads, M)
     N = M * M
+    rb = None if bias is None else relative_bias(bias, M)[None]
     qw = rope_rotate(_windows(q, M, shift), theta_row, theta_col, M)
     kw = rope_rotate(_windows(k, M, shift), theta_row, theta_col, M)
     vw = _windows(v, M, shift)
@@ -195,6 +225,8 @@ def wattn_fwd_ref(q, k, v, theta_row, theta_col, M, shift):
     lw = np.empty(vw.shape[:3], dtype=np.float64)
     for sl in _chunks(qw.shape[0], heads, N):
         S = qw[sl] @ np.swapaxes(kw[sl], -1, -2) / np.sqrt(d)
+        if rb is not None:
+            S = S + rb
         if live_all is not None:
             S = np.where(live_all[sl], S, -np.inf)
         m = S.max(axis=-1, keepdims=True)

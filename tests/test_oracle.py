@@ -43,8 +43,9 @@ def _rand_case(seed, B, Hg, Wg, H, D, theta_scale=1.0):
 
 # ----------------------------------------------------------------------------- brute force
 
-def brute_force_fwd(q, k, v, tr, tc, M, s):
-    """Per-token scalar loops; every key of the grid is tested for membership."""
+def brute_force_fwd(q, k, v, tr, tc, M, s, bias=None):
+    """Per-token scalar loops; every key of the grid is tested for membership.  With a bias table, the
+    pair of query (Y, X) and key (Y2, X2) (shifted frame) adds bias[h][Y%M - Y2%M + M-1][X%M - X2%M + M-1]."""
     B, Hg, Wg, H, D = q.shape
 
     def shifted(y, x):
@@ -82,7 +83,10 @@ def brute_force_fwd(q, k, v, tr, tc, M, s):
                             if (region(Y2, Hg), region(X2, Wg)) != lab:
                                 continue
                             kt = rot(k[b, y2, x2, h], h, Y2 % M, X2 % M)
-                            scores.append(sum(qt[i] * kt[i] for i in range(D)) / math.sqrt(D))
+                            sc = sum(qt[i] * kt[i] for i in range(D)) / math.sqrt(D)
+                            if bias is not None:
+                                sc += float(bias[h][Y % M - Y2 % M + M - 1][X % M - X2 % M + M - 1])
+                            scores.append(sc)
                             vals.append(v[b, y2, x2, h])
                     mx = max(scores)
                     e = [math.exp(t - mx) for t in scores]
@@ -113,6 +117,60 @@ def pin_brute_force(fwd=None):
 
 def test_brute_force():
     pin_brute_force()
+
+
+BIAS_CASES = [(1, 4, 4, 2, 8, 2, 0), (1, 6, 6, 1, 8, 3, 1), (2, 6, 9, 2, 4, 3, 2), (1, 8, 8, 1, 4, 4, 3)]
+
+
+def pin_bias_brute_force(fwd=None, scores=None):
+    """The relative-position bias term against the scalar loops, on shifted and unshifted grids, and
+    the materialized scores: with q = k = 0 every score is the bias of its pair."""
+    fwd = fwd or oracle.wattn_fwd_ref
+    scores = scores or oracle.window_scores_ref
+    for i, (B, Hg, Wg, H, D, M, s) in enumerate(BIAS_CASES):
+        q, k, v, _, tr, tc = _rand_case(40 + i, B, Hg, Wg, H, D)
+        bias = np.random.default_rng(140 + i).standard_normal((H, 2 * M - 1, 2 * M - 1))
+        o, l = fwd(q, k, v, tr, tc, M, s, bias=bias)
+        ob, lb = brute_force_fwd(q, k, v, tr, tc, M, s, bias=bias)
+        np.testing.assert_allclose(o, ob, rtol=0, atol=1e-12)
+        np.testing.assert_allclose(l, lb, rtol=0, atol=1e-12)
+    M = 3
+    z = np.zeros((1, M, M, 1, 4))
+    bias = np.arange(25, dtype=np.float64).reshape(1, 5, 5)
+    S = scores(z, z, np.zeros((1, 1)), np.zeros((1, 1)), M, 0, bias=bias)[0, 0]
+    for i in range(M * M):
+        for j in range(M * M):
+            assert S[i, j] == bias[0, i // M - j // M + M - 1, i % M - j % M + M - 1]
+
+
+def test_relative_bias_brute_force():
+    pin_bias_brute_force()
+
+
+def test_bias_shape_is_checked():
+    z = np.zeros((1, 4, 4, 2, 8))
+    t = np.zeros((2, 2))
+    with pytest.raises(ValueError):
+        oracle.wattn_fwd_ref(z, z, z, t, t, 2, 0, bias=np.zeros((2, 4, 4)))
+
+
+def test_bias_pin_catches_planted_mistakes():
+    """Two plausible index mistakes planted in the bias gather (CPU only): the offset taken key minus
+    query, and the row and column offsets swapped.  The brute-force pin fails for both."""
+    orig = wattn_ref.relative_bias
+
+    def key_minus_query(bias, M):
+        return np.swapaxes(orig(bias, M), -1, -2)
+
+    def axes_swapped(bias, M):
+        return orig(np.swapaxes(np.asarray(bias), -1, -2), M)
+
+    for mutant in (key_minus_query, axes_swapped):
+        wattn_ref.relative_bias = mutant
+        try:
+            assert _fails(lambda: pin_bias_brute_force()), mutant.__name__
+        finally:
+            wattn_ref.relative_bias = orig
 
 
 # ----------------------------------------------------------------------------- golden closed form

@@ -204,6 +204,45 @@ def config_timing(dev, name, shift, passes, steps, warmup):
     return res
 
 
+def materialized_vs_fused(dev, steps, warmup):
+    """The forward computed the standard Swin way, with every window's score matrix in HBM (the
+    materialized comparison path), against the fused forward, at M = 8, 16 and 32 on the stage-1 grids:
+    milliseconds per call and the bytes of score workspace the materialized path needs (the fused path
+    needs none)."""
+    import torch
+    import vision_transformer_windowed_amd as F
+    from vision_transformer_windowed_amd.inputs import WORKLOADS, workload_inputs
+    res = []
+    for name in ("swin_t_s1_p4_m8", "flashswin_t_s1_p2_m16", "flashswin_t_s1_p2_m32"):
+        w = WORKLOADS[name]
+        x = {k: v.to(dev) for k, v in workload_inputs(name, with_dout=False).items()}
+        q, k, v, tr, tc = x["q"], x["k"], x["v"], x["theta_row"], x["theta_col"]
+        out = torch.empty_like(q)
+        lse = torch.empty(q.shape[:4], device=dev, dtype=torch.float32)
+        nbytes = F.flashswin_wattn_fwd_materialized_workspace_size(*q.shape, w["M"], 0, F.FSW_BF16)
+        ws = torch.empty(nbytes, device=dev, dtype=torch.uint8)
+        stream = torch.cuda.current_stream(dev)
+        row = {"workload": name, "M": w["M"], "materialized_workspace_bytes": nbytes}
+        for tag, fn in (("fused_ms", lambda: F.wattn_fwd(q, k, v, tr, tc, w["M"], 0, out=out, lse=lse)),
+                        ("materialized_ms", lambda: F.wattn_fwd_materialized(q, k, v, tr, tc, w["M"], 0, out=out,
+                                                                             lse=lse, workspace=ws))):
+            for _ in range(warmup):
+                fn()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(steps):
+                fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            row[tag] = round(e0.elapsed_time(e1) / steps, 4)
+        row["materialized_over_fused"] = round(row["materialized_ms"] / row["fused_ms"], 3)
+        res.append(row)
+        del ws
+        torch.cuda.empty_cache()
+    return res
+
+
 def m16_step(dev, steps, warmup):
     """Forward and backward at M = 16 (the pages' comparison-table window) on the stage-1 grid."""
     return config_timing(dev, "flashswin_t_s1_p2_m16", 0, ("fwd", "bwd"), steps, warmup)
@@ -362,7 +401,7 @@ def main():
                         "launches": CALL_LAUNCHES["wattn_bwd"], "launch_ms": round(bwd_ms, 4),
                         "flops_per_call": bwd_flops, "kernel_source_sha": sha}
     roofline = fwd_roofline if fwd_roofline is not None else bwd_roofline
-    m8 = packed = m16 = masked = bwd32 = None
+    m8 = packed = m16 = masked = bwd32 = mat = None
     if not args.no_secondary and args.only == "step":
         m8 = m8_forward_roofline(dev, max(args.steps, 10), max(args.warmup, 2))
         packed = packed_forward(dev, max(args.steps, 10), max(args.warmup, 2))
@@ -371,6 +410,7 @@ def main():
                                max(args.warmup, 2))
         bwd32 = [config_timing(dev, "flashswin_t_s1_p2_m32_bwd", s, ("bwd",), max(args.steps, 10),
                                max(args.warmup, 2)) for s in WORKLOADS["flashswin_t_s1_p2_m32_bwd"]["shifts"]]
+        mat = materialized_vs_fused(dev, 5, 1)
 
     gpu_out = {"out": out, "lse": lse, "dq": grads[0], "dk": grads[1], "dv": grads[2]}
     cpu, parity = (None, None)
@@ -409,6 +449,7 @@ def main():
         "m16_step": m16,
         "m32_shift16_fwd": masked,
         "m32_bwd_b32": bwd32,
+        "materialized_vs_fused": mat,
         "cpu_baseline": cpu,
         "parity_sample": parity,
         "input_gen_s": round(gen_s, 1),

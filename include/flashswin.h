@@ -153,6 +153,41 @@ int flashswin_wattn_bwd_packed(const void* qkv, const void* out, const void* dou
                                int64_t B, int64_t Hg, int64_t Wg, int heads, int d,
                                int M, int shift, int dtype, void* hip_stream);
 
+/*
+ * Bytes of workspace flashswin_wattn_fwd_materialized needs: the float32 score rows of every
+ * window-head, heads * windows * N * NP * 4 with N = M*M and NP = N rounded up to a multiple of 32.
+ * 0 when B == 0 and for arguments that call would reject (including dtype other than bf16 or d != 32).
+ */
+size_t flashswin_wattn_fwd_materialized_workspace_size(int64_t B, int64_t Hg, int64_t Wg, int heads, int d,
+                                                       int M, int shift, int dtype);
+
+/*
+ * Forward window attention computed the standard Swin way, with the score matrix of every window
+ * materialized in HBM: a comparison path for memory and time, not the method's path ([FS] Abstract:
+ * standard window attention materializes the M^2 x M^2 score matrix, O(M^4) memory per window, and
+ * adds the learned relative-position bias elementwise to the scores; Figure 1(C) and Table S1: memory
+ * against M; Figure S1: throughput against M).
+ *
+ *   Same attention as flashswin_wattn_fwd (RoPE, shift, region mask, scale 1/sqrt(d)), plus an
+ *   optional bias:
+ *   bias         device, float32 [heads, 2M-1, 2M-1], 4-byte aligned, or NULL for none: the pair of
+ *                query i and key j at in-window positions (r_i, c_i), (r_j, c_j) adds
+ *                bias[h, r_i - r_j + M - 1, c_i - c_j + M - 1] to its score.
+ *   workspace    device, at least flashswin_wattn_fwd_materialized_workspace_size() bytes, 256-byte
+ *                aligned: the float32 scores, then the bf16 probabilities in place.
+ *   q, k, v, theta_row, theta_col, out, lse: as in flashswin_wattn_fwd (lse may be NULL).  out, lse and
+ *   the workspace may not share a byte with any input or with each other.
+ *   Three kernels: scores (MFMA, fp16 operands when in range, else bf16; float32 scores), row softmax
+ *   (bf16 probabilities), P.V (MFMA).  Implemented for dtype FSW_BF16 and d == 32 only
+ *   (FSW_ERR_UNSUPPORTED otherwise).
+ * Returns FSW_OK, FSW_ERR_INVALID_ARG, FSW_ERR_UNSUPPORTED, FSW_ERR_WORKSPACE or FSW_ERR_HIP.
+ */
+int flashswin_wattn_fwd_materialized(const void* q, const void* k, const void* v,
+                                     const float* theta_row, const float* theta_col, const float* bias,
+                                     void* out, float* lse, void* workspace, size_t workspace_bytes,
+                                     int64_t B, int64_t Hg, int64_t Wg, int heads, int d,
+                                     int M, int shift, int dtype, void* hip_stream);
+
 /* Size of the fixed per-GPU scratch array behind flashswin_wattn_bwd_noalloc: 32 MiB. */
 #define FLASHSWIN_SCRATCH_BYTES (32u * 1024u * 1024u)
 

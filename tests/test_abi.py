@@ -192,3 +192,37 @@ def bwd_packed(**kw):
 ])
 def test_packed_backward_rejects_before_launch(kw, status):
     assert bwd_packed(**kw) == status
+
+
+def mat(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, tr=FAKE + 3 * GIB, tc=FAKE + 3 * GIB + 256, bias=None, out=FAKE + GIB,
+             lse=FAKE + 2 * GIB, ws=FAKE + 4 * GIB, wsb=1 << 30, B=1, Hg=16, Wg=16, heads=2, d=32, M=8, shift=0,
+             dtype=F.FSW_BF16)
+    a.update(kw)
+    return F.flashswin_wattn_fwd_materialized(a["q"], a["k"], a["v"], a["tr"], a["tc"], a["bias"], a["out"], a["lse"],
+                                              a["ws"], a["wsb"], a["B"], a["Hg"], a["Wg"], a["heads"], a["d"], a["M"],
+                                              a["shift"], a["dtype"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=F.FSW_F32), F.FSW_ERR_UNSUPPORTED),   # bf16 only
+    (dict(d=16), F.FSW_ERR_UNSUPPORTED),              # d = 32 only
+    (dict(Hg=12), F.FSW_ERR_INVALID_ARG),
+    (dict(wsb=1024), F.FSW_ERR_WORKSPACE),            # too small
+    (dict(ws=None), F.FSW_ERR_WORKSPACE),
+    (dict(ws=FAKE + 4 * GIB + 16), F.FSW_ERR_WORKSPACE),  # not 256-byte aligned
+    (dict(bias=FAKE + 5 * GIB + 2), F.FSW_ERR_INVALID_ARG),  # misaligned bias
+    (dict(bias=FAKE + GIB), F.FSW_ERR_INVALID_ARG),   # bias inside out
+    (dict(ws=FAKE), F.FSW_ERR_INVALID_ARG),           # workspace over the inputs
+    (dict(q=None), F.FSW_ERR_INVALID_ARG),
+])
+def test_materialized_rejects_before_launch(kw, status):
+    assert mat(**kw) == status
+
+
+def test_materialized_workspace_size():
+    # 16 x 16 grid, M = 8: 4 windows x 2 heads x 64 rows x 64 floats
+    assert F.flashswin_wattn_fwd_materialized_workspace_size(1, 16, 16, 2, 32, 8, 0, F.FSW_BF16) == 4 * 2 * 64 * 64 * 4
+    # M = 5: N = 25 rows of 32 floats
+    assert F.flashswin_wattn_fwd_materialized_workspace_size(1, 10, 10, 1, 32, 5, 2, F.FSW_BF16) == 4 * 25 * 32 * 4
+    assert F.flashswin_wattn_fwd_materialized_workspace_size(1, 16, 16, 2, 32, 8, 0, F.FSW_F32) == 0

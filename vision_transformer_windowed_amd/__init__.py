@@ -30,11 +30,14 @@ from ._lib import (  # noqa: F401
     flashswin_wattn_bwd_noalloc,
     flashswin_wattn_bwd_packed,
     flashswin_wattn_fwd,
+    flashswin_wattn_fwd_materialized,
+    flashswin_wattn_fwd_materialized_workspace_size,
     flashswin_wattn_fwd_packed,
     load,
     wattn_bwd,
     wattn_bwd_packed,
     wattn_fwd,
+    wattn_fwd_materialized,
     wattn_fwd_packed,
     window_attention,
     window_attention_packed,

@@ -27,6 +27,8 @@ EXPORTED = (
     "flashswin_wattn_fwd_packed",
     "flashswin_wattn_bwd_packed",
     "flashswin_wattn_bwd_noalloc",
+    "flashswin_wattn_fwd_materialized_workspace_size",
+    "flashswin_wattn_fwd_materialized",
     "flashswin_status_string",
     "flashswin_version",
 )
@@ -63,6 +65,10 @@ def load():
     lib.flashswin_wattn_bwd_packed.argtypes = [vp] * 9 + [vp, sz, i64, i64, i64, i32, i32, i32, i32, i32, vp]
     lib.flashswin_wattn_bwd_noalloc.restype = i32
     lib.flashswin_wattn_bwd_noalloc.argtypes = [vp] * 13 + [i64, i64, i64, i32, i32, i32, i32, i32, vp]
+    lib.flashswin_wattn_fwd_materialized_workspace_size.restype = sz
+    lib.flashswin_wattn_fwd_materialized_workspace_size.argtypes = [i64, i64, i64, i32, i32, i32, i32, i32]
+    lib.flashswin_wattn_fwd_materialized.restype = i32
+    lib.flashswin_wattn_fwd_materialized.argtypes = [vp] * 9 + [sz, i64, i64, i64, i32, i32, i32, i32, i32, vp]
     lib.flashswin_status_string.restype = ctypes.c_char_p
     lib.flashswin_status_string.argtypes = [i32]
     lib.flashswin_version.restype = i32
@@ -111,6 +117,17 @@ def flashswin_wattn_bwd_noalloc(q, k, v, out, dout, lse, theta_row, theta_col, d
     """Raw call of the backward that uses the library's fixed per-GPU scratch instead of a workspace."""
     return load().flashswin_wattn_bwd_noalloc(q, k, v, out, dout, lse, theta_row, theta_col, dq, dk, dv,
                                               dtheta_row, dtheta_col, B, Hg, Wg, heads, d, M, shift, dtype, stream)
+
+
+def flashswin_wattn_fwd_materialized_workspace_size(B, Hg, Wg, heads, d, M, shift, dtype):
+    return load().flashswin_wattn_fwd_materialized_workspace_size(B, Hg, Wg, heads, d, M, shift, dtype)
+
+
+def flashswin_wattn_fwd_materialized(q, k, v, theta_row, theta_col, bias, out, lse, workspace, workspace_bytes, B,
+                                     Hg, Wg, heads, d, M, shift, dtype, stream):
+    """Raw call of the materialized comparison forward (scores in the caller's workspace)."""
+    return load().flashswin_wattn_fwd_materialized(q, k, v, theta_row, theta_col, bias, out, lse, workspace,
+                                                   workspace_bytes, B, Hg, Wg, heads, d, M, shift, dtype, stream)
 
 
 def flashswin_status_string(status):
@@ -196,6 +213,39 @@ def wattn_fwd(q, k, v, theta_row, theta_col, M, shift=0, out=None, lse=None, nee
     if st != FSW_OK:
         raise FlashSwinError(st, "flashswin_wattn_fwd")
     return out, lse
+
+
+def wattn_fwd_materialized(q, k, v, theta_row, theta_col, M, shift=0, bias=None, out=None, lse=None,
+                           workspace=None, need_lse=True):
+    """The materialized comparison forward (scores in HBM, then softmax, then P.V; bf16, d = 32), with an
+    optional relative-position bias [heads, 2M-1, 2M-1].  Returns (out, lse, workspace bytes used)."""
+    B, Hg, Wg, H, D = q.shape
+    code = _dtype_code(q)
+    dev = q.device
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check_grid(name, t, q.shape, q.dtype, dev)
+    for name, t in (("theta_row", theta_row), ("theta_col", theta_col)):
+        _check_grid(name, t, (H, D // 4), torch.float32, dev)
+    if bias is not None:
+        _check_grid("bias", bias, (H, 2 * int(M) - 1, 2 * int(M) - 1), torch.float32, dev)
+    if out is None:
+        out = torch.empty_like(q)
+    _check_grid("out", out, q.shape, q.dtype, dev)
+    if need_lse:
+        if lse is None:
+            lse = torch.empty((B, Hg, Wg, H), device=dev, dtype=torch.float32)
+        _check_grid("lse", lse, (B, Hg, Wg, H), torch.float32, dev)
+    else:
+        lse = None
+    nbytes = flashswin_wattn_fwd_materialized_workspace_size(B, Hg, Wg, H, D, int(M), int(shift), code)
+    workspace, wbytes = _workspace(workspace, nbytes, dev)
+    with torch.cuda.device(dev):
+        st = flashswin_wattn_fwd_materialized(_ptr(q), _ptr(k), _ptr(v), _ptr(theta_row), _ptr(theta_col),
+                                              _ptr(bias), _ptr(out), _ptr(lse), _ptr(workspace), wbytes, B, Hg, Wg,
+                                              H, D, int(M), int(shift), code, _stream(dev))
+    if st != FSW_OK:
+        raise FlashSwinError(st, "flashswin_wattn_fwd_materialized")
+    return out, lse, nbytes
 
 
 def wattn_bwd(q, k, v, out, dout, lse, theta_row, theta_col, M, shift=0, workspace=None, grads=None):

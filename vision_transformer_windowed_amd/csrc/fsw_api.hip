@@ -286,6 +286,40 @@ int flashswin_wattn_bwd_packed(const void* qkv, const void* out, const void* dou
                   dtheta_row, dtheta_col, workspace, workspace_bytes, g, dtype, hip_stream);
 }
 
+size_t flashswin_wattn_fwd_materialized_workspace_size(int64_t B, int64_t Hg, int64_t Wg, int heads, int d, int M,
+                                                       int shift, int dtype) {
+  fsw::Geom g;
+  if (check_shape(B, Hg, Wg, heads, d, M, shift, dtype, &g) != FSW_OK) return 0;
+  if (B == 0 || dtype != FSW_BF16 || d != 32) return 0;
+  return fsw::materialized_workspace_bytes(g);
+}
+
+int flashswin_wattn_fwd_materialized(const void* q, const void* k, const void* v, const float* theta_row,
+                                     const float* theta_col, const float* bias, void* out, float* lse,
+                                     void* workspace, size_t workspace_bytes, int64_t B, int64_t Hg, int64_t Wg,
+                                     int heads, int d, int M, int shift, int dtype, void* hip_stream) {
+  fsw::Geom g;
+  int st = check_shape(B, Hg, Wg, heads, d, M, shift, dtype, &g);
+  if (st != FSW_OK) return st;
+  if (dtype != FSW_BF16 || d != 32) return FSW_ERR_UNSUPPORTED;
+  if (B == 0) return FSW_OK;
+  if (!q || !k || !v || !out || !theta_row || !theta_col) return FSW_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16)) return FSW_ERR_INVALID_ARG;
+  if (!aligned(theta_row, 4) || !aligned(theta_col, 4) || (lse && !aligned(lse, 4)) || (bias && !aligned(bias, 4)))
+    return FSW_ERR_INVALID_ARG;
+  const size_t need = fsw::materialized_workspace_bytes(g);
+  if (!workspace || !aligned(workspace, 256) || workspace_bytes < need) return FSW_ERR_WORKSPACE;
+  const Sizes z = sizes_of(g, dtype);
+  const size_t bias_bytes = (size_t)heads * (2 * M - 1) * (2 * M - 1) * sizeof(float);
+  const Span outs[] = {{out, z.tens}, {lse, z.lse}, {workspace, need}};
+  const Span ins[] = {{q, z.tens},          {k, z.tens},          {v, z.tens},
+                      {theta_row, z.theta}, {theta_col, z.theta}, {bias, bias ? bias_bytes : 0}};
+  if (!outputs_disjoint(outs, ins)) return FSW_ERR_INVALID_ARG;
+  fsw::FwdArgs a{q, k, v, theta_row, theta_col, out, lse, g, dtype};
+  const hipError_t e = fsw::launch_fwd_materialized(a, bias, workspace, reinterpret_cast<hipStream_t>(hip_stream));
+  return e == hipSuccess ? FSW_OK : FSW_ERR_HIP;
+}
+
 int flashswin_wattn_bwd_noalloc(const void* q, const void* k, const void* v, const void* out, const void* dout,
                                 const float* lse, const float* theta_row, const float* theta_col, void* dq, void* dk,
                                 void* dv, float* dtheta_row, float* dtheta_col, int64_t B, int64_t Hg, int64_t Wg,

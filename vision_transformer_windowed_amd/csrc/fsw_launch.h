@@ -59,6 +59,10 @@ hipError_t launch_bwd_mfma(const BwdArgs& a, hipStream_t st);
 int64_t bwd_mfma_partials(const Geom& g);
 constexpr bool kHaveMfmaBwd = true;
 
+// Materialized comparison path (bf16, d == 32): scores in HBM, softmax, P.V.
+size_t materialized_workspace_bytes(const Geom& g);
+hipError_t launch_fwd_materialized(const FwdArgs& a, const float* bias, void* workspace, hipStream_t st);
+
 // Deterministic fixed-order reduction of dtheta partials into dth_row / dth_col.
 hipError_t launch_dtheta_reduce(const float* partials, int64_t n_partials, int64_t partials_per_head_stride,
                                 const Geom& g, float* dth_row, float* dth_col, hipStream_t st);

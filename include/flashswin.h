@@ -68,7 +68,9 @@ typedef enum { FSW_F32 = 0, FSW_BF16 = 1 } fsw_dtype;
  *   out and lse may not share a byte with q, k, v, theta_row, theta_col or each other
  *   (FSW_ERR_INVALID_ARG); the inputs may share memory.
  *   B >= 0 (B == 0 returns FSW_OK with nothing enqueued); Hg, Wg positive multiples of M;
- *   1 <= M <= 32; 0 <= shift < M; heads >= 1; d in {8, 16, 32, 64}; dtype FSW_F32 or FSW_BF16.
+ *   1 <= M <= 128; 0 <= shift < M; heads >= 1; d in {8, 16, 32, 64}; dtype FSW_F32 or FSW_BF16.
+ *   bf16 with d == 32 and M <= 32 runs on the MFMA kernels; every other case runs on kernels with
+ *   float32 arithmetic that stream the keys through LDS (correct for every supported shape, not tuned).
  *   Needs no workspace.  bf16 inputs are rounded once more to bf16 after the rotation and the
  *   scaling, P is rounded to bf16 for the P.V product, accumulation is float32; float32 inputs
  *   are computed in float32 throughout.
@@ -178,7 +180,7 @@ size_t flashswin_wattn_fwd_materialized_workspace_size(int64_t B, int64_t Hg, in
  *   q, k, v, theta_row, theta_col, out, lse: as in flashswin_wattn_fwd (lse may be NULL).  out, lse and
  *   the workspace may not share a byte with any input or with each other.
  *   Three kernels: scores (MFMA, fp16 operands when in range, else bf16; float32 scores), row softmax
- *   (bf16 probabilities), P.V (MFMA).  Implemented for dtype FSW_BF16 and d == 32 only
+ *   (bf16 probabilities), P.V (MFMA).  Implemented for dtype FSW_BF16, d == 32 and M <= 32 only
  *   (FSW_ERR_UNSUPPORTED otherwise).
  * Returns FSW_OK, FSW_ERR_INVALID_ARG, FSW_ERR_UNSUPPORTED, FSW_ERR_WORKSPACE or FSW_ERR_HIP.
  */

@@ -56,7 +56,7 @@ def fwd(**kw):
     (dict(d=6), F.FSW_ERR_INVALID_ARG),            # d not a multiple of 4
     (dict(d=12), F.FSW_ERR_UNSUPPORTED),           # valid d without a kernel
     (dict(d=128), F.FSW_ERR_UNSUPPORTED),
-    (dict(Hg=64, Wg=64, M=64), F.FSW_ERR_UNSUPPORTED),  # windows beyond 32 x 32
+    (dict(Hg=256, Wg=256, M=256), F.FSW_ERR_UNSUPPORTED),  # windows beyond 128 x 128
     (dict(heads=0), F.FSW_ERR_INVALID_ARG),
     (dict(B=-1), F.FSW_ERR_INVALID_ARG),
     (dict(M=0), F.FSW_ERR_INVALID_ARG),
@@ -207,6 +207,7 @@ def mat(**kw):
 @pytest.mark.parametrize("kw,status", [
     (dict(dtype=F.FSW_F32), F.FSW_ERR_UNSUPPORTED),   # bf16 only
     (dict(d=16), F.FSW_ERR_UNSUPPORTED),              # d = 32 only
+    (dict(Hg=64, Wg=64, M=64), F.FSW_ERR_UNSUPPORTED),  # M <= 32 only
     (dict(Hg=12), F.FSW_ERR_INVALID_ARG),
     (dict(wsb=1024), F.FSW_ERR_WORKSPACE),            # too small
     (dict(ws=None), F.FSW_ERR_WORKSPACE),

@@ -134,6 +134,11 @@ FWD_SMALL = [
     (1, 64, 64, 1, 32, 32, 31, "bf16"),
     (1, 64, 64, 1, 32, 32, 1, "bf16"),
     (1, 8, 16, 40, 32, 8, 3, "bf16"),
+    # windows larger than 32 x 32 (the float32-arithmetic kernels stream the keys)
+    (1, 40, 80, 1, 32, 40, 0, "bf16"),
+    (1, 64, 64, 1, 32, 64, 32, "bf16"),
+    (1, 48, 96, 2, 16, 48, 7, "f32"),
+    (1, 64, 64, 1, 64, 64, 0, "f32"),
 ]
 
 
@@ -386,6 +391,10 @@ BWD_SMALL = [
     (1, 64, 64, 1, 32, 32, 31, "bf16"),
     (1, 64, 64, 1, 32, 32, 1, "bf16"),
     (1, 8, 16, 40, 32, 8, 3, "bf16"),
+    # windows larger than 32 x 32
+    (1, 40, 40, 1, 32, 40, 13, "bf16"),
+    (1, 64, 64, 1, 32, 64, 0, "bf16"),
+    (1, 48, 48, 1, 16, 48, 24, "f32"),
 ]
 
 

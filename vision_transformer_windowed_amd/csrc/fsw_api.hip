@@ -2,7 +2,8 @@
 //
 // Every check runs on the host before any HIP call, so an invalid call never touches the device.
 // Dispatch: bf16 with d == 32 and M <= 32 goes to the MFMA kernels; everything else (float32
-// tensors, other d) goes to the float32-arithmetic kernels.
+// tensors, other d, windows larger than 32 x 32) goes to the float32-arithmetic kernels, which
+// stream the keys through LDS in tiles and take any window size up to kMaxWindow.
 #include <algorithm>
 #include <mutex>
 
@@ -17,7 +18,8 @@ static __device__ __align__(256) unsigned char scratch[FLASHSWIN_SCRATCH_BYTES];
 
 namespace {
 
-constexpr int kMaxM = 32;
+constexpr int kMaxM = 32;        // largest window of the MFMA kernels
+constexpr int kMaxWindow = 128;  // largest window of any kernel (N = 16384 tokens)
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
@@ -30,7 +32,7 @@ int check_shape(int64_t B, int64_t Hg, int64_t Wg, int heads, int d, int M, int 
   if (shift < 0 || shift >= M) return FSW_ERR_INVALID_ARG;
   if (d % 4 != 0) return FSW_ERR_INVALID_ARG;
   if (dtype != FSW_F32 && dtype != FSW_BF16) return FSW_ERR_INVALID_ARG;
-  if (!supported_d(d) || M > kMaxM) return FSW_ERR_UNSUPPORTED;
+  if (!supported_d(d) || M > kMaxWindow) return FSW_ERR_UNSUPPORTED;
   // int32 grid coordinates and int64 element offsets: keep every product well inside int64,
   // and the flat 1-D launch grid inside 2^31 workgroups.
   const int64_t lim = (int64_t)1 << 30;
@@ -290,7 +292,7 @@ size_t flashswin_wattn_fwd_materialized_workspace_size(int64_t B, int64_t Hg, in
                                                        int shift, int dtype) {
   fsw::Geom g;
   if (check_shape(B, Hg, Wg, heads, d, M, shift, dtype, &g) != FSW_OK) return 0;
-  if (B == 0 || dtype != FSW_BF16 || d != 32) return 0;
+  if (B == 0 || dtype != FSW_BF16 || d != 32 || M > kMaxM) return 0;
   return fsw::materialized_workspace_bytes(g);
 }
 
@@ -301,7 +303,7 @@ int flashswin_wattn_fwd_materialized(const void* q, const void* k, const void* v
   fsw::Geom g;
   int st = check_shape(B, Hg, Wg, heads, d, M, shift, dtype, &g);
   if (st != FSW_OK) return st;
-  if (dtype != FSW_BF16 || d != 32) return FSW_ERR_UNSUPPORTED;
+  if (dtype != FSW_BF16 || d != 32 || M > kMaxM) return FSW_ERR_UNSUPPORTED;
   if (B == 0) return FSW_OK;
   if (!q || !k || !v || !out || !theta_row || !theta_col) return FSW_ERR_INVALID_ARG;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16)) return FSW_ERR_INVALID_ARG;

@@ -44,7 +44,7 @@ struct BwdArgs {
   int64_t n_partials;
 };
 
-// Scalar (float32-arithmetic) paths: any d in {8,16,32,64}, any M <= 32, either dtype.
+// Scalar (float32-arithmetic) paths: any d in {8,16,32,64}, any window size, either dtype.
 hipError_t launch_fwd_scalar(const FwdArgs& a, hipStream_t st);
 hipError_t launch_bwd_scalar(const BwdArgs& a, hipStream_t st);
 // Number of dtheta partial rows the scalar backward writes.

@@ -199,6 +199,9 @@ def config_timing(dev, name, shift, passes, steps, warmup):
         res[tag + "_ms"] = round(ms, 4)
         res[tag + "_tflops"] = round(tf, 2)
         res[tag + "_mfma_frac"] = round(tf / BF16_MFMA_PEAK_TFLOPS, 4)
+        if tag == "fwd":  # q, k, v read and out written once, lse written: the forward's HBM floor
+            nbytes = 4 * q.numel() * q.element_size() + lse.numel() * 4
+            res["fwd_hbm_frac"] = round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
         if shift:
             res[tag + "_tflops_live"] = round(tf * live, 2)
     return res
@@ -403,7 +406,7 @@ def main():
                         "launches": CALL_LAUNCHES["wattn_bwd"], "launch_ms": round(bwd_ms, 4),
                         "flops_per_call": bwd_flops, "kernel_source_sha": sha}
     roofline = fwd_roofline if fwd_roofline is not None else bwd_roofline
-    m8 = packed = m16 = masked = bwd32 = mat = None
+    m8 = packed = m16 = masked = bwd32 = mat = d64 = None
     if not args.no_secondary and args.only == "step":
         m8 = m8_forward_roofline(dev, max(args.steps, 10), max(args.warmup, 2))
         packed = packed_forward(dev, max(args.steps, 10), max(args.warmup, 2))
@@ -412,6 +415,8 @@ def main():
                                max(args.warmup, 2))
         bwd32 = [config_timing(dev, "flashswin_t_s1_p2_m32_bwd", s, ("bwd",), max(args.steps, 10),
                                max(args.warmup, 2)) for s in WORKLOADS["flashswin_t_s1_p2_m32_bwd"]["shifts"]]
+        d64 = [config_timing(dev, "wide_heads_s1_p2_m16_d64", s, ("fwd",), max(args.steps, 10), max(args.warmup, 2))
+               for s in WORKLOADS["wide_heads_s1_p2_m16_d64"]["shifts"]]
         mat = materialized_vs_fused(dev, 5, 1)
 
     gpu_out = {"out": out, "lse": lse, "dq": grads[0], "dk": grads[1], "dv": grads[2]}
@@ -452,6 +457,7 @@ def main():
         "m32_shift16_fwd": masked,
         "m32_bwd_b32": bwd32,
         "materialized_vs_fused": mat,
+        "d64_m16_fwd": d64,
         "cpu_baseline": cpu,
         "parity_sample": parity,
         "input_gen_s": round(gen_s, 1),

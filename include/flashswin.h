@@ -69,11 +69,12 @@ typedef enum { FSW_F32 = 0, FSW_BF16 = 1 } fsw_dtype;
  *   (FSW_ERR_INVALID_ARG); the inputs may share memory.
  *   B >= 0 (B == 0 returns FSW_OK with nothing enqueued); Hg, Wg positive multiples of M;
  *   1 <= M <= 128; 0 <= shift < M; heads >= 1; d in {8, 16, 32, 64}; dtype FSW_F32 or FSW_BF16.
- *   bf16 with d == 32 and M <= 32 runs on the MFMA kernels; every other case runs on kernels with
- *   float32 arithmetic that stream the keys through LDS (correct for every supported shape, not tuned).
- *   Needs no workspace.  bf16 inputs are rounded once more to bf16 after the rotation and the
- *   scaling, P is rounded to bf16 for the P.V product, accumulation is float32; float32 inputs
- *   are computed in float32 throughout.
+ *   bf16 with d == 32 and M <= 32, and bf16 with d == 64 and M*M <= 512 (M <= 22), run on the MFMA
+ *   kernels; every other case runs on kernels with float32 arithmetic that stream the keys through
+ *   LDS (correct for every supported shape, not tuned).  Needs no workspace.  On the MFMA kernels
+ *   the rotated, scaled score operands are rounded to fp16 when every one of a window-head's is in
+ *   fp16 range, else to bf16; P is rounded to bf16 for the P.V product; accumulation is float32.
+ *   float32 inputs are computed in float32 throughout.
  * Returns FSW_OK, FSW_ERR_INVALID_ARG, FSW_ERR_UNSUPPORTED or FSW_ERR_HIP.
  */
 int flashswin_wattn_fwd(const void* q, const void* k, const void* v,

@@ -134,6 +134,15 @@ FWD_SMALL = [
     (1, 64, 64, 1, 32, 32, 31, "bf16"),
     (1, 64, 64, 1, 32, 32, 1, "bf16"),
     (1, 8, 16, 40, 32, 8, 3, "bf16"),
+    # d = 64 on MFMA (windows of up to 512 padded tokens); M = 23 runs the float32-arithmetic kernels
+    (1, 16, 16, 2, 64, 8, 3, "bf16"),
+    (1, 33, 33, 1, 64, 11, 4, "bf16"),
+    (1, 24, 24, 2, 64, 12, 5, "bf16"),
+    (1, 32, 32, 2, 64, 16, 0, "bf16"),
+    (1, 48, 32, 3, 64, 16, 8, "bf16"),
+    (1, 40, 40, 2, 64, 20, 7, "bf16"),
+    (1, 44, 44, 1, 64, 22, 5, "bf16"),
+    (1, 46, 46, 1, 64, 23, 0, "bf16"),
     # windows larger than 32 x 32 (the float32-arithmetic kernels stream the keys)
     (1, 40, 80, 1, 32, 40, 0, "bf16"),
     (1, 64, 64, 1, 32, 64, 32, "bf16"),
@@ -201,13 +210,14 @@ def test_forward_nan_stays_in_its_window_region():
     assert not torch.isnan(out[..., 1, :].float()).any()  # other head untouched
 
 
-@pytest.mark.parametrize("M,shift,grid", [(32, 16, 64), (32, 0, 64), (8, 3, 32), (12, 5, 36)])
-def test_forward_loose_bound_falls_back(M, shift, grid):
+@pytest.mark.parametrize("M,shift,grid,D", [(32, 16, 64, 32), (32, 0, 64, 32), (8, 3, 32, 32), (12, 5, 36, 32),
+                                            (16, 8, 32, 64), (20, 7, 40, 64)])
+def test_forward_loose_bound_falls_back(M, shift, grid, D):
     """One key with a large norm makes max|q| * max|k| overshoot the true row maximum of most
     queries by more than 80 (log2 units): their sums under the bound reference fall below
     2^-80 and the kernels redo those rows with the exact maximum.  Logits reach ~40 here; the
     operands stay in fp16 range, so LSE is held to the fp16 rounding bound (lse_rounding_bound)."""
-    H, D = 2, 32
+    H = 2
     x = make_inputs(1, grid, grid, H, D, "bf16", seed=31 + M)
     ky, kx = grid // 2 + 1, 3
     x["k"][0, ky, kx, 0] *= 14.0
@@ -237,16 +247,18 @@ def _aligned_large_inputs(B, grid, H, D, amp, seed):
     return x
 
 
-@pytest.mark.parametrize("M,shift,grid,amp,u", [
-    (32, 16, 64, 1024.0, U_FP16), (32, 0, 64, 4096.0, U_BF16), (8, 3, 32, 1024.0, U_FP16),
-    (8, 0, 32, 4096.0, U_BF16), (16, 8, 32, 1024.0, U_FP16), (12, 5, 36, 4096.0, U_BF16)])
-def test_forward_aligned_large_norms(M, shift, grid, amp, u):
+@pytest.mark.parametrize("M,shift,grid,amp,u,D", [
+    (32, 16, 64, 1024.0, U_FP16, 32), (32, 0, 64, 4096.0, U_BF16, 32), (8, 3, 32, 1024.0, U_FP16, 32),
+    (8, 0, 32, 4096.0, U_BF16, 32), (16, 8, 32, 1024.0, U_FP16, 32), (12, 5, 36, 4096.0, U_BF16, 32),
+    (16, 8, 32, 1024.0, U_FP16, 64), (20, 0, 40, 4096.0, U_BF16, 64)])
+def test_forward_aligned_large_norms(M, shift, grid, amp, u, D):
     """Aligned queries and keys with large norms (q = k): the computed score of a query with its own
     key sits at the bound up to operand rounding, which alone can exceed it by far more than 128
     (log2 units).  The widened reference keeps every exponent finite, the sums underflow, and the
     exact-maximum pass gives O = v of the query's own token.  amp = 1024 keeps the rotated operands in
-    fp16 range (|k~| = 5793); amp = 4096 (|k~| = 23170) takes the bf16 operand path."""
-    H, D = 2, 32
+    fp16 range (|k~| = 5793 at d = 32, 8192 at d = 64); amp = 4096 (|k~| = 23170, 32768) takes the
+    bf16 operand path."""
+    H = 2
     x = _aligned_large_inputs(1, grid, H, D, amp, seed=71 + M + shift)
     xd = to_dev(x)
     out, lse = F.wattn_fwd(xd["q"], xd["k"], xd["v"], xd["theta_row"], xd["theta_col"], M, shift)
@@ -275,7 +287,8 @@ def _scaled_window_inputs(case, seed, with_dout):
 
 
 BF16_PATH_CASES = [(1, 64, 64, 2, 32, 32, 16), (1, 64, 64, 2, 32, 32, 0), (2, 32, 32, 3, 32, 8, 3),
-                   (1, 32, 32, 3, 32, 8, 0), (1, 32, 48, 2, 32, 16, 8), (1, 24, 24, 2, 32, 12, 5)]
+                   (1, 32, 32, 3, 32, 8, 0), (1, 32, 48, 2, 32, 16, 8), (1, 24, 24, 2, 32, 12, 5),
+                   (1, 32, 48, 2, 64, 16, 8), (1, 40, 40, 1, 64, 20, 3)]
 
 
 @pytest.mark.parametrize("case", BF16_PATH_CASES, ids=lambda c: "B{}_{}x{}_h{}_d{}_M{}_s{}".format(*c))
@@ -344,16 +357,18 @@ SAMPLE_IMAGES = {
     "swin_t_s1_p4_m8": [0, 1, 127],
     "flashswin_t_s1_p2_m32": [0, 127],
     "flashswin_t_s2_shift16_m32": [0, 64, 127],
+    "wide_heads_s1_p2_m16_d64": [0, 63],
 }
 
 
-@pytest.mark.parametrize("name", ["tiny_f32_m8", "swin_t_s1_p4_m8", "flashswin_t_s1_p2_m32",
-                                  "flashswin_t_s2_shift16_m32"])
-def test_forward_workload(name):
+@pytest.mark.parametrize("name,s", [("tiny_f32_m8", 0), ("swin_t_s1_p4_m8", 0), ("flashswin_t_s1_p2_m32", 0),
+                                    ("flashswin_t_s2_shift16_m32", 16), ("wide_heads_s1_p2_m16_d64", 0),
+                                    ("wide_heads_s1_p2_m16_d64", 8)])
+def test_forward_workload(name, s):
     w = WORKLOADS[name]
+    assert s in w["shifts"]
     x = workload_inputs(name, with_dout=False)
     xd = to_dev(x)
-    s = w["shifts"][0]
     out, lse = F.wattn_fwd(xd["q"], xd["k"], xd["v"], xd["theta_row"], xd["theta_col"], w["M"], s)
     torch.cuda.synchronize()
     imgs = SAMPLE_IMAGES.get(name, list(range(w["B"])))

@@ -1,9 +1,10 @@
 // C ABI of the window-attention library: argument validation, workspace sizing, dispatch.
 //
 // Every check runs on the host before any HIP call, so an invalid call never touches the device.
-// Dispatch: bf16 with d == 32 and M <= 32 goes to the MFMA kernels; everything else (float32
-// tensors, other d, windows larger than 32 x 32) goes to the float32-arithmetic kernels, which
-// stream the keys through LDS in tiles and take any window size up to kMaxWindow.
+// Dispatch: bf16 with d == 32 and M <= 32 goes to the MFMA kernels, forward and backward; the bf16
+// d == 64 forward of windows up to 22 x 22 too.  Everything else (float32 tensors, other d, larger
+// windows, the d == 64 backward) goes to the float32-arithmetic kernels, which stream the keys
+// through LDS in tiles and take any window size up to kMaxWindow.
 #include <algorithm>
 #include <mutex>
 
@@ -112,8 +113,10 @@ WsLayout workspace_layout(const fsw::Geom& g, bool mfma) {
   return w;
 }
 
-bool use_mfma_fwd(const fsw::Geom& g, int dtype) { return dtype == FSW_BF16 && g.d == 32 && g.M <= kMaxM; }
-bool use_mfma(const fsw::Geom& g, int dtype) { return fsw::kHaveMfmaBwd && use_mfma_fwd(g, dtype); }
+bool use_mfma_fwd(const fsw::Geom& g, int dtype) { return dtype == FSW_BF16 && fsw::fwd_mfma_supported(g); }
+bool use_mfma(const fsw::Geom& g, int dtype) {
+  return fsw::kHaveMfmaBwd && dtype == FSW_BF16 && g.d == 32 && g.M <= kMaxM;
+}
 
 // Pointer checks and dispatch of a forward whose shape (and q/k/v token stride) is in g.
 int fwd_impl(const void* q, const void* k, const void* v, const float* theta_row, const float* theta_col, void* out,

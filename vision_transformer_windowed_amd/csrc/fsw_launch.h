@@ -50,11 +50,14 @@ hipError_t launch_bwd_scalar(const BwdArgs& a, hipStream_t st);
 // Number of dtheta partial rows the scalar backward writes.
 int64_t bwd_scalar_partials(const Geom& g);
 
-// bf16 MFMA paths (d == 32, M <= 32).
+// bf16 MFMA forward: d == 32 with M <= 32, and d == 64 with at most 512 padded window tokens
+// (M <= 22), where the window's K~ and V rows fit LDS.
+bool fwd_mfma_supported(const Geom& g);
 hipError_t launch_fwd_mfma(const FwdArgs& a, hipStream_t st);
 // M = 8 windows: one wave per window-head.
 bool fwd_m8_supported(const Geom& g);
 hipError_t launch_fwd_m8(const FwdArgs& a, hipStream_t st);
+// bf16 MFMA backward (d == 32, M <= 32).
 hipError_t launch_bwd_mfma(const BwdArgs& a, hipStream_t st);
 int64_t bwd_mfma_partials(const Geom& g);
 constexpr bool kHaveMfmaBwd = true;

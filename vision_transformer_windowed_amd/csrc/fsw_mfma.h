@@ -198,11 +198,12 @@ __device__ __forceinline__ uint32_t wave_or(uint32_t x) {
   return x;
 }
 
-// Rotate 8 consecutive channels (4 pairs) with the LDS sin/cos table; pairs j0..j0+3 of `axis`.
+// Rotate 8 consecutive channels (4 pairs) with the LDS sin/cos table [axis][position][p4] (p4 = d/4
+// pairs per axis); pairs j0..j0+3 of `axis`.
 __device__ __forceinline__ void rotate8(float (&x)[8], const float* sn, const float* cs, int axis, int M, int p,
-                                        int j0) {
-  const float* s = sn + (axis * M + p) * 8 + j0;
-  const float* c = cs + (axis * M + p) * 8 + j0;
+                                        int j0, int p4 = 8) {
+  const float* s = sn + (axis * M + p) * p4 + j0;
+  const float* c = cs + (axis * M + p) * p4 + j0;
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
     const float a = x[2 * u], b = x[2 * u + 1];

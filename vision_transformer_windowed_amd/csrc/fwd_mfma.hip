@@ -1,4 +1,5 @@
-// bf16 window-attention forward on MFMA (gfx950), d = 32, any M <= 32.
+// bf16 window-attention forward on MFMA (gfx950), d = 32 (any M <= 32) and d = 64 (windows of up to
+// 512 tokens, M <= 22, whose K~ and V fit LDS).
 //
 // Exact softmax attention inside each window with window-local 2D RoPE on Q and K, without storing
 // the score matrix (FlashSwin paper card, "FLASHSWIN: Unlocking Large Windows and Dense Tokens in
@@ -7,8 +8,10 @@
 // Workgroup = (window, head, block of NWAVES*32 queries).  The window's K (rotated) and V rows are
 // staged once in LDS (the P.V operands are read transposed by ds_read_b64_tr_b16); each wave owns
 // 32 queries (one MFMA tile) held as B operands and walks the keys in 32-key blocks:
-// S^T = K~ Q^T (2 MFMAs), P = exp2(S^T), O^T += V^T P^T (2 MFMAs).  One tile per wave keeps a wave
-// under 128 registers, so four waves share each SIMD and hide each other's latencies.  The shift
+// S^T = K~ Q^T (d/16 MFMAs), P = exp2(S^T), O^T += V^T P^T (d/16 MFMAs: d/32 output tiles of 32
+// channels).  One tile per wave keeps a wave
+// under 128 registers at d = 32, so four waves share each SIMD and hide each other's latencies
+// (d = 64 doubles the query operands and O^T accumulators: two waves per SIMD, up to 256).  The shift
 // and window partition are index arithmetic on the loads and stores.  A window with a single Swin
 // region and an even number of whole 32-key blocks takes a branch-free, software-pipelined loop
 // (the score MFMAs of block b+1 are issued before the exponentials of block b).  Other windows mask
@@ -41,37 +44,54 @@ namespace {
 constexpr float kLowSum = 8.271806125530277e-25f;  // 2^-80
 constexpr int kMaxWaves = 16;
 constexpr int kMaxQBlocks = 2;
+constexpr int kMaxNP64 = 512;  // d = 64: largest padded window whose K~ and V rows fit LDS
 
 __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 __device__ __forceinline__ uint32_t uniform(uint32_t x) { return (uint32_t)__builtin_amdgcn_readfirstlane((int)x); }
 
+// Row strides (elements) of the staged K~ and V rows for head dim D.  K~ rows carry 16 bytes of pad
+// (conflict-free 16-byte row reads); 64-channel V rows too (128-byte rows would put the four rows of a
+// transposing read in two bank groups), 32-channel V rows need none.
+template <int D>
+struct FwdDim {
+  static constexpr int KS = D + 8;
+  static constexpr int VS = D == 32 ? 32 : D + 8;
+  static constexpr int P4 = D / 4;      // RoPE pairs per axis
+  static constexpr int PARTS = D / 8;   // 16-byte parts of a token row
+  static constexpr int KSTEPS = D / 16; // k-steps of a score product
+  static constexpr int OT = D / 32;     // O^T tiles of 32 channels
+};
+static_assert(FwdDim<32>::KS == kKStride, "d = 32 K~ stride");
+
 struct FwdSmem {
-  uint16_t* K;     // [NP][kKStride]
-  uint16_t* V;     // [NP][32] row-major; P.V operands come from transposing LDS reads
-  float* sn;       // [2][M][8]  sin of RoPE angle (row axis, column axis)
-  float* cs;       // [2][M][8]  cos
+  uint16_t* K;     // [NP][KS]
+  uint16_t* V;     // [NP][VS] row-major; P.V operands come from transposing LDS reads
+  float* sn;       // [2][M][D/4]  sin of RoPE angle (row axis, column axis)
+  float* cs;       // [2][M][D/4]  cos
   uint16_t* rc;    // [NP]  r << 8 | c of every slot (see WinOrder); read in windows split by a shift
   uint8_t* lab;    // [NP]  key labels, 0xff past the window
   uint32_t* blk;   // [NP/32]  bits 0..8: labels present, bit 9: all 32 keys valid
   float* red;      // [2 * kMaxWaves]: per-wave max |k~|^2, then max |q^|^2
 };
 
+template <int D>
 __host__ __device__ inline size_t fwd_smem_bytes(int NP, int M) {
-  size_t b = (size_t)NP * kKStride * 2 + (size_t)NP * 32 * 2;
-  b += (size_t)2 * 2 * M * 8 * 4;
+  size_t b = (size_t)NP * FwdDim<D>::KS * 2 + (size_t)NP * FwdDim<D>::VS * 2;
+  b += (size_t)2 * 2 * M * FwdDim<D>::P4 * 4;
   b += (size_t)NP * 2 + (size_t)NP;
   b = (b + 3) & ~(size_t)3;
   b += (size_t)(NP / 32) * 4 + 2 * kMaxWaves * 4;
   return b;
 }
 
+template <int D>
 __device__ inline FwdSmem carve(unsigned char* base, int NP, int M) {
   FwdSmem s;
   s.K = reinterpret_cast<uint16_t*>(base);
-  s.V = s.K + (size_t)NP * kKStride;
-  s.sn = reinterpret_cast<float*>(s.V + (size_t)NP * 32);
-  s.cs = s.sn + 2 * M * 8;
-  s.rc = reinterpret_cast<uint16_t*>(s.cs + 2 * M * 8);
+  s.V = s.K + (size_t)NP * FwdDim<D>::KS;
+  s.sn = reinterpret_cast<float*>(s.V + (size_t)NP * FwdDim<D>::VS);
+  s.cs = s.sn + 2 * M * FwdDim<D>::P4;
+  s.rc = reinterpret_cast<uint16_t*>(s.cs + 2 * M * FwdDim<D>::P4);
   s.lab = reinterpret_cast<uint8_t*>(s.rc + NP);
   size_t off = ((size_t)(s.lab + NP - base) + 3) & ~(size_t)3;
   s.blk = reinterpret_cast<uint32_t*>(base + off);
@@ -108,21 +128,35 @@ __device__ __forceinline__ int64_t tok_of(const Geom& g, const WinHead& w, int M
   return (w.b * g.Hg + y) * g.Wg + x;
 }
 
+// The wave's query operands: k-step t of the score product takes channels 16t + 8h .. 16t + 8h + 7.
+template <int D>
+using QOps = uint4[FwdDim<D>::KSTEPS];
+// The wave's O^T accumulators: tile t holds channels 32t .. 32t + 31.
+template <int D>
+using OAcc = f32x16_t[FwdDim<D>::OT];
+
 // Score tile S^T = K~ Q^T + cinit of key block b.
-template <bool H16>
-__device__ __forceinline__ f32x16_t block_scores(const FwdSmem& sm, int b, int row, int h, uint4 qb0, uint4 qb1,
+template <bool H16, int D>
+__device__ __forceinline__ f32x16_t block_scores(const FwdSmem& sm, int b, int row, int h, const QOps<D>& qop,
                                                  const f32x16_t& cinit) {
-  const uint16_t* krow = sm.K + (size_t)(b * 32 + row) * kKStride + 8 * h;
-  f32x16_t s = mfma_op<H16>(*reinterpret_cast<const uint4*>(krow), qb0, cinit);
-  return mfma_op<H16>(*reinterpret_cast<const uint4*>(krow + 16), qb1, s);
+  const uint16_t* krow = sm.K + (size_t)(b * 32 + row) * FwdDim<D>::KS + 8 * h;
+  f32x16_t s = mfma_op<H16>(*reinterpret_cast<const uint4*>(krow), qop[0], cinit);
+#pragma unroll
+  for (int t = 1; t < FwdDim<D>::KSTEPS; ++t) s = mfma_op<H16>(*reinterpret_cast<const uint4*>(krow + 16 * t), qop[t], s);
+  return s;
 }
 
 // P = exp2(S^T - m) of key block b (masked by `live` when MASK), row sums, O^T += V^T P^T.
-template <bool MASK, bool SUBM>
+template <bool MASK, bool SUBM, int D>
 __device__ __forceinline__ void block_consume(const FwdSmem& sm, int b, int lane, uint32_t live, float m,
-                                              const f32x16_t& s, float& la, float& lb, f32x16_t& o) {
-  const bf16x8_t va0 = as_bf16x8(tr_operand(sm.V, 32, b * 32, lane));
-  const bf16x8_t va1 = as_bf16x8(tr_operand(sm.V, 32, b * 32 + 16, lane));
+                                              const f32x16_t& s, float& la, float& lb, OAcc<D>& o) {
+  constexpr int OT = FwdDim<D>::OT, VS = FwdDim<D>::VS;
+  bf16x8_t va0[OT], va1[OT];
+#pragma unroll
+  for (int t = 0; t < OT; ++t) {
+    va0[t] = as_bf16x8(tr_operand(sm.V + 32 * t, VS, b * 32, lane));
+    va1[t] = as_bf16x8(tr_operand(sm.V + 32 * t, VS, b * 32 + 16, lane));
+  }
   float p[16];
 #pragma unroll
   for (int v = 0; v < 16; ++v) p[v] = __builtin_amdgcn_exp2f(SUBM ? s[v] - m : s[v]);
@@ -138,24 +172,35 @@ __device__ __forceinline__ void block_consume(const FwdSmem& sm, int b, int lane
     la = add_pair(pk[e], la);
     lb = add_pair(pk[e + 1], lb);
   }
-  o = mfma32x32x16(va0, as_bf16x8(make_uint4(pk[0], pk[1], pk[2], pk[3])), o);
-  o = mfma32x32x16(va1, as_bf16x8(make_uint4(pk[4], pk[5], pk[6], pk[7])), o);
+#pragma unroll
+  for (int t = 0; t < OT; ++t) {
+    o[t] = mfma32x32x16(va0[t], as_bf16x8(make_uint4(pk[0], pk[1], pk[2], pk[3])), o[t]);
+    o[t] = mfma32x32x16(va1[t], as_bf16x8(make_uint4(pk[4], pk[5], pk[6], pk[7])), o[t]);
+  }
 }
 
 // Pipelined pass over an even number of key blocks kb0 .. kb1-1, all whole and of the wave's one
 // label: no masks, no skips, two score buffers.
-template <bool H16>
-__device__ __forceinline__ void pass_uniform(const FwdSmem& sm, int kb0, int kb1, int lane, uint4 qb0, uint4 qb1,
-                                             const f32x16_t& cinit, float& l, f32x16_t& o) {
+template <bool H16, int D>
+__device__ __forceinline__ void pass_uniform(const FwdSmem& sm, int kb0, int kb1, int lane, const QOps<D>& qop,
+                                             const f32x16_t& cinit, float& l, OAcc<D>& o) {
   const int h = lane >> 5, row = lane & 31;
   float la = 0.f, lb = 0.f;
+  if constexpr (D == 64) {  // no prefetch: the second score tile does not fit the register budget
+    for (int kb = kb0; kb < kb1; ++kb) {
+      const f32x16_t sa = block_scores<H16, D>(sm, kb, row, h, qop, cinit);
+      block_consume<false, false, D>(sm, kb, lane, 0xffffu, 0.f, sa, la, lb, o);
+    }
+    l = la + lb;
+    return;
+  }
   // the prefetch after the last pair recomputes block kb1-1 and is not used
-  f32x16_t sa = block_scores<H16>(sm, kb0, row, h, qb0, qb1, cinit);
+  f32x16_t sa = block_scores<H16, D>(sm, kb0, row, h, qop, cinit);
   for (int kb = kb0; kb < kb1; kb += 2) {
-    const f32x16_t sb = block_scores<H16>(sm, kb + 1, row, h, qb0, qb1, cinit);
-    block_consume<false, false>(sm, kb, lane, 0xffffu, 0.f, sa, la, lb, o);
-    sa = block_scores<H16>(sm, min(kb + 2, kb1 - 1), row, h, qb0, qb1, cinit);
-    block_consume<false, false>(sm, kb + 1, lane, 0xffffu, 0.f, sb, la, lb, o);
+    const f32x16_t sb = block_scores<H16, D>(sm, kb + 1, row, h, qop, cinit);
+    block_consume<false, false, D>(sm, kb, lane, 0xffffu, 0.f, sa, la, lb, o);
+    sa = block_scores<H16, D>(sm, min(kb + 2, kb1 - 1), row, h, qop, cinit);
+    block_consume<false, false, D>(sm, kb + 1, lane, 0xffffu, 0.f, sb, la, lb, o);
   }
   l = la + lb;
 }
@@ -164,10 +209,10 @@ __device__ __forceinline__ void pass_uniform(const FwdSmem& sm, int kb0, int kb1
 //  MODE 0: scores offset by `cinit`; p = exp2(s); accumulate l and O.
 //  MODE 1: exact maximum only: m = max over live keys of the raw score.
 //  MODE 2: p = exp2(s - m) with the exact per-query maximum; accumulate l and O.
-template <int MODE, bool H16>
+template <int MODE, bool H16, int D>
 __device__ __forceinline__ void pass_general(const FwdSmem& sm, int NB, int lane, uint32_t wave_labels,
-                                             bool wave_single, uint4 qb0, uint4 qb1, int qlab,
-                                             const f32x16_t& cinit, float& m, float& l, f32x16_t& o) {
+                                             bool wave_single, const QOps<D>& qop, int qlab,
+                                             const f32x16_t& cinit, float& m, float& l, OAcc<D>& o) {
   const int h = lane >> 5, row = lane & 31;
   float la = l, lb = 0.f;
   for (int kb = 0; kb < NB; ++kb) {
@@ -175,7 +220,7 @@ __device__ __forceinline__ void pass_general(const FwdSmem& sm, int NB, int lane
     const uint32_t bl = info & 0x1ffu;
     if ((bl & wave_labels) == 0) continue;  // no query of this wave may see these keys
     const bool need_mask = !((info >> 9) & 1u) || !wave_single || bl != wave_labels;
-    const f32x16_t s = block_scores<H16>(sm, kb, row, h, qb0, qb1, cinit);
+    const f32x16_t s = block_scores<H16, D>(sm, kb, row, h, qop, cinit);
     const uint32_t live = need_mask ? live_bits(sm.lab, kb, h, qlab) : 0xffffu;
     if (MODE == 1) {
 #pragma unroll
@@ -184,9 +229,9 @@ __device__ __forceinline__ void pass_general(const FwdSmem& sm, int NB, int lane
       continue;
     }
     if (need_mask)
-      block_consume<true, MODE == 2>(sm, kb, lane, live, m, s, la, lb, o);
+      block_consume<true, MODE == 2, D>(sm, kb, lane, live, m, s, la, lb, o);
     else
-      block_consume<false, MODE == 2>(sm, kb, lane, live, m, s, la, lb, o);
+      block_consume<false, MODE == 2, D>(sm, kb, lane, live, m, s, la, lb, o);
   }
   l = la + lb;
 }
@@ -194,20 +239,20 @@ __device__ __forceinline__ void pass_general(const FwdSmem& sm, int NB, int lane
 // The attention of the wave's tile: the pipelined pass when its live keys are one even run of
 // whole blocks kb0 .. kb1-1 of its own label (run), else the general pass; then the exact-maximum fallback
 // when the bound reference was too loose for some query.
-template <bool H16>
+template <bool H16, int D>
 __device__ __forceinline__ void attend(const FwdSmem& sm, int NB, int lane, bool run, int kb0, int kb1,
                                        uint32_t wave_labels,
-                                       bool wave_single, uint4 qb0, uint4 qb1, int qlab, bool qvalid, float bound,
-                                       float& ref, float& l, f32x16_t& o) {
+                                       bool wave_single, const QOps<D>& qop, int qlab, bool qvalid, float bound,
+                                       float& ref, float& l, OAcc<D>& o) {
   const float refb = bound * bound_margin<H16>();
   f32x16_t cinit;
 #pragma unroll
   for (int v2 = 0; v2 < 16; ++v2) cinit[v2] = -refb;
   float m = 0.f;
   if (run)
-    pass_uniform<H16>(sm, kb0, kb1, lane, qb0, qb1, cinit, l, o);
+    pass_uniform<H16, D>(sm, kb0, kb1, lane, qop, cinit, l, o);
   else if (wave_labels != 0)
-    pass_general<0, H16>(sm, NB, lane, wave_labels, wave_single, qb0, qb1, qlab, cinit, m, l, o);
+    pass_general<0, H16, D>(sm, NB, lane, wave_labels, wave_single, qop, qlab, cinit, m, l, o);
   ref = refb;
   const float lsum = halves_sum(l);
   const bool low = qvalid && !(lsum >= kLowSum && lsum < INFINITY);
@@ -216,30 +261,34 @@ __device__ __forceinline__ void attend(const FwdSmem& sm, int NB, int lane, bool
 #pragma unroll
     for (int v2 = 0; v2 < 16; ++v2) zero[v2] = 0.f;
     m = -INFINITY;
-    pass_general<1, H16>(sm, NB, lane, wave_labels, wave_single, qb0, qb1, qlab, zero, m, l, o);
+    pass_general<1, H16, D>(sm, NB, lane, wave_labels, wave_single, qop, qlab, zero, m, l, o);
     m = halves_max(m);
     if (!(m > -INFINITY)) m = 0.f;  // invalid query lanes
     l = 0.f;
 #pragma unroll
-    for (int v2 = 0; v2 < 16; ++v2) o[v2] = 0.f;
-    pass_general<2, H16>(sm, NB, lane, wave_labels, wave_single, qb0, qb1, qlab, zero, m, l, o);
+    for (int t = 0; t < FwdDim<D>::OT; ++t)
+#pragma unroll
+      for (int v2 = 0; v2 < 16; ++v2) o[t][v2] = 0.f;
+    pass_general<2, H16, D>(sm, NB, lane, wave_labels, wave_single, qop, qlab, zero, m, l, o);
     ref = m;
   }
 }
 
 // Rotated K~ rows of the staged items (raw bf16 loads in kraw) into LDS in fp16 (h16) or bf16;
-// returns this thread's max |k|^2 (rotation keeps norms).
-template <int MAXIT>
+// returns this thread's max |k|^2 (rotation keeps norms).  Item it is 16-byte part it % PARTS of
+// key it / PARTS; the PARTS parts of a key are consecutive lanes.
+template <int MAXIT, int D>
 __device__ __forceinline__ float stage_k(const FwdSmem& sm, const uint4 (&kraw)[MAXIT], int M, bool split, int NP,
                                          int tid, int nt, bool h16) {
+  constexpr int PARTS = FwdDim<D>::PARTS, AXP = PARTS / 2;
   const int N = M * M;
   float kmax2 = 0.f;
 #pragma unroll
   for (int i = 0; i < MAXIT; ++i) {
     const int it = tid + i * nt;
-    if (it >= NP * 4) break;  // uniform across a wave: NP * 4 is a multiple of 64
-    const int key = it >> 2;
-    const int part = it & 3;
+    if (it >= NP * PARTS) break;  // uniform across a wave: NP * PARTS is a multiple of 64
+    const int key = it / PARTS;
+    const int part = it % PARTS;
     uint4 kr = make_uint4(0, 0, 0, 0);
     float ss = 0.f;
     if (key < N) {
@@ -248,29 +297,32 @@ __device__ __forceinline__ float stage_k(const FwdSmem& sm, const uint4 (&kraw)[
       ss = norm2_bf16x8(kraw[i], 0.f);
       float x[8];
       unpack8(kraw[i], x);
-      const int axis = part >> 1;
-      rotate8(x, sm.sn, sm.cs, axis, M, axis ? c : r, (part & 1) * 4);
+      const int axis = part / AXP;
+      rotate8(x, sm.sn, sm.cs, axis, M, axis ? c : r, (part % AXP) * 4, FwdDim<D>::P4);
       kr = pack8_op(x, h16);
     }
-    *reinterpret_cast<uint4*>(sm.K + (size_t)key * kKStride + part * 8) = kr;
-    ss = quad_sum(ss);  // the 4 parts of the key
+    *reinterpret_cast<uint4*>(sm.K + (size_t)key * FwdDim<D>::KS + part * 8) = kr;
+    ss = quad_sum(ss);  // the parts of the key
+    if (PARTS == 8)  // the other quad of the 8 lanes (row_half_mirror: lane i <- lane 7 - i)
+      ss += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(ss), 0x141, 0xf, 0xf, false));
     kmax2 = fmaxf(kmax2, ss);
   }
   return kmax2;
 }
 
 // Global loads of the thread's K and V items (16 bytes each), issued together.
-template <int MAXIT>
+template <int MAXIT, int D>
 __device__ __forceinline__ void load_kv(const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, const Geom& g,
                                         const WinHead& w, const uint16_t* rc, int M, int NP, int tid, int nt,
                                         bool with_v, uint4 (&kraw)[MAXIT], uint4 (&vraw)[MAXIT]) {
+  constexpr int PARTS = FwdDim<D>::PARTS;
   const int N = M * M;
 #pragma unroll
   for (int i = 0; i < MAXIT; ++i) {
     const int it = tid + i * nt;
-    const int key = it >> 2;
+    const int key = it / PARTS;
     kraw[i] = vraw[i] = make_uint4(0, 0, 0, 0);
-    if (it < NP * 4 && key < N) {
+    if (it < NP * PARTS && key < N) {
       int r, c;
       if (rc) {
         const int rk = rc[key];
@@ -280,18 +332,25 @@ __device__ __forceinline__ void load_kv(const uint16_t* __restrict__ k, const ui
         r = key / M;
         c = key - (key / M) * M;
       }
-      const int64_t off = tok_of(g, w, M, r, c) * g.xs + w.h * 32 + (it & 3) * 8;
+      const int64_t off = tok_of(g, w, M, r, c) * g.xs + w.h * D + (it % PARTS) * 8;
       kraw[i] = *reinterpret_cast<const uint4*>(k + off);
       if (with_v) vraw[i] = *reinterpret_cast<const uint4*>(v + off);
     }
   }
 }
 
+// Waves per SIMD the register budget is set for: four (128 registers) for workgroups of 8 or more waves
+// at d = 32; d = 64 holds twice the query operands and O^T accumulators and takes two (256).
+template <int NWAVES, int D>
+constexpr int fwd_min_waves() {
+  return D == 32 ? (NWAVES >= 8 ? 4 : 1) : (NWAVES >= 4 ? 2 : 1);
+}
+
 // NWAVES waves of one 32-query tile each; one workgroup per window-head stages the window's K/V
 // once and then walks its query blocks of NWAVES*32 queries.  MT: compile-time window size
-// (0 = g.M at run time).  NPMAX: the largest padded window this configuration serves.
-template <int NWAVES, int MT, int NPMAX>
-__global__ __launch_bounds__(NWAVES * 64, NWAVES >= 8 ? 4 : 1) void fwd_mfma_kernel(const uint16_t* __restrict__ q,
+// (0 = g.M at run time).  NPMAX: the largest padded window this configuration serves.  D: head dim.
+template <int NWAVES, int MT, int NPMAX, int D>
+__global__ __launch_bounds__(NWAVES * 64, (fwd_min_waves<NWAVES, D>())) void fwd_mfma_kernel(const uint16_t* __restrict__ q,
                                                                const uint16_t* __restrict__ k,
                                                                const uint16_t* __restrict__ v,
                                                                const float* __restrict__ th_row,
@@ -299,16 +358,16 @@ __global__ __launch_bounds__(NWAVES * 64, NWAVES >= 8 ? 4 : 1) void fwd_mfma_ker
                                                                uint16_t* __restrict__ out, float* __restrict__ lse,
                                                                Geom g, int nqb, int NP, int nsplit) {
   extern __shared__ __align__(16) unsigned char smem_raw[];
-  constexpr int D = 32;
+  using Dim = FwdDim<D>;
   constexpr int NT = NWAVES * 64;
-  constexpr int MAXIT = (NPMAX * 4 + NT - 1) / NT;
+  constexpr int MAXIT = (NPMAX * Dim::PARTS + NT - 1) / NT;
   constexpr int QBM = (NPMAX + NWAVES * 32 - 1) / (NWAVES * 32);  // query blocks per window, at most
   static_assert(NWAVES <= kMaxWaves, "too many waves");
   static_assert(QBM <= kMaxQBlocks, "too many query blocks");
   const int M = MT > 0 ? MT : g.M;
   const int N = M * M;
   const int NB = NP / 32;
-  const FwdSmem sm = carve(smem_raw, NP, M);
+  const FwdSmem sm = carve<D>(smem_raw, NP, M);
 
   // Work of this workgroup: window-head wh, query blocks qoff .. qoff + nqw - 1.  The first nsplit
   // window-heads are split into one workgroup per query block, dispatched first (the first
@@ -353,28 +412,30 @@ __global__ __launch_bounds__(NWAVES * 64, NWAVES >= 8 ? 4 : 1) void fwd_mfma_ker
 
   // 1. every global load of the thread (K and V items, the queries of every block)
   uint4 kraw[MAXIT], vraw[MAXIT];
-  load_kv<MAXIT>(k, v, g, w, split ? sm.rc : nullptr, M, NP, tid, NT, true, kraw, vraw);
-  // the lane's query of block qb (two 16-byte halves: channels 8h.., 16+8h..)
-  auto load_q = [&](int qb, uint4& a, uint4& b) {
+  load_kv<MAXIT, D>(k, v, g, w, split ? sm.rc : nullptr, M, NP, tid, NT, true, kraw, vraw);
+  // the lane's query of block qb (16-byte pieces: channels 16t + 8h .. 16t + 8h + 7)
+  auto load_q = [&](int qb, QOps<D>& a) {
     const int qi = (qoff + qb) * NT / 2 + wave * 32 + col;
-    a = b = make_uint4(0, 0, 0, 0);
+#pragma unroll
+    for (int t = 0; t < Dim::KSTEPS; ++t) a[t] = make_uint4(0, 0, 0, 0);
     if (qb < nqw && qi < N) {
       const int rc = split ? (int)sm.rc[qi] : (qi / M) << 8 | (qi - (qi / M) * M);
       const int64_t off = tok_of(g, w, M, rc >> 8, rc & 255) * g.xs + w.h * D;
-      a = *reinterpret_cast<const uint4*>(q + off + 8 * h);
-      b = *reinterpret_cast<const uint4*>(q + off + 16 + 8 * h);
+#pragma unroll
+      for (int t = 0; t < Dim::KSTEPS; ++t) a[t] = *reinterpret_cast<const uint4*>(q + off + 16 * t + 8 * h);
     }
   };
-  uint4 qraw[QBM][2];
+  uint4 qraw[QBM][Dim::KSTEPS];
 #pragma unroll
-  for (int qb = 0; qb < QBM; ++qb) load_q(qb, qraw[qb][0], qraw[qb][1]);
+  for (int qb = 0; qb < QBM; ++qb) load_q(qb, qraw[qb]);
 
   // 2. RoPE sin/cos table (while the loads are in flight)
-  for (int i = tid; i < 2 * M * 8; i += NT) {
-    const int axis = i / (M * 8);
-    const int p = (i / 8) % M;
-    const int j = i % 8;
-    const float th = axis ? th_col[w.h * 8 + j] : th_row[w.h * 8 + j];
+  constexpr int P4 = Dim::P4;
+  for (int i = tid; i < 2 * M * P4; i += NT) {
+    const int axis = i / (M * P4);
+    const int p = (i / P4) % M;
+    const int j = i % P4;
+    const float th = axis ? th_col[w.h * P4 + j] : th_row[w.h * P4 + j];
     float s, c;
     rope_sincos(th, p, &s, &c);
     sm.sn[i] = s;
@@ -383,11 +444,12 @@ __global__ __launch_bounds__(NWAVES * 64, NWAVES >= 8 ? 4 : 1) void fwd_mfma_ker
   __syncthreads();
 
   // 3. K~ rows (rotated, fp16), V rows, block label summaries, norms
-  float kmax2 = stage_k<MAXIT>(sm, kraw, M, split, NP, tid, NT, true);
+  float kmax2 = stage_k<MAXIT, D>(sm, kraw, M, split, NP, tid, NT, true);
 #pragma unroll
   for (int i = 0; i < MAXIT; ++i) {
     const int it = tid + i * NT;
-    if (it < NP * 4) *reinterpret_cast<uint4*>(sm.V + (size_t)(it >> 2) * 32 + (it & 3) * 8) = vraw[i];
+    if (it < NP * Dim::PARTS)
+      *reinterpret_cast<uint4*>(sm.V + (size_t)(it / Dim::PARTS) * Dim::VS + (it % Dim::PARTS) * 8) = vraw[i];
   }
   for (int b = tid; b < NB; b += NT) {
     uint32_t bits = 0, full = 1;
@@ -400,12 +462,15 @@ __global__ __launch_bounds__(NWAVES * 64, NWAVES >= 8 ? 4 : 1) void fwd_mfma_ker
     }
     sm.blk[b] = bits | (full << 9);
   }
-  const float qscale = kLog2e * 0.17677669529663687f;  // log2(e) / sqrt(32)
+  // log2(e) / sqrt(d)
+  const float qscale = kLog2e * (D == 32 ? 0.17677669529663687f : 0.125f);
   float qn2max[QBM];
 #pragma unroll
   for (int qb = 0; qb < QBM; ++qb) {
-    const float qn2 = halves_sum(norm2_bf16x8(qraw[qb][1], norm2_bf16x8(qraw[qb][0], 0.f)));
-    qn2max[qb] = wave_max(qn2) * (qscale * qscale);
+    float qn2 = 0.f;
+#pragma unroll
+    for (int t = 0; t < Dim::KSTEPS; ++t) qn2 = norm2_bf16x8(qraw[qb][t], qn2);
+    qn2max[qb] = wave_max(halves_sum(qn2)) * (qscale * qscale);
   }
   kmax2 = wave_max(kmax2);
   if (lane == 0) {
@@ -426,9 +491,9 @@ __global__ __launch_bounds__(NWAVES * 64, NWAVES >= 8 ? 4 : 1) void fwd_mfma_ker
   // fp16 score operands unless some |k~| or |q^| (hence some component) could leave fp16 range
   const bool h16 = kmax < kF16Limit && sqrtf(qmax2_all) < kF16Limit;
   if (!h16) {
-    load_kv<MAXIT>(k, v, g, w, split ? sm.rc : nullptr, M, NP, tid, NT, false, kraw, vraw);
+    load_kv<MAXIT, D>(k, v, g, w, split ? sm.rc : nullptr, M, NP, tid, NT, false, kraw, vraw);
     __syncthreads();
-    stage_k<MAXIT>(sm, kraw, M, split, NP, tid, NT, false);
+    stage_k<MAXIT, D>(sm, kraw, M, split, NP, tid, NT, false);
     __syncthreads();
   }
 #pragma unroll
@@ -439,24 +504,20 @@ __global__ __launch_bounds__(NWAVES * 64, NWAVES >= 8 ? 4 : 1) void fwd_mfma_ker
     const bool qvalid = qi < N;
     const int qrc = !qvalid ? 0 : split ? (int)sm.rc[qi] : (qi / M) << 8 | (qi - (qi / M) * M);
     const int qr = qrc >> 8, qc = qrc & 255;
-    uint4 qb0, qb1;
-    {
-      // block 0's query was loaded with K and V; later blocks reload theirs (an L2 hit) during
-      // the previous block's epilogue: keeping every block's raw query live across attend() costs
-      // registers
-      const uint4 qa = qraw[qb][0], qc2 = qraw[qb][1];
-      float x[8], y[8];
-      unpack8(qa, x);
-      unpack8(qc2, y);
-      rotate8(x, sm.sn, sm.cs, 0, M, qr, 4 * h);
-      rotate8(y, sm.sn, sm.cs, 1, M, qc, 4 * h);
+    QOps<D> qop;
+    // block 0's query was loaded with K and V; later blocks reload theirs (an L2 hit) during the
+    // previous block's epilogue: keeping every block's raw query live across attend() costs registers.
+    // Piece t holds channels 16t + 8h ..: axis (16t) / (d/2), pairs from ((16t) % (d/2) + 8h) / 2.
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        x[e] *= qscale;
-        y[e] *= qscale;
-      }
-      qb0 = pack8_op(x, h16);
-      qb1 = pack8_op(y, h16);
+    for (int t = 0; t < Dim::KSTEPS; ++t) {
+      constexpr int HALF = D / 2;
+      const int axis = (16 * t) / HALF;
+      float x[8];
+      unpack8(qraw[qb][t], x);
+      rotate8(x, sm.sn, sm.cs, axis, M, axis ? qc : qr, ((16 * t) % HALF) / 2 + 4 * h, P4);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] *= qscale;
+      qop[t] = pack8_op(x, h16);
     }
     const float bound = sqrtf(qn2max[qb]) * kmax;  // >= every score of this wave (log2 units)
     const int qlab = qvalid ? token_label(g, w.wy, w.wx, qr, qc) : 0xff;
@@ -475,47 +536,52 @@ __global__ __launch_bounds__(NWAVES * 64, NWAVES >= 8 ? 4 : 1) void fwd_mfma_ker
       kb1 = be >> 5;
     }
 
-    f32x16_t o;
+    OAcc<D> o;
     float l = 0.f, ref;
 #pragma unroll
-    for (int v2 = 0; v2 < 16; ++v2) o[v2] = 0.f;
+    for (int t = 0; t < Dim::OT; ++t)
+#pragma unroll
+      for (int v2 = 0; v2 < 16; ++v2) o[t][v2] = 0.f;
     if (h16)
-      attend<true>(sm, NB, lane, run, kb0, kb1, wave_labels, wave_single, qb0, qb1, qlab, qvalid, bound, ref, l, o);
+      attend<true, D>(sm, NB, lane, run, kb0, kb1, wave_labels, wave_single, qop, qlab, qvalid, bound, ref, l, o);
     else
-      attend<false>(sm, NB, lane, run, kb0, kb1, wave_labels, wave_single, qb0, qb1, qlab, qvalid, bound, ref, l, o);
+      attend<false, D>(sm, NB, lane, run, kb0, kb1, wave_labels, wave_single, qop, qlab, qvalid, bound, ref, l, o);
 
     // the next block's query loads go out before this block's epilogue
-    if (qb + 1 < QBM) load_q(qb + 1, qraw[qb + 1][0], qraw[qb + 1][1]);  // zeros past the last block
-    // 5. epilogue: O = O^T / l (lane: query col, channels 8g + 4h + j), LSE = (ref + log2 l) ln 2
+    if (qb + 1 < QBM) load_q(qb + 1, qraw[qb + 1]);  // zeros past the last block
+    // 5. epilogue: O = O^T / l (lane: query col, channels 32t + 8g + 4h + j), LSE = (ref + log2 l) ln 2
     const float lt = halves_sum(l);
     if (qvalid) {
       const int64_t qtok = tok_of(g, w, M, qr, qc);
       const float inv = 1.f / lt;
-      uint16_t* dst = out + qtok * g.os + w.h * D + 4 * h;
 #pragma unroll
-      for (int gq = 0; gq < 4; ++gq) {
-        uint2 pr;
-        pr.x = pack2(o[4 * gq] * inv, o[4 * gq + 1] * inv);
-        pr.y = pack2(o[4 * gq + 2] * inv, o[4 * gq + 3] * inv);
-        *reinterpret_cast<uint2*>(dst + 8 * gq) = pr;
+      for (int t = 0; t < Dim::OT; ++t) {
+        uint16_t* dst = out + qtok * g.os + w.h * D + 32 * t + 4 * h;
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq) {
+          uint2 pr;
+          pr.x = pack2(o[t][4 * gq] * inv, o[t][4 * gq + 1] * inv);
+          pr.y = pack2(o[t][4 * gq + 2] * inv, o[t][4 * gq + 3] * inv);
+          *reinterpret_cast<uint2*>(dst + 8 * gq) = pr;
+        }
       }
       if (lse && h == 0) lse[qtok * g.heads + w.h] = (ref + __log2f(lt)) * kLn2;
     }
   }
 }
 
-template <int NWAVES, int MT, int NPMAX>
+template <int NWAVES, int MT, int NPMAX, int D>
 hipError_t launch_nw(const FwdArgs& a, hipStream_t st) {
   const Geom& g = a.g;
   const int NP = (g.N + 31) / 32 * 32;
   const int nqb = (g.N + NWAVES * 32 - 1) / (NWAVES * 32);
-  const size_t smem = fwd_smem_bytes(NP, g.M);
+  const size_t smem = fwd_smem_bytes<D>(NP, g.M);
   // The dynamic-LDS limit is raised on the current device, once per device (beyond kMaxDevices:
   // on every call).
   constexpr int kMaxDevices = 64;
   static std::once_flag once[kMaxDevices];
   const auto raise = [] {
-    (void)hipFuncSetAttribute((const void*)fwd_mfma_kernel<NWAVES, MT, NPMAX>,
+    (void)hipFuncSetAttribute((const void*)fwd_mfma_kernel<NWAVES, MT, NPMAX, D>,
                               hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
   };
   int dev = 0;
@@ -528,7 +594,7 @@ hipError_t launch_nw(const FwdArgs& a, hipStream_t st) {
   // two query blocks and enough work for several rounds of workgroups per CU
   const int nsplit = (nqb == 2 && nwh >= 64 * 8) ? 64 : 0;
   const int64_t blocks = nwh + nsplit;
-  hipLaunchKernelGGL((fwd_mfma_kernel<NWAVES, MT, NPMAX>), dim3((unsigned)blocks), dim3(NWAVES * 64), smem, st,
+  hipLaunchKernelGGL((fwd_mfma_kernel<NWAVES, MT, NPMAX, D>), dim3((unsigned)blocks), dim3(NWAVES * 64), smem, st,
                      (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, a.th_row, a.th_col,
                      (uint16_t*)a.out, a.lse, g, nqb, NP, nsplit);
   return hipGetLastError();
@@ -536,16 +602,30 @@ hipError_t launch_nw(const FwdArgs& a, hipStream_t st) {
 
 }  // namespace
 
+bool fwd_mfma_supported(const Geom& g) {
+  const int NP = (g.N + 31) / 32 * 32;
+  return (g.d == 32 && g.M <= 32) || (g.d == 64 && NP <= kMaxNP64);
+}
+
 hipError_t launch_fwd_mfma(const FwdArgs& a, hipStream_t st) {
   const int N = a.g.N;
-  if (a.g.M == 32) return launch_nw<16, 32, 1024>(a, st);
+  if (!fwd_mfma_supported(a.g)) return hipErrorInvalidValue;
+  if (a.g.d == 64) {
+    if (N <= 64) return launch_nw<2, 0, 64, 64>(a, st);
+    if (N <= 128) return launch_nw<4, 0, 128, 64>(a, st);
+    // four waves of two query tiles: two workgroups share a CU (LDS), one stages while the other computes
+    if (a.g.M == 16) return launch_nw<4, 16, 256, 64>(a, st);
+    if (N <= 256) return launch_nw<4, 0, 256, 64>(a, st);
+    return launch_nw<8, 0, kMaxNP64, 64>(a, st);
+  }
+  if (a.g.M == 32) return launch_nw<16, 32, 1024, 32>(a, st);
   if (fwd_m8_supported(a.g)) return launch_fwd_m8(a, st);
-  if (a.g.M == 8) return launch_nw<2, 8, 64>(a, st);
-  if (a.g.M == 16) return launch_nw<8, 16, 256>(a, st);
-  if (N <= 64) return launch_nw<2, 0, 64>(a, st);
-  if (N <= 128) return launch_nw<4, 0, 128>(a, st);
-  if (N <= 256) return launch_nw<8, 0, 256>(a, st);
-  return launch_nw<16, 0, 1024>(a, st);
+  if (a.g.M == 8) return launch_nw<2, 8, 64, 32>(a, st);
+  if (a.g.M == 16) return launch_nw<8, 16, 256, 32>(a, st);
+  if (N <= 64) return launch_nw<2, 0, 64, 32>(a, st);
+  if (N <= 128) return launch_nw<4, 0, 128, 32>(a, st);
+  if (N <= 256) return launch_nw<8, 0, 256, 32>(a, st);
+  return launch_nw<16, 0, 1024, 32>(a, st);
 }
 
 }  // namespace fsw

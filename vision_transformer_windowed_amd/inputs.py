@@ -24,6 +24,8 @@ WORKLOADS = {
     "flashswin_t_s1_p2_m32_bwd": dict(B=32, Hg=128, Wg=128, heads=3, d=32, M=32, shifts=(0, 16), dtype="bf16", kind="bwd", seed=1004),
     # the M = 16 windows of the pages' comparison tables, on the stage-1 grid of the M = 32 workload
     "flashswin_t_s1_p2_m16": dict(B=128, Hg=128, Wg=128, heads=3, d=32, M=16, shifts=(0, 8), dtype="bf16", kind="fwd", seed=1005),
+    # 64-wide heads (C = 192 in 3 heads) at M = 16 on the same stage-1 grid: the q/k/v bytes of the M = 32 workload
+    "wide_heads_s1_p2_m16_d64": dict(B=64, Hg=128, Wg=128, heads=3, d=64, M=16, shifts=(0, 8), dtype="bf16", kind="fwd", seed=1006),
 }
 
 

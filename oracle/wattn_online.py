@@ -5,9 +5,12 @@ cross-check O1.  Only tests, the smoke check and the benchmark's CPU-baseline
 leg use this module.  It shares no helper with O1:
 
 * no roll and no reshape-partition: each window of the shifted frame gathers
-  its tokens from the original grid with (wy*M + r + s) mod Hg and
-  (wx*M + c + s) mod Wg, and results are scattered back to the same tokens;
-* the region of a shifted-frame row Y is (Y >= Hg-M) + (Y >= Hg-s) (likewise
+  its tokens from the original grid with (wy*M + r + s) mod Hp and
+  (wx*M + c + s) mod Wp, and results are scattered back to the same tokens;
+  Hp, Wp are Hg, Wg rounded up to multiples of M, and a window token whose row
+  is >= Hg or column >= Wg is padding: never a key, never written back (the
+  padded-grid reading of O1);
+* the region of a shifted-frame row Y is (Y >= Hp-M) + (Y >= Hp-s) (likewise
   for columns), compared as a pair;
 * RoPE is a complex phase: channel pair (a, b) is z = a + i*b and the rotated
   pair is z * exp(i*phi) ([FS] Abstract and Figure 1(B): window-local 2D RoPE
@@ -28,36 +31,45 @@ import numpy as np
 
 
 def _window_coords(Hg, Wg, M, s, wy, wx):
-    """Original-grid rows/cols of shifted-frame window (wy, wx) and region ids of its tokens."""
+    """Padded-grid rows/cols of shifted-frame window (wy, wx), region ids of its tokens and whether
+    each token (n = r*M + c) is a grid token rather than padding."""
+    Hp, Wp = -(-Hg // M) * M, -(-Wg // M) * M
     Y = wy * M + np.arange(M)
     X = wx * M + np.arange(M)
-    ys = (Y + s) % Hg
-    xs = (X + s) % Wg
+    ys = (Y + s) % Hp
+    xs = (X + s) % Wp
     if s > 0:
-        ry = (Y >= Hg - M).astype(np.int64) + (Y >= Hg - s).astype(np.int64)
-        rx = (X >= Wg - M).astype(np.int64) + (X >= Wg - s).astype(np.int64)
+        ry = (Y >= Hp - M).astype(np.int64) + (Y >= Hp - s).astype(np.int64)
+        rx = (X >= Wp - M).astype(np.int64) + (X >= Wp - s).astype(np.int64)
     else:
         ry = np.zeros(M, dtype=np.int64)
         rx = np.zeros(M, dtype=np.int64)
-    # token n = r*M + c
     reg_r = np.repeat(ry, M)
     reg_c = np.tile(rx, M)
-    return ys, xs, reg_r, reg_c
+    real = (np.repeat(ys, M) < Hg) & (np.tile(xs, M) < Wg)
+    return ys, xs, reg_r, reg_c, real
 
 
 def _gather(x, ys, xs):
-    """x [B,Hg,Wg,heads,d] -> [B, heads, M*M, d] for the window rows ys, cols xs."""
-    w = x[:, ys][:, :, xs]  # B, M, M, heads, d
-    B, M1, M2, H, D = w.shape
-    return np.transpose(w.reshape(B, M1 * M2, H, D), (0, 2, 1, 3)).astype(np.float64)
+    """x [B,Hg,Wg,heads,(d)] -> [B, heads, M*M, (d)] for the window rows ys, cols xs; padding rows and
+    columns (>= Hg, >= Wg) read as zero."""
+    Hg, Wg = x.shape[1:3]
+    w = x[:, np.minimum(ys, Hg - 1)][:, :, np.minimum(xs, Wg - 1)]  # B, M, M, heads, (d)
+    keep = (ys < Hg)[:, None] & (xs < Wg)[None, :]
+    w = np.where(keep.reshape((1, len(ys), len(xs)) + (1,) * (w.ndim - 3)), w, 0.0)
+    B, M1, M2 = w.shape[:3]
+    w = w.reshape((B, M1 * M2) + w.shape[3:])
+    return np.moveaxis(w, 2, 1).astype(np.float64)
 
 
 def _scatter(dst, w, ys, xs):
-    """Inverse of _gather for dst [B,Hg,Wg,heads,(d)] and w [B, heads, N, (d)]."""
+    """Inverse of _gather for dst [B,Hg,Wg,heads,(d)] and w [B, heads, N, (d)]: grid tokens only."""
+    Hg, Wg = dst.shape[1:3]
     B, H, N = w.shape[:3]
     M = len(ys)
     t = np.moveaxis(w, 1, 2).reshape((B, M, M, H) + w.shape[3:])
-    dst[np.ix_(np.arange(B), ys, xs)] = t
+    ry, cx = np.nonzero(ys < Hg)[0], np.nonzero(xs < Wg)[0]
+    dst[np.ix_(np.arange(B), ys[ry], xs[cx])] = t[:, ry][:, :, cx]
 
 
 def _phase(theta_row, theta_col, M):
@@ -97,9 +109,9 @@ def wattn_fwd_online(q, k, v, theta_row, theta_col, M, shift, key_tile=24):
     out = np.zeros((B, Hg, Wg, H, D), dtype=np.float64)
     lse = np.zeros((B, Hg, Wg, H), dtype=np.float64)
     inv_sqrt_d = 1.0 / np.sqrt(D)
-    for wy in range(Hg // M):
-        for wx in range(Wg // M):
-            ys, xs, reg_r, reg_c = _window_coords(Hg, Wg, M, shift, wy, wx)
+    for wy in range(-(-Hg // M)):
+        for wx in range(-(-Wg // M)):
+            ys, xs, reg_r, reg_c, real = _window_coords(Hg, Wg, M, shift, wy, wx)
             qt = _to_real(_to_complex(_gather(q, ys, xs)) * ph[None])
             kt = _to_real(_to_complex(_gather(k, ys, xs)) * ph[None])
             vt = _gather(v, ys, xs)
@@ -110,6 +122,7 @@ def wattn_fwd_online(q, k, v, theta_row, theta_col, M, shift, key_tile=24):
                 j1 = min(N, j0 + key_tile)
                 s = qt @ np.swapaxes(kt[:, :, j0:j1], -1, -2) * inv_sqrt_d
                 same = (reg_r[:, None] == reg_r[None, j0:j1]) & (reg_c[:, None] == reg_c[None, j0:j1])
+                same &= real[None, j0:j1]
                 s = np.where(same[None, None], s, -np.inf)
                 new_max = np.maximum(run_max, s.max(axis=-1))
                 ref = np.where(np.isfinite(new_max), new_max, 0.0)
@@ -118,8 +131,9 @@ def wattn_fwd_online(q, k, v, theta_row, theta_col, M, shift, key_tile=24):
                 run_sum = alpha * run_sum + p.sum(axis=-1)
                 acc = alpha[..., None] * acc + p @ vt[:, :, j0:j1]
                 run_max = new_max
-            _scatter(out, acc / run_sum[..., None], ys, xs)
-            _scatter(lse, run_max + np.log(run_sum), ys, xs)
+            with np.errstate(divide="ignore", invalid="ignore"):  # padding queries: dropped by _scatter
+                _scatter(out, acc / run_sum[..., None], ys, xs)
+                _scatter(lse, run_max + np.log(run_sum), ys, xs)
     return out, lse
 
 
@@ -136,9 +150,9 @@ def wattn_bwd_online(q, k, v, out, lse, dout, theta_row, theta_col, M, shift, ke
     dv = np.zeros((B, Hg, Wg, H, D))
     dphi_pos = np.zeros((H, D // 2))  # accumulated p * dL/dphi per (head, pair)
     inv_sqrt_d = 1.0 / np.sqrt(D)
-    for wy in range(Hg // M):
-        for wx in range(Wg // M):
-            ys, xs, reg_r, reg_c = _window_coords(Hg, Wg, M, shift, wy, wx)
+    for wy in range(-(-Hg // M)):
+        for wx in range(-(-Wg // M)):
+            ys, xs, reg_r, reg_c, real = _window_coords(Hg, Wg, M, shift, wy, wx)
             zq = _to_complex(_gather(q, ys, xs)) * ph[None]
             zk = _to_complex(_gather(k, ys, xs)) * ph[None]
             qt, kt = _to_real(zq), _to_real(zk)
@@ -154,6 +168,7 @@ def wattn_bwd_online(q, k, v, out, lse, dout, theta_row, theta_col, M, shift, ke
                 j1 = min(N, j0 + key_tile)
                 s = qt @ np.swapaxes(kt[:, :, j0:j1], -1, -2) * inv_sqrt_d
                 same = (reg_r[:, None] == reg_r[None, j0:j1]) & (reg_c[:, None] == reg_c[None, j0:j1])
+                same &= real[:, None] & real[None, j0:j1]
                 p = np.where(same[None, None], np.exp(s - l_w[..., None]), 0.0)
                 dvt[:, :, j0:j1] = np.swapaxes(p, -1, -2) @ dot
                 dp = dot @ np.swapaxes(vt[:, :, j0:j1], -1, -2)

@@ -25,7 +25,11 @@ Conventions the pages leave open, and the reading taken here:
 * rotation (a, b) -> (a cos phi - b sin phi, a sin phi + b cos phi), the same
   for Q and K; positions (r, c) are in the shifted frame;
 * scores S = q~ . k~ / sqrt(d); masked pairs are excluded (weight exactly 0);
-* LSE = natural log of sum_j exp(S_ij) over the live keys.
+* LSE = natural log of sum_j exp(S_ij) over the live keys;
+* a grid whose sides are not multiples of M is extended to the next multiples
+  Hp x Wp (as Swin pads its feature map before the shift); the roll, the
+  windows and the regions are those of the Hp x Wp grid, and the added tokens
+  are absent: they are no key of any query, and have no output.
 
 The forward also takes an optional relative-position bias, the term that the
 standard Swin window attention adds to its materialized scores and FlashSwin
@@ -54,17 +58,17 @@ def check_bias(bias, heads, M):
 def check_args(shape, theta_row_shape, theta_col_shape, M, shift):
     """Validate a call; raises ValueError with the reason.
 
-    shape = (B, Hg, Wg, heads, d).  Hg and Wg must be multiples of M
-    (non-divisible grids are rejected rather than padded), 0 <= shift < M,
-    d a multiple of 4, theta arrays of shape [heads, d/4].
+    shape = (B, Hg, Wg, heads, d).  Hg, Wg >= 1 (grids that M does not divide
+    are padded, see the module notes), 0 <= shift < M, d a multiple of 4,
+    theta arrays of shape [heads, d/4].
     """
     if len(shape) != 5:
         raise ValueError("q/k/v must be [B, Hg, Wg, heads, d]")
     B, Hg, Wg, heads, d = shape
     if B < 0 or heads < 1:
         raise ValueError("need B >= 0 and heads >= 1")
-    if M < 1 or Hg % M or Wg % M:
-        raise ValueError("Hg and Wg must be positive multiples of M")
+    if M < 1 or Hg < 1 or Wg < 1:
+        raise ValueError("need Hg, Wg, M >= 1")
     if not (0 <= shift < M):
         raise ValueError("need 0 <= shift < M")
     if d % 4 or d < 4:
@@ -84,6 +88,21 @@ def _unroll(x, s):
     if s == 0:
         return x
     return np.roll(x, shift=(s, s), axis=(1, 2))
+
+
+def _padded(n, M):
+    """The multiple of M that a grid side of n tokens is extended to."""
+    return -(-n // M) * M
+
+
+def _pad(x, M):
+    """[B, Hg, Wg, *rest] -> [B, Hp, Wp, *rest], the added tokens zero (they are masked out)."""
+    Hg, Wg = x.shape[1:3]
+    Hp, Wp = _padded(Hg, M), _padded(Wg, M)
+    if (Hp, Wp) == (Hg, Wg):
+        return x
+    widths = [(0, 0), (0, Hp - Hg), (0, Wp - Wg)] + [(0, 0)] * (x.ndim - 3)
+    return np.pad(x, widths)
 
 
 def _partition(x, M):
@@ -151,17 +170,29 @@ def rope_rotate(xw, theta_row, theta_col, M, inverse=False):
 
 
 def _windows(x, M, s):
-    """Grid tensor [B, Hg, Wg, heads, d] -> windowed float64 [nWin, heads, N, d]."""
-    xw = _partition(_roll(np.asarray(x, dtype=np.float64), s), M)
+    """Grid tensor [B, Hg, Wg, heads, d] -> windowed float64 [nWin, heads, N, d] (grid padded to Hp x Wp)."""
+    xw = _partition(_roll(_pad(np.asarray(x, dtype=np.float64), M), s), M)
     return np.ascontiguousarray(np.swapaxes(xw, 1, 2))
 
 
+def _grid_back(xw, B, Hg, Wg, M, s):
+    """Inverse of _windows for [nWin, heads, N, ...]: un-partition the Hp x Wp grid, roll back, crop."""
+    Hp, Wp = _padded(Hg, M), _padded(Wg, M)
+    return _unroll(_unpartition(np.swapaxes(xw, 1, 2), B, Hp, Wp, M), s)[:, :Hg, :Wg]
+
+
 def _window_mask(B, Hg, Wg, M, s):
-    """Boolean live-pair mask [nWin, 1, N, N] or None when s == 0."""
-    if s == 0:
+    """Boolean live-pair mask [nWin, 1, N, N]: same Swin region and a key that is a grid token (not
+    padding); None when every pair is live (no shift, no padding)."""
+    Hp, Wp = _padded(Hg, M), _padded(Wg, M)
+    if s == 0 and (Hp, Wp) == (Hg, Wg):
         return None
-    lab = region_labels(Hg, Wg, M, s).reshape(-1, M * M)  # [nH*nW, N]
+    lab = region_labels(Hp, Wp, M, s).reshape(-1, M * M)  # [nH*nW, N]
     live = lab[:, :, None] == lab[:, None, :]
+    real = np.zeros((1, Hp, Wp), dtype=bool)
+    real[:, :Hg, :Wg] = True
+    real_w = _partition(_roll(real, s), M)  # [nH*nW, N]: is window token n a grid token
+    live = live & real_w[:, None, :]
     live = np.broadcast_to(live[None], (B,) + live.shape).reshape(-1, 1, M * M, M * M)
     return live
 
@@ -205,6 +236,16 @@ def _chunks(n_win, heads, N):
         yield slice(lo, min(n_win, lo + per))
 
 
+def _softmax_rows(S):
+    """Row softmax of S (masked entries -inf): (P, row max m, row sum of exp(S - m)).  A row with no
+    live entry (only a padding query, whose result is dropped) gets P = 0."""
+    m = S.max(axis=-1, keepdims=True)
+    m = np.where(np.isfinite(m), m, 0.0)
+    e = np.exp(S - m)
+    ssum = e.sum(axis=-1, keepdims=True)
+    return e / np.where(ssum > 0, ssum, 1.0), m, ssum
+
+
 def wattn_fwd_ref(q, k, v, theta_row, theta_col, M, shift, bias=None):
     """Forward: returns (out [B,Hg,Wg,heads,d] float64, lse [B,Hg,Wg,heads] float64).
 
@@ -229,15 +270,11 @@ def wattn_fwd_ref(q, k, v, theta_row, theta_col, M, shift, bias=None):
             S = S + rb
         if live_all is not None:
             S = np.where(live_all[sl], S, -np.inf)
-        m = S.max(axis=-1, keepdims=True)
-        e = np.exp(S - m)
-        ssum = e.sum(axis=-1, keepdims=True)
-        P = e / ssum
+        P, m, ssum = _softmax_rows(S)
         ow[sl] = P @ vw[sl]
-        lw[sl] = (m + np.log(ssum))[..., 0]
-    out = _unroll(_unpartition(np.swapaxes(ow, 1, 2), B, Hg, Wg, M), shift)
-    lse = _unroll(_unpartition(np.swapaxes(lw, 1, 2), B, Hg, Wg, M), shift)
-    return out, lse
+        with np.errstate(divide="ignore"):
+            lw[sl] = (m + np.log(ssum))[..., 0]
+    return _grid_back(ow, B, Hg, Wg, M, shift), _grid_back(lw, B, Hg, Wg, M, shift)
 
 
 def _dtheta_terms(xt, dxt, M):
@@ -288,9 +325,7 @@ def wattn_bwd_ref(q, k, v, dout, theta_row, theta_col, M, shift):
         S = qw[sl] @ np.swapaxes(kw[sl], -1, -2) * scale
         if live_all is not None:
             S = np.where(live_all[sl], S, -np.inf)
-        m = S.max(axis=-1, keepdims=True)
-        e = np.exp(S - m)
-        P = e / e.sum(axis=-1, keepdims=True)
+        P = _softmax_rows(S)[0]
         dvw[sl] = np.swapaxes(P, -1, -2) @ dow[sl]
         dP = dow[sl] @ np.swapaxes(vw[sl], -1, -2)
         Dr = (P * dP).sum(axis=-1, keepdims=True)
@@ -303,6 +338,6 @@ def wattn_bwd_ref(q, k, v, dout, theta_row, theta_col, M, shift):
     dkw = rope_rotate(dkt, theta_row, theta_col, M, inverse=True)
 
     def back(xw):
-        return _unroll(_unpartition(np.swapaxes(xw, 1, 2), B, Hg, Wg, M), shift)
+        return _grid_back(xw, B, Hg, Wg, M, shift)
 
     return back(dqw), back(dkw), back(dvw), tr_q + tr_k, tc_q + tc_k

@@ -45,11 +45,15 @@ def _rand_case(seed, B, Hg, Wg, H, D, theta_scale=1.0):
 
 def brute_force_fwd(q, k, v, tr, tc, M, s, bias=None):
     """Per-token scalar loops; every key of the grid is tested for membership.  With a bias table, the
-    pair of query (Y, X) and key (Y2, X2) (shifted frame) adds bias[h][Y%M - Y2%M + M-1][X%M - X2%M + M-1]."""
+    pair of query (Y, X) and key (Y2, X2) (shifted frame) adds bias[h][Y%M - Y2%M + M-1][X%M - X2%M + M-1].
+    A grid that M does not divide lives in the frame of its padded extent Hp x Wp (the next multiples of
+    M): the shifted frame, the windows and the regions are those of Hp x Wp, and only grid tokens are
+    ever keys."""
     B, Hg, Wg, H, D = q.shape
+    Hp, Wp = -(-Hg // M) * M, -(-Wg // M) * M
 
     def shifted(y, x):
-        return (y - s) % Hg, (x - s) % Wg
+        return (y - s) % Hp, (x - s) % Wp
 
     def region(Y, size):
         if s == 0 or Y < size - M:
@@ -71,7 +75,7 @@ def brute_force_fwd(q, k, v, tr, tc, M, s, bias=None):
         for y in range(Hg):
             for x in range(Wg):
                 Y, X = shifted(y, x)
-                lab = (region(Y, Hg), region(X, Wg))
+                lab = (region(Y, Hp), region(X, Wp))
                 for h in range(H):
                     qt = rot(q[b, y, x, h], h, Y % M, X % M)
                     scores, vals = [], []
@@ -80,7 +84,7 @@ def brute_force_fwd(q, k, v, tr, tc, M, s, bias=None):
                             Y2, X2 = shifted(y2, x2)
                             if Y2 // M != Y // M or X2 // M != X // M:
                                 continue
-                            if (region(Y2, Hg), region(X2, Wg)) != lab:
+                            if (region(Y2, Hp), region(X2, Wp)) != lab:
                                 continue
                             kt = rot(k[b, y2, x2, h], h, Y2 % M, X2 % M)
                             sc = sum(qt[i] * kt[i] for i in range(D)) / math.sqrt(D)
@@ -117,6 +121,91 @@ def pin_brute_force(fwd=None):
 
 def test_brute_force():
     pin_brute_force()
+
+
+# Grids that M does not divide (padded reading): one or both sides ragged, with and without a shift,
+# shifts whose last-window regions hold only padding rows, a grid smaller than one window.
+PAD_CASES = [
+    # B, Hg, Wg, H, D, M, s
+    (1, 5, 6, 1, 8, 4, 0),
+    (1, 7, 7, 2, 8, 3, 1),
+    (1, 10, 9, 1, 4, 4, 2),
+    (2, 6, 11, 1, 8, 4, 3),
+    (1, 3, 2, 1, 4, 4, 1),
+]
+
+
+def pin_padded_brute_force(fwd=None):
+    fwd = fwd or oracle.wattn_fwd_ref
+    for i, (B, Hg, Wg, H, D, M, s) in enumerate(PAD_CASES):
+        q, k, v, _, tr, tc = _rand_case(70 + i, B, Hg, Wg, H, D)
+        o, l = fwd(q, k, v, tr, tc, M, s)
+        ob, lb = brute_force_fwd(q, k, v, tr, tc, M, s)
+        assert o.shape == q.shape and l.shape == q.shape[:4]
+        np.testing.assert_allclose(o, ob, rtol=0, atol=1e-12)
+        np.testing.assert_allclose(l, lb, rtol=0, atol=1e-12)
+
+
+def test_padded_grid_brute_force():
+    pin_padded_brute_force()
+
+
+def test_padded_grid_without_shift_is_attention_over_clipped_windows():
+    """Without a shift a padded grid's windows are the M x M boxes of the grid clipped at its edges:
+    library attention (theta = 0) over the tokens of each clipped box."""
+    B, Hg, Wg, H, D, M = 1, 10, 7, 2, 8, 4
+    q, k, v, _, tr, tc = _rand_case(77, B, Hg, Wg, H, D)
+    o, l = oracle.wattn_fwd_ref(q, k, v, np.zeros_like(tr), np.zeros_like(tc), M, 0)
+    for y0 in range(0, Hg, M):
+        for x0 in range(0, Wg, M):
+            box = (slice(None), slice(y0, min(Hg, y0 + M)), slice(x0, min(Wg, x0 + M)))
+            n = (min(Hg, y0 + M) - y0) * (min(Wg, x0 + M) - x0)
+
+            def flat(t):
+                return torch.from_numpy(t[box].reshape(B, n, H, D).transpose(0, 2, 1, 3).copy())
+
+            ref = torch.nn.functional.scaled_dot_product_attention(flat(q), flat(k), flat(v))
+            got = o[box].reshape(B, n, H, D).transpose(0, 2, 1, 3)
+            np.testing.assert_allclose(got, ref.numpy(), rtol=0, atol=1e-12)
+
+
+def test_padded_grid_pin_catches_planted_mistakes():
+    """Plausible padding mistakes planted in O1 (CPU only), each caught by the padded brute force:
+    padding kept as zero-valued keys, the Swin regions cut at the grid size instead of the padded size,
+    and the shift applied before the padding."""
+    orig_mask, orig_windows = wattn_ref._window_mask, wattn_ref._windows
+
+    def zero_keys(B, Hg, Wg, M, s):  # the mask of a grid that is Hp x Wp in truth: no padding excluded
+        return orig_mask(B, wattn_ref._padded(Hg, M), wattn_ref._padded(Wg, M), M, s)
+
+    def regions_at_grid_size(B, Hg, Wg, M, s):
+        Hp, Wp = wattn_ref._padded(Hg, M), wattn_ref._padded(Wg, M)
+
+        def cuts(size, n):
+            Y = np.arange(n)
+            return (Y >= size - M).astype(np.int64) + (Y >= size - s) if s else np.zeros(n, dtype=np.int64)
+
+        lab = 3 * cuts(Hg, Hp)[:, None] + cuts(Wg, Wp)[None, :]
+        lab = lab.reshape(Hp // M, M, Wp // M, M).swapaxes(1, 2).reshape(-1, M * M)
+        real = np.zeros((1, Hp, Wp), dtype=bool)
+        real[:, :Hg, :Wg] = True
+        real_w = wattn_ref._partition(wattn_ref._roll(real, s), M)
+        live = (lab[:, :, None] == lab[:, None, :]) & real_w[:, None, :]
+        return np.broadcast_to(live[None], (B,) + live.shape).reshape(-1, 1, M * M, M * M)
+
+    def roll_before_pad(x, M, s):
+        xw = wattn_ref._partition(wattn_ref._pad(wattn_ref._roll(np.asarray(x, dtype=np.float64), s), M), M)
+        return np.ascontiguousarray(np.swapaxes(xw, 1, 2))
+
+    for name, mutant in (("_window_mask", zero_keys), ("_window_mask", regions_at_grid_size),
+                         ("_windows", roll_before_pad)):
+        saved = getattr(wattn_ref, name)
+        setattr(wattn_ref, name, mutant)
+        try:
+            assert _fails(pin_padded_brute_force), mutant.__name__
+        finally:
+            setattr(wattn_ref, name, saved)
+    assert (wattn_ref._window_mask, wattn_ref._windows) == (orig_mask, orig_windows)
 
 
 BIAS_CASES = [(1, 4, 4, 2, 8, 2, 0), (1, 6, 6, 1, 8, 3, 1), (2, 6, 9, 2, 4, 3, 2), (1, 8, 8, 1, 4, 4, 3)]
@@ -362,6 +451,7 @@ FD_CASES = [
     # B, Hg, Wg, H, D, M, s
     (1, 4, 4, 2, 8, 2, 1),
     (1, 6, 6, 1, 4, 3, 2),
+    (1, 5, 3, 1, 4, 2, 1),  # padded grid
 ]
 
 
@@ -481,6 +571,10 @@ O12_CASES = [
     (1, 12, 12, 2, 16, 6, 3),
     (1, 16, 16, 2, 32, 8, 4),
     (2, 3, 3, 1, 4, 1, 0),
+    # padded grids
+    (1, 10, 9, 2, 8, 4, 2),
+    (2, 7, 13, 1, 16, 6, 5),
+    (1, 3, 2, 1, 4, 4, 1),
 ]
 
 
@@ -566,7 +660,7 @@ def test_o1_matches_o2_on_tiny_workload():
 # ----------------------------------------------------------------------------- argument checks
 
 @pytest.mark.parametrize("shape,M,s", [
-    ((1, 8, 8, 2, 8), 3, 0),   # grid not a multiple of M
+    ((1, 0, 8, 2, 8), 4, 0),   # empty grid side
     ((1, 8, 8, 2, 8), 4, 4),   # shift >= M
     ((1, 8, 8, 2, 8), 4, -1),  # negative shift
     ((1, 8, 8, 2, 6), 4, 0),   # d not a multiple of 4

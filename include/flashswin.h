@@ -67,8 +67,13 @@ typedef enum { FSW_F32 = 0, FSW_BF16 = 1 } fsw_dtype;
  *                caller does not need it (inference).
  *   out and lse may not share a byte with q, k, v, theta_row, theta_col or each other
  *   (FSW_ERR_INVALID_ARG); the inputs may share memory.
- *   B >= 0 (B == 0 returns FSW_OK with nothing enqueued); Hg, Wg positive multiples of M;
- *   1 <= M <= 128; 0 <= shift < M; heads >= 1; d in {8, 16, 32, 64}; dtype FSW_F32 or FSW_BF16.
+ *   B >= 0 (B == 0 returns FSW_OK with nothing enqueued); Hg, Wg >= 1; 1 <= M <= 128;
+ *   0 <= shift < M; heads >= 1; d in {8, 16, 32, 64}; dtype FSW_F32 or FSW_BF16.
+ *   A grid whose sides M does not divide is taken as padded to the next multiples of M, as Swin pads
+ *   its feature map before the shift (the pages do not say): the shift, the windows and the Swin
+ *   regions are those of the padded grid, and the added tokens are absent, no key of any query and
+ *   no output.  (A caller that wants Swin's zero-valued padding tokens as keys pads q, k, v itself.)
+ *   Padded grids run on the float32-arithmetic kernels.
  *   bf16 with d == 32 and M <= 32, and bf16 with d == 64 and M*M <= 512 (M <= 22), run on the MFMA
  *   kernels; every other case runs on kernels with float32 arithmetic that stream the keys through
  *   LDS (correct for every supported shape, not tuned).  Needs no workspace.  On the MFMA kernels
@@ -181,8 +186,8 @@ size_t flashswin_wattn_fwd_materialized_workspace_size(int64_t B, int64_t Hg, in
  *   q, k, v, theta_row, theta_col, out, lse: as in flashswin_wattn_fwd (lse may be NULL).  out, lse and
  *   the workspace may not share a byte with any input or with each other.
  *   Three kernels: scores (MFMA, fp16 operands when in range, else bf16; float32 scores), row softmax
- *   (bf16 probabilities), P.V (MFMA).  Implemented for dtype FSW_BF16, d == 32 and M <= 32 only
- *   (FSW_ERR_UNSUPPORTED otherwise).
+ *   (bf16 probabilities), P.V (MFMA).  Implemented for dtype FSW_BF16, d == 32, M <= 32 and grids
+ *   that M divides only (FSW_ERR_UNSUPPORTED otherwise).
  * Returns FSW_OK, FSW_ERR_INVALID_ARG, FSW_ERR_UNSUPPORTED, FSW_ERR_WORKSPACE or FSW_ERR_HIP.
  */
 int flashswin_wattn_fwd_materialized(const void* q, const void* k, const void* v,

@@ -49,8 +49,8 @@ def fwd(**kw):
 
 
 @pytest.mark.parametrize("kw,status", [
-    (dict(Hg=12), F.FSW_ERR_INVALID_ARG),          # Hg not a multiple of M
-    (dict(Wg=20), F.FSW_ERR_INVALID_ARG),          # Wg not a multiple of M
+    (dict(Hg=0), F.FSW_ERR_INVALID_ARG),           # empty grid side
+    (dict(Wg=-3), F.FSW_ERR_INVALID_ARG),
     (dict(shift=8), F.FSW_ERR_INVALID_ARG),        # shift >= M
     (dict(shift=-1), F.FSW_ERR_INVALID_ARG),       # negative shift
     (dict(d=6), F.FSW_ERR_INVALID_ARG),            # d not a multiple of 4
@@ -98,7 +98,7 @@ def bwd(**kw):
 
 
 @pytest.mark.parametrize("kw,status", [
-    (dict(Hg=10), F.FSW_ERR_INVALID_ARG),
+    (dict(Hg=0), F.FSW_ERR_INVALID_ARG),
     (dict(shift=9), F.FSW_ERR_INVALID_ARG),
     (dict(lse=None), F.FSW_ERR_INVALID_ARG),       # the backward needs the forward's LSE
     (dict(dout=None), F.FSW_ERR_INVALID_ARG),
@@ -123,7 +123,7 @@ def test_backward_rejects_before_launch(kw, status):
 def test_workspace_size():
     ws = F.flashswin_wattn_bwd_workspace_size
     assert ws(0, 16, 16, 2, 32, 8, 0, 1) == 0
-    assert ws(1, 12, 16, 2, 32, 8, 0, 1) == 0           # invalid shape
+    assert ws(1, 0, 16, 2, 32, 8, 0, 1) == 0            # invalid shape
     small = ws(1, 16, 16, 2, 32, 8, 0, 1)
     big = ws(4, 16, 16, 2, 32, 8, 0, 1)
     assert 0 < small < big
@@ -146,7 +146,7 @@ def fwd_packed(**kw):
 
 
 @pytest.mark.parametrize("kw,status", [
-    (dict(Hg=12), F.FSW_ERR_INVALID_ARG),
+    (dict(Wg=0), F.FSW_ERR_INVALID_ARG),
     (dict(qkv=None), F.FSW_ERR_INVALID_ARG),
     (dict(qkv=FAKE + 8), F.FSW_ERR_INVALID_ARG),            # misaligned
     (dict(out=None), F.FSW_ERR_INVALID_ARG),
@@ -208,7 +208,8 @@ def mat(**kw):
     (dict(dtype=F.FSW_F32), F.FSW_ERR_UNSUPPORTED),   # bf16 only
     (dict(d=16), F.FSW_ERR_UNSUPPORTED),              # d = 32 only
     (dict(Hg=64, Wg=64, M=64), F.FSW_ERR_UNSUPPORTED),  # M <= 32 only
-    (dict(Hg=12), F.FSW_ERR_INVALID_ARG),
+    (dict(Hg=12), F.FSW_ERR_UNSUPPORTED),             # padded grids: the fused kernels only
+    (dict(Hg=0), F.FSW_ERR_INVALID_ARG),
     (dict(wsb=1024), F.FSW_ERR_WORKSPACE),            # too small
     (dict(ws=None), F.FSW_ERR_WORKSPACE),
     (dict(ws=FAKE + 4 * GIB + 16), F.FSW_ERR_WORKSPACE),  # not 256-byte aligned
@@ -227,3 +228,17 @@ def test_materialized_workspace_size():
     # M = 5: N = 25 rows of 32 floats
     assert F.flashswin_wattn_fwd_materialized_workspace_size(1, 10, 10, 1, 32, 5, 2, F.FSW_BF16) == 4 * 25 * 32 * 4
     assert F.flashswin_wattn_fwd_materialized_workspace_size(1, 16, 16, 2, 32, 8, 0, F.FSW_F32) == 0
+    assert F.flashswin_wattn_fwd_materialized_workspace_size(1, 12, 16, 2, 32, 8, 0, F.FSW_BF16) == 0  # padded
+
+
+def test_padded_grid_workspace_counts_padded_windows():
+    """A 10 x 13 grid with M = 4 is padded to 12 x 16: 3 x 4 windows.  The backward workspace holds
+    Delta for the 130 grid tokens, per-window-head maxima and the float32-arithmetic kernels' dtheta
+    partial rows (one row per kernel, window-head and 128-query block), 256-byte aligned sections."""
+    def al(n):
+        return (n + 255) // 256 * 256
+    B, Hg, Wg, H, d, M = 2, 10, 13, 3, 32, 4
+    nwin = B * 3 * 4
+    want = al(B * Hg * Wg * H * 4) + al(nwin * H * 4 * 4) + al(H * 2 * nwin * 1 * (d // 2) * 4)
+    for dt in (F.FSW_BF16, F.FSW_F32):
+        assert F.flashswin_wattn_bwd_workspace_size(B, Hg, Wg, H, d, M, 1, dt) == want

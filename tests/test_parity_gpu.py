@@ -148,6 +148,16 @@ FWD_SMALL = [
     (1, 64, 64, 1, 32, 64, 32, "bf16"),
     (1, 48, 96, 2, 16, 48, 7, "f32"),
     (1, 64, 64, 1, 64, 64, 0, "f32"),
+] + [
+    # grids that M does not divide (padded to the next multiple; the padding tokens are absent)
+    (1, 10, 13, 2, 32, 4, 0, "f32"),
+    (1, 10, 9, 1, 16, 4, 2, "f32"),
+    (2, 7, 13, 2, 8, 6, 5, "f32"),
+    (1, 3, 2, 1, 32, 4, 1, "f32"),
+    (1, 50, 75, 3, 32, 8, 4, "bf16"),
+    (1, 50, 38, 2, 32, 16, 8, "bf16"),
+    (1, 40, 29, 2, 64, 12, 6, "bf16"),
+    (1, 100, 70, 1, 32, 32, 16, "bf16"),
 ]
 
 
@@ -410,6 +420,13 @@ BWD_SMALL = [
     (1, 40, 40, 1, 32, 40, 13, "bf16"),
     (1, 64, 64, 1, 32, 64, 0, "bf16"),
     (1, 48, 48, 1, 16, 48, 24, "f32"),
+    # grids that M does not divide (padded)
+    (1, 10, 13, 2, 32, 4, 1, "f32"),
+    (2, 7, 13, 1, 16, 6, 5, "f32"),
+    (1, 10, 9, 1, 8, 4, 2, "f32"),
+    (1, 50, 75, 2, 32, 8, 4, "bf16"),
+    (1, 50, 38, 1, 32, 16, 8, "bf16"),
+    (1, 40, 29, 1, 64, 12, 6, "bf16"),
 ]
 
 

@@ -8,7 +8,8 @@
 //   dq~_i = sum_j dS_ij k~_j / sqrt(d),   dk~_j = sum_i dS_ij q~_i / sqrt(d),
 //   dq = R^T dq~, dk = R^T dk~, and for a rotated pair (a, b) at angle theta * p,
 //   dtheta += p (dx~_b x~_a - dx~_a x~_b) over all Q and K tokens.
-// Three kernels: Delta; dK/dV with one thread per key; dQ with one thread per query.  The theta
+// Three kernels: Delta; dK/dV with one thread per key; dQ with one thread per query.  Padding tokens
+// of a padded grid are neither queries nor keys (no loads, no stores, no dtheta terms).  The theta
 // gradient is reduced per workgroup in a fixed order into a partials buffer, then summed over
 // workgroups in a fixed order, so results are bit-reproducible.
 #include <algorithm>
@@ -91,7 +92,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkdv_scalar_kernel(
   const int tid = threadIdx.x;
   const int N = g.N;
   const int j = (int)(blk % nb) * kBwdThreads + tid;
-  const bool active = j < N;
+  const bool active = j < N && token_real(g, w.wy, w.wx, j / g.M, j % g.M);  // padding is no key
   const float* tr = th_row + w.h * (D / 4);
   const float* tc = th_col + w.h * (D / 4);
   const int64_t xs = g.xs, os = g.os;
@@ -120,7 +121,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkdv_scalar_kernel(
     __syncthreads();
     {
       const int i = t0 + tid;
-      if (i < N) {
+      if (i < N && token_real(g, w.wy, w.wx, i / g.M, i % g.M)) {
         const int r = i / g.M, c = i - (i / g.M) * g.M;
         const int64_t tok = token_index(g, w.b, w.wy, w.wx, r, c);
         float qv[D], gv[D];
@@ -185,7 +186,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dq_scalar_kernel(
   const int tid = threadIdx.x;
   const int N = g.N;
   const int i = (int)(blk % nb) * kBwdThreads + tid;
-  const bool active = i < N;
+  const bool active = i < N && token_real(g, w.wy, w.wx, i / g.M, i % g.M);  // padding is no query
   const float* tr = th_row + w.h * (D / 4);
   const float* tc = th_col + w.h * (D / 4);
   const int64_t xs = g.xs, os = g.os;
@@ -220,7 +221,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dq_scalar_kernel(
     __syncthreads();
     {
       const int j = t0 + tid;
-      if (j < N) {
+      if (j < N && token_real(g, w.wy, w.wx, j / g.M, j % g.M)) {
         const int r = j / g.M, c = j - (j / g.M) * g.M;
         const int64_t tok = token_index(g, w.b, w.wy, w.wx, r, c);
         float kv[D], vv[D];

@@ -3,8 +3,9 @@
 // Every check runs on the host before any HIP call, so an invalid call never touches the device.
 // Dispatch: bf16 with d == 32 and M <= 32 goes to the MFMA kernels, forward and backward; the bf16
 // d == 64 forward of windows up to 22 x 22 too.  Everything else (float32 tensors, other d, larger
-// windows, the d == 64 backward) goes to the float32-arithmetic kernels, which stream the keys
-// through LDS in tiles and take any window size up to kMaxWindow.
+// windows, the d == 64 backward, grids that M does not divide) goes to the float32-arithmetic
+// kernels, which stream the keys through LDS in tiles, take any window size up to kMaxWindow and
+// skip the padding tokens of a padded grid.
 #include <algorithm>
 #include <mutex>
 
@@ -29,7 +30,6 @@ bool supported_d(int d) { return d == 8 || d == 16 || d == 32 || d == 64; }
 // Shape rules shared by forward, backward and workspace sizing.  Fills g on success.
 int check_shape(int64_t B, int64_t Hg, int64_t Wg, int heads, int d, int M, int shift, int dtype, fsw::Geom* g) {
   if (B < 0 || Hg < 1 || Wg < 1 || heads < 1 || M < 1 || d < 1) return FSW_ERR_INVALID_ARG;
-  if (Hg % M != 0 || Wg % M != 0) return FSW_ERR_INVALID_ARG;
   if (shift < 0 || shift >= M) return FSW_ERR_INVALID_ARG;
   if (d % 4 != 0) return FSW_ERR_INVALID_ARG;
   if (dtype != FSW_F32 && dtype != FSW_BF16) return FSW_ERR_INVALID_ARG;
@@ -40,7 +40,9 @@ int check_shape(int64_t B, int64_t Hg, int64_t Wg, int heads, int d, int M, int 
   if (Hg > lim || Wg > lim || heads > (1 << 20)) return FSW_ERR_UNSUPPORTED;
   const long double elems = (long double)B * Hg * Wg * heads * d;
   if (elems > (long double)((int64_t)1 << 56)) return FSW_ERR_UNSUPPORTED;
-  const long double wgs = (long double)B * (Hg / M) * (Wg / M) * heads * 8;
+  // a grid that M does not divide is padded to the next multiples of M (see fsw::Geom)
+  const int64_t nH = (Hg + M - 1) / M, nW = (Wg + M - 1) / M;
+  const long double wgs = (long double)B * nH * nW * heads * 8;
   if (wgs > (long double)((int64_t)1 << 31) - 1) return FSW_ERR_UNSUPPORTED;
   g->B = B;
   g->Hg = (int)Hg;
@@ -49,8 +51,10 @@ int check_shape(int64_t B, int64_t Hg, int64_t Wg, int heads, int d, int M, int 
   g->d = d;
   g->M = M;
   g->shift = shift;
-  g->nH = (int)(Hg / M);
-  g->nW = (int)(Wg / M);
+  g->nH = (int)nH;
+  g->nW = (int)nW;
+  g->Hp = (int)(nH * M);
+  g->Wp = (int)(nW * M);
   g->N = M * M;
   g->xs = (int64_t)heads * d;
   g->os = (int64_t)heads * d;
@@ -113,9 +117,13 @@ WsLayout workspace_layout(const fsw::Geom& g, bool mfma) {
   return w;
 }
 
-bool use_mfma_fwd(const fsw::Geom& g, int dtype) { return dtype == FSW_BF16 && fsw::fwd_mfma_supported(g); }
+// Padded grids run on the float32-arithmetic kernels, the only ones that skip padding tokens.
+bool padded(const fsw::Geom& g) { return g.Hp != g.Hg || g.Wp != g.Wg; }
+bool use_mfma_fwd(const fsw::Geom& g, int dtype) {
+  return dtype == FSW_BF16 && !padded(g) && fsw::fwd_mfma_supported(g);
+}
 bool use_mfma(const fsw::Geom& g, int dtype) {
-  return fsw::kHaveMfmaBwd && dtype == FSW_BF16 && g.d == 32 && g.M <= kMaxM;
+  return fsw::kHaveMfmaBwd && dtype == FSW_BF16 && !padded(g) && g.d == 32 && g.M <= kMaxM;
 }
 
 // Pointer checks and dispatch of a forward whose shape (and q/k/v token stride) is in g.
@@ -295,7 +303,7 @@ size_t flashswin_wattn_fwd_materialized_workspace_size(int64_t B, int64_t Hg, in
                                                        int shift, int dtype) {
   fsw::Geom g;
   if (check_shape(B, Hg, Wg, heads, d, M, shift, dtype, &g) != FSW_OK) return 0;
-  if (B == 0 || dtype != FSW_BF16 || d != 32 || M > kMaxM) return 0;
+  if (B == 0 || dtype != FSW_BF16 || d != 32 || M > kMaxM || padded(g)) return 0;
   return fsw::materialized_workspace_bytes(g);
 }
 
@@ -306,7 +314,7 @@ int flashswin_wattn_fwd_materialized(const void* q, const void* k, const void* v
   fsw::Geom g;
   int st = check_shape(B, Hg, Wg, heads, d, M, shift, dtype, &g);
   if (st != FSW_OK) return st;
-  if (dtype != FSW_BF16 || d != 32 || M > kMaxM) return FSW_ERR_UNSUPPORTED;
+  if (dtype != FSW_BF16 || d != 32 || M > kMaxM || padded(g)) return FSW_ERR_UNSUPPORTED;
   if (B == 0) return FSW_OK;
   if (!q || !k || !v || !out || !theta_row || !theta_col) return FSW_ERR_INVALID_ARG;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16)) return FSW_ERR_INVALID_ARG;

@@ -12,11 +12,16 @@
 
 namespace fsw {
 
-// Shape of one call, passed to kernels by value.
+// Shape of one call, passed to kernels by value.  A grid whose sides M does not divide is taken as
+// padded to Hp x Wp (the next multiples of M), as Swin pads its feature map before the shift: the
+// roll, the windows and the regions are those of Hp x Wp, and the added tokens (row >= Hg or column
+// >= Wg) are absent, no key of any query and no output.  Only the float32-arithmetic kernels take
+// padded grids; elsewhere Hp == Hg and Wp == Wg.
 struct Geom {
   int64_t B;
   int Hg, Wg, heads, d, M, shift;
-  int nH, nW;  // windows per image along rows / columns
+  int nH, nW;  // windows per image along rows / columns: Hp / M, Wp / M
+  int Hp, Wp;  // padded extents
   int N;       // tokens per window, M*M
   int64_t xs;  // elements between consecutive tokens of q, k, v and of dq, dk, dv
   int64_t os;  // elements between consecutive tokens of out and dout (heads * d)
@@ -48,7 +53,7 @@ __device__ __forceinline__ int region_of(int Y, int size, int M, int shift) {
 
 // Label of in-window token (r, c) of window (wy, wx); tokens attend only to equal labels.
 __device__ __forceinline__ int token_label(const Geom& g, int wy, int wx, int r, int c) {
-  return 3 * region_of(wy * g.M + r, g.Hg, g.M, g.shift) + region_of(wx * g.M + c, g.Wg, g.M, g.shift);
+  return 3 * region_of(wy * g.M + r, g.Hp, g.M, g.shift) + region_of(wx * g.M + c, g.Wp, g.M, g.shift);
 }
 
 // Order in which the kernels enumerate a window's tokens ("slots"): grouped by Swin region, so that
@@ -100,11 +105,17 @@ __device__ __forceinline__ void slot_rc(const WinOrder& o, int j, int& r, int& c
   c = c0 + j - qt * w;
 }
 
-// Token index (b, y, x) in the grid of in-window position (r, c) of window (wy, wx) of image b.
+// Token index (b, y, x) in the grid of in-window position (r, c) of window (wy, wx) of image b; the
+// position must not be padding (token_real).
 __device__ __forceinline__ int64_t token_index(const Geom& g, int64_t b, int wy, int wx, int r, int c) {
-  const int y = grid_coord(wy * g.M + r, g.shift, g.Hg);
-  const int x = grid_coord(wx * g.M + c, g.shift, g.Wg);
+  const int y = grid_coord(wy * g.M + r, g.shift, g.Hp);
+  const int x = grid_coord(wx * g.M + c, g.shift, g.Wp);
   return (b * g.Hg + y) * g.Wg + x;
+}
+
+// Whether in-window position (r, c) of window (wy, wx) is a grid token rather than padding.
+__device__ __forceinline__ bool token_real(const Geom& g, int wy, int wx, int r, int c) {
+  return grid_coord(wy * g.M + r, g.shift, g.Hp) < g.Hg && grid_coord(wx * g.M + c, g.shift, g.Wp) < g.Wg;
 }
 
 // Decompose a flat window-head index wh = ((b*nH + wy)*nW + wx)*heads + h.

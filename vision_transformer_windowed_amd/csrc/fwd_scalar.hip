@@ -4,9 +4,9 @@
 // softmax so no score matrix is stored (FlashSwin paper card, "FLASHSWIN: Unlocking Large Windows
 // and Dense Tokens in Swin Vision Transformers with Memory Efficient Attention": Abstract and
 // Figure 1(B)).  This path serves float32 tensors (all arithmetic in float32, no reduced-precision
-// products) and every (M, d) the MFMA path does not cover.  Keys are staged per tile in LDS after
-// rotation; each thread keeps its query's running max, running sum and output accumulator in
-// registers.
+// products) and every (M, d) the MFMA path does not cover, and grids padded to a multiple of M
+// (padding tokens are neither queries nor keys).  Keys are staged per tile in LDS after rotation;
+// each thread keeps its query's running max, running sum and output accumulator in registers.
 #include "fsw_common.h"
 #include "fsw_launch.h"
 
@@ -32,7 +32,7 @@ __global__ __launch_bounds__(kScalarThreads) void fwd_scalar_kernel(const IO* __
   const int tid = threadIdx.x;
   const int N = g.N;
   const int n = qb * kScalarThreads + tid;
-  const bool active = n < N;
+  const bool active = n < N && token_real(g, w.wy, w.wx, n / g.M, n % g.M);
   const float* tr = th_row + w.h * (D / 4);
   const float* tc = th_col + w.h * (D / 4);
   const int64_t xs = g.xs, os = g.os;
@@ -63,7 +63,7 @@ __global__ __launch_bounds__(kScalarThreads) void fwd_scalar_kernel(const IO* __
     __syncthreads();
     {
       const int j = t0 + tid;
-      if (j < N) {
+      if (j < N && token_real(g, w.wy, w.wx, j / g.M, j % g.M)) {
         const int r = j / g.M, c = j - (j / g.M) * g.M;
         const int64_t tok = token_index(g, w.b, w.wy, w.wx, r, c);
         float kv[D], vv[D];
@@ -77,7 +77,8 @@ __global__ __launch_bounds__(kScalarThreads) void fwd_scalar_kernel(const IO* __
         }
         sLab[tid] = token_label(g, w.wy, w.wx, r, c);
       } else {
-        // past the end of the window: never matches a query label; zero rows keep 0 * row finite
+        // past the end of the window, or padding: never matches a query label; zero rows keep 0 * row
+        // finite
 #pragma unroll
         for (int i = 0; i < D; ++i) {
           sK[tid][i] = 0.f;

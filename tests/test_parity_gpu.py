@@ -73,12 +73,15 @@ def assert_close_rowwise(name, got, ref, bound, rel_l2):
 
 
 def window_max(a, M, s):
-    """a [B, Hg, Wg, H] -> for every token, the maximum of a over the tokens of its shifted window."""
+    """a [B, Hg, Wg, H] >= 0 -> for every token, the maximum of a over the tokens of its shifted window
+    (a grid that M does not divide is padded with zeros to the next multiple, as the kernels see it)."""
     B, Hg, Wg, H = a.shape
-    r = np.roll(a, (-s, -s), axis=(1, 2)).reshape(B, Hg // M, M, Wg // M, M, H)
+    Hp, Wp = -(-Hg // M) * M, -(-Wg // M) * M
+    a = np.pad(a, [(0, 0), (0, Hp - Hg), (0, Wp - Wg), (0, 0)])
+    r = np.roll(a, (-s, -s), axis=(1, 2)).reshape(B, Hp // M, M, Wp // M, M, H)
     m = r.max(axis=(2, 4), keepdims=True)
-    m = np.broadcast_to(m, r.shape).reshape(B, Hg, Wg, H)
-    return np.roll(m, (s, s), axis=(1, 2))
+    m = np.broadcast_to(m, r.shape).reshape(B, Hp, Wp, H)
+    return np.roll(m, (s, s), axis=(1, 2))[:, :Hg, :Wg]
 
 
 def lse_rounding_bound(q, k, M, s, u):
@@ -221,7 +224,7 @@ def test_forward_nan_stays_in_its_window_region():
 
 
 @pytest.mark.parametrize("M,shift,grid,D", [(32, 16, 64, 32), (32, 0, 64, 32), (8, 3, 32, 32), (12, 5, 36, 32),
-                                            (16, 8, 32, 64), (20, 7, 40, 64)])
+                                            (16, 8, 32, 64), (20, 7, 40, 64), (16, 8, 40, 32)])
 def test_forward_loose_bound_falls_back(M, shift, grid, D):
     """One key with a large norm makes max|q| * max|k| overshoot the true row maximum of most
     queries by more than 80 (log2 units): their sums under the bound reference fall below
@@ -260,7 +263,7 @@ def _aligned_large_inputs(B, grid, H, D, amp, seed):
 @pytest.mark.parametrize("M,shift,grid,amp,u,D", [
     (32, 16, 64, 1024.0, U_FP16, 32), (32, 0, 64, 4096.0, U_BF16, 32), (8, 3, 32, 1024.0, U_FP16, 32),
     (8, 0, 32, 4096.0, U_BF16, 32), (16, 8, 32, 1024.0, U_FP16, 32), (12, 5, 36, 4096.0, U_BF16, 32),
-    (16, 8, 32, 1024.0, U_FP16, 64), (20, 0, 40, 4096.0, U_BF16, 64)])
+    (16, 8, 32, 1024.0, U_FP16, 64), (20, 0, 40, 4096.0, U_BF16, 64), (32, 16, 80, 1024.0, U_FP16, 32)])
 def test_forward_aligned_large_norms(M, shift, grid, amp, u, D):
     """Aligned queries and keys with large norms (q = k): the computed score of a query with its own
     key sits at the bound up to operand rounding, which alone can exceed it by far more than 128

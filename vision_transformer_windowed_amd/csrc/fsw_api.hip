@@ -3,9 +3,9 @@
 // Every check runs on the host before any HIP call, so an invalid call never touches the device.
 // Dispatch: bf16 with d == 32 and M <= 32 goes to the MFMA kernels, forward and backward; the bf16
 // d == 64 forward of windows up to 22 x 22 too.  Everything else (float32 tensors, other d, larger
-// windows, the d == 64 backward, grids that M does not divide) goes to the float32-arithmetic
-// kernels, which stream the keys through LDS in tiles, take any window size up to kMaxWindow and
-// skip the padding tokens of a padded grid.
+// windows, the d == 64 backward, the backward of grids that M does not divide) goes to the
+// float32-arithmetic kernels, which stream the keys through LDS in tiles, take any window size up to
+// kMaxWindow and skip the padding tokens of a padded grid.
 #include <algorithm>
 #include <mutex>
 
@@ -117,11 +117,10 @@ WsLayout workspace_layout(const fsw::Geom& g, bool mfma) {
   return w;
 }
 
-// Padded grids run on the float32-arithmetic kernels, the only ones that skip padding tokens.
+// The backward of a padded grid runs on the float32-arithmetic kernels (the MFMA forward skips
+// padding tokens too).
 bool padded(const fsw::Geom& g) { return g.Hp != g.Hg || g.Wp != g.Wg; }
-bool use_mfma_fwd(const fsw::Geom& g, int dtype) {
-  return dtype == FSW_BF16 && !padded(g) && fsw::fwd_mfma_supported(g);
-}
+bool use_mfma_fwd(const fsw::Geom& g, int dtype) { return dtype == FSW_BF16 && fsw::fwd_mfma_supported(g); }
 bool use_mfma(const fsw::Geom& g, int dtype) {
   return fsw::kHaveMfmaBwd && dtype == FSW_BF16 && !padded(g) && g.d == 32 && g.M <= kMaxM;
 }

@@ -292,7 +292,9 @@ __global__ __launch_bounds__(kM8Waves * 64, 4) void fwd_m8_kernel(const uint16_t
 
 }  // namespace
 
-bool fwd_m8_supported(const Geom& g) { return g.M == 8 && g.d == 32 && g.heads <= kM8MaxHeads; }
+bool fwd_m8_supported(const Geom& g) {
+  return g.M == 8 && g.d == 32 && g.heads <= kM8MaxHeads && g.Hp == g.Hg && g.Wp == g.Wg;  // no padding
+}
 
 hipError_t launch_fwd_m8(const FwdArgs& a, hipStream_t st) {
   const Geom& g = a.g;

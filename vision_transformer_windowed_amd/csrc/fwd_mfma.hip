@@ -12,7 +12,8 @@
 // channels).  One tile per wave keeps a wave
 // under 128 registers at d = 32, so four waves share each SIMD and hide each other's latencies
 // (d = 64 doubles the query operands and O^T accumulators: two waves per SIMD, up to 256).  The shift
-// and window partition are index arithmetic on the loads and stores.  A window with a single Swin
+// and window partition are index arithmetic on the loads and stores; the padding tokens of a grid
+// padded to a multiple of M are neither loaded nor stored and carry no query's label.  A window with a single Swin
 // region and an even number of whole 32-key blocks takes a branch-free, software-pipelined loop
 // (the score MFMAs of block b+1 are issued before the exponentials of block b).  Other windows mask
 // per element in key blocks whose labels are mixed and skip blocks with no label in common with
@@ -119,13 +120,30 @@ __device__ __forceinline__ void band_of(const WinOrder& o, int j, int& bs, int& 
 }
 
 // Grid token of in-window position (r, c) with the window size M passed explicitly (a constant in
-// the specialised kernels, so the index arithmetic folds).
+// the specialised kernels, so the index arithmetic folds); the position must not be padding.
 __device__ __forceinline__ int64_t tok_of(const Geom& g, const WinHead& w, int M, int r, int c) {
   int y = w.wy * M + r + g.shift;
-  y = y >= g.Hg ? y - g.Hg : y;
+  y = y >= g.Hp ? y - g.Hp : y;
   int x = w.wx * M + c + g.shift;
-  x = x >= g.Wg ? x - g.Wg : x;
+  x = x >= g.Wp ? x - g.Wp : x;
   return (w.b * g.Hg + y) * g.Wg + x;
+}
+
+// Whether in-window position (r, c) is a grid token rather than padding of a padded grid.
+__device__ __forceinline__ bool tok_real(const Geom& g, const WinHead& w, int M, int r, int c) {
+  int y = w.wy * M + r + g.shift;
+  y = y >= g.Hp ? y - g.Hp : y;
+  int x = w.wx * M + c + g.shift;
+  x = x >= g.Wp ? x - g.Wp : x;
+  return y < g.Hg && x < g.Wg;
+}
+
+// Whether window (wy, wx) holds padding tokens: some row or column of it maps past the grid.
+__device__ inline bool window_padded(const Geom& g, const WinHead& w, int M) {
+  if (g.Hp == g.Hg && g.Wp == g.Wg) return false;
+  bool p = false;
+  for (int i = 0; i < M; ++i) p |= !tok_real(g, w, M, i, 0) || !tok_real(g, w, M, 0, i);
+  return p;
 }
 
 // The wave's query operands: k-step t of the score product takes channels 16t + 8h .. 16t + 8h + 7.
@@ -314,7 +332,7 @@ __device__ __forceinline__ float stage_k(const FwdSmem& sm, const uint4 (&kraw)[
 template <int MAXIT, int D>
 __device__ __forceinline__ void load_kv(const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, const Geom& g,
                                         const WinHead& w, const uint16_t* rc, int M, int NP, int tid, int nt,
-                                        bool with_v, uint4 (&kraw)[MAXIT], uint4 (&vraw)[MAXIT]) {
+                                        bool with_v, bool pad, uint4 (&kraw)[MAXIT], uint4 (&vraw)[MAXIT]) {
   constexpr int PARTS = FwdDim<D>::PARTS;
   const int N = M * M;
 #pragma unroll
@@ -332,9 +350,11 @@ __device__ __forceinline__ void load_kv(const uint16_t* __restrict__ k, const ui
         r = key / M;
         c = key - (key / M) * M;
       }
-      const int64_t off = tok_of(g, w, M, r, c) * g.xs + w.h * D + (it % PARTS) * 8;
-      kraw[i] = *reinterpret_cast<const uint4*>(k + off);
-      if (with_v) vraw[i] = *reinterpret_cast<const uint4*>(v + off);
+      if (!pad || tok_real(g, w, M, r, c)) {  // padding stays zero
+        const int64_t off = tok_of(g, w, M, r, c) * g.xs + w.h * D + (it % PARTS) * 8;
+        kraw[i] = *reinterpret_cast<const uint4*>(k + off);
+        if (with_v) vraw[i] = *reinterpret_cast<const uint4*>(v + off);
+      }
     }
   }
 }
@@ -349,7 +369,9 @@ constexpr int fwd_min_waves() {
 // NWAVES waves of one 32-query tile each; one workgroup per window-head stages the window's K/V
 // once and then walks its query blocks of NWAVES*32 queries.  MT: compile-time window size
 // (0 = g.M at run time).  NPMAX: the largest padded window this configuration serves.  D: head dim.
-template <int NWAVES, int MT, int NPMAX, int D>
+// PAD: the grid is padded to a multiple of M (the padding checks cost a few percent, so grids that M
+// divides run an instance without them).
+template <int NWAVES, int MT, int NPMAX, int D, bool PAD>
 __global__ __launch_bounds__(NWAVES * 64, (fwd_min_waves<NWAVES, D>())) void fwd_mfma_kernel(const uint16_t* __restrict__ q,
                                                                const uint16_t* __restrict__ k,
                                                                const uint16_t* __restrict__ v,
@@ -397,14 +419,16 @@ __global__ __launch_bounds__(NWAVES * 64, (fwd_min_waves<NWAVES, D>())) void fwd
 
   // 0. slot order: in-window position and label of every slot.  In a window split by the shift the
   // loads below take their addresses from this table; otherwise slots are row-major.
+  // Padding tokens of a padded grid get label 0xff, like the slots past the window: no query's label.
   const bool split = wo.ra != M || wo.ca != M;  // one window per workgroup: uniform
+  const bool pad = PAD && window_padded(g, w, M);
   for (int n = tid; n < NP; n += NT) {
     uint8_t lb = 0xff;
     if (n < N) {
       int r, c;
       slot_rc(wo, n, r, c);
       sm.rc[n] = (uint16_t)(r << 8 | c);
-      lb = (uint8_t)token_label(g, w.wy, w.wx, r, c);
+      if (!pad || tok_real(g, w, M, r, c)) lb = (uint8_t)token_label(g, w.wy, w.wx, r, c);
     }
     sm.lab[n] = lb;
   }
@@ -412,7 +436,7 @@ __global__ __launch_bounds__(NWAVES * 64, (fwd_min_waves<NWAVES, D>())) void fwd
 
   // 1. every global load of the thread (K and V items, the queries of every block)
   uint4 kraw[MAXIT], vraw[MAXIT];
-  load_kv<MAXIT, D>(k, v, g, w, split ? sm.rc : nullptr, M, NP, tid, NT, true, kraw, vraw);
+  load_kv<MAXIT, D>(k, v, g, w, split ? sm.rc : nullptr, M, NP, tid, NT, true, pad, kraw, vraw);
   // the lane's query of block qb (16-byte pieces: channels 16t + 8h .. 16t + 8h + 7)
   auto load_q = [&](int qb, QOps<D>& a) {
     const int qi = (qoff + qb) * NT / 2 + wave * 32 + col;
@@ -420,9 +444,11 @@ __global__ __launch_bounds__(NWAVES * 64, (fwd_min_waves<NWAVES, D>())) void fwd
     for (int t = 0; t < Dim::KSTEPS; ++t) a[t] = make_uint4(0, 0, 0, 0);
     if (qb < nqw && qi < N) {
       const int rc = split ? (int)sm.rc[qi] : (qi / M) << 8 | (qi - (qi / M) * M);
-      const int64_t off = tok_of(g, w, M, rc >> 8, rc & 255) * g.xs + w.h * D;
+      if (!pad || tok_real(g, w, M, rc >> 8, rc & 255)) {  // padding stays zero
+        const int64_t off = tok_of(g, w, M, rc >> 8, rc & 255) * g.xs + w.h * D;
 #pragma unroll
-      for (int t = 0; t < Dim::KSTEPS; ++t) a[t] = *reinterpret_cast<const uint4*>(q + off + 16 * t + 8 * h);
+        for (int t = 0; t < Dim::KSTEPS; ++t) a[t] = *reinterpret_cast<const uint4*>(q + off + 16 * t + 8 * h);
+      }
     }
   };
   uint4 qraw[QBM][Dim::KSTEPS];
@@ -491,7 +517,7 @@ __global__ __launch_bounds__(NWAVES * 64, (fwd_min_waves<NWAVES, D>())) void fwd
   // fp16 score operands unless some |k~| or |q^| (hence some component) could leave fp16 range
   const bool h16 = kmax < kF16Limit && sqrtf(qmax2_all) < kF16Limit;
   if (!h16) {
-    load_kv<MAXIT, D>(k, v, g, w, split ? sm.rc : nullptr, M, NP, tid, NT, false, kraw, vraw);
+    load_kv<MAXIT, D>(k, v, g, w, split ? sm.rc : nullptr, M, NP, tid, NT, false, pad, kraw, vraw);
     __syncthreads();
     stage_k<MAXIT, D>(sm, kraw, M, split, NP, tid, NT, false);
     __syncthreads();
@@ -501,7 +527,7 @@ __global__ __launch_bounds__(NWAVES * 64, (fwd_min_waves<NWAVES, D>())) void fwd
     if (qb >= nqw) break;
     // 4. the wave's query operands (rotated, scaled by log2(e)/sqrt(d)), reference bound, labels
     const int qi = (qoff + qb) * NT / 2 + wave * 32 + col;
-    const bool qvalid = qi < N;
+    const bool qvalid = qi < N && (!pad || sm.lab[qi] != 0xff);
     const int qrc = !qvalid ? 0 : split ? (int)sm.rc[qi] : (qi / M) << 8 | (qi - (qi / M) * M);
     const int qr = qrc >> 8, qc = qrc & 255;
     QOps<D> qop;
@@ -528,7 +554,7 @@ __global__ __launch_bounds__(NWAVES * 64, (fwd_min_waves<NWAVES, D>())) void fwd
     // them (every window without a shift, and the bands of the usual shifted shapes).
     int kb0 = 0, kb1 = 0;
     bool run = false;
-    if (wave_single) {
+    if (wave_single && !pad) {  // a padded window's bands hold padding: the masked general pass
       int bs, be;
       band_of(wo, uniform((qoff + qb) * NT / 2 + wave * 32), bs, be);
       run = ((bs | be) & 31) == 0 && (((be - bs) >> 5) & 1) == 0;
@@ -570,7 +596,7 @@ __global__ __launch_bounds__(NWAVES * 64, (fwd_min_waves<NWAVES, D>())) void fwd
   }
 }
 
-template <int NWAVES, int MT, int NPMAX, int D>
+template <int NWAVES, int MT, int NPMAX, int D, bool PAD = false>
 hipError_t launch_nw(const FwdArgs& a, hipStream_t st) {
   const Geom& g = a.g;
   const int NP = (g.N + 31) / 32 * 32;
@@ -581,7 +607,7 @@ hipError_t launch_nw(const FwdArgs& a, hipStream_t st) {
   constexpr int kMaxDevices = 64;
   static std::once_flag once[kMaxDevices];
   const auto raise = [] {
-    (void)hipFuncSetAttribute((const void*)fwd_mfma_kernel<NWAVES, MT, NPMAX, D>,
+    (void)hipFuncSetAttribute((const void*)fwd_mfma_kernel<NWAVES, MT, NPMAX, D, PAD>,
                               hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
   };
   int dev = 0;
@@ -594,7 +620,7 @@ hipError_t launch_nw(const FwdArgs& a, hipStream_t st) {
   // two query blocks and enough work for several rounds of workgroups per CU
   const int nsplit = (nqb == 2 && nwh >= 64 * 8) ? 64 : 0;
   const int64_t blocks = nwh + nsplit;
-  hipLaunchKernelGGL((fwd_mfma_kernel<NWAVES, MT, NPMAX, D>), dim3((unsigned)blocks), dim3(NWAVES * 64), smem, st,
+  hipLaunchKernelGGL((fwd_mfma_kernel<NWAVES, MT, NPMAX, D, PAD>), dim3((unsigned)blocks), dim3(NWAVES * 64), smem, st,
                      (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, a.th_row, a.th_col,
                      (uint16_t*)a.out, a.lse, g, nqb, NP, nsplit);
   return hipGetLastError();
@@ -610,6 +636,18 @@ bool fwd_mfma_supported(const Geom& g) {
 hipError_t launch_fwd_mfma(const FwdArgs& a, hipStream_t st) {
   const int N = a.g.N;
   if (!fwd_mfma_supported(a.g)) return hipErrorInvalidValue;
+  if (a.g.Hp != a.g.Hg || a.g.Wp != a.g.Wg) {  // padded grid: the run-time-M instances with padding checks
+    if (a.g.d == 64) {
+      if (N <= 64) return launch_nw<2, 0, 64, 64, true>(a, st);
+      if (N <= 128) return launch_nw<4, 0, 128, 64, true>(a, st);
+      if (N <= 256) return launch_nw<4, 0, 256, 64, true>(a, st);
+      return launch_nw<8, 0, kMaxNP64, 64, true>(a, st);
+    }
+    if (N <= 64) return launch_nw<2, 0, 64, 32, true>(a, st);
+    if (N <= 128) return launch_nw<4, 0, 128, 32, true>(a, st);
+    if (N <= 256) return launch_nw<8, 0, 256, 32, true>(a, st);
+    return launch_nw<16, 0, 1024, 32, true>(a, st);
+  }
   if (a.g.d == 64) {
     if (N <= 64) return launch_nw<2, 0, 64, 64>(a, st);
     if (N <= 128) return launch_nw<4, 0, 128, 64>(a, st);

@@ -415,8 +415,8 @@ def main():
                                max(args.warmup, 2))
         bwd32 = [config_timing(dev, "flashswin_t_s1_p2_m32_bwd", s, ("bwd",), max(args.steps, 10),
                                max(args.warmup, 2)) for s in WORKLOADS["flashswin_t_s1_p2_m32_bwd"]["shifts"]]
-        d64 = [config_timing(dev, "wide_heads_s1_p2_m16_d64", s, ("fwd",), max(args.steps, 10), max(args.warmup, 2))
-               for s in WORKLOADS["wide_heads_s1_p2_m16_d64"]["shifts"]]
+        d64 = [config_timing(dev, "wide_heads_s1_p2_m16_d64", s, ("fwd", "bwd"), max(args.steps, 10),
+                             max(args.warmup, 2)) for s in WORKLOADS["wide_heads_s1_p2_m16_d64"]["shifts"]]
         mat = materialized_vs_fused(dev, 5, 1)
 
     gpu_out = {"out": out, "lse": lse, "dq": grads[0], "dk": grads[1], "dv": grads[2]}
@@ -457,7 +457,7 @@ def main():
         "m32_shift16_fwd": masked,
         "m32_bwd_b32": bwd32,
         "materialized_vs_fused": mat,
-        "d64_m16_fwd": d64,
+        "d64_m16_step": d64,
         "cpu_baseline": cpu,
         "parity_sample": parity,
         "input_gen_s": round(gen_s, 1),

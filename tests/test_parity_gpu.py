@@ -423,6 +423,14 @@ BWD_SMALL = [
     (1, 40, 40, 1, 32, 40, 13, "bf16"),
     (1, 64, 64, 1, 32, 64, 0, "bf16"),
     (1, 48, 48, 1, 16, 48, 24, "f32"),
+    # d = 64 on MFMA (windows of up to 256 tokens); M = 20 runs the float32-arithmetic kernels
+    (2, 8, 8, 2, 64, 4, 1, "bf16"),
+    (1, 16, 16, 2, 64, 8, 3, "bf16"),
+    (1, 33, 33, 1, 64, 11, 4, "bf16"),
+    (1, 24, 24, 2, 64, 12, 5, "bf16"),
+    (1, 32, 32, 2, 64, 16, 0, "bf16"),
+    (1, 48, 32, 3, 64, 16, 8, "bf16"),
+    (1, 40, 40, 1, 64, 20, 7, "bf16"),
     # grids that M does not divide (padded)
     (1, 10, 13, 2, 32, 4, 1, "f32"),
     (2, 7, 13, 1, 16, 6, 5, "f32"),
@@ -545,6 +553,28 @@ def test_m16_workload(shift):
     assert_close("O", _np(out[imgs]), ro, 2e-2, 5e-3)
     assert_close("LSE", _np(lse[imgs]), rl, 2e-2, 5e-3)
     oracle_bwd_over_batch(x, M, shift, got, chunk=16)
+
+
+@pytest.mark.parametrize("shift", [0, 8])
+def test_d64_workload(shift):
+    """64-wide heads at M = 16 at full size (64 images of 128 x 128 tokens, 3 heads of d = 64): forward on
+    sampled images, and the backward's dq, dk, dv of all images and its full-batch dtheta, against the
+    oracle."""
+    name = "wide_heads_s1_p2_m16_d64"
+    w = WORKLOADS[name]
+    M = w["M"]
+    x = workload_inputs(name, with_dout=True)
+    xd = to_dev(x)
+    out, lse = F.wattn_fwd(xd["q"], xd["k"], xd["v"], xd["theta_row"], xd["theta_col"], M, shift)
+    got = F.wattn_bwd(xd["q"], xd["k"], xd["v"], out, xd["dout"], lse, xd["theta_row"], xd["theta_col"], M,
+                      shift)
+    torch.cuda.synchronize()
+    imgs = [0, w["B"] - 1]
+    (q, k, v), tr, tc = oracle_args(x, imgs)
+    ro, rl = oracle.wattn_fwd_ref(q, k, v, tr, tc, M, shift)
+    assert_close("O", _np(out[imgs]), ro, 2e-2, 5e-3)
+    assert_close("LSE", _np(lse[imgs]), rl, 2e-2, 5e-3)
+    oracle_bwd_over_batch(x, M, shift, got, chunk=8)
 
 
 def test_autograd_matches_backward_entry_point():

@@ -1,11 +1,11 @@
 // C ABI of the window-attention library: argument validation, workspace sizing, dispatch.
 //
 // Every check runs on the host before any HIP call, so an invalid call never touches the device.
-// Dispatch: bf16 with d == 32 and M <= 32 goes to the MFMA kernels, forward and backward; the bf16
-// d == 64 forward of windows up to 22 x 22 too.  Everything else (float32 tensors, other d, larger
-// windows, the d == 64 backward, the backward of grids that M does not divide) goes to the
-// float32-arithmetic kernels, which stream the keys through LDS in tiles, take any window size up to
-// kMaxWindow and skip the padding tokens of a padded grid.
+// Dispatch: bf16 with d == 32 and M <= 32 goes to the MFMA kernels, forward and backward; bf16 with
+// d == 64 too, for windows up to 22 x 22 in the forward and 16 x 16 in the backward.  Everything else
+// (float32 tensors, other d, larger windows, the backward of grids that M does not divide) goes to
+// the float32-arithmetic kernels, which stream the keys through LDS in tiles, take any window size
+// up to kMaxWindow and skip the padding tokens of a padded grid.
 #include <algorithm>
 #include <mutex>
 
@@ -105,14 +105,19 @@ struct WsLayout {
   int64_t n_partials;
 };
 
-WsLayout workspace_layout(const fsw::Geom& g, bool mfma) {
+// Kernel family of a backward call.
+enum class BwdPath { kScalar, kMfma32, kMfma64 };
+
+WsLayout workspace_layout(const fsw::Geom& g, BwdPath path) {
   WsLayout w;
   const int64_t rows = g.B * g.Hg * g.Wg * g.heads;
   const int64_t nwh = g.B * g.nH * g.nW * g.heads;
   w.delta_off = 0;
   w.scal_off = align256((size_t)rows * sizeof(float));
   w.partials_off = w.scal_off + align256((size_t)nwh * 4 * sizeof(float));
-  w.n_partials = mfma ? fsw::bwd_mfma_partials(g) : fsw::bwd_scalar_partials(g);
+  w.n_partials = path == BwdPath::kMfma32   ? fsw::bwd_mfma_partials(g)
+                 : path == BwdPath::kMfma64 ? fsw::bwd_d64_partials(g)
+                                            : fsw::bwd_scalar_partials(g);
   w.total = w.partials_off + align256((size_t)w.n_partials * (g.d / 2) * sizeof(float));
   return w;
 }
@@ -121,8 +126,11 @@ WsLayout workspace_layout(const fsw::Geom& g, bool mfma) {
 // padding tokens too).
 bool padded(const fsw::Geom& g) { return g.Hp != g.Hg || g.Wp != g.Wg; }
 bool use_mfma_fwd(const fsw::Geom& g, int dtype) { return dtype == FSW_BF16 && fsw::fwd_mfma_supported(g); }
-bool use_mfma(const fsw::Geom& g, int dtype) {
-  return fsw::kHaveMfmaBwd && dtype == FSW_BF16 && !padded(g) && g.d == 32 && g.M <= kMaxM;
+BwdPath bwd_path(const fsw::Geom& g, int dtype) {
+  if (dtype != FSW_BF16 || padded(g)) return BwdPath::kScalar;
+  if (fsw::kHaveMfmaBwd && g.d == 32 && g.M <= kMaxM) return BwdPath::kMfma32;
+  if (fsw::bwd_d64_supported(g)) return BwdPath::kMfma64;
+  return BwdPath::kScalar;
 }
 
 // Pointer checks and dispatch of a forward whose shape (and q/k/v token stride) is in g.
@@ -157,8 +165,8 @@ int bwd_impl(const void* q, const void* k, const void* v, const void* out, const
              void* hip_stream) {
   if (!bwd_pointers_ok(q, k, v, out, dout, lse, theta_row, theta_col, dq, dk, dv, dtheta_row, dtheta_col))
     return FSW_ERR_INVALID_ARG;
-  const bool mfma = use_mfma(g, dtype);
-  const WsLayout ws = workspace_layout(g, mfma);
+  const BwdPath path = bwd_path(g, dtype);
+  const WsLayout ws = workspace_layout(g, path);
   if (!workspace || !aligned(workspace, 256) || workspace_bytes < ws.total) return FSW_ERR_WORKSPACE;
   char* base = static_cast<char*>(workspace);
   fsw::BwdArgs a{q,  k,  v,          out,        dout, lse, theta_row, theta_col,
@@ -166,7 +174,9 @@ int bwd_impl(const void* q, const void* k, const void* v, const void* out, const
                  reinterpret_cast<float*>(base + ws.delta_off), reinterpret_cast<float*>(base + ws.scal_off),
                  reinterpret_cast<float*>(base + ws.partials_off), ws.n_partials};
   hipStream_t s = reinterpret_cast<hipStream_t>(hip_stream);
-  const hipError_t e = mfma ? fsw::launch_bwd_mfma(a, s) : fsw::launch_bwd_scalar(a, s);
+  const hipError_t e = path == BwdPath::kMfma32   ? fsw::launch_bwd_mfma(a, s)
+                       : path == BwdPath::kMfma64 ? fsw::launch_bwd_d64(a, s)
+                                                  : fsw::launch_bwd_scalar(a, s);
   return e == hipSuccess ? FSW_OK : FSW_ERR_HIP;
 }
 
@@ -252,7 +262,7 @@ size_t flashswin_wattn_bwd_workspace_size(int64_t B, int64_t Hg, int64_t Wg, int
   fsw::Geom g;
   if (check_shape(B, Hg, Wg, heads, d, M, shift, dtype, &g) != FSW_OK) return 0;
   if (B == 0) return 0;
-  return workspace_layout(g, use_mfma(g, dtype)).total;
+  return workspace_layout(g, bwd_path(g, dtype)).total;
 }
 
 int flashswin_wattn_bwd(const void* q, const void* k, const void* v, const void* out, const void* dout,
@@ -341,7 +351,7 @@ int flashswin_wattn_bwd_noalloc(const void* q, const void* k, const void* v, con
   if (st != FSW_OK) return st;
   if (B == 0) return FSW_OK;
   // the size limit is checked before any HIP call
-  const size_t need = workspace_layout(g, use_mfma(g, dtype)).total;
+  const size_t need = workspace_layout(g, bwd_path(g, dtype)).total;
   if (need > (size_t)FLASHSWIN_SCRATCH_BYTES) return FSW_ERR_SCRATCH;
   const Sizes z = sizes_of(g, dtype);
   const Span outs[] = {{dq, z.tens}, {dk, z.tens}, {dv, z.tens}, {dtheta_row, z.theta}, {dtheta_col, z.theta}};

@@ -60,6 +60,10 @@ hipError_t launch_fwd_m8(const FwdArgs& a, hipStream_t st);
 // bf16 MFMA backward (d == 32, M <= 32).
 hipError_t launch_bwd_mfma(const BwdArgs& a, hipStream_t st);
 int64_t bwd_mfma_partials(const Geom& g);
+// bf16 MFMA backward for d == 64 and windows of at most 256 tokens (grids that M divides).
+bool bwd_d64_supported(const Geom& g);
+hipError_t launch_bwd_d64(const BwdArgs& a, hipStream_t st);
+int64_t bwd_d64_partials(const Geom& g);
 constexpr bool kHaveMfmaBwd = true;
 
 // Materialized comparison path (bf16, d == 32): scores in HBM, softmax, P.V.

@@ -30,6 +30,8 @@ pages for those conventions).
 from .wattn_ref import (  # noqa: F401
     check_args,
     check_bias,
+    check_lowrank,
+    lowrank_bias,
     region_labels,
     relative_bias,
     rope_rotate,

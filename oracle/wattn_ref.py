@@ -38,6 +38,14 @@ path.  Reading (the pages give no index convention): a per-head table
 bias[h, 2M-1, 2M-1], and the pair (query i, key j) at in-window positions
 (r_i, c_i), (r_j, c_j) gets bias[h, r_i - r_j + M - 1, c_i - c_j + M - 1].
 
+The forward and backward also take an optional rank-r additive bias, the learned low-rank bias
+factorization of the FlashBias comparison model ([FS] Table S1 and the Table 4 caption: a trainable
+rank-16 bias factorization whose parameters grow with M^2).  Reading: per head, factors
+U, W [heads, N, r] over the in-window token index n = r*M + c (the shifted frame, as for RoPE); the
+pair (query i, key j) adds sum_t U[h, n_i, t] W[h, n_j, t] to its scaled score, before the mask.
+Factors shared by all heads are the same array repeated per head.  The backward then also returns
+dU = sum over windows of dS W and dW = sum over windows of dS^T U.
+
 Parity: pinned by tests/test_oracle.py (brute force, library attention for
 theta = 0, constant-V, closed-form RoPE pair, region decomposition, finite
 differences, invariants, agreement with O2).  The RoPE conventions above are
@@ -53,6 +61,22 @@ def check_bias(bias, heads, M):
     """Validate an optional relative-position bias table [heads, 2M-1, 2M-1]."""
     if bias is not None and tuple(np.shape(bias)) != (heads, 2 * M - 1, 2 * M - 1):
         raise ValueError("bias must be [heads, 2M-1, 2M-1]")
+
+
+def check_lowrank(lowrank, heads, M):
+    """Validate optional rank-r bias factors (U, W), each [heads, M*M, r] with r >= 1."""
+    if lowrank is None:
+        return
+    U, W = lowrank
+    su, sw = np.shape(U), np.shape(W)
+    if len(su) != 3 or su != sw or su[:2] != (heads, M * M) or su[2] < 1:
+        raise ValueError("lowrank factors must both be [heads, M*M, r], r >= 1")
+
+
+def lowrank_bias(lowrank):
+    """The bias of every (query i, key j) pair of a window, [heads, N, N]: U[h] @ W[h]^T."""
+    U, W = (np.asarray(x, dtype=np.float64) for x in lowrank)
+    return U @ np.swapaxes(W, -1, -2)
 
 
 def check_args(shape, theta_row_shape, theta_col_shape, M, shift):
@@ -246,18 +270,23 @@ def _softmax_rows(S):
     return e / np.where(ssum > 0, ssum, 1.0), m, ssum
 
 
-def wattn_fwd_ref(q, k, v, theta_row, theta_col, M, shift, bias=None):
+def wattn_fwd_ref(q, k, v, theta_row, theta_col, M, shift, bias=None, lowrank=None):
     """Forward: returns (out [B,Hg,Wg,heads,d] float64, lse [B,Hg,Wg,heads] float64).
 
-    bias: optional relative-position bias table [heads, 2M-1, 2M-1] added to the scores."""
+    bias: optional relative-position bias table [heads, 2M-1, 2M-1] added to the scores.
+    lowrank: optional rank-r bias factors (U, W), each [heads, M*M, r]; U W^T is added to the scores."""
     q = np.asarray(q)
     B, Hg, Wg, heads, d = q.shape
     theta_row = np.asarray(theta_row, dtype=np.float64)
     theta_col = np.asarray(theta_col, dtype=np.float64)
     check_args(q.shape, theta_row.shape, theta_col.shape, M, shift)
     check_bias(bias, heads, M)
+    check_lowrank(lowrank, heads, M)
     N = M * M
     rb = None if bias is None else relative_bias(bias, M)[None]
+    if lowrank is not None:
+        lb = lowrank_bias(lowrank)[None]
+        rb = lb if rb is None else rb + lb
     qw = rope_rotate(_windows(q, M, shift), theta_row, theta_col, M)
     kw = rope_rotate(_windows(k, M, shift), theta_row, theta_col, M)
     vw = _windows(v, M, shift)
@@ -299,19 +328,27 @@ def _dtheta_terms(xt, dxt, M):
     return res[0], res[1]
 
 
-def wattn_bwd_ref(q, k, v, dout, theta_row, theta_col, M, shift):
+def wattn_bwd_ref(q, k, v, dout, theta_row, theta_col, M, shift, lowrank=None):
     """Analytic backward of wattn_fwd_ref.
 
-    Returns (dq, dk, dv [B,Hg,Wg,heads,d], dtheta_row, dtheta_col [heads,d/4]), float64.
+    Returns (dq, dk, dv [B,Hg,Wg,heads,d], dtheta_row, dtheta_col [heads,d/4]), float64, and with
+    lowrank = (U, W) also (dU, dW [heads, M*M, r]).
     dV = P^T dO; dP = dO V^T; D_i = sum_j P_ij dP_ij; dS = P o (dP - D);
-    dq~ = dS k~ / sqrt(d); dk~ = dS^T q~ / sqrt(d); dq = R^T dq~, dk = R^T dk~.
+    dq~ = dS k~ / sqrt(d); dk~ = dS^T q~ / sqrt(d); dq = R^T dq~, dk = R^T dk~;
+    dU = sum over windows of dS W; dW = sum over windows of dS^T U.
     """
     q = np.asarray(q)
     B, Hg, Wg, heads, d = q.shape
     theta_row = np.asarray(theta_row, dtype=np.float64)
     theta_col = np.asarray(theta_col, dtype=np.float64)
     check_args(q.shape, theta_row.shape, theta_col.shape, M, shift)
+    check_lowrank(lowrank, heads, M)
     N = M * M
+    lb = None if lowrank is None else lowrank_bias(lowrank)[None]
+    if lowrank is not None:
+        U, W = (np.asarray(x, dtype=np.float64) for x in lowrank)
+        dU = np.zeros_like(U)
+        dW = np.zeros_like(W)
     qw = rope_rotate(_windows(q, M, shift), theta_row, theta_col, M)
     kw = rope_rotate(_windows(k, M, shift), theta_row, theta_col, M)
     vw = _windows(v, M, shift)
@@ -323,6 +360,8 @@ def wattn_bwd_ref(q, k, v, dout, theta_row, theta_col, M, shift):
     scale = 1.0 / np.sqrt(d)
     for sl in _chunks(qw.shape[0], heads, N):
         S = qw[sl] @ np.swapaxes(kw[sl], -1, -2) * scale
+        if lb is not None:
+            S = S + lb
         if live_all is not None:
             S = np.where(live_all[sl], S, -np.inf)
         P = _softmax_rows(S)[0]
@@ -332,6 +371,9 @@ def wattn_bwd_ref(q, k, v, dout, theta_row, theta_col, M, shift):
         dS = P * (dP - Dr)
         dqt[sl] = dS @ kw[sl] * scale
         dkt[sl] = np.swapaxes(dS, -1, -2) @ qw[sl] * scale
+        if lowrank is not None:
+            dU += (dS @ W[None]).sum(axis=0)
+            dW += (np.swapaxes(dS, -1, -2) @ U[None]).sum(axis=0)
     tr_q, tc_q = _dtheta_terms(qw, dqt, M)
     tr_k, tc_k = _dtheta_terms(kw, dkt, M)
     dqw = rope_rotate(dqt, theta_row, theta_col, M, inverse=True)
@@ -340,4 +382,5 @@ def wattn_bwd_ref(q, k, v, dout, theta_row, theta_col, M, shift):
     def back(xw):
         return _grid_back(xw, B, Hg, Wg, M, shift)
 
-    return back(dqw), back(dkw), back(dvw), tr_q + tr_k, tc_q + tc_k
+    grads = (back(dqw), back(dkw), back(dvw), tr_q + tr_k, tc_q + tc_k)
+    return grads if lowrank is None else grads + (dU, dW)

@@ -43,12 +43,12 @@ def _rand_case(seed, B, Hg, Wg, H, D, theta_scale=1.0):
 
 # ----------------------------------------------------------------------------- brute force
 
-def brute_force_fwd(q, k, v, tr, tc, M, s, bias=None):
+def brute_force_fwd(q, k, v, tr, tc, M, s, bias=None, lowrank=None):
     """Per-token scalar loops; every key of the grid is tested for membership.  With a bias table, the
     pair of query (Y, X) and key (Y2, X2) (shifted frame) adds bias[h][Y%M - Y2%M + M-1][X%M - X2%M + M-1].
     A grid that M does not divide lives in the frame of its padded extent Hp x Wp (the next multiples of
     M): the shifted frame, the windows and the regions are those of Hp x Wp, and only grid tokens are
-    ever keys."""
+    ever keys.  With rank-r factors (U, W), the pair also adds sum_t U[h][nq][t] W[h][nk][t], n = (Y%M)*M + X%M."""
     B, Hg, Wg, H, D = q.shape
     Hp, Wp = -(-Hg // M) * M, -(-Wg // M) * M
 
@@ -90,6 +90,10 @@ def brute_force_fwd(q, k, v, tr, tc, M, s, bias=None):
                             sc = sum(qt[i] * kt[i] for i in range(D)) / math.sqrt(D)
                             if bias is not None:
                                 sc += float(bias[h][Y % M - Y2 % M + M - 1][X % M - X2 % M + M - 1])
+                            if lowrank is not None:
+                                nq, nk = (Y % M) * M + X % M, (Y2 % M) * M + X2 % M
+                                sc += sum(float(lowrank[0][h][nq][t]) * float(lowrank[1][h][nk][t])
+                                          for t in range(len(lowrank[0][h][nq])))
                             scores.append(sc)
                             vals.append(v[b, y2, x2, h])
                     mx = max(scores)
@@ -234,6 +238,124 @@ def pin_bias_brute_force(fwd=None, scores=None):
 
 def test_relative_bias_brute_force():
     pin_bias_brute_force()
+
+
+# Rank-r bias factors (FlashBias reading): (B, Hg, Wg, H, D, M, s, r)
+LOWRANK_CASES = [(1, 4, 4, 2, 8, 2, 0, 1), (1, 6, 6, 1, 8, 3, 1, 3), (2, 6, 9, 2, 4, 3, 2, 2), (1, 10, 9, 1, 4, 4, 2, 5)]
+
+
+def _factors(seed, H, M, r, scale=0.7):
+    rng = np.random.default_rng(seed)
+    return rng.standard_normal((H, M * M, r)) * scale, rng.standard_normal((H, M * M, r)) * scale
+
+
+def pin_lowrank_brute_force(fwd=None):
+    fwd = fwd or oracle.wattn_fwd_ref
+    for i, (B, Hg, Wg, H, D, M, s, r) in enumerate(LOWRANK_CASES):
+        q, k, v, _, tr, tc = _rand_case(90 + i, B, Hg, Wg, H, D)
+        lr = _factors(95 + i, H, M, r)
+        o, l = fwd(q, k, v, tr, tc, M, s, lowrank=lr)
+        ob, lb = brute_force_fwd(q, k, v, tr, tc, M, s, lowrank=lr)
+        np.testing.assert_allclose(o, ob, rtol=0, atol=1e-12)
+        np.testing.assert_allclose(l, lb, rtol=0, atol=1e-12)
+
+
+def test_lowrank_brute_force():
+    pin_lowrank_brute_force()
+
+
+def test_lowrank_constant_bias_shifts_lse_only():
+    """Rank 1 with U = c and W = 1 adds the same c to every score: softmax, hence O, is unchanged and
+    LSE moves by exactly c."""
+    B, Hg, Wg, H, D, M, s = 1, 8, 8, 2, 8, 4, 2
+    q, k, v, _, tr, tc = _rand_case(97, B, Hg, Wg, H, D)
+    c = 1.75
+    lr = (np.full((H, M * M, 1), c), np.ones((H, M * M, 1)))
+    o0, l0 = oracle.wattn_fwd_ref(q, k, v, tr, tc, M, s)
+    o1, l1 = oracle.wattn_fwd_ref(q, k, v, tr, tc, M, s, lowrank=lr)
+    np.testing.assert_allclose(o1, o0, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(l1, l0 + c, rtol=0, atol=1e-13)
+
+
+def test_lowrank_full_rank_factors_reproduce_the_relative_bias_table():
+    """A relative-position table's pair matrix B[h] (N x N) is U W^T exactly for U = B[h], W = I
+    (rank N): the low-rank route equals the table route, which the bias brute force pins."""
+    B, Hg, Wg, H, D, M, s = 1, 6, 9, 2, 8, 3, 1
+    q, k, v, _, tr, tc = _rand_case(98, B, Hg, Wg, H, D)
+    table = np.random.default_rng(99).standard_normal((H, 2 * M - 1, 2 * M - 1))
+    pair = oracle.relative_bias(table, M)
+    lr = (pair, np.broadcast_to(np.eye(M * M), (H, M * M, M * M)).copy())
+    o0, l0 = oracle.wattn_fwd_ref(q, k, v, tr, tc, M, s, bias=table)
+    o1, l1 = oracle.wattn_fwd_ref(q, k, v, tr, tc, M, s, lowrank=lr)
+    np.testing.assert_allclose(o1, o0, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(l1, l0, rtol=0, atol=1e-12)
+
+
+def pin_lowrank_finite_differences(fwd=None, bwd=None):
+    """Central differences of L = sum(O * dO) for dq, dk, dv, dtheta and the factors dU, dW."""
+    fwd = fwd or oracle.wattn_fwd_ref
+    bwd = bwd or oracle.wattn_bwd_ref
+    h = 1e-6
+    for i, (B, Hg, Wg, H, D, M, s, r) in enumerate([(1, 4, 4, 1, 4, 2, 1, 2), (1, 5, 3, 1, 4, 2, 1, 3)]):
+        q, k, v, do, tr, tc = _rand_case(110 + i, B, Hg, Wg, H, D)
+        U, W = _factors(115 + i, H, M, r)
+        args = [q, k, v, tr, tc, U, W]
+        grads = bwd(q, k, v, do, tr, tc, M, s, lowrank=(U, W))
+        assert len(grads) == 7
+
+        def loss(a):
+            o, _ = fwd(a[0], a[1], a[2], a[3], a[4], M, s, lowrank=(a[5], a[6]))
+            return float((o * do).sum())
+
+        for which in range(7):
+            base = args[which]
+            num = np.zeros_like(base)
+            it = np.nditer(base, flags=["multi_index"])
+            for _ in it:
+                idx = it.multi_index
+                plus = [a.copy() for a in args]
+                minus = [a.copy() for a in args]
+                plus[which][idx] += h
+                minus[which][idx] -= h
+                num[idx] = (loss(plus) - loss(minus)) / (2 * h)
+            np.testing.assert_allclose(grads[which], num, rtol=0, atol=2e-8 * max(1.0, np.abs(num).max()))
+
+
+def test_lowrank_finite_differences():
+    pin_lowrank_finite_differences()
+
+
+def test_lowrank_pins_catch_planted_mistakes():
+    """Plausible mistakes planted in the oracle's low-rank bias (CPU only): the factors' roles swapped
+    (W U^T), the bias scaled by 1/sqrt(d) like the scores, the factors summed over the rank before the
+    product.  The brute-force pin fails for each."""
+    orig = wattn_ref.lowrank_bias
+
+    def swapped(lowrank):
+        return orig((lowrank[1], lowrank[0]))
+
+    def scaled(lowrank):
+        return orig(lowrank) / np.sqrt(8.0)
+
+    def summed_factors(lowrank):  # (sum_t U)(sum_t W) instead of sum_t U W
+        U, W = (np.asarray(x, dtype=np.float64) for x in lowrank)
+        return U.sum(axis=-1)[..., :, None] * W.sum(axis=-1)[..., None, :]
+
+    for mutant in (swapped, scaled, summed_factors):
+        wattn_ref.lowrank_bias = mutant
+        try:
+            assert _fails(pin_lowrank_brute_force), mutant.__name__
+        finally:
+            wattn_ref.lowrank_bias = orig
+
+
+def test_lowrank_shape_is_checked():
+    q = np.zeros((1, 4, 4, 2, 8))
+    th = np.zeros((2, 2))
+    for bad in ((np.zeros((2, 16, 3)), np.zeros((2, 16, 2))), (np.zeros((1, 16, 2)), np.zeros((1, 16, 2))),
+                (np.zeros((2, 9, 2)), np.zeros((2, 9, 2))), (np.zeros((2, 16, 0)), np.zeros((2, 16, 0)))):
+        with pytest.raises(ValueError):
+            oracle.wattn_fwd_ref(q, q, q, th, th, 4, 0, lowrank=bad)
 
 
 def test_bias_shape_is_checked():

@@ -162,6 +162,64 @@ int flashswin_wattn_bwd_packed(const void* qkv, const void* out, const void* dou
                                int64_t B, int64_t Hg, int64_t Wg, int heads, int d,
                                int M, int shift, int dtype, void* hip_stream);
 
+/* Largest rank of the low-rank bias factors of flashswin_wattn_fwd_lowrank / _bwd_lowrank. */
+#define FLASHSWIN_MAX_RANK 32
+
+/*
+ * flashswin_wattn_fwd with a rank-r additive bias on the scores: the learned low-rank bias
+ * factorization of the FlashBias comparison model ([FS] Table S1: a trainable rank-16 bias
+ * factorization whose parameters grow with the window; Table 4 caption), folded into the fused
+ * attention as r extra score channels.
+ *
+ *   bias_u,
+ *   bias_w       device, float32 [heads, M*M, rank], 4-byte aligned: per head, factors over the
+ *                in-window token index n = r*M + c (shifted frame, as for RoPE).  The pair (query i,
+ *                key j) adds sum_t bias_u[h, n_i, t] * bias_w[h, n_j, t] to its scaled score
+ *                q~ . k~ / sqrt(d), before the region mask.  Factors shared by all heads are passed
+ *                repeated per head.
+ *   rank         1 <= rank <= FLASHSWIN_MAX_RANK (rank < 1: FSW_ERR_INVALID_ARG; larger:
+ *                FSW_ERR_UNSUPPORTED).
+ *   Every other argument as in flashswin_wattn_fwd; out and lse may not share a byte with the
+ *   factors.  LSE includes the bias.  Runs on the float32-arithmetic kernels (any supported d, M,
+ *   dtype, padded grids included).
+ * Returns FSW_OK, FSW_ERR_INVALID_ARG, FSW_ERR_UNSUPPORTED or FSW_ERR_HIP.
+ */
+int flashswin_wattn_fwd_lowrank(const void* q, const void* k, const void* v,
+                                const float* theta_row, const float* theta_col,
+                                const float* bias_u, const float* bias_w, int rank,
+                                void* out, float* lse,
+                                int64_t B, int64_t Hg, int64_t Wg, int heads, int d,
+                                int M, int shift, int dtype, void* hip_stream);
+
+/*
+ * Bytes of workspace flashswin_wattn_bwd_lowrank needs: the backward's own workspace plus the
+ * per-window gradients of both factors (2 * windows * heads * M*M * rank * 4 bytes).  0 when B == 0
+ * and for arguments that call would reject.
+ */
+size_t flashswin_wattn_bwd_lowrank_workspace_size(int64_t B, int64_t Hg, int64_t Wg, int heads, int d,
+                                                  int M, int shift, int dtype, int rank);
+
+/*
+ * Backward of flashswin_wattn_fwd_lowrank ([FS] Table S1: the trainable factorization).  Besides
+ * the outputs of flashswin_wattn_bwd it writes the factor gradients
+ *   dbias_u      device, float32 [heads, M*M, rank], 4-byte aligned, overwritten:
+ *                sum over all windows of dS W (dS = dL/d(score) = P (dP - Delta));
+ *   dbias_w      likewise, sum over all windows of dS^T U.
+ * Both are summed over the windows in a fixed order (bit-reproducible).  The outputs may not share
+ * a byte with any input, the workspace or each other.  lse must come from
+ * flashswin_wattn_fwd_lowrank with the same factors.
+ * Returns FSW_OK, FSW_ERR_INVALID_ARG, FSW_ERR_UNSUPPORTED, FSW_ERR_WORKSPACE or FSW_ERR_HIP.
+ */
+int flashswin_wattn_bwd_lowrank(const void* q, const void* k, const void* v, const void* out,
+                                const void* dout, const float* lse,
+                                const float* theta_row, const float* theta_col,
+                                const float* bias_u, const float* bias_w, int rank,
+                                void* dq, void* dk, void* dv, float* dtheta_row, float* dtheta_col,
+                                float* dbias_u, float* dbias_w,
+                                void* workspace, size_t workspace_bytes,
+                                int64_t B, int64_t Hg, int64_t Wg, int heads, int d,
+                                int M, int shift, int dtype, void* hip_stream);
+
 /*
  * Bytes of workspace flashswin_wattn_fwd_materialized needs: the float32 score rows of every
  * window-head, heads * windows * N * NP * 4 with N = M*M and NP = N rounded up to a multiple of 32.

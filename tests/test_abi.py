@@ -242,3 +242,78 @@ def test_padded_grid_workspace_counts_padded_windows():
     want = al(B * Hg * Wg * H * 4) + al(nwin * H * 4 * 4) + al(H * 2 * nwin * 1 * (d // 2) * 4)
     for dt in (F.FSW_BF16, F.FSW_F32):
         assert F.flashswin_wattn_bwd_workspace_size(B, Hg, Wg, H, d, M, 1, dt) == want
+
+
+# ----------------------------------------------------------------------- low-rank bias entry points
+# Shape 1 x 16 x 16 tokens, 2 heads, d 32, M 8: factors [2, 64, rank] float32.
+
+def fwd_lr(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, tr=FAKE + 3 * GIB, tc=FAKE + 3 * GIB + 256, bu=FAKE + 4 * GIB,
+             bw=FAKE + 5 * GIB, rank=4, out=FAKE + GIB, lse=FAKE + 2 * GIB, B=1, Hg=16, Wg=16, heads=2, d=32, M=8,
+             shift=0, dtype=F.FSW_BF16)
+    a.update(kw)
+    return F.flashswin_wattn_fwd_lowrank(a["q"], a["k"], a["v"], a["tr"], a["tc"], a["bu"], a["bw"], a["rank"],
+                                         a["out"], a["lse"], a["B"], a["Hg"], a["Wg"], a["heads"], a["d"], a["M"],
+                                         a["shift"], a["dtype"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(rank=0), F.FSW_ERR_INVALID_ARG),
+    (dict(rank=-2), F.FSW_ERR_INVALID_ARG),
+    (dict(rank=F.MAX_RANK + 1), F.FSW_ERR_UNSUPPORTED),
+    (dict(bu=None), F.FSW_ERR_INVALID_ARG),
+    (dict(bw=None), F.FSW_ERR_INVALID_ARG),
+    (dict(bu=FAKE + 4 * GIB + 2), F.FSW_ERR_INVALID_ARG),  # misaligned factor
+    (dict(out=FAKE + 4 * GIB), F.FSW_ERR_INVALID_ARG),     # out over the U factor
+    (dict(lse=FAKE + 5 * GIB + 64), F.FSW_ERR_INVALID_ARG),  # lse inside the W factor (2 x 64 x 4 floats)
+    (dict(shift=8), F.FSW_ERR_INVALID_ARG),
+    (dict(d=12), F.FSW_ERR_UNSUPPORTED),
+])
+def test_lowrank_forward_rejects_before_launch(kw, status):
+    assert fwd_lr(**kw) == status
+
+
+def test_lowrank_forward_empty_batch_is_a_no_op():
+    assert fwd_lr(B=0, q=None, k=None, v=None, out=None, lse=None, tr=None, tc=None) == F.FSW_OK
+
+
+def test_lowrank_workspace_adds_the_per_window_factor_gradients():
+    def al(n):
+        return (n + 255) // 256 * 256
+    for dt in (F.FSW_BF16, F.FSW_F32):
+        base = F.flashswin_wattn_bwd_workspace_size(1, 16, 16, 2, 32, 8, 4, F.FSW_F32)  # the float32-arithmetic layout
+        got = F.flashswin_wattn_bwd_lowrank_workspace_size(1, 16, 16, 2, 32, 8, 4, dt, 5)
+        assert got == base + al(2 * 4 * 2 * 64 * 5 * 4)
+    assert F.flashswin_wattn_bwd_lowrank_workspace_size(1, 16, 16, 2, 32, 8, 4, F.FSW_BF16, 0) == 0
+    assert F.flashswin_wattn_bwd_lowrank_workspace_size(1, 16, 16, 2, 32, 8, 4, F.FSW_BF16, F.MAX_RANK + 1) == 0
+
+
+def bwd_lr(**kw):
+    a = dict(q=FAKE, k=FAKE + GIB, v=FAKE + 2 * GIB, out=FAKE + 3 * GIB, dout=FAKE + 4 * GIB,
+             lse=FAKE + 5 * GIB, tr=FAKE + 6 * GIB, tc=FAKE + 6 * GIB + 256, bu=FAKE + 12 * GIB, bw=FAKE + 13 * GIB,
+             rank=3, dq=FAKE + 7 * GIB, dk=FAKE + 8 * GIB, dv=FAKE + 9 * GIB, dtr=FAKE + 10 * GIB,
+             dtc=FAKE + 10 * GIB + 256, dbu=FAKE + 14 * GIB, dbw=FAKE + 15 * GIB, ws=FAKE + 11 * GIB, wsb=None,
+             B=1, Hg=16, Wg=16, heads=2, d=32, M=8, shift=4, dtype=F.FSW_BF16)
+    a.update(kw)
+    if a["wsb"] is None:
+        a["wsb"] = F.flashswin_wattn_bwd_lowrank_workspace_size(a["B"], a["Hg"], a["Wg"], a["heads"], a["d"], a["M"],
+                                                                a["shift"], a["dtype"], max(a["rank"], 1))
+    return F.flashswin_wattn_bwd_lowrank(a["q"], a["k"], a["v"], a["out"], a["dout"], a["lse"], a["tr"], a["tc"],
+                                         a["bu"], a["bw"], a["rank"], a["dq"], a["dk"], a["dv"], a["dtr"], a["dtc"],
+                                         a["dbu"], a["dbw"], a["ws"], a["wsb"], a["B"], a["Hg"], a["Wg"], a["heads"],
+                                         a["d"], a["M"], a["shift"], a["dtype"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(rank=0), F.FSW_ERR_INVALID_ARG),
+    (dict(rank=F.MAX_RANK + 1), F.FSW_ERR_UNSUPPORTED),
+    (dict(dbu=None), F.FSW_ERR_INVALID_ARG),
+    (dict(dbw=FAKE + 15 * GIB + 1), F.FSW_ERR_INVALID_ARG),  # misaligned
+    (dict(dbu=FAKE + 12 * GIB), F.FSW_ERR_INVALID_ARG),      # dU over U
+    (dict(dbw=FAKE + 14 * GIB + 128), F.FSW_ERR_INVALID_ARG),  # dW inside dU (2 x 64 x 3 floats)
+    (dict(dbu=FAKE + 11 * GIB + 512), F.FSW_ERR_INVALID_ARG),  # dU inside the workspace
+    (dict(wsb=1024), F.FSW_ERR_WORKSPACE),
+    (dict(lse=None), F.FSW_ERR_INVALID_ARG),
+])
+def test_lowrank_backward_rejects_before_launch(kw, status):
+    assert bwd_lr(**kw) == status

@@ -1,0 +1,117 @@
+"""GPU parity of the rank-r additive bias (flashswin_wattn_fwd_lowrank / flashswin_wattn_bwd_lowrank)
+against the fp64 oracle: O, LSE, dQ, dK, dV, dtheta and the factor gradients dU, dW.
+
+The factors are N(0, 0.5^2) per entry; the oracle adds U[h, n_i] . W[h, n_j] to the scaled score of
+every pair before the region mask.  Tolerances are those of test_parity_gpu.py: bf16 inputs, max-abs
+<= 2e-2 and relative L2 <= 5e-3 (for dtheta, dU and dW, which are sums over the whole batch, max-abs
+relative to max|ref|); float32 inputs, 1e-5 both, max-abs relative to max|ref| when that exceeds 1."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import vision_transformer_windowed_amd as F
+from vision_transformer_windowed_amd.inputs import make_inputs
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def _np(t):
+    return t.detach().to("cpu", torch.float64).numpy()
+
+
+def _close(name, got, ref, max_abs, rel, scale_abs=False):
+    err = np.abs(got - ref).max()
+    l2 = np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-300)
+    bound = max_abs * max(1.0, np.abs(ref).max()) if scale_abs else max_abs
+    print(f"  {name}: max-abs {err:.3e} (bound {bound:.3e}) rel-L2 {l2:.3e}", flush=True)
+    assert np.all(np.isfinite(got)), name
+    assert err <= bound and l2 <= rel, name
+
+
+def _factors(H, M, r, seed):
+    g = torch.Generator().manual_seed(seed)
+    return (torch.randn((H, M * M, r), generator=g) * 0.5, torch.randn((H, M * M, r), generator=g) * 0.5)
+
+
+CASES = [
+    # B, Hg, Wg, heads, d, M, shift, rank, dtype
+    (1, 16, 16, 2, 32, 8, 0, 16, "f32"),
+    (2, 12, 12, 1, 16, 6, 3, 4, "f32"),
+    (1, 10, 13, 2, 32, 4, 1, 3, "f32"),      # padded grid
+    (1, 32, 32, 2, 32, 8, 4, 16, "bf16"),
+    (1, 32, 48, 1, 32, 16, 8, 16, "bf16"),
+    (1, 64, 64, 1, 32, 32, 16, 8, "bf16"),
+    (1, 24, 24, 2, 64, 12, 5, 32, "bf16"),
+    (1, 14, 14, 1, 8, 7, 2, 1, "bf16"),
+    (1, 50, 38, 1, 32, 16, 8, 16, "bf16"),   # padded grid
+]
+
+
+def _run(case):
+    B, Hg, Wg, H, D, M, s, r, dt = case
+    x = make_inputs(B, Hg, Wg, H, D, dt, seed=900 + M + s + r, with_dout=True)
+    U, W = _factors(H, M, r, seed=950 + M + r)
+    xd = {n: t.to(DEV) for n, t in x.items()}
+    Ud, Wd = U.to(DEV), W.to(DEV)
+    out, lse = F.wattn_fwd_lowrank(xd["q"], xd["k"], xd["v"], xd["theta_row"], xd["theta_col"], Ud, Wd, M, s)
+    grads = F.wattn_bwd_lowrank(xd["q"], xd["k"], xd["v"], out, xd["dout"], lse, xd["theta_row"], xd["theta_col"],
+                                Ud, Wd, M, s)
+    torch.cuda.synchronize()
+    q, k, v, do = (x[n].double().numpy() for n in ("q", "k", "v", "dout"))
+    tr, tc = x["theta_row"].double().numpy(), x["theta_col"].double().numpy()
+    lr = (U.double().numpy(), W.double().numpy())
+    ref_fwd = oracle.wattn_fwd_ref(q, k, v, tr, tc, M, s, lowrank=lr)
+    ref_bwd = oracle.wattn_bwd_ref(q, k, v, do, tr, tc, M, s, lowrank=lr)
+    return (out, lse), grads, ref_fwd, ref_bwd
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "B{}_{}x{}_h{}_d{}_M{}_s{}_r{}_{}".format(*c))
+def test_lowrank_matches_oracle(case):
+    dt = case[-1]
+    (out, lse), grads, (ro, rl), rg = _run(case)
+    if dt == "f32":
+        tol = dict(max_abs=1e-5, rel=1e-5, scale_abs=True)
+        _close("O", _np(out), ro, **tol)
+        _close("LSE", _np(lse), rl, **tol)
+    else:
+        _close("O", _np(out), ro, 2e-2, 5e-3)
+        _close("LSE", _np(lse), rl, 2e-2, 5e-3)
+    names = ("dQ", "dK", "dV", "dtheta_row", "dtheta_col", "dU", "dW")
+    for i, (name, got, ref) in enumerate(zip(names, grads, rg)):
+        if dt == "f32":
+            _close(name, _np(got), ref, 1e-5, 1e-5, scale_abs=True)
+        else:
+            _close(name, _np(got), ref, 2e-2, 5e-3, scale_abs=i >= 3)
+
+
+def test_lowrank_factor_gradients_are_reproducible():
+    """dU and dW are per-window sums reduced in a fixed order: two calls give identical bits."""
+    B, Hg, Wg, H, D, M, s, r = 2, 32, 32, 2, 32, 8, 4, 8
+    x = make_inputs(B, Hg, Wg, H, D, "bf16", seed=971, with_dout=True)
+    U, W = (t.to(DEV) for t in _factors(H, M, r, seed=972))
+    xd = {n: t.to(DEV) for n, t in x.items()}
+    out, lse = F.wattn_fwd_lowrank(xd["q"], xd["k"], xd["v"], xd["theta_row"], xd["theta_col"], U, W, M, s)
+    g1 = F.wattn_bwd_lowrank(xd["q"], xd["k"], xd["v"], out, xd["dout"], lse, xd["theta_row"], xd["theta_col"], U,
+                             W, M, s)
+    g2 = F.wattn_bwd_lowrank(xd["q"], xd["k"], xd["v"], out, xd["dout"], lse, xd["theta_row"], xd["theta_col"], U,
+                             W, M, s)
+    torch.cuda.synchronize()
+    for a, b in zip(g1, g2):
+        assert torch.equal(a, b)
+
+
+def test_lowrank_zero_factors_equal_the_plain_forward():
+    """U = W = 0 adds nothing: the low-rank forward (float32-arithmetic kernels) equals the plain forward
+    of the same inputs on the float32 path."""
+    B, Hg, Wg, H, D, M, s = 1, 16, 16, 2, 32, 8, 3
+    x = make_inputs(B, Hg, Wg, H, D, "f32", seed=973)
+    xd = {n: t.to(DEV) for n, t in x.items()}
+    Z = torch.zeros((H, M * M, 2), device=DEV)
+    o1, l1 = F.wattn_fwd_lowrank(xd["q"], xd["k"], xd["v"], xd["theta_row"], xd["theta_col"], Z, Z, M, s)
+    o0, l0 = F.wattn_fwd(xd["q"], xd["k"], xd["v"], xd["theta_row"], xd["theta_col"], M, s)
+    torch.cuda.synchronize()
+    assert torch.allclose(o1, o0, rtol=0, atol=1e-6) and torch.allclose(l1, l0, rtol=0, atol=1e-6)

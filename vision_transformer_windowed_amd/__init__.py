@@ -19,6 +19,7 @@ from ._lib import (  # noqa: F401
     FSW_OK,
     FlashSwinError,
     LIB_PATH,
+    MAX_RANK,
     SCRATCH_BYTES,
     WindowAttention,
     WindowAttentionPacked,
@@ -27,16 +28,21 @@ from ._lib import (  # noqa: F401
     flashswin_version,
     flashswin_wattn_bwd,
     flashswin_wattn_bwd_workspace_size,
+    flashswin_wattn_bwd_lowrank,
+    flashswin_wattn_bwd_lowrank_workspace_size,
     flashswin_wattn_bwd_noalloc,
     flashswin_wattn_bwd_packed,
     flashswin_wattn_fwd,
+    flashswin_wattn_fwd_lowrank,
     flashswin_wattn_fwd_materialized,
     flashswin_wattn_fwd_materialized_workspace_size,
     flashswin_wattn_fwd_packed,
     load,
     wattn_bwd,
+    wattn_bwd_lowrank,
     wattn_bwd_packed,
     wattn_fwd,
+    wattn_fwd_lowrank,
     wattn_fwd_materialized,
     wattn_fwd_packed,
     window_attention,

@@ -18,6 +18,7 @@ LIB_PATH = os.path.join(_HERE, "libflashswin.so")
 
 FSW_OK, FSW_ERR_INVALID_ARG, FSW_ERR_UNSUPPORTED, FSW_ERR_WORKSPACE, FSW_ERR_HIP, FSW_ERR_SCRATCH = range(6)
 SCRATCH_BYTES = 32 * 1024 * 1024  # FLASHSWIN_SCRATCH_BYTES of include/flashswin.h
+MAX_RANK = 32  # FLASHSWIN_MAX_RANK of include/flashswin.h
 FSW_F32, FSW_BF16 = 0, 1
 
 EXPORTED = (
@@ -29,6 +30,9 @@ EXPORTED = (
     "flashswin_wattn_bwd_noalloc",
     "flashswin_wattn_fwd_materialized_workspace_size",
     "flashswin_wattn_fwd_materialized",
+    "flashswin_wattn_fwd_lowrank",
+    "flashswin_wattn_bwd_lowrank_workspace_size",
+    "flashswin_wattn_bwd_lowrank",
     "flashswin_status_string",
     "flashswin_version",
 )
@@ -69,6 +73,13 @@ def load():
     lib.flashswin_wattn_fwd_materialized_workspace_size.argtypes = [i64, i64, i64, i32, i32, i32, i32, i32]
     lib.flashswin_wattn_fwd_materialized.restype = i32
     lib.flashswin_wattn_fwd_materialized.argtypes = [vp] * 9 + [sz, i64, i64, i64, i32, i32, i32, i32, i32, vp]
+    lib.flashswin_wattn_fwd_lowrank.restype = i32
+    lib.flashswin_wattn_fwd_lowrank.argtypes = [vp] * 7 + [i32, vp, vp, i64, i64, i64, i32, i32, i32, i32, i32, vp]
+    lib.flashswin_wattn_bwd_lowrank_workspace_size.restype = sz
+    lib.flashswin_wattn_bwd_lowrank_workspace_size.argtypes = [i64, i64, i64, i32, i32, i32, i32, i32, i32]
+    lib.flashswin_wattn_bwd_lowrank.restype = i32
+    lib.flashswin_wattn_bwd_lowrank.argtypes = ([vp] * 10 + [i32] + [vp] * 8 + [sz, i64, i64, i64, i32, i32, i32, i32, i32,
+                                                                        vp])
     lib.flashswin_status_string.restype = ctypes.c_char_p
     lib.flashswin_status_string.argtypes = [i32]
     lib.flashswin_version.restype = i32
@@ -128,6 +139,25 @@ def flashswin_wattn_fwd_materialized(q, k, v, theta_row, theta_col, bias, out, l
     """Raw call of the materialized comparison forward (scores in the caller's workspace)."""
     return load().flashswin_wattn_fwd_materialized(q, k, v, theta_row, theta_col, bias, out, lse, workspace,
                                                    workspace_bytes, B, Hg, Wg, heads, d, M, shift, dtype, stream)
+
+
+def flashswin_wattn_fwd_lowrank(q, k, v, theta_row, theta_col, bias_u, bias_w, rank, out, lse, B, Hg, Wg, heads, d,
+                                M, shift, dtype, stream):
+    """Raw call of the forward with a rank-r additive bias U W^T on the scores."""
+    return load().flashswin_wattn_fwd_lowrank(q, k, v, theta_row, theta_col, bias_u, bias_w, rank, out, lse, B, Hg,
+                                              Wg, heads, d, M, shift, dtype, stream)
+
+
+def flashswin_wattn_bwd_lowrank_workspace_size(B, Hg, Wg, heads, d, M, shift, dtype, rank):
+    return load().flashswin_wattn_bwd_lowrank_workspace_size(B, Hg, Wg, heads, d, M, shift, dtype, rank)
+
+
+def flashswin_wattn_bwd_lowrank(q, k, v, out, dout, lse, theta_row, theta_col, bias_u, bias_w, rank, dq, dk, dv,
+                                dtheta_row, dtheta_col, dbias_u, dbias_w, workspace, workspace_bytes, B, Hg, Wg, heads,
+                                d, M, shift, dtype, stream):
+    return load().flashswin_wattn_bwd_lowrank(q, k, v, out, dout, lse, theta_row, theta_col, bias_u, bias_w, rank, dq,
+                                              dk, dv, dtheta_row, dtheta_col, dbias_u, dbias_w, workspace,
+                                              workspace_bytes, B, Hg, Wg, heads, d, M, shift, dtype, stream)
 
 
 def flashswin_status_string(status):
@@ -280,6 +310,71 @@ def wattn_bwd(q, k, v, out, dout, lse, theta_row, theta_col, M, shift=0, workspa
     if st != FSW_OK:
         raise FlashSwinError(st, "flashswin_wattn_bwd")
     return dq, dk, dv, dtr, dtc
+
+
+def _check_factors(bias_u, bias_w, H, M, dev):
+    if bias_u.dim() != 3:
+        raise ValueError("bias_u must be [heads, M*M, rank]")
+    rank = bias_u.shape[2]
+    for name, t in (("bias_u", bias_u), ("bias_w", bias_w)):
+        _check_grid(name, t, (H, int(M) * int(M), rank), torch.float32, dev)
+    return rank
+
+
+def wattn_fwd_lowrank(q, k, v, theta_row, theta_col, bias_u, bias_w, M, shift=0, out=None, lse=None, need_lse=True):
+    """Forward with a rank-r additive bias bias_u[n_i] . bias_w[n_j] on the scores (factors float32
+    [heads, M*M, rank]).  Returns (out, lse)."""
+    B, Hg, Wg, H, D = q.shape
+    code = _dtype_code(q)
+    dev = q.device
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check_grid(name, t, q.shape, q.dtype, dev)
+    for name, t in (("theta_row", theta_row), ("theta_col", theta_col)):
+        _check_grid(name, t, (H, D // 4), torch.float32, dev)
+    rank = _check_factors(bias_u, bias_w, H, M, dev)
+    if out is None:
+        out = torch.empty_like(q)
+    _check_grid("out", out, q.shape, q.dtype, dev)
+    if need_lse:
+        if lse is None:
+            lse = torch.empty((B, Hg, Wg, H), device=dev, dtype=torch.float32)
+        _check_grid("lse", lse, (B, Hg, Wg, H), torch.float32, dev)
+    else:
+        lse = None
+    with torch.cuda.device(dev):
+        st = flashswin_wattn_fwd_lowrank(_ptr(q), _ptr(k), _ptr(v), _ptr(theta_row), _ptr(theta_col), _ptr(bias_u),
+                                         _ptr(bias_w), rank, _ptr(out), _ptr(lse), B, Hg, Wg, H, D, int(M), int(shift),
+                                         code, _stream(dev))
+    if st != FSW_OK:
+        raise FlashSwinError(st, "flashswin_wattn_fwd_lowrank")
+    return out, lse
+
+
+def wattn_bwd_lowrank(q, k, v, out, dout, lse, theta_row, theta_col, bias_u, bias_w, M, shift=0, workspace=None):
+    """Backward of wattn_fwd_lowrank.  Returns (dq, dk, dv, dtheta_row, dtheta_col, dbias_u, dbias_w)."""
+    B, Hg, Wg, H, D = q.shape
+    code = _dtype_code(q)
+    dev = q.device
+    for name, t in (("q", q), ("k", k), ("v", v), ("out", out), ("dout", dout)):
+        _check_grid(name, t, q.shape, q.dtype, dev)
+    _check_grid("lse", lse, (B, Hg, Wg, H), torch.float32, dev)
+    for name, t in (("theta_row", theta_row), ("theta_col", theta_col)):
+        _check_grid(name, t, (H, D // 4), torch.float32, dev)
+    rank = _check_factors(bias_u, bias_w, H, M, dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    dtr, dtc = torch.empty_like(theta_row), torch.empty_like(theta_col)
+    dbu, dbw = torch.empty_like(bias_u), torch.empty_like(bias_w)
+    nbytes = flashswin_wattn_bwd_lowrank_workspace_size(B, Hg, Wg, H, D, int(M), int(shift), code, rank)
+    workspace, wbytes = _workspace(workspace, nbytes, dev)
+    with torch.cuda.device(dev):
+        st = flashswin_wattn_bwd_lowrank(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _ptr(lse),
+                                         _ptr(theta_row), _ptr(theta_col), _ptr(bias_u), _ptr(bias_w), rank, _ptr(dq),
+                                         _ptr(dk), _ptr(dv), _ptr(dtr), _ptr(dtc), _ptr(dbu), _ptr(dbw),
+                                         _ptr(workspace), wbytes, B, Hg, Wg, H, D, int(M), int(shift), code,
+                                         _stream(dev))
+    if st != FSW_OK:
+        raise FlashSwinError(st, "flashswin_wattn_bwd_lowrank")
+    return dq, dk, dv, dtr, dtc, dbu, dbw
 
 
 def _packed_shape(qkv):

@@ -8,6 +8,9 @@
 //   dq~_i = sum_j dS_ij k~_j / sqrt(d),   dk~_j = sum_i dS_ij q~_i / sqrt(d),
 //   dq = R^T dq~, dk = R^T dk~, and for a rotated pair (a, b) at angle theta * p,
 //   dtheta += p (dx~_b x~_a - dx~_a x~_b) over all Q and K tokens.
+// With a rank-r bias U[n_i] . W[n_j] on the scores (the FlashBias factorization on the same paper card,
+// Table S1), dW[n_j] = sum_i dS_ij U[n_i] and dU[n_i] = sum_j dS_ij W[n_j] per window: the dK/dV and dQ
+// kernels write them per window and position, and a last kernel sums the windows in a fixed order.
 // Three kernels: Delta; dK/dV with one thread per key; dQ with one thread per query.  Padding tokens
 // of a padded grid are neither queries nor keys (no loads, no stores, no dtheta terms).  The theta
 // gradient is reduced per workgroup in a fixed order into a partials buffer, then summed over
@@ -75,16 +78,18 @@ __device__ __forceinline__ int64_t partial_row(const Geom& g, int64_t blk, int n
   return ((int64_t)h * 2 + which) * per_head + win * nb + (blk % nb);
 }
 
-template <typename IO, int D>
+template <typename IO, int D, bool LR>
 __global__ __launch_bounds__(kBwdThreads) void bwd_dkdv_scalar_kernel(
     const IO* __restrict__ q, const IO* __restrict__ k, const IO* __restrict__ v, const IO* __restrict__ dout,
     const float* __restrict__ lse, const float* __restrict__ delta, const float* __restrict__ th_row,
     const float* __restrict__ th_col, IO* __restrict__ dk, IO* __restrict__ dv, float* __restrict__ partials, Geom g,
-    int nb) {
+    int nb, LowRank lr, float* __restrict__ wparts) {
+  constexpr int R = LR ? kMaxRank : 1;
   __shared__ float sQ[kBwdThreads][D];  // q~ * log2(e) / sqrt(d)
   __shared__ float sG[kBwdThreads][D];  // dO
   __shared__ float sL[kBwdThreads];     // lse * log2(e)
   __shared__ float sDel[kBwdThreads];
+  __shared__ float sU[LR ? kBwdThreads : 1][R];  // the queries' U rows
   __shared__ int sLab[kBwdThreads];
 
   const int64_t blk = blockIdx.x;
@@ -99,9 +104,18 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkdv_scalar_kernel(
   const float qscale = kLog2e * rsqrtf((float)D);
 
   float kt[D], vv[D];
+  float wk[R], dwk[R];  // the key's W row times log2(e), and its gradient
+#pragma unroll
+  for (int t = 0; t < R; ++t) wk[t] = dwk[t] = 0.f;
   int klab = -2, kr = 0, kc = 0;
   int64_t ktok = 0;
   if (active) {
+    if (LR) {
+      const float* wrow = lr.w + ((int64_t)w.h * N + j) * lr.rank;
+#pragma unroll
+      for (int t = 0; t < R; ++t)
+        if (t < lr.rank) wk[t] = wrow[t] * kLog2e;
+    }
     kr = j / g.M;
     kc = j - kr * g.M;
     ktok = token_index(g, w.b, w.wy, w.wx, kr, kc);
@@ -136,6 +150,11 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkdv_scalar_kernel(
         sL[tid] = lse[tok * g.heads + w.h] * kLog2e;
         sDel[tid] = delta[tok * g.heads + w.h];
         sLab[tid] = token_label(g, w.wy, w.wx, r, c);
+        if (LR) {
+          const float* urow = lr.u + ((int64_t)w.h * N + i) * lr.rank;
+#pragma unroll
+          for (int t = 0; t < R; ++t) sU[tid][t] = t < lr.rank ? urow[t] : 0.f;
+        }
       } else {
         sLab[tid] = -1;
       }
@@ -150,12 +169,21 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkdv_scalar_kernel(
         s2 = __builtin_fmaf(sQ[i][e], kt[e], s2);
         dp = __builtin_fmaf(sG[i][e], vv[e], dp);
       }
+      if (LR) {
+#pragma unroll
+        for (int t = 0; t < R; ++t) s2 = __builtin_fmaf(sU[i][t], wk[t], s2);
+      }
       const float p = exp2f(s2 - sL[i]);
       const float ds = p * (dp - sDel[i]) * kLn2;  // dS / log2(e), pairs with the log2(e) in sQ
 #pragma unroll
       for (int e = 0; e < D; ++e) {
         dvv[e] = __builtin_fmaf(p, sG[i][e], dvv[e]);
         dkt[e] = __builtin_fmaf(ds, sQ[i][e], dkt[e]);
+      }
+      if (LR) {
+        const float dsn = p * (dp - sDel[i]);  // dS
+#pragma unroll
+        for (int t = 0; t < R; ++t) dwk[t] = __builtin_fmaf(dsn, sU[i][t], dwk[t]);
       }
     }
   }
@@ -169,16 +197,25 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkdv_scalar_kernel(
     store_row<D>(dk + ktok * xs + w.h * D, dkt);
     store_row<D>(dv + ktok * xs + w.h * D, dvv);
   }
+  if (LR && j < N) {  // this window's dW row of position j (zero for padding)
+    float* dst = wparts + ((blk / nb) * N + j) * lr.rank;
+#pragma unroll
+    for (int t = 0; t < R; ++t)
+      if (t < lr.rank) dst[t] = dwk[t];
+  }
   reduce_dtheta_block<D>(terms, partials + partial_row(g, blk, nb, 0) * (D / 2));
 }
 
-template <typename IO, int D>
+template <typename IO, int D, bool LR>
 __global__ __launch_bounds__(kBwdThreads) void bwd_dq_scalar_kernel(
     const IO* __restrict__ q, const IO* __restrict__ k, const IO* __restrict__ v, const IO* __restrict__ dout,
     const float* __restrict__ lse, const float* __restrict__ delta, const float* __restrict__ th_row,
-    const float* __restrict__ th_col, IO* __restrict__ dq, float* __restrict__ partials, Geom g, int nb) {
+    const float* __restrict__ th_col, IO* __restrict__ dq, float* __restrict__ partials, Geom g, int nb, LowRank lr,
+    float* __restrict__ uparts) {
+  constexpr int R = LR ? kMaxRank : 1;
   __shared__ float sK[kBwdThreads][D];  // k~
   __shared__ float sV[kBwdThreads][D];
+  __shared__ float sW[LR ? kBwdThreads : 1][R];  // the keys' W rows
   __shared__ int sLab[kBwdThreads];
 
   const int64_t blk = blockIdx.x;
@@ -194,10 +231,19 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dq_scalar_kernel(
   const float kscale = rsqrtf((float)D);
 
   float qt[D], qs[D], gv[D];
+  float uq[R], duq[R];  // the query's U row times log2(e), and its gradient
+#pragma unroll
+  for (int t = 0; t < R; ++t) uq[t] = duq[t] = 0.f;
   float l2 = 0.f, del = 0.f;
   int qlab = -2, qr = 0, qc = 0;
   int64_t qtok = 0;
   if (active) {
+    if (LR) {
+      const float* urow = lr.u + ((int64_t)w.h * N + i) * lr.rank;
+#pragma unroll
+      for (int t = 0; t < R; ++t)
+        if (t < lr.rank) uq[t] = urow[t] * kLog2e;
+    }
     qr = i / g.M;
     qc = i - qr * g.M;
     qtok = token_index(g, w.b, w.wy, w.wx, qr, qc);
@@ -234,6 +280,11 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dq_scalar_kernel(
           sV[tid][e] = vv[e];
         }
         sLab[tid] = token_label(g, w.wy, w.wx, r, c);
+        if (LR) {
+          const float* wrow = lr.w + ((int64_t)w.h * N + j) * lr.rank;
+#pragma unroll
+          for (int t = 0; t < R; ++t) sW[tid][t] = t < lr.rank ? wrow[t] : 0.f;
+        }
       } else {
         sLab[tid] = -1;
       }
@@ -248,10 +299,19 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dq_scalar_kernel(
         s2 = __builtin_fmaf(qs[e], sK[j][e], s2);
         dp = __builtin_fmaf(gv[e], sV[j][e], dp);
       }
+      if (LR) {
+#pragma unroll
+        for (int t = 0; t < R; ++t) s2 = __builtin_fmaf(uq[t], sW[j][t], s2);
+      }
       const float p = exp2f(s2 - l2);
       const float ds = p * (dp - del) * kscale;
 #pragma unroll
       for (int e = 0; e < D; ++e) dqt[e] = __builtin_fmaf(ds, sK[j][e], dqt[e]);
+      if (LR) {
+        const float dsn = p * (dp - del);  // dS
+#pragma unroll
+        for (int t = 0; t < R; ++t) duq[t] = __builtin_fmaf(dsn, sW[j][t], duq[t]);
+      }
     }
   }
 
@@ -263,7 +323,24 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dq_scalar_kernel(
     rope_unrotate<D>(dqt, tr, tc, qr, qc);
     store_row<D>(dq + qtok * xs + w.h * D, dqt);
   }
+  if (LR && i < N) {  // this window's dU row of position i (zero for padding)
+    float* dst = uparts + ((blk / nb) * N + i) * lr.rank;
+#pragma unroll
+    for (int t = 0; t < R; ++t)
+      if (t < lr.rank) dst[t] = duq[t];
+  }
   reduce_dtheta_block<D>(terms, partials + partial_row(g, blk, nb, 1) * (D / 2));
+}
+
+// Factor gradients: out[e] = sum over windows w of parts[w][e] in window order, e over the
+// heads * N * rank entries of one factor (parts laid out [windows][heads][N][rank]).
+__global__ __launch_bounds__(256) void lowrank_reduce_kernel(const float* __restrict__ parts, int64_t nwin,
+                                                             int64_t per_win, float* __restrict__ out) {
+  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (e >= per_win) return;
+  float s = 0.f;
+  for (int64_t w = 0; w < nwin; ++w) s += parts[w * per_win + e];
+  out[e] = s;
 }
 
 // Sum the partial rows of one (head, pair-slot) in a fixed order: thread t takes rows t, t+256, ...
@@ -314,17 +391,40 @@ static hipError_t launch_bwd_scalar_t(const BwdArgs& a, hipStream_t st) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int nb = (g.N + kBwdThreads - 1) / kBwdThreads;
-  const int64_t blocks = g.B * g.nH * g.nW * g.heads * nb;
-  hipLaunchKernelGGL((bwd_dkdv_scalar_kernel<IO, D>), dim3((unsigned)blocks), dim3(kBwdThreads), 0, st,
-                     (const IO*)a.q, (const IO*)a.k, (const IO*)a.v, (const IO*)a.dout, a.lse, a.delta, a.th_row,
-                     a.th_col, (IO*)a.dk, (IO*)a.dv, a.partials, g, nb);
+  const int64_t nwin = g.B * g.nH * g.nW;
+  const int64_t blocks = nwin * g.heads * nb;
+  const int64_t per_win = (int64_t)g.heads * g.N * a.lr.rank;  // entries of one factor
+  float* wparts = a.lr_parts;
+  float* uparts = a.lr.rank > 0 ? a.lr_parts + nwin * per_win : nullptr;
+  if (a.lr.rank > 0)
+    hipLaunchKernelGGL((bwd_dkdv_scalar_kernel<IO, D, true>), dim3((unsigned)blocks), dim3(kBwdThreads), 0, st,
+                       (const IO*)a.q, (const IO*)a.k, (const IO*)a.v, (const IO*)a.dout, a.lse, a.delta, a.th_row,
+                       a.th_col, (IO*)a.dk, (IO*)a.dv, a.partials, g, nb, a.lr, wparts);
+  else
+    hipLaunchKernelGGL((bwd_dkdv_scalar_kernel<IO, D, false>), dim3((unsigned)blocks), dim3(kBwdThreads), 0, st,
+                       (const IO*)a.q, (const IO*)a.k, (const IO*)a.v, (const IO*)a.dout, a.lse, a.delta, a.th_row,
+                       a.th_col, (IO*)a.dk, (IO*)a.dv, a.partials, g, nb, a.lr, wparts);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((bwd_dq_scalar_kernel<IO, D>), dim3((unsigned)blocks), dim3(kBwdThreads), 0, st,
-                     (const IO*)a.q, (const IO*)a.k, (const IO*)a.v, (const IO*)a.dout, a.lse, a.delta, a.th_row,
-                     a.th_col, (IO*)a.dq, a.partials, g, nb);
+  if (a.lr.rank > 0)
+    hipLaunchKernelGGL((bwd_dq_scalar_kernel<IO, D, true>), dim3((unsigned)blocks), dim3(kBwdThreads), 0, st,
+                       (const IO*)a.q, (const IO*)a.k, (const IO*)a.v, (const IO*)a.dout, a.lse, a.delta, a.th_row,
+                       a.th_col, (IO*)a.dq, a.partials, g, nb, a.lr, uparts);
+  else
+    hipLaunchKernelGGL((bwd_dq_scalar_kernel<IO, D, false>), dim3((unsigned)blocks), dim3(kBwdThreads), 0, st,
+                       (const IO*)a.q, (const IO*)a.k, (const IO*)a.v, (const IO*)a.dout, a.lse, a.delta, a.th_row,
+                       a.th_col, (IO*)a.dq, a.partials, g, nb, a.lr, uparts);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if (a.lr.rank > 0) {
+    const unsigned rblocks = (unsigned)((per_win + 255) / 256);
+    hipLaunchKernelGGL(lowrank_reduce_kernel, dim3(rblocks), dim3(256), 0, st, (const float*)wparts, nwin, per_win,
+                       a.dw);
+    hipLaunchKernelGGL(lowrank_reduce_kernel, dim3(rblocks), dim3(256), 0, st, (const float*)uparts, nwin, per_win,
+                       a.du);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   const int64_t rows_per_head = 2 * g.B * g.nH * g.nW * nb;
   return launch_dtheta_reduce(a.partials, a.n_partials, rows_per_head, g, a.dth_row, a.dth_col, st);
 }

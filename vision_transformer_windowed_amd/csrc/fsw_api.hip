@@ -101,14 +101,15 @@ Sizes sizes_of(const fsw::Geom& g, int dtype) {
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct WsLayout {
-  size_t delta_off, scal_off, partials_off, total;
+  size_t delta_off, scal_off, partials_off, lr_off, total;
   int64_t n_partials;
 };
 
 // Kernel family of a backward call.
 enum class BwdPath { kScalar, kMfma32, kMfma64 };
 
-WsLayout workspace_layout(const fsw::Geom& g, BwdPath path) {
+// rank > 0: room for the per-window gradients of both low-rank bias factors.
+WsLayout workspace_layout(const fsw::Geom& g, BwdPath path, int rank = 0) {
   WsLayout w;
   const int64_t rows = g.B * g.Hg * g.Wg * g.heads;
   const int64_t nwh = g.B * g.nH * g.nW * g.heads;
@@ -118,7 +119,8 @@ WsLayout workspace_layout(const fsw::Geom& g, BwdPath path) {
   w.n_partials = path == BwdPath::kMfma32   ? fsw::bwd_mfma_partials(g)
                  : path == BwdPath::kMfma64 ? fsw::bwd_d64_partials(g)
                                             : fsw::bwd_scalar_partials(g);
-  w.total = w.partials_off + align256((size_t)w.n_partials * (g.d / 2) * sizeof(float));
+  w.lr_off = w.partials_off + align256((size_t)w.n_partials * (g.d / 2) * sizeof(float));
+  w.total = w.lr_off + align256((size_t)2 * g.B * g.nH * g.nW * g.heads * g.N * rank * sizeof(float));
   return w;
 }
 
@@ -126,8 +128,9 @@ WsLayout workspace_layout(const fsw::Geom& g, BwdPath path) {
 // padding tokens too).
 bool padded(const fsw::Geom& g) { return g.Hp != g.Hg || g.Wp != g.Wg; }
 bool use_mfma_fwd(const fsw::Geom& g, int dtype) { return dtype == FSW_BF16 && fsw::fwd_mfma_supported(g); }
-BwdPath bwd_path(const fsw::Geom& g, int dtype) {
-  if (dtype != FSW_BF16 || padded(g)) return BwdPath::kScalar;
+// A low-rank bias runs on the float32-arithmetic kernels.
+BwdPath bwd_path(const fsw::Geom& g, int dtype, int rank = 0) {
+  if (dtype != FSW_BF16 || padded(g) || rank > 0) return BwdPath::kScalar;
   if (fsw::kHaveMfmaBwd && g.d == 32 && g.M <= kMaxM) return BwdPath::kMfma32;
   if (fsw::bwd_d64_supported(g)) return BwdPath::kMfma64;
   return BwdPath::kScalar;
@@ -135,13 +138,14 @@ BwdPath bwd_path(const fsw::Geom& g, int dtype) {
 
 // Pointer checks and dispatch of a forward whose shape (and q/k/v token stride) is in g.
 int fwd_impl(const void* q, const void* k, const void* v, const float* theta_row, const float* theta_col, void* out,
-             float* lse, const fsw::Geom& g, int dtype, void* hip_stream) {
+             float* lse, const fsw::Geom& g, int dtype, void* hip_stream, const fsw::LowRank& lr = {}) {
   if (!q || !k || !v || !out || !theta_row || !theta_col) return FSW_ERR_INVALID_ARG;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16)) return FSW_ERR_INVALID_ARG;
   if (!aligned(theta_row, 4) || !aligned(theta_col, 4) || (lse && !aligned(lse, 4))) return FSW_ERR_INVALID_ARG;
-  fsw::FwdArgs a{q, k, v, theta_row, theta_col, out, lse, g, dtype};
+  fsw::FwdArgs a{q, k, v, theta_row, theta_col, out, lse, g, dtype, lr};
   hipStream_t s = reinterpret_cast<hipStream_t>(hip_stream);
-  const hipError_t e = use_mfma_fwd(g, dtype) ? fsw::launch_fwd_mfma(a, s) : fsw::launch_fwd_scalar(a, s);
+  const bool mfma = lr.rank == 0 && use_mfma_fwd(g, dtype);
+  const hipError_t e = mfma ? fsw::launch_fwd_mfma(a, s) : fsw::launch_fwd_scalar(a, s);
   return e == hipSuccess ? FSW_OK : FSW_ERR_HIP;
 }
 
@@ -162,17 +166,18 @@ bool bwd_pointers_ok(const void* q, const void* k, const void* v, const void* ou
 int bwd_impl(const void* q, const void* k, const void* v, const void* out, const void* dout, const float* lse,
              const float* theta_row, const float* theta_col, void* dq, void* dk, void* dv, float* dtheta_row,
              float* dtheta_col, void* workspace, size_t workspace_bytes, const fsw::Geom& g, int dtype,
-             void* hip_stream) {
+             void* hip_stream, const fsw::LowRank& lr = {}, float* du = nullptr, float* dw = nullptr) {
   if (!bwd_pointers_ok(q, k, v, out, dout, lse, theta_row, theta_col, dq, dk, dv, dtheta_row, dtheta_col))
     return FSW_ERR_INVALID_ARG;
-  const BwdPath path = bwd_path(g, dtype);
-  const WsLayout ws = workspace_layout(g, path);
+  const BwdPath path = bwd_path(g, dtype, lr.rank);
+  const WsLayout ws = workspace_layout(g, path, lr.rank);
   if (!workspace || !aligned(workspace, 256) || workspace_bytes < ws.total) return FSW_ERR_WORKSPACE;
   char* base = static_cast<char*>(workspace);
   fsw::BwdArgs a{q,  k,  v,          out,        dout, lse, theta_row, theta_col,
                  dq, dk, dv,         dtheta_row, dtheta_col, g, dtype,
                  reinterpret_cast<float*>(base + ws.delta_off), reinterpret_cast<float*>(base + ws.scal_off),
-                 reinterpret_cast<float*>(base + ws.partials_off), ws.n_partials};
+                 reinterpret_cast<float*>(base + ws.partials_off), ws.n_partials, lr, du, dw,
+                 reinterpret_cast<float*>(base + ws.lr_off)};
   hipStream_t s = reinterpret_cast<hipStream_t>(hip_stream);
   const hipError_t e = path == BwdPath::kMfma32   ? fsw::launch_bwd_mfma(a, s)
                        : path == BwdPath::kMfma64 ? fsw::launch_bwd_d64(a, s)
@@ -306,6 +311,74 @@ int flashswin_wattn_bwd_packed(const void* qkv, const void* out, const void* dou
   char* dx = static_cast<char*>(dqkv);
   return bwd_impl(x, x + slot, x + 2 * slot, out, dout, lse, theta_row, theta_col, dx, dx + slot, dx + 2 * slot,
                   dtheta_row, dtheta_col, workspace, workspace_bytes, g, dtype, hip_stream);
+}
+
+// Low-rank bias factors of a call: rank in [1, kMaxRank], U and W non-null and 4-byte aligned.
+static_assert(fsw::kMaxRank == FLASHSWIN_MAX_RANK, "rank limit of the kernels and of the header");
+static int check_lowrank(const float* u, const float* w, int rank) {
+  if (rank < 1) return FSW_ERR_INVALID_ARG;
+  if (rank > fsw::kMaxRank) return FSW_ERR_UNSUPPORTED;
+  if (!u || !w || !aligned(u, 4) || !aligned(w, 4)) return FSW_ERR_INVALID_ARG;
+  return FSW_OK;
+}
+
+static size_t factor_bytes(const fsw::Geom& g, int rank) { return (size_t)g.heads * g.N * rank * sizeof(float); }
+
+int flashswin_wattn_fwd_lowrank(const void* q, const void* k, const void* v, const float* theta_row,
+                                const float* theta_col, const float* bias_u, const float* bias_w, int rank, void* out,
+                                float* lse, int64_t B, int64_t Hg, int64_t Wg, int heads, int d, int M, int shift,
+                                int dtype, void* hip_stream) {
+  fsw::Geom g;
+  int st = check_shape(B, Hg, Wg, heads, d, M, shift, dtype, &g);
+  if (st != FSW_OK) return st;
+  if ((st = check_lowrank(bias_u, bias_w, rank)) != FSW_OK) return st;
+  if (B == 0) return FSW_OK;
+  const Sizes z = sizes_of(g, dtype);
+  const size_t fb = factor_bytes(g, rank);
+  const Span outs[] = {{out, z.tens}, {lse, z.lse}};
+  const Span ins[] = {{q, z.tens}, {k, z.tens}, {v, z.tens}, {theta_row, z.theta}, {theta_col, z.theta},
+                      {bias_u, fb}, {bias_w, fb}};
+  if (!outputs_disjoint(outs, ins)) return FSW_ERR_INVALID_ARG;
+  fsw::LowRank lr;
+  lr.u = bias_u;
+  lr.w = bias_w;
+  lr.rank = rank;
+  return fwd_impl(q, k, v, theta_row, theta_col, out, lse, g, dtype, hip_stream, lr);
+}
+
+size_t flashswin_wattn_bwd_lowrank_workspace_size(int64_t B, int64_t Hg, int64_t Wg, int heads, int d, int M,
+                                                  int shift, int dtype, int rank) {
+  fsw::Geom g;
+  if (check_shape(B, Hg, Wg, heads, d, M, shift, dtype, &g) != FSW_OK) return 0;
+  if (B == 0 || rank < 1 || rank > fsw::kMaxRank) return 0;
+  return workspace_layout(g, bwd_path(g, dtype, rank), rank).total;
+}
+
+int flashswin_wattn_bwd_lowrank(const void* q, const void* k, const void* v, const void* out, const void* dout,
+                                const float* lse, const float* theta_row, const float* theta_col,
+                                const float* bias_u, const float* bias_w, int rank, void* dq, void* dk, void* dv,
+                                float* dtheta_row, float* dtheta_col, float* dbias_u, float* dbias_w,
+                                void* workspace, size_t workspace_bytes, int64_t B, int64_t Hg, int64_t Wg, int heads,
+                                int d, int M, int shift, int dtype, void* hip_stream) {
+  fsw::Geom g;
+  int st = check_shape(B, Hg, Wg, heads, d, M, shift, dtype, &g);
+  if (st != FSW_OK) return st;
+  if ((st = check_lowrank(bias_u, bias_w, rank)) != FSW_OK) return st;
+  if (B == 0) return FSW_OK;
+  if (!dbias_u || !dbias_w || !aligned(dbias_u, 4) || !aligned(dbias_w, 4)) return FSW_ERR_INVALID_ARG;
+  const Sizes z = sizes_of(g, dtype);
+  const size_t fb = factor_bytes(g, rank);
+  const Span outs[] = {{dq, z.tens},         {dk, z.tens},          {dv, z.tens}, {dtheta_row, z.theta},
+                       {dtheta_col, z.theta}, {dbias_u, fb}, {dbias_w, fb}, {workspace, workspace_bytes}};
+  const Span ins[] = {{q, z.tens},    {k, z.tens},   {v, z.tens},          {out, z.tens},        {dout, z.tens},
+                      {lse, z.lse},   {bias_u, fb},  {bias_w, fb},         {theta_row, z.theta}, {theta_col, z.theta}};
+  if (!outputs_disjoint(outs, ins)) return FSW_ERR_INVALID_ARG;
+  fsw::LowRank lr;
+  lr.u = bias_u;
+  lr.w = bias_w;
+  lr.rank = rank;
+  return bwd_impl(q, k, v, out, dout, lse, theta_row, theta_col, dq, dk, dv, dtheta_row, dtheta_col, workspace,
+                  workspace_bytes, g, dtype, hip_stream, lr, dbias_u, dbias_w);
 }
 
 size_t flashswin_wattn_fwd_materialized_workspace_size(int64_t B, int64_t Hg, int64_t Wg, int heads, int d, int M,

@@ -9,6 +9,17 @@
 
 namespace fsw {
 
+// Largest rank of the low-rank additive bias factors.
+constexpr int kMaxRank = 32;
+
+// Optional rank-r additive bias: per head, factors U, W [heads, M*M, rank] (float32) over in-window
+// positions; the pair (i, j) adds U[n_i] . W[n_j] to its scaled score.  rank == 0: no bias.
+struct LowRank {
+  const float* u = nullptr;
+  const float* w = nullptr;
+  int rank = 0;
+};
+
 struct FwdArgs {
   const void* q;
   const void* k;
@@ -19,6 +30,7 @@ struct FwdArgs {
   float* lse;  // may be null
   Geom g;
   int dtype;  // 0 = float32, 1 = bf16
+  LowRank lr = {};
 };
 
 struct BwdArgs {
@@ -42,9 +54,14 @@ struct BwdArgs {
   float* scal;      // [windows*heads][4]  per window-head: max |dO|, max |v|, max |q|, max |k| components
   float* partials;  // [n_partials][2][d/4]  per-workgroup dtheta partial sums
   int64_t n_partials;
+  LowRank lr = {};
+  float* du = nullptr;      // [heads, M*M, rank]  gradient of the bias factors (rank > 0)
+  float* dw = nullptr;
+  float* lr_parts = nullptr;  // [2][windows][heads][M*M][rank]  per-window factor gradients (rank > 0)
 };
 
-// Scalar (float32-arithmetic) paths: any d in {8,16,32,64}, any window size, either dtype.
+// Scalar (float32-arithmetic) paths: any d in {8,16,32,64}, any window size, either dtype; the only
+// paths that take a low-rank bias.
 hipError_t launch_fwd_scalar(const FwdArgs& a, hipStream_t st);
 hipError_t launch_bwd_scalar(const BwdArgs& a, hipStream_t st);
 // Number of dtheta partial rows the scalar backward writes.

@@ -7,6 +7,9 @@
 // products) and every (M, d) the MFMA path does not cover, and grids padded to a multiple of M
 // (padding tokens are neither queries nor keys).  Keys are staged per tile in LDS after rotation;
 // each thread keeps its query's running max, running sum and output accumulator in registers.
+// With LR it also adds a rank-r bias U[n_i] . W[n_j] to every score (the learned low-rank bias
+// factorization of the FlashBias comparison model on the same paper card, Table S1): the query's U
+// row lives in registers (zero past the rank), the keys' W rows are staged beside K.
 #include "fsw_common.h"
 #include "fsw_launch.h"
 
@@ -15,15 +18,17 @@ namespace fsw {
 constexpr int kScalarThreads = 128;  // queries per workgroup == keys per LDS tile
 constexpr int kChunk = 16;           // scores held in registers between max updates
 
-template <typename IO, int D>
+template <typename IO, int D, bool LR>
 __global__ __launch_bounds__(kScalarThreads) void fwd_scalar_kernel(const IO* __restrict__ q, const IO* __restrict__ k,
                                                                      const IO* __restrict__ v,
                                                                      const float* __restrict__ th_row,
                                                                      const float* __restrict__ th_col,
                                                                      IO* __restrict__ out, float* __restrict__ lse,
-                                                                     Geom g, int nqb) {
+                                                                     Geom g, int nqb, LowRank lr) {
+  constexpr int R = LR ? kMaxRank : 1;
   __shared__ float sK[kScalarThreads][D];
   __shared__ float sV[kScalarThreads][D];
+  __shared__ float sW[LR ? kScalarThreads : 1][R];
   __shared__ int sLab[kScalarThreads];
 
   const int64_t blk = blockIdx.x;
@@ -38,9 +43,18 @@ __global__ __launch_bounds__(kScalarThreads) void fwd_scalar_kernel(const IO* __
   const int64_t xs = g.xs, os = g.os;
 
   float qv[D];
+  float ub[R];  // the query's U row times log2(e) (scores are kept in log2 units)
+#pragma unroll
+  for (int t = 0; t < R; ++t) ub[t] = 0.f;
   int qlab = 0;
   int64_t qtok = 0;
   if (active) {
+    if (LR) {
+      const float* urow = lr.u + ((int64_t)w.h * N + n) * lr.rank;
+#pragma unroll
+      for (int t = 0; t < R; ++t)
+        if (t < lr.rank) ub[t] = urow[t] * kLog2e;
+    }
     const int r = n / g.M, c = n - (n / g.M) * g.M;
     qtok = token_index(g, w.b, w.wy, w.wx, r, c);
     load_row<D>(q + qtok * xs + w.h * D, qv);
@@ -76,6 +90,11 @@ __global__ __launch_bounds__(kScalarThreads) void fwd_scalar_kernel(const IO* __
           sV[tid][i] = vv[i];
         }
         sLab[tid] = token_label(g, w.wy, w.wx, r, c);
+        if (LR) {
+          const float* wrow = lr.w + ((int64_t)w.h * N + j) * lr.rank;
+#pragma unroll
+          for (int t = 0; t < R; ++t) sW[tid][t] = t < lr.rank ? wrow[t] : 0.f;
+        }
       } else {
         // past the end of the window, or padding: never matches a query label; zero rows keep 0 * row
         // finite
@@ -83,6 +102,10 @@ __global__ __launch_bounds__(kScalarThreads) void fwd_scalar_kernel(const IO* __
         for (int i = 0; i < D; ++i) {
           sK[tid][i] = 0.f;
           sV[tid][i] = 0.f;
+        }
+        if (LR) {
+#pragma unroll
+          for (int t = 0; t < R; ++t) sW[tid][t] = 0.f;
         }
         sLab[tid] = -1;
       }
@@ -99,6 +122,10 @@ __global__ __launch_bounds__(kScalarThreads) void fwd_scalar_kernel(const IO* __
         if (j < tn && sLab[j] == qlab) {
 #pragma unroll
           for (int i = 0; i < D; ++i) dot = __builtin_fmaf(qv[i], sK[j][i], dot);
+          if (LR) {
+#pragma unroll
+            for (int t = 0; t < R; ++t) dot = __builtin_fmaf(ub[t], sW[j][t], dot);
+          }
         } else {
           dot = -INFINITY;
         }
@@ -138,8 +165,14 @@ static hipError_t launch_fwd_scalar_t(const FwdArgs& a, hipStream_t st) {
   const int nqb = (a.g.N + kScalarThreads - 1) / kScalarThreads;
   const int64_t nwh = a.g.B * a.g.nH * a.g.nW * a.g.heads;
   const int64_t blocks = nwh * nqb;
-  hipLaunchKernelGGL((fwd_scalar_kernel<IO, D>), dim3((unsigned)blocks), dim3(kScalarThreads), 0, st,
-                     (const IO*)a.q, (const IO*)a.k, (const IO*)a.v, a.th_row, a.th_col, (IO*)a.out, a.lse, a.g, nqb);
+  if (a.lr.rank > 0)
+    hipLaunchKernelGGL((fwd_scalar_kernel<IO, D, true>), dim3((unsigned)blocks), dim3(kScalarThreads), 0, st,
+                       (const IO*)a.q, (const IO*)a.k, (const IO*)a.v, a.th_row, a.th_col, (IO*)a.out, a.lse, a.g, nqb,
+                       a.lr);
+  else
+    hipLaunchKernelGGL((fwd_scalar_kernel<IO, D, false>), dim3((unsigned)blocks), dim3(kScalarThreads), 0, st,
+                       (const IO*)a.q, (const IO*)a.k, (const IO*)a.v, a.th_row, a.th_col, (IO*)a.out, a.lse, a.g, nqb,
+                       a.lr);
   return hipGetLastError();
 }
 

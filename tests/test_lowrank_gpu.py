@@ -48,6 +48,13 @@ CASES = [
     (1, 24, 24, 2, 64, 12, 5, 32, "bf16"),
     (1, 14, 14, 1, 8, 7, 2, 1, "bf16"),
     (1, 50, 38, 1, 32, 16, 8, 16, "bf16"),   # padded grid
+    # bf16, d = 32, windows of up to 512 tokens: the MFMA forward with the bias as extra score channels
+    (2, 16, 16, 2, 32, 8, 3, 32, "bf16"),
+    (1, 24, 24, 2, 32, 12, 5, 20, "bf16"),
+    (1, 32, 32, 3, 32, 16, 0, 1, "bf16"),
+    (1, 40, 40, 2, 32, 20, 7, 16, "bf16"),
+    (1, 44, 44, 1, 32, 22, 0, 32, "bf16"),
+    (1, 10, 10, 2, 32, 5, 2, 9, "bf16"),
 ]
 
 
@@ -115,3 +122,50 @@ def test_lowrank_zero_factors_equal_the_plain_forward():
     o0, l0 = F.wattn_fwd(xd["q"], xd["k"], xd["v"], xd["theta_row"], xd["theta_col"], M, s)
     torch.cuda.synchronize()
     assert torch.allclose(o1, o0, rtol=0, atol=1e-6) and torch.allclose(l1, l0, rtol=0, atol=1e-6)
+
+
+@pytest.mark.parametrize("M,shift,rank", [(16, 8, 16), (12, 5, 32)])
+def test_lowrank_bf16_operand_path(M, shift, rank):
+    """W scaled by 2^12 and U by 2^-12 leaves every bias term unchanged, but |W| leaves fp16 range, so
+    the MFMA forward takes bf16 score operands for every window-head (the backward, on the float32
+    kernels, is unaffected).  O and LSE against the oracle, and dU times 2^-12 and dW times 2^12 (the
+    unscaled magnitudes)."""
+    B, Hg, Wg, H, D = 1, 2 * M, 2 * M, 2, 32
+    x = make_inputs(B, Hg, Wg, H, D, "bf16", seed=980 + M, with_dout=True)
+    U, W = _factors(H, M, rank, seed=985 + M)
+    U, W = U * 2.0 ** -12, W * 2.0 ** 12
+    xd = {n: t.to(DEV) for n, t in x.items()}
+    out, lse = F.wattn_fwd_lowrank(xd["q"], xd["k"], xd["v"], xd["theta_row"], xd["theta_col"], U.to(DEV),
+                                   W.to(DEV), M, shift)
+    grads = F.wattn_bwd_lowrank(xd["q"], xd["k"], xd["v"], out, xd["dout"], lse, xd["theta_row"], xd["theta_col"],
+                                U.to(DEV), W.to(DEV), M, shift)
+    torch.cuda.synchronize()
+    q, k, v, do = (x[n].double().numpy() for n in ("q", "k", "v", "dout"))
+    tr, tc = x["theta_row"].double().numpy(), x["theta_col"].double().numpy()
+    lr = (U.double().numpy(), W.double().numpy())
+    ro, rl = oracle.wattn_fwd_ref(q, k, v, tr, tc, M, shift, lowrank=lr)
+    _close("O", _np(out), ro, 2e-2, 5e-3)
+    _close("LSE", _np(lse), rl, 2e-2, 5e-3)
+    rg = oracle.wattn_bwd_ref(q, k, v, do, tr, tc, M, shift, lowrank=lr)
+    _close("dU (x 2^-12)", _np(grads[5]) * 2.0 ** -12, rg[5] * 2.0 ** -12, 2e-2, 5e-3, scale_abs=True)
+    _close("dW (x 2^12)", _np(grads[6]) * 2.0 ** 12, rg[6] * 2.0 ** 12, 2e-2, 5e-3, scale_abs=True)
+
+
+def test_lowrank_large_bias_falls_back():
+    """A key whose W row has an entry of 200 in a column that every U row leaves at 0 adds nothing to
+    any score but makes max|k'| about 200, so the bound max|q'| max|k'| overshoots every row's maximum
+    by far more than 80 (log2 units): the MFMA forward redoes the rows with the exact maximum."""
+    B, Hg, Wg, H, D, M, s, r = 1, 32, 32, 2, 32, 16, 8, 4
+    x = make_inputs(B, Hg, Wg, H, D, "bf16", seed=990)
+    U, W = _factors(H, M, r, seed=991)
+    U[:, :, 0] = 0.0
+    W[:, 5, 0] = 200.0
+    xd = {n: t.to(DEV) for n, t in x.items()}
+    out, lse = F.wattn_fwd_lowrank(xd["q"], xd["k"], xd["v"], xd["theta_row"], xd["theta_col"], U.to(DEV),
+                                   W.to(DEV), M, s)
+    torch.cuda.synchronize()
+    q, k, v = (x[n].double().numpy() for n in ("q", "k", "v"))
+    tr, tc = x["theta_row"].double().numpy(), x["theta_col"].double().numpy()
+    ro, rl = oracle.wattn_fwd_ref(q, k, v, tr, tc, M, s, lowrank=(U.double().numpy(), W.double().numpy()))
+    _close("O", _np(out), ro, 2e-2, 5e-3)
+    _close("LSE", _np(lse), rl, 2e-2, 5e-3)

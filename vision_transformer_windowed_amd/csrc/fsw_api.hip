@@ -144,7 +144,8 @@ int fwd_impl(const void* q, const void* k, const void* v, const float* theta_row
   if (!aligned(theta_row, 4) || !aligned(theta_col, 4) || (lse && !aligned(lse, 4))) return FSW_ERR_INVALID_ARG;
   fsw::FwdArgs a{q, k, v, theta_row, theta_col, out, lse, g, dtype, lr};
   hipStream_t s = reinterpret_cast<hipStream_t>(hip_stream);
-  const bool mfma = lr.rank == 0 && use_mfma_fwd(g, dtype);
+  const bool mfma = lr.rank == 0 ? use_mfma_fwd(g, dtype)
+                                  : dtype == FSW_BF16 && fsw::fwd_mfma_lowrank_supported(g, lr.rank);
   const hipError_t e = mfma ? fsw::launch_fwd_mfma(a, s) : fsw::launch_fwd_scalar(a, s);
   return e == hipSuccess ? FSW_OK : FSW_ERR_HIP;
 }

@@ -70,6 +70,9 @@ int64_t bwd_scalar_partials(const Geom& g);
 // bf16 MFMA forward: d == 32 with M <= 32, and d == 64 with at most 512 padded window tokens
 // (M <= 22), where the window's K~ and V rows fit LDS.
 bool fwd_mfma_supported(const Geom& g);
+// The MFMA forward with a low-rank bias: bf16, d == 32, at most 512 padded window tokens, rank <= 32,
+// grids that M divides.
+bool fwd_mfma_lowrank_supported(const Geom& g, int rank);
 hipError_t launch_fwd_mfma(const FwdArgs& a, hipStream_t st);
 // M = 8 windows: one wave per window-head.
 bool fwd_m8_supported(const Geom& g);

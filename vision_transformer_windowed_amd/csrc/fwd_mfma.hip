@@ -46,21 +46,25 @@ constexpr float kLowSum = 8.271806125530277e-25f;  // 2^-80
 constexpr int kMaxWaves = 16;
 constexpr int kMaxQBlocks = 2;
 constexpr int kMaxNP64 = 512;  // d = 64: largest padded window whose K~ and V rows fit LDS
+constexpr int kMaxNPLowRank = 512;  // d = 32 with bias channels: largest padded window served
 
 __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 __device__ __forceinline__ uint32_t uniform(uint32_t x) { return (uint32_t)__builtin_amdgcn_readfirstlane((int)x); }
 
-// Row strides (elements) of the staged K~ and V rows for head dim D.  K~ rows carry 16 bytes of pad
-// (conflict-free 16-byte row reads); 64-channel V rows too (128-byte rows would put the four rows of a
-// transposing read in two bank groups), 32-channel V rows need none.
-template <int D>
+// Row strides (elements) of the staged K~ and V rows for head dim D and RK channels of a low-rank
+// bias (the factors' rank rounded up to 16; 0 without one).  K~ rows hold the D rotated channels,
+// then the key's W factor row, then 16 bytes of pad (conflict-free 16-byte row reads); 64-channel V
+// rows are padded too (128-byte rows would put the four rows of a transposing read in two bank
+// groups), 32-channel V rows need none.
+template <int D, int RK = 0>
 struct FwdDim {
-  static constexpr int KS = D + 8;
+  static constexpr int KS = D + RK + 8;
   static constexpr int VS = D == 32 ? 32 : D + 8;
-  static constexpr int P4 = D / 4;      // RoPE pairs per axis
-  static constexpr int PARTS = D / 8;   // 16-byte parts of a token row
-  static constexpr int KSTEPS = D / 16; // k-steps of a score product
-  static constexpr int OT = D / 32;     // O^T tiles of 32 channels
+  static constexpr int P4 = D / 4;             // RoPE pairs per axis
+  static constexpr int PARTS = D / 8;          // 16-byte parts of a token row
+  static constexpr int DSTEPS = D / 16;        // k-steps over the head channels
+  static constexpr int KSTEPS = (D + RK) / 16; // k-steps of a score product (head, then bias channels)
+  static constexpr int OT = D / 32;            // O^T tiles of 32 channels
 };
 static_assert(FwdDim<32>::KS == kKStride, "d = 32 K~ stride");
 
@@ -75,9 +79,9 @@ struct FwdSmem {
   float* red;      // [2 * kMaxWaves]: per-wave max |k~|^2, then max |q^|^2
 };
 
-template <int D>
+template <int D, int RK = 0>
 __host__ __device__ inline size_t fwd_smem_bytes(int NP, int M) {
-  size_t b = (size_t)NP * FwdDim<D>::KS * 2 + (size_t)NP * FwdDim<D>::VS * 2;
+  size_t b = (size_t)NP * FwdDim<D, RK>::KS * 2 + (size_t)NP * FwdDim<D>::VS * 2;
   b += (size_t)2 * 2 * M * FwdDim<D>::P4 * 4;
   b += (size_t)NP * 2 + (size_t)NP;
   b = (b + 3) & ~(size_t)3;
@@ -85,11 +89,11 @@ __host__ __device__ inline size_t fwd_smem_bytes(int NP, int M) {
   return b;
 }
 
-template <int D>
+template <int D, int RK = 0>
 __device__ inline FwdSmem carve(unsigned char* base, int NP, int M) {
   FwdSmem s;
   s.K = reinterpret_cast<uint16_t*>(base);
-  s.V = s.K + (size_t)NP * FwdDim<D>::KS;
+  s.V = s.K + (size_t)NP * FwdDim<D, RK>::KS;
   s.sn = reinterpret_cast<float*>(s.V + (size_t)NP * FwdDim<D>::VS);
   s.cs = s.sn + 2 * M * FwdDim<D>::P4;
   s.rc = reinterpret_cast<uint16_t*>(s.cs + 2 * M * FwdDim<D>::P4);
@@ -147,20 +151,21 @@ __device__ inline bool window_padded(const Geom& g, const WinHead& w, int M) {
 }
 
 // The wave's query operands: k-step t of the score product takes channels 16t + 8h .. 16t + 8h + 7.
-template <int D>
-using QOps = uint4[FwdDim<D>::KSTEPS];
+template <int D, int RK = 0>
+using QOps = uint4[FwdDim<D, RK>::KSTEPS];
 // The wave's O^T accumulators: tile t holds channels 32t .. 32t + 31.
 template <int D>
 using OAcc = f32x16_t[FwdDim<D>::OT];
 
 // Score tile S^T = K~ Q^T + cinit of key block b.
-template <bool H16, int D>
-__device__ __forceinline__ f32x16_t block_scores(const FwdSmem& sm, int b, int row, int h, const QOps<D>& qop,
+template <bool H16, int D, int RK = 0>
+__device__ __forceinline__ f32x16_t block_scores(const FwdSmem& sm, int b, int row, int h, const QOps<D, RK>& qop,
                                                  const f32x16_t& cinit) {
-  const uint16_t* krow = sm.K + (size_t)(b * 32 + row) * FwdDim<D>::KS + 8 * h;
+  const uint16_t* krow = sm.K + (size_t)(b * 32 + row) * FwdDim<D, RK>::KS + 8 * h;
   f32x16_t s = mfma_op<H16>(*reinterpret_cast<const uint4*>(krow), qop[0], cinit);
 #pragma unroll
-  for (int t = 1; t < FwdDim<D>::KSTEPS; ++t) s = mfma_op<H16>(*reinterpret_cast<const uint4*>(krow + 16 * t), qop[t], s);
+  for (int t = 1; t < FwdDim<D, RK>::KSTEPS; ++t)
+    s = mfma_op<H16>(*reinterpret_cast<const uint4*>(krow + 16 * t), qop[t], s);
   return s;
 }
 
@@ -199,25 +204,25 @@ __device__ __forceinline__ void block_consume(const FwdSmem& sm, int b, int lane
 
 // Pipelined pass over an even number of key blocks kb0 .. kb1-1, all whole and of the wave's one
 // label: no masks, no skips, two score buffers.
-template <bool H16, int D>
-__device__ __forceinline__ void pass_uniform(const FwdSmem& sm, int kb0, int kb1, int lane, const QOps<D>& qop,
+template <bool H16, int D, int RK = 0>
+__device__ __forceinline__ void pass_uniform(const FwdSmem& sm, int kb0, int kb1, int lane, const QOps<D, RK>& qop,
                                              const f32x16_t& cinit, float& l, OAcc<D>& o) {
   const int h = lane >> 5, row = lane & 31;
   float la = 0.f, lb = 0.f;
   if constexpr (D == 64) {  // no prefetch: the second score tile does not fit the register budget
     for (int kb = kb0; kb < kb1; ++kb) {
-      const f32x16_t sa = block_scores<H16, D>(sm, kb, row, h, qop, cinit);
+      const f32x16_t sa = block_scores<H16, D, RK>(sm, kb, row, h, qop, cinit);
       block_consume<false, false, D>(sm, kb, lane, 0xffffu, 0.f, sa, la, lb, o);
     }
     l = la + lb;
     return;
   }
   // the prefetch after the last pair recomputes block kb1-1 and is not used
-  f32x16_t sa = block_scores<H16, D>(sm, kb0, row, h, qop, cinit);
+  f32x16_t sa = block_scores<H16, D, RK>(sm, kb0, row, h, qop, cinit);
   for (int kb = kb0; kb < kb1; kb += 2) {
-    const f32x16_t sb = block_scores<H16, D>(sm, kb + 1, row, h, qop, cinit);
+    const f32x16_t sb = block_scores<H16, D, RK>(sm, kb + 1, row, h, qop, cinit);
     block_consume<false, false, D>(sm, kb, lane, 0xffffu, 0.f, sa, la, lb, o);
-    sa = block_scores<H16, D>(sm, min(kb + 2, kb1 - 1), row, h, qop, cinit);
+    sa = block_scores<H16, D, RK>(sm, min(kb + 2, kb1 - 1), row, h, qop, cinit);
     block_consume<false, false, D>(sm, kb + 1, lane, 0xffffu, 0.f, sb, la, lb, o);
   }
   l = la + lb;
@@ -227,9 +232,9 @@ __device__ __forceinline__ void pass_uniform(const FwdSmem& sm, int kb0, int kb1
 //  MODE 0: scores offset by `cinit`; p = exp2(s); accumulate l and O.
 //  MODE 1: exact maximum only: m = max over live keys of the raw score.
 //  MODE 2: p = exp2(s - m) with the exact per-query maximum; accumulate l and O.
-template <int MODE, bool H16, int D>
+template <int MODE, bool H16, int D, int RK = 0>
 __device__ __forceinline__ void pass_general(const FwdSmem& sm, int NB, int lane, uint32_t wave_labels,
-                                             bool wave_single, const QOps<D>& qop, int qlab,
+                                             bool wave_single, const QOps<D, RK>& qop, int qlab,
                                              const f32x16_t& cinit, float& m, float& l, OAcc<D>& o) {
   const int h = lane >> 5, row = lane & 31;
   float la = l, lb = 0.f;
@@ -238,7 +243,7 @@ __device__ __forceinline__ void pass_general(const FwdSmem& sm, int NB, int lane
     const uint32_t bl = info & 0x1ffu;
     if ((bl & wave_labels) == 0) continue;  // no query of this wave may see these keys
     const bool need_mask = !((info >> 9) & 1u) || !wave_single || bl != wave_labels;
-    const f32x16_t s = block_scores<H16, D>(sm, kb, row, h, qop, cinit);
+    const f32x16_t s = block_scores<H16, D, RK>(sm, kb, row, h, qop, cinit);
     const uint32_t live = need_mask ? live_bits(sm.lab, kb, h, qlab) : 0xffffu;
     if (MODE == 1) {
 #pragma unroll
@@ -257,10 +262,10 @@ __device__ __forceinline__ void pass_general(const FwdSmem& sm, int NB, int lane
 // The attention of the wave's tile: the pipelined pass when its live keys are one even run of
 // whole blocks kb0 .. kb1-1 of its own label (run), else the general pass; then the exact-maximum fallback
 // when the bound reference was too loose for some query.
-template <bool H16, int D>
+template <bool H16, int D, int RK = 0>
 __device__ __forceinline__ void attend(const FwdSmem& sm, int NB, int lane, bool run, int kb0, int kb1,
                                        uint32_t wave_labels,
-                                       bool wave_single, const QOps<D>& qop, int qlab, bool qvalid, float bound,
+                                       bool wave_single, const QOps<D, RK>& qop, int qlab, bool qvalid, float bound,
                                        float& ref, float& l, OAcc<D>& o) {
   const float refb = bound * bound_margin<H16>();
   f32x16_t cinit;
@@ -268,9 +273,9 @@ __device__ __forceinline__ void attend(const FwdSmem& sm, int NB, int lane, bool
   for (int v2 = 0; v2 < 16; ++v2) cinit[v2] = -refb;
   float m = 0.f;
   if (run)
-    pass_uniform<H16, D>(sm, kb0, kb1, lane, qop, cinit, l, o);
+    pass_uniform<H16, D, RK>(sm, kb0, kb1, lane, qop, cinit, l, o);
   else if (wave_labels != 0)
-    pass_general<0, H16, D>(sm, NB, lane, wave_labels, wave_single, qop, qlab, cinit, m, l, o);
+    pass_general<0, H16, D, RK>(sm, NB, lane, wave_labels, wave_single, qop, qlab, cinit, m, l, o);
   ref = refb;
   const float lsum = halves_sum(l);
   const bool low = qvalid && !(lsum >= kLowSum && lsum < INFINITY);
@@ -279,7 +284,7 @@ __device__ __forceinline__ void attend(const FwdSmem& sm, int NB, int lane, bool
 #pragma unroll
     for (int v2 = 0; v2 < 16; ++v2) zero[v2] = 0.f;
     m = -INFINITY;
-    pass_general<1, H16, D>(sm, NB, lane, wave_labels, wave_single, qop, qlab, zero, m, l, o);
+    pass_general<1, H16, D, RK>(sm, NB, lane, wave_labels, wave_single, qop, qlab, zero, m, l, o);
     m = halves_max(m);
     if (!(m > -INFINITY)) m = 0.f;  // invalid query lanes
     l = 0.f;
@@ -287,7 +292,7 @@ __device__ __forceinline__ void attend(const FwdSmem& sm, int NB, int lane, bool
     for (int t = 0; t < FwdDim<D>::OT; ++t)
 #pragma unroll
       for (int v2 = 0; v2 < 16; ++v2) o[t][v2] = 0.f;
-    pass_general<2, H16, D>(sm, NB, lane, wave_labels, wave_single, qop, qlab, zero, m, l, o);
+    pass_general<2, H16, D, RK>(sm, NB, lane, wave_labels, wave_single, qop, qlab, zero, m, l, o);
     ref = m;
   }
 }
@@ -295,7 +300,7 @@ __device__ __forceinline__ void attend(const FwdSmem& sm, int NB, int lane, bool
 // Rotated K~ rows of the staged items (raw bf16 loads in kraw) into LDS in fp16 (h16) or bf16;
 // returns this thread's max |k|^2 (rotation keeps norms).  Item it is 16-byte part it % PARTS of
 // key it / PARTS; the PARTS parts of a key are consecutive lanes.
-template <int MAXIT, int D>
+template <int MAXIT, int D, int RK = 0>
 __device__ __forceinline__ float stage_k(const FwdSmem& sm, const uint4 (&kraw)[MAXIT], int M, bool split, int NP,
                                          int tid, int nt, bool h16) {
   constexpr int PARTS = FwdDim<D>::PARTS, AXP = PARTS / 2;
@@ -319,13 +324,61 @@ __device__ __forceinline__ float stage_k(const FwdSmem& sm, const uint4 (&kraw)[
       rotate8(x, sm.sn, sm.cs, axis, M, axis ? c : r, (part % AXP) * 4, FwdDim<D>::P4);
       kr = pack8_op(x, h16);
     }
-    *reinterpret_cast<uint4*>(sm.K + (size_t)key * FwdDim<D>::KS + part * 8) = kr;
+    *reinterpret_cast<uint4*>(sm.K + (size_t)key * FwdDim<D, RK>::KS + part * 8) = kr;
     ss = quad_sum(ss);  // the parts of the key
     if (PARTS == 8)  // the other quad of the 8 lanes (row_half_mirror: lane i <- lane 7 - i)
       ss += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(ss), 0x141, 0xf, 0xf, false));
     kmax2 = fmaxf(kmax2, ss);
   }
   return kmax2;
+}
+
+// The W factor rows of the staged keys into channels D .. D + RK of their K~ rows (zero past the rank
+// and past the window), in fp16 (h16) or bf16; returns this thread's largest |W[n]|^2 (the key norms
+// that bound the scores add it to the largest |k~|^2).  Item it: 8-channel part it % (RK/8) of slot
+// it / (RK/8); the slot's in-window position n = r*M + c indexes the factor.
+template <int D, int RK>
+__device__ inline float stage_w(const FwdSmem& sm, const LowRank& lr, int head, int M, bool split, int NP, int tid,
+                                int nt, bool h16) {
+  constexpr int WP = RK / 8;
+  const int N = M * M;
+  float wmax2 = 0.f;
+  for (int it = tid; it < NP * WP; it += nt) {
+    const int key = it / WP, part = it % WP;
+    float x[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = 0.f;
+    if (key < N) {
+      const int rc = split ? (int)sm.rc[key] : (key / M) << 8 | (key - (key / M) * M);
+      const float* wrow = lr.w + ((int64_t)head * N + (rc >> 8) * M + (rc & 255)) * lr.rank;
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (part * 8 + e < lr.rank) x[e] = wrow[part * 8 + e];
+    }
+    float ss = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ss += x[e] * x[e];
+    // the WP parts of a slot are consecutive lanes (NP * WP is a multiple of 64: uniform trip count)
+#pragma unroll
+    for (int o = 1; o < WP; o <<= 1) ss += __shfl_xor(ss, o, 64);
+    wmax2 = fmaxf(wmax2, ss);
+    *reinterpret_cast<uint4*>(sm.K + (size_t)key * FwdDim<D, RK>::KS + D + part * 8) = pack8_op(x, h16);
+  }
+  return wmax2;
+}
+
+// The lane's bias channels of query slot rc (r << 8 | c): log2(e) U[n] for channels 16t + 8h + e,
+// t < RK / 16, e < 8 (zero past the rank), into u[8t + e].
+template <int RK>
+__device__ __forceinline__ void load_u(const LowRank& lr, int head, int N, int rc, int M, int h, float (&u)[RK / 2]) {
+  const float* urow = lr.u + ((int64_t)head * N + (rc >> 8) * M + (rc & 255)) * lr.rank;
+#pragma unroll
+  for (int t = 0; t < RK / 16; ++t)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int ch = 16 * t + 8 * h + e;
+      u[8 * t + e] = ch < lr.rank ? urow[ch] * kLog2e : 0.f;
+    }
 }
 
 // Global loads of the thread's K and V items (16 bytes each), issued together.
@@ -370,17 +423,19 @@ constexpr int fwd_min_waves() {
 // once and then walks its query blocks of NWAVES*32 queries.  MT: compile-time window size
 // (0 = g.M at run time).  NPMAX: the largest padded window this configuration serves.  D: head dim.
 // PAD: the grid is padded to a multiple of M (the padding checks cost a few percent, so grids that M
-// divides run an instance without them).
-template <int NWAVES, int MT, int NPMAX, int D, bool PAD>
+// divides run an instance without them).  RK: channels of a low-rank bias U[n_i] . W[n_j] (the rank
+// rounded up to 16, 0 for none), folded into the score product as extra channels: the query operand
+// carries log2(e) U[n_i] after its rotated, scaled channels, the staged key row W[n_j] after K~.
+template <int NWAVES, int MT, int NPMAX, int D, bool PAD, int RK = 0>
 __global__ __launch_bounds__(NWAVES * 64, (fwd_min_waves<NWAVES, D>())) void fwd_mfma_kernel(const uint16_t* __restrict__ q,
                                                                const uint16_t* __restrict__ k,
                                                                const uint16_t* __restrict__ v,
                                                                const float* __restrict__ th_row,
                                                                const float* __restrict__ th_col,
                                                                uint16_t* __restrict__ out, float* __restrict__ lse,
-                                                               Geom g, int nqb, int NP, int nsplit) {
+                                                               Geom g, int nqb, int NP, int nsplit, LowRank lr) {
   extern __shared__ __align__(16) unsigned char smem_raw[];
-  using Dim = FwdDim<D>;
+  using Dim = FwdDim<D, RK>;
   constexpr int NT = NWAVES * 64;
   constexpr int MAXIT = (NPMAX * Dim::PARTS + NT - 1) / NT;
   constexpr int QBM = (NPMAX + NWAVES * 32 - 1) / (NWAVES * 32);  // query blocks per window, at most
@@ -389,7 +444,7 @@ __global__ __launch_bounds__(NWAVES * 64, (fwd_min_waves<NWAVES, D>())) void fwd
   const int M = MT > 0 ? MT : g.M;
   const int N = M * M;
   const int NB = NP / 32;
-  const FwdSmem sm = carve<D>(smem_raw, NP, M);
+  const FwdSmem sm = carve<D, RK>(smem_raw, NP, M);
 
   // Work of this workgroup: window-head wh, query blocks qoff .. qoff + nqw - 1.  The first nsplit
   // window-heads are split into one workgroup per query block, dispatched first (the first
@@ -438,20 +493,20 @@ __global__ __launch_bounds__(NWAVES * 64, (fwd_min_waves<NWAVES, D>())) void fwd
   uint4 kraw[MAXIT], vraw[MAXIT];
   load_kv<MAXIT, D>(k, v, g, w, split ? sm.rc : nullptr, M, NP, tid, NT, true, pad, kraw, vraw);
   // the lane's query of block qb (16-byte pieces: channels 16t + 8h .. 16t + 8h + 7)
-  auto load_q = [&](int qb, QOps<D>& a) {
+  auto load_q = [&](int qb, uint4 (&a)[Dim::DSTEPS]) {
     const int qi = (qoff + qb) * NT / 2 + wave * 32 + col;
 #pragma unroll
-    for (int t = 0; t < Dim::KSTEPS; ++t) a[t] = make_uint4(0, 0, 0, 0);
+    for (int t = 0; t < Dim::DSTEPS; ++t) a[t] = make_uint4(0, 0, 0, 0);
     if (qb < nqw && qi < N) {
       const int rc = split ? (int)sm.rc[qi] : (qi / M) << 8 | (qi - (qi / M) * M);
       if (!pad || tok_real(g, w, M, rc >> 8, rc & 255)) {  // padding stays zero
         const int64_t off = tok_of(g, w, M, rc >> 8, rc & 255) * g.xs + w.h * D;
 #pragma unroll
-        for (int t = 0; t < Dim::KSTEPS; ++t) a[t] = *reinterpret_cast<const uint4*>(q + off + 16 * t + 8 * h);
+        for (int t = 0; t < Dim::DSTEPS; ++t) a[t] = *reinterpret_cast<const uint4*>(q + off + 16 * t + 8 * h);
       }
     }
   };
-  uint4 qraw[QBM][Dim::KSTEPS];
+  uint4 qraw[QBM][Dim::DSTEPS];
 #pragma unroll
   for (int qb = 0; qb < QBM; ++qb) load_q(qb, qraw[qb]);
 
@@ -470,7 +525,8 @@ __global__ __launch_bounds__(NWAVES * 64, (fwd_min_waves<NWAVES, D>())) void fwd
   __syncthreads();
 
   // 3. K~ rows (rotated, fp16), V rows, block label summaries, norms
-  float kmax2 = stage_k<MAXIT, D>(sm, kraw, M, split, NP, tid, NT, true);
+  float kmax2 = stage_k<MAXIT, D, RK>(sm, kraw, M, split, NP, tid, NT, true);
+  if constexpr (RK > 0) kmax2 += stage_w<D, RK>(sm, lr, w.h, M, split, NP, tid, NT, true);
 #pragma unroll
   for (int i = 0; i < MAXIT; ++i) {
     const int it = tid + i * NT;
@@ -495,8 +551,20 @@ __global__ __launch_bounds__(NWAVES * 64, (fwd_min_waves<NWAVES, D>())) void fwd
   for (int qb = 0; qb < QBM; ++qb) {
     float qn2 = 0.f;
 #pragma unroll
-    for (int t = 0; t < Dim::KSTEPS; ++t) qn2 = norm2_bf16x8(qraw[qb][t], qn2);
-    qn2max[qb] = wave_max(halves_sum(qn2)) * (qscale * qscale);
+    for (int t = 0; t < Dim::DSTEPS; ++t) qn2 = norm2_bf16x8(qraw[qb][t], qn2);
+    if constexpr (RK > 0) {  // plus |log2(e) U[n_q]|^2 of the bias channels
+      qn2 *= qscale * qscale;
+      const int qi = (qoff + qb) * NT / 2 + wave * 32 + col;
+      if (qb < nqw && qi < N) {
+        float u[RK / 2];
+        load_u<RK>(lr, w.h, N, split ? (int)sm.rc[qi] : (qi / M) << 8 | (qi - (qi / M) * M), M, h, u);
+#pragma unroll
+        for (int e = 0; e < RK / 2; ++e) qn2 += u[e] * u[e];
+      }
+      qn2max[qb] = wave_max(halves_sum(qn2));
+    } else {
+      qn2max[qb] = wave_max(halves_sum(qn2)) * (qscale * qscale);
+    }
   }
   kmax2 = wave_max(kmax2);
   if (lane == 0) {
@@ -519,7 +587,8 @@ __global__ __launch_bounds__(NWAVES * 64, (fwd_min_waves<NWAVES, D>())) void fwd
   if (!h16) {
     load_kv<MAXIT, D>(k, v, g, w, split ? sm.rc : nullptr, M, NP, tid, NT, false, pad, kraw, vraw);
     __syncthreads();
-    stage_k<MAXIT, D>(sm, kraw, M, split, NP, tid, NT, false);
+    stage_k<MAXIT, D, RK>(sm, kraw, M, split, NP, tid, NT, false);
+    if constexpr (RK > 0) stage_w<D, RK>(sm, lr, w.h, M, split, NP, tid, NT, false);
     __syncthreads();
   }
 #pragma unroll
@@ -530,12 +599,12 @@ __global__ __launch_bounds__(NWAVES * 64, (fwd_min_waves<NWAVES, D>())) void fwd
     const bool qvalid = qi < N && (!pad || sm.lab[qi] != 0xff);
     const int qrc = !qvalid ? 0 : split ? (int)sm.rc[qi] : (qi / M) << 8 | (qi - (qi / M) * M);
     const int qr = qrc >> 8, qc = qrc & 255;
-    QOps<D> qop;
+    QOps<D, RK> qop;
     // block 0's query was loaded with K and V; later blocks reload theirs (an L2 hit) during the
     // previous block's epilogue: keeping every block's raw query live across attend() costs registers.
     // Piece t holds channels 16t + 8h ..: axis (16t) / (d/2), pairs from ((16t) % (d/2) + 8h) / 2.
 #pragma unroll
-    for (int t = 0; t < Dim::KSTEPS; ++t) {
+    for (int t = 0; t < Dim::DSTEPS; ++t) {
       constexpr int HALF = D / 2;
       const int axis = (16 * t) / HALF;
       float x[8];
@@ -544,6 +613,19 @@ __global__ __launch_bounds__(NWAVES * 64, (fwd_min_waves<NWAVES, D>())) void fwd
 #pragma unroll
       for (int e = 0; e < 8; ++e) x[e] *= qscale;
       qop[t] = pack8_op(x, h16);
+    }
+    if constexpr (RK > 0) {  // the bias channels: log2(e) U[n_q], lane h holding 8h.. of each 16
+      float u[RK / 2];
+#pragma unroll
+      for (int e = 0; e < RK / 2; ++e) u[e] = 0.f;
+      if (qvalid) load_u<RK>(lr, w.h, N, qrc, M, h, u);
+#pragma unroll
+      for (int t = 0; t < RK / 16; ++t) {
+        float x[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = u[8 * t + e];
+        qop[Dim::DSTEPS + t] = pack8_op(x, h16);
+      }
     }
     const float bound = sqrtf(qn2max[qb]) * kmax;  // >= every score of this wave (log2 units)
     const int qlab = qvalid ? token_label(g, w.wy, w.wx, qr, qc) : 0xff;
@@ -569,9 +651,9 @@ __global__ __launch_bounds__(NWAVES * 64, (fwd_min_waves<NWAVES, D>())) void fwd
 #pragma unroll
       for (int v2 = 0; v2 < 16; ++v2) o[t][v2] = 0.f;
     if (h16)
-      attend<true, D>(sm, NB, lane, run, kb0, kb1, wave_labels, wave_single, qop, qlab, qvalid, bound, ref, l, o);
+      attend<true, D, RK>(sm, NB, lane, run, kb0, kb1, wave_labels, wave_single, qop, qlab, qvalid, bound, ref, l, o);
     else
-      attend<false, D>(sm, NB, lane, run, kb0, kb1, wave_labels, wave_single, qop, qlab, qvalid, bound, ref, l, o);
+      attend<false, D, RK>(sm, NB, lane, run, kb0, kb1, wave_labels, wave_single, qop, qlab, qvalid, bound, ref, l, o);
 
     // the next block's query loads go out before this block's epilogue
     if (qb + 1 < QBM) load_q(qb + 1, qraw[qb + 1]);  // zeros past the last block
@@ -596,18 +678,18 @@ __global__ __launch_bounds__(NWAVES * 64, (fwd_min_waves<NWAVES, D>())) void fwd
   }
 }
 
-template <int NWAVES, int MT, int NPMAX, int D, bool PAD = false>
+template <int NWAVES, int MT, int NPMAX, int D, bool PAD = false, int RK = 0>
 hipError_t launch_nw(const FwdArgs& a, hipStream_t st) {
   const Geom& g = a.g;
   const int NP = (g.N + 31) / 32 * 32;
   const int nqb = (g.N + NWAVES * 32 - 1) / (NWAVES * 32);
-  const size_t smem = fwd_smem_bytes<D>(NP, g.M);
+  const size_t smem = fwd_smem_bytes<D, RK>(NP, g.M);
   // The dynamic-LDS limit is raised on the current device, once per device (beyond kMaxDevices:
   // on every call).
   constexpr int kMaxDevices = 64;
   static std::once_flag once[kMaxDevices];
   const auto raise = [] {
-    (void)hipFuncSetAttribute((const void*)fwd_mfma_kernel<NWAVES, MT, NPMAX, D, PAD>,
+    (void)hipFuncSetAttribute((const void*)fwd_mfma_kernel<NWAVES, MT, NPMAX, D, PAD, RK>,
                               hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
   };
   int dev = 0;
@@ -620,9 +702,9 @@ hipError_t launch_nw(const FwdArgs& a, hipStream_t st) {
   // two query blocks and enough work for several rounds of workgroups per CU
   const int nsplit = (nqb == 2 && nwh >= 64 * 8) ? 64 : 0;
   const int64_t blocks = nwh + nsplit;
-  hipLaunchKernelGGL((fwd_mfma_kernel<NWAVES, MT, NPMAX, D, PAD>), dim3((unsigned)blocks), dim3(NWAVES * 64), smem, st,
+  hipLaunchKernelGGL((fwd_mfma_kernel<NWAVES, MT, NPMAX, D, PAD, RK>), dim3((unsigned)blocks), dim3(NWAVES * 64), smem, st,
                      (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, a.th_row, a.th_col,
-                     (uint16_t*)a.out, a.lse, g, nqb, NP, nsplit);
+                     (uint16_t*)a.out, a.lse, g, nqb, NP, nsplit, a.lr);
   return hipGetLastError();
 }
 
@@ -633,8 +715,29 @@ bool fwd_mfma_supported(const Geom& g) {
   return (g.d == 32 && g.M <= 32) || (g.d == 64 && NP <= kMaxNP64);
 }
 
+bool fwd_mfma_lowrank_supported(const Geom& g, int rank) {
+  const int NP = (g.N + 31) / 32 * 32;
+  return g.d == 32 && NP <= kMaxNPLowRank && rank >= 1 && rank <= 32 && g.Hp == g.Hg && g.Wp == g.Wg;
+}
+
+namespace {
+// d = 32 with RK bias channels, run-time M (windows of up to kMaxNPLowRank padded tokens).
+template <int RK>
+hipError_t launch_lowrank(const FwdArgs& a, hipStream_t st) {
+  const int N = a.g.N;
+  if (N <= 64) return launch_nw<2, 0, 64, 32, false, RK>(a, st);
+  if (N <= 128) return launch_nw<4, 0, 128, 32, false, RK>(a, st);
+  if (N <= 256) return launch_nw<8, 0, 256, 32, false, RK>(a, st);
+  return launch_nw<8, 0, kMaxNPLowRank, 32, false, RK>(a, st);
+}
+}  // namespace
+
 hipError_t launch_fwd_mfma(const FwdArgs& a, hipStream_t st) {
   const int N = a.g.N;
+  if (a.lr.rank > 0) {
+    if (!fwd_mfma_lowrank_supported(a.g, a.lr.rank)) return hipErrorInvalidValue;
+    return a.lr.rank <= 16 ? launch_lowrank<16>(a, st) : launch_lowrank<32>(a, st);
+  }
   if (!fwd_mfma_supported(a.g)) return hipErrorInvalidValue;
   if (a.g.Hp != a.g.Hg || a.g.Wp != a.g.Wg) {  // padded grid: the run-time-M instances with padding checks
     if (a.g.d == 64) {

@@ -73,8 +73,7 @@ typedef enum { FSW_F32 = 0, FSW_BF16 = 1 } fsw_dtype;
  *   its feature map before the shift (the pages do not say): the shift, the windows and the Swin
  *   regions are those of the padded grid, and the added tokens are absent, no key of any query and
  *   no output.  (A caller that wants Swin's zero-valued padding tokens as keys pads q, k, v itself.)
- *   The forward of a padded grid runs on the kernels its d and M select; its backward runs on the
- *   float32-arithmetic kernels.
+ *   Padded grids run on the kernels their d and M select.
  *   bf16 with d == 32 and M <= 32, and bf16 with d == 64 and M*M <= 512 (M <= 22), run on the MFMA
  *   kernels; every other case runs on kernels with float32 arithmetic that stream the keys through
  *   LDS (correct for every supported shape, not tuned).  Needs no workspace.  On the MFMA kernels

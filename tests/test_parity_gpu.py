@@ -438,6 +438,10 @@ BWD_SMALL = [
     (1, 50, 75, 2, 32, 8, 4, "bf16"),
     (1, 50, 38, 1, 32, 16, 8, "bf16"),
     (1, 40, 29, 1, 64, 12, 6, "bf16"),
+    (1, 70, 100, 1, 32, 32, 16, "bf16"),
+    (1, 45, 20, 2, 32, 20, 7, "bf16"),
+    (1, 30, 47, 1, 64, 16, 8, "bf16"),
+    (2, 9, 7, 1, 32, 4, 3, "bf16"),
 ]
 
 

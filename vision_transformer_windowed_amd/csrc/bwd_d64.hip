@@ -187,7 +187,7 @@ __global__ __launch_bounds__(256) void bwd_pre64_kernel(const uint16_t* __restri
   float mx[4] = {0.f, 0.f, 0.f, 0.f};
   for (int n0 = 0; n0 < g.N; n0 += 32) {  // uniform trip count: every lane reaches the shuffles
     const int n = n0 + (tid >> 3);
-    const bool ok = n < g.N;
+    const bool ok = n < g.N && token_real(g, w.wy, w.wx, n / g.M, n % g.M);
     float s = 0.f;
     int64_t tok = 0;
     if (ok) {
@@ -242,7 +242,7 @@ __host__ __device__ inline size_t kv_smem_bytes(int NP, int M, int NW) {
   return (size_t)NP * kRS * 2 * 3 + (size_t)NP * 4 * 2 + (size_t)2 * 2 * M * 16 * 4 + (size_t)NW * 32 * 4 + NP;
 }
 
-template <int NW, bool H16>
+template <int NW, bool H16, bool PAD>
 __device__ inline void dkdv64_body(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                                    const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout,
                                    const float* __restrict__ lse, const float* __restrict__ delta,
@@ -266,7 +266,7 @@ __device__ inline void dkdv64_body(const uint16_t* __restrict__ q, const uint16_
     uint4 qo = make_uint4(0, 0, 0, 0), go = qo, gs = qo;
     float lv = 0.f, dl = 0.f;
     uint8_t lb = 0xff;
-    if (n < N) {
+    if (n < N && (!PAD || token_real(g, w.wy, w.wx, n / M, n % M))) {  // padding stays zero, label 0xff
       const int r = n / M, c = n - (n / M) * M;
       const int64_t tok = token_index(g, w.b, w.wy, w.wx, r, c);
       const uint4 qr = *reinterpret_cast<const uint4*>(q + tok * g.xs + w.h * D6 + 8 * part);
@@ -291,7 +291,7 @@ __device__ inline void dkdv64_body(const uint16_t* __restrict__ q, const uint16_
 
   // 2. the lane's key: K~ operands (k-step t: channels 16t + 8h ..), tau V as bf16 B operands
   const int kj = wave * 32 + col;
-  const bool kvalid = kj < N;
+  const bool kvalid = kj < N && (!PAD || token_real(g, w.wy, w.wx, kj / M, kj % M));  // a padding key is no key
   const int kr = kvalid ? kj / M : 0, kc = kvalid ? kj - (kj / M) * M : 0;
   int64_t koff = 0;
   uint4 kb[4], vb[4];
@@ -397,7 +397,7 @@ __device__ inline void dkdv64_body(const uint16_t* __restrict__ q, const uint16_
   reduce_dtheta64<NW>(th, sm.red, partials + (((int64_t)w.h * 2 + 0) * nwin + wh / g.heads) * 32, lane, wave, tid);
 }
 
-template <int NW>
+template <int NW, bool PAD>
 __global__ __launch_bounds__(NW * 64, 1) void bwd_dkdv64_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ delta,
@@ -416,14 +416,16 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dkdv64_kernel(
   sm.lab = reinterpret_cast<uint8_t*>(sm.red + NW * 32);
   const int64_t wh = xcd_order(blockIdx.x, gridDim.x);
   const WinHead w = decode_winhead(g, wh);
-  // several Swin regions only in the last window row and column of a shifted grid
-  const bool masked = (g.shift > 0 && (w.wy == g.nH - 1 || w.wx == g.nW - 1)) || NP != g.N;
+  // several Swin regions (or padding) only in the last window row and column of a shifted (or
+  // padded) grid
+  const bool edge = w.wy == g.nH - 1 || w.wx == g.nW - 1;
+  const bool masked = ((g.shift > 0 || g.Hp != g.Hg || g.Wp != g.Wg) && edge) || NP != g.N;
   fill_table64(sm.sn, sm.cs, th_row, th_col, w.h, g.M, threadIdx.x, NW * 64);
   __syncthreads();
   if (h16_window(scal, wh))
-    dkdv64_body<NW, true>(q, k, v, dout, lse, delta, scal, dk, dv, partials, g, NP, sm, w, wh, masked);
+    dkdv64_body<NW, true, PAD>(q, k, v, dout, lse, delta, scal, dk, dv, partials, g, NP, sm, w, wh, masked);
   else
-    dkdv64_body<NW, false>(q, k, v, dout, lse, delta, scal, dk, dv, partials, g, NP, sm, w, wh, masked);
+    dkdv64_body<NW, false, PAD>(q, k, v, dout, lse, delta, scal, dk, dv, partials, g, NP, sm, w, wh, masked);
 }
 
 // ---------------------------------------------------------------------------------------- dQ
@@ -440,7 +442,7 @@ __host__ __device__ inline size_t q_smem_bytes(int NP, int M, int NW) {
   return (size_t)NP * kRS * 2 * 2 + (size_t)2 * 2 * M * 16 * 4 + (size_t)NW * 32 * 4 + NP;
 }
 
-template <int NW, bool H16>
+template <int NW, bool H16, bool PAD>
 __device__ inline void dq64_body(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                                  const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout,
                                  const float* __restrict__ lse, const float* __restrict__ delta,
@@ -462,7 +464,7 @@ __device__ inline void dq64_body(const uint16_t* __restrict__ q, const uint16_t*
     const int n = it >> 3, part = it & 7;
     uint4 ko = make_uint4(0, 0, 0, 0), vo = ko;
     uint8_t lb = 0xff;
-    if (n < N) {
+    if (n < N && (!PAD || token_real(g, w.wy, w.wx, n / M, n % M))) {  // padding stays zero, label 0xff
       const int r = n / M, c = n - (n / M) * M;
       const int64_t off = token_index(g, w.b, w.wy, w.wx, r, c) * g.xs + w.h * D6 + 8 * part;
       ko = rot_part64<H16>(*reinterpret_cast<const uint4*>(k + off), sm.sn, sm.cs, M, r, c, part, 1.f);
@@ -476,7 +478,7 @@ __device__ inline void dq64_body(const uint16_t* __restrict__ q, const uint16_t*
 
   // 2. the lane's query: Q^ operands, tau dO as bf16 B operands, -LSE and -tau Delta
   const int qi = wave * 32 + col;
-  const bool qvalid = qi < N;
+  const bool qvalid = qi < N && (!PAD || token_real(g, w.wy, w.wx, qi / M, qi % M));  // a padding query is no query
   const int qr = qvalid ? qi / M : 0, qc = qvalid ? qi - (qi / M) * M : 0;
   int64_t qoff = 0;
   uint4 qb[4], gb[4];
@@ -550,7 +552,7 @@ __device__ inline void dq64_body(const uint16_t* __restrict__ q, const uint16_t*
   reduce_dtheta64<NW>(th, sm.red, partials + (((int64_t)w.h * 2 + 1) * nwin + wh / g.heads) * 32, lane, wave, tid);
 }
 
-template <int NW>
+template <int NW, bool PAD>
 __global__ __launch_bounds__(NW * 64, 1) void bwd_dq64_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ delta,
@@ -566,13 +568,14 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq64_kernel(
   sm.lab = reinterpret_cast<uint8_t*>(sm.red + NW * 32);
   const int64_t wh = xcd_order(blockIdx.x, gridDim.x);
   const WinHead w = decode_winhead(g, wh);
-  const bool masked = (g.shift > 0 && (w.wy == g.nH - 1 || w.wx == g.nW - 1)) || NP != g.N;
+  const bool edge = w.wy == g.nH - 1 || w.wx == g.nW - 1;
+  const bool masked = ((g.shift > 0 || g.Hp != g.Hg || g.Wp != g.Wg) && edge) || NP != g.N;
   fill_table64(sm.sn, sm.cs, th_row, th_col, w.h, g.M, threadIdx.x, NW * 64);
   __syncthreads();
   if (h16_window(scal, wh))
-    dq64_body<NW, true>(q, k, v, dout, lse, delta, scal, dq, partials, g, NP, sm, w, wh, masked);
+    dq64_body<NW, true, PAD>(q, k, v, dout, lse, delta, scal, dq, partials, g, NP, sm, w, wh, masked);
   else
-    dq64_body<NW, false>(q, k, v, dout, lse, delta, scal, dq, partials, g, NP, sm, w, wh, masked);
+    dq64_body<NW, false, PAD>(q, k, v, dout, lse, delta, scal, dq, partials, g, NP, sm, w, wh, masked);
 }
 
 // The dynamic-LDS limit of a kernel is raised on the current device, once per device (beyond
@@ -589,21 +592,21 @@ void raise_lds_limit(F* kernel, std::once_flag (&once)[64]) {
     raise();
 }
 
-template <int NW>
+template <int NW, bool PAD>
 hipError_t launch_d64(const BwdArgs& a, hipStream_t st) {
   const Geom& g = a.g;
   const int NP = (g.N + 31) / 32 * 32;
   if (NP > NW * 32) return hipErrorInvalidConfiguration;
   static std::once_flag once_kv[64], once_q[64];
-  raise_lds_limit(bwd_dkdv64_kernel<NW>, once_kv);
-  raise_lds_limit(bwd_dq64_kernel<NW>, once_q);
+  raise_lds_limit(bwd_dkdv64_kernel<NW, PAD>, once_kv);
+  raise_lds_limit(bwd_dq64_kernel<NW, PAD>, once_q);
   const int64_t nwh = g.B * g.nH * g.nW * g.heads;
-  hipLaunchKernelGGL((bwd_dkdv64_kernel<NW>), dim3((unsigned)nwh), dim3(NW * 64), kv_smem_bytes(NP, g.M, NW), st,
+  hipLaunchKernelGGL((bwd_dkdv64_kernel<NW, PAD>), dim3((unsigned)nwh), dim3(NW * 64), kv_smem_bytes(NP, g.M, NW), st,
                      (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (const uint16_t*)a.dout, a.lse,
                      a.delta, a.scal, a.th_row, a.th_col, (uint16_t*)a.dk, (uint16_t*)a.dv, a.partials, g, NP);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((bwd_dq64_kernel<NW>), dim3((unsigned)nwh), dim3(NW * 64), q_smem_bytes(NP, g.M, NW), st,
+  hipLaunchKernelGGL((bwd_dq64_kernel<NW, PAD>), dim3((unsigned)nwh), dim3(NW * 64), q_smem_bytes(NP, g.M, NW), st,
                      (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (const uint16_t*)a.dout, a.lse,
                      a.delta, a.scal, a.th_row, a.th_col, (uint16_t*)a.dq, a.partials, g, NP);
   e = hipGetLastError();
@@ -613,9 +616,7 @@ hipError_t launch_d64(const BwdArgs& a, hipStream_t st) {
 
 }  // namespace
 
-bool bwd_d64_supported(const Geom& g) {
-  return g.d == 64 && g.N <= kMaxN6 && g.Hp == g.Hg && g.Wp == g.Wg;
-}
+bool bwd_d64_supported(const Geom& g) { return g.d == 64 && g.N <= kMaxN6; }
 
 int64_t bwd_d64_partials(const Geom& g) { return (int64_t)g.heads * 2 * g.B * g.nH * g.nW; }
 
@@ -628,9 +629,14 @@ hipError_t launch_bwd_d64(const BwdArgs& a, hipStream_t st) {
                      a.scal, g);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (g.N <= 64) return launch_d64<2>(a, st);
-  if (g.N <= 128) return launch_d64<4>(a, st);
-  return launch_d64<8>(a, st);
+  if (g.Hp != g.Hg || g.Wp != g.Wg) {  // padded grid: the instances with padding checks
+    if (g.N <= 64) return launch_d64<2, true>(a, st);
+    if (g.N <= 128) return launch_d64<4, true>(a, st);
+    return launch_d64<8, true>(a, st);
+  }
+  if (g.N <= 64) return launch_d64<2, false>(a, st);
+  if (g.N <= 128) return launch_d64<4, false>(a, st);
+  return launch_d64<8, false>(a, st);
 }
 
 }  // namespace fsw

@@ -193,11 +193,15 @@ __global__ __launch_bounds__(kPreThreads) void bwd_pre_kernel(const uint16_t* __
 #pragma unroll
     for (int u = 0; u < kPreBatch; ++u) {
       const int n = (st * kPreBatch + u) * T + t0;
-      ok[u] = act && n < g.N;
-      // an item past the end reads the window's first token again: the maxima are unchanged by a
-      // repeated value and its Delta is not stored
-      const int y = grid_coord(wy * g.M + (ok[u] ? r : 0), g.shift, g.Hg);
-      const int x = grid_coord(wx * g.M + (ok[u] ? c : 0), g.shift, g.Wg);
+      const bool in = act && n < g.N;
+      // Positions wrap at the padded extents.  An item past the end reads the window's first slot
+      // again, and a padding position (or a padding first slot) reads the image's last row or column
+      // instead: the maxima can only grow, which keeps every operand in range, and no Delta is stored
+      // for either.
+      const int yp = grid_coord(wy * g.M + (in ? r : 0), g.shift, g.Hp);
+      const int xp = grid_coord(wx * g.M + (in ? c : 0), g.shift, g.Wp);
+      ok[u] = in && yp < g.Hg && xp < g.Wg;
+      const int y = min(yp, g.Hg - 1), x = min(xp, g.Wg - 1);
       tok[u] = (img + (Off)y) * (Off)g.Wg + (Off)x;
       const Off oo = tok[u] * os2 + ch2, xo = tok[u] * xs2 + ch2;
       ro[u] = load_stream(po + oo);
@@ -275,7 +279,7 @@ __host__ __device__ inline size_t dq_smem(int NP, int M, int cmax) {
 // Each wave owns S sets of 32 queries (lane = query within a set).  The sets share every LDS
 // operand read (K~ and V rows, the transposed K~^T), so staging and LDS traffic per tile shrink
 // with S, and the S independent tiles give the scheduler work to interleave.
-template <int NW, int MT, int S, bool H16>
+template <int NW, int MT, int S, bool H16, bool PAD>
 __device__ inline void dq_body(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                                const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout,
                                const float* __restrict__ lse, const float* __restrict__ delta,
@@ -289,6 +293,8 @@ __device__ inline void dq_body(const uint16_t* __restrict__ q, const uint16_t* _
   const int M = MT > 0 ? MT : g.M;
   const int N = M * M;
   const WinOrder wo = win_order(g, M, w.wy, w.wx);
+  // padding tokens of a padded grid are neither loaded nor stored (PAD instances only)
+  const bool gpad = PAD && (g.Hp != g.Hg || g.Wp != g.Wg);
   const int CH = chunk_len(NP, KC);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int h = lane >> 5, col = lane & 31;
@@ -306,9 +312,11 @@ __device__ inline void dq_body(const uint16_t* __restrict__ q, const uint16_t* _
       if (it < CH * 4 && kn < N) {
         int r_, c_;
         slot_rc(wo, kn, r_, c_);
-        const int64_t off = token_index(g, w.b, w.wy, w.wx, r_, c_) * xs + w.h * D + (it & 3) * 8;
-        ik[i] = *reinterpret_cast<const uint4*>(k + off);
-        iv[i] = *reinterpret_cast<const uint4*>(v + off);
+        if (!gpad || token_real(g, w.wy, w.wx, r_, c_)) {  // padding stays zero
+          const int64_t off = token_index(g, w.b, w.wy, w.wx, r_, c_) * xs + w.h * D + (it & 3) * 8;
+          ik[i] = *reinterpret_cast<const uint4*>(k + off);
+          iv[i] = *reinterpret_cast<const uint4*>(v + off);
+        }
       }
     }
   };
@@ -334,9 +342,12 @@ __device__ inline void dq_body(const uint16_t* __restrict__ q, const uint16_t* _
 #pragma unroll
   for (int t = 0; t < S; ++t) {
     const int qi = qbase + 32 * t;
-    const bool valid = qi < N;
+    bool valid = qi < N;
     int r = 0, c = 0;
-    if (valid) slot_rc(wo, qi, r, c);
+    if (valid) {
+      slot_rc(wo, qi, r, c);
+      valid = !gpad || token_real(g, w.wy, w.wx, r, c);  // a padding query is no query
+    }
     qlab[t] = valid ? token_label(g, w.wy, w.wx, r, c) : 0xff;
     wl |= valid ? (1u << qlab[t]) : 0u;
     qb0[t] = qb1[t] = gb0[t] = gb1[t] = make_uint4(0, 0, 0, 0);
@@ -385,7 +396,7 @@ __device__ inline void dq_body(const uint16_t* __restrict__ q, const uint16_t* _
         }
         *reinterpret_cast<uint4*>(sm.K + srow(n, part)) = kr;
         *reinterpret_cast<uint4*>(sm.V + srow(n, part)) = iv[i];
-        if (part == 0) sm.lab[n] = chunk_label(g, w, wo, kn, sm.blk + buf * (KC / 32), n);
+        if (part == 0) sm.lab[n] = chunk_label<PAD>(g, w, wo, kn, sm.blk + buf * (KC / 32), n);
       }
     }
     if (tid < KC / 32) sm.blk[(buf ^ 1) * (KC / 32) + tid] = 0;
@@ -458,9 +469,9 @@ __device__ inline void dq_body(const uint16_t* __restrict__ q, const uint16_t* _
 #pragma unroll
   for (int t = 0; t < S; ++t) {
     const int qi = qbase + 32 * t;
-    if (qi < N) {
-      int r, c;
-      slot_rc(wo, qi, r, c);
+    int r = 0, c = 0;
+    if (qi < N) slot_rc(wo, qi, r, c);
+    if (qi < N && (!gpad || token_real(g, w.wy, w.wx, r, c))) {
       const int64_t off = token_index(g, w.b, w.wy, w.wx, r, c) * xs + w.h * D;
       // dq~ = acc / tau / sqrt(d); the dtheta integrand takes q~ as the dK product saw it
       unrotate_store(acc[t], 0.17677669529663687f / ds_scale, kQScale, H16, q + off, dq + off, sm.sn, sm.cs, M, r, c,
@@ -471,7 +482,7 @@ __device__ inline void dq_body(const uint16_t* __restrict__ q, const uint16_t* _
   reduce_dtheta<NW>(th, sm.red, partials + prow * 16, lane, wave, tid);
 }
 
-template <int NW, int MT, int S>
+template <int NW, int MT, int S, bool PAD>
 __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_mfma_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ delta,
@@ -497,9 +508,9 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_mfma_kernel(
   fill_table(sm.sn, sm.cs, th_row, th_col, w.h, M, threadIdx.x, NW * 64);
   __syncthreads();
   if (window_h16(scal, wh))
-    dq_body<NW, MT, S, true>(q, k, v, dout, lse, delta, scal, dq, partials, g, nb, NP, sm, w, wh, (int)(lb % nb));
+    dq_body<NW, MT, S, true, PAD>(q, k, v, dout, lse, delta, scal, dq, partials, g, nb, NP, sm, w, wh, (int)(lb % nb));
   else
-    dq_body<NW, MT, S, false>(q, k, v, dout, lse, delta, scal, dq, partials, g, nb, NP, sm, w, wh, (int)(lb % nb));
+    dq_body<NW, MT, S, false, PAD>(q, k, v, dout, lse, delta, scal, dq, partials, g, nb, NP, sm, w, wh, (int)(lb % nb));
 }
 
 // -------------------------------------------------------------------------------------- dK / dV
@@ -524,7 +535,7 @@ __host__ __device__ inline size_t dkdv_smem(int NP, int M, int cmax) {
 
 // Each wave owns S sets of 32 keys (lane = key within a set); the sets share the LDS reads of the
 // query-side operands (Q^ and dO rows, -LSE and -tau Delta, the transposed Q^T and (g dO)^T).
-template <int NW, int MT, int S, bool H16>
+template <int NW, int MT, int S, bool H16, bool PAD>
 __device__ inline void dkdv_body(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                                  const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout,
                                  const float* __restrict__ lse, const float* __restrict__ delta,
@@ -538,6 +549,8 @@ __device__ inline void dkdv_body(const uint16_t* __restrict__ q, const uint16_t*
   const int M = MT > 0 ? MT : g.M;
   const int N = M * M;
   const WinOrder wo = win_order(g, M, w.wy, w.wx);
+  // padding tokens of a padded grid are neither loaded nor stored (PAD instances only)
+  const bool gpad = PAD && (g.Hp != g.Hg || g.Wp != g.Wg);
   const int CH = chunk_len(NP, KC);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int h = lane >> 5, col = lane & 31;
@@ -559,13 +572,15 @@ __device__ inline void dkdv_body(const uint16_t* __restrict__ q, const uint16_t*
       if (it < CH * 4 && qn < N) {
         int r_, c_;
         slot_rc(wo, qn, r_, c_);
-        const int64_t t_ = token_index(g, w.b, w.wy, w.wx, r_, c_);
-        const int64_t off = t_ * xs + w.h * D + (it & 3) * 8;
-        iq[i] = *reinterpret_cast<const uint4*>(q + off);
-        ig[i] = *reinterpret_cast<const uint4*>(dout + t_ * g.os + w.h * D + (it & 3) * 8);
-        if ((it & 3) == 0) {
-          il[i] = lse[t_ * g.heads + w.h];
-          id[i] = delta[t_ * g.heads + w.h];
+        if (!gpad || token_real(g, w.wy, w.wx, r_, c_)) {  // padding stays zero
+          const int64_t t_ = token_index(g, w.b, w.wy, w.wx, r_, c_);
+          const int64_t off = t_ * xs + w.h * D + (it & 3) * 8;
+          iq[i] = *reinterpret_cast<const uint4*>(q + off);
+          ig[i] = *reinterpret_cast<const uint4*>(dout + t_ * g.os + w.h * D + (it & 3) * 8);
+          if ((it & 3) == 0) {
+            il[i] = lse[t_ * g.heads + w.h];
+            id[i] = delta[t_ * g.heads + w.h];
+          }
         }
       }
     }
@@ -592,9 +607,12 @@ __device__ inline void dkdv_body(const uint16_t* __restrict__ q, const uint16_t*
 #pragma unroll
   for (int t = 0; t < S; ++t) {
     const int kj = kbase + 32 * t;
-    const bool valid = kj < N;
+    bool valid = kj < N;
     int r = 0, c = 0;
-    if (valid) slot_rc(wo, kj, r, c);
+    if (valid) {
+      slot_rc(wo, kj, r, c);
+      valid = !gpad || token_real(g, w.wy, w.wx, r, c);  // a padding key is no key
+    }
     klab[t] = valid ? token_label(g, w.wy, w.wx, r, c) : 0xff;
     wl |= valid ? (1u << klab[t]) : 0u;
     kb0[t] = kb1[t] = vb0[t] = vb1[t] = make_uint4(0, 0, 0, 0);
@@ -639,7 +657,7 @@ __device__ inline void dkdv_body(const uint16_t* __restrict__ q, const uint16_t*
         if (part == 0) {
           sm.L[n] = -il[i] * kLog2e;
           sm.Dl[n] = -id[i] * ds_scale;
-          sm.lab[n] = chunk_label(g, w, wo, qn, sm.blk + buf * (KC / 32), n);
+          sm.lab[n] = chunk_label<PAD>(g, w, wo, qn, sm.blk + buf * (KC / 32), n);
         }
       }
     }
@@ -746,9 +764,9 @@ __device__ inline void dkdv_body(const uint16_t* __restrict__ q, const uint16_t*
 #pragma unroll
   for (int t = 0; t < S; ++t) {
     const int kj = kbase + 32 * t;
-    if (kj < N) {
-      int r, c;
-      slot_rc(wo, kj, r, c);
+    int r = 0, c = 0;
+    if (kj < N) slot_rc(wo, kj, r, c);
+    if (kj < N && (!gpad || token_real(g, w.wy, w.wx, r, c))) {
       const int64_t off = token_index(g, w.b, w.wy, w.wx, r, c) * xs + w.h * D;
       // dV = accv / g: lane holds channels 8g + 4h + j of its key
 #pragma unroll
@@ -766,7 +784,7 @@ __device__ inline void dkdv_body(const uint16_t* __restrict__ q, const uint16_t*
   reduce_dtheta<NW>(th, sm.red, partials + prow * 16, lane, wave, tid);
 }
 
-template <int NW, int MT, int S>
+template <int NW, int MT, int S, bool PAD>
 __global__ __launch_bounds__(NW * 64, 2) void bwd_dkdv_mfma_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ delta,
@@ -795,10 +813,10 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dkdv_mfma_kernel(
   fill_table(sm.sn, sm.cs, th_row, th_col, w.h, M, threadIdx.x, NW * 64);
   __syncthreads();
   if (window_h16(scal, wh))
-    dkdv_body<NW, MT, S, true>(q, k, v, dout, lse, delta, scal, dk, dv, partials, g, nb, NP, sm, w, wh,
+    dkdv_body<NW, MT, S, true, PAD>(q, k, v, dout, lse, delta, scal, dk, dv, partials, g, nb, NP, sm, w, wh,
                                (int)(lb % nb));
   else
-    dkdv_body<NW, MT, S, false>(q, k, v, dout, lse, delta, scal, dk, dv, partials, g, nb, NP, sm, w, wh,
+    dkdv_body<NW, MT, S, false, PAD>(q, k, v, dout, lse, delta, scal, dk, dv, partials, g, nb, NP, sm, w, wh,
                                 (int)(lb % nb));
 }
 
@@ -824,7 +842,7 @@ int64_t blocks_per_windowhead(const Geom& g) {
   return (g.N + m.waves * m.sets * 32 - 1) / (m.waves * m.sets * 32);
 }
 
-template <int NW, int MT, int S>
+template <int NW, int MT, int S, bool PAD = false>
 hipError_t launch_main(const BwdArgs& a, hipStream_t st) {
   const Geom& g = a.g;
   const int64_t nwh = g.B * g.nH * g.nW * g.heads;
@@ -833,13 +851,13 @@ hipError_t launch_main(const BwdArgs& a, hipStream_t st) {
   if (m.waves != NW || m.sets != S) return hipErrorInvalidConfiguration;
   const int nb = (int)blocks_per_windowhead(g);
   const int64_t blocks = nwh * nb;
-  hipLaunchKernelGGL((bwd_dkdv_mfma_kernel<NW, MT, S>), dim3((unsigned)blocks), dim3(NW * 64),
+  hipLaunchKernelGGL((bwd_dkdv_mfma_kernel<NW, MT, S, PAD>), dim3((unsigned)blocks), dim3(NW * 64),
                      dkdv_smem<NW>(NP, g.M, chunk_max(MT)), st, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
                      (const uint16_t*)a.dout, a.lse, a.delta, a.scal, a.th_row, a.th_col, (uint16_t*)a.dk,
                      (uint16_t*)a.dv, a.partials, g, nb, NP);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((bwd_dq_mfma_kernel<NW, MT, S>), dim3((unsigned)blocks), dim3(NW * 64), dq_smem<NW>(NP, g.M, chunk_max(MT)),
+  hipLaunchKernelGGL((bwd_dq_mfma_kernel<NW, MT, S, PAD>), dim3((unsigned)blocks), dim3(NW * 64), dq_smem<NW>(NP, g.M, chunk_max(MT)),
                      st, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (const uint16_t*)a.dout,
                      a.lse, a.delta, a.scal, a.th_row, a.th_col, (uint16_t*)a.dq, a.partials, g, nb, NP);
   e = hipGetLastError();
@@ -869,10 +887,15 @@ hipError_t launch_bwd_mfma(const BwdArgs& a, hipStream_t st) {
                        (const uint16_t*)a.k, a.delta, a.scal, g);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  const MainShape m = bwd_shape(g);
+  if (g.Hp != g.Hg || g.Wp != g.Wg) {  // padded grid: the run-time-M instances with padding checks
+    if (m.waves == 8) return launch_main<8, 0, 2, true>(a, st);
+    if (m.waves == 4) return m.sets == 2 ? launch_main<4, 0, 2, true>(a, st) : launch_main<4, 0, 1, true>(a, st);
+    return launch_main<2, 0, 1, true>(a, st);
+  }
   if (g.M == 32) return launch_main<8, 32, 2>(a, st);
   if (g.M == 8) return launch_main<2, 8, 1>(a, st);
   if (g.M == 16) return launch_main<4, 16, 2>(a, st);
-  const MainShape m = bwd_shape(g);
   if (m.waves == 8) return launch_main<8, 0, 2>(a, st);
   if (m.waves == 4) return m.sets == 2 ? launch_main<4, 0, 2>(a, st) : launch_main<4, 0, 1>(a, st);
   return launch_main<2, 0, 1>(a, st);

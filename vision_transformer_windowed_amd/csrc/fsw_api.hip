@@ -2,10 +2,10 @@
 //
 // Every check runs on the host before any HIP call, so an invalid call never touches the device.
 // Dispatch: bf16 with d == 32 and M <= 32 goes to the MFMA kernels, forward and backward; bf16 with
-// d == 64 too, for windows up to 22 x 22 in the forward and 16 x 16 in the backward.  Everything else
-// (float32 tensors, other d, larger windows, the backward of grids that M does not divide) goes to
-// the float32-arithmetic kernels, which stream the keys through LDS in tiles, take any window size
-// up to kMaxWindow and skip the padding tokens of a padded grid.
+// d == 64 too, for windows up to 22 x 22 in the forward and 16 x 16 in the backward; grids that M does
+// not divide included.  Everything else (float32 tensors, other d, larger windows, the backward of a
+// low-rank bias) goes to the float32-arithmetic kernels, which stream the keys through LDS in tiles
+// and take any window size up to kMaxWindow.
 #include <algorithm>
 #include <mutex>
 
@@ -124,13 +124,13 @@ WsLayout workspace_layout(const fsw::Geom& g, BwdPath path, int rank = 0) {
   return w;
 }
 
-// The backward of a padded grid runs on the float32-arithmetic kernels (the MFMA forward skips
-// padding tokens too).
+// Padded grids: padding tokens are skipped by every kernel family except the materialized comparison
+// and the M = 8 forward variant.
 bool padded(const fsw::Geom& g) { return g.Hp != g.Hg || g.Wp != g.Wg; }
 bool use_mfma_fwd(const fsw::Geom& g, int dtype) { return dtype == FSW_BF16 && fsw::fwd_mfma_supported(g); }
 // A low-rank bias runs on the float32-arithmetic kernels.
 BwdPath bwd_path(const fsw::Geom& g, int dtype, int rank = 0) {
-  if (dtype != FSW_BF16 || padded(g) || rank > 0) return BwdPath::kScalar;
+  if (dtype != FSW_BF16 || rank > 0) return BwdPath::kScalar;
   if (fsw::kHaveMfmaBwd && g.d == 32 && g.M <= kMaxM) return BwdPath::kMfma32;
   if (fsw::bwd_d64_supported(g)) return BwdPath::kMfma64;
   return BwdPath::kScalar;

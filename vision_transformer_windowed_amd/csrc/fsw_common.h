@@ -15,8 +15,8 @@ namespace fsw {
 // Shape of one call, passed to kernels by value.  A grid whose sides M does not divide is taken as
 // padded to Hp x Wp (the next multiples of M), as Swin pads its feature map before the shift: the
 // roll, the windows and the regions are those of Hp x Wp, and the added tokens (row >= Hg or column
-// >= Wg) are absent, no key of any query and no output.  The float32-arithmetic kernels and the MFMA
-// forward (not its M = 8 variant) take padded grids; elsewhere Hp == Hg and Wp == Wg.
+// >= Wg) are absent, no key of any query and no output.  Every kernel family but the M = 8 forward
+// variant and the materialized comparison takes padded grids; elsewhere Hp == Hg and Wp == Wg.
 struct Geom {
   int64_t B;
   int Hg, Wg, heads, d, M, shift;

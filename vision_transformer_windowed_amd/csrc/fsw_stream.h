@@ -79,8 +79,11 @@ __device__ inline uint32_t range_labels(const Geom& g, const WinHead& w, const W
   return m;
 }
 
-// Label of chunk slot tn, staged at chunk position n (0xff past the window), and its block summary
-// bit (bit L for label L, bit 10 for a position past the window) OR-ed into blk[n / 32].
+// Label of chunk slot tn, staged at chunk position n (0xff past the window and for the padding of a
+// padded grid), and its block summary bit (bit L for label L, bit 10 for a position past the window or
+// padding) OR-ed into blk[n / 32].
+// PAD: the grid may be padded (instances for padded grids only).
+template <bool PAD>
 __device__ __forceinline__ uint8_t chunk_label(const Geom& g, const WinHead& w, const WinOrder& wo, int tn,
                                                uint32_t* blk, int n) {
   const int N = wo.M * wo.M;
@@ -88,7 +91,7 @@ __device__ __forceinline__ uint8_t chunk_label(const Geom& g, const WinHead& w, 
   if (tn < N) {
     int r, c;
     slot_rc(wo, tn, r, c);
-    lb = (uint8_t)token_label(g, w.wy, w.wx, r, c);
+    if (!PAD || token_real(g, w.wy, w.wx, r, c)) lb = (uint8_t)token_label(g, w.wy, w.wx, r, c);
   }
   atomicOr(&blk[n >> 5], lb == 0xff ? (1u << 10) : (1u << lb));
   return lb;

@@ -36,7 +36,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
 # the forward kernel instance each window size launches (M = 8: one wave per window-head)
-FWD_KERNEL = {32: "fwd_mfma_kernel<16, 32, 1024, 32, false>", 16: "fwd_mfma_kernel<8, 16, 256, 32, false>", 8: "fwd_m8_kernel"}
+FWD_KERNEL = {32: "fwd_mfma_kernel<16, 32, 1024, 32, false, 0>", 16: "fwd_mfma_kernel<8, 16, 256, 32, false, 0>", 8: "fwd_m8_kernel"}
 # kernels each C-ABI call launches, in order
 CALL_LAUNCHES = {"wattn_fwd": ["fwd_mfma_kernel"],
                  "wattn_bwd": ["bwd_pre_kernel", "bwd_dkdv_mfma_kernel", "bwd_dq_mfma_kernel", "dtheta_reduce_kernel"]}
@@ -231,16 +231,17 @@ def materialized_vs_fused(dev, steps, warmup):
                                                                              lse=lse, workspace=ws))):
             if tag == "materialized_ms":  # the fused call is timed before the score workspace exists
                 ws = torch.empty(nbytes, device=dev, dtype=torch.uint8)
-            for _ in range(warmup):
+            n_steps, n_warm = (steps, warmup) if tag == "materialized_ms" else (4 * steps, 4 * warmup + 2)
+            for _ in range(n_warm):
                 fn()
             torch.cuda.synchronize()
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record(stream)
-            for _ in range(steps):
+            for _ in range(n_steps):
                 fn()
             e1.record(stream)
             torch.cuda.synchronize()
-            row[tag] = round(e0.elapsed_time(e1) / steps, 4)
+            row[tag] = round(e0.elapsed_time(e1) / n_steps, 4)
         row["materialized_over_fused"] = round(row["materialized_ms"] / row["fused_ms"], 3)
         res.append(row)
         del ws

@@ -472,6 +472,52 @@ def test_backward_small(case):
     _bwd_check(x, M, s, dt)
 
 
+# (B, Hg, Wg, heads, d, M, shift, offset): bf16 padded grids on the MFMA backward (d = 64 whole-window
+# kernels, d = 32 chunked kernels) whose padding, rolled by the shift, reaches the second-to-last
+# window row and column (shift + padding > M)
+FAR_NEGATIVE_CASES = [(1, 40, 29, 1, 64, 12, 6, 4.5), (1, 50, 38, 1, 32, 16, 8, 5.0),
+                      (1, 26, 37, 2, 64, 16, 12, 4.5)]
+
+
+@pytest.mark.parametrize("case", FAR_NEGATIVE_CASES, ids=lambda c: "{}x{}_d{}_M{}_s{}".format(*c[1:3], *c[4:7]))
+def test_backward_padded_far_negative_scores(case):
+    """Q near -a and K near +a in every channel with theta = 0 put every score of a real pair near
+    -a^2 sqrt(d) (all far below -89), so exp(-LSE) overflows float32; V = 0.  Then O = 0, dP = dO V^T = 0 and
+    Delta = 0, so dS = P (dP - Delta) = 0 for every real pair: dQ, dK and dtheta are exactly zero, and
+    dV = P^T dO carries the probabilities.  A padding key (a zero vector, score 0) must get P = 0
+    exactly rather than exp(0 - LSE) = inf, which would make its dS = inf * 0 = NaN and dQ = dS K
+    NaN.  Padding sits in interior windows as well as in the last window row and column.  LSE is
+    compared within the large-logit rounding bound of the module docstring (fp16 operands: every
+    component is far inside fp16 range)."""
+    B, Hg, Wg, H, D, M, s, a = case
+    Hp, Wp = -(-Hg // M) * M, -(-Wg // M) * M
+    assert s + Hp - Hg > M and s + Wp - Wg > M and a * a * D ** 0.5 > 128
+    x = make_inputs(B, Hg, Wg, H, D, "bf16", seed=_seed(case) + 2, with_dout=True)
+    x["q"] = (x["q"].float() - a).to(torch.bfloat16)
+    x["k"] = (x["k"].float() + a).to(torch.bfloat16)
+    x["v"].zero_()
+    x["theta_row"].zero_()
+    x["theta_col"].zero_()
+    xd = to_dev(x)
+    out, lse = F.wattn_fwd(xd["q"], xd["k"], xd["v"], xd["theta_row"], xd["theta_col"], M, s)
+    dq, dk, dv, dtr, dtc = F.wattn_bwd(xd["q"], xd["k"], xd["v"], out, xd["dout"], lse, xd["theta_row"],
+                                       xd["theta_col"], M, s)
+    torch.cuda.synchronize()
+    (q, k, v), tr, tc = oracle_args(x)
+    ro, rl = oracle.wattn_fwd_ref(q, k, v, tr, tc, M, s)
+    g = oracle.wattn_bwd_ref(q, k, v, x["dout"].double().numpy(), tr, tc, M, s)
+    assert rl.max() < -89.0  # exp(-LSE) is beyond float32 for every query
+    assert not out.any()
+    assert_close_rowwise("LSE", _np(lse), rl, lse_rounding_bound(q, k, M, s, U_FP16), 5e-3)
+    for name, got in (("dQ", dq), ("dK", dk), ("dtheta_row", dtr), ("dtheta_col", dtc)):
+        print(f"  {name}: {int((got != 0).sum())} nonzero, {int((~torch.isfinite(got)).sum())} non-finite",
+              flush=True)
+        assert not got.any(), name
+    # dV = P^T dO sums up to a window of dO rows (entries reach 20 and more) and P carries the
+    # large-logit LSE rounding, so its max-abs bound is relative to max|dV|
+    assert_close("dV", _np(dv), g[2], 2e-2, 5e-3, scale_abs=True)
+
+
 def oracle_bwd_over_batch(x, M, s, got, chunk=4):
     """Run the oracle's backward over the whole batch in chunks of `chunk` images (windows never cross
     images, so each chunk is exact for its images) and compare dq, dk, dv of every image with `got`

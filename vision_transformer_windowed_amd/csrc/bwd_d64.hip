@@ -416,10 +416,11 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dkdv64_kernel(
   sm.lab = reinterpret_cast<uint8_t*>(sm.red + NW * 32);
   const int64_t wh = xcd_order(blockIdx.x, gridDim.x);
   const WinHead w = decode_winhead(g, wh);
-  // several Swin regions (or padding) only in the last window row and column of a shifted (or
-  // padded) grid
+  // Several Swin regions only in the last window row and column of a shifted grid.  Padding can sit
+  // in the last two window rows or columns of a shifted padded grid: every window of a padded grid is
+  // masked (a padding key must get P = 0 exactly, not exp2(0 - LSE)).
   const bool edge = w.wy == g.nH - 1 || w.wx == g.nW - 1;
-  const bool masked = ((g.shift > 0 || g.Hp != g.Hg || g.Wp != g.Wg) && edge) || NP != g.N;
+  const bool masked = (g.shift > 0 && edge) || PAD || NP != g.N;
   fill_table64(sm.sn, sm.cs, th_row, th_col, w.h, g.M, threadIdx.x, NW * 64);
   __syncthreads();
   if (h16_window(scal, wh))
@@ -569,7 +570,7 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq64_kernel(
   const int64_t wh = xcd_order(blockIdx.x, gridDim.x);
   const WinHead w = decode_winhead(g, wh);
   const bool edge = w.wy == g.nH - 1 || w.wx == g.nW - 1;
-  const bool masked = ((g.shift > 0 || g.Hp != g.Hg || g.Wp != g.Wg) && edge) || NP != g.N;
+  const bool masked = (g.shift > 0 && edge) || PAD || NP != g.N;  // as in the dK/dV kernel
   fill_table64(sm.sn, sm.cs, th_row, th_col, w.h, g.M, threadIdx.x, NW * 64);
   __syncthreads();
   if (h16_window(scal, wh))

@@ -13,8 +13,10 @@ from vision_transformer_windowed_amd.inputs import make_inputs
 DEV = "cuda:0"
 
 # (B, Hg, Wg, heads, d, M, shift, dtype): the bf16 M = 32 MFMA kernels, then a smaller input on the
-# M = 8 MFMA kernels, then float32 (the float32-arithmetic kernels)
-CALLS = [(4, 64, 64, 3, 32, 32, 16, "bf16"), (1, 32, 32, 2, 32, 8, 3, "bf16"), (1, 16, 16, 2, 32, 8, 4, "f32")]
+# M = 8 MFMA kernels, then float32 (the float32-arithmetic kernels), the d = 64 MFMA kernels, and a
+# padded grid (the MFMA instances with padding checks)
+CALLS = [(4, 64, 64, 3, 32, 32, 16, "bf16"), (1, 32, 32, 2, 32, 8, 3, "bf16"), (1, 16, 16, 2, 32, 8, 4, "f32"),
+         (2, 32, 32, 2, 64, 16, 8, "bf16"), (1, 50, 38, 2, 32, 16, 8, "bf16")]
 
 
 def _args(x, out, lse, grads):

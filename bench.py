@@ -207,6 +207,53 @@ def config_timing(dev, name, shift, passes, steps, warmup):
     return res
 
 
+def lowrank_step(dev, steps, warmup, rank=16):
+    """Forward and backward with a rank-16 additive bias (factors U, W [heads, M*M, 16], N(0, 0.5^2)) on
+    the M = 16 stage-1 workload at s = 0, beside the same calls without the bias.  FLOP conventions: the
+    bias adds r channels to the score contraction, so the forward is 4 N^2 d + 2 N^2 r and the backward
+    10 N^2 d + 6 N^2 r (S recomputed with the r channels, dU = dS W and dW = dS^T U)."""
+    import torch
+    import vision_transformer_windowed_amd as F
+    from vision_transformer_windowed_amd.inputs import WORKLOADS, workload_inputs
+    name = "flashswin_t_s1_p2_m16"
+    w = WORKLOADS[name]
+    M, d = w["M"], w["d"]
+    x = {k: v.to(dev) for k, v in workload_inputs(name, with_dout=True).items()}
+    q, k, v, tr, tc, dout = x["q"], x["k"], x["v"], x["theta_row"], x["theta_col"], x["dout"]
+    g = torch.Generator().manual_seed(2024)
+    U = (torch.randn((w["heads"], M * M, rank), generator=g) * 0.5).to(dev)
+    W = (torch.randn((w["heads"], M * M, rank), generator=g) * 0.5).to(dev)
+    out = torch.empty_like(q)
+    lse = torch.empty(q.shape[:4], device=dev, dtype=torch.float32)
+    ws = torch.empty(max(F.flashswin_wattn_bwd_lowrank_workspace_size(*q.shape, M, 0, F.FSW_BF16, rank), 1),
+                     device=dev, dtype=torch.uint8)
+    fns = {"fwd": lambda: F.wattn_fwd_lowrank(q, k, v, tr, tc, U, W, M, 0, out=out, lse=lse),
+           "bwd": lambda: F.wattn_bwd_lowrank(q, k, v, out, dout, lse, tr, tc, U, W, M, 0, workspace=ws)}
+    fns["fwd"]()
+    stream = torch.cuda.current_stream(dev)
+    N = M * M
+    nwh = w["B"] * (w["Hg"] // M) * (w["Wg"] // M) * w["heads"]
+    flops = {"fwd": (4.0 * N * N * d + 2.0 * N * N * rank) * nwh, "bwd": (10.0 * N * N * d + 6.0 * N * N * rank) * nwh}
+    res = {"workload": name, "shift": 0, "rank": rank}
+    for tag in ("fwd", "bwd"):
+        fn = fns[tag]
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(steps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / steps
+        tf = flops[tag] / (ms * 1e-3) / 1e12
+        res[tag + "_ms"] = round(ms, 4)
+        res[tag + "_tflops"] = round(tf, 2)
+        res[tag + "_mfma_frac"] = round(tf / BF16_MFMA_PEAK_TFLOPS, 4)
+    return res
+
+
 def materialized_vs_fused(dev, steps, warmup):
     """The forward computed the standard Swin way, with every window's score matrix in HBM (the
     materialized comparison path), against the fused forward, at M = 8, 16 and 32 on the stage-1 grids:
@@ -407,7 +454,7 @@ def main():
                         "launches": CALL_LAUNCHES["wattn_bwd"], "launch_ms": round(bwd_ms, 4),
                         "flops_per_call": bwd_flops, "kernel_source_sha": sha}
     roofline = fwd_roofline if fwd_roofline is not None else bwd_roofline
-    m8 = packed = m16 = masked = bwd32 = mat = d64 = None
+    m8 = packed = m16 = masked = bwd32 = mat = d64 = lowrank = None
     if not args.no_secondary and args.only == "step":
         m8 = m8_forward_roofline(dev, max(args.steps, 10), max(args.warmup, 2))
         packed = packed_forward(dev, max(args.steps, 10), max(args.warmup, 2))
@@ -419,6 +466,7 @@ def main():
         d64 = [config_timing(dev, "wide_heads_s1_p2_m16_d64", s, ("fwd", "bwd"), max(args.steps, 10),
                              max(args.warmup, 2)) for s in WORKLOADS["wide_heads_s1_p2_m16_d64"]["shifts"]]
         mat = materialized_vs_fused(dev, 5, 1)
+        lowrank = lowrank_step(dev, max(args.steps // 4, 3), 1)
 
     gpu_out = {"out": out, "lse": lse, "dq": grads[0], "dk": grads[1], "dv": grads[2]}
     cpu, parity = (None, None)
@@ -459,6 +507,7 @@ def main():
         "m32_bwd_b32": bwd32,
         "materialized_vs_fused": mat,
         "d64_m16_step": d64,
+        "lowrank_r16_m16_step": lowrank,
         "cpu_baseline": cpu,
         "parity_sample": parity,
         "input_gen_s": round(gen_s, 1),

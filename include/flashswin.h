@@ -179,8 +179,9 @@ int flashswin_wattn_bwd_packed(const void* qkv, const void* out, const void* dou
  *   rank         1 <= rank <= FLASHSWIN_MAX_RANK (rank < 1: FSW_ERR_INVALID_ARG; larger:
  *                FSW_ERR_UNSUPPORTED).
  *   Every other argument as in flashswin_wattn_fwd; out and lse may not share a byte with the
- *   factors.  LSE includes the bias.  Runs on the float32-arithmetic kernels (any supported d, M,
- *   dtype, padded grids included).
+ *   factors.  LSE includes the bias.  bf16 with d = 32, windows of at most 512 tokens and grids that
+ *   M divides runs on the MFMA forward with the bias as extra score channels; every other supported
+ *   d, M, dtype and padded grid runs on the float32-arithmetic kernels.
  * Returns FSW_OK, FSW_ERR_INVALID_ARG, FSW_ERR_UNSUPPORTED or FSW_ERR_HIP.
  */
 int flashswin_wattn_fwd_lowrank(const void* q, const void* k, const void* v,
@@ -191,9 +192,10 @@ int flashswin_wattn_fwd_lowrank(const void* q, const void* k, const void* v,
                                 int M, int shift, int dtype, void* hip_stream);
 
 /*
- * Bytes of workspace flashswin_wattn_bwd_lowrank needs: the backward's own workspace plus the
- * per-window gradients of both factors (2 * windows * heads * M*M * rank * 4 bytes).  0 when B == 0
- * and for arguments that call would reject.
+ * Bytes of workspace flashswin_wattn_bwd_lowrank needs: the workspace of the kernels that serve the
+ * shape plus room for partial sums of both factor gradients (2 * windows * heads * M*M * rank * 4
+ * bytes, and 8 bytes per head on the MFMA kernels).  0 when B == 0 and for arguments that call would
+ * reject.
  */
 size_t flashswin_wattn_bwd_lowrank_workspace_size(int64_t B, int64_t Hg, int64_t Wg, int heads, int d,
                                                   int M, int shift, int dtype, int rank);
@@ -206,7 +208,10 @@ size_t flashswin_wattn_bwd_lowrank_workspace_size(int64_t B, int64_t Hg, int64_t
  *   dbias_w      likewise, sum over all windows of dS^T U.
  * Both are summed over the windows in a fixed order (bit-reproducible).  The outputs may not share
  * a byte with any input, the workspace or each other.  lse must come from
- * flashswin_wattn_fwd_lowrank with the same factors.
+ * flashswin_wattn_fwd_lowrank with the same factors.  bf16 with d = 32, windows of at most 256
+ * tokens (M <= 16) and grids that M divides runs on the whole-window MFMA kernels (the factors as
+ * extra channels of the score products, their gradients from the extra output rows, summed per
+ * group of windows); every other supported shape runs on the float32-arithmetic kernels.
  * Returns FSW_OK, FSW_ERR_INVALID_ARG, FSW_ERR_UNSUPPORTED, FSW_ERR_WORKSPACE or FSW_ERR_HIP.
  */
 int flashswin_wattn_bwd_lowrank(const void* q, const void* k, const void* v, const void* out,

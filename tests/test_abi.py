@@ -278,12 +278,18 @@ def test_lowrank_forward_empty_batch_is_a_no_op():
 
 
 def test_lowrank_workspace_adds_the_per_window_factor_gradients():
+    """float32 kernels: their plain workspace plus two [windows][heads][N][rank] float blocks.  bf16 MFMA
+    kernels (d = 32, windows of at most 256 tokens): Delta, the four maxima per window-head, one dtheta
+    row of d/2 floats per window-head and side, then the same two blocks and two factor maxima per head."""
     def al(n):
         return (n + 255) // 256 * 256
-    for dt in (F.FSW_BF16, F.FSW_F32):
-        base = F.flashswin_wattn_bwd_workspace_size(1, 16, 16, 2, 32, 8, 4, F.FSW_F32)  # the float32-arithmetic layout
-        got = F.flashswin_wattn_bwd_lowrank_workspace_size(1, 16, 16, 2, 32, 8, 4, dt, 5)
-        assert got == base + al(2 * 4 * 2 * 64 * 5 * 4)
+    nwin, heads, N, r = 4, 2, 64, 5
+    lr = 2 * nwin * heads * N * r * 4
+    base = F.flashswin_wattn_bwd_workspace_size(1, 16, 16, 2, 32, 8, 4, F.FSW_F32)  # the float32-arithmetic layout
+    assert F.flashswin_wattn_bwd_lowrank_workspace_size(1, 16, 16, 2, 32, 8, 4, F.FSW_F32, r) == base + al(lr)
+    nwh = nwin * heads
+    mfma = al(16 * 16 * heads * 4) + al(nwh * 4 * 4) + al(2 * nwh * 16 * 4) + al(lr + 2 * heads * 4)
+    assert F.flashswin_wattn_bwd_lowrank_workspace_size(1, 16, 16, 2, 32, 8, 4, F.FSW_BF16, r) == mfma
     assert F.flashswin_wattn_bwd_lowrank_workspace_size(1, 16, 16, 2, 32, 8, 4, F.FSW_BF16, 0) == 0
     assert F.flashswin_wattn_bwd_lowrank_workspace_size(1, 16, 16, 2, 32, 8, 4, F.FSW_BF16, F.MAX_RANK + 1) == 0
 

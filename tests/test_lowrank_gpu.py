@@ -1,10 +1,16 @@
 """GPU parity of the rank-r additive bias (flashswin_wattn_fwd_lowrank / flashswin_wattn_bwd_lowrank)
 against the fp64 oracle: O, LSE, dQ, dK, dV, dtheta and the factor gradients dU, dW.
 
+bf16 d = 32 with windows of at most 256 tokens runs the whole-window MFMA backward (the bias as extra
+score channels; the factor gradients summed over groups of windows); larger windows, other d, float32
+and padded grids run the float32-arithmetic kernels.
+
 The factors are N(0, 0.5^2) per entry; the oracle adds U[h, n_i] . W[h, n_j] to the scaled score of
 every pair before the region mask.  Tolerances are those of test_parity_gpu.py: bf16 inputs, max-abs
 <= 2e-2 and relative L2 <= 5e-3 (for dtheta, dU and dW, which are sums over the whole batch, max-abs
-relative to max|ref|); float32 inputs, 1e-5 both, max-abs relative to max|ref| when that exceeds 1."""
+relative to max|ref|); float32 inputs, 1e-5 both, max-abs relative to max|ref| when that exceeds 1.
+A bf16 output is stored rounded, up to 2^-9 of its own magnitude, which at |dV| of 4 and more is
+itself near 2e-2: for bf16 tensors the per-element bound is 2e-2 + 2^-8 |ref|."""
 
 import numpy as np
 import pytest
@@ -23,13 +29,16 @@ def _np(t):
     return t.detach().to("cpu", torch.float64).numpy()
 
 
-def _close(name, got, ref, max_abs, rel, scale_abs=False):
-    err = np.abs(got - ref).max()
+def _close(name, got, ref, max_abs, rel, scale_abs=False, bf16_store=False):
+    diff = np.abs(got - ref)
+    err = diff.max()
     l2 = np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-300)
     bound = max_abs * max(1.0, np.abs(ref).max()) if scale_abs else max_abs
-    print(f"  {name}: max-abs {err:.3e} (bound {bound:.3e}) rel-L2 {l2:.3e}", flush=True)
+    ratio = (diff / (bound + (2.0 ** -8 * np.abs(ref) if bf16_store else 0.0))).max()
+    print(f"  {name}: max-abs {err:.3e} (bound {bound:.3e}{' + 2^-8 |ref|' if bf16_store else ''}, worst ratio "
+          f"{ratio:.3f}, max|ref| {np.abs(ref).max():.3e}) rel-L2 {l2:.3e}", flush=True)
     assert np.all(np.isfinite(got)), name
-    assert err <= bound and l2 <= rel, name
+    assert ratio <= 1.0 and l2 <= rel, name
 
 
 def _factors(H, M, r, seed):
@@ -55,6 +64,11 @@ CASES = [
     (1, 40, 40, 2, 32, 20, 7, 16, "bf16"),
     (1, 44, 44, 1, 32, 22, 0, 32, "bf16"),
     (1, 10, 10, 2, 32, 5, 2, 9, "bf16"),
+    # enough window-heads that the MFMA backward gives each workgroup several windows of one head:
+    # 135 windows x 16 heads (2 per group, the last group one window), 279 x 30 (8 per group, the last 7)
+    (15, 24, 24, 16, 32, 8, 3, 16, "bf16"),
+    (31, 24, 24, 30, 32, 8, 5, 24, "bf16"),
+    (2, 64, 64, 3, 32, 16, 8, 16, "bf16"),
 ]
 
 
@@ -85,14 +99,14 @@ def test_lowrank_matches_oracle(case):
         _close("O", _np(out), ro, **tol)
         _close("LSE", _np(lse), rl, **tol)
     else:
-        _close("O", _np(out), ro, 2e-2, 5e-3)
+        _close("O", _np(out), ro, 2e-2, 5e-3, bf16_store=True)
         _close("LSE", _np(lse), rl, 2e-2, 5e-3)
     names = ("dQ", "dK", "dV", "dtheta_row", "dtheta_col", "dU", "dW")
     for i, (name, got, ref) in enumerate(zip(names, grads, rg)):
         if dt == "f32":
             _close(name, _np(got), ref, 1e-5, 1e-5, scale_abs=True)
         else:
-            _close(name, _np(got), ref, 2e-2, 5e-3, scale_abs=i >= 3)
+            _close(name, _np(got), ref, 2e-2, 5e-3, scale_abs=i >= 3, bf16_store=i < 3)
 
 
 def test_lowrank_factor_gradients_are_reproducible():
@@ -126,14 +140,15 @@ def test_lowrank_zero_factors_equal_the_plain_forward():
 
 @pytest.mark.parametrize("M,shift,rank", [(16, 8, 16), (12, 5, 32)])
 def test_lowrank_bf16_operand_path(M, shift, rank):
-    """W scaled by 2^12 and U by 2^-12 leaves every bias term unchanged, but |W| leaves fp16 range, so
-    the MFMA forward takes bf16 score operands for every window-head (the backward, on the float32
-    kernels, is unaffected).  O and LSE against the oracle, and dU times 2^-12 and dW times 2^12 (the
-    unscaled magnitudes)."""
+    """W scaled by 2^14 and U by 2^-14 leaves every bias term unchanged, but max|W| of every head leaves
+    fp16 range (about 2.5 sigma of thousands of entries times 2^13 > 2^14), so the MFMA forward and
+    backward take bf16 operands for every window-head.  O and LSE against the oracle, and dU times 2^-14
+    and dW times 2^14 (the unscaled magnitudes)."""
     B, Hg, Wg, H, D = 1, 2 * M, 2 * M, 2, 32
     x = make_inputs(B, Hg, Wg, H, D, "bf16", seed=980 + M, with_dout=True)
     U, W = _factors(H, M, rank, seed=985 + M)
-    U, W = U * 2.0 ** -12, W * 2.0 ** 12
+    U, W = U * 2.0 ** -14, W * 2.0 ** 14
+    assert float(W.abs().amax(dim=(1, 2)).min()) >= 2.0 ** 14
     xd = {n: t.to(DEV) for n, t in x.items()}
     out, lse = F.wattn_fwd_lowrank(xd["q"], xd["k"], xd["v"], xd["theta_row"], xd["theta_col"], U.to(DEV),
                                    W.to(DEV), M, shift)
@@ -147,8 +162,8 @@ def test_lowrank_bf16_operand_path(M, shift, rank):
     _close("O", _np(out), ro, 2e-2, 5e-3)
     _close("LSE", _np(lse), rl, 2e-2, 5e-3)
     rg = oracle.wattn_bwd_ref(q, k, v, do, tr, tc, M, shift, lowrank=lr)
-    _close("dU (x 2^-12)", _np(grads[5]) * 2.0 ** -12, rg[5] * 2.0 ** -12, 2e-2, 5e-3, scale_abs=True)
-    _close("dW (x 2^12)", _np(grads[6]) * 2.0 ** 12, rg[6] * 2.0 ** 12, 2e-2, 5e-3, scale_abs=True)
+    _close("dU (x 2^-14)", _np(grads[5]) * 2.0 ** -14, rg[5] * 2.0 ** -14, 2e-2, 5e-3, scale_abs=True)
+    _close("dW (x 2^14)", _np(grads[6]) * 2.0 ** 14, rg[6] * 2.0 ** 14, 2e-2, 5e-3, scale_abs=True)
 
 
 def test_lowrank_large_bias_falls_back():

@@ -332,15 +332,25 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dq_scalar_kernel(
   reduce_dtheta_block<D>(terms, partials + partial_row(g, blk, nb, 1) * (D / 2));
 }
 
-// Factor gradients: out[e] = sum over windows w of parts[w][e] in window order, e over the
-// heads * N * rank entries of one factor (parts laid out [windows][heads][N][rank]).
-__global__ __launch_bounds__(256) void lowrank_reduce_kernel(const float* __restrict__ parts, int64_t nwin,
-                                                             int64_t per_win, float* __restrict__ out) {
-  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (e >= per_win) return;
+// Factor gradients: out[e] = sum over rows r of parts[r][e] (parts laid out [rows][heads][N][rank]).
+// A workgroup takes 16 entries; thread (slice s, entry) sums rows s, s + 16, ... in order, then thread
+// s = 0 adds the 16 slice sums in order.
+__global__ __launch_bounds__(256) void lowrank_reduce_kernel(const float* __restrict__ parts, int64_t nrows,
+                                                             int64_t per_row, float* __restrict__ out) {
+  __shared__ float red[16][16];
+  const int el = threadIdx.x & 15, sl = threadIdx.x >> 4;
+  const int64_t e = (int64_t)blockIdx.x * 16 + el;
   float s = 0.f;
-  for (int64_t w = 0; w < nwin; ++w) s += parts[w * per_win + e];
-  out[e] = s;
+  if (e < per_row)
+    for (int64_t r = sl; r < nrows; r += 16) s += parts[r * per_row + e];
+  red[sl][el] = s;
+  __syncthreads();
+  if (sl == 0 && e < per_row) {
+    float t = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) t += red[i][el];
+    out[e] = t;
+  }
 }
 
 // Sum the partial rows of one (head, pair-slot) in a fixed order: thread t takes rows t, t+256, ...
@@ -366,6 +376,13 @@ __global__ __launch_bounds__(256) void dtheta_reduce_kernel(const float* __restr
     else
       dth_col[h * quarter_d + e - quarter_d] = red[0];
   }
+}
+
+hipError_t launch_lowrank_reduce(const float* parts, int64_t nrows, int64_t per_row, float* out, hipStream_t st) {
+  if (per_row <= 0) return hipSuccess;
+  hipLaunchKernelGGL(lowrank_reduce_kernel, dim3((unsigned)((per_row + 15) / 16)), dim3(256), 0, st, parts, nrows,
+                     per_row, out);
+  return hipGetLastError();
 }
 
 hipError_t launch_dtheta_reduce(const float* partials, int64_t n_partials, int64_t rows_per_head, const Geom& g,
@@ -417,12 +434,9 @@ static hipError_t launch_bwd_scalar_t(const BwdArgs& a, hipStream_t st) {
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (a.lr.rank > 0) {
-    const unsigned rblocks = (unsigned)((per_win + 255) / 256);
-    hipLaunchKernelGGL(lowrank_reduce_kernel, dim3(rblocks), dim3(256), 0, st, (const float*)wparts, nwin, per_win,
-                       a.dw);
-    hipLaunchKernelGGL(lowrank_reduce_kernel, dim3(rblocks), dim3(256), 0, st, (const float*)uparts, nwin, per_win,
-                       a.du);
-    e = hipGetLastError();
+    e = launch_lowrank_reduce(wparts, nwin, per_win, a.dw, st);
+    if (e != hipSuccess) return e;
+    e = launch_lowrank_reduce(uparts, nwin, per_win, a.du, st);
     if (e != hipSuccess) return e;
   }
   const int64_t rows_per_head = 2 * g.B * g.nH * g.nW * nb;

@@ -106,7 +106,7 @@ struct WsLayout {
 };
 
 // Kernel family of a backward call.
-enum class BwdPath { kScalar, kMfma32, kMfma64 };
+enum class BwdPath { kScalar, kMfma32, kMfma64, kMfmaLowRank };
 
 // rank > 0: room for the per-window gradients of both low-rank bias factors.
 WsLayout workspace_layout(const fsw::Geom& g, BwdPath path, int rank = 0) {
@@ -116,11 +116,13 @@ WsLayout workspace_layout(const fsw::Geom& g, BwdPath path, int rank = 0) {
   w.delta_off = 0;
   w.scal_off = align256((size_t)rows * sizeof(float));
   w.partials_off = w.scal_off + align256((size_t)nwh * 4 * sizeof(float));
-  w.n_partials = path == BwdPath::kMfma32   ? fsw::bwd_mfma_partials(g)
-                 : path == BwdPath::kMfma64 ? fsw::bwd_d64_partials(g)
-                                            : fsw::bwd_scalar_partials(g);
+  w.n_partials = path == BwdPath::kMfma32 ? fsw::bwd_mfma_partials(g)
+                 : path == BwdPath::kMfma64 || path == BwdPath::kMfmaLowRank ? fsw::bwd_window_partials(g)
+                                                                             : fsw::bwd_scalar_partials(g);
   w.lr_off = w.partials_off + align256((size_t)w.n_partials * (g.d / 2) * sizeof(float));
-  w.total = w.lr_off + align256((size_t)2 * g.B * g.nH * g.nW * g.heads * g.N * rank * sizeof(float));
+  const int64_t lr_floats = 2 * g.B * g.nH * g.nW * g.heads * g.N * rank +
+                            (path == BwdPath::kMfmaLowRank ? fsw::lowrank_mfma_extra_floats(g) : 0);
+  w.total = w.lr_off + align256((size_t)lr_floats * sizeof(float));
   return w;
 }
 
@@ -128,9 +130,12 @@ WsLayout workspace_layout(const fsw::Geom& g, BwdPath path, int rank = 0) {
 // and the M = 8 forward variant.
 bool padded(const fsw::Geom& g) { return g.Hp != g.Hg || g.Wp != g.Wg; }
 bool use_mfma_fwd(const fsw::Geom& g, int dtype) { return dtype == FSW_BF16 && fsw::fwd_mfma_supported(g); }
-// A low-rank bias runs on the float32-arithmetic kernels.
+// A low-rank bias runs on the whole-window MFMA kernels where they serve the shape, else on the
+// float32-arithmetic kernels.
 BwdPath bwd_path(const fsw::Geom& g, int dtype, int rank = 0) {
-  if (dtype != FSW_BF16 || rank > 0) return BwdPath::kScalar;
+  if (rank > 0)
+    return dtype == FSW_BF16 && fsw::bwd_lowrank_mfma_supported(g, rank) ? BwdPath::kMfmaLowRank : BwdPath::kScalar;
+  if (dtype != FSW_BF16) return BwdPath::kScalar;
   if (fsw::kHaveMfmaBwd && g.d == 32 && g.M <= kMaxM) return BwdPath::kMfma32;
   if (fsw::bwd_d64_supported(g)) return BwdPath::kMfma64;
   return BwdPath::kScalar;
@@ -180,9 +185,10 @@ int bwd_impl(const void* q, const void* k, const void* v, const void* out, const
                  reinterpret_cast<float*>(base + ws.partials_off), ws.n_partials, lr, du, dw,
                  reinterpret_cast<float*>(base + ws.lr_off)};
   hipStream_t s = reinterpret_cast<hipStream_t>(hip_stream);
-  const hipError_t e = path == BwdPath::kMfma32   ? fsw::launch_bwd_mfma(a, s)
-                       : path == BwdPath::kMfma64 ? fsw::launch_bwd_d64(a, s)
-                                                  : fsw::launch_bwd_scalar(a, s);
+  const hipError_t e = path == BwdPath::kMfma32         ? fsw::launch_bwd_mfma(a, s)
+                       : path == BwdPath::kMfma64       ? fsw::launch_bwd_d64(a, s)
+                       : path == BwdPath::kMfmaLowRank  ? fsw::launch_bwd_lowrank_mfma(a, s)
+                                                        : fsw::launch_bwd_scalar(a, s);
   return e == hipSuccess ? FSW_OK : FSW_ERR_HIP;
 }
 

@@ -60,8 +60,8 @@ struct BwdArgs {
   float* lr_parts = nullptr;  // [2][windows][heads][M*M][rank]  per-window factor gradients (rank > 0)
 };
 
-// Scalar (float32-arithmetic) paths: any d in {8,16,32,64}, any window size, either dtype; the only
-// paths that take a low-rank bias.
+// Scalar (float32-arithmetic) paths: any d in {8,16,32,64}, any window size, either dtype, with or
+// without a low-rank bias.
 hipError_t launch_fwd_scalar(const FwdArgs& a, hipStream_t st);
 hipError_t launch_bwd_scalar(const BwdArgs& a, hipStream_t st);
 // Number of dtheta partial rows the scalar backward writes.
@@ -80,15 +80,25 @@ hipError_t launch_fwd_m8(const FwdArgs& a, hipStream_t st);
 // bf16 MFMA backward (d == 32, M <= 32).
 hipError_t launch_bwd_mfma(const BwdArgs& a, hipStream_t st);
 int64_t bwd_mfma_partials(const Geom& g);
-// bf16 MFMA backward for d == 64 and windows of at most 256 tokens (grids that M divides).
+// bf16 MFMA backward for d == 64 and windows of at most 256 tokens.
 bool bwd_d64_supported(const Geom& g);
 hipError_t launch_bwd_d64(const BwdArgs& a, hipStream_t st);
-int64_t bwd_d64_partials(const Geom& g);
+// bf16 MFMA backward with a low-rank bias: d == 32, windows of at most 256 tokens, rank <= 32, grids
+// that M divides.  Its workspace needs lowrank_mfma_extra_floats(g) floats after the float32 kernels'
+// two [windows][heads][M*M][rank] blocks.
+bool bwd_lowrank_mfma_supported(const Geom& g, int rank);
+hipError_t launch_bwd_lowrank_mfma(const BwdArgs& a, hipStream_t st);
+inline int64_t lowrank_mfma_extra_floats(const Geom& g) { return 2 * (int64_t)g.heads; }
+// dtheta partial rows of the whole-window kernels (d == 64, and the low-rank ones).
+int64_t bwd_window_partials(const Geom& g);
 constexpr bool kHaveMfmaBwd = true;
 
 // Materialized comparison path (bf16, d == 32): scores in HBM, softmax, P.V.
 size_t materialized_workspace_bytes(const Geom& g);
 hipError_t launch_fwd_materialized(const FwdArgs& a, const float* bias, void* workspace, hipStream_t st);
+
+// Factor gradients: out[e] = sum over rows r < nrows of parts[r * per_row + e], in a fixed order.
+hipError_t launch_lowrank_reduce(const float* parts, int64_t nrows, int64_t per_row, float* out, hipStream_t st);
 
 // Deterministic fixed-order reduction of dtheta partials into dth_row / dth_col.
 hipError_t launch_dtheta_reduce(const float* partials, int64_t n_partials, int64_t partials_per_head_stride,

@@ -872,7 +872,7 @@ int64_t bwd_mfma_partials(const Geom& g) {
   return (int64_t)g.heads * 2 * g.B * g.nH * g.nW * blocks_per_windowhead(g);
 }
 
-hipError_t launch_bwd_mfma(const BwdArgs& a, hipStream_t st) {
+hipError_t launch_bwd_pre32(const BwdArgs& a, hipStream_t st) {
   const Geom& g = a.g;
   const int64_t pre_blocks = g.B * g.nH * g.nW * ((g.heads + kPreHeads - 1) / kPreHeads);
   // every byte offset the pre-kernel forms is below 2 * tokens * max(xs, os)
@@ -885,7 +885,12 @@ hipError_t launch_bwd_mfma(const BwdArgs& a, hipStream_t st) {
     hipLaunchKernelGGL(bwd_pre_kernel<int64_t>, dim3((unsigned)pre_blocks), dim3(kPreThreads), 0, st,
                        (const uint16_t*)a.out, (const uint16_t*)a.dout, (const uint16_t*)a.v, (const uint16_t*)a.q,
                        (const uint16_t*)a.k, a.delta, a.scal, g);
-  hipError_t e = hipGetLastError();
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_mfma(const BwdArgs& a, hipStream_t st) {
+  const Geom& g = a.g;
+  const hipError_t e = launch_bwd_pre32(a, st);
   if (e != hipSuccess) return e;
   const MainShape m = bwd_shape(g);
   if (g.Hp != g.Hg || g.Wp != g.Wg) {  // padded grid: the run-time-M instances with padding checks

@@ -228,7 +228,9 @@ __device__ inline void reduce_dtheta(float (&t)[D / 4], float* red, float* dst, 
 // ------------------------------------------------------------------------------------ prologue
 
 // One workgroup per window-head: Delta of its tokens and scal[wh] = {max |dO|, max |v|, max |q|, max |k|}.
-// Thread: 16-byte part p = tid % (D/8) of tokens tid / (D/8), tid / (D/8) + 256 / (D/8), ...
+// Thread: 16-byte part p = tid % (D/8) of tokens tid / (D/8), tid / (D/8) + 256 / (D/8), ...  Launched
+// for d = 64; the bias kernels (d = 32) take the prologue of the chunked d = 32 kernels, which reads
+// several heads' slices of a token row at once.
 template <int D>
 __global__ __launch_bounds__(256) void bwd_pre_win_kernel(const uint16_t* __restrict__ out,
                                                           const uint16_t* __restrict__ dout,
@@ -889,11 +891,7 @@ hipError_t launch_bwd_lowrank_mfma(const BwdArgs& a, hipStream_t st) {
   const Geom& g = a.g;
   if (!bwd_lowrank_mfma_supported(g, a.lr.rank) || !a.lr.u || !a.lr.w || !a.du || !a.dw || !a.lr_parts)
     return hipErrorInvalidValue;
-  const int64_t nwh = g.B * g.nH * g.nW * g.heads;
-  hipLaunchKernelGGL(bwd_pre_win_kernel<32>, dim3((unsigned)nwh), dim3(256), 0, st, (const uint16_t*)a.out,
-                     (const uint16_t*)a.dout, (const uint16_t*)a.v, (const uint16_t*)a.q, (const uint16_t*)a.k, a.delta,
-                     a.scal, g);
-  const hipError_t e = hipGetLastError();
+  const hipError_t e = launch_bwd_pre32(a, st);  // the d = 32 prologue: several heads per workgroup
   if (e != hipSuccess) return e;
   if (a.lr.rank <= 16) return launch_win_nw<32, 16, false>(a, st);
   return launch_win_nw<32, 32, false>(a, st);

@@ -79,6 +79,8 @@ bool fwd_m8_supported(const Geom& g);
 hipError_t launch_fwd_m8(const FwdArgs& a, hipStream_t st);
 // bf16 MFMA backward (d == 32, M <= 32).
 hipError_t launch_bwd_mfma(const BwdArgs& a, hipStream_t st);
+// Its prologue alone (bf16, d == 32): Delta and the per-window-head maxima into a.delta, a.scal.
+hipError_t launch_bwd_pre32(const BwdArgs& a, hipStream_t st);
 int64_t bwd_mfma_partials(const Geom& g);
 // bf16 MFMA backward for d == 64 and windows of at most 256 tokens.
 bool bwd_d64_supported(const Geom& g);

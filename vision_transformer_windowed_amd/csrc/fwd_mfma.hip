@@ -727,6 +727,7 @@ hipError_t launch_lowrank(const FwdArgs& a, hipStream_t st) {
   const int N = a.g.N;
   if (N <= 64) return launch_nw<2, 0, 64, 32, false, RK>(a, st);
   if (N <= 128) return launch_nw<4, 0, 128, 32, false, RK>(a, st);
+  if (a.g.M == 16) return launch_nw<8, 16, 256, 32, false, RK>(a, st);  // window size fixed at compile time
   if (N <= 256) return launch_nw<8, 0, 256, 32, false, RK>(a, st);
   return launch_nw<8, 0, kMaxNPLowRank, 32, false, RK>(a, st);
 }

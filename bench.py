@@ -19,7 +19,8 @@ against the HBM peak, with its own `traffic` read the same way.
 only).
 
 Modes for profiling runs: --only fwd|bwd runs just that call per step; --copy-calibration runs a
-plain streaming kernel of known traffic, b = -a over 1 GiB (for scaling HBM counters).
+plain streaming kernel of known traffic, b = -a over 1 GiB (for scaling HBM counters);
+--lowrank-only prints the rank-16 bias line alone.
 """
 
 import argparse
@@ -353,6 +354,7 @@ def main():
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--lowrank-only", action="store_true")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -378,6 +380,9 @@ def main():
             torch.neg(a, out=b)
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration_bytes": n * 4, "kernel": "neg", "launches": args.warmup + args.steps}))
+        return
+    if args.lowrank_only:  # the rank-16 bias line alone (profiling runs)
+        print(json.dumps(lowrank_step(dev, args.steps, args.warmup)), flush=True)
         return
 
     w = WORKLOADS[args.workload]

@@ -280,7 +280,8 @@ def test_lowrank_forward_empty_batch_is_a_no_op():
 def test_lowrank_workspace_adds_the_per_window_factor_gradients():
     """float32 kernels: their plain workspace plus two [windows][heads][N][rank] float blocks.  bf16 MFMA
     kernels (d = 32, windows of at most 256 tokens): Delta, the four maxima per window-head, one dtheta
-    row of d/2 floats per window-head and side, then the same two blocks and two factor maxima per head."""
+    row of d/2 floats per window-head and side, then the same two blocks, up to 64 floats of alignment,
+    both factors zero-padded to 32 channels and two factor maxima per head."""
     def al(n):
         return (n + 255) // 256 * 256
     nwin, heads, N, r = 4, 2, 64, 5
@@ -288,7 +289,8 @@ def test_lowrank_workspace_adds_the_per_window_factor_gradients():
     base = F.flashswin_wattn_bwd_workspace_size(1, 16, 16, 2, 32, 8, 4, F.FSW_F32)  # the float32-arithmetic layout
     assert F.flashswin_wattn_bwd_lowrank_workspace_size(1, 16, 16, 2, 32, 8, 4, F.FSW_F32, r) == base + al(lr)
     nwh = nwin * heads
-    mfma = al(16 * 16 * heads * 4) + al(nwh * 4 * 4) + al(2 * nwh * 16 * 4) + al(lr + 2 * heads * 4)
+    extra = (64 + 2 * heads * N * F.MAX_RANK + 2 * heads) * 4
+    mfma = al(16 * 16 * heads * 4) + al(nwh * 4 * 4) + al(2 * nwh * 16 * 4) + al(lr + extra)
     assert F.flashswin_wattn_bwd_lowrank_workspace_size(1, 16, 16, 2, 32, 8, 4, F.FSW_BF16, r) == mfma
     assert F.flashswin_wattn_bwd_lowrank_workspace_size(1, 16, 16, 2, 32, 8, 4, F.FSW_BF16, 0) == 0
     assert F.flashswin_wattn_bwd_lowrank_workspace_size(1, 16, 16, 2, 32, 8, 4, F.FSW_BF16, F.MAX_RANK + 1) == 0

@@ -120,14 +120,19 @@ __device__ __forceinline__ uint4 rot_part(uint4 raw, const float* sn, const floa
   return pack8_op(x, H16);
 }
 
-// Channels c0 .. c0 + 7 of row n of a head's bias factor (float32 [heads][N][rank], zero past the
-// rank), times `scale`, packed to the operand format.
+// Channels c0 .. c0 + 7 (c0 a multiple of 8 below RK) of row n of a head's zero-padded bias factor
+// (float32 [heads][N][RK], written by factor_prep_kernel): two aligned 16-byte words.
+template <int RK>
+__device__ __forceinline__ const uint4* factor_row8(const float* f, int head, int n, int c0, int N) {
+  return reinterpret_cast<const uint4*>(f + ((int64_t)head * N + n) * RK + c0);
+}
+
+// Eight factor values (two words of factor_row8) times `scale`, packed to the operand format.
 template <bool H16>
-__device__ __forceinline__ uint4 factor_part(const float* f, int head, int n, int c0, int rank, int N, float scale) {
-  const float* row = f + ((int64_t)head * N + n) * rank;
-  float x[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) x[e] = c0 + e < rank ? row[c0 + e] * scale : 0.f;
+__device__ __forceinline__ uint4 factor_op(uint4 a, uint4 b, float scale) {
+  const float x[8] = {__uint_as_float(a.x) * scale, __uint_as_float(a.y) * scale, __uint_as_float(a.z) * scale,
+                      __uint_as_float(a.w) * scale, __uint_as_float(b.x) * scale, __uint_as_float(b.y) * scale,
+                      __uint_as_float(b.z) * scale, __uint_as_float(b.w) * scale};
   return pack8_op(x, H16);
 }
 
@@ -155,6 +160,11 @@ __device__ inline void unrotate_store(const f32x16_t (&acc)[NA], float scale, fl
                                       int r, int c, int h, float (&t)[D / 4]) {
   constexpr int PA = D / 4;
   const float inv_op = 1.f / op_scale;
+  uint2 rawg[D / 32][4];  // every load first: one wait instead of one per group
+#pragma unroll
+  for (int ct = 0; ct < D / 32; ++ct)
+#pragma unroll
+    for (int gq = 0; gq < 4; ++gq) rawg[ct][gq] = *reinterpret_cast<const uint2*>(xsrc + 32 * ct + 8 * gq + 4 * h);
 #pragma unroll
   for (int ct = 0; ct < D / 32; ++ct) {
 #pragma unroll
@@ -164,7 +174,7 @@ __device__ inline void unrotate_store(const f32x16_t (&acc)[NA], float scale, fl
       const int gg = (ach % (D / 2)) / 8;
       const int pos = axis ? c : r;
       const int ch = ach + 4 * h;
-      const uint2 raw = *reinterpret_cast<const uint2*>(xsrc + ch);
+      const uint2 raw = rawg[ct][gq];
       const float xin[4] = {__uint_as_float(raw.x << 16), __uint_as_float(raw.x & 0xffff0000u),
                             __uint_as_float(raw.y << 16), __uint_as_float(raw.y & 0xffff0000u)};
       float res[4];
@@ -283,15 +293,22 @@ __global__ __launch_bounds__(256) void bwd_pre_win_kernel(const uint16_t* __rest
   if (tid < 4) scal[wh * 4 + tid] = fmaxf(fmaxf(red[0][tid], red[1][tid]), fmaxf(red[2][tid], red[3][tid]));
 }
 
-// Largest |component| of each head's bias factors: fmax[2h] = max |U[h]|, fmax[2h + 1] = max |W[h]|
-// (a NaN counts as infinity).  One workgroup per head.
-__global__ __launch_bounds__(256) void factor_max_kernel(const float* __restrict__ u, const float* __restrict__ w,
-                                                         int64_t per_head, float* __restrict__ fmax) {
+// Per head: the bias factors zero-padded from rank to RK channels (upad, wpad [heads][N][RK], so that
+// the kernels read eight channels as two aligned 16-byte words), and their largest |component|:
+// fmax[2h] = max |U[h]|, fmax[2h + 1] = max |W[h]| (a NaN counts as infinity).  One workgroup per head.
+template <int RK>
+__global__ __launch_bounds__(256) void factor_prep_kernel(const float* __restrict__ u, const float* __restrict__ w,
+                                                          int rank, int N, float* __restrict__ upad,
+                                                          float* __restrict__ wpad, float* __restrict__ fmax) {
   __shared__ float red[4][2];
   const int h = blockIdx.x, tid = threadIdx.x;
   float mu = 0.f, mw = 0.f;
-  for (int64_t i = tid; i < per_head; i += 256) {
-    const float a = u[h * per_head + i], b = w[h * per_head + i];
+  for (int i = tid; i < N * RK; i += 256) {
+    const int n = i / RK, c = i % RK;
+    const int64_t src = ((int64_t)h * N + n) * rank + c;
+    const float a = c < rank ? u[src] : 0.f, b = c < rank ? w[src] : 0.f;
+    upad[(int64_t)h * N * RK + i] = a;
+    wpad[(int64_t)h * N * RK + i] = b;
     mu = fmaxf(mu, a != a ? INFINITY : fabsf(a));
     mw = fmaxf(mw, b != b ? INFINITY : fabsf(b));
   }
@@ -341,38 +358,77 @@ __device__ inline void dkdv_body(const uint16_t* __restrict__ q, const uint16_t*
                                  const WinHead& w, int64_t wh, bool masked, const LowRank& lr, float (&fac)[16]) {
   using WD = WDim<D, RK>;
   constexpr int NT = NW * 64;
-  constexpr int IPT = kMaxNW * 8 / NT;  // staged 16-byte items per thread, at most
+  constexpr int IPT = 4;  // staged 16-byte items per thread: NP <= 32 NW tokens of 8 items
   const int M = g.M, N = g.N;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int h = lane >> 5, col = lane & 31;
   const float g_scale = scale_to_2p14(scal[wh * 4]);                                   // dO of the dV product
   const float ds_scale = scale_to_2p14(2.f * D * scal[wh * 4] * scal[wh * 4 + 1]);  // |tau dS| <= 2^14
 
-  // 1. stage every query-side row of the window (item it: part it % 8 of token it / 8)
+  // 1. every global load first (the staged items: part it % 8 of token it / 8; then the lane's key), so
+  //    that their latencies overlap; the transforms follow
+  // (the loads of an item are unconditional inside one test, so the compiler keeps them in one batch:
+  //  a part beyond the head's channels reads channels of part D/8 - 1, and LSE and Delta are read by
+  //  every part, kept by part 0)
+  uint4 ra[IPT], rb[IPT];
+  float rl[IPT], rd[IPT];
+  const int64_t tok0 = w.b * g.Hg * g.Wg;  // a grid token of the image: the address of items that are none
+#pragma unroll
+  for (int i = 0; i < IPT; ++i) {
+    const int it = tid + i * NT;
+    const int n = it >> 3, part = it & 7;
+    const bool ok = it < NP * 8 && n < N && (!PAD || token_real(g, w.wy, w.wx, n / M, n % M));
+    const int64_t tok = ok ? token_index(g, w.b, w.wy, w.wx, n / M, n % M) : tok0;
+    const int pc = min(part, D / 8 - 1);
+    const uint4* pa = reinterpret_cast<const uint4*>(q + tok * g.xs + w.h * D + 8 * pc);
+    const uint4* pb = reinterpret_cast<const uint4*>(dout + tok * g.os + w.h * D + 8 * pc);
+    if constexpr (RK > 0) {
+      if (part >= D / 8) {  // a bias part: its eight padded U channels instead
+        pa = factor_row8<RK>(lr.u, w.h, ok ? n : 0, min(8 * part - D, RK - 8), N);
+        pb = pa + 1;
+      }
+    }
+    ra[i] = *pa;
+    rb[i] = *pb;
+    rl[i] = lse[tok * g.heads + w.h];
+    rd[i] = delta[tok * g.heads + w.h];
+  }
+  const int kj = wave * 32 + col;
+  const bool kvalid = kj < N && (!PAD || token_real(g, w.wy, w.wx, kj / M, kj % M));  // a padding key is no key
+  const int kr = kvalid ? kj / M : 0, kc = kvalid ? kj - (kj / M) * M : 0;
+  int64_t koff = 0;
+  uint4 kb[WD::KST], vb[WD::DST], fw[WD::KST - WD::DST + 1];
+  koff = (kvalid ? token_index(g, w.b, w.wy, w.wx, kr, kc) : tok0) * g.xs + w.h * D;
+#pragma unroll
+  for (int t = 0; t < WD::DST; ++t) {
+    kb[t] = *reinterpret_cast<const uint4*>(k + koff + 16 * t + 8 * h);
+    vb[t] = *reinterpret_cast<const uint4*>(v + koff + 16 * t + 8 * h);
+  }
+#pragma unroll
+  for (int t = WD::DST; t < WD::KST; ++t) {
+    const uint4* f = factor_row8<RK>(lr.w, w.h, kvalid ? kj : 0, 16 * t + 8 * h - D, N);
+    kb[t] = f[0];
+    fw[t - WD::DST] = f[1];
+  }
+
+  // 2. stage every query-side row of the window
 #pragma unroll
   for (int i = 0; i < IPT; ++i) {
     const int it = tid + i * NT;
     if (it >= NP * 8) break;  // uniform across a wave: NP * 8 is a multiple of 256
     const int n = it >> 3, part = it & 7;
     uint4 qo = make_uint4(0, 0, 0, 0), go = qo, gs = qo;
-    float lv = 0.f, dl = 0.f;
     uint8_t lb = 0xff;
     if (n < N && (!PAD || token_real(g, w.wy, w.wx, n / M, n % M))) {  // padding stays zero, label 0xff
       const int r = n / M, c = n - (n / M) * M;
-      const int64_t tok = token_index(g, w.b, w.wy, w.wx, r, c);
       if (part < D / 8) {
-        const uint4 qr = *reinterpret_cast<const uint4*>(q + tok * g.xs + w.h * D + 8 * part);
-        go = *reinterpret_cast<const uint4*>(dout + tok * g.os + w.h * D + 8 * part);
-        qo = rot_part<D, H16>(qr, sm.sn, sm.cs, M, r, c, part, WD::kQScale);
+        go = rb[i];
+        qo = rot_part<D, H16>(ra[i], sm.sn, sm.cs, M, r, c, part, WD::kQScale);
         gs = scaled_part<H16>(go, g_scale);
       } else if (part < WD::DK / 8) {
-        qo = factor_part<H16>(lr.u, w.h, n, 8 * part - D, lr.rank, N, kLog2e);
+        qo = factor_op<H16>(ra[i], rb[i], kLog2e);
       }
-      if (part == 0) {
-        lv = -lse[tok * g.heads + w.h] * kLog2e;
-        dl = -delta[tok * g.heads + w.h] * ds_scale;
-        lb = (uint8_t)token_label(g, w.wy, w.wx, r, c);
-      }
+      if (part == 0) lb = (uint8_t)token_label(g, w.wy, w.wx, r, c);
     }
     *reinterpret_cast<uint4*>(sm.Q + n * kRS + 8 * part) = qo;
     if (part < D / 8) {
@@ -380,34 +436,30 @@ __device__ inline void dkdv_body(const uint16_t* __restrict__ q, const uint16_t*
       *reinterpret_cast<uint4*>(sm.Gs + n * kRS + 8 * part) = gs;
     }
     if (part == 0) {
-      sm.L[n] = lv;
-      sm.Dl[n] = dl;
+      sm.L[n] = lb != 0xff ? -rl[i] * kLog2e : 0.f;  // lb: the label of a grid token, 0xff otherwise
+      sm.Dl[n] = lb != 0xff ? -rd[i] * ds_scale : 0.f;
       sm.lab[n] = lb;
     }
   }
 
-  // 2. the lane's key: K~' operands (k-step t: channels 16t + 8h ..), tau V as bf16 B operands
-  const int kj = wave * 32 + col;
-  const bool kvalid = kj < N && (!PAD || token_real(g, w.wy, w.wx, kj / M, kj % M));  // a padding key is no key
-  const int kr = kvalid ? kj / M : 0, kc = kvalid ? kj - (kj / M) * M : 0;
-  int64_t koff = 0;
-  uint4 kb[WD::KST], vb[WD::DST];
+  // 3. the lane's key: K~' operands (k-step t: channels 16t + 8h ..), tau V as bf16 B operands (zero for
+  //    a lane without a key)
   int klab = 0xff;
-#pragma unroll
-  for (int t = 0; t < WD::KST; ++t) kb[t] = make_uint4(0, 0, 0, 0);
-#pragma unroll
-  for (int t = 0; t < WD::DST; ++t) vb[t] = make_uint4(0, 0, 0, 0);
   if (kvalid) {
-    koff = token_index(g, w.b, w.wy, w.wx, kr, kc) * g.xs + w.h * D;
     klab = token_label(g, w.wy, w.wx, kr, kc);
 #pragma unroll
     for (int t = 0; t < WD::DST; ++t) {
-      kb[t] = rot_part<D, H16>(*reinterpret_cast<const uint4*>(k + koff + 16 * t + 8 * h), sm.sn, sm.cs, M, kr, kc,
-                               2 * t + h, 1.f);
-      vb[t] = scaled_part<false>(*reinterpret_cast<const uint4*>(v + koff + 16 * t + 8 * h), ds_scale);
+      kb[t] = rot_part<D, H16>(kb[t], sm.sn, sm.cs, M, kr, kc, 2 * t + h, 1.f);
+      vb[t] = scaled_part<false>(vb[t], ds_scale);
     }
 #pragma unroll
-    for (int t = WD::DST; t < WD::KST; ++t) kb[t] = factor_part<H16>(lr.w, w.h, kj, 16 * t + 8 * h - D, lr.rank, N, 1.f);
+    for (int t = WD::DST; t < WD::KST; ++t)
+      kb[t] = factor_op<H16>(kb[t], fw[t - WD::DST], 1.f);
+  } else {
+#pragma unroll
+    for (int t = 0; t < WD::KST; ++t) kb[t] = make_uint4(0, 0, 0, 0);
+#pragma unroll
+    for (int t = 0; t < WD::DST; ++t) vb[t] = make_uint4(0, 0, 0, 0);
   }
   f32x16_t accv[WD::VT], acck[WD::KT];
 #pragma unroll
@@ -420,7 +472,7 @@ __device__ inline void dkdv_body(const uint16_t* __restrict__ q, const uint16_t*
     for (int e = 0; e < 16; ++e) acck[ct][e] = 0.f;
   __syncthreads();
 
-  // 3. every 32-query block against the wave's 32 keys
+  // 4. every 32-query block against the wave's 32 keys
   const int NB = NP >> 5;
   for (int qb = 0; qb < NB; ++qb) {
     f32x16_t cL, cD;
@@ -483,7 +535,7 @@ __device__ inline void dkdv_body(const uint16_t* __restrict__ q, const uint16_t*
     }
   }
 
-  // 4. dV = accv / g; dk~ = acck ln 2 / tau (the Q^ operand carried log2(e) / sqrt(d)); dW rows
+  // 5. dV = accv / g; dk~ = acck ln 2 / tau (the Q^ operand carried log2(e) / sqrt(d)); dW rows
   //    (the log2(e) U channels) likewise ln 2 / tau; dtheta terms
   float th[D / 4];
 #pragma unroll
@@ -616,13 +668,57 @@ __device__ inline void dq_body(const uint16_t* __restrict__ q, const uint16_t* _
                                const LowRank& lr, float (&fac)[16]) {
   using WD = WDim<D, RK>;
   constexpr int NT = NW * 64;
-  constexpr int IPT = kMaxNW * 8 / NT;
+  constexpr int IPT = 4;  // staged 16-byte items per thread: NP <= 32 NW tokens of 8 items
   const int M = g.M, N = g.N;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int h = lane >> 5, col = lane & 31;
   const float ds_scale = scale_to_2p14(2.f * D * scal[wh * 4] * scal[wh * 4 + 1]);
 
-  // 1. stage the window's rotated K~ (then W) and V rows
+  // 1. every global load first (the staged K, V or W items, then the lane's query), so that their
+  //    latencies overlap; the transforms follow
+  // (as in the dK/dV kernel, the loads of an item are unconditional inside one test)
+  uint4 ra[IPT], rb[IPT];
+  const int64_t tok0 = w.b * g.Hg * g.Wg;  // a grid token of the image: the address of items that are none
+#pragma unroll
+  for (int i = 0; i < IPT; ++i) {
+    const int it = tid + i * NT;
+    const int n = it >> 3, part = it & 7;
+    const bool ok = it < NP * 8 && n < N && (!PAD || token_real(g, w.wy, w.wx, n / M, n % M));
+    const int64_t off = (ok ? token_index(g, w.b, w.wy, w.wx, n / M, n % M) : tok0) * g.xs + w.h * D +
+                        8 * min(part, D / 8 - 1);
+    const uint4* pa = reinterpret_cast<const uint4*>(k + off);
+    const uint4* pb = reinterpret_cast<const uint4*>(v + off);
+    if constexpr (RK > 0) {
+      if (part >= D / 8) {  // a bias part: its eight padded W channels instead
+        pa = factor_row8<RK>(lr.w, w.h, ok ? n : 0, min(8 * part - D, RK - 8), N);
+        pb = pa + 1;
+      }
+    }
+    ra[i] = *pa;
+    rb[i] = *pb;
+  }
+  const int qi = wave * 32 + col;
+  const bool qvalid = qi < N && (!PAD || token_real(g, w.wy, w.wx, qi / M, qi % M));  // a padding query is no query
+  const int qr = qvalid ? qi / M : 0, qc = qvalid ? qi - (qi / M) * M : 0;
+  int64_t qoff = 0;
+  uint4 qb[WD::KST], gb[WD::DST], fu[WD::KST - WD::DST + 1];
+  const int64_t qtok = qvalid ? token_index(g, w.b, w.wy, w.wx, qr, qc) : tok0;
+  qoff = qtok * g.xs + w.h * D;
+  const int64_t goff = qtok * g.os + w.h * D;
+  float lse2 = lse[qtok * g.heads + w.h], del = delta[qtok * g.heads + w.h];
+#pragma unroll
+  for (int t = 0; t < WD::DST; ++t) {
+    qb[t] = *reinterpret_cast<const uint4*>(q + qoff + 16 * t + 8 * h);
+    gb[t] = *reinterpret_cast<const uint4*>(dout + goff + 16 * t + 8 * h);
+  }
+#pragma unroll
+  for (int t = WD::DST; t < WD::KST; ++t) {
+    const uint4* f = factor_row8<RK>(lr.u, w.h, qvalid ? qi : 0, 16 * t + 8 * h - D, N);
+    qb[t] = f[0];
+    fu[t - WD::DST] = f[1];
+  }
+
+  // 2. stage the window's rotated K~ (then W) and V rows
 #pragma unroll
   for (int i = 0; i < IPT; ++i) {
     const int it = tid + i * NT;
@@ -633,11 +729,10 @@ __device__ inline void dq_body(const uint16_t* __restrict__ q, const uint16_t* _
     if (n < N && (!PAD || token_real(g, w.wy, w.wx, n / M, n % M))) {  // padding stays zero, label 0xff
       const int r = n / M, c = n - (n / M) * M;
       if (part < D / 8) {
-        const int64_t off = token_index(g, w.b, w.wy, w.wx, r, c) * g.xs + w.h * D + 8 * part;
-        ko = rot_part<D, H16>(*reinterpret_cast<const uint4*>(k + off), sm.sn, sm.cs, M, r, c, part, 1.f);
-        vo = *reinterpret_cast<const uint4*>(v + off);
+        ko = rot_part<D, H16>(ra[i], sm.sn, sm.cs, M, r, c, part, 1.f);
+        vo = rb[i];
       } else if (part < WD::DK / 8) {
-        ko = factor_part<H16>(lr.w, w.h, n, 8 * part - D, lr.rank, N, 1.f);
+        ko = factor_op<H16>(ra[i], rb[i], 1.f);
       }
       if (part == 0) lb = (uint8_t)token_label(g, w.wy, w.wx, r, c);
     }
@@ -646,34 +741,26 @@ __device__ inline void dq_body(const uint16_t* __restrict__ q, const uint16_t* _
     if (part == 0) sm.lab[n] = lb;
   }
 
-  // 2. the lane's query: Q^' operands, tau dO as bf16 B operands, -LSE and -tau Delta
-  const int qi = wave * 32 + col;
-  const bool qvalid = qi < N && (!PAD || token_real(g, w.wy, w.wx, qi / M, qi % M));  // a padding query is no query
-  const int qr = qvalid ? qi / M : 0, qc = qvalid ? qi - (qi / M) * M : 0;
-  int64_t qoff = 0;
-  uint4 qb[WD::KST], gb[WD::DST];
+  // 3. the lane's query: Q^' operands, tau dO as bf16 B operands, -LSE and -tau Delta
   int qlab = 0xff;
-  float lse2 = 0.f, del = 0.f;
-#pragma unroll
-  for (int t = 0; t < WD::KST; ++t) qb[t] = make_uint4(0, 0, 0, 0);
-#pragma unroll
-  for (int t = 0; t < WD::DST; ++t) gb[t] = make_uint4(0, 0, 0, 0);
   if (qvalid) {
-    const int64_t tok = token_index(g, w.b, w.wy, w.wx, qr, qc);
-    qoff = tok * g.xs + w.h * D;
-    const int64_t goff = tok * g.os + w.h * D;
     qlab = token_label(g, w.wy, w.wx, qr, qc);
-    lse2 = lse[tok * g.heads + w.h] * kLog2e;
-    del = delta[tok * g.heads + w.h] * ds_scale;
+    lse2 *= kLog2e;
+    del *= ds_scale;
 #pragma unroll
     for (int t = 0; t < WD::DST; ++t) {
-      qb[t] = rot_part<D, H16>(*reinterpret_cast<const uint4*>(q + qoff + 16 * t + 8 * h), sm.sn, sm.cs, M, qr, qc,
-                               2 * t + h, WD::kQScale);
-      gb[t] = scaled_part<false>(*reinterpret_cast<const uint4*>(dout + goff + 16 * t + 8 * h), ds_scale);
+      qb[t] = rot_part<D, H16>(qb[t], sm.sn, sm.cs, M, qr, qc, 2 * t + h, WD::kQScale);
+      gb[t] = scaled_part<false>(gb[t], ds_scale);
     }
 #pragma unroll
     for (int t = WD::DST; t < WD::KST; ++t)
-      qb[t] = factor_part<H16>(lr.u, w.h, qi, 16 * t + 8 * h - D, lr.rank, N, kLog2e);
+      qb[t] = factor_op<H16>(qb[t], fu[t - WD::DST], kLog2e);
+  } else {  // a lane without a query: zero operands, reference 0
+    lse2 = del = 0.f;
+#pragma unroll
+    for (int t = 0; t < WD::KST; ++t) qb[t] = make_uint4(0, 0, 0, 0);
+#pragma unroll
+    for (int t = 0; t < WD::DST; ++t) gb[t] = make_uint4(0, 0, 0, 0);
   }
   f32x16_t cL, cD, acc[WD::KT];
 #pragma unroll
@@ -687,7 +774,7 @@ __device__ inline void dq_body(const uint16_t* __restrict__ q, const uint16_t* _
     for (int e = 0; e < 16; ++e) acc[ct][e] = 0.f;
   __syncthreads();
 
-  // 3. every 32-key block against the wave's 32 queries
+  // 4. every 32-key block against the wave's 32 queries
   const int NB = NP >> 5;
   for (int kb = 0; kb < NB; ++kb) {
     const uint16_t* krow = sm.K + (kb * 32 + col) * kRS + 8 * h;
@@ -721,7 +808,7 @@ __device__ inline void dq_body(const uint16_t* __restrict__ q, const uint16_t* _
     }
   }
 
-  // 4. dq~ = acc / tau / sqrt(d); the dtheta integrand takes q~ as the dK product saw it; dU rows
+  // 5. dq~ = acc / tau / sqrt(d); the dtheta integrand takes q~ as the dK product saw it; dU rows
   //    (the W channels) acc / tau
   float th[D / 4];
 #pragma unroll
@@ -824,27 +911,35 @@ hipError_t launch_win(const BwdArgs& a, hipStream_t st) {
   const int64_t ngroups = (nwin + G - 1) / G;
   const int64_t blocks = ngroups * g.heads;
   const int64_t per_group = (int64_t)g.heads * g.N * a.lr.rank;  // entries of one factor
-  // bias workspace: dW partials [ngroups][heads][N][rank], dU partials, then the factor maxima (at the
-  // offset of the float32 kernels' two [windows][heads][N][rank] blocks)
+  // bias workspace: dW partials [ngroups][heads][N][rank], dU partials; from the first 256-byte
+  // boundary past the float32 kernels' two [windows][heads][N][rank] blocks: the padded factors
+  // [heads][N][RK] and the factor maxima
   float* wparts = a.lr_parts;
   float* uparts = RK > 0 ? a.lr_parts + ngroups * per_group : nullptr;
-  float* fmax = RK > 0 ? a.lr_parts + 2 * nwin * per_group : nullptr;
+  float* extra = a.lr_parts + (2 * nwin * per_group + 63) / 64 * 64;
+  LowRank lrp = a.lr;
+  float* fmax = nullptr;
   if constexpr (RK > 0) {
-    hipLaunchKernelGGL(factor_max_kernel, dim3((unsigned)g.heads), dim3(256), 0, st, a.lr.u, a.lr.w,
-                       (int64_t)g.N * a.lr.rank, fmax);
+    float* upad = extra;
+    float* wpad = upad + (int64_t)g.heads * g.N * RK;
+    fmax = wpad + (int64_t)g.heads * g.N * RK;
+    hipLaunchKernelGGL(factor_prep_kernel<RK>, dim3((unsigned)g.heads), dim3(256), 0, st, a.lr.u, a.lr.w, a.lr.rank,
+                       g.N, upad, wpad, fmax);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+    lrp.u = upad;
+    lrp.w = wpad;
   }
   hipLaunchKernelGGL((bwd_dkdv_win_kernel<D, RK, NW, PAD>), dim3((unsigned)blocks), dim3(NW * 64),
                      kv_smem_bytes<D>(NP, g.M, NW), st, (const uint16_t*)a.q, (const uint16_t*)a.k,
                      (const uint16_t*)a.v, (const uint16_t*)a.dout, a.lse, a.delta, a.scal, a.th_row, a.th_col,
-                     (uint16_t*)a.dk, (uint16_t*)a.dv, a.partials, g, NP, a.lr, fmax, wparts, (int)G);
+                     (uint16_t*)a.dk, (uint16_t*)a.dv, a.partials, g, NP, lrp, fmax, wparts, (int)G);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((bwd_dq_win_kernel<D, RK, NW, PAD>), dim3((unsigned)blocks), dim3(NW * 64),
                      q_smem_bytes<D>(NP, g.M, NW), st, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
                      (const uint16_t*)a.dout, a.lse, a.delta, a.scal, a.th_row, a.th_col, (uint16_t*)a.dq, a.partials,
-                     g, NP, a.lr, fmax, uparts, (int)G);
+                     g, NP, lrp, fmax, uparts, (int)G);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   if constexpr (RK > 0) {

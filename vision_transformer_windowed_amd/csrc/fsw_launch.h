@@ -87,10 +87,13 @@ bool bwd_d64_supported(const Geom& g);
 hipError_t launch_bwd_d64(const BwdArgs& a, hipStream_t st);
 // bf16 MFMA backward with a low-rank bias: d == 32, windows of at most 256 tokens, rank <= 32, grids
 // that M divides.  Its workspace needs lowrank_mfma_extra_floats(g) floats after the float32 kernels'
-// two [windows][heads][M*M][rank] blocks.
+// two [windows][heads][M*M][rank] blocks: up to a 256-byte boundary, the factors zero-padded to 32
+// channels, and two maxima per head.
 bool bwd_lowrank_mfma_supported(const Geom& g, int rank);
 hipError_t launch_bwd_lowrank_mfma(const BwdArgs& a, hipStream_t st);
-inline int64_t lowrank_mfma_extra_floats(const Geom& g) { return 2 * (int64_t)g.heads; }
+inline int64_t lowrank_mfma_extra_floats(const Geom& g) {
+  return 64 + 2 * (int64_t)g.heads * g.N * kMaxRank + 2 * (int64_t)g.heads;
+}
 // dtheta partial rows of the whole-window kernels (d == 64, and the low-rank ones).
 int64_t bwd_window_partials(const Geom& g);
 constexpr bool kHaveMfmaBwd = true;

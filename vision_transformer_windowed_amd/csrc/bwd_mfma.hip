@@ -302,22 +302,23 @@ __device__ inline void dq_body(const uint16_t* __restrict__ q, const uint16_t* _
   const float ds_scale = pow2_scale(64.f * scal[wh * 4] * scal[wh * 4 + 1]);
 
   uint4 ik[IPT], iv[IPT];
+  // Branch-free, so that the loads go out in one batch: an item that is none (past the chunk or the
+  // window, or padding) reads a grid token of the image, and its bit in iok stays clear.
+  uint32_t iok = 0;
   auto load_chunk = [&](int c0) {
+    iok = 0;
 #pragma unroll
     for (int i = 0; i < IPT; ++i) {
       const int it = tid + i * NT;
       const int kn = c0 + (it >> 2);
-      ik[i] = make_uint4(0, 0, 0, 0);
-      iv[i] = ik[i];
-      if (it < CH * 4 && kn < N) {
-        int r_, c_;
-        slot_rc(wo, kn, r_, c_);
-        if (!gpad || token_real(g, w.wy, w.wx, r_, c_)) {  // padding stays zero
-          const int64_t off = token_index(g, w.b, w.wy, w.wx, r_, c_) * xs + w.h * D + (it & 3) * 8;
-          ik[i] = *reinterpret_cast<const uint4*>(k + off);
-          iv[i] = *reinterpret_cast<const uint4*>(v + off);
-        }
-      }
+      int r_ = 0, c_ = 0;
+      if (kn < N) slot_rc(wo, kn, r_, c_);
+      const bool ok = it < CH * 4 && kn < N && (!gpad || token_real(g, w.wy, w.wx, r_, c_));
+      iok |= ok ? 1u << i : 0u;
+      const int64_t tok = ok ? token_index(g, w.b, w.wy, w.wx, r_, c_) : w.b * g.Hg * g.Wg;
+      const int64_t off = tok * xs + w.h * D + (it & 3) * 8;
+      ik[i] = *reinterpret_cast<const uint4*>(k + off);
+      iv[i] = *reinterpret_cast<const uint4*>(v + off);
     }
   };
   // In a window split by the shift, chunks holding none of the labels of this workgroup's queries
@@ -333,11 +334,15 @@ __device__ inline void dq_body(const uint16_t* __restrict__ q, const uint16_t* _
   int c0 = next_chunk(0);
   if (c0 < NP) load_chunk(c0);
 
-  // the lane's queries: Q^ operands, tau * dO as bf16 B operands, -LSE and -tau Delta
+  // the lane's queries: Q^ operands, tau * dO as bf16 B operands, -LSE and -tau Delta.  The loads of
+  // every set go out before any is used (branch-free: a lane without a query reads a grid token of the
+  // image and zeroes it), so that their latencies overlap.
   const int qbase = (qblock * NW + wave) * 32 * S + col;
   uint4 qb0[S], qb1[S], gb0[S], gb1[S];
   f32x16_t cL[S], cD[S], acc[S];
-  int qlab[S];
+  int qlab[S], qr[S], qc[S];
+  bool qval[S];
+  float ql[S], qd[S];
   uint32_t wl = 0;
 #pragma unroll
   for (int t = 0; t < S; ++t) {
@@ -348,23 +353,33 @@ __device__ inline void dq_body(const uint16_t* __restrict__ q, const uint16_t* _
       slot_rc(wo, qi, r, c);
       valid = !gpad || token_real(g, w.wy, w.wx, r, c);  // a padding query is no query
     }
-    qlab[t] = valid ? token_label(g, w.wy, w.wx, r, c) : 0xff;
+    qval[t] = valid;
+    qr[t] = r;
+    qc[t] = c;
+    const int64_t tok = valid ? token_index(g, w.b, w.wy, w.wx, r, c) : w.b * g.Hg * g.Wg;
+    const int64_t off = tok * xs + w.h * D, goff = tok * g.os + w.h * D;
+    qb0[t] = *reinterpret_cast<const uint4*>(q + off + 8 * h);
+    qb1[t] = *reinterpret_cast<const uint4*>(q + off + 16 + 8 * h);
+    gb0[t] = *reinterpret_cast<const uint4*>(dout + goff + 8 * h);
+    gb1[t] = *reinterpret_cast<const uint4*>(dout + goff + 16 + 8 * h);
+    ql[t] = lse[tok * g.heads + w.h];
+    qd[t] = delta[tok * g.heads + w.h];
+  }
+#pragma unroll
+  for (int t = 0; t < S; ++t) {
+    const bool valid = qval[t];
+    qlab[t] = valid ? token_label(g, w.wy, w.wx, qr[t], qc[t]) : 0xff;
     wl |= valid ? (1u << qlab[t]) : 0u;
-    qb0[t] = qb1[t] = gb0[t] = gb1[t] = make_uint4(0, 0, 0, 0);
     float lse2 = 0.f, del = 0.f;
     if (valid) {
-      const int64_t tok = token_index(g, w.b, w.wy, w.wx, r, c);
-      const int64_t off = tok * xs + w.h * D, goff = tok * g.os + w.h * D;
-      const uint4 q0 = *reinterpret_cast<const uint4*>(q + off + 8 * h);
-      const uint4 q1 = *reinterpret_cast<const uint4*>(q + off + 16 + 8 * h);
-      const uint4 g0 = *reinterpret_cast<const uint4*>(dout + goff + 8 * h);
-      const uint4 g1 = *reinterpret_cast<const uint4*>(dout + goff + 16 + 8 * h);
-      lse2 = lse[tok * g.heads + w.h] * kLog2e;
-      del = delta[tok * g.heads + w.h] * ds_scale;
-      qb0[t] = rotated_part<H16>(q0, sm.sn, sm.cs, M, r, c, h, kQScale);
-      qb1[t] = rotated_part<H16>(q1, sm.sn, sm.cs, M, r, c, 2 + h, kQScale);
-      gb0[t] = scaled_part<false>(g0, ds_scale);
-      gb1[t] = scaled_part<false>(g1, ds_scale);
+      lse2 = ql[t] * kLog2e;
+      del = qd[t] * ds_scale;
+      qb0[t] = rotated_part<H16>(qb0[t], sm.sn, sm.cs, M, qr[t], qc[t], h, kQScale);
+      qb1[t] = rotated_part<H16>(qb1[t], sm.sn, sm.cs, M, qr[t], qc[t], 2 + h, kQScale);
+      gb0[t] = scaled_part<false>(gb0[t], ds_scale);
+      gb1[t] = scaled_part<false>(gb1[t], ds_scale);
+    } else {
+      qb0[t] = qb1[t] = gb0[t] = gb1[t] = make_uint4(0, 0, 0, 0);
     }
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
@@ -388,14 +403,15 @@ __device__ inline void dq_body(const uint16_t* __restrict__ q, const uint16_t* _
       const int it = tid + i * NT;
       if (it < CH * 4) {
         const int n = it >> 2, part = it & 3, kn = c0 + n;
+        const bool ok = (iok >> i) & 1u;  // padding and slots past the window stay zero
         uint4 kr = make_uint4(0, 0, 0, 0);
-        if (kn < N) {
+        if (ok) {
           int r_, c_;
           slot_rc(wo, kn, r_, c_);
           kr = rotated_part<H16>(ik[i], sm.sn, sm.cs, M, r_, c_, part, 1.f);
         }
         *reinterpret_cast<uint4*>(sm.K + srow(n, part)) = kr;
-        *reinterpret_cast<uint4*>(sm.V + srow(n, part)) = iv[i];
+        *reinterpret_cast<uint4*>(sm.V + srow(n, part)) = ok ? iv[i] : make_uint4(0, 0, 0, 0);
         if (part == 0) sm.lab[n] = chunk_label<PAD>(g, w, wo, kn, sm.blk + buf * (KC / 32), n);
       }
     }
@@ -560,29 +576,25 @@ __device__ inline void dkdv_body(const uint16_t* __restrict__ q, const uint16_t*
 
   uint4 iq[IPT], ig[IPT];
   float il[IPT], id[IPT];
+  // Branch-free, so that the loads go out in one batch: an item that is none (past the chunk or the
+  // window, or padding) reads a grid token of the image, and its bit in iok stays clear; LSE and Delta
+  // are read by every part and kept by part 0.
+  uint32_t iok = 0;
   auto load_chunk = [&](int c0) {
+    iok = 0;
 #pragma unroll
     for (int i = 0; i < IPT; ++i) {
       const int it = tid + i * NT;
       const int qn = c0 + (it >> 2);
-      iq[i] = make_uint4(0, 0, 0, 0);
-      ig[i] = iq[i];
-      il[i] = 0.f;
-      id[i] = 0.f;
-      if (it < CH * 4 && qn < N) {
-        int r_, c_;
-        slot_rc(wo, qn, r_, c_);
-        if (!gpad || token_real(g, w.wy, w.wx, r_, c_)) {  // padding stays zero
-          const int64_t t_ = token_index(g, w.b, w.wy, w.wx, r_, c_);
-          const int64_t off = t_ * xs + w.h * D + (it & 3) * 8;
-          iq[i] = *reinterpret_cast<const uint4*>(q + off);
-          ig[i] = *reinterpret_cast<const uint4*>(dout + t_ * g.os + w.h * D + (it & 3) * 8);
-          if ((it & 3) == 0) {
-            il[i] = lse[t_ * g.heads + w.h];
-            id[i] = delta[t_ * g.heads + w.h];
-          }
-        }
-      }
+      int r_ = 0, c_ = 0;
+      if (qn < N) slot_rc(wo, qn, r_, c_);
+      const bool ok = it < CH * 4 && qn < N && (!gpad || token_real(g, w.wy, w.wx, r_, c_));
+      iok |= ok ? 1u << i : 0u;
+      const int64_t t_ = ok ? token_index(g, w.b, w.wy, w.wx, r_, c_) : w.b * g.Hg * g.Wg;
+      iq[i] = *reinterpret_cast<const uint4*>(q + t_ * xs + w.h * D + (it & 3) * 8);
+      ig[i] = *reinterpret_cast<const uint4*>(dout + t_ * g.os + w.h * D + (it & 3) * 8);
+      il[i] = lse[t_ * g.heads + w.h];
+      id[i] = delta[t_ * g.heads + w.h];
     }
   };
   // In a window split by the shift, chunks holding none of the labels of this workgroup's keys are
@@ -598,11 +610,14 @@ __device__ inline void dkdv_body(const uint16_t* __restrict__ q, const uint16_t*
   int c0 = next_chunk(0);
   if (c0 < NP) load_chunk(c0);
 
-  // the lane's keys (one per set): K~ operands, tau * V as bf16 B operands
+  // the lane's keys (one per set): K~ operands, tau * V as bf16 B operands.  The loads of every set
+  // go out before any is used (branch-free: a lane without a key reads a grid token of the image and
+  // zeroes it), so that their latencies overlap.
   const int kbase = (kblock * NW + wave) * 32 * S + col;
   uint4 kb0[S], kb1[S], vb0[S], vb1[S];
   f32x16_t accv[S], acck[S];
-  int klab[S];
+  int klab[S], kr[S], kc[S];
+  bool kval[S];
   uint32_t wl = 0;
 #pragma unroll
   for (int t = 0; t < S; ++t) {
@@ -613,19 +628,27 @@ __device__ inline void dkdv_body(const uint16_t* __restrict__ q, const uint16_t*
       slot_rc(wo, kj, r, c);
       valid = !gpad || token_real(g, w.wy, w.wx, r, c);  // a padding key is no key
     }
-    klab[t] = valid ? token_label(g, w.wy, w.wx, r, c) : 0xff;
+    kval[t] = valid;
+    kr[t] = r;
+    kc[t] = c;
+    const int64_t off = (valid ? token_index(g, w.b, w.wy, w.wx, r, c) : w.b * g.Hg * g.Wg) * xs + w.h * D;
+    kb0[t] = *reinterpret_cast<const uint4*>(k + off + 8 * h);
+    kb1[t] = *reinterpret_cast<const uint4*>(k + off + 16 + 8 * h);
+    vb0[t] = *reinterpret_cast<const uint4*>(v + off + 8 * h);
+    vb1[t] = *reinterpret_cast<const uint4*>(v + off + 16 + 8 * h);
+  }
+#pragma unroll
+  for (int t = 0; t < S; ++t) {
+    const bool valid = kval[t];
+    klab[t] = valid ? token_label(g, w.wy, w.wx, kr[t], kc[t]) : 0xff;
     wl |= valid ? (1u << klab[t]) : 0u;
-    kb0[t] = kb1[t] = vb0[t] = vb1[t] = make_uint4(0, 0, 0, 0);
     if (valid) {
-      const int64_t off = token_index(g, w.b, w.wy, w.wx, r, c) * xs + w.h * D;
-      const uint4 k0 = *reinterpret_cast<const uint4*>(k + off + 8 * h);
-      const uint4 k1 = *reinterpret_cast<const uint4*>(k + off + 16 + 8 * h);
-      const uint4 v0 = *reinterpret_cast<const uint4*>(v + off + 8 * h);
-      const uint4 v1 = *reinterpret_cast<const uint4*>(v + off + 16 + 8 * h);
-      kb0[t] = rotated_part<H16>(k0, sm.sn, sm.cs, M, r, c, h, 1.f);
-      kb1[t] = rotated_part<H16>(k1, sm.sn, sm.cs, M, r, c, 2 + h, 1.f);
-      vb0[t] = scaled_part<false>(v0, ds_scale);
-      vb1[t] = scaled_part<false>(v1, ds_scale);
+      kb0[t] = rotated_part<H16>(kb0[t], sm.sn, sm.cs, M, kr[t], kc[t], h, 1.f);
+      kb1[t] = rotated_part<H16>(kb1[t], sm.sn, sm.cs, M, kr[t], kc[t], 2 + h, 1.f);
+      vb0[t] = scaled_part<false>(vb0[t], ds_scale);
+      vb1[t] = scaled_part<false>(vb1[t], ds_scale);
+    } else {
+      kb0[t] = kb1[t] = vb0[t] = vb1[t] = make_uint4(0, 0, 0, 0);
     }
 #pragma unroll
     for (int e = 0; e < 16; ++e) accv[t][e] = acck[t][e] = 0.f;
@@ -645,18 +668,20 @@ __device__ inline void dkdv_body(const uint16_t* __restrict__ q, const uint16_t*
       const int it = tid + i * NT;
       if (it < CH * 4) {
         const int n = it >> 2, part = it & 3, qn = c0 + n;
+        const bool ok = (iok >> i) & 1u;  // padding and slots past the window stay zero
         uint4 qr = make_uint4(0, 0, 0, 0);
-        if (qn < N) {
+        if (ok) {
           int r_, c_;
           slot_rc(wo, qn, r_, c_);
           qr = rotated_part<H16>(iq[i], sm.sn, sm.cs, M, r_, c_, part, kQScale);
         }
+        const uint4 gr = ok ? ig[i] : make_uint4(0, 0, 0, 0);
         *reinterpret_cast<uint4*>(sm.Q + srow(n, part)) = qr;
-        *reinterpret_cast<uint4*>(sm.G + srow(n, part)) = ig[i];
-        *reinterpret_cast<uint4*>(sm.Gs + srow(n, part)) = scaled_part<H16>(ig[i], g_scale);
+        *reinterpret_cast<uint4*>(sm.G + srow(n, part)) = gr;
+        *reinterpret_cast<uint4*>(sm.Gs + srow(n, part)) = scaled_part<H16>(gr, g_scale);
         if (part == 0) {
-          sm.L[n] = -il[i] * kLog2e;
-          sm.Dl[n] = -id[i] * ds_scale;
+          sm.L[n] = ok ? -il[i] * kLog2e : 0.f;
+          sm.Dl[n] = ok ? -id[i] * ds_scale : 0.f;
           sm.lab[n] = chunk_label<PAD>(g, w, wo, qn, sm.blk + buf * (KC / 32), n);
         }
       }

@@ -208,6 +208,9 @@ def config_timing(dev, name, shift, passes, steps, warmup):
     return res
 
 
+LOWRANK_SEED = 2024  # factors of the rank-16 bias line (inputs.lowrank_factors)
+
+
 def lowrank_step(dev, steps, warmup, rank=16):
     """Forward and backward with a rank-16 additive bias (factors U, W [heads, M*M, 16], N(0, 0.5^2)) on
     the M = 16 stage-1 workload at s = 0, beside the same calls without the bias.  FLOP conventions: the
@@ -215,15 +218,13 @@ def lowrank_step(dev, steps, warmup, rank=16):
     10 N^2 d + 6 N^2 r (S recomputed with the r channels, dU = dS W and dW = dS^T U)."""
     import torch
     import vision_transformer_windowed_amd as F
-    from vision_transformer_windowed_amd.inputs import WORKLOADS, workload_inputs
+    from vision_transformer_windowed_amd.inputs import WORKLOADS, lowrank_factors, workload_inputs
     name = "flashswin_t_s1_p2_m16"
     w = WORKLOADS[name]
     M, d = w["M"], w["d"]
     x = {k: v.to(dev) for k, v in workload_inputs(name, with_dout=True).items()}
     q, k, v, tr, tc, dout = x["q"], x["k"], x["v"], x["theta_row"], x["theta_col"], x["dout"]
-    g = torch.Generator().manual_seed(2024)
-    U = (torch.randn((w["heads"], M * M, rank), generator=g) * 0.5).to(dev)
-    W = (torch.randn((w["heads"], M * M, rank), generator=g) * 0.5).to(dev)
+    U, W = (t.to(dev) for t in lowrank_factors(w["heads"], M, rank, seed=LOWRANK_SEED))
     out = torch.empty_like(q)
     lse = torch.empty(q.shape[:4], device=dev, dtype=torch.float32)
     ws = torch.empty(max(F.flashswin_wattn_bwd_lowrank_workspace_size(*q.shape, M, 0, F.FSW_BF16, rank), 1),

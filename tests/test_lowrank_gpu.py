@@ -18,7 +18,7 @@ import torch
 
 import oracle
 import vision_transformer_windowed_amd as F
-from vision_transformer_windowed_amd.inputs import make_inputs
+from vision_transformer_windowed_amd.inputs import WORKLOADS, lowrank_factors, make_inputs, workload_inputs
 
 pytestmark = pytest.mark.gpu
 
@@ -184,3 +184,51 @@ def test_lowrank_large_bias_falls_back():
     ro, rl = oracle.wattn_fwd_ref(q, k, v, tr, tc, M, s, lowrank=(U.double().numpy(), W.double().numpy()))
     _close("O", _np(out), ro, 2e-2, 5e-3)
     _close("LSE", _np(lse), rl, 2e-2, 5e-3)
+
+
+def test_lowrank_workload():
+    """The rank-16 bias at the size and launch configuration the benchmark times (flashswin_t_s1_p2_m16:
+    128 images of 128 x 128 tokens, 3 heads, M = 16, s = 0; the benchmark's factors, seed 2024; the
+    MFMA backward walks 8 windows per workgroup): the forward on sampled images; the backward's dq, dk,
+    dv of every image and its full-batch dtheta, dU and dW, against the oracle run over the batch in
+    chunks of 16 images (windows never cross images; dtheta, dU and dW are sums over the chunks)."""
+    name, rank, seed = "flashswin_t_s1_p2_m16", 16, 2024
+    w = WORKLOADS[name]
+    B, M = w["B"], w["M"]
+    x = workload_inputs(name, with_dout=True)
+    U, W = lowrank_factors(w["heads"], M, rank, seed)
+    xd = {n: t.to(DEV) for n, t in x.items()}
+    out, lse = F.wattn_fwd_lowrank(xd["q"], xd["k"], xd["v"], xd["theta_row"], xd["theta_col"], U.to(DEV),
+                                   W.to(DEV), M, 0)
+    grads = F.wattn_bwd_lowrank(xd["q"], xd["k"], xd["v"], out, xd["dout"], lse, xd["theta_row"], xd["theta_col"],
+                                U.to(DEV), W.to(DEV), M, 0)
+    torch.cuda.synchronize()
+    tr, tc = x["theta_row"].double().numpy(), x["theta_col"].double().numpy()
+    lr = (U.double().numpy(), W.double().numpy())
+    imgs = [0, B - 1]
+    q, k, v = (x[n][imgs].double().numpy() for n in ("q", "k", "v"))
+    ro, rl = oracle.wattn_fwd_ref(q, k, v, tr, tc, M, 0, lowrank=lr)
+    _close("O (images 0, B-1)", _np(out[imgs]), ro, 2e-2, 5e-3, bf16_store=True)
+    _close("LSE (images 0, B-1)", _np(lse[imgs]), rl, 2e-2, 5e-3)
+    worst = {n: 0.0 for n in ("dQ", "dK", "dV")}
+    sq = {n: [0.0, 0.0] for n in worst}
+    sums = [np.zeros(tr.shape), np.zeros(tc.shape), np.zeros(lr[0].shape), np.zeros(lr[1].shape)]
+    for b0 in range(0, B, 16):
+        sl = slice(b0, b0 + 16)
+        q, k, v, do = (x[n][sl].double().numpy() for n in ("q", "k", "v", "dout"))
+        g = oracle.wattn_bwd_ref(q, k, v, do, tr, tc, M, 0, lowrank=lr)
+        for name_, ref, t in zip(("dQ", "dK", "dV"), g[:3], grads[:3]):
+            mine = _np(t[sl])
+            assert np.all(np.isfinite(mine)), name_
+            worst[name_] = max(worst[name_], float((np.abs(mine - ref) / (2e-2 + 2.0 ** -8 * np.abs(ref))).max()))
+            sq[name_][0] += float(((mine - ref) ** 2).sum())
+            sq[name_][1] += float((ref ** 2).sum())
+        for acc, part in zip(sums, g[3:]):
+            acc += part
+    for name_ in worst:
+        l2 = (sq[name_][0] / sq[name_][1]) ** 0.5
+        print(f"  {name_} (all {B} images): worst err / (2e-2 + 2^-8 |ref|) {worst[name_]:.3f}, rel-L2 {l2:.3e}",
+              flush=True)
+        assert worst[name_] <= 1.0 and l2 <= 5e-3, name_
+    for name_, got, ref in zip(("dtheta_row", "dtheta_col", "dU", "dW"), grads[3:], sums):
+        _close(f"{name_} (all {B} images)", _np(got), ref, 2e-2, 5e-3, scale_abs=True)

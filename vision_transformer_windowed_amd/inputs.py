@@ -11,6 +11,8 @@ from the geometric schedule 10000^(-2i/(d/2)), i < d/4, used as the
 initialisation in the FlashSwin paper card's Figure S4, plus that noise.
 `make_device_inputs` draws Q, K, V, dO the same way from a generator on the GPU
 itself, for tensors too large to draw on the host (theta as above).
+`lowrank_factors` draws the two factors of a rank-r additive bias, U then W
+[heads, M*M, r] ~ N(0, 0.5^2) in float32, from a CPU generator seeded with `seed`.
 """
 
 import torch
@@ -77,3 +79,10 @@ def workload_inputs(name, with_dout=None, batch=None):
     B = w["B"] if batch is None else batch
     wd = (w["kind"] == "bwd") if with_dout is None else with_dout
     return make_inputs(B, w["Hg"], w["Wg"], w["heads"], w["d"], w["dtype"], w["seed"], with_dout=wd)
+
+
+def lowrank_factors(heads, M, rank, seed):
+    """Factors U, W [heads, M*M, rank] of a rank-r additive bias, N(0, 0.5^2) float32 CPU tensors."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(int(seed))
+    return (torch.randn((heads, M * M, rank), generator=g) * 0.5, torch.randn((heads, M * M, rank), generator=g) * 0.5)

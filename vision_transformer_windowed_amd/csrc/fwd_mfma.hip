@@ -333,13 +333,60 @@ __device__ __forceinline__ float stage_k(const FwdSmem& sm, const uint4 (&kraw)[
   return kmax2;
 }
 
-// The W factor rows of the staged keys into channels D .. D + RK of their K~ rows (zero past the rank
-// and past the window), in fp16 (h16) or bf16; returns this thread's largest |W[n]|^2 (the key norms
-// that bound the scores add it to the largest |k~|^2).  Item it: 8-channel part it % (RK/8) of slot
-// it / (RK/8); the slot's in-window position n = r*M + c indexes the factor.
-template <int D, int RK>
-__device__ inline float stage_w(const FwdSmem& sm, const LowRank& lr, int head, int M, bool split, int NP, int tid,
+// Raw W factor values of the thread's staged items (item it = tid + i nt: 8-channel part it % (RK/8)
+// of slot it / (RK/8); the slot's in-window position n = r*M + c indexes the factor).  The loads are
+// unconditional (slot and channel clamped into the factor), so they go out in one batch with the K
+// and V loads; stage_w zeroes what lies past the rank or the window.
+template <int RK, int WIT>
+__device__ __forceinline__ void load_w(const FwdSmem& sm, const LowRank& lr, int head, int M, bool split, int NP,
+                                       int tid, int nt, float (&wr)[WIT][8]) {
+  constexpr int WP = RK / 8;
+  const int N = M * M;
+#pragma unroll
+  for (int i = 0; i < WIT; ++i) {
+    const int it = tid + i * nt;
+    const int key = it < NP * WP && it / WP < N ? it / WP : 0, part = it % WP;
+    const int rc = split ? (int)sm.rc[key] : (key / M) << 8 | (key - (key / M) * M);
+    const float* wrow = lr.w + ((int64_t)head * N + (rc >> 8) * M + (rc & 255)) * lr.rank;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) wr[i][e] = wrow[min(part * 8 + e, lr.rank - 1)];
+  }
+}
+
+// The W factor rows of the staged keys (load_w) into channels D .. D + RK of their K~ rows (zero past
+// the rank and past the window), in fp16 (h16) or bf16; returns this thread's largest |W[n]|^2 (the key
+// norms that bound the scores add it to the largest |k~|^2).
+template <int D, int RK, int WIT>
+__device__ inline float stage_w(const FwdSmem& sm, const float (&wr)[WIT][8], int rank, int M, int NP, int tid,
                                 int nt, bool h16) {
+  constexpr int WP = RK / 8;
+  const int N = M * M;
+  float wmax2 = 0.f;
+#pragma unroll
+  for (int i = 0; i < WIT; ++i) {
+    const int it = tid + i * nt;
+    if (it >= NP * WP) break;  // uniform across a wave: NP * WP is a multiple of 64
+    const int key = it / WP, part = it % WP;
+    float x[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = key < N && part * 8 + e < rank ? wr[i][e] : 0.f;
+    float ss = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ss += x[e] * x[e];
+    // the WP parts of a slot are consecutive lanes
+#pragma unroll
+    for (int o = 1; o < WP; o <<= 1) ss += __shfl_xor(ss, o, 64);
+    wmax2 = fmaxf(wmax2, ss);
+    *reinterpret_cast<uint4*>(sm.K + (size_t)key * FwdDim<D, RK>::KS + D + part * 8) = pack8_op(x, h16);
+  }
+  return wmax2;
+}
+
+// stage_w for the run-time-M instances, whose registers the batched loads would overflow: each item's
+// W channels loaded as it is staged (zero past the rank and past the window).
+template <int D, int RK>
+__device__ inline float stage_w_direct(const FwdSmem& sm, const LowRank& lr, int head, int M, bool split, int NP,
+                                       int tid, int nt, bool h16) {
   constexpr int WP = RK / 8;
   const int N = M * M;
   float wmax2 = 0.f;
@@ -367,10 +414,21 @@ __device__ inline float stage_w(const FwdSmem& sm, const LowRank& lr, int head, 
   return wmax2;
 }
 
-// The lane's bias channels of query slot rc (r << 8 | c): log2(e) U[n] for channels 16t + 8h + e,
-// t < RK / 16, e < 8 (zero past the rank), into u[8t + e].
+// Raw U factor values of the lane's bias channels 16t + 8h + e (t < RK / 16, e < 8) of query slot rc
+// (r << 8 | c), into u[8t + e]: unconditional loads (channel clamped into the rank); u_val masks them.
 template <int RK>
 __device__ __forceinline__ void load_u(const LowRank& lr, int head, int N, int rc, int M, int h, float (&u)[RK / 2]) {
+  const float* urow = lr.u + ((int64_t)head * N + (rc >> 8) * M + (rc & 255)) * lr.rank;
+#pragma unroll
+  for (int t = 0; t < RK / 16; ++t)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) u[8 * t + e] = urow[min(16 * t + 8 * h + e, lr.rank - 1)];
+}
+// load_u for the run-time-M instances: log2(e) U[n] of the lane's channels 16t + 8h + e, each loaded
+// only when within the rank (zero past it), into u[8t + e].
+template <int RK>
+__device__ __forceinline__ void load_u_direct(const LowRank& lr, int head, int N, int rc, int M, int h,
+                                              float (&u)[RK / 2]) {
   const float* urow = lr.u + ((int64_t)head * N + (rc >> 8) * M + (rc & 255)) * lr.rank;
 #pragma unroll
   for (int t = 0; t < RK / 16; ++t)
@@ -379,6 +437,11 @@ __device__ __forceinline__ void load_u(const LowRank& lr, int head, int N, int r
       const int ch = 16 * t + 8 * h + e;
       u[8 * t + e] = ch < lr.rank ? urow[ch] * kLog2e : 0.f;
     }
+}
+// log2(e) U of bias channel 16t + 8h + e (zero past the rank) from load_u's values.
+template <int RK>
+__device__ __forceinline__ float u_val(const float (&u)[RK / 2], int t, int e, int h, int rank) {
+  return 16 * t + 8 * h + e < rank ? u[8 * t + e] * kLog2e : 0.f;
 }
 
 // Global loads of the thread's K and V items (16 bytes each), issued together.
@@ -509,6 +572,24 @@ __global__ __launch_bounds__(NWAVES * 64, (fwd_min_waves<NWAVES, D>())) void fwd
   uint4 qraw[QBM][Dim::DSTEPS];
 #pragma unroll
   for (int qb = 0; qb < QBM; ++qb) load_q(qb, qraw[qb]);
+  // The bias factors of the staged keys and of the queries: with the window size fixed at compile
+  // time, in the same batch (kEarly); in the run-time-M instances, whose registers that would
+  // overflow, each in a batch of its own right before its use.
+  constexpr bool kEarly = MT > 0;
+  constexpr int WIT = RK > 0 ? (NPMAX * (RK / 8) + NT - 1) / NT : 1;
+  float wraw[WIT][8];
+  float uraw[kEarly ? QBM : 1][RK > 0 ? RK / 2 : 1];
+  // the lane's query slot of block qb (r << 8 | c), 0 past the window
+  auto q_rc = [&](int qb) {
+    const int qi = (qoff + qb) * NT / 2 + wave * 32 + col;
+    if (!(qb < nqw && qi < N)) return 0;
+    return split ? (int)sm.rc[qi] : (qi / M) << 8 | (qi - (qi / M) * M);
+  };
+  if constexpr (RK > 0 && kEarly) {
+    load_w<RK, WIT>(sm, lr, w.h, M, split, NP, tid, NT, wraw);
+#pragma unroll
+    for (int qb = 0; qb < QBM; ++qb) load_u<RK>(lr, w.h, N, q_rc(qb), M, h, uraw[qb]);
+  }
 
   // 2. RoPE sin/cos table (while the loads are in flight)
   constexpr int P4 = Dim::P4;
@@ -526,7 +607,12 @@ __global__ __launch_bounds__(NWAVES * 64, (fwd_min_waves<NWAVES, D>())) void fwd
 
   // 3. K~ rows (rotated, fp16), V rows, block label summaries, norms
   float kmax2 = stage_k<MAXIT, D, RK>(sm, kraw, M, split, NP, tid, NT, true);
-  if constexpr (RK > 0) kmax2 += stage_w<D, RK>(sm, lr, w.h, M, split, NP, tid, NT, true);
+  if constexpr (RK > 0) {
+    if constexpr (kEarly)
+      kmax2 += stage_w<D, RK, WIT>(sm, wraw, lr.rank, M, NP, tid, NT, true);
+    else
+      kmax2 += stage_w_direct<D, RK>(sm, lr, w.h, M, split, NP, tid, NT, true);
+  }
 #pragma unroll
   for (int i = 0; i < MAXIT; ++i) {
     const int it = tid + i * NT;
@@ -556,10 +642,20 @@ __global__ __launch_bounds__(NWAVES * 64, (fwd_min_waves<NWAVES, D>())) void fwd
       qn2 *= qscale * qscale;
       const int qi = (qoff + qb) * NT / 2 + wave * 32 + col;
       if (qb < nqw && qi < N) {
-        float u[RK / 2];
-        load_u<RK>(lr, w.h, N, split ? (int)sm.rc[qi] : (qi / M) << 8 | (qi - (qi / M) * M), M, h, u);
+        if constexpr (kEarly) {
 #pragma unroll
-        for (int e = 0; e < RK / 2; ++e) qn2 += u[e] * u[e];
+          for (int t = 0; t < RK / 16; ++t)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const float u = u_val<RK>(uraw[kEarly ? qb : 0], t, e, h, lr.rank);
+              qn2 += u * u;
+            }
+        } else {
+          float u[RK / 2];
+          load_u_direct<RK>(lr, w.h, N, q_rc(qb), M, h, u);
+#pragma unroll
+          for (int e = 0; e < RK / 2; ++e) qn2 += u[e] * u[e];
+        }
       }
       qn2max[qb] = wave_max(halves_sum(qn2));
     } else {
@@ -588,7 +684,12 @@ __global__ __launch_bounds__(NWAVES * 64, (fwd_min_waves<NWAVES, D>())) void fwd
     load_kv<MAXIT, D>(k, v, g, w, split ? sm.rc : nullptr, M, NP, tid, NT, false, pad, kraw, vraw);
     __syncthreads();
     stage_k<MAXIT, D, RK>(sm, kraw, M, split, NP, tid, NT, false);
-    if constexpr (RK > 0) stage_w<D, RK>(sm, lr, w.h, M, split, NP, tid, NT, false);
+    if constexpr (RK > 0 && kEarly) {
+      load_w<RK, WIT>(sm, lr, w.h, M, split, NP, tid, NT, wraw);
+      stage_w<D, RK, WIT>(sm, wraw, lr.rank, M, NP, tid, NT, false);
+    } else if constexpr (RK > 0) {
+      stage_w_direct<D, RK>(sm, lr, w.h, M, split, NP, tid, NT, false);
+    }
     __syncthreads();
   }
 #pragma unroll
@@ -615,15 +716,18 @@ __global__ __launch_bounds__(NWAVES * 64, (fwd_min_waves<NWAVES, D>())) void fwd
       qop[t] = pack8_op(x, h16);
     }
     if constexpr (RK > 0) {  // the bias channels: log2(e) U[n_q], lane h holding 8h.. of each 16
-      float u[RK / 2];
+      float ul[RK / 2];
 #pragma unroll
-      for (int e = 0; e < RK / 2; ++e) u[e] = 0.f;
-      if (qvalid) load_u<RK>(lr, w.h, N, qrc, M, h, u);
+      for (int e = 0; e < RK / 2; ++e) ul[e] = 0.f;
+      if constexpr (!kEarly) {
+        if (qvalid) load_u_direct<RK>(lr, w.h, N, qrc, M, h, ul);
+      }
 #pragma unroll
       for (int t = 0; t < RK / 16; ++t) {
         float x[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) x[e] = u[8 * t + e];
+        for (int e = 0; e < 8; ++e)
+          x[e] = kEarly ? (qvalid ? u_val<RK>(uraw[kEarly ? qb : 0], t, e, h, lr.rank) : 0.f) : ul[8 * t + e];
         qop[Dim::DSTEPS + t] = pack8_op(x, h16);
       }
     }
@@ -656,7 +760,10 @@ __global__ __launch_bounds__(NWAVES * 64, (fwd_min_waves<NWAVES, D>())) void fwd
       attend<false, D, RK>(sm, NB, lane, run, kb0, kb1, wave_labels, wave_single, qop, qlab, qvalid, bound, ref, l, o);
 
     // the next block's query loads go out before this block's epilogue
-    if (qb + 1 < QBM) load_q(qb + 1, qraw[qb + 1]);  // zeros past the last block
+    if (qb + 1 < QBM) {
+      load_q(qb + 1, qraw[qb + 1]);  // zeros past the last block
+      if constexpr (RK > 0 && kEarly) load_u<RK>(lr, w.h, N, q_rc(qb + 1), M, h, uraw[qb + 1]);
+    }
     // 5. epilogue: O = O^T / l (lane: query col, channels 32t + 8g + 4h + j), LSE = (ref + log2 l) ln 2
     const float lt = halves_sum(l);
     if (qvalid) {

@@ -69,6 +69,10 @@ CASES = [
     (15, 24, 24, 16, 32, 8, 3, 16, "bf16"),
     (31, 24, 24, 30, 32, 8, 5, 24, "bf16"),
     (2, 64, 64, 3, 32, 16, 8, 16, "bf16"),
+    # M = 16 (the forward instances that load the factors with K, V and Q): ranks that leave part of
+    # an 8-channel group or of the second 16-channel step empty
+    (1, 32, 32, 2, 32, 16, 8, 20, "bf16"),
+    (1, 48, 32, 1, 32, 16, 0, 9, "bf16"),
 ]
 
 

@@ -4,7 +4,9 @@
 Workload (default): FlashSwin-T stage 1 with p=2, M=32: q/k/v/dO [128, 128, 128, 3, 32] bf16,
 no shift, seeded synthetic N(0,1) inputs (no dataset), RoPE theta from the geometric schedule plus
 N(0, 0.01^2) noise.  One step = the whole hot path over the batch: the forward (RoPE, exact-softmax
-attention, LSE) then the backward (Delta, recomputed P, dQ/dK/dV, dtheta).  FLOPs per window-head:
+attention, LSE, and a 16-byte operand summary per window-head) then the backward (Delta, recomputed P,
+dQ/dK/dV, dtheta; its prologue reads O and dO and takes the q/k/v maxima from the summary, as the
+autograd wrapper does).  FLOPs per window-head:
 4 N^2 d forward + 10 N^2 d backward (N = M^2), the dense convention of the workload's metric.
 
 Prints ONE JSON line.  `roofline` describes the forward kernel of the workload (one launch of
@@ -169,13 +171,16 @@ def config_timing(dev, name, shift, passes, steps, warmup):
     q, k, v, tr, tc = x["q"], x["k"], x["v"], x["theta_row"], x["theta_col"]
     out = torch.empty_like(q)
     lse = torch.empty(q.shape[:4], device=dev, dtype=torch.float32)
-    fns = {"fwd": lambda: F.wattn_fwd(q, k, v, tr, tc, M, shift, out=out, lse=lse)}
+    # with a backward, the forward also writes the operand summary the backward's prologue takes
+    stats = F.new_stats(q, M, shift) if "bwd" in passes else None
+    fns = {"fwd": lambda: F.wattn_fwd(q, k, v, tr, tc, M, shift, out=out, lse=lse, stats=stats)}
     if "bwd" in passes:
         dout = x["dout"]
         grads = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v), torch.empty_like(tr),
                  torch.empty_like(tc))
         ws = torch.empty(max(F.bwd_workspace_bytes(q, M, shift), 1), device=dev, dtype=torch.uint8)
-        fns["bwd"] = lambda: F.wattn_bwd(q, k, v, out, dout, lse, tr, tc, M, shift, workspace=ws, grads=grads)
+        fns["bwd"] = lambda: F.wattn_bwd(q, k, v, out, dout, lse, tr, tc, M, shift, workspace=ws, grads=grads,
+                                         stats=stats)
         fns["fwd"]()  # out and lse for the backward
     stream = torch.cuda.current_stream(dev)
     N = M * M
@@ -229,8 +234,9 @@ def lowrank_step(dev, steps, warmup, rank=16):
     lse = torch.empty(q.shape[:4], device=dev, dtype=torch.float32)
     ws = torch.empty(max(F.flashswin_wattn_bwd_lowrank_workspace_size(*q.shape, M, 0, F.FSW_BF16, rank), 1),
                      device=dev, dtype=torch.uint8)
-    fns = {"fwd": lambda: F.wattn_fwd_lowrank(q, k, v, tr, tc, U, W, M, 0, out=out, lse=lse),
-           "bwd": lambda: F.wattn_bwd_lowrank(q, k, v, out, dout, lse, tr, tc, U, W, M, 0, workspace=ws)}
+    stats = F.new_stats(q, M, 0)
+    fns = {"fwd": lambda: F.wattn_fwd_lowrank(q, k, v, tr, tc, U, W, M, 0, out=out, lse=lse, stats=stats),
+           "bwd": lambda: F.wattn_bwd_lowrank(q, k, v, out, dout, lse, tr, tc, U, W, M, 0, workspace=ws, stats=stats)}
     fns["fwd"]()
     stream = torch.cuda.current_stream(dev)
     N = M * M
@@ -400,12 +406,14 @@ def main():
     grads = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v), torch.empty_like(tr),
              torch.empty_like(tc))
     ws = torch.empty(max(F.bwd_workspace_bytes(q, M, shift), 1), device=dev, dtype=torch.uint8)
+    # the forward's operand summary (16 bytes per window-head): the backward's prologue reads O and dO only
+    stats = F.new_stats(q, M, shift)
 
     def fwd():
-        F.wattn_fwd(q, k, v, tr, tc, M, shift, out=out, lse=lse)
+        F.wattn_fwd(q, k, v, tr, tc, M, shift, out=out, lse=lse, stats=stats)
 
     def bwd():
-        F.wattn_bwd(q, k, v, out, dout, lse, tr, tc, M, shift, workspace=ws, grads=grads)
+        F.wattn_bwd(q, k, v, out, dout, lse, tr, tc, M, shift, workspace=ws, grads=grads, stats=stats)
 
     fwd()  # the backward needs a valid LSE even in --only bwd mode
     for _ in range(args.warmup):

@@ -259,6 +259,66 @@ int flashswin_wattn_fwd_materialized(const void* q, const void* k, const void* v
                                      int64_t B, int64_t Hg, int64_t Wg, int heads, int d,
                                      int M, int shift, int dtype, void* hip_stream);
 
+/*
+ * Bytes of the operand summary of flashswin_wattn_fwd_stats / _bwd_stats: 16 per window-head,
+ * B * ceil(Hg/M) * ceil(Wg/M) * heads * 16.  0 for arguments those calls would reject.
+ */
+size_t flashswin_wattn_stats_bytes(int64_t B, int64_t Hg, int64_t Wg, int heads, int d, int M,
+                                   int shift, int dtype);
+
+/*
+ * The forward of flashswin_wattn_fwd (rank == 0) or of flashswin_wattn_fwd_lowrank (rank >= 1, same
+ * factor rules), which also writes a per-window-head summary of its inputs for
+ * flashswin_wattn_bwd_stats: the same attention ([FS] Abstract: fused window attention, recomputed in
+ * the backward from the saved log-sum-exp), with no change to out or lse.
+ *
+ *   bias_u, bias_w, rank  as in flashswin_wattn_fwd_lowrank; rank == 0: no bias (bias_u and bias_w are
+ *                not read and may be NULL).
+ *   stats        device, float32, flashswin_wattn_stats_bytes() bytes, 4-byte aligned, overwritten:
+ *                per window-head (window-major, heads fastest) four values that summarize the largest
+ *                |component| of that window's q, k and v rows of the head.  The content is private to
+ *                this library version; pass it unchanged to flashswin_wattn_bwd_stats with the same
+ *                q, k and v.  Written for dtype FSW_BF16 with d 32 or 64 (the shapes whose backward
+ *                reads it); left unwritten otherwise.
+ *   Every other argument as in flashswin_wattn_fwd; stats may not share a byte with an input, out
+ *   or lse.  The MFMA forward computes the summary from the rows it already holds (no extra reads);
+ *   the other forward kernels are followed by one pass over q, k and v.
+ * Returns FSW_OK, FSW_ERR_INVALID_ARG, FSW_ERR_UNSUPPORTED or FSW_ERR_HIP.
+ */
+int flashswin_wattn_fwd_stats(const void* q, const void* k, const void* v,
+                              const float* theta_row, const float* theta_col,
+                              const float* bias_u, const float* bias_w, int rank,
+                              void* out, float* lse, float* stats,
+                              int64_t B, int64_t Hg, int64_t Wg, int heads, int d,
+                              int M, int shift, int dtype, void* hip_stream);
+
+/*
+ * The backward of flashswin_wattn_bwd (rank == 0) or of flashswin_wattn_bwd_lowrank (rank >= 1) with
+ * the summary of flashswin_wattn_fwd_stats: the prologue that computes Delta = rowsum(dO * O) reads
+ * only O and dO instead of O, dO, q, k and v (the MFMA kernels size their fp16 operand scaling from
+ * the summary).  Outputs are bit-identical to those calls on grids that M divides; on a padded grid
+ * the summary, which covers only grid tokens, may choose another power-of-two operand scale, with
+ * the same error bound.
+ *
+ *   stats        device, float32, flashswin_wattn_stats_bytes() bytes, 4-byte aligned: written by
+ *                flashswin_wattn_fwd_stats for the same q, k, v and shape; read only.
+ *   dbias_u, dbias_w  as in flashswin_wattn_bwd_lowrank when rank >= 1; not written (may be NULL)
+ *                when rank == 0.
+ *   workspace    flashswin_wattn_bwd_workspace_size() bytes (rank == 0) or
+ *                flashswin_wattn_bwd_lowrank_workspace_size() bytes (rank >= 1).
+ *   Every other argument as in flashswin_wattn_bwd; the outputs may not share a byte with stats.
+ * Returns FSW_OK, FSW_ERR_INVALID_ARG, FSW_ERR_UNSUPPORTED, FSW_ERR_WORKSPACE or FSW_ERR_HIP.
+ */
+int flashswin_wattn_bwd_stats(const void* q, const void* k, const void* v, const void* out,
+                              const void* dout, const float* lse,
+                              const float* theta_row, const float* theta_col,
+                              const float* bias_u, const float* bias_w, int rank, const float* stats,
+                              void* dq, void* dk, void* dv, float* dtheta_row, float* dtheta_col,
+                              float* dbias_u, float* dbias_w,
+                              void* workspace, size_t workspace_bytes,
+                              int64_t B, int64_t Hg, int64_t Wg, int heads, int d,
+                              int M, int shift, int dtype, void* hip_stream);
+
 /* Size of the fixed per-GPU scratch array behind flashswin_wattn_bwd_noalloc: 32 MiB. */
 #define FLASHSWIN_SCRATCH_BYTES (32u * 1024u * 1024u)
 

@@ -325,3 +325,85 @@ def bwd_lr(**kw):
 ])
 def test_lowrank_backward_rejects_before_launch(kw, status):
     assert bwd_lr(**kw) == status
+
+
+# ------------------------------------------------------------------ forward operand summary entry points
+# Shape 1 x 16 x 16 tokens, 2 heads, d 32, M 8: 4 windows x 2 heads x 4 floats of summary.
+
+def test_stats_bytes():
+    assert F.flashswin_wattn_stats_bytes(1, 16, 16, 2, 32, 8, 0, F.FSW_BF16) == 4 * 2 * 16
+    assert F.flashswin_wattn_stats_bytes(3, 10, 13, 5, 64, 4, 1, F.FSW_BF16) == 3 * 3 * 4 * 5 * 16  # padded grid
+    assert F.flashswin_wattn_stats_bytes(1, 16, 16, 2, 32, 8, 8, F.FSW_BF16) == 0  # shift >= M: rejected
+
+
+def fwd_st(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, tr=FAKE + 3 * GIB, tc=FAKE + 3 * GIB + 256, bu=None, bw=None, rank=0,
+             out=FAKE + GIB, lse=FAKE + 2 * GIB, st=FAKE + 6 * GIB, B=1, Hg=16, Wg=16, heads=2, d=32, M=8, shift=0,
+             dtype=F.FSW_BF16)
+    a.update(kw)
+    return F.flashswin_wattn_fwd_stats(a["q"], a["k"], a["v"], a["tr"], a["tc"], a["bu"], a["bw"], a["rank"],
+                                       a["out"], a["lse"], a["st"], a["B"], a["Hg"], a["Wg"], a["heads"], a["d"],
+                                       a["M"], a["shift"], a["dtype"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(st=None), F.FSW_ERR_INVALID_ARG),
+    (dict(st=FAKE + 6 * GIB + 2), F.FSW_ERR_INVALID_ARG),    # misaligned
+    (dict(st=FAKE + GIB + 64), F.FSW_ERR_INVALID_ARG),       # inside out
+    (dict(st=FAKE + 3 * GIB + 8), F.FSW_ERR_INVALID_ARG),    # over theta_row
+    (dict(rank=-1), F.FSW_ERR_INVALID_ARG),
+    (dict(rank=2), F.FSW_ERR_INVALID_ARG),                   # a bias rank without factors
+    (dict(rank=F.MAX_RANK + 1, bu=FAKE + 4 * GIB, bw=FAKE + 5 * GIB), F.FSW_ERR_UNSUPPORTED),
+    (dict(rank=2, bu=FAKE + 4 * GIB, bw=FAKE + 5 * GIB, st=FAKE + 5 * GIB + 16), F.FSW_ERR_INVALID_ARG),  # in W
+    (dict(shift=8), F.FSW_ERR_INVALID_ARG),
+    (dict(d=12), F.FSW_ERR_UNSUPPORTED),
+])
+def test_stats_forward_rejects_before_launch(kw, status):
+    assert fwd_st(**kw) == status
+
+
+def test_stats_forward_empty_batch_is_a_no_op():
+    assert fwd_st(B=0, q=None, k=None, v=None, out=None, lse=None, tr=None, tc=None, st=None) == F.FSW_OK
+
+
+def bwd_st(**kw):
+    a = dict(q=FAKE, k=FAKE + GIB, v=FAKE + 2 * GIB, out=FAKE + 3 * GIB, dout=FAKE + 4 * GIB,
+             lse=FAKE + 5 * GIB, tr=FAKE + 6 * GIB, tc=FAKE + 6 * GIB + 256, bu=None, bw=None, rank=0,
+             st=FAKE + 16 * GIB, dq=FAKE + 7 * GIB, dk=FAKE + 8 * GIB, dv=FAKE + 9 * GIB, dtr=FAKE + 10 * GIB,
+             dtc=FAKE + 10 * GIB + 256, dbu=None, dbw=None, ws=FAKE + 11 * GIB, wsb=None,
+             B=1, Hg=16, Wg=16, heads=2, d=32, M=8, shift=4, dtype=F.FSW_BF16)
+    a.update(kw)
+    if a["wsb"] is None:
+        a["wsb"] = (F.flashswin_wattn_bwd_lowrank_workspace_size(a["B"], a["Hg"], a["Wg"], a["heads"], a["d"],
+                                                                 a["M"], a["shift"], a["dtype"], a["rank"])
+                    if a["rank"] > 0 else
+                    F.flashswin_wattn_bwd_workspace_size(a["B"], a["Hg"], a["Wg"], a["heads"], a["d"], a["M"],
+                                                         a["shift"], a["dtype"]))
+    return F.flashswin_wattn_bwd_stats(a["q"], a["k"], a["v"], a["out"], a["dout"], a["lse"], a["tr"], a["tc"],
+                                       a["bu"], a["bw"], a["rank"], a["st"], a["dq"], a["dk"], a["dv"], a["dtr"],
+                                       a["dtc"], a["dbu"], a["dbw"], a["ws"], a["wsb"], a["B"], a["Hg"], a["Wg"],
+                                       a["heads"], a["d"], a["M"], a["shift"], a["dtype"], None)
+
+
+LR = dict(rank=3, bu=FAKE + 12 * GIB, bw=FAKE + 13 * GIB, dbu=FAKE + 14 * GIB, dbw=FAKE + 15 * GIB)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(st=None), F.FSW_ERR_INVALID_ARG),
+    (dict(st=FAKE + 16 * GIB + 1), F.FSW_ERR_INVALID_ARG),  # misaligned
+    (dict(st=FAKE + 7 * GIB + 32), F.FSW_ERR_INVALID_ARG),  # inside dq
+    (dict(st=FAKE + 11 * GIB + 512), F.FSW_ERR_INVALID_ARG),  # inside the workspace
+    (dict(wsb=1024), F.FSW_ERR_WORKSPACE),
+    (dict(lse=None), F.FSW_ERR_INVALID_ARG),
+    (dict(LR, dbu=None), F.FSW_ERR_INVALID_ARG),
+    (dict(LR, bw=None), F.FSW_ERR_INVALID_ARG),
+    (dict(LR, dbw=FAKE + 14 * GIB + 128), F.FSW_ERR_INVALID_ARG),  # dW inside dU
+    (dict(LR, st=FAKE + 15 * GIB + 64), F.FSW_ERR_INVALID_ARG),   # dW over the summary
+    (dict(rank=F.MAX_RANK + 1, bu=FAKE + 12 * GIB, bw=FAKE + 13 * GIB), F.FSW_ERR_UNSUPPORTED),
+])
+def test_stats_backward_rejects_before_launch(kw, status):
+    assert bwd_st(**kw) == status
+
+
+def test_stats_backward_empty_batch_is_a_no_op():
+    assert bwd_st(B=0, wsb=0, q=None, k=None, v=None, out=None, dout=None, lse=None, st=None) == F.FSW_OK

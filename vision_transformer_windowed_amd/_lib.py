@@ -33,6 +33,9 @@ EXPORTED = (
     "flashswin_wattn_fwd_lowrank",
     "flashswin_wattn_bwd_lowrank_workspace_size",
     "flashswin_wattn_bwd_lowrank",
+    "flashswin_wattn_stats_bytes",
+    "flashswin_wattn_fwd_stats",
+    "flashswin_wattn_bwd_stats",
     "flashswin_status_string",
     "flashswin_version",
 )
@@ -80,6 +83,13 @@ def load():
     lib.flashswin_wattn_bwd_lowrank.restype = i32
     lib.flashswin_wattn_bwd_lowrank.argtypes = ([vp] * 10 + [i32] + [vp] * 8 + [sz, i64, i64, i64, i32, i32, i32, i32, i32,
                                                                         vp])
+    lib.flashswin_wattn_stats_bytes.restype = sz
+    lib.flashswin_wattn_stats_bytes.argtypes = [i64, i64, i64, i32, i32, i32, i32, i32]
+    lib.flashswin_wattn_fwd_stats.restype = i32
+    lib.flashswin_wattn_fwd_stats.argtypes = [vp] * 7 + [i32] + [vp] * 3 + [i64, i64, i64, i32, i32, i32, i32, i32, vp]
+    lib.flashswin_wattn_bwd_stats.restype = i32
+    lib.flashswin_wattn_bwd_stats.argtypes = ([vp] * 10 + [i32] + [vp] * 9 + [sz, i64, i64, i64, i32, i32, i32, i32,
+                                                                          i32, vp])
     lib.flashswin_status_string.restype = ctypes.c_char_p
     lib.flashswin_status_string.argtypes = [i32]
     lib.flashswin_version.restype = i32
@@ -160,8 +170,44 @@ def flashswin_wattn_bwd_lowrank(q, k, v, out, dout, lse, theta_row, theta_col, b
                                               workspace_bytes, B, Hg, Wg, heads, d, M, shift, dtype, stream)
 
 
+def flashswin_wattn_stats_bytes(B, Hg, Wg, heads, d, M, shift, dtype):
+    return load().flashswin_wattn_stats_bytes(B, Hg, Wg, heads, d, M, shift, dtype)
+
+
+def flashswin_wattn_fwd_stats(q, k, v, theta_row, theta_col, bias_u, bias_w, rank, out, lse, stats, B, Hg, Wg, heads,
+                              d, M, shift, dtype, stream):
+    """Raw call of the forward (rank 0: no bias) that also writes the operand summary for the backward."""
+    return load().flashswin_wattn_fwd_stats(q, k, v, theta_row, theta_col, bias_u, bias_w, rank, out, lse, stats, B,
+                                            Hg, Wg, heads, d, M, shift, dtype, stream)
+
+
+def flashswin_wattn_bwd_stats(q, k, v, out, dout, lse, theta_row, theta_col, bias_u, bias_w, rank, stats, dq, dk, dv,
+                              dtheta_row, dtheta_col, dbias_u, dbias_w, workspace, workspace_bytes, B, Hg, Wg, heads,
+                              d, M, shift, dtype, stream):
+    """Raw call of the backward that takes the forward's operand summary (its prologue reads only O, dO)."""
+    return load().flashswin_wattn_bwd_stats(q, k, v, out, dout, lse, theta_row, theta_col, bias_u, bias_w, rank,
+                                            stats, dq, dk, dv, dtheta_row, dtheta_col, dbias_u, dbias_w, workspace,
+                                            workspace_bytes, B, Hg, Wg, heads, d, M, shift, dtype, stream)
+
+
 def flashswin_status_string(status):
     return status_string(status)
+
+
+def new_stats(q, M, shift=0):
+    """An uninitialised operand-summary tensor (float32) for wattn_fwd(..., stats=) of q's shape."""
+    B, Hg, Wg, H, D = q.shape
+    n = flashswin_wattn_stats_bytes(B, Hg, Wg, H, D, int(M), int(shift), _dtype_code(q)) // 4
+    return torch.empty(max(n, 1), device=q.device, dtype=torch.float32)
+
+
+def _check_stats(stats, q, M, shift):
+    B, Hg, Wg, H, D = q.shape
+    n = flashswin_wattn_stats_bytes(B, Hg, Wg, H, D, int(M), int(shift), _dtype_code(q)) // 4
+    if not stats.is_cuda or stats.device != q.device or stats.dtype != torch.float32 or not stats.is_contiguous():
+        raise ValueError(f"stats must be a contiguous float32 tensor on {q.device}")
+    if stats.numel() < n:
+        raise ValueError(f"stats holds {stats.numel()} floats, the shape needs {n}")
 
 
 def bwd_workspace_bytes(q, M, shift=0):
@@ -217,8 +263,11 @@ def _workspace(workspace, nbytes, device):
     return ws, ws.numel()
 
 
-def wattn_fwd(q, k, v, theta_row, theta_col, M, shift=0, out=None, lse=None, need_lse=True):
-    """Forward window attention on the GPU.  Returns (out, lse); lse is None when need_lse=False."""
+def wattn_fwd(q, k, v, theta_row, theta_col, M, shift=0, out=None, lse=None, need_lse=True, stats=None):
+    """Forward window attention on the GPU.  Returns (out, lse); lse is None when need_lse=False.
+
+    `stats` (from new_stats) is filled with the operand summary that wattn_bwd(..., stats=) takes.
+    """
     if q.dim() != 5:
         raise ValueError("q must be [B, Hg, Wg, heads, d]")
     B, Hg, Wg, H, D = q.shape
@@ -237,6 +286,15 @@ def wattn_fwd(q, k, v, theta_row, theta_col, M, shift=0, out=None, lse=None, nee
         _check_grid("lse", lse, (B, Hg, Wg, H), torch.float32, dev)
     else:
         lse = None
+    if stats is not None:
+        _check_stats(stats, q, M, shift)
+        with torch.cuda.device(dev):
+            st = flashswin_wattn_fwd_stats(_ptr(q), _ptr(k), _ptr(v), _ptr(theta_row), _ptr(theta_col), None, None, 0,
+                                           _ptr(out), _ptr(lse), _ptr(stats), B, Hg, Wg, H, D, int(M), int(shift),
+                                           code, _stream(dev))
+        if st != FSW_OK:
+            raise FlashSwinError(st, "flashswin_wattn_fwd_stats")
+        return out, lse
     with torch.cuda.device(dev):
         st = flashswin_wattn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(theta_row), _ptr(theta_col), _ptr(out),
                                  _ptr(lse), B, Hg, Wg, H, D, int(M), int(shift), code, _stream(dev))
@@ -278,10 +336,11 @@ def wattn_fwd_materialized(q, k, v, theta_row, theta_col, M, shift=0, bias=None,
     return out, lse, nbytes
 
 
-def wattn_bwd(q, k, v, out, dout, lse, theta_row, theta_col, M, shift=0, workspace=None, grads=None):
+def wattn_bwd(q, k, v, out, dout, lse, theta_row, theta_col, M, shift=0, workspace=None, grads=None, stats=None):
     """Backward on the GPU.  Returns (dq, dk, dv, dtheta_row, dtheta_col).
 
-    `grads` may hold preallocated (dq, dk, dv, dtheta_row, dtheta_col) to write into.
+    `grads` may hold preallocated (dq, dk, dv, dtheta_row, dtheta_col) to write into.  `stats`: the
+    summary that wattn_fwd(..., stats=) wrote for these q, k, v (the prologue then reads only O, dO).
     """
     B, Hg, Wg, H, D = q.shape
     code = _dtype_code(q)
@@ -303,6 +362,16 @@ def wattn_bwd(q, k, v, out, dout, lse, theta_row, theta_col, M, shift=0, workspa
             _check_grid(name, t, (H, D // 4), torch.float32, dev)
     nbytes = flashswin_wattn_bwd_workspace_size(B, Hg, Wg, H, D, int(M), int(shift), code)
     workspace, wbytes = _workspace(workspace, nbytes, dev)
+    if stats is not None:
+        _check_stats(stats, q, M, shift)
+        with torch.cuda.device(dev):
+            st = flashswin_wattn_bwd_stats(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _ptr(lse),
+                                           _ptr(theta_row), _ptr(theta_col), None, None, 0, _ptr(stats), _ptr(dq),
+                                           _ptr(dk), _ptr(dv), _ptr(dtr), _ptr(dtc), None, None, _ptr(workspace),
+                                           wbytes, B, Hg, Wg, H, D, int(M), int(shift), code, _stream(dev))
+        if st != FSW_OK:
+            raise FlashSwinError(st, "flashswin_wattn_bwd_stats")
+        return dq, dk, dv, dtr, dtc
     with torch.cuda.device(dev):
         st = flashswin_wattn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _ptr(lse), _ptr(theta_row),
                                  _ptr(theta_col), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dtr), _ptr(dtc),
@@ -321,9 +390,10 @@ def _check_factors(bias_u, bias_w, H, M, dev):
     return rank
 
 
-def wattn_fwd_lowrank(q, k, v, theta_row, theta_col, bias_u, bias_w, M, shift=0, out=None, lse=None, need_lse=True):
+def wattn_fwd_lowrank(q, k, v, theta_row, theta_col, bias_u, bias_w, M, shift=0, out=None, lse=None, need_lse=True,
+                      stats=None):
     """Forward with a rank-r additive bias bias_u[n_i] . bias_w[n_j] on the scores (factors float32
-    [heads, M*M, rank]).  Returns (out, lse)."""
+    [heads, M*M, rank]).  Returns (out, lse).  `stats`: as in wattn_fwd."""
     B, Hg, Wg, H, D = q.shape
     code = _dtype_code(q)
     dev = q.device
@@ -341,6 +411,15 @@ def wattn_fwd_lowrank(q, k, v, theta_row, theta_col, bias_u, bias_w, M, shift=0,
         _check_grid("lse", lse, (B, Hg, Wg, H), torch.float32, dev)
     else:
         lse = None
+    if stats is not None:
+        _check_stats(stats, q, M, shift)
+        with torch.cuda.device(dev):
+            st = flashswin_wattn_fwd_stats(_ptr(q), _ptr(k), _ptr(v), _ptr(theta_row), _ptr(theta_col), _ptr(bias_u),
+                                           _ptr(bias_w), rank, _ptr(out), _ptr(lse), _ptr(stats), B, Hg, Wg, H, D,
+                                           int(M), int(shift), code, _stream(dev))
+        if st != FSW_OK:
+            raise FlashSwinError(st, "flashswin_wattn_fwd_stats")
+        return out, lse
     with torch.cuda.device(dev):
         st = flashswin_wattn_fwd_lowrank(_ptr(q), _ptr(k), _ptr(v), _ptr(theta_row), _ptr(theta_col), _ptr(bias_u),
                                          _ptr(bias_w), rank, _ptr(out), _ptr(lse), B, Hg, Wg, H, D, int(M), int(shift),
@@ -350,8 +429,10 @@ def wattn_fwd_lowrank(q, k, v, theta_row, theta_col, bias_u, bias_w, M, shift=0,
     return out, lse
 
 
-def wattn_bwd_lowrank(q, k, v, out, dout, lse, theta_row, theta_col, bias_u, bias_w, M, shift=0, workspace=None):
-    """Backward of wattn_fwd_lowrank.  Returns (dq, dk, dv, dtheta_row, dtheta_col, dbias_u, dbias_w)."""
+def wattn_bwd_lowrank(q, k, v, out, dout, lse, theta_row, theta_col, bias_u, bias_w, M, shift=0, workspace=None,
+                      stats=None):
+    """Backward of wattn_fwd_lowrank.  Returns (dq, dk, dv, dtheta_row, dtheta_col, dbias_u, dbias_w).
+    `stats`: as in wattn_bwd."""
     B, Hg, Wg, H, D = q.shape
     code = _dtype_code(q)
     dev = q.device
@@ -366,6 +447,17 @@ def wattn_bwd_lowrank(q, k, v, out, dout, lse, theta_row, theta_col, bias_u, bia
     dbu, dbw = torch.empty_like(bias_u), torch.empty_like(bias_w)
     nbytes = flashswin_wattn_bwd_lowrank_workspace_size(B, Hg, Wg, H, D, int(M), int(shift), code, rank)
     workspace, wbytes = _workspace(workspace, nbytes, dev)
+    if stats is not None:
+        _check_stats(stats, q, M, shift)
+        with torch.cuda.device(dev):
+            st = flashswin_wattn_bwd_stats(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _ptr(lse),
+                                           _ptr(theta_row), _ptr(theta_col), _ptr(bias_u), _ptr(bias_w), rank,
+                                           _ptr(stats), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dtr), _ptr(dtc), _ptr(dbu),
+                                           _ptr(dbw), _ptr(workspace), wbytes, B, Hg, Wg, H, D, int(M), int(shift),
+                                           code, _stream(dev))
+        if st != FSW_OK:
+            raise FlashSwinError(st, "flashswin_wattn_bwd_stats")
+        return dq, dk, dv, dtr, dtc, dbu, dbw
     with torch.cuda.device(dev):
         st = flashswin_wattn_bwd_lowrank(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _ptr(lse),
                                          _ptr(theta_row), _ptr(theta_col), _ptr(bias_u), _ptr(bias_w), rank, _ptr(dq),
@@ -446,15 +538,17 @@ class WindowAttention(torch.autograd.Function):
 
     @staticmethod
     def forward(ctx, q, k, v, theta_row, theta_col, M, shift):
-        out, lse = wattn_fwd(q, k, v, theta_row, theta_col, M, shift)
-        ctx.save_for_backward(q, k, v, out, lse, theta_row, theta_col)
+        # the operand summary (16 bytes per window-head) spares the backward's prologue q, k and v
+        stats = new_stats(q, M, shift)
+        out, lse = wattn_fwd(q, k, v, theta_row, theta_col, M, shift, stats=stats)
+        ctx.save_for_backward(q, k, v, out, lse, theta_row, theta_col, stats)
         ctx.M, ctx.shift = M, shift
         return out
 
     @staticmethod
     def backward(ctx, dout):
-        q, k, v, out, lse, tr, tc = ctx.saved_tensors
-        dq, dk, dv, dtr, dtc = wattn_bwd(q, k, v, out, dout.contiguous(), lse, tr, tc, ctx.M, ctx.shift)
+        q, k, v, out, lse, tr, tc, stats = ctx.saved_tensors
+        dq, dk, dv, dtr, dtc = wattn_bwd(q, k, v, out, dout.contiguous(), lse, tr, tc, ctx.M, ctx.shift, stats=stats)
         return dq, dk, dv, dtr, dtc, None, None
 
 

@@ -127,18 +127,6 @@ __device__ inline void unrotate_store(const f32x16_t& dxt, float scale, float op
 
 // ------------------------------------------------------------------------------------ prologue
 
-// Running maximum of |x| over the two bf16 values of a pair, kept as two 16-bit integers: |x| of a
-// bf16 value orders as its bits with the sign cleared.
-typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
-__device__ __forceinline__ uint32_t absmax_pair(uint32_t acc, uint32_t pair) {
-  return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(u16x2_t, acc),
-                                                                __builtin_bit_cast(u16x2_t, pair & 0x7fff7fffu)));
-}
-// The larger of the two maxima as a float; a NaN component counts as infinity.
-__device__ __forceinline__ float absmax_value(uint32_t acc) {
-  return __uint_as_float(min(max(acc & 0xffffu, acc >> 16), 0x7f80u) << 16);
-}
-
 // One workgroup per window and group of up to kPreHeads heads: Delta for every token and head, and
 // scal[wh] = {max |dO|, max |v|, max |q|, max |k|} over each window-head's components.  The heads of
 // a token sit side by side in one row, so the group's slice of every token row is read whole and
@@ -152,14 +140,18 @@ constexpr int kPreBatch = 4;
 constexpr int kPreHeads = 16;
 // Off is the type of byte offsets into the tensors: uint32_t when every offset fits (the host checks),
 // which keeps the per-item address arithmetic to a few 32-bit instructions.
-template <typename Off>
+template <typename Off, bool STATS>
 __global__ __launch_bounds__(kPreThreads) void bwd_pre_kernel(const uint16_t* __restrict__ out,
                                                               const uint16_t* __restrict__ dout,
                                                               const uint16_t* __restrict__ v,
                                                               const uint16_t* __restrict__ q,
                                                               const uint16_t* __restrict__ k,
                                                               float* __restrict__ delta, float* __restrict__ scal,
-                                                              Geom g) {
+                                                              const float* __restrict__ stats, Geom g) {
+  // STATS: the forward's per-window-head maxima of q, k and v (stats[wh] = {max |q| of a first and of
+  // a second workgroup's queries, max |k|, max |v|}) stand in for those rows, and only O and dO are
+  // read, twice as many tokens per batch.
+  constexpr int kBatch = STATS ? 2 * kPreBatch : kPreBatch;
   __shared__ float red[4][kPreThreads];
   const int groups = (g.heads + kPreHeads - 1) / kPreHeads;
   const int64_t blk = xcd_order(blockIdx.x, gridDim.x);
@@ -185,14 +177,14 @@ __global__ __launch_bounds__(kPreThreads) void bwd_pre_kernel(const uint16_t* __
   const int dr = T / g.M, dc = T - dr * g.M;
   int r = t0 / g.M, c = t0 - (t0 / g.M) * g.M;
   uint32_t am[4] = {0u, 0u, 0u, 0u};
-  const int steps = (g.N + T * kPreBatch - 1) / (T * kPreBatch);
+  const int steps = (g.N + T * kBatch - 1) / (T * kBatch);
   for (int st = 0; st < steps; ++st) {  // uniform trip count: the shuffles below see every lane
-    uint4 ro[kPreBatch], rd[kPreBatch], rv[kPreBatch], rq[kPreBatch], rk[kPreBatch];
-    Off tok[kPreBatch];
-    bool ok[kPreBatch];
+    uint4 ro[kBatch], rd[kBatch], rv[STATS ? 1 : kBatch], rq[STATS ? 1 : kBatch], rk[STATS ? 1 : kBatch];
+    Off tok[kBatch];
+    bool ok[kBatch];
 #pragma unroll
-    for (int u = 0; u < kPreBatch; ++u) {
-      const int n = (st * kPreBatch + u) * T + t0;
+    for (int u = 0; u < kBatch; ++u) {
+      const int n = (st * kBatch + u) * T + t0;
       const bool in = act && n < g.N;
       // Positions wrap at the padded extents.  An item past the end reads the window's first slot
       // again, and a padding position (or a padding first slot) reads the image's last row or column
@@ -203,12 +195,15 @@ __global__ __launch_bounds__(kPreThreads) void bwd_pre_kernel(const uint16_t* __
       ok[u] = in && yp < g.Hg && xp < g.Wg;
       const int y = min(yp, g.Hg - 1), x = min(xp, g.Wg - 1);
       tok[u] = (img + (Off)y) * (Off)g.Wg + (Off)x;
-      const Off oo = tok[u] * os2 + ch2, xo = tok[u] * xs2 + ch2;
+      const Off oo = tok[u] * os2 + ch2;
       ro[u] = load_stream(po + oo);
       rd[u] = load_stream(pd + oo);
-      rv[u] = load_stream(pv + xo);
-      rq[u] = load_stream(pq + xo);
-      rk[u] = load_stream(pk + xo);
+      if constexpr (!STATS) {
+        const Off xo = tok[u] * xs2 + ch2;
+        rv[u] = load_stream(pv + xo);
+        rq[u] = load_stream(pq + xo);
+        rk[u] = load_stream(pk + xo);
+      }
       c += dc;
       r += dr;
       if (c >= g.M) {
@@ -217,19 +212,19 @@ __global__ __launch_bounds__(kPreThreads) void bwd_pre_kernel(const uint16_t* __
       }
     }
 #pragma unroll
-    for (int u = 0; u < kPreBatch; ++u) {
-      const uint32_t wo[4] = {ro[u].x, ro[u].y, ro[u].z, ro[u].w}, wd[4] = {rd[u].x, rd[u].y, rd[u].z, rd[u].w},
-                     wv[4] = {rv[u].x, rv[u].y, rv[u].z, rv[u].w}, wq[4] = {rq[u].x, rq[u].y, rq[u].z, rq[u].w},
-                     wk[4] = {rk[u].x, rk[u].y, rk[u].z, rk[u].w};
+    for (int u = 0; u < kBatch; ++u) {
+      const uint32_t wo[4] = {ro[u].x, ro[u].y, ro[u].z, ro[u].w}, wd[4] = {rd[u].x, rd[u].y, rd[u].z, rd[u].w};
       float s = 0.f;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, wo[e]), __builtin_bit_cast(bf16x2_t, wd[e]),
                                             s, false);
         am[0] = absmax_pair(am[0], wd[e]);
-        am[1] = absmax_pair(am[1], wv[e]);
-        am[2] = absmax_pair(am[2], wq[e]);
-        am[3] = absmax_pair(am[3], wk[e]);
+      }
+      if constexpr (!STATS) {
+        am[1] = absmax_x8(am[1], rv[u]);
+        am[2] = absmax_x8(am[2], rq[u]);
+        am[3] = absmax_x8(am[3], rk[u]);
       }
       // Delta of the token and head: its four 8-channel parts sit in four consecutive lanes
       s += __shfl_xor(s, 1, 64);
@@ -237,16 +232,23 @@ __global__ __launch_bounds__(kPreThreads) void bwd_pre_kernel(const uint16_t* __
       if (ok[u] && (p & 3) == 0) delta[tok[u] * (Off)g.heads + (Off)(h0 + (p >> 2))] = s;
     }
   }
+  constexpr int kRed = STATS ? 1 : 4;  // quantities reduced here
 #pragma unroll
-  for (int i = 0; i < 4; ++i) red[i][tid] = absmax_value(am[i]);
+  for (int i = 0; i < kRed; ++i) red[i][tid] = absmax_value(am[i]);
   __syncthreads();
   if (tid < P) {  // one thread per (head, quantity): the maximum over its head's parts and tokens
     const int i = tid & 3, hh = tid >> 2;
+    const int64_t wh = win * g.heads + h0 + hh;
     float m = 0.f;
-    for (int t = 0; t < T; ++t)
+    if (STATS && i > 0) {
+      const float* s4 = stats + wh * 4;
+      m = i == 1 ? s4[3] : i == 2 ? fmaxf(s4[0], s4[1]) : s4[2];
+    } else {
+      for (int t = 0; t < T; ++t)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) m = fmaxf(m, red[i][t * P + hh * 4 + j]);
-    scal[((win * g.heads) + h0 + hh) * 4 + i] = m;
+        for (int j = 0; j < 4; ++j) m = fmaxf(m, red[i][t * P + hh * 4 + j]);
+    }
+    scal[wh * 4 + i] = m;
   }
 }
 
@@ -902,14 +904,11 @@ hipError_t launch_bwd_pre32(const BwdArgs& a, hipStream_t st) {
   const int64_t pre_blocks = g.B * g.nH * g.nW * ((g.heads + kPreHeads - 1) / kPreHeads);
   // every byte offset the pre-kernel forms is below 2 * tokens * max(xs, os)
   const bool off32 = (double)g.B * g.Hg * g.Wg * 2.0 * (double)std::max(g.xs, g.os) < 4294967296.0;
-  if (off32)
-    hipLaunchKernelGGL(bwd_pre_kernel<uint32_t>, dim3((unsigned)pre_blocks), dim3(kPreThreads), 0, st,
-                       (const uint16_t*)a.out, (const uint16_t*)a.dout, (const uint16_t*)a.v, (const uint16_t*)a.q,
-                       (const uint16_t*)a.k, a.delta, a.scal, g);
-  else
-    hipLaunchKernelGGL(bwd_pre_kernel<int64_t>, dim3((unsigned)pre_blocks), dim3(kPreThreads), 0, st,
-                       (const uint16_t*)a.out, (const uint16_t*)a.dout, (const uint16_t*)a.v, (const uint16_t*)a.q,
-                       (const uint16_t*)a.k, a.delta, a.scal, g);
+  auto* const kern = off32 ? (a.stats ? bwd_pre_kernel<uint32_t, true> : bwd_pre_kernel<uint32_t, false>)
+                            : (a.stats ? bwd_pre_kernel<int64_t, true> : bwd_pre_kernel<int64_t, false>);
+  hipLaunchKernelGGL(kern, dim3((unsigned)pre_blocks), dim3(kPreThreads), 0, st, (const uint16_t*)a.out,
+                     (const uint16_t*)a.dout, (const uint16_t*)a.v, (const uint16_t*)a.q, (const uint16_t*)a.k, a.delta,
+                     a.scal, a.stats, g);
   return hipGetLastError();
 }
 

@@ -237,24 +237,35 @@ __device__ inline void reduce_dtheta(float (&t)[D / 4], float* red, float* dst, 
 
 // ------------------------------------------------------------------------------------ prologue
 
-// One workgroup per window-head: Delta of its tokens and scal[wh] = {max |dO|, max |v|, max |q|, max |k|}.
-// Thread: 16-byte part p = tid % (D/8) of tokens tid / (D/8), tid / (D/8) + 256 / (D/8), ...  Launched
-// for d = 64; the bias kernels (d = 32) take the prologue of the chunked d = 32 kernels, which reads
-// several heads' slices of a token row at once.
-template <int D>
+// What a prologue workgroup reads and writes.
+enum PreMode {
+  kPreFull = 0,    // O, dO, q, k, v: Delta and scal
+  kPreStats = 1,   // O and dO: Delta and max |dO|; the other maxima come from the forward's stats
+  kPreMaxima = 2,  // q, k, v: the forward's stats, for the forward kernels that do not produce them
+};
+
+// One workgroup per window-head: Delta of its tokens and scal[wh] = {max |dO|, max |v|, max |q|, max |k|}
+// (or, kPreMaxima, stats[wh] = {max |q|, 0, max |k|, max |v|}).  Thread: 16-byte part p = tid % (D/8)
+// of tokens tid / (D/8), tid / (D/8) + 256 / (D/8), ...  The full prologue is launched for d = 64; the
+// bias kernels (d = 32) take the prologue of the chunked d = 32 kernels, which reads several heads'
+// slices of a token row at once.
+template <int D, int MODE>
 __global__ __launch_bounds__(256) void bwd_pre_win_kernel(const uint16_t* __restrict__ out,
                                                           const uint16_t* __restrict__ dout,
                                                           const uint16_t* __restrict__ v,
                                                           const uint16_t* __restrict__ q,
                                                           const uint16_t* __restrict__ k, float* __restrict__ delta,
-                                                          float* __restrict__ scal, Geom g) {
+                                                          float* __restrict__ scal, float* __restrict__ stats,
+                                                          Geom g) {
   constexpr int PPT = D / 8;        // parts per token
   constexpr int TPP = 256 / PPT;    // tokens per pass
   __shared__ float red[4][4];
   const int64_t wh = xcd_order(blockIdx.x, gridDim.x);
   const WinHead w = decode_winhead(g, wh);
   const int tid = threadIdx.x, p = tid % PPT;
-  float mx[4] = {0.f, 0.f, 0.f, 0.f};
+  float mx[4] = {0.f, 0.f, 0.f, 0.f};  // max |dO|, |v|, |q|, |k|
+  // a NaN component counts as infinity (fmaxf would drop it)
+  const auto amax = [](float m, float x) { return fmaxf(m, x != x ? INFINITY : fabsf(x)); };
   for (int n0 = 0; n0 < g.N; n0 += TPP) {  // uniform trip count: every lane reaches the shuffles
     const int n = n0 + tid / PPT;
     const bool ok = n < g.N && token_real(g, w.wy, w.wx, n / g.M, n % g.M);
@@ -263,25 +274,34 @@ __global__ __launch_bounds__(256) void bwd_pre_win_kernel(const uint16_t* __rest
     if (ok) {
       tok = token_index(g, w.b, w.wy, w.wx, n / g.M, n % g.M);
       const int64_t xo = tok * g.xs + w.h * D + 8 * p, oo = tok * g.os + w.h * D + 8 * p;
-      float o8[8], d8[8], v8[8], q8[8], k8[8];
-      unpack8(*reinterpret_cast<const uint4*>(out + oo), o8);
-      unpack8(*reinterpret_cast<const uint4*>(dout + oo), d8);
-      unpack8(*reinterpret_cast<const uint4*>(v + xo), v8);
-      unpack8(*reinterpret_cast<const uint4*>(q + xo), q8);
-      unpack8(*reinterpret_cast<const uint4*>(k + xo), k8);
+      if constexpr (MODE != kPreMaxima) {
+        float o8[8], d8[8];
+        unpack8(*reinterpret_cast<const uint4*>(out + oo), o8);
+        unpack8(*reinterpret_cast<const uint4*>(dout + oo), d8);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        s = __builtin_fmaf(o8[e], d8[e], s);
-        // a NaN component counts as infinity (fmaxf would drop it)
-        mx[0] = fmaxf(mx[0], d8[e] != d8[e] ? INFINITY : fabsf(d8[e]));
-        mx[1] = fmaxf(mx[1], v8[e] != v8[e] ? INFINITY : fabsf(v8[e]));
-        mx[2] = fmaxf(mx[2], q8[e] != q8[e] ? INFINITY : fabsf(q8[e]));
-        mx[3] = fmaxf(mx[3], k8[e] != k8[e] ? INFINITY : fabsf(k8[e]));
+        for (int e = 0; e < 8; ++e) {
+          s = __builtin_fmaf(o8[e], d8[e], s);
+          mx[0] = amax(mx[0], d8[e]);
+        }
+      }
+      if constexpr (MODE != kPreStats) {
+        float v8[8], q8[8], k8[8];
+        unpack8(*reinterpret_cast<const uint4*>(v + xo), v8);
+        unpack8(*reinterpret_cast<const uint4*>(q + xo), q8);
+        unpack8(*reinterpret_cast<const uint4*>(k + xo), k8);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          mx[1] = amax(mx[1], v8[e]);
+          mx[2] = amax(mx[2], q8[e]);
+          mx[3] = amax(mx[3], k8[e]);
+        }
       }
     }
+    if constexpr (MODE != kPreMaxima) {
 #pragma unroll
-    for (int o = 1; o < PPT; o <<= 1) s += __shfl_xor(s, o, 64);
-    if (ok && p == 0) delta[tok * g.heads + w.h] = s;
+      for (int o = 1; o < PPT; o <<= 1) s += __shfl_xor(s, o, 64);
+      if (ok && p == 0) delta[tok * g.heads + w.h] = s;
+    }
   }
 #pragma unroll
   for (int i = 0; i < 4; ++i) mx[i] = wave_max(mx[i]);
@@ -290,7 +310,17 @@ __global__ __launch_bounds__(256) void bwd_pre_win_kernel(const uint16_t* __rest
     for (int i = 0; i < 4; ++i) red[tid >> 6][i] = mx[i];
   }
   __syncthreads();
-  if (tid < 4) scal[wh * 4 + tid] = fmaxf(fmaxf(red[0][tid], red[1][tid]), fmaxf(red[2][tid], red[3][tid]));
+  if (tid < 4) {
+    const auto total = [&](int i) { return fmaxf(fmaxf(red[0][i], red[1][i]), fmaxf(red[2][i], red[3][i])); };
+    if constexpr (MODE == kPreMaxima) {
+      stats[wh * 4 + tid] = tid == 0 ? total(2) : tid == 1 ? 0.f : tid == 2 ? total(3) : total(1);
+    } else if constexpr (MODE == kPreStats) {
+      const float* s4 = stats + wh * 4;
+      scal[wh * 4 + tid] = tid == 0 ? total(0) : tid == 1 ? s4[3] : tid == 2 ? fmaxf(s4[0], s4[1]) : s4[2];
+    } else {
+      scal[wh * 4 + tid] = total(tid);
+    }
+  }
 }
 
 // Per head: the bias factors zero-padded from rank to RK channels (upad, wpad [heads][N][RK], so that
@@ -973,13 +1003,31 @@ hipError_t launch_bwd_d64(const BwdArgs& a, hipStream_t st) {
   const Geom& g = a.g;
   if (!bwd_d64_supported(g)) return hipErrorInvalidValue;
   const int64_t nwh = g.B * g.nH * g.nW * g.heads;
-  hipLaunchKernelGGL(bwd_pre_win_kernel<64>, dim3((unsigned)nwh), dim3(256), 0, st, (const uint16_t*)a.out,
-                     (const uint16_t*)a.dout, (const uint16_t*)a.v, (const uint16_t*)a.q, (const uint16_t*)a.k, a.delta,
-                     a.scal, g);
+  if (a.stats)
+    hipLaunchKernelGGL((bwd_pre_win_kernel<64, kPreStats>), dim3((unsigned)nwh), dim3(256), 0, st,
+                       (const uint16_t*)a.out, (const uint16_t*)a.dout, (const uint16_t*)a.v, (const uint16_t*)a.q,
+                       (const uint16_t*)a.k, a.delta, a.scal, const_cast<float*>(a.stats), g);
+  else
+    hipLaunchKernelGGL((bwd_pre_win_kernel<64, kPreFull>), dim3((unsigned)nwh), dim3(256), 0, st,
+                       (const uint16_t*)a.out, (const uint16_t*)a.dout, (const uint16_t*)a.v, (const uint16_t*)a.q,
+                       (const uint16_t*)a.k, a.delta, a.scal, nullptr, g);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (g.Hp != g.Hg || g.Wp != g.Wg) return launch_win_nw<64, 0, true>(a, st);  // the instances with padding checks
   return launch_win_nw<64, 0, false>(a, st);
+}
+
+hipError_t launch_operand_maxima(const FwdArgs& a, hipStream_t st) {
+  const Geom& g = a.g;
+  if (!a.stats || a.dtype != 1 || (g.d != 32 && g.d != 64)) return hipErrorInvalidValue;
+  const int64_t nwh = g.B * g.nH * g.nW * g.heads;
+  if (g.d == 32)
+    hipLaunchKernelGGL((bwd_pre_win_kernel<32, kPreMaxima>), dim3((unsigned)nwh), dim3(256), 0, st, nullptr, nullptr,
+                       (const uint16_t*)a.v, (const uint16_t*)a.q, (const uint16_t*)a.k, nullptr, nullptr, a.stats, g);
+  else
+    hipLaunchKernelGGL((bwd_pre_win_kernel<64, kPreMaxima>), dim3((unsigned)nwh), dim3(256), 0, st, nullptr, nullptr,
+                       (const uint16_t*)a.v, (const uint16_t*)a.q, (const uint16_t*)a.k, nullptr, nullptr, a.stats, g);
+  return hipGetLastError();
 }
 
 hipError_t launch_bwd_lowrank_mfma(const BwdArgs& a, hipStream_t st) {

@@ -142,16 +142,23 @@ BwdPath bwd_path(const fsw::Geom& g, int dtype, int rank = 0) {
 }
 
 // Pointer checks and dispatch of a forward whose shape (and q/k/v token stride) is in g.
+// stats (optional): the backward's operand maxima, from the MFMA forward itself or from a kernel of
+// their own after the float32-arithmetic forward (bf16, d 32 or 64; other shapes leave them unwritten:
+// no backward reads them).
 int fwd_impl(const void* q, const void* k, const void* v, const float* theta_row, const float* theta_col, void* out,
-             float* lse, const fsw::Geom& g, int dtype, void* hip_stream, const fsw::LowRank& lr = {}) {
+             float* lse, const fsw::Geom& g, int dtype, void* hip_stream, const fsw::LowRank& lr = {},
+             float* stats = nullptr) {
   if (!q || !k || !v || !out || !theta_row || !theta_col) return FSW_ERR_INVALID_ARG;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16)) return FSW_ERR_INVALID_ARG;
   if (!aligned(theta_row, 4) || !aligned(theta_col, 4) || (lse && !aligned(lse, 4))) return FSW_ERR_INVALID_ARG;
   fsw::FwdArgs a{q, k, v, theta_row, theta_col, out, lse, g, dtype, lr};
+  a.stats = stats;
   hipStream_t s = reinterpret_cast<hipStream_t>(hip_stream);
   const bool mfma = lr.rank == 0 ? use_mfma_fwd(g, dtype)
                                   : dtype == FSW_BF16 && fsw::fwd_mfma_lowrank_supported(g, lr.rank);
-  const hipError_t e = mfma ? fsw::launch_fwd_mfma(a, s) : fsw::launch_fwd_scalar(a, s);
+  hipError_t e = mfma ? fsw::launch_fwd_mfma(a, s) : fsw::launch_fwd_scalar(a, s);
+  if (e == hipSuccess && stats && !mfma && dtype == FSW_BF16 && (g.d == 32 || g.d == 64))
+    e = fsw::launch_operand_maxima(a, s);
   return e == hipSuccess ? FSW_OK : FSW_ERR_HIP;
 }
 
@@ -172,7 +179,8 @@ bool bwd_pointers_ok(const void* q, const void* k, const void* v, const void* ou
 int bwd_impl(const void* q, const void* k, const void* v, const void* out, const void* dout, const float* lse,
              const float* theta_row, const float* theta_col, void* dq, void* dk, void* dv, float* dtheta_row,
              float* dtheta_col, void* workspace, size_t workspace_bytes, const fsw::Geom& g, int dtype,
-             void* hip_stream, const fsw::LowRank& lr = {}, float* du = nullptr, float* dw = nullptr) {
+             void* hip_stream, const fsw::LowRank& lr = {}, float* du = nullptr, float* dw = nullptr,
+             const float* stats = nullptr) {
   if (!bwd_pointers_ok(q, k, v, out, dout, lse, theta_row, theta_col, dq, dk, dv, dtheta_row, dtheta_col))
     return FSW_ERR_INVALID_ARG;
   const BwdPath path = bwd_path(g, dtype, lr.rank);
@@ -184,6 +192,7 @@ int bwd_impl(const void* q, const void* k, const void* v, const void* out, const
                  reinterpret_cast<float*>(base + ws.delta_off), reinterpret_cast<float*>(base + ws.scal_off),
                  reinterpret_cast<float*>(base + ws.partials_off), ws.n_partials, lr, du, dw,
                  reinterpret_cast<float*>(base + ws.lr_off)};
+  a.stats = stats;
   hipStream_t s = reinterpret_cast<hipStream_t>(hip_stream);
   const hipError_t e = path == BwdPath::kMfma32         ? fsw::launch_bwd_mfma(a, s)
                        : path == BwdPath::kMfma64       ? fsw::launch_bwd_d64(a, s)
@@ -420,6 +429,72 @@ int flashswin_wattn_fwd_materialized(const void* q, const void* k, const void* v
   fsw::FwdArgs a{q, k, v, theta_row, theta_col, out, lse, g, dtype};
   const hipError_t e = fsw::launch_fwd_materialized(a, bias, workspace, reinterpret_cast<hipStream_t>(hip_stream));
   return e == hipSuccess ? FSW_OK : FSW_ERR_HIP;
+}
+
+size_t flashswin_wattn_stats_bytes(int64_t B, int64_t Hg, int64_t Wg, int heads, int d, int M, int shift, int dtype) {
+  fsw::Geom g;
+  if (check_shape(B, Hg, Wg, heads, d, M, shift, dtype, &g) != FSW_OK) return 0;
+  return (size_t)(g.B * g.nH * g.nW * g.heads) * 4 * sizeof(float);
+}
+
+int flashswin_wattn_fwd_stats(const void* q, const void* k, const void* v, const float* theta_row,
+                              const float* theta_col, const float* bias_u, const float* bias_w, int rank, void* out,
+                              float* lse, float* stats, int64_t B, int64_t Hg, int64_t Wg, int heads, int d, int M,
+                              int shift, int dtype, void* hip_stream) {
+  fsw::Geom g;
+  int st = check_shape(B, Hg, Wg, heads, d, M, shift, dtype, &g);
+  if (st != FSW_OK) return st;
+  if (rank != 0 && (st = check_lowrank(bias_u, bias_w, rank)) != FSW_OK) return st;
+  if (B == 0) return FSW_OK;
+  if (!stats || !aligned(stats, 4)) return FSW_ERR_INVALID_ARG;
+  const Sizes z = sizes_of(g, dtype);
+  const size_t fb = rank > 0 ? factor_bytes(g, rank) : 0;
+  const size_t sb = (size_t)(g.B * g.nH * g.nW * g.heads) * 4 * sizeof(float);
+  const Span outs[] = {{out, z.tens}, {lse, z.lse}, {stats, sb}};
+  const Span ins[] = {{q, z.tens}, {k, z.tens}, {v, z.tens}, {theta_row, z.theta}, {theta_col, z.theta},
+                      {bias_u, fb}, {bias_w, fb}};
+  if (!outputs_disjoint(outs, ins)) return FSW_ERR_INVALID_ARG;
+  fsw::LowRank lr;
+  if (rank > 0) {
+    lr.u = bias_u;
+    lr.w = bias_w;
+    lr.rank = rank;
+  }
+  return fwd_impl(q, k, v, theta_row, theta_col, out, lse, g, dtype, hip_stream, lr, stats);
+}
+
+int flashswin_wattn_bwd_stats(const void* q, const void* k, const void* v, const void* out, const void* dout,
+                              const float* lse, const float* theta_row, const float* theta_col, const float* bias_u,
+                              const float* bias_w, int rank, const float* stats, void* dq, void* dk, void* dv,
+                              float* dtheta_row, float* dtheta_col, float* dbias_u, float* dbias_w, void* workspace,
+                              size_t workspace_bytes, int64_t B, int64_t Hg, int64_t Wg, int heads, int d, int M,
+                              int shift, int dtype, void* hip_stream) {
+  fsw::Geom g;
+  int st = check_shape(B, Hg, Wg, heads, d, M, shift, dtype, &g);
+  if (st != FSW_OK) return st;
+  if (rank != 0 && (st = check_lowrank(bias_u, bias_w, rank)) != FSW_OK) return st;
+  if (B == 0) return FSW_OK;
+  if (!stats || !aligned(stats, 4)) return FSW_ERR_INVALID_ARG;
+  if (rank > 0 && (!dbias_u || !dbias_w || !aligned(dbias_u, 4) || !aligned(dbias_w, 4))) return FSW_ERR_INVALID_ARG;
+  const Sizes z = sizes_of(g, dtype);
+  const size_t fb = rank > 0 ? factor_bytes(g, rank) : 0;
+  const size_t sb = (size_t)(g.B * g.nH * g.nW * g.heads) * 4 * sizeof(float);
+  const Span outs[] = {{dq, z.tens},         {dk, z.tens},          {dv, z.tens},
+                       {dtheta_row, z.theta}, {dtheta_col, z.theta}, {dbias_u, fb},
+                       {dbias_w, fb},         {workspace, workspace_bytes}};
+  const Span ins[] = {{q, z.tens},    {k, z.tens},  {v, z.tens},   {out, z.tens},        {dout, z.tens},
+                      {lse, z.lse},   {bias_u, fb}, {bias_w, fb},  {theta_row, z.theta}, {theta_col, z.theta},
+                      {stats, sb}};
+  if (!outputs_disjoint(outs, ins)) return FSW_ERR_INVALID_ARG;
+  fsw::LowRank lr;
+  if (rank > 0) {
+    lr.u = bias_u;
+    lr.w = bias_w;
+    lr.rank = rank;
+  }
+  return bwd_impl(q, k, v, out, dout, lse, theta_row, theta_col, dq, dk, dv, dtheta_row, dtheta_col, workspace,
+                  workspace_bytes, g, dtype, hip_stream, lr, rank > 0 ? dbias_u : nullptr,
+                  rank > 0 ? dbias_w : nullptr, stats);
 }
 
 int flashswin_wattn_bwd_noalloc(const void* q, const void* k, const void* v, const void* out, const void* dout,

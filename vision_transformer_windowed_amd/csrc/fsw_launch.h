@@ -31,6 +31,9 @@ struct FwdArgs {
   Geom g;
   int dtype;  // 0 = float32, 1 = bf16
   LowRank lr = {};
+  // Optional (bf16, d 32 or 64): per window-head operand maxima for the backward, [windows*heads][4]
+  // = {max |q| over the queries of a first workgroup, of a second (0 if none), max |k|, max |v|}.
+  float* stats = nullptr;
 };
 
 struct BwdArgs {
@@ -58,6 +61,8 @@ struct BwdArgs {
   float* du = nullptr;      // [heads, M*M, rank]  gradient of the bias factors (rank > 0)
   float* dw = nullptr;
   float* lr_parts = nullptr;  // [2][windows][heads][M*M][rank]  per-window factor gradients (rank > 0)
+  // The forward's operand maxima (FwdArgs::stats) or null: with them the prologue reads only O and dO.
+  const float* stats = nullptr;
 };
 
 // Scalar (float32-arithmetic) paths: any d in {8,16,32,64}, any window size, either dtype, with or
@@ -74,6 +79,11 @@ bool fwd_mfma_supported(const Geom& g);
 // grids that M divides.
 bool fwd_mfma_lowrank_supported(const Geom& g, int rank);
 hipError_t launch_fwd_mfma(const FwdArgs& a, hipStream_t st);
+// The same with a.stats set: the kernels that also write the operand maxima (fwd_mfma_stats.hip).
+hipError_t launch_fwd_mfma_stats(const FwdArgs& a, hipStream_t st);
+// FwdArgs::stats of a bf16 forward (d 32 or 64) from q, k and v, for the forward kernels that do not
+// produce them.
+hipError_t launch_operand_maxima(const FwdArgs& a, hipStream_t st);
 // M = 8 windows: one wave per window-head.
 bool fwd_m8_supported(const Geom& g);
 hipError_t launch_fwd_m8(const FwdArgs& a, hipStream_t st);

@@ -187,6 +187,22 @@ __device__ __forceinline__ float quad_sum(float x) {
   return x + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xf, 0xf, false));  // [2,3,0,1]
 }
 
+// Running maximum of |x| over the two bf16 values of a pair, kept as two 16-bit integers: |x| of a
+// bf16 value orders as its bits with the sign cleared.
+typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t absmax_pair(uint32_t acc, uint32_t pair) {
+  return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(u16x2_t, acc),
+                                                                __builtin_bit_cast(u16x2_t, pair & 0x7fff7fffu)));
+}
+// The larger of the two maxima as a float; a NaN component counts as infinity.
+__device__ __forceinline__ float absmax_value(uint32_t acc) {
+  return __uint_as_float(min(max(acc & 0xffffu, acc >> 16), 0x7f80u) << 16);
+}
+// absmax_pair over the four pairs of eight bf16 values.
+__device__ __forceinline__ uint32_t absmax_x8(uint32_t acc, const uint4& x) {
+  return absmax_pair(absmax_pair(absmax_pair(absmax_pair(acc, x.x), x.y), x.z), x.w);
+}
+
 __device__ __forceinline__ float wave_max(float x) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, 64));

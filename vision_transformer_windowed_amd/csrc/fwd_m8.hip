@@ -229,7 +229,7 @@ __global__ __launch_bounds__(kM8Waves * 64, 4) void fwd_m8_kernel(const uint16_t
                                                                const float* __restrict__ th_row,
                                                                const float* __restrict__ th_col,
                                                                uint16_t* __restrict__ out, float* __restrict__ lse,
-                                                               Geom g, int64_t nwh) {
+                                                               float* __restrict__ stats, Geom g, int64_t nwh) {
   extern __shared__ __align__(16) unsigned char smem_raw[];
   // [heads][2 axes][8 positions][8 pairs] sin, then cos; per wave: V rows [64][32], labels [64]
   float* tsn = reinterpret_cast<float*>(smem_raw);
@@ -275,6 +275,23 @@ __global__ __launch_bounds__(kM8Waves * 64, 4) void fwd_m8_kernel(const uint16_t
     qm = fmaxf(qm, qn2[b]);
   }
   const bool h16 = kmax < kF16Limit && sqrtf(qm) * kM8QScale < kF16Limit;
+  if (stats) {  // the window-head's largest |component| of q, k (registers) and v (LDS row of the lane)
+    uint32_t aq = 0, ak = 0, av = 0;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      aq = absmax_x8(aq, qr[b]);
+      ak = absmax_x8(ak, kr[b]);
+      av = absmax_x8(av, *reinterpret_cast<const uint4*>(vs + lane * 32 + b * 8));
+    }
+    const float mq = wave_max(absmax_value(aq)), mk = wave_max(absmax_value(ak)), mv = wave_max(absmax_value(av));
+    if (lane == 0) {
+      float* const s4 = stats + wh * 4;
+      s4[0] = mq;
+      s4[1] = 0.f;
+      s4[2] = mk;
+      s4[3] = mv;
+    }
+  }
   const float* sn = tsn + w.h * 128;
   const float* cs = tcs + w.h * 128;
   if (h16) {
@@ -302,7 +319,8 @@ hipError_t launch_fwd_m8(const FwdArgs& a, hipStream_t st) {
   const size_t smem = (size_t)g.heads * 128 * 4 * 2 + (size_t)kM8Waves * kM8WaveLds * 2;
   const int64_t grid = (nwh + kM8Waves - 1) / kM8Waves;
   hipLaunchKernelGGL(fwd_m8_kernel, dim3((unsigned)grid), dim3(kM8Waves * 64), smem, st, (const uint16_t*)a.q,
-                     (const uint16_t*)a.k, (const uint16_t*)a.v, a.th_row, a.th_col, (uint16_t*)a.out, a.lse, g, nwh);
+                     (const uint16_t*)a.k, (const uint16_t*)a.v, a.th_row, a.th_col, (uint16_t*)a.out, a.lse, a.stats,
+                     g, nwh);
   return hipGetLastError();
 }
 

@@ -38,8 +38,10 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
-# the forward kernel instance each window size launches (M = 8: one wave per window-head)
-FWD_KERNEL = {32: "fwd_mfma_kernel<16, 32, 1024, 32, false, 0>", 16: "fwd_mfma_kernel<8, 16, 256, 32, false, 0>", 8: "fwd_m8_kernel"}
+# the forward kernel instance the step launches at each window size (the instances that write the
+# operand summary; M = 8: one wave per window-head)
+FWD_KERNEL = {32: "fwd_mfma_kernel<16, 32, 1024, 32, false, 0, true>", 16: "fwd_mfma_kernel<8, 16, 256, 32, false, 0, true>",
+              8: "fwd_m8_kernel"}
 # kernels each C-ABI call launches, in order
 CALL_LAUNCHES = {"wattn_fwd": ["fwd_mfma_kernel"],
                  "wattn_bwd": ["bwd_pre_kernel", "bwd_dkdv_mfma_kernel", "bwd_dq_mfma_kernel", "dtheta_reduce_kernel"]}

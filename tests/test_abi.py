@@ -31,7 +31,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert F.flashswin_version() >= 100
+    assert F.flashswin_version() >= 102
     for code in range(5):
         assert F.flashswin_status_string(code).startswith("FSW_")
     assert "unknown" in F.flashswin_status_string(99)

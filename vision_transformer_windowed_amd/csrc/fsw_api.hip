@@ -228,7 +228,7 @@ void* scratch_address(hipError_t* err) {
 
 extern "C" {
 
-int flashswin_version(void) { return 101; }
+int flashswin_version(void) { return 102; }
 
 const char* flashswin_status_string(int status) {
   switch (status) {

@@ -319,6 +319,30 @@ int flashswin_wattn_bwd_stats(const void* q, const void* k, const void* v, const
                               int64_t B, int64_t Hg, int64_t Wg, int heads, int d,
                               int M, int shift, int dtype, void* hip_stream);
 
+/*
+ * flashswin_wattn_fwd_packed that also writes the operand summary of flashswin_wattn_fwd_stats
+ * (stats: flashswin_wattn_stats_bytes() bytes, 4-byte aligned, not sharing a byte with qkv, theta,
+ * out or lse), for flashswin_wattn_bwd_packed_stats.  out and lse are bit-identical to
+ * flashswin_wattn_fwd_packed.  Returns as flashswin_wattn_fwd_packed.
+ */
+int flashswin_wattn_fwd_packed_stats(const void* qkv, const float* theta_row, const float* theta_col,
+                                     void* out, float* lse, float* stats,
+                                     int64_t B, int64_t Hg, int64_t Wg, int heads, int d,
+                                     int M, int shift, int dtype, void* hip_stream);
+
+/*
+ * flashswin_wattn_bwd_packed with the summary of flashswin_wattn_fwd_packed_stats (read only; the
+ * outputs may not share a byte with it): the prologue reads O and dO only.  Results as
+ * flashswin_wattn_bwd_stats describes against flashswin_wattn_bwd (bit-identical on grids that M
+ * divides).  Returns as flashswin_wattn_bwd_packed.
+ */
+int flashswin_wattn_bwd_packed_stats(const void* qkv, const void* out, const void* dout, const float* lse,
+                                     const float* theta_row, const float* theta_col, const float* stats,
+                                     void* dqkv, float* dtheta_row, float* dtheta_col,
+                                     void* workspace, size_t workspace_bytes,
+                                     int64_t B, int64_t Hg, int64_t Wg, int heads, int d,
+                                     int M, int shift, int dtype, void* hip_stream);
+
 /* Size of the fixed per-GPU scratch array behind flashswin_wattn_bwd_noalloc: 32 MiB. */
 #define FLASHSWIN_SCRATCH_BYTES (32u * 1024u * 1024u)
 

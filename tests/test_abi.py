@@ -407,3 +407,53 @@ def test_stats_backward_rejects_before_launch(kw, status):
 
 def test_stats_backward_empty_batch_is_a_no_op():
     assert bwd_st(B=0, wsb=0, q=None, k=None, v=None, out=None, dout=None, lse=None, st=None) == F.FSW_OK
+
+
+def fwd_pst(**kw):
+    a = dict(qkv=FAKE, tr=FAKE + 4 * GIB, tc=FAKE + 4 * GIB + 256, out=FAKE + GIB, lse=FAKE + 2 * GIB,
+             st=FAKE + 6 * GIB, B=1, Hg=16, Wg=16, heads=2, d=32, M=8, shift=0, dtype=F.FSW_BF16)
+    a.update(kw)
+    return F.flashswin_wattn_fwd_packed_stats(a["qkv"], a["tr"], a["tc"], a["out"], a["lse"], a["st"], a["B"],
+                                              a["Hg"], a["Wg"], a["heads"], a["d"], a["M"], a["shift"], a["dtype"],
+                                              None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(st=None), F.FSW_ERR_INVALID_ARG),
+    (dict(st=FAKE + 6 * GIB + 2), F.FSW_ERR_INVALID_ARG),  # misaligned
+    (dict(st=FAKE + 64), F.FSW_ERR_INVALID_ARG),           # inside qkv
+    (dict(st=FAKE + 2 * GIB + 16), F.FSW_ERR_INVALID_ARG),  # inside lse
+    (dict(shift=8), F.FSW_ERR_INVALID_ARG),
+])
+def test_packed_stats_forward_rejects_before_launch(kw, status):
+    assert fwd_pst(**kw) == status
+
+
+def bwd_pst(**kw):
+    a = dict(qkv=FAKE, out=FAKE + 3 * GIB, dout=FAKE + 4 * GIB, lse=FAKE + 5 * GIB, tr=FAKE + 6 * GIB,
+             tc=FAKE + 6 * GIB + 256, st=FAKE + 16 * GIB, dqkv=FAKE + 7 * GIB, dtr=FAKE + 10 * GIB,
+             dtc=FAKE + 10 * GIB + 256, ws=FAKE + 11 * GIB, wsb=None, B=1, Hg=16, Wg=16, heads=2, d=32, M=8,
+             shift=4, dtype=F.FSW_BF16)
+    a.update(kw)
+    if a["wsb"] is None:
+        a["wsb"] = F.flashswin_wattn_bwd_workspace_size(a["B"], a["Hg"], a["Wg"], a["heads"], a["d"], a["M"],
+                                                         a["shift"], a["dtype"])
+    return F.flashswin_wattn_bwd_packed_stats(a["qkv"], a["out"], a["dout"], a["lse"], a["tr"], a["tc"], a["st"],
+                                              a["dqkv"], a["dtr"], a["dtc"], a["ws"], a["wsb"], a["B"], a["Hg"],
+                                              a["Wg"], a["heads"], a["d"], a["M"], a["shift"], a["dtype"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(st=None), F.FSW_ERR_INVALID_ARG),
+    (dict(st=FAKE + 16 * GIB + 1), F.FSW_ERR_INVALID_ARG),   # misaligned
+    (dict(st=FAKE + 7 * GIB + 32), F.FSW_ERR_INVALID_ARG),   # inside dqkv
+    (dict(st=FAKE + 11 * GIB + 512), F.FSW_ERR_INVALID_ARG),  # inside the workspace
+    (dict(wsb=1024), F.FSW_ERR_WORKSPACE),
+])
+def test_packed_stats_backward_rejects_before_launch(kw, status):
+    assert bwd_pst(**kw) == status
+
+
+def test_packed_stats_empty_batch_is_a_no_op():
+    assert fwd_pst(B=0, qkv=None, out=None, lse=None, tr=None, tc=None, st=None) == F.FSW_OK
+    assert bwd_pst(B=0, wsb=0, qkv=None, out=None, dout=None, lse=None, st=None, dqkv=None) == F.FSW_OK

@@ -122,3 +122,28 @@ def test_packed_autograd_matches_separate():
         assert torch.equal(qkv.grad[:, :, :, i], t.grad), i
     assert torch.equal(tr.grad, tr2.grad)
     assert torch.equal(tc.grad, tc2.grad)
+
+
+@pytest.mark.parametrize("case", CASES, ids=IDS)
+def test_packed_with_summary_equals_separate(case):
+    """The packed calls with the operand summary: the summary, out, LSE and the packed gradient are
+    bit-identical to the separate-tensor calls with the summary on the slices (every case above has a
+    grid that M divides)."""
+    B, Hg, Wg, H, D, M, s, dt = case
+    print("case", case, flush=True)
+    x, qkv = packed_inputs(case, seed=21, with_dout=True)
+    tr, tc, dout = x["theta_row"].to(DEV), x["theta_col"].to(DEV), x["dout"].to(DEV)
+    q, k, v = (qkv[:, :, :, i].contiguous() for i in range(3))
+    st_p, st_s = F.new_stats(q, M, s), F.new_stats(q, M, s)
+    st_p.fill_(-1.0)
+    st_s.fill_(-1.0)
+    out_p, lse_p = F.wattn_fwd_packed(qkv, tr, tc, M, s, stats=st_p)
+    out_s, lse_s = F.wattn_fwd(q, k, v, tr, tc, M, s, stats=st_s)
+    dqkv, dtr_p, dtc_p = F.wattn_bwd_packed(qkv, out_p, dout, lse_p, tr, tc, M, s, stats=st_p)
+    dq, dk, dv, dtr_s, dtc_s = F.wattn_bwd(q, k, v, out_s, dout, lse_s, tr, tc, M, s, stats=st_s)
+    torch.cuda.synchronize()
+    assert torch.equal(st_p, st_s)
+    assert torch.equal(out_p, out_s) and torch.equal(lse_p, lse_s)
+    for i, t in enumerate((dq, dk, dv)):
+        assert torch.equal(dqkv[:, :, :, i], t), i
+    assert torch.equal(dtr_p, dtr_s) and torch.equal(dtc_p, dtc_s)

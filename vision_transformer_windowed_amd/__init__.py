@@ -32,12 +32,14 @@ from ._lib import (  # noqa: F401
     flashswin_wattn_bwd_lowrank_workspace_size,
     flashswin_wattn_bwd_noalloc,
     flashswin_wattn_bwd_packed,
+    flashswin_wattn_bwd_packed_stats,
     flashswin_wattn_bwd_stats,
     flashswin_wattn_fwd,
     flashswin_wattn_fwd_lowrank,
     flashswin_wattn_fwd_materialized,
     flashswin_wattn_fwd_materialized_workspace_size,
     flashswin_wattn_fwd_packed,
+    flashswin_wattn_fwd_packed_stats,
     flashswin_wattn_fwd_stats,
     flashswin_wattn_stats_bytes,
     load,

@@ -36,6 +36,8 @@ EXPORTED = (
     "flashswin_wattn_stats_bytes",
     "flashswin_wattn_fwd_stats",
     "flashswin_wattn_bwd_stats",
+    "flashswin_wattn_fwd_packed_stats",
+    "flashswin_wattn_bwd_packed_stats",
     "flashswin_status_string",
     "flashswin_version",
 )
@@ -90,6 +92,10 @@ def load():
     lib.flashswin_wattn_bwd_stats.restype = i32
     lib.flashswin_wattn_bwd_stats.argtypes = ([vp] * 10 + [i32] + [vp] * 9 + [sz, i64, i64, i64, i32, i32, i32, i32,
                                                                           i32, vp])
+    lib.flashswin_wattn_fwd_packed_stats.restype = i32
+    lib.flashswin_wattn_fwd_packed_stats.argtypes = [vp] * 6 + [i64, i64, i64, i32, i32, i32, i32, i32, vp]
+    lib.flashswin_wattn_bwd_packed_stats.restype = i32
+    lib.flashswin_wattn_bwd_packed_stats.argtypes = [vp] * 10 + [vp, sz, i64, i64, i64, i32, i32, i32, i32, i32, vp]
     lib.flashswin_status_string.restype = ctypes.c_char_p
     lib.flashswin_status_string.argtypes = [i32]
     lib.flashswin_version.restype = i32
@@ -188,6 +194,19 @@ def flashswin_wattn_bwd_stats(q, k, v, out, dout, lse, theta_row, theta_col, bia
     return load().flashswin_wattn_bwd_stats(q, k, v, out, dout, lse, theta_row, theta_col, bias_u, bias_w, rank,
                                             stats, dq, dk, dv, dtheta_row, dtheta_col, dbias_u, dbias_w, workspace,
                                             workspace_bytes, B, Hg, Wg, heads, d, M, shift, dtype, stream)
+
+
+def flashswin_wattn_fwd_packed_stats(qkv, theta_row, theta_col, out, lse, stats, B, Hg, Wg, heads, d, M, shift, dtype,
+                                     stream):
+    return load().flashswin_wattn_fwd_packed_stats(qkv, theta_row, theta_col, out, lse, stats, B, Hg, Wg, heads, d, M,
+                                                   shift, dtype, stream)
+
+
+def flashswin_wattn_bwd_packed_stats(qkv, out, dout, lse, theta_row, theta_col, stats, dqkv, dtheta_row, dtheta_col,
+                                     workspace, workspace_bytes, B, Hg, Wg, heads, d, M, shift, dtype, stream):
+    return load().flashswin_wattn_bwd_packed_stats(qkv, out, dout, lse, theta_row, theta_col, stats, dqkv, dtheta_row,
+                                                   dtheta_col, workspace, workspace_bytes, B, Hg, Wg, heads, d, M,
+                                                   shift, dtype, stream)
 
 
 def flashswin_status_string(status):
@@ -476,8 +495,9 @@ def _packed_shape(qkv):
     return B, Hg, Wg, H, D
 
 
-def wattn_fwd_packed(qkv, theta_row, theta_col, M, shift=0, out=None, lse=None, need_lse=True):
-    """Forward from packed qkv [B, Hg, Wg, 3, heads, d], read in place.  Returns (out, lse)."""
+def wattn_fwd_packed(qkv, theta_row, theta_col, M, shift=0, out=None, lse=None, need_lse=True, stats=None):
+    """Forward from packed qkv [B, Hg, Wg, 3, heads, d], read in place.  Returns (out, lse).  `stats`:
+    as in wattn_fwd (new_stats of a q-shaped tensor, or of qkv[..., 0, :, :])."""
     B, Hg, Wg, H, D = _packed_shape(qkv)
     code = _dtype_code(qkv)
     dev = qkv.device
@@ -493,6 +513,14 @@ def wattn_fwd_packed(qkv, theta_row, theta_col, M, shift=0, out=None, lse=None, 
         _check_grid("lse", lse, (B, Hg, Wg, H), torch.float32, dev)
     else:
         lse = None
+    if stats is not None:
+        _check_stats(stats, out, M, shift)
+        with torch.cuda.device(dev):
+            st = flashswin_wattn_fwd_packed_stats(_ptr(qkv), _ptr(theta_row), _ptr(theta_col), _ptr(out), _ptr(lse),
+                                                  _ptr(stats), B, Hg, Wg, H, D, int(M), int(shift), code, _stream(dev))
+        if st != FSW_OK:
+            raise FlashSwinError(st, "flashswin_wattn_fwd_packed_stats")
+        return out, lse
     with torch.cuda.device(dev):
         st = flashswin_wattn_fwd_packed(_ptr(qkv), _ptr(theta_row), _ptr(theta_col), _ptr(out), _ptr(lse), B, Hg,
                                         Wg, H, D, int(M), int(shift), code, _stream(dev))
@@ -501,10 +529,11 @@ def wattn_fwd_packed(qkv, theta_row, theta_col, M, shift=0, out=None, lse=None, 
     return out, lse
 
 
-def wattn_bwd_packed(qkv, out, dout, lse, theta_row, theta_col, M, shift=0, workspace=None, grads=None):
+def wattn_bwd_packed(qkv, out, dout, lse, theta_row, theta_col, M, shift=0, workspace=None, grads=None, stats=None):
     """Backward of wattn_fwd_packed.  Returns (dqkv, dtheta_row, dtheta_col), dqkv packed like qkv.
 
-    `grads` may hold preallocated (dqkv, dtheta_row, dtheta_col) to write into.
+    `grads` may hold preallocated (dqkv, dtheta_row, dtheta_col) to write into.  `stats`: the summary
+    wattn_fwd_packed(..., stats=) wrote for this qkv.
     """
     B, Hg, Wg, H, D = _packed_shape(qkv)
     code = _dtype_code(qkv)
@@ -524,6 +553,16 @@ def wattn_bwd_packed(qkv, out, dout, lse, theta_row, theta_col, M, shift=0, work
             _check_grid(name, t, (H, D // 4), torch.float32, dev)
     nbytes = flashswin_wattn_bwd_workspace_size(B, Hg, Wg, H, D, int(M), int(shift), code)
     workspace, wbytes = _workspace(workspace, nbytes, dev)
+    if stats is not None:
+        _check_stats(stats, out, M, shift)
+        with torch.cuda.device(dev):
+            st = flashswin_wattn_bwd_packed_stats(_ptr(qkv), _ptr(out), _ptr(dout), _ptr(lse), _ptr(theta_row),
+                                                  _ptr(theta_col), _ptr(stats), _ptr(dqkv), _ptr(dtr), _ptr(dtc),
+                                                  _ptr(workspace), wbytes, B, Hg, Wg, H, D, int(M), int(shift), code,
+                                                  _stream(dev))
+        if st != FSW_OK:
+            raise FlashSwinError(st, "flashswin_wattn_bwd_packed_stats")
+        return dqkv, dtr, dtc
     with torch.cuda.device(dev):
         st = flashswin_wattn_bwd_packed(_ptr(qkv), _ptr(out), _ptr(dout), _ptr(lse), _ptr(theta_row),
                                         _ptr(theta_col), _ptr(dqkv), _ptr(dtr), _ptr(dtc), _ptr(workspace), wbytes,
@@ -562,15 +601,16 @@ class WindowAttentionPacked(torch.autograd.Function):
 
     @staticmethod
     def forward(ctx, qkv, theta_row, theta_col, M, shift):
-        out, lse = wattn_fwd_packed(qkv, theta_row, theta_col, M, shift)
-        ctx.save_for_backward(qkv, out, lse, theta_row, theta_col)
+        stats = new_stats(qkv[:, :, :, 0], M, shift)  # the operand summary, as in WindowAttention
+        out, lse = wattn_fwd_packed(qkv, theta_row, theta_col, M, shift, stats=stats)
+        ctx.save_for_backward(qkv, out, lse, theta_row, theta_col, stats)
         ctx.M, ctx.shift = M, shift
         return out
 
     @staticmethod
     def backward(ctx, dout):
-        qkv, out, lse, tr, tc = ctx.saved_tensors
-        dqkv, dtr, dtc = wattn_bwd_packed(qkv, out, dout.contiguous(), lse, tr, tc, ctx.M, ctx.shift)
+        qkv, out, lse, tr, tc, stats = ctx.saved_tensors
+        dqkv, dtr, dtc = wattn_bwd_packed(qkv, out, dout.contiguous(), lse, tr, tc, ctx.M, ctx.shift, stats=stats)
         return dqkv, dtr, dtc, None, None
 
 

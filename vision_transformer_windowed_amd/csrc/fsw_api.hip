@@ -258,24 +258,42 @@ int flashswin_wattn_fwd(const void* q, const void* k, const void* v, const float
   return fwd_impl(q, k, v, theta_row, theta_col, out, lse, g, dtype, hip_stream);
 }
 
-int flashswin_wattn_fwd_packed(const void* qkv, const float* theta_row, const float* theta_col, void* out, float* lse,
-                               int64_t B, int64_t Hg, int64_t Wg, int heads, int d, int M, int shift, int dtype,
-                               void* hip_stream) {
+// The packed forward, with the operand summary when stats is non-null.
+static int fwd_packed_impl(const void* qkv, const float* theta_row, const float* theta_col, void* out, float* lse,
+                           float* stats, bool with_stats, int64_t B, int64_t Hg, int64_t Wg, int heads, int d, int M,
+                           int shift, int dtype, void* hip_stream) {
   fsw::Geom g;
   int st = check_shape(B, Hg, Wg, heads, d, M, shift, dtype, &g);
   if (st != FSW_OK) return st;
   if (B == 0) return FSW_OK;
   if ((long double)B * Hg * Wg * 3 * heads * d > (long double)((int64_t)1 << 56)) return FSW_ERR_UNSUPPORTED;
   if (!qkv) return FSW_ERR_INVALID_ARG;
+  if (with_stats && (!stats || !aligned(stats, 4))) return FSW_ERR_INVALID_ARG;
   const size_t eb = elem_bytes(dtype);
   const Sizes z = sizes_of(g, dtype);
-  const Span outs[] = {{out, z.tens}, {lse, z.lse}};
+  const size_t sb = with_stats ? (size_t)(g.B * g.nH * g.nW * g.heads) * 4 * sizeof(float) : 0;
+  const Span outs[] = {{out, z.tens}, {lse, z.lse}, {stats, sb}};
   const Span ins[] = {{qkv, 3 * z.tens}, {theta_row, z.theta}, {theta_col, z.theta}};
   if (!outputs_disjoint(outs, ins)) return FSW_ERR_INVALID_ARG;
   g.xs = 3 * g.os;
   const char* base = static_cast<const char*>(qkv);
   const size_t slot = (size_t)g.os * eb;  // bytes from q to k and from k to v within a token
-  return fwd_impl(base, base + slot, base + 2 * slot, theta_row, theta_col, out, lse, g, dtype, hip_stream);
+  return fwd_impl(base, base + slot, base + 2 * slot, theta_row, theta_col, out, lse, g, dtype, hip_stream, {},
+                  with_stats ? stats : nullptr);
+}
+
+int flashswin_wattn_fwd_packed(const void* qkv, const float* theta_row, const float* theta_col, void* out, float* lse,
+                               int64_t B, int64_t Hg, int64_t Wg, int heads, int d, int M, int shift, int dtype,
+                               void* hip_stream) {
+  return fwd_packed_impl(qkv, theta_row, theta_col, out, lse, nullptr, false, B, Hg, Wg, heads, d, M, shift, dtype,
+                         hip_stream);
+}
+
+int flashswin_wattn_fwd_packed_stats(const void* qkv, const float* theta_row, const float* theta_col, void* out,
+                                     float* lse, float* stats, int64_t B, int64_t Hg, int64_t Wg, int heads, int d,
+                                     int M, int shift, int dtype, void* hip_stream) {
+  return fwd_packed_impl(qkv, theta_row, theta_col, out, lse, stats, true, B, Hg, Wg, heads, d, M, shift, dtype,
+                         hip_stream);
 }
 
 size_t flashswin_wattn_bwd_workspace_size(int64_t B, int64_t Hg, int64_t Wg, int heads, int d, int M, int shift,
@@ -304,29 +322,51 @@ int flashswin_wattn_bwd(const void* q, const void* k, const void* v, const void*
                   workspace_bytes, g, dtype, hip_stream);
 }
 
-int flashswin_wattn_bwd_packed(const void* qkv, const void* out, const void* dout, const float* lse,
-                               const float* theta_row, const float* theta_col, void* dqkv, float* dtheta_row,
-                               float* dtheta_col, void* workspace, size_t workspace_bytes, int64_t B, int64_t Hg,
-                               int64_t Wg, int heads, int d, int M, int shift, int dtype, void* hip_stream) {
+// The packed backward, taking the forward's operand summary when stats is non-null.
+static int bwd_packed_impl(const void* qkv, const void* out, const void* dout, const float* lse,
+                           const float* theta_row, const float* theta_col, const float* stats, bool with_stats,
+                           void* dqkv, float* dtheta_row, float* dtheta_col, void* workspace, size_t workspace_bytes,
+                           int64_t B, int64_t Hg, int64_t Wg, int heads, int d, int M, int shift, int dtype,
+                           void* hip_stream) {
   fsw::Geom g;
   int st = check_shape(B, Hg, Wg, heads, d, M, shift, dtype, &g);
   if (st != FSW_OK) return st;
   if (B == 0) return FSW_OK;
   if ((long double)B * Hg * Wg * 3 * heads * d > (long double)((int64_t)1 << 56)) return FSW_ERR_UNSUPPORTED;
   if (!qkv || !dqkv) return FSW_ERR_INVALID_ARG;
+  if (with_stats && (!stats || !aligned(stats, 4))) return FSW_ERR_INVALID_ARG;
   const size_t eb = elem_bytes(dtype);
   const Sizes z = sizes_of(g, dtype);
+  const size_t sb = with_stats ? (size_t)(g.B * g.nH * g.nW * g.heads) * 4 * sizeof(float) : 0;
   const Span outs[] = {{dqkv, 3 * z.tens}, {dtheta_row, z.theta}, {dtheta_col, z.theta},
                        {workspace, workspace_bytes}};
   const Span ins[] = {{qkv, 3 * z.tens}, {out, z.tens}, {dout, z.tens}, {lse, z.lse}, {theta_row, z.theta},
-                      {theta_col, z.theta}};
+                      {theta_col, z.theta}, {stats, sb}};
   if (!outputs_disjoint(outs, ins)) return FSW_ERR_INVALID_ARG;
   g.xs = 3 * g.os;
   const size_t slot = (size_t)g.os * eb;
   const char* x = static_cast<const char*>(qkv);
   char* dx = static_cast<char*>(dqkv);
   return bwd_impl(x, x + slot, x + 2 * slot, out, dout, lse, theta_row, theta_col, dx, dx + slot, dx + 2 * slot,
-                  dtheta_row, dtheta_col, workspace, workspace_bytes, g, dtype, hip_stream);
+                  dtheta_row, dtheta_col, workspace, workspace_bytes, g, dtype, hip_stream, {}, nullptr, nullptr,
+                  with_stats ? stats : nullptr);
+}
+
+int flashswin_wattn_bwd_packed(const void* qkv, const void* out, const void* dout, const float* lse,
+                               const float* theta_row, const float* theta_col, void* dqkv, float* dtheta_row,
+                               float* dtheta_col, void* workspace, size_t workspace_bytes, int64_t B, int64_t Hg,
+                               int64_t Wg, int heads, int d, int M, int shift, int dtype, void* hip_stream) {
+  return bwd_packed_impl(qkv, out, dout, lse, theta_row, theta_col, nullptr, false, dqkv, dtheta_row, dtheta_col,
+                         workspace, workspace_bytes, B, Hg, Wg, heads, d, M, shift, dtype, hip_stream);
+}
+
+int flashswin_wattn_bwd_packed_stats(const void* qkv, const void* out, const void* dout, const float* lse,
+                                     const float* theta_row, const float* theta_col, const float* stats, void* dqkv,
+                                     float* dtheta_row, float* dtheta_col, void* workspace, size_t workspace_bytes,
+                                     int64_t B, int64_t Hg, int64_t Wg, int heads, int d, int M, int shift, int dtype,
+                                     void* hip_stream) {
+  return bwd_packed_impl(qkv, out, dout, lse, theta_row, theta_col, stats, true, dqkv, dtheta_row, dtheta_col,
+                         workspace, workspace_bytes, B, Hg, Wg, heads, d, M, shift, dtype, hip_stream);
 }
 
 // Low-rank bias factors of a call: rank in [1, kMaxRank], U and W non-null and 4-byte aligned.

@@ -626,14 +626,14 @@ __global__ __launch_bounds__(NWAVES * 64, (fwd_min_waves<NWAVES, D>())) void fwd
   // at its register limit there and spills.)  The slots were cleared before the barrier that ends
   // step 2; one thread folds them after the barrier below.
   unsigned* const red_u = reinterpret_cast<unsigned*>(sm.red + 2 * kMaxWaves);
-  const auto wave_absmax = [&](int slot, uint32_t acc) {
+  const auto fold_absmax = [&](int slot, uint32_t acc) {
     atomicMax(red_u + slot * 4 + (lane & 3), __float_as_uint(absmax_value(acc)));
   };
   if constexpr (STATS) {
     uint32_t a = 0;
 #pragma unroll
     for (int i = 0; i < MAXIT; ++i) a = absmax_x8(a, kraw[i]);
-    wave_absmax(1, a);
+    fold_absmax(1, a);
   }
   float kmax2 = stage_k<MAXIT, D, RK>(sm, kraw, M, split, NP, tid, NT, true);
   if constexpr (RK > 0) {
@@ -652,7 +652,7 @@ __global__ __launch_bounds__(NWAVES * 64, (fwd_min_waves<NWAVES, D>())) void fwd
     uint32_t a = 0;
 #pragma unroll
     for (int i = 0; i < MAXIT; ++i) a = absmax_x8(a, vraw[i]);
-    wave_absmax(2, a);
+    fold_absmax(2, a);
   }
   for (int b = tid; b < NB; b += NT) {
     uint32_t bits = 0, full = 1;
@@ -711,7 +711,7 @@ __global__ __launch_bounds__(NWAVES * 64, (fwd_min_waves<NWAVES, D>())) void fwd
     for (int qb = 0; qb < QBM; ++qb)
 #pragma unroll
       for (int t = 0; t < Dim::DSTEPS; ++t) a = absmax_x8(a, qraw[qb][t]);
-    wave_absmax(0, a);
+    fold_absmax(0, a);
   }
   __syncthreads();
   if (STATS && tid == 0) {

@@ -175,3 +175,35 @@ def test_float32_summary_is_not_written():
     assert torch.all(stats == -3.0)
     for n, a, b in zip(("dQ", "dK", "dV", "dtheta_row", "dtheta_col"), got, ref):
         assert torch.equal(a, b), n
+
+
+def _small_bf16_cases():
+    from test_parity_gpu import BWD_SMALL
+    return [c for c in BWD_SMALL if c[-1] == "bf16"]
+
+
+@pytest.mark.parametrize("case", _small_bf16_cases(), ids=lambda c: "B{}_{}x{}_h{}_d{}_M{}_s{}_{}".format(*c))
+def test_summary_path_matches_oracle_on_the_small_backward_cases(case):
+    """Every bf16 case of the small backward set (MFMA and float32-arithmetic kernels, shifts, padded
+    grids, d = 16, 32, 64, windows up to 64 x 64) through the calls with the operand summary, against
+    the fp64 oracle at the backward's bf16 tolerances (max-abs 2e-2, relative L2 5e-3; dtheta max-abs
+    relative to max |ref|)."""
+    B, Hg, Wg, H, D, M, s, dt = case
+    print("case", case, flush=True)
+    x = make_inputs(B, Hg, Wg, H, D, dt, seed=_seed(case) + 5, with_dout=True)
+    xd = {n: t.to(DEV) for n, t in x.items()}
+    stats = F.new_stats(xd["q"], M, s)
+    out, lse = F.wattn_fwd(xd["q"], xd["k"], xd["v"], xd["theta_row"], xd["theta_col"], M, s, stats=stats)
+    got = F.wattn_bwd(xd["q"], xd["k"], xd["v"], out, xd["dout"], lse, xd["theta_row"], xd["theta_col"], M, s,
+                      stats=stats)
+    torch.cuda.synchronize()
+    q, k, v = (x[n].double().numpy() for n in ("q", "k", "v"))
+    tr, tc = x["theta_row"].double().numpy(), x["theta_col"].double().numpy()
+    g = oracle.wattn_bwd_ref(q, k, v, x["dout"].double().numpy(), tr, tc, M, s)
+    for i, n in enumerate(("dQ", "dK", "dV", "dtheta_row", "dtheta_col")):
+        a = got[i].detach().to("cpu", torch.float64).numpy()
+        err = np.abs(a - g[i]).max()
+        l2 = np.linalg.norm(a - g[i]) / max(np.linalg.norm(g[i]), 1e-300)
+        bound = 2e-2 * (max(1.0, np.abs(g[i]).max()) if i >= 3 else 1.0)
+        print(f"  {n}: max-abs {err:.3e} (tol {bound:.1e})  rel-L2 {l2:.3e}", flush=True)
+        assert np.all(np.isfinite(a)) and err <= bound and l2 <= 5e-3, n

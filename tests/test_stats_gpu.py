@@ -207,3 +207,29 @@ def test_summary_path_matches_oracle_on_the_small_backward_cases(case):
         bound = 2e-2 * (max(1.0, np.abs(g[i]).max()) if i >= 3 else 1.0)
         print(f"  {n}: max-abs {err:.3e} (tol {bound:.1e})  rel-L2 {l2:.3e}", flush=True)
         assert np.all(np.isfinite(a)) and err <= bound and l2 <= 5e-3, n
+
+
+@pytest.mark.parametrize("name,rank", [("flashswin_t_s1_p2_m32", 0), ("flashswin_t_s1_p2_m16", 0),
+                                       ("wide_heads_s1_p2_m16_d64", 0), ("flashswin_t_s1_p2_m16", 16)])
+def test_benchmark_workloads_with_summary_are_bit_identical(name, rank):
+    """The benchmark's full-size workloads, in the launch configuration it times: the forward with the
+    summary returns the plain forward's out and LSE, and the backward with the summary the plain
+    backward's gradients, bit for bit (the plain calls are held to the oracle by the workload tests)."""
+    from vision_transformer_windowed_amd.inputs import WORKLOADS, workload_inputs
+    w = WORKLOADS[name]
+    M = w["M"]
+    print("workload", name, "rank", rank, flush=True)
+    xd = {n: t.to(DEV) for n, t in workload_inputs(name, with_dout=True).items()}
+    case = (w["B"], w["Hg"], w["Wg"], w["heads"], w["d"], M, 0, rank)
+    if rank:
+        U, W = lowrank_factors(w["heads"], M, rank, seed=2024)
+        xd["U"], xd["W"] = U.to(DEV), W.to(DEV)
+    stats = F.new_stats(xd["q"], M, 0)
+    o1, l1 = _fwd(xd, case, stats)
+    o0, l0 = _fwd(xd, case)
+    assert torch.equal(o1, o0) and torch.equal(l1, l0)
+    g1 = _bwd(xd, case, o0, l0, stats)
+    g0 = _bwd(xd, case, o0, l0)
+    torch.cuda.synchronize()
+    for n, a, b in zip(("dQ", "dK", "dV", "dtheta_row", "dtheta_col", "dU", "dW"), g1, g0):
+        assert torch.equal(a, b), n
